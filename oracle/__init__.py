@@ -1,0 +1,204 @@
+"""CPU oracle for token-block MXFP8 causal packed attention (the FLAMIA method).
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, by ``__graft_entry__.smoke()`` and by
+the CPU-baseline leg of ``bench.py``.  The product path (the HIP library and its Python
+binding) never imports, links or runs anything in this directory, and the two share no
+code.  The arithmetic lives in ``flamia_oracle.c`` (plain C, double precision); this
+module only marshals numpy arrays through ctypes.
+
+Tensor conventions: BF16 tensors are passed as numpy ``uint16`` bit patterns with layout
+[T, H, d]; codes are ``uint8`` [T, H, d]; scale tables ``uint8`` [H, T] holding the E8M0
+byte (exponent + 127); LSE and D are ``float32`` [H, T]; ``cu`` is int32 [n_docs + 1].
+"""
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "flamia_oracle.c")
+_SO = os.path.join(_HERE, "_build", "liboracle.so")
+_lib = None
+
+
+def build():
+    """Compile the oracle with gcc (-O2, no fast-math, no FP contraction, OpenMP)."""
+    os.makedirs(os.path.dirname(_SO), exist_ok=True)
+    tmp = _SO + ".tmp%d" % os.getpid()
+    subprocess.check_call(["gcc", "-O2", "-std=c99", "-fopenmp", "-ffp-contract=off", "-shared",
+                           "-fPIC", _SRC, "-o", tmp, "-lm"])
+    os.replace(tmp, _SO)
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_SO) or os.path.getmtime(_SO) < os.path.getmtime(_SRC):
+            build()
+        _lib = ctypes.CDLL(_SO)
+        _lib.orc_e4m3_decode.restype = ctypes.c_double
+        _lib.orc_e4m3_rne.restype = ctypes.c_uint8
+        _lib.orc_e8m0_roundup.restype = ctypes.c_int
+        _lib.orc_e8m0_floor.restype = ctypes.c_int
+        for f in ("orc_e4m3_rne", "orc_e8m0_roundup", "orc_e8m0_floor"):
+            getattr(_lib, f).argtypes = [ctypes.c_double]
+        _lib.orc_worklist.restype = ctypes.c_int
+        _lib.orc_num_threads.restype = ctypes.c_int
+    return _lib
+
+
+def _p(a):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def num_threads():
+    return lib().orc_num_threads()
+
+
+# ---------------------------------------------------------------------------------------
+# number formats
+def e4m3_rne(y):
+    y = _c(y, np.float64)
+    out = np.empty(y.shape, np.uint8)
+    lib().orc_e4m3_rne_array(_p(y), _p(out), ctypes.c_long(y.size))
+    return out
+
+
+def e4m3_decode(c):
+    c = _c(c, np.uint8)
+    out = np.empty(c.shape, np.float64)
+    lib().orc_e4m3_decode_array(_p(c), _p(out), ctypes.c_long(c.size))
+    return out
+
+
+def bf16_rne(y):
+    y = _c(y, np.float64)
+    out = np.empty(y.shape, np.uint16)
+    lib().orc_bf16_rne_array(_p(y), _p(out), ctypes.c_long(y.size))
+    return out
+
+
+def f16_rne(y):
+    y = _c(y, np.float64)
+    out = np.empty(y.shape, np.uint16)
+    lib().orc_f16_rne_array(_p(y), _p(out), ctypes.c_long(y.size))
+    return out
+
+
+def e8m0_roundup(a):
+    a = _c(a, np.float64)
+    out = np.empty(a.shape, np.int32)
+    lib().orc_e8m0_roundup_array(_p(a), _p(out), ctypes.c_long(a.size))
+    return out
+
+
+def e8m0_floor(a):
+    return int(lib().orc_e8m0_floor(float(a)))
+
+
+# ---------------------------------------------------------------------------------------
+# the method
+def quantize(x_bits, cu, floor_rule=False):
+    """Token-block quantiser: returns (codes [T,H,d] u8, scales [H,T] u8)."""
+    x = _c(x_bits, np.uint16)
+    T, H, d = x.shape
+    cu = _c(cu, np.int32)
+    codes = np.empty((T, H, d), np.uint8)
+    scales = np.empty((H, T), np.uint8)
+    lib().orc_quantize(_p(x), T, H, d, _p(cu), len(cu) - 1, _p(codes), _p(scales), int(bool(floor_rule)))
+    return codes, scales
+
+
+def worklist(cu, kind, n_workers):
+    """Sorted work list: int32 [n_items, 4] rows {doc, blk, cost, worker}; kind 0 = fwd, 1 = bwd."""
+    cu = _c(cu, np.int32)
+    n_docs = len(cu) - 1
+    cap = int(sum((int(cu[k + 1] - cu[k]) + 127) // 128 for k in range(n_docs))) + 1
+    out = np.empty((cap, 4), np.int32)
+    n = lib().orc_worklist(_p(cu), n_docs, int(kind), int(n_workers), _p(out), cap)
+    assert n >= 0
+    return out[:n].copy()
+
+
+def fwd(q, sq, k, sk, v, sv, cu, softmax_scale=None, p_shift=8, exact_p=False, want_o64=False):
+    """Returns (O bits u16 [T,Hq,d], LSE f32 [Hq,T] in log2 units, O64 or None)."""
+    q, k, v = _c(q, np.uint8), _c(k, np.uint8), _c(v, np.uint8)
+    sq, sk, sv = _c(sq, np.uint8), _c(sk, np.uint8), _c(sv, np.uint8)
+    T, Hq, d = q.shape
+    Hkv = k.shape[1]
+    if softmax_scale is None:
+        softmax_scale = 1.0 / np.sqrt(d)
+    cu = _c(cu, np.int32)
+    o = np.empty((T, Hq, d), np.uint16)
+    lse = np.empty((Hq, T), np.float32)
+    o64 = np.empty((T, Hq, d), np.float64) if want_o64 else None
+    lib().orc_fwd(_p(q), _p(sq), _p(k), _p(sk), _p(v), _p(sv), T, Hq, Hkv, d, ctypes.c_double(softmax_scale),
+                  _p(cu), len(cu) - 1, int(p_shift), int(bool(exact_p)), _p(o), _p(lse),
+                  _p(o64) if o64 is not None else None)
+    return o, lse, o64
+
+
+def quantize_do(do_bits, o_bits, cu):
+    """dO quantiser + D: returns (codes, scales, D f32 [H,T])."""
+    do_bits, o_bits = _c(do_bits, np.uint16), _c(o_bits, np.uint16)
+    T, H, d = do_bits.shape
+    cu = _c(cu, np.int32)
+    codes = np.empty((T, H, d), np.uint8)
+    scales = np.empty((H, T), np.uint8)
+    D = np.empty((H, T), np.float32)
+    lib().orc_quantize_do(_p(do_bits), _p(o_bits), T, H, d, _p(cu), len(cu) - 1, _p(codes), _p(scales), _p(D))
+    return codes, scales, D
+
+
+def dq_exponents(sk, sv, sdo, cu, Hkv, d, causal_dq):
+    sk, sv, sdo = _c(sk, np.uint8), _c(sv, np.uint8), _c(sdo, np.uint8)
+    Hq, T = sdo.shape
+    cu = _c(cu, np.int32)
+    pi = np.empty((Hq, T), np.int16)
+    lib().orc_dq_exponents(_p(sk), _p(sv), _p(sdo), T, Hq, Hkv, d, _p(cu), len(cu) - 1, int(bool(causal_dq)), _p(pi))
+    return pi
+
+
+class _Dbg(ctypes.Structure):
+    _fields_ = [("p_scale", ctypes.c_void_p), ("ds_scale", ctypes.c_void_p),
+                ("p_code", ctypes.c_void_p), ("ds_code", ctypes.c_void_p)]
+
+
+def bwd(q, sq, k, sk, v, sv, do, sdo, lse, D, cu, softmax_scale=None, causal_dq=False, exact=0,
+        want64=False, debug=False):
+    """Returns dict with dq, dk, dv (u16 BF16 bits), pi (i16 [Hq,T]) and optionally the
+    double-precision values (dq64, dk64, dv64) and, for single-document calls, the block
+    exponents/codes of the P and dS operands (p_scale, ds_scale [Hq,nb,nb]; p_code,
+    ds_code [Hq,L,L])."""
+    q, k, v, do = (_c(a, np.uint8) for a in (q, k, v, do))
+    sq, sk, sv, sdo = (_c(a, np.uint8) for a in (sq, sk, sv, sdo))
+    lse, D = _c(lse, np.float32), _c(D, np.float32)
+    T, Hq, d = q.shape
+    Hkv = k.shape[1]
+    if softmax_scale is None:
+        softmax_scale = 1.0 / np.sqrt(d)
+    cu = _c(cu, np.int32)
+    out = dict(dq=np.empty((T, Hq, d), np.uint16), dk=np.empty((T, Hkv, d), np.uint16),
+               dv=np.empty((T, Hkv, d), np.uint16), pi=np.empty((Hq, T), np.int16))
+    if want64:
+        out.update(dq64=np.empty((T, Hq, d)), dk64=np.empty((T, Hkv, d)), dv64=np.empty((T, Hkv, d)))
+    dbg = None
+    if debug:
+        assert len(cu) == 2 and cu[0] == 0
+        L = int(cu[1])
+        nb = (L + 31) // 32
+        out.update(p_scale=np.zeros((Hq, nb, nb), np.uint8), ds_scale=np.zeros((Hq, nb, nb), np.uint8),
+                   p_code=np.zeros((Hq, L, L), np.uint8), ds_code=np.zeros((Hq, L, L), np.uint8))
+        dbg = _Dbg(out["p_scale"].ctypes.data, out["ds_scale"].ctypes.data,
+                   out["p_code"].ctypes.data, out["ds_code"].ctypes.data)
+    lib().orc_bwd(_p(q), _p(sq), _p(k), _p(sk), _p(v), _p(sv), _p(do), _p(sdo), _p(lse), _p(D),
+                  T, Hq, Hkv, d, ctypes.c_double(softmax_scale), _p(cu), len(cu) - 1, int(bool(causal_dq)),
+                  int(exact), _p(out["dq"]), _p(out["dk"]), _p(out["dv"]), _p(out["pi"]),
+                  _p(out["dq64"]) if want64 else None, _p(out["dk64"]) if want64 else None,
+                  _p(out["dv64"]) if want64 else None, ctypes.byref(dbg) if dbg is not None else None)
+    return out

@@ -1,0 +1,625 @@
+/*
+ * CPU oracle for causal, packed-document attention on token-block MXFP8 operands
+ * (the FLAMIA method: "FLAMIA: FLAsh MIcroscaling Attention for Fast and Causally
+ * Safe Training on Blackwell", as reviewed on jaehun.me and summarised on agihunt.info).
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may call this file: only the
+ * tests, the smoke check and the CPU-baseline leg of the benchmark load it.  It shares
+ * no code, header, table or constant with the HIP library.
+ *
+ * Style: plain scalar loops in double precision.  Values are rounded only where the
+ * method itself rounds or stores a narrower type:
+ *   - operand codes (E4M3, round-to-nearest-even) and block exponents (E8M0),
+ *   - the probability and dS operands of the products (E4M3 + E8M0),
+ *   - the FP16 dQ accumulator,
+ *   - the stored outputs: O, dQ, dK, dV in BF16, LSE and D in FP32.
+ * Everything else (scores, softmax, dot products) is computed in double.
+ *
+ * Where the pages leave a step open, the reading taken is stated next to the code
+ * (the same readings are listed in the design notes of the repository).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define E4M3_MAX 448.0
+#define BLK 32        /* tokens per scale block (jaehun.me §3.1, MXFP8 path) */
+#define KV_TILE 128   /* key tile: running-max update and dQ partial-sum granularity */
+
+/* ------------------------------------------------------------------------------------
+ * Number formats
+ * ---------------------------------------------------------------------------------- */
+
+/* OCP E4M3 ("FN" variant): 1 sign, 4 exponent bits (bias 7), 3 mantissa bits; largest
+ * finite value 448 (jaehun.me §2); 0x7F / 0xFF are NaN; no infinity.  Normal values
+ * (1 + m/8) * 2^(e-7) for e = 1..15, subnormals (m/8) * 2^-6. */
+double orc_e4m3_decode(uint8_t c) {
+  int s = c >> 7, e = (c >> 3) & 15, m = c & 7;
+  double v;
+  if (e == 15 && m == 7) return NAN;
+  v = (e == 0) ? ldexp((double)m, -9) : ldexp((double)(8 + m), e - 10);
+  return s ? -v : v;
+}
+
+/* Round a double to the nearest E4M3 value, ties to even.  The sign is kept for results
+ * that round to zero.  Magnitudes that round past 448 give NaN (no saturation); the
+ * round-up exponent rule below guarantees this never happens for quantised operands. */
+uint8_t orc_e4m3_rne(double y) {
+  uint8_t sign = signbit(y) ? 0x80 : 0x00;
+  double a = fabs(y), m;
+  int e, E;
+  if (isnan(a)) return (uint8_t)(sign | 0x7F);
+  if (a < ldexp(1.0, -6)) {
+    /* subnormal range: quantum 2^-9 */
+    m = nearbyint(ldexp(a, 9));
+    return (uint8_t)(sign | (uint8_t)m); /* m == 8 encodes the smallest normal, 2^-6 */
+  }
+  frexp(a, &e);
+  E = e - 1; /* a = 1.f * 2^E, E >= -6 */
+  m = nearbyint(ldexp(a, 3 - E)); /* 8 <= m <= 16 */
+  if (m == 16.0) { m = 8.0; E += 1; }
+  if (E > 8 || (E == 8 && m > 14.0)) return (uint8_t)(sign | 0x7F);
+  return (uint8_t)(sign | ((E + 7) << 3) | ((int)m - 8));
+}
+
+/* Round-up E8M0 exponent (jaehun.me §3.2; agihunt.info): the smallest integer s such
+ * that amax <= 448 * 2^s, so no element of the block exceeds the largest code after
+ * scaling.  Clamped to the E8M0 range [-127, 127]; an all-zero block gets -127.
+ * Returns 128 (byte 0xFF, the E8M0 NaN) for a NaN or infinite amax. */
+int orc_e8m0_roundup(double amax) {
+  int e, s;
+  if (isnan(amax) || isinf(amax)) return 128;
+  if (amax == 0.0) return -127;
+  frexp(amax, &e);
+  s = e - 9;
+  while (amax > ldexp(E4M3_MAX, s)) s++;
+  while (amax <= ldexp(E4M3_MAX, s - 1)) s--;
+  if (s < -127) s = -127;
+  if (s > 127) s = 127;
+  return s;
+}
+
+/* The OCP reference conversion's exponent (jaehun.me §2): floor(log2 amax) - e_max with
+ * e_max = 8 for E4M3.  Kept only as the leaking foil of the worked example; elements
+ * above 448 after scaling are clipped to 448. */
+int orc_e8m0_floor(double amax) {
+  int e, s;
+  if (isnan(amax) || isinf(amax)) return 128;
+  if (amax == 0.0) return -127;
+  frexp(amax, &e); /* amax = f * 2^e, f in [0.5, 1): floor(log2 amax) = e - 1 */
+  s = (e - 1) - 8;
+  if (s < -127) s = -127;
+  if (s > 127) s = 127;
+  return s;
+}
+
+/* BF16: 8-bit significand, 8-bit exponent; round to nearest even directly from double
+ * (a detour through float could round twice). */
+uint16_t orc_bf16_rne(double v) {
+  uint16_t sign = signbit(v) ? 0x8000 : 0;
+  double a = fabs(v), m, r;
+  int e, q;
+  float f;
+  uint32_t u;
+  if (isnan(v)) return 0x7FC0;
+  if (a == 0.0) return sign;
+  if (isinf(a)) return (uint16_t)(sign | 0x7F80);
+  frexp(a, &e);
+  q = (e - 1 < -126) ? -133 : (e - 1) - 7; /* quantum: 2^-133 below the normal range */
+  m = nearbyint(ldexp(a, -q));
+  r = ldexp(m, q);
+  if (r >= ldexp(1.0, 128)) return (uint16_t)(sign | 0x7F80);
+  f = (float)r; /* exact */
+  memcpy(&u, &f, 4);
+  return (uint16_t)(sign | ((u >> 16) & 0x7FFF));
+}
+
+double orc_bf16_decode(uint16_t b) {
+  uint32_t u = (uint32_t)b << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return (double)f;
+}
+
+/* IEEE binary16, round to nearest even directly from double; overflow gives infinity. */
+uint16_t orc_f16_rne(double v) {
+  uint16_t sign = signbit(v) ? 0x8000 : 0;
+  double a = fabs(v), m, r;
+  int e, q, E;
+  if (isnan(v)) return 0x7E00;
+  if (a == 0.0) return sign;
+  if (isinf(a)) return (uint16_t)(sign | 0x7C00);
+  frexp(a, &e);
+  q = (e - 1 < -14) ? -24 : (e - 1) - 10;
+  m = nearbyint(ldexp(a, -q));
+  r = ldexp(m, q);
+  if (r >= 65536.0) return (uint16_t)(sign | 0x7C00);
+  if (r < ldexp(1.0, -14)) return (uint16_t)(sign | (uint16_t)m); /* subnormal (m == 1024 is 2^-14) */
+  frexp(r, &e);
+  E = e - 1;
+  return (uint16_t)(sign | ((E + 15) << 10) | ((uint16_t)(ldexp(r, 10 - E) - 1024.0)));
+}
+
+double orc_f16_decode(uint16_t h) {
+  int s = h >> 15, e = (h >> 10) & 31, m = h & 1023;
+  double v;
+  if (e == 31) return m ? NAN : (s ? -INFINITY : INFINITY);
+  v = (e == 0) ? ldexp((double)m, -24) : ldexp((double)(1024 + m), e - 25);
+  return s ? -v : v;
+}
+
+/* ------------------------------------------------------------------------------------
+ * Token-block quantiser (jaehun.me §3.1, §3.2, §3.4 "Packed documents"; agihunt.info)
+ *
+ * x: BF16 bit patterns [T][H][d] (contiguous).  For every document k = [cu[k], cu[k+1])
+ * and every block b of 32 consecutive tokens counted from the document start (the last
+ * block may be shorter), and every head h: amax over the block's tokens and all d
+ * channels -> exponent s -> scale byte s + 127 written for each token of the block in
+ * scales[h][t] (dense table, one entry per token); codes = E4M3_RNE(x * 2^-s).
+ * Tokens outside every document get code 0 and scale byte 0.
+ * floor_rule = 1 selects the leaking floor exponent (with clipping) as a test foil.
+ * ---------------------------------------------------------------------------------- */
+void orc_quantize(const uint16_t* x, int T, int H, int d, const int32_t* cu, int n_docs,
+                  uint8_t* codes, uint8_t* scales, int floor_rule) {
+  int k, h, t, c;
+  memset(codes, 0, (size_t)T * H * d);
+  memset(scales, 0, (size_t)H * T);
+  for (k = 0; k < n_docs; ++k) {
+    int t_begin = cu[k], t_end = cu[k + 1];
+    int t0;
+    for (t0 = t_begin; t0 < t_end; t0 += BLK) {
+      int t1 = t0 + BLK < t_end ? t0 + BLK : t_end;
+      for (h = 0; h < H; ++h) {
+        double amax = 0.0;
+        int s;
+        for (t = t0; t < t1; ++t)
+          for (c = 0; c < d; ++c) {
+            double a = fabs(orc_bf16_decode(x[((size_t)t * H + h) * d + c]));
+            if (a > amax || isnan(a)) amax = a;
+          }
+        s = floor_rule ? orc_e8m0_floor(amax) : orc_e8m0_roundup(amax);
+        for (t = t0; t < t1; ++t) {
+          scales[(size_t)h * T + t] = (uint8_t)(s + 127);
+          for (c = 0; c < d; ++c) {
+            double y = ldexp(orc_bf16_decode(x[((size_t)t * H + h) * d + c]), -s);
+            if (floor_rule) {
+              if (y > E4M3_MAX) y = E4M3_MAX;
+              if (y < -E4M3_MAX) y = -E4M3_MAX;
+            }
+            codes[((size_t)t * H + h) * d + c] = (s == 128) ? 0x7F : orc_e4m3_rne(y);
+          }
+        }
+      }
+    }
+  }
+}
+
+/* Decoded copy of a whole quantised tensor, [T][H][d] in double (elementwise). */
+static double* deq_all(const uint8_t* codes, const uint8_t* scales, int T, int H, int d) {
+  size_t n = (size_t)T * H * d, z;
+  double* out = (double*)malloc(sizeof(double) * (n ? n : 1));
+  for (z = 0; z < n; ++z) {
+    int t = (int)(z / ((size_t)H * d)), h = (int)((z / d) % H);
+    out[z] = ldexp(orc_e4m3_decode(codes[z]), (int)scales[(size_t)h * T + t] - 127);
+  }
+  return out;
+}
+
+/* Document index of every token (-1 for tokens outside every document). */
+static int* doc_map(const int32_t* cu, int n_docs, int T) {
+  int* m = (int*)malloc(sizeof(int) * (T ? T : 1));
+  int t, k;
+  for (t = 0; t < T; ++t) m[t] = -1;
+  for (k = 0; k < n_docs; ++k)
+    for (t = cu[k]; t < cu[k + 1]; ++t) m[t] = k;
+  return m;
+}
+
+/* ------------------------------------------------------------------------------------
+ * Work lists (jaehun.me §3.4 "Work scheduling"; agihunt.info)
+ *
+ * kind 0 (forward): one item per 256 consecutive queries of a document, counted from
+ *   the document start; cost = number of 128-key blocks the item visits, which for a
+ *   causal item b is ceil(min(256(b+1), L) / 128).
+ * kind 1 (backward): one item per 128-key tile kappa of a document; cost = number of
+ *   128-query tiles at or after the key tile, ceil((L - 128 kappa) / 128).
+ * Items are enumerated document by document, block by block, then sorted by descending
+ * cost with ties kept in enumeration order; `worker` tags the items in alternating
+ * (serpentine) directions across n_workers.  Output: 4 ints per item
+ * {doc, blk, cost, worker}.  Returns the item count, or -1 if cap is too small.
+ * ---------------------------------------------------------------------------------- */
+static int cmp_items(const void* a, const void* b) {
+  const int32_t* x = (const int32_t*)a;
+  const int32_t* y = (const int32_t*)b;
+  if (x[2] != y[2]) return x[2] > y[2] ? -1 : 1; /* cost descending */
+  return x[3] < y[3] ? -1 : (x[3] > y[3]); /* then enumeration order */
+}
+
+int orc_worklist(const int32_t* cu, int n_docs, int kind, int n_workers, int32_t* out, int cap) {
+  int k, n = 0, i;
+  int32_t* tmp;
+  for (k = 0; k < n_docs; ++k) {
+    int L = cu[k + 1] - cu[k];
+    n += kind == 0 ? (L + 255) / 256 : (L + 127) / 128;
+  }
+  if (n > cap) return -1;
+  tmp = (int32_t*)malloc(sizeof(int32_t) * 4 * (n > 0 ? n : 1));
+  n = 0;
+  for (k = 0; k < n_docs; ++k) {
+    int L = cu[k + 1] - cu[k], b;
+    int nb = kind == 0 ? (L + 255) / 256 : (L + 127) / 128;
+    for (b = 0; b < nb; ++b) {
+      int cost;
+      if (kind == 0) {
+        int hi = 256 * (b + 1) < L ? 256 * (b + 1) : L;
+        cost = (hi + 127) / 128;
+      } else {
+        cost = (L - 128 * b + 127) / 128;
+      }
+      tmp[4 * n + 0] = k;
+      tmp[4 * n + 1] = b;
+      tmp[4 * n + 2] = cost;
+      tmp[4 * n + 3] = n; /* enumeration index, for the stable tie-break */
+      n++;
+    }
+  }
+  qsort(tmp, (size_t)n, sizeof(int32_t) * 4, cmp_items);
+  for (i = 0; i < n; ++i) {
+    int r = i / n_workers, w = i % n_workers;
+    out[4 * i + 0] = tmp[4 * i + 0];
+    out[4 * i + 1] = tmp[4 * i + 1];
+    out[4 * i + 2] = tmp[4 * i + 2];
+    out[4 * i + 3] = (r % 2 == 0) ? w : n_workers - 1 - w;
+  }
+  free(tmp);
+  return n;
+}
+
+/* ------------------------------------------------------------------------------------
+ * Forward (jaehun.me §1.2 and §3.1; online softmax of the FlashAttention family)
+ *
+ * Scores in the base-2 domain: t_ij = softmax_scale * log2(e) * sum_c deq(Q_ic) deq(K_jc)
+ * (row and column scale factors sit outside the code dot product, jaehun.me §3.1).
+ * For each query row i of a document (offset r), key tiles kappa = floor(r/128) down to 0
+ * are visited (tiles counted from the document start; the diagonal tile first).  Per tile:
+ *   m' = max(m, max_j t_ij);  alpha = 2^(m - m');  p_j = 2^(t_ij - m');  l = alpha l + sum p_j;
+ *   Phat_j = E4M3_RNE(2^p_shift p_j);  acc = alpha acc + 2^-p_shift sum_j Phat_j deq(V_j).
+ * O_i = BF16(acc / l), LSE_i = FP32(m + log2 l).  Rows outside every document: O = 0,
+ * LSE = +inf.  exact_p = 1 skips the Phat rounding (used by the exact-arithmetic pins).
+ * o64 (optional) receives acc / l in double.  GQA: query head h reads KV head
+ * h / (Hq / Hkv).
+ * ---------------------------------------------------------------------------------- */
+void orc_fwd(const uint8_t* q, const uint8_t* sq, const uint8_t* k, const uint8_t* sk,
+             const uint8_t* v, const uint8_t* sv, int T, int Hq, int Hkv, int d,
+             double softmax_scale, const int32_t* cu, int n_docs, int p_shift, int exact_p,
+             uint16_t* o, float* lse, double* o64) {
+  const int group = Hq / Hkv;
+  const double c_scale = softmax_scale * 1.4426950408889634074; /* log2(e) */
+  double* Qd = deq_all(q, sq, T, Hq, d);
+  double* Kd = deq_all(k, sk, T, Hkv, d);
+  double* Vd = deq_all(v, sv, T, Hkv, d);
+  int* dm = doc_map(cu, n_docs, T);
+  long long task, n_tasks = (long long)T * Hq;
+#pragma omp parallel for schedule(dynamic, 64)
+  for (task = 0; task < n_tasks; ++task) {
+    int row = (int)(task / Hq), hh = (int)(task % Hq), g = hh / group;
+    int doc = dm[row], kappa, j, cc;
+    double m = -INFINITY, l = 0.0;
+    double acc[256];
+    double t_tile[KV_TILE];
+    const double* qi = Qd + ((size_t)row * Hq + hh) * d;
+    if (doc < 0) {
+      lse[(size_t)hh * T + row] = INFINITY;
+      for (cc = 0; cc < d; ++cc) {
+        o[((size_t)row * Hq + hh) * d + cc] = 0;
+        if (o64) o64[((size_t)row * Hq + hh) * d + cc] = 0.0;
+      }
+      continue;
+    }
+    for (cc = 0; cc < d; ++cc) acc[cc] = 0.0;
+    {
+      int start = cu[doc], r = row - start;
+      for (kappa = r / KV_TILE; kappa >= 0; --kappa) {
+        int j0 = kappa * KV_TILE, j1 = (kappa + 1) * KV_TILE;
+        double mt = -INFINITY, m_new, alpha, sum = 0.0;
+        if (j1 > r + 1) j1 = r + 1; /* causal: keys j <= i only */
+        for (j = j0; j < j1; ++j) {
+          const double* kj = Kd + ((size_t)(start + j) * Hkv + g) * d;
+          double dot = 0.0;
+          for (cc = 0; cc < d; ++cc) dot += qi[cc] * kj[cc];
+          t_tile[j - j0] = dot * c_scale;
+          if (t_tile[j - j0] > mt) mt = t_tile[j - j0];
+        }
+        m_new = m > mt ? m : mt;
+        alpha = (m == -INFINITY) ? 0.0 : exp2(m - m_new);
+        for (cc = 0; cc < d; ++cc) acc[cc] *= alpha;
+        for (j = j0; j < j1; ++j) {
+          const double* vj = Vd + ((size_t)(start + j) * Hkv + g) * d;
+          double p = exp2(t_tile[j - j0] - m_new);
+          double ph = exact_p ? p : ldexp(orc_e4m3_decode(orc_e4m3_rne(ldexp(p, p_shift))), -p_shift);
+          sum += p;
+          for (cc = 0; cc < d; ++cc) acc[cc] += ph * vj[cc];
+        }
+        l = alpha * l + sum;
+        m = m_new;
+      }
+      for (cc = 0; cc < d; ++cc) {
+        o[((size_t)row * Hq + hh) * d + cc] = orc_bf16_rne(acc[cc] / l);
+        if (o64) o64[((size_t)row * Hq + hh) * d + cc] = acc[cc] / l;
+      }
+      lse[(size_t)hh * T + row] = (float)(m + log2(l));
+    }
+  }
+  free(Qd); free(Kd); free(Vd); free(dm);
+}
+
+/* ------------------------------------------------------------------------------------
+ * dO quantiser and D (jaehun.me §3.3): dO is quantised by the same token-block rule as
+ * the inputs, and D_i = sum_c deq(dO_ic) * O_ic uses that same quantised dO (the one the
+ * backward's dP product reads) and the stored BF16 output O.  D is stored in FP32;
+ * rows outside every document get D = 0.
+ * ---------------------------------------------------------------------------------- */
+void orc_quantize_do(const uint16_t* dO, const uint16_t* O, int T, int H, int d,
+                     const int32_t* cu, int n_docs, uint8_t* codes, uint8_t* scales, float* D) {
+  int i, h, c;
+  int* dm;
+  double* dOd;
+  orc_quantize(dO, T, H, d, cu, n_docs, codes, scales, 0);
+  dm = doc_map(cu, n_docs, T);
+  dOd = deq_all(codes, scales, T, H, d);
+  for (i = 0; i < T; ++i)
+    for (h = 0; h < H; ++h) {
+      double s = 0.0;
+      if (dm[i] >= 0)
+        for (c = 0; c < d; ++c)
+          s += dOd[((size_t)i * H + h) * d + c] * orc_bf16_decode(O[((size_t)i * H + h) * d + c]);
+      D[(size_t)h * T + i] = (float)s;
+    }
+  free(dm);
+  free(dOd);
+}
+
+/* ------------------------------------------------------------------------------------
+ * dQ prescale exponent pi (jaehun.me §3.2 "Accumulator leakage", §3.4 "Backward pass")
+ *
+ * dQ partial sums are accumulated in FP16 after multiplication by 2^pi.  The pages give
+ * only the ingredients (dO, V and K magnitudes; sequence-wide by default, visible keys
+ * only with the causal option).  Reading: with C_d the smallest integer such that
+ * 2 d 448^3 <= 2^C_d, any partial sum of row i is at most 2^(C_d + E_i) with
+ * E_i = e(dO_i) + max e(V) + max e(K) over the relevant keys, so pi_i = 15 - C_d - E_i
+ * keeps every partial and the running sum below 2^15 < 65504.
+ *   default (causal_dq = 0): maxima over every token of the call, per query head;
+ *                            e(dO) also the maximum over the call;
+ *   causal  (causal_dq = 1): e(dO_i) of the row's own block, maxima of e(V), e(K) over the
+ *                            blocks of the row's document up to and including the
+ *                            row's own block.
+ * pi is clamped to [-64, 64].  Output pi[h][t]; rows outside documents get 0.
+ * ---------------------------------------------------------------------------------- */
+static int cd_const(int d) {
+  double bound = 2.0 * d * E4M3_MAX * E4M3_MAX * E4M3_MAX;
+  int C = 0;
+  while (ldexp(1.0, C) < bound) C++;
+  return C;
+}
+
+void orc_dq_exponents(const uint8_t* sk, const uint8_t* sv, const uint8_t* sdo, int T, int Hq, int Hkv,
+                      int d, const int32_t* cu, int n_docs, int causal_dq, int16_t* pi) {
+  const int group = Hq / Hkv, C = cd_const(d);
+  int h, kk, t;
+  memset(pi, 0, sizeof(int16_t) * (size_t)Hq * T);
+  for (h = 0; h < Hq; ++h) {
+    int g = h / group;
+    int max_do = -1000, max_v = -1000, max_k = -1000;
+    for (kk = 0; kk < n_docs; ++kk)
+      for (t = cu[kk]; t < cu[kk + 1]; ++t) {
+        int edo = (int)sdo[(size_t)h * T + t] - 127, ev = (int)sv[(size_t)g * T + t] - 127,
+            ek = (int)sk[(size_t)g * T + t] - 127;
+        if (edo > max_do) max_do = edo;
+        if (ev > max_v) max_v = ev;
+        if (ek > max_k) max_k = ek;
+      }
+    for (kk = 0; kk < n_docs; ++kk)
+      for (t = cu[kk]; t < cu[kk + 1]; ++t) {
+        int E, p;
+        if (!causal_dq) {
+          E = max_do + max_v + max_k;
+        } else {
+          int r = t - cu[kk];
+          int block_end = cu[kk] + (r / BLK + 1) * BLK;
+          int pv = -1000, pk = -1000, u;
+          if (block_end > cu[kk + 1]) block_end = cu[kk + 1];
+          for (u = cu[kk]; u < block_end; ++u) {
+            int ev = (int)sv[(size_t)g * T + u] - 127, ek = (int)sk[(size_t)g * T + u] - 127;
+            if (ev > pv) pv = ev;
+            if (ek > pk) pk = ek;
+          }
+          E = ((int)sdo[(size_t)h * T + t] - 127) + pv + pk;
+        }
+        p = 15 - C - E;
+        if (p < -64) p = -64;
+        if (p > 64) p = 64;
+        pi[(size_t)h * T + t] = (int16_t)p;
+      }
+  }
+}
+
+/* ------------------------------------------------------------------------------------
+ * Backward (jaehun.me §1.2, §3.1, §3.3; agihunt.info)
+ *
+ * For visible pairs (j <= i, same document):
+ *   t_ij as in the forward;  P_ij = 2^(t_ij - LSE_i) with the stored FP32 LSE;
+ *   dP_ij = sum_c deq(dO_ic) deq(V_jc);  dS_ij = P_ij (dP_ij - D_i) with the stored FP32 D.
+ * Operands of the gradient products: P and dS are each quantised to E4M3 with one
+ * round-up E8M0 exponent per 32x32 block (query block x key block, both counted from the
+ * document start; invisible entries count as zero in the block maximum).
+ *   dV_j = sum_{h in group} sum_i deq(Phat_ij) deq(dO_i)
+ *   dK_j = softmax_scale sum_{h in group} sum_i deq(dShat_ij) deq(Q_i)
+ *   dQ_i: for key tiles kappa ascending, part = sum_{j in kappa} deq(dShat_ij) deq(K_j),
+ *         acc16 = FP16(acc16 + FP16(part 2^pi_i));  dQ_i = BF16(softmax_scale acc16 2^-pi_i).
+ * exact bits: 1 = no Phat rounding, 2 = no dShat rounding, 4 = FP64 instead of the FP16
+ * accumulator (with pi still applied and removed).  Outputs are BF16; d?64 (optional)
+ * receive the values before the final BF16 rounding.  dbg_* (optional, single-document
+ * calls only) receive the P and dS block exponent bytes [Hq][nb][nb] and codes
+ * [Hq][L][L] (0 for invisible entries).
+ * ---------------------------------------------------------------------------------- */
+typedef struct {
+  uint8_t* p_scale;
+  uint8_t* ds_scale;
+  uint8_t* p_code;
+  uint8_t* ds_code;
+} orc_bwd_debug;
+
+void orc_bwd(const uint8_t* q, const uint8_t* sq, const uint8_t* k, const uint8_t* sk,
+             const uint8_t* v, const uint8_t* sv, const uint8_t* dO, const uint8_t* sdo,
+             const float* lse, const float* D, int T, int Hq, int Hkv, int d,
+             double softmax_scale, const int32_t* cu, int n_docs, int causal_dq, int exact,
+             uint16_t* dq, uint16_t* dk, uint16_t* dv, int16_t* pi_out,
+             double* dq64, double* dk64, double* dv64, const orc_bwd_debug* dbg) {
+  const int group = Hq / Hkv;
+  const double c_scale = softmax_scale * 1.4426950408889634074;
+  int16_t* pi = (int16_t*)malloc(sizeof(int16_t) * (size_t)Hq * T + 2);
+  long long task, n_tasks = (long long)n_docs * Hkv;
+  size_t n_q = (size_t)T * Hq * d, n_kv = (size_t)T * Hkv * d, z;
+  double* Qd = deq_all(q, sq, T, Hq, d);
+  double* Kd = deq_all(k, sk, T, Hkv, d);
+  double* Vd = deq_all(v, sv, T, Hkv, d);
+  double* dOd = deq_all(dO, sdo, T, Hq, d);
+  orc_dq_exponents(sk, sv, sdo, T, Hq, Hkv, d, cu, n_docs, causal_dq, pi);
+  if (pi_out) memcpy(pi_out, pi, sizeof(int16_t) * (size_t)Hq * T);
+  for (z = 0; z < n_q; ++z) { dq[z] = 0; if (dq64) dq64[z] = 0.0; }
+  for (z = 0; z < n_kv; ++z) { dk[z] = 0; dv[z] = 0; if (dk64) dk64[z] = 0.0; if (dv64) dv64[z] = 0.0; }
+
+#pragma omp parallel for schedule(dynamic, 1)
+  for (task = 0; task < n_tasks; ++task) {
+    int doc = (int)(task / Hkv), g = (int)(task % Hkv);
+    int start = cu[doc], L = cu[doc + 1] - start;
+    int nb = (L + BLK - 1) / BLK, hq, bq, bk, ii, jj, cc;
+    double* dk_acc;
+    double* dv_acc;
+    double P[BLK][BLK], dS[BLK][BLK];
+    uint8_t Pc[BLK][BLK], dSc[BLK][BLK];
+    double part[BLK * 256];
+    double acc16[BLK * 256];
+    if (L <= 0) continue;
+    dk_acc = (double*)calloc((size_t)L * d, sizeof(double));
+    dv_acc = (double*)calloc((size_t)L * d, sizeof(double));
+    for (hq = g * group; hq < (g + 1) * group; ++hq) {
+      for (bq = 0; bq < nb; ++bq) {
+        int i0 = bq * BLK, i1 = i0 + BLK < L ? i0 + BLK : L;
+        int kappa, kappa_last = (i1 - 1) / KV_TILE;
+        for (z = 0; z < (size_t)BLK * d; ++z) acc16[z] = 0.0;
+        for (kappa = 0; kappa <= kappa_last; ++kappa) {
+          for (z = 0; z < (size_t)BLK * d; ++z) part[z] = 0.0;
+          for (bk = kappa * (KV_TILE / BLK); bk < (kappa + 1) * (KV_TILE / BLK) && bk <= bq; ++bk) {
+            int j0 = bk * BLK, j1 = j0 + BLK < L ? j0 + BLK : L;
+            double pmax = 0.0, dsmax = 0.0;
+            int sp, sds;
+            /* P, dP, dS on the 32x32 block */
+            for (ii = i0; ii < i1; ++ii)
+              for (jj = j0; jj < j1; ++jj) {
+                double dot = 0.0, dp = 0.0, p;
+                if (jj > ii) { P[ii - i0][jj - j0] = 0.0; dS[ii - i0][jj - j0] = 0.0; continue; }
+                const double* qi = Qd + ((size_t)(start + ii) * Hq + hq) * d;
+                const double* doi = dOd + ((size_t)(start + ii) * Hq + hq) * d;
+                const double* kj = Kd + ((size_t)(start + jj) * Hkv + g) * d;
+                const double* vj = Vd + ((size_t)(start + jj) * Hkv + g) * d;
+                for (cc = 0; cc < d; ++cc) {
+                  dot += qi[cc] * kj[cc];
+                  dp += doi[cc] * vj[cc];
+                }
+                p = exp2(dot * c_scale - (double)lse[(size_t)hq * T + start + ii]);
+                P[ii - i0][jj - j0] = p;
+                dS[ii - i0][jj - j0] = p * (dp - (double)D[(size_t)hq * T + start + ii]);
+                if (fabs(p) > pmax) pmax = fabs(p);
+                if (fabs(dS[ii - i0][jj - j0]) > dsmax) dsmax = fabs(dS[ii - i0][jj - j0]);
+              }
+            /* block quantisation of the two product operands */
+            sp = orc_e8m0_roundup(pmax);
+            sds = orc_e8m0_roundup(dsmax);
+            for (ii = i0; ii < i1; ++ii)
+              for (jj = j0; jj < j1; ++jj) {
+                if (jj > ii) { Pc[ii - i0][jj - j0] = 0; dSc[ii - i0][jj - j0] = 0; continue; }
+                Pc[ii - i0][jj - j0] = orc_e4m3_rne(ldexp(P[ii - i0][jj - j0], -sp));
+                dSc[ii - i0][jj - j0] = orc_e4m3_rne(ldexp(dS[ii - i0][jj - j0], -sds));
+                if (!(exact & 1)) P[ii - i0][jj - j0] = ldexp(orc_e4m3_decode(Pc[ii - i0][jj - j0]), sp);
+                if (!(exact & 2)) dS[ii - i0][jj - j0] = ldexp(orc_e4m3_decode(dSc[ii - i0][jj - j0]), sds);
+              }
+            if (dbg && n_docs == 1) {
+              size_t bi = ((size_t)hq * nb + bq) * nb + bk;
+              if (dbg->p_scale) dbg->p_scale[bi] = (uint8_t)(sp + 127);
+              if (dbg->ds_scale) dbg->ds_scale[bi] = (uint8_t)(sds + 127);
+              for (ii = i0; ii < i1; ++ii)
+                for (jj = j0; jj < j1; ++jj) {
+                  size_t ci = ((size_t)hq * L + ii) * L + jj;
+                  if (dbg->p_code) dbg->p_code[ci] = Pc[ii - i0][jj - j0];
+                  if (dbg->ds_code) dbg->ds_code[ci] = dSc[ii - i0][jj - j0];
+                }
+            }
+            /* the three gradient products of this block */
+            for (ii = i0; ii < i1; ++ii)
+              for (jj = j0; jj < j1 && jj <= ii; ++jj) {
+                double ph = P[ii - i0][jj - j0], dsh = dS[ii - i0][jj - j0];
+                const double* qi = Qd + ((size_t)(start + ii) * Hq + hq) * d;
+                const double* doi = dOd + ((size_t)(start + ii) * Hq + hq) * d;
+                const double* kj = Kd + ((size_t)(start + jj) * Hkv + g) * d;
+                for (cc = 0; cc < d; ++cc) {
+                  dv_acc[(size_t)jj * d + cc] += ph * doi[cc];
+                  dk_acc[(size_t)jj * d + cc] += dsh * qi[cc];
+                  part[(size_t)(ii - i0) * d + cc] += dsh * kj[cc];
+                }
+              }
+          }
+          /* FP16 accumulation of this key tile's partial sums, in ascending tile order */
+          for (ii = i0; ii < i1; ++ii) {
+            int p = pi[(size_t)hq * T + start + ii];
+            for (cc = 0; cc < d; ++cc) {
+              double x = ldexp(part[(size_t)(ii - i0) * d + cc], p);
+              double* a = &acc16[(size_t)(ii - i0) * d + cc];
+              if (exact & 4) *a += x;
+              else *a = orc_f16_decode(orc_f16_rne(*a + orc_f16_decode(orc_f16_rne(x))));
+            }
+          }
+        }
+        for (ii = i0; ii < i1; ++ii) {
+          int p = pi[(size_t)hq * T + start + ii];
+          for (cc = 0; cc < d; ++cc) {
+            double val = softmax_scale * ldexp(acc16[(size_t)(ii - i0) * d + cc], -p);
+            dq[((size_t)(start + ii) * Hq + hq) * d + cc] = orc_bf16_rne(val);
+            if (dq64) dq64[((size_t)(start + ii) * Hq + hq) * d + cc] = val;
+          }
+        }
+      }
+    }
+    for (jj = 0; jj < L; ++jj)
+      for (cc = 0; cc < d; ++cc) {
+        double kval = softmax_scale * dk_acc[(size_t)jj * d + cc], vval = dv_acc[(size_t)jj * d + cc];
+        dk[((size_t)(start + jj) * Hkv + g) * d + cc] = orc_bf16_rne(kval);
+        dv[((size_t)(start + jj) * Hkv + g) * d + cc] = orc_bf16_rne(vval);
+        if (dk64) dk64[((size_t)(start + jj) * Hkv + g) * d + cc] = kval;
+        if (dv64) dv64[((size_t)(start + jj) * Hkv + g) * d + cc] = vval;
+      }
+    free(dk_acc);
+    free(dv_acc);
+  }
+  free(pi);
+  free(Qd); free(Kd); free(Vd); free(dOd);
+}
+
+int orc_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
+/* Array forms of the codecs (elementwise), for the tests. */
+void orc_e4m3_rne_array(const double* y, uint8_t* out, long n) { long i; for (i = 0; i < n; ++i) out[i] = orc_e4m3_rne(y[i]); }
+void orc_e4m3_decode_array(const uint8_t* c, double* out, long n) { long i; for (i = 0; i < n; ++i) out[i] = orc_e4m3_decode(c[i]); }
+void orc_bf16_rne_array(const double* y, uint16_t* out, long n) { long i; for (i = 0; i < n; ++i) out[i] = orc_bf16_rne(y[i]); }
+void orc_f16_rne_array(const double* y, uint16_t* out, long n) { long i; for (i = 0; i < n; ++i) out[i] = orc_f16_rne(y[i]); }
+void orc_e8m0_roundup_array(const double* a, int32_t* out, long n) { long i; for (i = 0; i < n; ++i) out[i] = orc_e8m0_roundup(a[i]); }

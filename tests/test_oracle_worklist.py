@@ -1,0 +1,71 @@
+"""Pins for the oracle's work lists (jaehun.me section 3.4 "Work scheduling": an item is
+256 consecutive queries of one document, its cost the number of key blocks it visits,
+items sorted by descending cost and assigned in alternating directions; the backward
+orders key tiles by descending cost.  agihunt.info: the list for 131,072 one-token
+documents)."""
+import numpy as np
+
+from precision_causal_attention_token_amd import workloads
+
+
+def _check(orc, cu, G=7):
+    L = np.diff(cu).astype(np.int64)
+    for kind, size in ((0, 256), (1, 128)):
+        items = orc.worklist(cu, kind, G)
+        n_expect = int(((L + size - 1) // size).sum())
+        assert items.shape == (n_expect, 4)                               # W1: item count
+        # W2: closed-form total cost.  fwd: doc with n items and m = ceil(L/128) key tiles
+        # costs 2 + 4 + ... + 2(n-1) + m = n(n-1) + m ; bwd: m + (m-1) + ... + 1.
+        m = (L + 127) // 128
+        n = (L + 255) // 256
+        total = (n * (n - 1) + m)[L > 0].sum() if kind == 0 else (m * (m + 1) // 2).sum()
+        assert items[:, 2].sum() == total
+        # W3: a permutation of the enumeration, non-increasing cost, ties in enumeration order
+        enum = [(k, b) for k in range(len(L)) for b in range(int((L[k] + size - 1) // size))]
+        assert sorted(map(tuple, items[:, :2].tolist())) == enum
+        assert np.all(np.diff(items[:, 2]) <= 0)
+        for c in np.unique(items[:, 2]):
+            sel = items[items[:, 2] == c, :2]
+            keys = sel[:, 0].astype(np.int64) * 1_000_000 + sel[:, 1]
+            assert np.all(np.diff(keys) > 0)
+        # each item's cost against its own definition (brute force over its keys)
+        for doc, blk, cost, _ in items[:50]:
+            Ld = int(L[doc])
+            if kind == 0:
+                qs = range(256 * blk, min(256 * (blk + 1), Ld))
+                visited = {j // 128 for i in qs for j in range(0, i + 1, 127)} | {i // 128 for i in qs}
+                assert cost == len(visited)
+            else:
+                assert cost == len(range(128 * blk, Ld, 128))
+        # serpentine tags
+        idx = np.arange(len(items))
+        r, w = idx // G, idx % G
+        assert np.array_equal(items[:, 3], np.where(r % 2 == 0, w, G - 1 - w))
+
+
+def test_random_small(orc):
+    for seed in range(8):
+        lens = workloads.random_lengths(3000, 1, 700, seed=seed)
+        if seed % 2:
+            lens[1] = 0  # an empty document
+        _check(orc, workloads.cu_seqlens(lens))
+
+
+def test_lognormal_workload(orc):
+    _check(orc, workloads.cu_seqlens(workloads.doc_lengths("lognormal")))
+
+
+def test_extreme_packing_lists(orc):
+    """W4: one 131072-token document -> forward costs 1024, 1022, ..., 2; 131072 one-token
+    documents -> 131072 cost-1 items in enumeration order."""
+    one = workloads.cu_seqlens([131072])
+    f = orc.worklist(one, 0, 256)
+    assert np.array_equal(f[:, 2], np.arange(1024, 0, -2))
+    assert np.array_equal(f[:, 1], np.arange(511, -1, -1))
+    b = orc.worklist(one, 1, 256)
+    assert np.array_equal(b[:, 2], np.arange(1024, 0, -1))
+    toks = workloads.cu_seqlens([1] * 131072)
+    for kind in (0, 1):
+        t = orc.worklist(toks, kind, 256)
+        assert len(t) == 131072 and np.all(t[:, 2] == 1)
+        assert np.array_equal(t[:, 0], np.arange(131072)) and not t[:, 1].any()
