@@ -1,0 +1,186 @@
+#!/usr/bin/env python3
+"""Throughput of the causal token-block MXFP8 attention training call on one MI355X.
+
+A step is one pass of the whole hot path over one batch of synthetic packed input already
+resident in HBM: quantise Q, K, V -> forward -> quantise dO (+ D) -> backward.  The work lists
+are built once per micro-batch (jaehun.me review §3.4) and are timed separately.
+
+value = algorithmic FLOP per step / step time, with the causal FLOP count
+14 * d * Hq * sum_docs L (L + 1) / 2 (forward 4d, backward 10d per visible query-key pair).
+
+Prints one JSON line.  Extra objects: `roofline` (dominant kernel vs the MI355X dense FP8
+peak, timed with HIP events on the launch stream), `quantize` (HBM roofline of the quantiser
+passes), `stages_ms`, `worklist_ms`, and `cpu_baseline` (the CPU oracle on a bounded sample
+of the same workload).
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "causal MXFP8 attn fwd+bwd TFLOPS incl. quantize; % of MI355X MXFP8 peak"
+PEAK_FP8_TFLOPS = 5000.0     # MI355X dense FP8 / MXFP8 matrix peak
+PEAK_HBM_GBPS = 8000.0       # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="long")
+    ap.add_argument("--causal-dq", action="store_true", help="causal dQ prescale option")
+    ap.add_argument("--cpu-pairs", type=float, default=2.0e7, help="query-key pairs in the CPU-oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def cpu_baseline(workload_name, pairs_budget):
+    """Time the oracle (test infrastructure, untuned) on a bounded sample: documents of the
+    workload in order, each truncated to 4096 tokens, one head, until pairs_budget
+    query-key pairs are covered."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from precision_causal_attention_token_amd import workloads
+
+    cu, shp, (q, k, v, do) = workloads.workload(workload_name)
+    lens, spans, pairs = [], [], 0
+    for a, b in zip(cu[:-1], cu[1:]):
+        L = min(int(b - a), 4096)
+        if L <= 0:
+            continue
+        lens.append(L)
+        spans.append((int(a), int(a) + L))
+        pairs += L * (L + 1) // 2
+        if pairs >= pairs_budget:
+            break
+    idx = np.concatenate([np.arange(a, b) for a, b in spans])
+    cs = workloads.cu_seqlens(lens)
+
+    def bits(x):
+        return x[idx][:, :1].contiguous().view(torch.int16).numpy().view(np.uint16)
+
+    oracle.lib()
+    t0 = time.perf_counter()
+    qc = [oracle.quantize(bits(x), cs) for x in (q, k, v)]
+    o, lse, _ = oracle.fwd(*qc[0], *qc[1], *qc[2], cs)
+    dc, dsc, D = oracle.quantize_do(bits(do), o, cs)
+    oracle.bwd(*qc[0], *qc[1], *qc[2], dc, dsc, lse, D, cs)
+    dt = time.perf_counter() - t0
+    flop = 14.0 * shp.d * 1 * pairs
+    return {"value": flop / dt / 1e12, "unit": "TFLOPS", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": "%s workload: first %d documents (each truncated to 4096 tokens, %d tokens), head 0 only, "
+                      "%d query-key pairs; quantise + forward + dO pass + backward in %.2f s"
+                      % (workload_name, len(lens), len(idx), pairs, dt),
+            "seconds": dt}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: the path has no multi-GPU component (--gpus %d refused)" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import precision_causal_attention_token_amd as fl
+    from precision_causal_attention_token_amd import workloads
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cu, shp, (q, k, v, do) = workloads.workload(args.workload)
+    T, Hq, Hkv, d = shp.T, shp.Hq, shp.Hkv, shp.d
+    pairs = workloads.visible_pairs(cu)
+    flop = 14.0 * d * Hq * pairs
+    q, k, v, do = (x.to(dev) for x in (q, k, v, do))
+    cu_d = torch.as_tensor(cu).to(dev)
+    print("bench: workload %s T=%d Hq=%d Hkv=%d d=%d docs=%d pairs=%d" % (args.workload, T, Hq, Hkv, d,
+                                                                          len(cu) - 1, pairs), file=sys.stderr,
+          flush=True)
+
+    # work lists: built once per micro-batch, timed on their own
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    wl_ms = []
+    for _ in range(5):
+        e0, e1 = ev(), ev()
+        e0.record()
+        lists = fl.Lists(cu_d, T)
+        e1.record()
+        torch.cuda.synchronize()
+        wl_ms.append(e0.elapsed_time(e1))
+    ws = torch.empty(fl.load_library().flamia_bwd_workspace_bytes(T, Hq), dtype=torch.uint8, device=dev)
+
+    stage_names = ("quantize_qkv", "fwd", "quantize_do", "bwd")
+
+    def step(evs=None):
+        if evs: evs[0].record()
+        qz, kz, vz = fl.quantize([q, k, v], cu_d)
+        if evs: evs[1].record()
+        o, lse = fl.fwd(qz, kz, vz, cu_d, lists.fwd)
+        if evs: evs[2].record()
+        dc, dsc, D = fl.quantize_do(do, o, cu_d)
+        if evs: evs[3].record()
+        out = fl.bwd(qz, kz, vz, (dc, dsc), lse, D, cu_d, lists.bwd, None, args.causal_dq, workspace=ws)
+        if evs: evs[4].record()
+        return out
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    assert fl.bwd_status(ws, T, Hq) == 0
+
+    # timed region: exactly K steps, bracketed by device synchronisation
+    all_evs = [[ev() for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(all_evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    stages = {nm: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in all_evs])) for j, nm in enumerate(stage_names)}
+    assert fl.bwd_status(ws, T, Hq) == 0
+
+    value = flop / (ms_per_step * 1e-3) / 1e12
+    fwd_flop, bwd_flop = 4.0 * d * Hq * pairs, 10.0 * d * Hq * pairs
+    dom = "bwd" if stages["bwd"] >= stages["fwd"] else "fwd"
+    dom_flop = bwd_flop if dom == "bwd" else fwd_flop
+    achieved = dom_flop / (stages[dom] * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "kernel": "flamia_bwd (prologue + main kernel)" if dom == "bwd" else "flamia_fwd",
+                "achieved": achieved, "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_FP8_TFLOPS,
+                "traffic": None}
+    n_qkv = T * (Hq + 2 * Hkv) * d
+    qkv_bytes = 3 * n_qkv + T * (Hq + 2 * Hkv)
+    do_bytes = 5 * T * Hq * d + 5 * T * Hq
+    quant = {"qkv_GBps": qkv_bytes / (stages["quantize_qkv"] * 1e-3) / 1e9,
+             "do_GBps": do_bytes / (stages["quantize_do"] * 1e-3) / 1e9, "peak_GBps": PEAK_HBM_GBPS}
+    quant["qkv_frac"] = quant["qkv_GBps"] / PEAK_HBM_GBPS
+    quant["do_frac"] = quant["do_GBps"] / PEAK_HBM_GBPS
+
+    res = {
+        "metric": METRIC, "value": value, "unit": "TFLOPS", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "mxfp8_e4m3", "data": "synthetic",
+        "config": {"workload": args.workload, "T": T, "Hq": Hq, "Hkv": Hkv, "d": d, "docs": len(cu) - 1,
+                   "visible_pairs": pairs, "flop_per_step": flop, "causal_dq_scale": bool(args.causal_dq)},
+        "frac_of_peak": value / PEAK_FP8_TFLOPS,
+        "roofline": roofline,
+        "quantize": quant,
+        "stages_ms": stages,
+        "worklist_ms": float(np.median(wl_ms)),
+        "peak_mem_GB": torch.cuda.max_memory_allocated() / 1e9,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_pairs)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,209 @@
+/*
+ * flamia.h — C ABI of libflamia.so: causal, packed-document attention forward and backward
+ * on token-block MXFP8 operands for AMD MI355X (gfx950).
+ *
+ * The method is the MXFP8 path of FLAMIA ("FLAMIA: FLAsh MIcroscaling Attention for Fast and
+ * Causally Safe Training on Blackwell"), as described by the jaehun.me review (cited [J]
+ * below, by section) and the agihunt.info summary ([A]).
+ *
+ * Conventions shared by every entry point
+ *  - All tensor pointers are DEVICE pointers; `stream` is a hipStream_t (NULL = default stream).
+ *    Every call only enqueues work on `stream` and returns; nothing synchronises with the host.
+ *  - The caller allocates and owns every buffer, including work lists and workspaces sized by
+ *    the *_bytes queries.  The library allocates no device memory and keeps no mutable global
+ *    state; buffers must stay alive until the enqueued work has completed.
+ *  - Packed layout: documents are consecutive token ranges of one row of T tokens, described by
+ *    `cu_seqlens` (int32, n_docs + 1 entries, non-decreasing, 0 <= cu_seqlens[0],
+ *    cu_seqlens[n_docs] <= T; a document k is [cu_seqlens[k], cu_seqlens[k+1]); empty documents
+ *    are allowed).  Tokens outside every document are "invalid rows": O = 0, LSE = +inf,
+ *    dQ = dK = dV = 0, codes 0, scale byte 0, D = 0 ([J] §3.4 "Packed documents").
+ *    cu_seqlens that violate these rules give undefined results (never checked on the device,
+ *    which would need a host synchronisation).
+ *  - Heads: Q and dO have Hq heads, K and V have Hkv heads, Hq % Hkv == 0; query head h reads
+ *    KV head h / (Hq / Hkv) (grouped-query attention, [J] §3.4 "Backward pass").
+ *  - Head dimension d is 64 or 128.  BF16 tensors are [T, H, d] with element strides
+ *    (stride_t, stride_h) and d contiguous.  Quantised codes are u8 [T, H, d] contiguous (OCP
+ *    E4M3FN); scale tables are u8 [H, T]: one E8M0 byte (exponent + 127) per token, equal for
+ *    all tokens of a 32-token document block ([J] §3.1, §3.4 "dense scale table").
+ *  - LSE is float32 [Hq, T] in log2 units: LSE_i = log2 sum_j 2^(t_ij) with
+ *    t_ij = softmax_scale * log2(e) * S_ij.
+ *  - Errors: argument checks run synchronously on the host and return a status; a failed
+ *    kernel launch returns FLAMIA_ERR_HIP.  No exception crosses the ABI.
+ */
+#ifndef FLAMIA_H
+#define FLAMIA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FLAMIA_OK = 0,
+  FLAMIA_ERR_NULL = 1,        /* a required pointer is NULL */
+  FLAMIA_ERR_SHAPE = 2,       /* negative or inconsistent sizes, bad strides */
+  FLAMIA_ERR_UNSUPPORTED = 3, /* d not in {64, 128}, Hq % Hkv != 0, T or n_docs beyond limits */
+  FLAMIA_ERR_WORKSPACE = 4,   /* a caller buffer is smaller than its *_bytes query */
+  FLAMIA_ERR_HIP = 5          /* a HIP call or kernel launch failed */
+} flamia_status;
+
+/* Host.  Static string naming a status. */
+const char* flamia_status_str(flamia_status s);
+
+/* Largest T accepted by the work-list builder and the quantiser (tokens per call). */
+#define FLAMIA_MAX_T (1 << 24)
+/* Largest total T accepted by flamia_build_worklist (its single-workgroup sort keeps the
+ * cost histogram and the list of multi-tile documents in LDS). */
+#define FLAMIA_MAX_T_WORKLIST (1 << 20)
+
+/* ------------------------------------------------------------------------------------------
+ * Work lists ([J] §3.4 "Work scheduling"; [A]).
+ *
+ * FLAMIA_LIST_FWD: one item per 256 consecutive queries of a document (block b covers document
+ *   offsets [256b, min(256b+256, L))); cost = number of 128-key tiles it visits,
+ *   ceil(min(256(b+1), L) / 128).
+ * FLAMIA_LIST_BWD: one item per 128-key tile kappa of a document; cost = number of 128-query
+ *   tiles at or after it, ceil((L - 128 kappa) / 128).
+ * Items are enumerated by (document, block) and stably sorted by descending cost; `worker`
+ * tags them in alternating (serpentine) order over n_workers: for list index i, with
+ * r = i / n_workers, worker = i % n_workers if r is even, else n_workers - 1 - i % n_workers.
+ * The list is built on the GPU with no host synchronisation; build it once per micro-batch
+ * and reuse it for every layer.
+ *
+ * Buffer layout: int32 header[4] = {n_items, kind, n_docs, 0}, then n_items flamia_work_item.
+ * ------------------------------------------------------------------------------------------ */
+typedef struct {
+  int32_t doc;    /* document index */
+  int32_t blk;    /* 256-query block (FWD) or 128-key tile (BWD), counted from the document start */
+  int32_t cost;   /* 128-key tiles visited (FWD) or 128-query tiles served (BWD) */
+  int32_t worker; /* serpentine tag over n_workers */
+} flamia_work_item;
+
+typedef enum { FLAMIA_LIST_FWD = 0, FLAMIA_LIST_BWD = 1 } flamia_list_kind;
+
+/* Host.  Bytes needed for a list over n_docs documents of total length T (an upper bound:
+ * 16 + 16 * (ceil(T / 128) + n_docs)). */
+size_t flamia_worklist_bytes(int32_t n_docs, int32_t T, int32_t kind);
+
+/* Enqueue the work-list build.  cu_seqlens: device int32 [n_docs + 1].  list: device buffer of
+ * list_bytes >= flamia_worklist_bytes(n_docs, T, kind).  n_workers >= 1.
+ * Errors: NULL pointers, n_docs < 0, T < 0 or T > FLAMIA_MAX_T_WORKLIST, bad kind,
+ * n_workers < 1, small buffer. */
+flamia_status flamia_build_worklist(const int32_t* cu_seqlens, int32_t n_docs, int32_t T, int32_t kind,
+                                    int32_t n_workers, void* list, size_t list_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * Token-block quantiser ([J] §3.1 MXFP8 path, §3.2 round-up exponents, §3.3 D, §3.4 fusion and
+ * packed documents; [A]).
+ *
+ * For each tensor, document k, 32-token block b counted from the document start (the last
+ * block may be shorter) and head h: amax = max |x| over the block's tokens and all d channels;
+ * s = the smallest integer with amax <= 448 * 2^s (clamped to [-127, 127]; amax = 0 gives
+ * -127); the byte s + 127 is written for every token of the block into scales[h][t]; codes are
+ * the E4M3 round-to-nearest-even of x * 2^-s (never saturating).  Each input byte is read once
+ * per call.  Up to three tensors (e.g. Q, K, V, with their own head counts) share one launch.
+ *
+ * dO pass: with `o` non-NULL, exactly one tensor (dO, H heads) is given, and D[h][t] =
+ * sum_c deq(dO_{t,h,c}) * O_{t,h,c} is also written (float32 [H, T]); deq(x) = code * 2^s, the
+ * same quantised dO that the backward's dP product reads ([J] §3.3).
+ * ------------------------------------------------------------------------------------------ */
+typedef struct {
+  const void* x;              /* bf16 [T, H, d], element strides below, d contiguous */
+  int64_t stride_t, stride_h; /* in elements */
+  int32_t H;                  /* heads of this tensor */
+  uint8_t* codes;             /* out: u8 [T, H, d] contiguous */
+  uint8_t* scales;            /* out: u8 [H, T] */
+} flamia_qtensor;
+
+/* Errors: NULL pointers, n_tensors not in [1, 3] (1 with `o`), H < 1, T < 0 or > FLAMIA_MAX_T,
+ * d not in {64, 128}, n_docs < 0, D NULL when o is given. */
+flamia_status flamia_quantize(const flamia_qtensor* tensors, int32_t n_tensors, int32_t T, int32_t d,
+                              const int32_t* cu_seqlens, int32_t n_docs, const void* o, int64_t o_stride_t,
+                              int64_t o_stride_h, float* D, void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * Forward ([J] §1.2, §3.1, §3.4; [A]).
+ *
+ * For each query row i of document k (offset r) and query head h (KV head g):
+ *   t_ij = softmax_scale * log2(e) * 2^(e(Q_i) + e(K_j)) * sum_c q(Q_ic) q(K_jc)   (j <= i)
+ * 128-key tiles counted from the document start are visited from the diagonal tile down to
+ * tile 0, the running max m updated once per tile; per tile p_j = 2^(t_ij - m),
+ * l = 2^(m_old - m) l + sum p_j, and the P operand is E4M3_RNE(2^8 p_j) with scale 2^-8.
+ * O_i = BF16(acc / l) is written into the packed output; LSE_i = m + log2 l.
+ * Work comes from a FLAMIA_LIST_FWD list built for the same cu_seqlens; (item, head) units are
+ * spread over a persistent grid in list order.  Invalid rows get O = 0 and LSE = +inf.
+ * ------------------------------------------------------------------------------------------ */
+typedef struct {
+  const uint8_t *q, *k, *v;       /* codes: q [T, Hq, d]; k, v [T, Hkv, d] */
+  const uint8_t *sq, *sk, *sv;    /* scale tables: sq [Hq, T]; sk, sv [Hkv, T] */
+  int32_t T, Hq, Hkv, d;
+  float softmax_scale;            /* <= 0 selects 1 / sqrt(d) */
+  const int32_t* cu_seqlens;      /* [n_docs + 1] */
+  int32_t n_docs;
+  const void* fwd_list;           /* FLAMIA_LIST_FWD list for cu_seqlens */
+  void* o;                        /* out: bf16 [T, Hq, d], element strides below */
+  int64_t o_stride_t, o_stride_h;
+  float* lse;                     /* out: float32 [Hq, T], log2 units */
+} flamia_fwd_args;
+
+/* Errors: NULL pointers, sizes, d, head ratio. */
+flamia_status flamia_fwd(const flamia_fwd_args* args, void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * Backward ([J] §1.2, §3.1, §3.2, §3.3, §3.4 "Backward pass"; [A]).
+ *
+ * Recomputes t_ij bit-identically to the forward (same codes, scales, matrix instruction and
+ * score scale), P_ij = 2^(t_ij - LSE_i), dP_ij = deq(dO_i) . deq(V_j), dS_ij = P_ij (dP_ij - D_i).
+ * The P and dS operands of the gradient products are E4M3 with one round-up E8M0 exponent per
+ * 32x32 block (query block x key block, both counted from the document start):
+ *   dV_j = sum_{h in group} sum_i deq(Phat_ij) deq(dO_i)
+ *   dK_j = softmax_scale * sum_{h in group} sum_i deq(dShat_ij) deq(Q_i)
+ *   dQ_i = BF16(softmax_scale * 2^-pi_i * acc16_i), acc16 the FP16 sum, over 128-key tiles in
+ *          ascending order, of FP16(2^pi_i * sum_{j in tile} deq(dShat_ij) deq(K_j)).
+ * The power-of-two prescale pi ([J] §3.2): with C_d = ceil(log2(2 d 448^3)),
+ *   pi_i = clamp(15 - C_d - E_i, -64, 64), E_i = e(dO) + e(V) + e(K) with
+ *   causal_dq_scale = 0: maxima over every token of the call (per query head);
+ *   causal_dq_scale = 1: e(dO_i) of the row's own block and maxima of e(V), e(K) over the row's
+ *                        document up to and including its own block, so no later token
+ *                        changes the rounding of earlier rows.
+ * The FP16 accumulation is done in place in the dq buffer (which must therefore hold d
+ * contiguous elements per (row, head)); the ascending order is enforced by per-(head, query
+ * tile) turn counters, which makes results bit-reproducible.
+ * Work comes from a FLAMIA_LIST_BWD list; each (item, KV head) unit runs all query heads of
+ * its group, so dK and dV are written once.
+ * ------------------------------------------------------------------------------------------ */
+typedef struct {
+  const uint8_t *q, *k, *v, *dO;      /* codes (dO: [T, Hq, d], from the dO quantiser pass) */
+  const uint8_t *sq, *sk, *sv, *sdO;  /* scale tables */
+  const float *lse, *D;               /* forward LSE and the dO pass's D, float32 [Hq, T] */
+  int32_t T, Hq, Hkv, d;
+  float softmax_scale;                /* must equal the forward's (<= 0: 1 / sqrt(d)) */
+  const int32_t* cu_seqlens;
+  int32_t n_docs;
+  const void* bwd_list;               /* FLAMIA_LIST_BWD list for cu_seqlens */
+  void *dq, *dk, *dv;                 /* out: bf16; dq [T, Hq, d], dk, dv [T, Hkv, d] */
+  int64_t dq_stride_t, dq_stride_h, dk_stride_t, dk_stride_h, dv_stride_t, dv_stride_h;
+  void* workspace;                    /* flamia_bwd_workspace_bytes(T, Hq) bytes, any contents */
+  size_t workspace_bytes;
+  int32_t causal_dq_scale;            /* 0: sequence-wide prescale (default); 1: causal */
+  int16_t* dq_exp_out;                /* optional out: pi as int16 [Hq, T] (0 on invalid rows) */
+} flamia_bwd_args;
+
+/* Host.  Workspace bytes for T tokens and Hq query heads (pi table, turn counters, a status
+ * word).  The dQ FP16 accumulator lives in the dq output itself. */
+size_t flamia_bwd_workspace_bytes(int32_t T, int32_t Hq);
+
+/* Errors: NULL pointers, sizes, d, head ratio, small workspace. */
+flamia_status flamia_bwd(const flamia_bwd_args* args, void* stream);
+
+/* Host.  Number of compute units of the current device, the persistent grid used by
+ * flamia_fwd / flamia_bwd (one workgroup per compute unit). */
+int32_t flamia_num_workers(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLAMIA_H */

@@ -125,8 +125,19 @@ def worklist(cu, kind, n_workers):
     return out[:n].copy()
 
 
-def fwd(q, sq, k, sk, v, sv, cu, softmax_scale=None, p_shift=8, exact_p=False, want_o64=False):
-    """Returns (O bits u16 [T,Hq,d], LSE f32 [Hq,T] in log2 units, O64 or None)."""
+def _sel(mask, n):
+    if mask is None:
+        return None
+    m = np.zeros(n, np.uint8)
+    m[np.asarray(mask)] = 1
+    return m
+
+
+def fwd(q, sq, k, sk, v, sv, cu, softmax_scale=None, p_shift=8, exact_p=False, want_o64=False,
+        docs=None, kv_heads=None, want_flip=False):
+    """Returns (O bits u16 [T,Hq,d], LSE f32 [Hq,T] in log2 units, O64 or None), plus the
+    one-flip allowance of O if want_flip.  ``docs`` / ``kv_heads`` (index lists) restrict the
+    work to those documents / KV heads; other rows are zero (O) or NaN (LSE)."""
     q, k, v = _c(q, np.uint8), _c(k, np.uint8), _c(v, np.uint8)
     sq, sk, sv = _c(sq, np.uint8), _c(sk, np.uint8), _c(sv, np.uint8)
     T, Hq, d = q.shape
@@ -134,12 +145,17 @@ def fwd(q, sq, k, sk, v, sv, cu, softmax_scale=None, p_shift=8, exact_p=False, w
     if softmax_scale is None:
         softmax_scale = 1.0 / np.sqrt(d)
     cu = _c(cu, np.int32)
-    o = np.empty((T, Hq, d), np.uint16)
-    lse = np.empty((Hq, T), np.float32)
-    o64 = np.empty((T, Hq, d), np.float64) if want_o64 else None
+    o = np.zeros((T, Hq, d), np.uint16)
+    lse = np.full((Hq, T), np.nan, np.float32)
+    o64 = np.zeros((T, Hq, d), np.float64) if want_o64 else None
+    sd, sk_ = _sel(docs, len(cu) - 1), _sel(kv_heads, Hkv)
+    flip = np.zeros((T, Hq, d), np.float64) if want_flip else None
     lib().orc_fwd(_p(q), _p(sq), _p(k), _p(sk), _p(v), _p(sv), T, Hq, Hkv, d, ctypes.c_double(softmax_scale),
                   _p(cu), len(cu) - 1, int(p_shift), int(bool(exact_p)), _p(o), _p(lse),
-                  _p(o64) if o64 is not None else None)
+                  _p(o64) if o64 is not None else None, _p(sd) if sd is not None else None,
+                  _p(sk_) if sk_ is not None else None, _p(flip) if flip is not None else None)
+    if want_flip:
+        return o, lse, o64, flip
     return o, lse, o64
 
 
@@ -170,7 +186,7 @@ class _Dbg(ctypes.Structure):
 
 
 def bwd(q, sq, k, sk, v, sv, do, sdo, lse, D, cu, softmax_scale=None, causal_dq=False, exact=0,
-        want64=False, debug=False):
+        want64=False, debug=False, docs=None, kv_heads=None, want_flip=False):
     """Returns dict with dq, dk, dv (u16 BF16 bits), pi (i16 [Hq,T]) and optionally the
     double-precision values (dq64, dk64, dv64) and, for single-document calls, the block
     exponents/codes of the P and dS operands (p_scale, ds_scale [Hq,nb,nb]; p_code,
@@ -187,6 +203,9 @@ def bwd(q, sq, k, sk, v, sv, do, sdo, lse, D, cu, softmax_scale=None, causal_dq=
                dv=np.empty((T, Hkv, d), np.uint16), pi=np.empty((Hq, T), np.int16))
     if want64:
         out.update(dq64=np.empty((T, Hq, d)), dk64=np.empty((T, Hkv, d)), dv64=np.empty((T, Hkv, d)))
+    if want_flip:
+        out.update(dq_flip=np.empty((T, Hq, d)), dk_flip=np.empty((T, Hkv, d)), dv_flip=np.empty((T, Hkv, d)))
+    sd, sk_ = _sel(docs, len(cu) - 1), _sel(kv_heads, Hkv)
     dbg = None
     if debug:
         assert len(cu) == 2 and cu[0] == 0
@@ -200,5 +219,31 @@ def bwd(q, sq, k, sk, v, sv, do, sdo, lse, D, cu, softmax_scale=None, causal_dq=
                   T, Hq, Hkv, d, ctypes.c_double(softmax_scale), _p(cu), len(cu) - 1, int(bool(causal_dq)),
                   int(exact), _p(out["dq"]), _p(out["dk"]), _p(out["dv"]), _p(out["pi"]),
                   _p(out["dq64"]) if want64 else None, _p(out["dk64"]) if want64 else None,
-                  _p(out["dv64"]) if want64 else None, ctypes.byref(dbg) if dbg is not None else None)
+                  _p(out["dv64"]) if want64 else None, ctypes.byref(dbg) if dbg is not None else None,
+                  _p(sd) if sd is not None else None, _p(sk_) if sk_ is not None else None,
+                  *((_p(out["dq_flip"]), _p(out["dk_flip"]), _p(out["dv_flip"])) if want_flip else (None, None, None)))
+    return out
+
+
+def allowance(q, sq, k, sk, v, sv, do, sdo, lse, D, o64, o_flip, pi, cu, softmax_scale=None, docs=None,
+              kv_heads=None, shared_stats=True):
+    """First-order bound, per output element, of the effect of the FP8 matrix instruction's
+    accumulation precision (test tolerance derivation, not the method).  Returns dict with
+    lse_a [Hq,T], o_a, dq_a [T,Hq,d], dk_a, dv_a [T,Hkv,d]."""
+    q, k, v, do = (_c(a, np.uint8) for a in (q, k, v, do))
+    sq, sk, sv, sdo = (_c(a, np.uint8) for a in (sq, sk, sv, sdo))
+    lse, D = _c(lse, np.float32), _c(D, np.float32)
+    o64, o_flip, pi = _c(o64, np.float64), _c(o_flip, np.float64), _c(pi, np.int16)
+    T, Hq, d = q.shape
+    Hkv = k.shape[1]
+    if softmax_scale is None:
+        softmax_scale = 1.0 / np.sqrt(d)
+    cu = _c(cu, np.int32)
+    out = dict(lse_a=np.empty((Hq, T)), o_a=np.empty((T, Hq, d)), dq_a=np.empty((T, Hq, d)),
+               dk_a=np.empty((T, Hkv, d)), dv_a=np.empty((T, Hkv, d)))
+    sd, sk_ = _sel(docs, len(cu) - 1), _sel(kv_heads, Hkv)
+    lib().orc_allowance(_p(q), _p(sq), _p(k), _p(sk), _p(v), _p(sv), _p(do), _p(sdo), _p(lse), _p(D), _p(o64),
+                        _p(o_flip), T, Hq, Hkv, d, ctypes.c_double(softmax_scale), _p(cu), len(cu) - 1, _p(pi),
+                        _p(sd) if sd is not None else None, _p(sk_) if sk_ is not None else None,
+                        int(bool(shared_stats)), _p(out["lse_a"]), _p(out["o_a"]), _p(out["dq_a"]), _p(out["dk_a"]), _p(out["dv_a"]))
     return out

@@ -1,0 +1,250 @@
+"""Token-block MXFP8 causal packed-document attention for AMD MI355X (gfx950).
+
+Python binding of ``libflamia.so`` (C ABI in ``include/flamia.h``).  This module only
+marshals arguments: it allocates outputs with torch on the current device, passes raw device
+pointers and the current HIP stream, and raises on a non-OK status.  Every step of the path
+(quantisation, work lists, forward, backward) runs in the library's HIP kernels; there is no
+fallback, and importing this module without a built library fails loudly.
+"""
+import ctypes
+import os
+
+import torch
+
+from . import workloads  # noqa: F401  (seeded synthetic inputs)
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libflamia.so")
+
+FLAMIA_LIST_FWD = 0
+FLAMIA_LIST_BWD = 1
+
+EXPORTED_SYMBOLS = (
+    "flamia_status_str", "flamia_worklist_bytes", "flamia_build_worklist", "flamia_quantize",
+    "flamia_fwd", "flamia_bwd", "flamia_bwd_workspace_bytes", "flamia_num_workers",
+)
+
+
+class _QTensor(ctypes.Structure):
+    _fields_ = [("x", ctypes.c_void_p), ("stride_t", ctypes.c_int64), ("stride_h", ctypes.c_int64),
+                ("H", ctypes.c_int32), ("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p)]
+
+
+class _FwdArgs(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("sq", ctypes.c_void_p), ("sk", ctypes.c_void_p), ("sv", ctypes.c_void_p),
+                ("T", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32), ("d", ctypes.c_int32),
+                ("softmax_scale", ctypes.c_float), ("cu_seqlens", ctypes.c_void_p), ("n_docs", ctypes.c_int32),
+                ("fwd_list", ctypes.c_void_p), ("o", ctypes.c_void_p), ("o_stride_t", ctypes.c_int64),
+                ("o_stride_h", ctypes.c_int64), ("lse", ctypes.c_void_p)]
+
+
+class _BwdArgs(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("dO", ctypes.c_void_p),
+                ("sq", ctypes.c_void_p), ("sk", ctypes.c_void_p), ("sv", ctypes.c_void_p), ("sdO", ctypes.c_void_p),
+                ("lse", ctypes.c_void_p), ("D", ctypes.c_void_p),
+                ("T", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32), ("d", ctypes.c_int32),
+                ("softmax_scale", ctypes.c_float), ("cu_seqlens", ctypes.c_void_p), ("n_docs", ctypes.c_int32),
+                ("bwd_list", ctypes.c_void_p), ("dq", ctypes.c_void_p), ("dk", ctypes.c_void_p), ("dv", ctypes.c_void_p),
+                ("dq_stride_t", ctypes.c_int64), ("dq_stride_h", ctypes.c_int64),
+                ("dk_stride_t", ctypes.c_int64), ("dk_stride_h", ctypes.c_int64),
+                ("dv_stride_t", ctypes.c_int64), ("dv_stride_h", ctypes.c_int64),
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+                ("causal_dq_scale", ctypes.c_int32), ("dq_exp_out", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def load_library(path=LIB_PATH):
+    """Load libflamia.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError("libflamia.so is not built (%s); run `python -m "
+                           "precision_causal_attention_token_amd.build`" % path)
+    lib = ctypes.CDLL(path)
+    lib.flamia_status_str.restype = ctypes.c_char_p
+    lib.flamia_status_str.argtypes = [ctypes.c_int]
+    lib.flamia_worklist_bytes.restype = ctypes.c_size_t
+    lib.flamia_worklist_bytes.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
+    lib.flamia_build_worklist.restype = ctypes.c_int
+    lib.flamia_build_worklist.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                          ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    lib.flamia_quantize.restype = ctypes.c_int
+    lib.flamia_quantize.argtypes = [ctypes.POINTER(_QTensor), ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                    ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int64,
+                                    ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+    lib.flamia_fwd.restype = ctypes.c_int
+    lib.flamia_fwd.argtypes = [ctypes.POINTER(_FwdArgs), ctypes.c_void_p]
+    lib.flamia_bwd.restype = ctypes.c_int
+    lib.flamia_bwd.argtypes = [ctypes.POINTER(_BwdArgs), ctypes.c_void_p]
+    lib.flamia_bwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.flamia_bwd_workspace_bytes.argtypes = [ctypes.c_int32, ctypes.c_int32]
+    lib.flamia_num_workers.restype = ctypes.c_int32
+    lib.flamia_num_workers.argtypes = []
+    _lib = lib
+    return lib
+
+
+class FlamiaError(RuntimeError):
+    pass
+
+
+def _check(status):
+    if status != 0:
+        raise FlamiaError("libflamia: %s (status %d)" % (load_library().flamia_status_str(status).decode(), status))
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _check_bf16(x, name):
+    if not x.is_cuda or x.dtype != torch.bfloat16 or x.dim() != 3 or x.stride(2) != 1:
+        raise ValueError("%s must be a CUDA bf16 tensor [T, H, d] with a contiguous last dim" % name)
+
+
+def _check_cu(cu):
+    if not cu.is_cuda or cu.dtype != torch.int32 or cu.dim() != 1 or not cu.is_contiguous():
+        raise ValueError("cu_seqlens must be a contiguous CUDA int32 vector")
+    return cu.numel() - 1
+
+
+def num_workers():
+    return int(load_library().flamia_num_workers())
+
+
+# ----------------------------------------------------------------------------------------
+def build_worklist(cu_seqlens, T, kind, n_workers=None):
+    """Sorted work list (int32 buffer: header {n_items, kind, n_docs, 0} + 4 ints per item)."""
+    lib = load_library()
+    n_docs = _check_cu(cu_seqlens)
+    nbytes = lib.flamia_worklist_bytes(n_docs, int(T), int(kind))
+    buf = torch.empty((nbytes + 3) // 4, dtype=torch.int32, device=cu_seqlens.device)
+    if n_workers is None:
+        n_workers = num_workers()
+    _check(lib.flamia_build_worklist(_ptr(cu_seqlens), n_docs, int(T), int(kind), int(n_workers), _ptr(buf),
+                                     buf.numel() * 4, _stream()))
+    return buf
+
+
+def worklist_items(buf):
+    """Host view of a list buffer: (n_items, int32 tensor [n_items, 4]) (synchronises)."""
+    n = int(buf[0].item())
+    return n, buf[4:4 + 4 * n].view(n, 4)
+
+
+def quantize(xs, cu_seqlens):
+    """Token-block MXFP8 quantisation of up to three BF16 tensors [T, H, d] in one launch.
+    Returns a list of (codes u8 [T, H, d], scales u8 [H, T])."""
+    lib = load_library()
+    n_docs = _check_cu(cu_seqlens)
+    T, _, d = xs[0].shape
+    arr = (_QTensor * len(xs))()
+    outs = []
+    for i, x in enumerate(xs):
+        _check_bf16(x, "x")
+        if x.shape[0] != T or x.shape[2] != d:
+            raise ValueError("tensors must share T and d")
+        H = x.shape[1]
+        codes = torch.empty((T, H, d), dtype=torch.uint8, device=x.device)
+        scales = torch.empty((H, T), dtype=torch.uint8, device=x.device)
+        arr[i] = _QTensor(x.data_ptr(), x.stride(0), x.stride(1), H, codes.data_ptr(), scales.data_ptr())
+        outs.append((codes, scales))
+    _check(lib.flamia_quantize(arr, len(xs), T, d, _ptr(cu_seqlens), n_docs, None, 0, 0, None, _stream()))
+    return outs
+
+
+def quantize_do(do, o, cu_seqlens):
+    """dO quantisation plus D = deq(dO) . O.  Returns (codes, scales, D f32 [H, T])."""
+    lib = load_library()
+    n_docs = _check_cu(cu_seqlens)
+    _check_bf16(do, "do")
+    _check_bf16(o, "o")
+    T, H, d = do.shape
+    codes = torch.empty((T, H, d), dtype=torch.uint8, device=do.device)
+    scales = torch.empty((H, T), dtype=torch.uint8, device=do.device)
+    D = torch.empty((H, T), dtype=torch.float32, device=do.device)
+    arr = (_QTensor * 1)()
+    arr[0] = _QTensor(do.data_ptr(), do.stride(0), do.stride(1), H, codes.data_ptr(), scales.data_ptr())
+    _check(lib.flamia_quantize(arr, 1, T, d, _ptr(cu_seqlens), n_docs, _ptr(o), o.stride(0), o.stride(1),
+                               _ptr(D), _stream()))
+    return codes, scales, D
+
+
+def fwd(q, k, v, cu_seqlens, fwd_list, softmax_scale=None, out=None):
+    """Forward on quantised operands.  q, k, v are (codes, scales) pairs.
+    Returns (O bf16 [T, Hq, d], LSE f32 [Hq, T] in log2 units)."""
+    lib = load_library()
+    n_docs = _check_cu(cu_seqlens)
+    (qc, qs), (kc, ks), (vc, vs) = q, k, v
+    T, Hq, d = qc.shape
+    Hkv = kc.shape[1]
+    o = out if out is not None else torch.empty((T, Hq, d), dtype=torch.bfloat16, device=qc.device)
+    lse = torch.empty((Hq, T), dtype=torch.float32, device=qc.device)
+    a = _FwdArgs(qc.data_ptr(), kc.data_ptr(), vc.data_ptr(), qs.data_ptr(), ks.data_ptr(), vs.data_ptr(),
+                 T, Hq, Hkv, d, float(softmax_scale or 0.0), cu_seqlens.data_ptr(), n_docs, fwd_list.data_ptr(),
+                 o.data_ptr(), o.stride(0), o.stride(1), lse.data_ptr())
+    _check(lib.flamia_fwd(ctypes.byref(a), _stream()))
+    return o, lse
+
+
+def bwd(q, k, v, do, lse, D, cu_seqlens, bwd_list, softmax_scale=None, causal_dq_scale=False, want_pi=False,
+        workspace=None):
+    """Backward on quantised operands.  q, k, v, do are (codes, scales) pairs; lse, D f32 [Hq, T].
+    Returns (dq, dk, dv) BF16, plus the prescale exponents pi int16 [Hq, T] if want_pi."""
+    lib = load_library()
+    n_docs = _check_cu(cu_seqlens)
+    (qc, qs), (kc, ks), (vc, vs), (dc, dsc) = q, k, v, do
+    T, Hq, d = qc.shape
+    Hkv = kc.shape[1]
+    dev = qc.device
+    dq = torch.empty((T, Hq, d), dtype=torch.bfloat16, device=dev)
+    dk = torch.empty((T, Hkv, d), dtype=torch.bfloat16, device=dev)
+    dv = torch.empty((T, Hkv, d), dtype=torch.bfloat16, device=dev)
+    nbytes = lib.flamia_bwd_workspace_bytes(T, Hq)
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    pi = torch.empty((Hq, T), dtype=torch.int16, device=dev) if want_pi else None
+    a = _BwdArgs(qc.data_ptr(), kc.data_ptr(), vc.data_ptr(), dc.data_ptr(),
+                 qs.data_ptr(), ks.data_ptr(), vs.data_ptr(), dsc.data_ptr(), lse.data_ptr(), D.data_ptr(),
+                 T, Hq, Hkv, d, float(softmax_scale or 0.0), cu_seqlens.data_ptr(), n_docs, bwd_list.data_ptr(),
+                 dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), dq.stride(0), dq.stride(1), dk.stride(0), dk.stride(1),
+                 dv.stride(0), dv.stride(1), workspace.data_ptr(), workspace.numel(), int(bool(causal_dq_scale)),
+                 pi.data_ptr() if pi is not None else None)
+    _check(lib.flamia_bwd(ctypes.byref(a), _stream()))
+    return (dq, dk, dv, pi) if want_pi else (dq, dk, dv)
+
+
+def bwd_status(workspace, T, Hq):
+    """Status word of the last backward that used `workspace` (0 = ok; bit 0 = a turn wait gave up)."""
+    pi_bytes = (T * Hq * 2 + 255) // 256 * 256
+    cnt_bytes = (T * Hq * 4 + 255) // 256 * 256
+    return int(workspace[pi_bytes + cnt_bytes:pi_bytes + cnt_bytes + 4].view(torch.int32).item())
+
+
+class Lists:
+    """Forward and backward work lists of one micro-batch (built once, reused by every layer)."""
+
+    def __init__(self, cu_seqlens, T):
+        self.fwd = build_worklist(cu_seqlens, T, FLAMIA_LIST_FWD)
+        self.bwd = build_worklist(cu_seqlens, T, FLAMIA_LIST_BWD)
+
+
+def training_call(q, k, v, do, cu_seqlens, lists=None, softmax_scale=None, causal_dq_scale=False):
+    """One attention training call: quantise Q, K, V -> forward -> quantise dO (+ D) -> backward.
+    Returns dict with o, lse, dq, dk, dv."""
+    T = q.shape[0]
+    if lists is None:
+        lists = Lists(cu_seqlens, T)
+    qz, kz, vz = quantize([q, k, v], cu_seqlens)
+    o, lse = fwd(qz, kz, vz, cu_seqlens, lists.fwd, softmax_scale)
+    dc, dsc, D = quantize_do(do, o, cu_seqlens)
+    dq, dk, dv = bwd(qz, kz, vz, (dc, dsc), lse, D, cu_seqlens, lists.bwd, softmax_scale, causal_dq_scale)
+    return dict(o=o, lse=lse, dq=dq, dk=dk, dv=dv)

@@ -1,0 +1,466 @@
+// Backward: causal packed-document attention on token-block MXFP8 operands
+// (jaehun.me review §1.2 gradient products, §3.1 operand formats, §3.2 dQ prescale,
+//  §3.3 recomputation with the same quantised operands and block-scaled dS, §3.4 backward pass,
+//  packed documents and work scheduling).
+//
+// Prologue (one workgroup per query head): the dQ prescale exponent pi of every row, zeroed
+// turn counters, zero gradients on rows outside every document.
+//
+// Main kernel: persistent grid, one 256-thread workgroup per compute unit.  A work unit is
+// (backward item = 128-key tile of a document, KV head).  Wave w owns keys 32w..32w+31; K^T and
+// V for those keys stay in registers as MFMA operands, dK^T and dV^T accumulate in registers
+// over all query heads of the group and all 64-query steps from the diagonal to the document
+// end.  Per step:
+//   S  (queries x keys) = Q K^T  and  dP = dO V^T          (A from the row-major Q / dO tiles)
+//     -> the score t is bit-identical to the forward's: same codes, scales, instruction and
+//        K ordering (the instruction gives identical results with its operands swapped);
+//   P = 2^(t - LSE), dS = P (dP - D); each wave's 32x32 blocks of P and dS get a round-up E8M0
+//     exponent from a wave-wide amax and E4M3 codes, already in operand order;
+//   dV^T += dO^T Phat,  dK^T += Q^T dShat                   (A via transpose reads of the tiles)
+//   dQ^T  = K^T dShat^T over the 128 keys                   (dShat staged in LDS [key][query])
+//   dQ partial -> FP16 (x 2^pi), added in place in the dq buffer in ascending key-tile order,
+//     enforced by a per-(head, query tile) turn counter; the diagonal tile's unit is the last
+//     contributor and writes the BF16 result.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace flamia {
+
+namespace {
+
+constexpr int BWD_THREADS = 256;
+constexpr int QT = 64;  // queries per step
+constexpr int SPIN_LIMIT = 1 << 20;  // polls (~0.1 s) before a turn wait gives up and flags an error
+
+template <int D>
+struct BwdSmem {
+  uint8_t k[KV_TILE * D];
+  uint8_t q[QT * D];
+  uint8_t dO[QT * D];
+  uint8_t ds[KV_TILE * QT];
+  uint8_t sk[KV_TILE];
+  float lse[QT];
+  float dd[QT];
+  int pi[QT];
+  int sq[2], sdo[2];
+  int ds_scale[2][4];
+};
+
+__device__ __forceinline__ uint32_t pack_half2(_Float16 a, _Float16 b) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+__device__ __forceinline__ _Float16 half_lo(uint32_t w) { return __builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFF)); }
+__device__ __forceinline__ _Float16 half_hi(uint32_t w) { return __builtin_bit_cast(_Float16, (uint16_t)(w >> 16)); }
+
+template <int D>
+__global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
+  constexpr int NC = D / 64;
+  constexpr int NDB = D / 32;
+  __shared__ BwdSmem<D> sm;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 31, hh = lane >> 5;
+  const int n_items = p.list[0];
+  const int4* items = reinterpret_cast<const int4*>(p.list + 4);
+  const int n_units = n_items * p.Hkv;
+  const int G = gridDim.x, wg = blockIdx.x;
+  const int grp = p.Hq / p.Hkv;
+  const float c = p.c;
+  const int T = p.T;
+
+  for (int round = 0;; ++round) {
+    const int u = round * G + ((round & 1) ? (G - 1 - wg) : wg);
+    if (u >= n_units) break;
+    const int4 it = items[u / p.Hkv];
+    const int g = u % p.Hkv;
+    const int doc = it.x, kappa = it.y;
+    const int doc_start = p.cu[doc];
+    const int L = p.cu[doc + 1] - doc_start;
+    const int key_rel = KV_TILE * kappa + 32 * wave + n;
+    const bool key_valid = key_rel < L;
+
+    // ---- K tile into LDS, stationary K / V operands into registers
+    __syncthreads();  // the previous unit no longer reads LDS
+    {
+      constexpr int CPR = D / 16;
+      for (int chunk = tid; chunk < KV_TILE * CPR; chunk += BWD_THREADS) {
+        const int row = chunk / CPR, col = (chunk % CPR) * 16;
+        const int key = KV_TILE * kappa + row;
+        uint4 v4 = make_uint4(0, 0, 0, 0);
+        if (key < L) v4 = *reinterpret_cast<const uint4*>(p.k + ((int64_t)(doc_start + key) * p.Hkv + g) * D + col);
+        *reinterpret_cast<uint4*>(&sm.k[lds_off<D>(row, col)]) = v4;
+      }
+      if (tid < KV_TILE) {
+        const int key = KV_TILE * kappa + tid;
+        sm.sk[tid] = key < L ? p.sk[(int64_t)g * T + doc_start + key] : (uint8_t)127;
+      }
+    }
+    __syncthreads();
+    v8i kop[NC], vop[NC];
+    const int k_scale = sm.sk[32 * wave + n];
+    int v_scale = 127;
+    {
+      const int64_t ka = (int64_t)(doc_start + key_rel);
+#pragma unroll
+      for (int cc = 0; cc < NC; ++cc) {
+        kop[cc] = lds_read_row32<D>(sm.k, 32 * wave + n, 64 * cc + 32 * hh);
+        if (key_valid) {
+          const uint4* src = reinterpret_cast<const uint4*>(p.v + (ka * p.Hkv + g) * D + 64 * cc + 32 * hh);
+          const uint4 a = src[0], b = src[1];
+          vop[cc][0] = a.x; vop[cc][1] = a.y; vop[cc][2] = a.z; vop[cc][3] = a.w;
+          vop[cc][4] = b.x; vop[cc][5] = b.y; vop[cc][6] = b.z; vop[cc][7] = b.w;
+        } else {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) vop[cc][i] = 0;
+        }
+      }
+      if (key_valid) v_scale = p.sv[(int64_t)g * T + doc_start + key_rel];
+    }
+
+    v16f dkacc[NDB], dvacc[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) { dkacc[db] = v16f{}; dvacc[db] = v16f{}; }
+
+    for (int hi = 0; hi < grp; ++hi) {
+      const int h = g * grp + hi;
+      for (int qt = 2 * kappa; QT * qt < L; ++qt) {
+        const int q0 = QT * qt;
+        __syncthreads();  // previous step's LDS readers are done
+        // ---- stage Q, dO tiles and per-row statistics
+        {
+          constexpr int CPR = D / 16;
+          for (int chunk = tid; chunk < QT * CPR; chunk += BWD_THREADS) {
+            const int row = chunk / CPR, col = (chunk % CPR) * 16;
+            const int qr = q0 + row;
+            uint4 a = make_uint4(0, 0, 0, 0), b = make_uint4(0, 0, 0, 0);
+            if (qr < L) {
+              const int64_t off = ((int64_t)(doc_start + qr) * p.Hq + h) * D + col;
+              a = *reinterpret_cast<const uint4*>(p.q + off);
+              b = *reinterpret_cast<const uint4*>(p.dO + off);
+            }
+            *reinterpret_cast<uint4*>(&sm.q[lds_off<D>(row, col)]) = a;
+            *reinterpret_cast<uint4*>(&sm.dO[lds_off<D>(row, col)]) = b;
+          }
+          if (tid < QT) {
+            const int qr = q0 + tid;
+            const bool ok = qr < L;
+            const int64_t ti = (int64_t)h * T + doc_start + qr;
+            sm.lse[tid] = ok ? p.lse[ti] : 0.f;
+            sm.dd[tid] = ok ? p.Dv[ti] : 0.f;
+            sm.pi[tid] = ok ? (int)p.pi[ti] : 0;
+          } else if (tid < QT + 2) {
+            const int qb = tid - QT, qr = q0 + 32 * qb;
+            const int64_t ti = (int64_t)h * T + doc_start + qr;
+            sm.sq[qb] = qr < L ? p.sq[ti] : 127;
+            sm.sdo[qb] = qr < L ? p.sdo[ti] : 127;
+          }
+        }
+        __syncthreads();
+
+        // ---- S and dP for this wave's 32 keys x 64 queries
+        v16f sacc[2], pacc[2];
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          sacc[qb] = v16f{};
+          pacc[qb] = v16f{};
+#pragma unroll
+          for (int cc = 0; cc < NC; ++cc) {
+            const v8i aq = lds_read_row32<D>(sm.q, 32 * qb + n, 64 * cc + 32 * hh);
+            sacc[qb] = mfma_scaled(aq, kop[cc], sacc[qb], sm.sq[qb], k_scale);
+            const v8i ad = lds_read_row32<D>(sm.dO, 32 * qb + n, 64 * cc + 32 * hh);
+            pacc[qb] = mfma_scaled(ad, vop[cc], pacc[qb], sm.sdo[qb], v_scale);
+          }
+        }
+        // ---- P, dS, block exponents, E4M3 operands
+        int pp[8], pd[8];
+        int sp[2], sds[2];
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          float pmax = 0.f, dmax = 0.f;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int qr = q0 + 32 * qb + acc_row(i, hh);
+            const bool vis = key_rel <= qr && qr < L;
+            const int qi = 32 * qb + acc_row(i, hh);
+            const float pv = vis ? __builtin_amdgcn_exp2f(fmaf(sacc[qb][i], c, -sm.lse[qi])) : 0.f;
+            const float dsv = pv * (pacc[qb][i] - sm.dd[qi]);
+            sacc[qb][i] = pv;
+            pacc[qb][i] = dsv;
+            pmax = fmaxf(pmax, pv);
+            dmax = fmaxf(dmax, fabsf(dsv));
+          }
+          sp[qb] = e8m0_roundup(wave_max(pmax));
+          sds[qb] = e8m0_roundup(wave_max(dmax));
+          const float fp = exp2i_neg(sp[qb]), fd = exp2i_neg(sds[qb]);
+#pragma unroll
+          for (int w4 = 0; w4 < 4; ++w4) {
+            pp[4 * qb + w4] = pack4_fp8(sacc[qb][4 * w4] * fp, sacc[qb][4 * w4 + 1] * fp, sacc[qb][4 * w4 + 2] * fp,
+                                        sacc[qb][4 * w4 + 3] * fp);
+            pd[4 * qb + w4] = pack4_fp8(pacc[qb][4 * w4] * fd, pacc[qb][4 * w4 + 1] * fd, pacc[qb][4 * w4 + 2] * fd,
+                                        pacc[qb][4 * w4 + 3] * fd);
+            // dS codes to LDS as [key][query]: 4 consecutive queries per dword
+            const int qcol = 32 * qb + 8 * w4 + 4 * hh;
+            *reinterpret_cast<int*>(&sm.ds[lds_off<QT>(32 * wave + n, qcol)]) = pd[4 * qb + w4];
+          }
+          if (lane == 0) sm.ds_scale[qb][wave] = sds[qb] + 127;
+        }
+        // ---- dV^T += dO^T Phat, dK^T += Q^T dShat
+        {
+          v8i bp, bd;
+#pragma unroll
+          for (int w = 0; w < 8; ++w) { bp[w] = pp[w]; bd[w] = pd[w]; }
+          const int sdo_h = sm.sdo[hh], sq_h = sm.sq[hh];
+          const int sp_h = (hh ? sp[1] : sp[0]) + 127, sds_h = (hh ? sds[1] : sds[0]) + 127;
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) {
+            const v8i ado = lds_read_tr32<D>(sm.dO, 0, 32 * db, lane);
+            dvacc[db] = mfma_scaled(ado, bp, dvacc[db], sdo_h, sp_h);
+            const v8i aq = lds_read_tr32<D>(sm.q, 0, 32 * db, lane);
+            dkacc[db] = mfma_scaled(aq, bd, dkacc[db], sq_h, sds_h);
+          }
+        }
+        __syncthreads();  // dShat tile and its exponents are complete
+
+        // ---- dQ^T = K^T dShat^T for this wave's slice
+        constexpr int NQB = (D == 128) ? 2 : 1;
+        const int dblk = (D == 128) ? wave : (wave & 1);
+        const int qb0 = (D == 128) ? 0 : (wave >> 1);
+        v16f dq[NQB];
+#pragma unroll
+        for (int x = 0; x < NQB; ++x) {
+          const int qb = qb0 + x;
+          dq[x] = v16f{};
+#pragma unroll
+          for (int ci = 0; ci < 2; ++ci) {
+            const v8i ak = lds_read_tr32<D>(sm.k, 64 * ci, 32 * dblk, lane);
+            const v8i bs = lds_read_tr32<QT>(sm.ds, 64 * ci, 32 * qb, lane);
+            dq[x] = mfma_scaled(ak, bs, dq[x], sm.sk[64 * ci + 32 * hh], sm.ds_scale[qb][2 * ci + hh]);
+          }
+        }
+
+        // ---- ordered FP16 accumulation of the partial sums (ascending key tiles)
+        int32_t* cnt = p.counters + (int64_t)h * T + doc_start + q0;
+        if (tid == 0 && kappa > 0) {
+          int spins = 0;
+          while (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != kappa) {
+            __builtin_amdgcn_s_sleep(4);
+            // give up after the limit, or at once if another wait already gave up
+            if (++spins > SPIN_LIMIT || __hip_atomic_load(p.status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
+              atomicOr(p.status, 1);
+              break;
+            }
+          }
+        }
+        if (tid == 0) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        __syncthreads();
+        const bool last = (kappa == qt / 2);
+#pragma unroll
+        for (int x = 0; x < NQB; ++x) {
+          const int qb = qb0 + x;
+          const int qi = 32 * qb + n;
+          const int qr = q0 + qi;
+          if (qr < L) {
+            const int pi = sm.pi[qi];
+            const float up = exp2i(pi), down = exp2i(-pi) * p.softmax_scale;
+            uint16_t* row = p.dq + (int64_t)(doc_start + qr) * p.dqst + (int64_t)h * p.dqsh;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const int d0 = 32 * dblk + 8 * j + 4 * hh;
+              uint64_t* ptr = reinterpret_cast<uint64_t*>(row + d0);
+              _Float16 a0 = (_Float16)(dq[x][4 * j + 0] * up), a1 = (_Float16)(dq[x][4 * j + 1] * up);
+              _Float16 a2 = (_Float16)(dq[x][4 * j + 2] * up), a3 = (_Float16)(dq[x][4 * j + 3] * up);
+              if (kappa > 0) {
+                const uint64_t old = __hip_atomic_load(ptr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                const uint32_t lo = (uint32_t)old, hi = (uint32_t)(old >> 32);
+                a0 = half_lo(lo) + a0;
+                a1 = half_hi(lo) + a1;
+                a2 = half_lo(hi) + a2;
+                a3 = half_hi(hi) + a3;
+              }
+              if (last) {
+                uint2 w;
+                w.x = pack_bf16((float)a0 * down, (float)a1 * down);
+                w.y = pack_bf16((float)a2 * down, (float)a3 * down);
+                *reinterpret_cast<uint2*>(ptr) = w;
+              } else {
+                const uint64_t nw = (uint64_t)pack_half2(a0, a1) | ((uint64_t)pack_half2(a2, a3) << 32);
+                __hip_atomic_store(ptr, nw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              }
+            }
+          }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        __syncthreads();
+        if (tid == 0 && !last) __hip_atomic_store(cnt, kappa + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+
+    // ---- dK, dV of this wave's keys
+    if (key_valid) {
+      uint16_t* krow = p.dk + (int64_t)(doc_start + key_rel) * p.dkst + (int64_t)g * p.dksh;
+      uint16_t* vrow = p.dv + (int64_t)(doc_start + key_rel) * p.dvst + (int64_t)g * p.dvsh;
+      const float ss = p.softmax_scale;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int d0 = 32 * db + 8 * j + 4 * hh;
+          uint2 wk, wv;
+          wk.x = pack_bf16(dkacc[db][4 * j] * ss, dkacc[db][4 * j + 1] * ss);
+          wk.y = pack_bf16(dkacc[db][4 * j + 2] * ss, dkacc[db][4 * j + 3] * ss);
+          wv.x = pack_bf16(dvacc[db][4 * j], dvacc[db][4 * j + 1]);
+          wv.y = pack_bf16(dvacc[db][4 * j + 2], dvacc[db][4 * j + 3]);
+          *reinterpret_cast<uint2*>(krow + d0) = wk;
+          *reinterpret_cast<uint2*>(vrow + d0) = wv;
+        }
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// Prologue: pi per (head, row), zeroed turn counters, zero rows outside every document.
+constexpr int PRO_THREADS = 1024;
+constexpr int PRO_CHUNK = 4 * PRO_THREADS;
+
+struct Seg {  // segmented running maximum: f = a segment starts inside, v/k = running maxima
+  int f, v, k;
+};
+__device__ __forceinline__ Seg seg_op(Seg a, Seg b) {
+  return Seg{a.f | b.f, b.f ? b.v : max(a.v, b.v), b.f ? b.k : max(a.k, b.k)};
+}
+
+template <int D>
+__global__ __launch_bounds__(PRO_THREADS) void bwd_prologue(BwdParams p) {
+  __shared__ uint8_t flags[PRO_CHUNK];
+  __shared__ int wv[PRO_THREADS / 64][3];
+  __shared__ int red[3][PRO_THREADS / 64];
+  __shared__ int kstart;
+  __shared__ Seg carry_sh;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = blockIdx.x, grp = p.Hq / p.Hkv, g = h / grp;
+  const int T = p.T;
+  const int C = (D == 128) ? 35 : 34;  // smallest C with 2 d 448^3 <= 2^C
+  const int c_lo = p.n_docs > 0 ? p.cu[0] : T;
+  const int c_hi = p.n_docs > 0 ? p.cu[p.n_docs] : T;
+  const uint8_t* sdo = p.sdo + (int64_t)h * T;
+  const uint8_t* sv = p.sv + (int64_t)g * T;
+  const uint8_t* sk = p.sk + (int64_t)g * T;
+  int16_t* pi = p.pi + (int64_t)h * T;
+
+  // zero rows outside every document, zero the turn counters and the status word
+  if (h == 0 && tid == 0) *p.status = 0;
+  for (int t = tid; t < T; t += PRO_THREADS) p.counters[(int64_t)h * T + t] = 0;
+  {
+    const int n_out = c_lo + (T - c_hi);
+    for (int x = tid; x < n_out * D; x += PRO_THREADS) {
+      const int r = x / D, dd = x % D;
+      const int t = r < c_lo ? r : c_hi + (r - c_lo);
+      p.dq[(int64_t)t * p.dqst + (int64_t)h * p.dqsh + dd] = 0;
+      if (h % grp == 0) {
+        p.dk[(int64_t)t * p.dkst + (int64_t)g * p.dksh + dd] = 0;
+        p.dv[(int64_t)t * p.dvst + (int64_t)g * p.dvsh + dd] = 0;
+      }
+    }
+  }
+
+  if (!p.causal) {
+    int mdo = 0, mv = 0, mk = 0;
+    for (int t = c_lo + tid; t < c_hi; t += PRO_THREADS) {
+      mdo = max(mdo, (int)sdo[t]);
+      mv = max(mv, (int)sv[t]);
+      mk = max(mk, (int)sk[t]);
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      mdo = max(mdo, __shfl_xor(mdo, off, 64));
+      mv = max(mv, __shfl_xor(mv, off, 64));
+      mk = max(mk, __shfl_xor(mk, off, 64));
+    }
+    if (lane == 0) { red[0][wave] = mdo; red[1][wave] = mv; red[2][wave] = mk; }
+    __syncthreads();
+    int a = 0, b = 0, cc = 0;
+    for (int w = 0; w < PRO_THREADS / 64; ++w) { a = max(a, red[0][w]); b = max(b, red[1][w]); cc = max(cc, red[2][w]); }
+    int val = 15 - C - ((a - 127) + (b - 127) + (cc - 127));
+    val = min(64, max(-64, val));
+    for (int t = tid; t < T; t += PRO_THREADS) {
+      const int16_t x = (t >= c_lo && t < c_hi) ? (int16_t)val : (int16_t)0;
+      pi[t] = x;
+      if (p.pi_out) p.pi_out[(int64_t)h * T + t] = x;
+    }
+    return;
+  }
+
+  // causal: running maxima of the V and K block exponents from each document's start
+  if (tid == 0) carry_sh = Seg{0, -1, -1};
+  for (int C0 = 0; C0 < T; C0 += PRO_CHUNK) {
+    for (int x = tid; x < PRO_CHUNK; x += PRO_THREADS) flags[x] = 0;
+    if (tid == 0) {  // first document starting at or after C0
+      int lo = 0, hi = p.n_docs;  // lower bound over cu[0 .. n_docs-1]
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (p.cu[mid] < C0) lo = mid + 1; else hi = mid;
+      }
+      kstart = lo;
+    }
+    __syncthreads();
+    for (int k = kstart + tid; k < p.n_docs && p.cu[k] < C0 + PRO_CHUNK; k += PRO_THREADS) flags[p.cu[k] - C0] = 1;
+    __syncthreads();
+    // thread-local inclusive scan of 4 tokens
+    Seg loc[4];
+    Seg run{0, -1, -1};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int t = C0 + 4 * tid + e;
+      Seg x{0, -1, -1};
+      if (t < T) x = Seg{(int)flags[4 * tid + e], (int)sv[t], (int)sk[t]};
+      run = seg_op(run, x);
+      loc[e] = run;
+    }
+    // workgroup exclusive scan of the per-thread aggregates
+    Seg incl = run;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      Seg y{__shfl_up(incl.f, off, 64), __shfl_up(incl.v, off, 64), __shfl_up(incl.k, off, 64)};
+      if (lane >= off) incl = seg_op(y, incl);
+    }
+    if (lane == 63) { wv[wave][0] = incl.f; wv[wave][1] = incl.v; wv[wave][2] = incl.k; }
+    __syncthreads();
+    Seg pre = carry_sh;  // everything before this chunk
+    for (int w = 0; w < wave; ++w) pre = seg_op(pre, Seg{wv[w][0], wv[w][1], wv[w][2]});
+    Seg ex_lane{__shfl_up(incl.f, 1, 64), __shfl_up(incl.v, 1, 64), __shfl_up(incl.k, 1, 64)};
+    if (lane > 0) pre = seg_op(pre, ex_lane);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int t = C0 + 4 * tid + e;
+      if (t >= T) continue;
+      const Seg s = seg_op(pre, loc[e]);
+      int16_t x = 0;
+      if (t >= c_lo && t < c_hi) {
+        int val = 15 - C - (((int)sdo[t] - 127) + (s.v - 127) + (s.k - 127));
+        x = (int16_t)min(64, max(-64, val));
+      }
+      pi[t] = x;
+      if (p.pi_out) p.pi_out[(int64_t)h * T + t] = x;
+    }
+    __syncthreads();
+    if (tid == PRO_THREADS - 1) carry_sh = seg_op(pre, run);
+    __syncthreads();
+  }
+}
+
+}  // namespace
+
+hipError_t launch_bwd(const BwdParams& p, int d, int grid, hipStream_t s) {
+  if (d == 128) {
+    hipLaunchKernelGGL(bwd_prologue<128>, dim3(p.Hq), dim3(PRO_THREADS), 0, s, p);
+    hipLaunchKernelGGL(bwd_kernel<128>, dim3(grid), dim3(BWD_THREADS), 0, s, p);
+  } else {
+    hipLaunchKernelGGL(bwd_prologue<64>, dim3(p.Hq), dim3(PRO_THREADS), 0, s, p);
+    hipLaunchKernelGGL(bwd_kernel<64>, dim3(grid), dim3(BWD_THREADS), 0, s, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace flamia

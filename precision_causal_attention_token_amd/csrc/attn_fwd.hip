@@ -1,0 +1,273 @@
+// Forward: causal packed-document attention on token-block MXFP8 operands
+// (jaehun.me review §1.2 online softmax, §3.1 token-block scales and score factorisation,
+//  §3.4 packed documents and work scheduling).
+//
+// Persistent grid, one 512-thread workgroup per compute unit.  A work unit is (forward item,
+// query head): 256 consecutive queries of one document.  Wave w (of 8) owns queries
+// 32w..32w+31 of the item.  Per 128-key tile (visited from the diagonal tile down to tile 0):
+//   S^T (keys x queries) = K Q^T   : scaled MFMA, A = K rows from LDS, B = Q held in registers;
+//                                    the hardware applies 2^(e(K) + e(Q)), the score scale
+//                                    softmax_scale*log2(e) is one FMA per element;
+//   online softmax per query       : each lane holds 64 of a query's 128 scores, the other 64
+//                                    sit in lane l ^ 32 (one permlane swap per reduction);
+//   P operand                      : E4M3(2^8 p) from the score registers, which already are in
+//                                    the MFMA operand order (no data movement between lanes);
+//   O^T += V^T P^T                 : A = V^T read from the row-major V tile with transpose reads.
+// One E4M3 copy of K and V serves both products; only the LDS read instruction differs.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace flamia {
+
+namespace {
+
+constexpr int FWD_WAVES = 8;
+constexpr int FWD_THREADS = 64 * FWD_WAVES;
+
+template <int D>
+struct FwdSmem {
+  uint8_t k[2][KV_TILE * D];
+  uint8_t v[2][KV_TILE * D];
+  uint8_t sk[2][KV_TILE];
+  uint8_t sv[2][KV_TILE];
+};
+
+// Prefetch of one K/V tile into registers: each thread moves 16-byte chunks.
+template <int D>
+struct TileRegs {
+  static constexpr int CHUNKS = KV_TILE * D / 16 / FWD_THREADS;  // per tensor per thread
+  uint4 k[CHUNKS], v[CHUNKS];
+  uint32_t sc;  // thread t < 128: sk byte of key t; 128 <= t < 256: sv byte of key t-128
+};
+
+template <int D>
+__device__ __forceinline__ void load_tile(TileRegs<D>& r, const FwdParams& p, int g, int doc_start, int L, int kappa) {
+  const int tid = threadIdx.x;
+  constexpr int CPR = D / 16;  // chunks per row
+#pragma unroll
+  for (int i = 0; i < TileRegs<D>::CHUNKS; ++i) {
+    const int chunk = tid + i * FWD_THREADS;
+    const int row = chunk / CPR, col = (chunk % CPR) * 16;
+    const int key = 128 * kappa + row;
+    if (key < L) {
+      const int64_t off = ((int64_t)(doc_start + key) * p.Hkv + g) * D + col;
+      r.k[i] = *reinterpret_cast<const uint4*>(p.k + off);
+      r.v[i] = *reinterpret_cast<const uint4*>(p.v + off);
+    } else {
+      r.k[i] = make_uint4(0, 0, 0, 0);
+      r.v[i] = make_uint4(0, 0, 0, 0);
+    }
+  }
+  r.sc = 127;
+  if (tid < 2 * KV_TILE) {
+    const int key = 128 * kappa + (tid & 127);
+    if (key < L) {
+      const uint8_t* tab = tid < KV_TILE ? p.sk : p.sv;
+      r.sc = tab[(int64_t)g * p.T + doc_start + key];
+    }
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void store_tile(const TileRegs<D>& r, FwdSmem<D>& sm, int buf) {
+  const int tid = threadIdx.x;
+  constexpr int CPR = D / 16;
+#pragma unroll
+  for (int i = 0; i < TileRegs<D>::CHUNKS; ++i) {
+    const int chunk = tid + i * FWD_THREADS;
+    const int row = chunk / CPR, col = (chunk % CPR) * 16;
+    *reinterpret_cast<uint4*>(&sm.k[buf][lds_off<D>(row, col)]) = r.k[i];
+    *reinterpret_cast<uint4*>(&sm.v[buf][lds_off<D>(row, col)]) = r.v[i];
+  }
+  if (tid < KV_TILE) sm.sk[buf][tid] = (uint8_t)r.sc;
+  else if (tid < 2 * KV_TILE) sm.sv[buf][tid - KV_TILE] = (uint8_t)r.sc;
+}
+
+template <int D>
+__global__ __launch_bounds__(FWD_THREADS) void fwd_kernel(FwdParams p) {
+  constexpr int NC = D / 64;   // 64-wide d chunks of the score contraction
+  constexpr int NDB = D / 32;  // 32-wide d blocks of the output
+  __shared__ FwdSmem<D> sm;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 31, hh = lane >> 5;
+  const int n_items = p.list[0];
+  const int4* items = reinterpret_cast<const int4*>(p.list + 4);
+  const int n_units = n_items * p.Hq;
+  const int G = gridDim.x, wg = blockIdx.x;
+  const int grp = p.Hq / p.Hkv;
+  const float c = p.c;
+
+  for (int round = 0;; ++round) {
+    const int u = round * G + ((round & 1) ? (G - 1 - wg) : wg);
+    if (u >= n_units) break;
+    const int4 it = items[u / p.Hq];
+    const int h = u % p.Hq, g = h / grp;
+    const int doc = it.x, b = it.y;
+    const int doc_start = p.cu[doc];
+    const int L = p.cu[doc + 1] - doc_start;
+    const int q_wave = ITEM_Q * b + 32 * wave;         // first query (document offset) of this wave
+    const bool wave_active = q_wave < L;
+    const int q_rel = q_wave + n;
+    const bool row_valid = q_rel < L;
+    const int kd = q_wave / KV_TILE;                    // this wave's diagonal tile
+    const int last_row = min(ITEM_Q * b + ITEM_Q, L) - 1;
+    const int kappa_hi = last_row / KV_TILE;
+
+    // Q operand (B of S^T): lane (n, hh) holds d = 64c + 32hh .. +31 of query n.
+    v8i qop[NC];
+    int q_scale = 127;
+    {
+      const int64_t qa = (int64_t)(doc_start + q_rel);
+#pragma unroll
+      for (int cc = 0; cc < NC; ++cc) {
+        if (row_valid) {
+          const uint4* src = reinterpret_cast<const uint4*>(p.q + (qa * p.Hq + h) * D + 64 * cc + 32 * hh);
+          const uint4 a = src[0], bb = src[1];
+          qop[cc][0] = a.x; qop[cc][1] = a.y; qop[cc][2] = a.z; qop[cc][3] = a.w;
+          qop[cc][4] = bb.x; qop[cc][5] = bb.y; qop[cc][6] = bb.z; qop[cc][7] = bb.w;
+        } else {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) qop[cc][i] = 0;
+        }
+      }
+      if (row_valid) q_scale = p.sq[(int64_t)h * p.T + doc_start + q_rel];
+    }
+
+    v16f oacc[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) oacc[db] = v16f{};
+    float m = -__builtin_inff();  // running max, score units
+    float l = 0.f;                // this lane's share of the row sum of 2^8 p
+
+    TileRegs<D> pre;
+    load_tile<D>(pre, p, g, doc_start, L, kappa_hi);
+    __syncthreads();  // previous unit's readers are done with both buffers
+    store_tile<D>(pre, sm, 0);
+    __syncthreads();
+    int buf = 0;
+    for (int kappa = kappa_hi; kappa >= 0; --kappa) {
+      if (kappa > 0) load_tile<D>(pre, p, g, doc_start, L, kappa - 1);
+      if (wave_active && kappa <= kd) {
+        const uint8_t* kt = sm.k[buf];
+        const uint8_t* vt = sm.v[buf];
+        // ---- S^T for the 4 key blocks of the tile
+        v16f s[4];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          s[kb] = v16f{};
+          const int ks = sm.sk[buf][32 * kb + n];
+#pragma unroll
+          for (int cc = 0; cc < NC; ++cc) {
+            const v8i a = lds_read_row32<D>(kt, 32 * kb + n, 64 * cc + 32 * hh);
+            s[kb] = mfma_scaled(a, qop[cc], s[kb], ks, q_scale);
+          }
+        }
+        // ---- causal mask on the diagonal tile (keys after the query)
+        if (kappa == kd) {
+#pragma unroll
+          for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const int key = KV_TILE * kappa + 32 * kb + acc_row(i, hh);
+              if (key > q_rel) s[kb][i] = -__builtin_inff();
+            }
+        }
+        // ---- running max (raw accumulator units, then scaled once)
+        float mx = -__builtin_inff();
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
+        mx = halves_max(mx);
+        const float m_new = fmaxf(m, mx * c);
+        const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+        if (__any(alpha != 1.0f)) {
+#pragma unroll
+          for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+          l *= alpha;
+        }
+        m = m_new;
+        // ---- p = 2^(t - m), scaled by 2^8 for the E4M3 operand; packed into operand order
+        const float bias = (float)P_SHIFT - m_new;
+        int pk[4][4];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int w4 = 0; w4 < 4; ++w4) {
+            const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][4 * w4 + 0], c, bias));
+            const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][4 * w4 + 1], c, bias));
+            const float p2 = __builtin_amdgcn_exp2f(fmaf(s[kb][4 * w4 + 2], c, bias));
+            const float p3 = __builtin_amdgcn_exp2f(fmaf(s[kb][4 * w4 + 3], c, bias));
+            l += (p0 + p1) + (p2 + p3);
+            pk[kb][w4] = pack4_fp8(p0, p1, p2, p3);
+          }
+        // ---- O^T += V^T P^T, two 64-key chunks
+#pragma unroll
+        for (int ci = 0; ci < 2; ++ci) {
+          v8i pop;
+#pragma unroll
+          for (int w = 0; w < 8; ++w) pop[w] = pk[2 * ci + (w >> 2)][w & 3];
+          const int vs = sm.sv[buf][64 * ci + 32 * hh];
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) {
+            const v8i a = lds_read_tr32<D>(vt, 64 * ci, 32 * db, lane);
+            oacc[db] = mfma_scaled(a, pop, oacc[db], vs, 127 - P_SHIFT);
+          }
+        }
+      }
+      if (kappa > 0) {
+        store_tile<D>(pre, sm, buf ^ 1);
+        __syncthreads();
+        buf ^= 1;
+      }
+    }
+
+    // ---- epilogue: O = acc / l, LSE = m + log2 l (l in units of 2^-8)
+    if (wave_active) {
+      const float lt = halves_sum(l);
+      if (row_valid) {
+        const float inv = 256.0f / lt;
+        uint16_t* orow = p.o + (int64_t)(doc_start + q_rel) * p.ost + (int64_t)h * p.osh;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int d0 = 32 * db + 8 * j + 4 * hh;
+            uint2 w;
+            w.x = pack_bf16(oacc[db][4 * j + 0] * inv, oacc[db][4 * j + 1] * inv);
+            w.y = pack_bf16(oacc[db][4 * j + 2] * inv, oacc[db][4 * j + 3] * inv);
+            *reinterpret_cast<uint2*>(orow + d0) = w;
+          }
+        if (hh == 0) p.lse[(int64_t)h * p.T + doc_start + q_rel] = m + __builtin_amdgcn_logf(lt) - (float)P_SHIFT;
+      }
+    }
+  }
+
+  // ---- rows outside every document: O = 0, LSE = +inf
+  const int c_lo = p.n_docs > 0 ? p.cu[0] : p.T;
+  const int c_hi = p.n_docs > 0 ? p.cu[p.n_docs] : p.T;
+  const int per = (p.T + G - 1) / G;
+  const int t0 = wg * per, t1 = min(t0 + per, p.T);
+  for (int t = t0; t < t1; ++t) {
+    if (t >= c_lo && t < c_hi) continue;
+    for (int x = tid; x < p.Hq * D; x += FWD_THREADS) {
+      const int hh2 = x / D, dd = x % D;
+      p.o[(int64_t)t * p.ost + (int64_t)hh2 * p.osh + dd] = 0;
+    }
+    for (int x = tid; x < p.Hq; x += FWD_THREADS) p.lse[(int64_t)x * p.T + t] = __builtin_inff();
+  }
+}
+
+}  // namespace
+
+hipError_t launch_fwd(const FwdParams& p, int d, int grid, hipStream_t s) {
+  if (d == 128) hipLaunchKernelGGL(fwd_kernel<128>, dim3(grid), dim3(FWD_THREADS), 0, s, p);
+  else hipLaunchKernelGGL(fwd_kernel<64>, dim3(grid), dim3(FWD_THREADS), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace flamia

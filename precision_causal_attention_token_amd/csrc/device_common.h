@@ -1,0 +1,177 @@
+// Device helpers shared by the gfx950 kernels of libflamia.
+//
+// Matrix instruction: v_mfma_scale_f32_32x32x64_f8f6f4 with E4M3 operands (format selectors 0).
+// Lane layout (64 lanes; lane l = n + 32 h, n in [0,32), h in {0,1}):
+//   operand bytes: lane (n, h) holds 32 K-values of row/column n; byte k (0..31) of group h is
+//     K index kidx(h, k) = 32 * (k / 16) + 8 * ((k % 16) / 4) + 4 * h + (k % 4)
+//     (any fixed permutation of K is valid as long as both operands use it; this one is the
+//     order in which the accumulator layout below hands out rows, so a score tile can be fed
+//     back as an operand without moving data between lanes);
+//   scale blocks: the scale byte of lane (n, 0) applies to K indices 0..31 of row n (bytes 0..15
+//     of both lane groups) and that of lane (n, 1) to K indices 32..63 (bytes 16..31);
+//   accumulator: lane (n, h) register i holds row 8 * (i / 4) + 4 * h + (i % 4), column n.
+// These were established by probes on the hardware (see the design notes).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace flamia {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v2i* lds_v2i_ptr;
+
+constexpr int BLK = 32;        // tokens per scale block
+constexpr int KV_TILE = 128;   // keys per tile (running-max and dQ-partial granularity)
+constexpr int ITEM_Q = 256;    // queries per forward work item
+constexpr int P_SHIFT = 8;     // forward probability operand: E4M3(2^8 p), scale 2^-8
+constexpr float LOG2E = 1.4426950408889634f;
+
+__device__ __forceinline__ v16f mfma_scaled(const v8i& a, const v8i& b, const v16f& c, int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
+}
+
+// Accumulator row held by register i of lane group h.
+__device__ __forceinline__ int acc_row(int i, int h) { return 8 * (i >> 2) + 4 * h + (i & 3); }
+
+// ---------------------------------------------------------------------------------------------
+// LDS tiles: [rows][COLS] bytes, COLS in {64, 128}, with the 16-byte chunks of each row permuted
+// by an XOR.  The permutation keeps two access patterns free of bank conflicts: 32 contiguous
+// bytes per lane of consecutive rows (row-major operand reads) and 8 rows
+// {4h..4h+3, 8+4h..8+4h+3} x 16 bytes (transpose reads).
+template <int COLS>
+__device__ __forceinline__ int lds_swizzle(int row) {
+  if constexpr (COLS == 128) return (row & 3) | ((((row >> 2) ^ (row >> 3)) & 1) << 2);
+  else return ((row >> 1) & 1) | ((((row >> 2) ^ (row >> 3)) & 1) << 1);
+}
+template <int COLS>
+__device__ __forceinline__ int lds_off(int row, int col) {
+  return row * COLS + ((((col >> 4) ^ lds_swizzle<COLS>(row)) << 4) | (col & 15));
+}
+
+// Row-major operand: lane reads 32 contiguous bytes of `row` starting at `col` (multiple of 32).
+template <int COLS>
+__device__ __forceinline__ v8i lds_read_row32(const uint8_t* tile, int row, int col) {
+  v4i lo = *reinterpret_cast<const v4i*>(tile + lds_off<COLS>(row, col));
+  v4i hi = *reinterpret_cast<const v4i*>(tile + lds_off<COLS>(row, col + 16));
+  v8i r;
+  r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
+  r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
+  return r;
+}
+
+// Transposed operand: the K dimension runs along the tile's rows.  For the 64-row K chunk that
+// starts at `row0` and the 32 columns that start at `col0` (the operand's M or N index), lane
+// (n, h) receives the 32 bytes tile[row0 + kidx(h, k)][col0 + n], k = 0..31, assembled with
+// ds_read_b64_tr_b8: in each 16-lane group, source lane s supplies the 8-byte piece of row
+// K_(s/2) at column chunk (s & 1), and output lane i receives column i of rows K_0..K_7.
+template <int COLS>
+__device__ __forceinline__ v8i lds_read_tr32(const uint8_t* tile, int row0, int col0, int lane) {
+  const int i = lane & 15;              // position in the 16-lane group
+  const int grp = lane >> 4;            // 16-lane group
+  const int h = grp >> 1;               // lane group of the operand layout
+  const int colbase = col0 + 16 * (grp & 1);
+  const int j = i >> 1, e = i & 1;
+  v8i r;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int row = row0 + 32 * (q >> 1) + 16 * (q & 1) + 8 * (j >> 2) + 4 * h + (j & 3);
+    const uint8_t* p = tile + lds_off<COLS>(row, colbase + 8 * e);
+    v2i t = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i_ptr)(p));
+    r[2 * q] = t[0];
+    r[2 * q + 1] = t[1];
+  }
+  return r;
+}
+
+// ---------------------------------------------------------------------------------------------
+// E8M0 / E4M3 helpers.
+
+// Smallest s with amax <= 448 * 2^s, clamped to >= -127 (amax = 0 or subnormal gives -127);
+// 128 for NaN / infinity.  Integer arithmetic on the float's fields: for amax = 1.f * 2^E,
+// s = E - 8 + (f > 0.75).
+__device__ __forceinline__ int e8m0_roundup(float amax) {
+  const uint32_t b = __float_as_uint(amax) & 0x7FFFFFFFu;
+  const int E = (int)(b >> 23);
+  if (E == 255) return 128;
+  if (E == 0) return -127;
+  const int s = (E - 127) - 8 + ((b & 0x7FFFFFu) > 0x600000u ? 1 : 0);
+  return s < -127 ? -127 : s;
+}
+// 2^-s as a float, for s in [-127, 127].
+__device__ __forceinline__ float exp2i_neg(int s) { return __uint_as_float((uint32_t)(127 - s) << 23); }
+__device__ __forceinline__ float exp2i(int s) { return __uint_as_float((uint32_t)(127 + s) << 23); }
+
+// E4M3 conversion: round to nearest even, hardware instruction.
+// Four floats -> one dword of E4M3 bytes (a0 lowest).
+__device__ __forceinline__ int pack4_fp8(float a0, float a1, float a2, float a3) {
+  const int r = __builtin_amdgcn_cvt_pk_fp8_f32(a0, a1, 0, false);
+  return __builtin_amdgcn_cvt_pk_fp8_f32(a2, a3, r, true);
+}
+
+// ---------------------------------------------------------------------------------------------
+// Wave reductions (64 lanes): DPP within rows of 16, then permlane swaps across rows.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float wave_max(float x) {
+  x = fmaxf(x, dpp<0xB1>(x));    // quad_perm [1,0,3,2]
+  x = fmaxf(x, dpp<0x4E>(x));    // quad_perm [2,3,0,1]
+  x = fmaxf(x, dpp<0x124>(x));   // row_ror:4
+  x = fmaxf(x, dpp<0x128>(x));   // row_ror:8
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_int(x), __float_as_int(x), false, false);
+  x = fmaxf(__int_as_float((int)a[0]), __int_as_float((int)a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
+  return fmaxf(__int_as_float((int)b[0]), __int_as_float((int)b[1]));
+}
+// Combine the two lane groups (l and l ^ 32).
+__device__ __forceinline__ float halves_max(float x) {
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
+  return fmaxf(__int_as_float((int)b[0]), __int_as_float((int)b[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
+  return __int_as_float((int)b[0]) + __int_as_float((int)b[1]);
+}
+// Max within each row of 16 lanes.
+__device__ __forceinline__ float row16_max(float x) {
+  x = fmaxf(x, dpp<0xB1>(x));
+  x = fmaxf(x, dpp<0x4E>(x));
+  x = fmaxf(x, dpp<0x124>(x));
+  x = fmaxf(x, dpp<0x128>(x));
+  return x;
+}
+__device__ __forceinline__ float row16_sum(float x) {
+  x = x + dpp<0xB1>(x);
+  x = x + dpp<0x4E>(x);
+  x = x + dpp<0x124>(x);
+  x = x + dpp<0x128>(x);
+  return x;
+}
+
+// bf16 helpers (round to nearest even; inputs here are finite).
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7F800000u) == 0x7F800000u) return (u >> 16) | ((u & 0xFFFFu) ? 0x40u : 0u);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) { return f32_to_bf16(a) | (f32_to_bf16(b) << 16); }
+
+// Document containing token t: the k with cu[k] <= t < cu[k+1], or -1.
+__device__ __forceinline__ int find_doc(const int32_t* __restrict__ cu, int n_docs, int t) {
+  if (n_docs <= 0 || t < cu[0] || t >= cu[n_docs]) return -1;
+  int lo = 0, hi = n_docs;  // invariant: cu[lo] <= t < cu[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (cu[mid] <= t) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+}  // namespace flamia

@@ -1,0 +1,186 @@
+// C ABI of libflamia (declared in include/flamia.h): argument checks and kernel launches.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/flamia.h"
+#include "kernels.h"
+
+using namespace flamia;
+
+namespace {
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// softmax_scale * log2(e), formed in double and rounded once; the forward and the backward
+// use this same float, so their scores agree bit for bit.
+float score_scale(float softmax_scale, int d) {
+  const double ss = softmax_scale > 0.f ? (double)softmax_scale : 1.0 / sqrt((double)d);
+  return (float)(ss * 1.4426950408889634074);
+}
+float resolved_scale(float softmax_scale, int d) {
+  return softmax_scale > 0.f ? softmax_scale : (float)(1.0 / sqrt((double)d));
+}
+
+int num_cus() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  return n;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* flamia_status_str(flamia_status s) {
+  switch (s) {
+    case FLAMIA_OK: return "ok";
+    case FLAMIA_ERR_NULL: return "null pointer";
+    case FLAMIA_ERR_SHAPE: return "bad shape or stride";
+    case FLAMIA_ERR_UNSUPPORTED: return "unsupported size";
+    case FLAMIA_ERR_WORKSPACE: return "buffer too small";
+    case FLAMIA_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+int32_t flamia_num_workers(void) { return num_cus(); }
+
+size_t flamia_worklist_bytes(int32_t n_docs, int32_t T, int32_t kind) {
+  (void)kind;
+  if (n_docs < 0 || T < 0) return 0;
+  return 16 + 16 * ((size_t)((T + 127) / 128) + (size_t)n_docs);
+}
+
+flamia_status flamia_build_worklist(const int32_t* cu_seqlens, int32_t n_docs, int32_t T, int32_t kind,
+                                    int32_t n_workers, void* list, size_t list_bytes, void* stream) {
+  if (!cu_seqlens || !list) return FLAMIA_ERR_NULL;
+  if (n_docs < 0 || T < 0 || n_workers < 1 || (kind != FLAMIA_LIST_FWD && kind != FLAMIA_LIST_BWD))
+    return FLAMIA_ERR_SHAPE;
+  if (T > FLAMIA_MAX_T_WORKLIST) return FLAMIA_ERR_UNSUPPORTED;
+  if (list_bytes < flamia_worklist_bytes(n_docs, T, kind)) return FLAMIA_ERR_WORKSPACE;
+  if (!aligned(list, 16)) return FLAMIA_ERR_SHAPE;
+  hipError_t e = launch_worklist(cu_seqlens, n_docs, T, kind, n_workers, static_cast<int32_t*>(list),
+                                 static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FLAMIA_OK : FLAMIA_ERR_HIP;
+}
+
+flamia_status flamia_quantize(const flamia_qtensor* tensors, int32_t n_tensors, int32_t T, int32_t d,
+                              const int32_t* cu_seqlens, int32_t n_docs, const void* o, int64_t o_stride_t,
+                              int64_t o_stride_h, float* D, void* stream) {
+  if (!tensors || !cu_seqlens) return FLAMIA_ERR_NULL;
+  if (n_tensors < 1 || n_tensors > 3 || (o && n_tensors != 1)) return FLAMIA_ERR_SHAPE;
+  if (T < 0 || n_docs < 0) return FLAMIA_ERR_SHAPE;
+  if (T > FLAMIA_MAX_T) return FLAMIA_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128) return FLAMIA_ERR_UNSUPPORTED;
+  if (o && !D) return FLAMIA_ERR_NULL;
+  QuantParams p{};
+  p.n_tensors = n_tensors;
+  p.T = T;
+  p.cu = cu_seqlens;
+  p.n_docs = n_docs;
+  p.maxH = 0;
+  for (int i = 0; i < n_tensors; ++i) {
+    const flamia_qtensor& t = tensors[i];
+    if (!t.x || !t.codes || !t.scales) return FLAMIA_ERR_NULL;
+    if (t.H < 1) return FLAMIA_ERR_SHAPE;
+    // 16-byte vector loads of 8 BF16 values
+    if (!aligned(t.x, 16) || (t.stride_t % 8) || (t.stride_h % 8) || t.stride_t < 0 || t.stride_h < 0)
+      return FLAMIA_ERR_SHAPE;
+    if (!aligned(t.codes, 16)) return FLAMIA_ERR_SHAPE;
+    p.t[i] = QTensorDev{static_cast<const uint16_t*>(t.x), t.stride_t, t.stride_h, t.H, t.codes, t.scales};
+    if (t.H > p.maxH) p.maxH = t.H;
+  }
+  if (o) {
+    if (!aligned(o, 16) || (o_stride_t % 8) || (o_stride_h % 8) || o_stride_t < 0 || o_stride_h < 0)
+      return FLAMIA_ERR_SHAPE;
+    p.o = static_cast<const uint16_t*>(o);
+    p.ost = o_stride_t;
+    p.osh = o_stride_h;
+    p.D = D;
+  }
+  if (p.maxH > 65535) return FLAMIA_ERR_UNSUPPORTED;
+  hipError_t e = launch_quantize(p, d, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FLAMIA_OK : FLAMIA_ERR_HIP;
+}
+
+flamia_status flamia_fwd(const flamia_fwd_args* a, void* stream) {
+  if (!a) return FLAMIA_ERR_NULL;
+  if (!a->q || !a->k || !a->v || !a->sq || !a->sk || !a->sv || !a->cu_seqlens || !a->fwd_list || !a->o || !a->lse)
+    return FLAMIA_ERR_NULL;
+  if (a->T < 0 || a->Hq < 1 || a->Hkv < 1 || a->n_docs < 0) return FLAMIA_ERR_SHAPE;
+  if (a->d != 64 && a->d != 128) return FLAMIA_ERR_UNSUPPORTED;
+  if (a->Hq % a->Hkv) return FLAMIA_ERR_UNSUPPORTED;
+  if (a->T > FLAMIA_MAX_T) return FLAMIA_ERR_UNSUPPORTED;
+  if (!aligned(a->o, 8) || (a->o_stride_t % 4) || (a->o_stride_h % 4) || a->o_stride_t < 0 || a->o_stride_h < 0)
+    return FLAMIA_ERR_SHAPE;
+  if (!aligned(a->q, 16) || !aligned(a->k, 16) || !aligned(a->v, 16) || !aligned(a->fwd_list, 16))
+    return FLAMIA_ERR_SHAPE;
+  const int grid = num_cus();
+  if (grid <= 0) return FLAMIA_ERR_HIP;
+  FwdParams p{};
+  p.q = a->q; p.k = a->k; p.v = a->v; p.sq = a->sq; p.sk = a->sk; p.sv = a->sv;
+  p.T = a->T; p.Hq = a->Hq; p.Hkv = a->Hkv;
+  p.c = score_scale(a->softmax_scale, a->d);
+  p.cu = a->cu_seqlens; p.n_docs = a->n_docs;
+  p.list = static_cast<const int32_t*>(a->fwd_list);
+  p.o = static_cast<uint16_t*>(a->o); p.ost = a->o_stride_t; p.osh = a->o_stride_h;
+  p.lse = a->lse;
+  hipError_t e = launch_fwd(p, a->d, grid, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FLAMIA_OK : FLAMIA_ERR_HIP;
+}
+
+size_t flamia_bwd_workspace_bytes(int32_t T, int32_t Hq) {
+  if (T < 0 || Hq < 0) return 0;
+  const size_t pi = ((size_t)T * Hq * 2 + 255) / 256 * 256;
+  const size_t cnt = ((size_t)T * Hq * 4 + 255) / 256 * 256;
+  return pi + cnt + 256;
+}
+
+flamia_status flamia_bwd(const flamia_bwd_args* a, void* stream) {
+  if (!a) return FLAMIA_ERR_NULL;
+  if (!a->q || !a->k || !a->v || !a->dO || !a->sq || !a->sk || !a->sv || !a->sdO || !a->lse || !a->D ||
+      !a->cu_seqlens || !a->bwd_list || !a->dq || !a->dk || !a->dv || !a->workspace)
+    return FLAMIA_ERR_NULL;
+  if (a->T < 0 || a->Hq < 1 || a->Hkv < 1 || a->n_docs < 0) return FLAMIA_ERR_SHAPE;
+  if (a->d != 64 && a->d != 128) return FLAMIA_ERR_UNSUPPORTED;
+  if (a->Hq % a->Hkv) return FLAMIA_ERR_UNSUPPORTED;
+  if (a->T > FLAMIA_MAX_T) return FLAMIA_ERR_UNSUPPORTED;
+  if (a->workspace_bytes < flamia_bwd_workspace_bytes(a->T, a->Hq)) return FLAMIA_ERR_WORKSPACE;
+  const int64_t st[6] = {a->dq_stride_t, a->dq_stride_h, a->dk_stride_t, a->dk_stride_h, a->dv_stride_t, a->dv_stride_h};
+  for (int i = 0; i < 6; ++i)
+    if (st[i] < 0 || (st[i] % 4)) return FLAMIA_ERR_SHAPE;
+  if (!aligned(a->dq, 8) || !aligned(a->dk, 8) || !aligned(a->dv, 8) || !aligned(a->workspace, 256))
+    return FLAMIA_ERR_SHAPE;
+  if (!aligned(a->q, 16) || !aligned(a->k, 16) || !aligned(a->v, 16) || !aligned(a->dO, 16) ||
+      !aligned(a->bwd_list, 16))
+    return FLAMIA_ERR_SHAPE;
+  const int grid = num_cus();
+  if (grid <= 0) return FLAMIA_ERR_HIP;
+  BwdParams p{};
+  p.q = a->q; p.k = a->k; p.v = a->v; p.dO = a->dO;
+  p.sq = a->sq; p.sk = a->sk; p.sv = a->sv; p.sdo = a->sdO;
+  p.lse = a->lse; p.Dv = a->D;
+  p.T = a->T; p.Hq = a->Hq; p.Hkv = a->Hkv;
+  p.c = score_scale(a->softmax_scale, a->d);
+  p.softmax_scale = resolved_scale(a->softmax_scale, a->d);
+  p.cu = a->cu_seqlens; p.n_docs = a->n_docs;
+  p.list = static_cast<const int32_t*>(a->bwd_list);
+  p.dq = static_cast<uint16_t*>(a->dq); p.dk = static_cast<uint16_t*>(a->dk); p.dv = static_cast<uint16_t*>(a->dv);
+  p.dqst = a->dq_stride_t; p.dqsh = a->dq_stride_h;
+  p.dkst = a->dk_stride_t; p.dksh = a->dk_stride_h;
+  p.dvst = a->dv_stride_t; p.dvsh = a->dv_stride_h;
+  uint8_t* ws = static_cast<uint8_t*>(a->workspace);
+  const size_t pi_bytes = ((size_t)a->T * a->Hq * 2 + 255) / 256 * 256;
+  const size_t cnt_bytes = ((size_t)a->T * a->Hq * 4 + 255) / 256 * 256;
+  p.pi = reinterpret_cast<int16_t*>(ws);
+  p.counters = reinterpret_cast<int32_t*>(ws + pi_bytes);
+  p.status = reinterpret_cast<int32_t*>(ws + pi_bytes + cnt_bytes);
+  p.pi_out = a->dq_exp_out;
+  p.causal = a->causal_dq_scale ? 1 : 0;
+  hipError_t e = launch_bwd(p, a->d, grid, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FLAMIA_OK : FLAMIA_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,64 @@
+// Internal launch interface between the C-ABI layer (flamia_api.hip) and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace flamia {
+
+struct QTensorDev {
+  const uint16_t* x;
+  int64_t st, sh;   // element strides
+  int32_t H;
+  uint8_t* codes;
+  uint8_t* scales;
+};
+
+struct QuantParams {
+  QTensorDev t[3];
+  int32_t n_tensors;
+  int32_t T, maxH;
+  const int32_t* cu;
+  int32_t n_docs;
+  const uint16_t* o;  // dO pass only
+  int64_t ost, osh;
+  float* D;
+};
+
+struct FwdParams {
+  const uint8_t *q, *k, *v, *sq, *sk, *sv;
+  int32_t T, Hq, Hkv;
+  float c;  // softmax_scale * log2(e), rounded once to float
+  const int32_t* cu;
+  int32_t n_docs;
+  const int32_t* list;
+  uint16_t* o;
+  int64_t ost, osh;
+  float* lse;
+};
+
+struct BwdParams {
+  const uint8_t *q, *k, *v, *dO, *sq, *sk, *sv, *sdo;
+  const float *lse, *Dv;
+  int32_t T, Hq, Hkv;
+  float c;              // softmax_scale * log2(e), identical to the forward's
+  float softmax_scale;
+  const int32_t* cu;
+  int32_t n_docs;
+  const int32_t* list;
+  uint16_t *dq, *dk, *dv;
+  int64_t dqst, dqsh, dkst, dksh, dvst, dvsh;
+  int16_t* pi;          // workspace: [Hq, T]
+  int32_t* counters;    // workspace: [Hq, T]
+  int32_t* status;      // workspace: error word(s)
+  int16_t* pi_out;      // optional copy of pi
+  int32_t causal;
+};
+
+hipError_t launch_quantize(const QuantParams& p, int d, hipStream_t s);
+hipError_t launch_worklist(const int32_t* cu, int n_docs, int T, int kind, int n_workers, int32_t* list,
+                           hipStream_t s);
+hipError_t launch_fwd(const FwdParams& p, int d, int grid, hipStream_t s);
+hipError_t launch_bwd(const BwdParams& p, int d, int grid, hipStream_t s);
+
+}  // namespace flamia

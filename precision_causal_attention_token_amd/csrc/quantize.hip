@@ -1,0 +1,173 @@
+// Token-block quantiser (FLAMIA MXFP8 path: jaehun.me review §3.1, §3.2, §3.3, §3.4).
+//
+// One workgroup owns the 32-token document blocks that START inside its 256-token window of
+// one head of one tensor.  Such a block may run up to 31 tokens past the window, so the
+// workgroup reads rows [W0, W0 + 287).  Each input row is loaded exactly once (kept in
+// registers between the amax and the code pass) by the workgroup that owns its block;
+// loads are 16 bytes per lane and a row of d BF16 values is covered by d/8 consecutive lanes.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace flamia {
+
+namespace {
+
+constexpr int WIN = 256;            // window of block starts per workgroup
+constexpr int ROWS = WIN + BLK - 1; // rows a workgroup may touch
+
+template <int D>
+__global__ __launch_bounds__(256) void quantize_kernel(QuantParams p) {
+  constexpr int LPR = D / 8;            // lanes per row
+  constexpr int RPP = 256 / LPR;        // rows per pass
+  constexpr int NPASS = (ROWS + RPP - 1) / RPP;
+  __shared__ int16_t own_start[ROWS];   // block start (relative) of an owned row, -1: not owned, -2: outside row to clear
+  __shared__ int16_t blk_len[ROWS];
+  __shared__ float rmax[ROWS];
+  __shared__ int16_t bexp[ROWS];        // exponent for every owned row
+
+  const int tid = threadIdx.x;
+  const int W0 = blockIdx.x * WIN;
+  const int h = blockIdx.y;
+  const QTensorDev& X = p.t[blockIdx.z];
+  if (h >= X.H) return;
+  const int T = p.T;
+
+  // ---- ownership of each row of the window
+  for (int r = tid; r < ROWS; r += 256) {
+    const int tau = W0 + r;
+    int16_t st = -1, len = 0;
+    if (tau < T) {
+      const int k = find_doc(p.cu, p.n_docs, tau);
+      if (k >= 0) {
+        const int c0 = p.cu[k], c1 = p.cu[k + 1];
+        const int bs = c0 + ((tau - c0) / BLK) * BLK;
+        if (bs >= W0 && bs < W0 + WIN) {
+          st = (int16_t)(bs - W0);
+          len = (int16_t)min(BLK, c1 - bs);
+        }
+      } else if (r < WIN) {
+        st = -2;
+      }
+    }
+    own_start[r] = st;
+    blk_len[r] = len;
+  }
+  __syncthreads();
+
+  // ---- pass 1: load owned rows, per-row amax
+  const int lr = tid / LPR, lc = tid % LPR;
+  uint4 vals[NPASS];
+#pragma unroll
+  for (int ps = 0; ps < NPASS; ++ps) {
+    const int r = ps * RPP + lr;
+    float m = 0.f;
+    vals[ps] = make_uint4(0, 0, 0, 0);
+    if (r < ROWS && own_start[r] >= 0) {
+      const int64_t tau = W0 + r;
+      vals[ps] = *reinterpret_cast<const uint4*>(X.x + tau * X.st + (int64_t)h * X.sh + 8 * lc);
+      const uint32_t w[4] = {vals[ps].x, vals[ps].y, vals[ps].z, vals[ps].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) m = fmaxf(m, fmaxf(fabsf(bf16_lo(w[i])), fabsf(bf16_hi(w[i]))));
+      // a NaN element makes the block's exponent NaN (byte 0xFF)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (((w[i] & 0x7F80u) == 0x7F80u) || ((w[i] & 0x7F800000u) == 0x7F800000u)) m = __int_as_float(0x7F800000);
+      }
+    }
+    if constexpr (LPR == 16) {
+      m = row16_max(m);
+    } else {
+      m = fmaxf(m, dpp<0xB1>(m));
+      m = fmaxf(m, dpp<0x4E>(m));
+      m = fmaxf(m, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(m), 0x101F)));  // xor 4
+    }
+    if (lc == 0 && r < ROWS) rmax[r] = m;
+  }
+  __syncthreads();
+
+  // ---- block exponents (thread per block start)
+  for (int r = tid; r < ROWS; r += 256) {
+    if (own_start[r] == r) {
+      float m = 0.f;
+      const int len = blk_len[r];
+      for (int i = 0; i < len; ++i) m = fmaxf(m, rmax[r + i]);
+      bexp[r] = (int16_t)e8m0_roundup(m);
+    }
+  }
+  __syncthreads();
+  // ---- scale bytes (thread per row)
+  for (int r = tid; r < ROWS; r += 256) {
+    const int st = own_start[r];
+    const int tau = W0 + r;
+    if (st >= 0) {
+      const int s = bexp[st];
+      X.scales[(int64_t)h * T + tau] = (uint8_t)(s + 127);
+    } else if (st == -2) {
+      X.scales[(int64_t)h * T + tau] = 0;
+    }
+  }
+
+  // ---- pass 2: codes (+ D for the dO pass)
+  const bool with_d = p.o != nullptr;
+#pragma unroll
+  for (int ps = 0; ps < NPASS; ++ps) {
+    const int r = ps * RPP + lr;
+    const int st = r < ROWS ? own_start[r] : -1;
+    const int64_t tau = W0 + r;
+    float dsum = 0.f;
+    if (st >= 0) {
+      const int s = bexp[st];
+      uint2 out;
+      if (s == 128) {
+        out = make_uint2(0x7F7F7F7Fu, 0x7F7F7F7Fu);
+      } else {
+        const float f = exp2i_neg(s);
+        const uint32_t w[4] = {vals[ps].x, vals[ps].y, vals[ps].z, vals[ps].w};
+        out.x = (uint32_t)pack4_fp8(bf16_lo(w[0]) * f, bf16_hi(w[0]) * f, bf16_lo(w[1]) * f, bf16_hi(w[1]) * f);
+        out.y = (uint32_t)pack4_fp8(bf16_lo(w[2]) * f, bf16_hi(w[2]) * f, bf16_lo(w[3]) * f, bf16_hi(w[3]) * f);
+        if (with_d) {
+          const uint4 ov = *reinterpret_cast<const uint4*>(p.o + tau * p.ost + (int64_t)h * p.osh + 8 * lc);
+          const uint32_t ow[4] = {ov.x, ov.y, ov.z, ov.w};
+          const float sc = exp2i(s);
+          const auto f0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)out.x, false);
+          const auto f1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)out.x, true);
+          const auto f2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)out.y, false);
+          const auto f3 = __builtin_amdgcn_cvt_pk_f32_fp8((int)out.y, true);
+          dsum += (f0[0] * sc) * bf16_lo(ow[0]);
+          dsum += (f0[1] * sc) * bf16_hi(ow[0]);
+          dsum += (f1[0] * sc) * bf16_lo(ow[1]);
+          dsum += (f1[1] * sc) * bf16_hi(ow[1]);
+          dsum += (f2[0] * sc) * bf16_lo(ow[2]);
+          dsum += (f2[1] * sc) * bf16_hi(ow[2]);
+          dsum += (f3[0] * sc) * bf16_lo(ow[3]);
+          dsum += (f3[1] * sc) * bf16_hi(ow[3]);
+        }
+      }
+      *reinterpret_cast<uint2*>(X.codes + (tau * X.H + h) * D + 8 * lc) = out;
+    } else if (st == -2) {
+      *reinterpret_cast<uint2*>(X.codes + (tau * X.H + h) * D + 8 * lc) = make_uint2(0, 0);
+    }
+    if (with_d) {
+      if constexpr (LPR == 16) {
+        dsum = row16_sum(dsum);
+      } else {
+        dsum = dsum + dpp<0xB1>(dsum);
+        dsum = dsum + dpp<0x4E>(dsum);
+        dsum = dsum + __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(dsum), 0x101F));
+      }
+      if (lc == 0 && (st >= 0 || st == -2)) p.D[(int64_t)h * T + tau] = dsum;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_quantize(const QuantParams& p, int d, hipStream_t s) {
+  if (p.T == 0) return hipSuccess;
+  dim3 grid((p.T + WIN - 1) / WIN, p.maxH, p.n_tensors);
+  if (d == 128) hipLaunchKernelGGL(quantize_kernel<128>, grid, dim3(256), 0, s, p);
+  else hipLaunchKernelGGL(quantize_kernel<64>, grid, dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace flamia

@@ -1,0 +1,194 @@
+// GPU work-list builder (jaehun.me review §3.4 "Work scheduling"; agihunt.info: the list for
+// 131,072 one-token documents).
+//
+// Items are (document, block) pairs stably sorted by descending cost.  The sort is a counting
+// sort done by one 1024-thread workgroup, using one property of these lists: inside a document
+// every item has a different cost.
+//   FWD: a document of length L with n = ceil(L/256) items and m = ceil(L/128) key tiles has
+//        the costs {2, 4, ..., 2n-2} and m, so it has an item of cost c iff
+//        (c even and c <= m) or c == m.
+//   BWD: key tile kappa costs m - kappa, so the costs are exactly 1..m.
+// Hence the position of item (document k, cost c) is
+//   #items of cost > c  +  #documents k' < k that have an item of cost c.
+// Cost-1 items come from documents with m == 1 (FWD) or m >= 1 (BWD) and are placed by a
+// prefix count over documents.  Items of cost >= 2 exist only in "long" documents (m >= 2,
+// at most T/129 of them), which are listed in LDS; for every cost c one thread walks that
+// list in document order and emits the items of cost c.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace flamia {
+
+namespace {
+
+constexpr int NT = 1024;
+
+__device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// Exclusive scan of one int per thread across the workgroup; returns the prefix, writes the
+// total to *total.  `scratch` holds NT/64 ints.
+__device__ int wg_exclusive_scan(int x, int* scratch, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int incl = x;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += y;
+  }
+  if (lane == 63) scratch[wave] = incl;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int run = 0;
+    for (int w = 0; w < NT / 64; ++w) {
+      const int t = scratch[w];
+      scratch[w] = run;
+      run += t;
+    }
+    scratch[NT / 64] = run;
+  }
+  __syncthreads();
+  const int res = scratch[wave] + incl - x;
+  *total = scratch[NT / 64];
+  __syncthreads();
+  return res;
+}
+
+__device__ __forceinline__ int serpentine(int i, int G) {
+  const int r = i / G, w = i - r * G;
+  return (r & 1) ? (G - 1 - w) : w;
+}
+
+template <int KIND>
+__device__ __forceinline__ bool has_cost(int m, int c) {
+  if constexpr (KIND == 0) return ((c & 1) == 0 && c <= m) || c == m;
+  else return c <= m;
+}
+
+template <int KIND>
+__global__ __launch_bounds__(NT) void worklist_kernel(const int32_t* __restrict__ cu, int n_docs, int max_cost,
+                                                      int max_long, int G, int32_t* __restrict__ list) {
+  extern __shared__ int smem[];
+  int* hist = smem;                        // [max_cost + 2]: items per cost
+  int* before = hist + (max_cost + 2);     // [max_cost + 2]: items of larger cost
+  int* long_doc = before + (max_cost + 2); // [max_long]
+  int* long_m = long_doc + max_long;       // [max_long]
+  int* scratch = long_m + max_long;        // [NT/64 + 1]
+
+  const int tid = threadIdx.x;
+  for (int c = tid; c < max_cost + 2; c += NT) hist[c] = 0;
+  __syncthreads();
+
+  // ---- phase A: per-thread contiguous range of documents
+  const int per = ceil_div(n_docs, NT);
+  const int k0 = min(tid * per, n_docs), k1 = min(k0 + per, n_docs);
+  int n1 = 0, nl = 0;
+  for (int k = k0; k < k1; ++k) {
+    const int L = cu[k + 1] - cu[k];
+    const int m = ceil_div(L, 128);
+    if (KIND == 0 ? (m == 1) : (m >= 1)) n1++;
+    if (m >= 2) {
+      nl++;
+      if (KIND == 0) {
+        const int n = ceil_div(L, 256);
+        for (int b = 0; b + 1 < n; ++b) atomicAdd(&hist[2 * b + 2], 1);
+        atomicAdd(&hist[m], 1);
+      } else {
+        for (int c = 2; c <= m; ++c) atomicAdd(&hist[c], 1);
+      }
+    }
+  }
+  if (n1) atomicAdd(&hist[1], n1);
+  int tot1, totl;
+  const int base1 = wg_exclusive_scan(n1, scratch, &tot1);
+  const int basel = wg_exclusive_scan(nl, scratch, &totl);
+  {
+    int j = basel;
+    for (int k = k0; k < k1; ++k) {
+      const int m = ceil_div(cu[k + 1] - cu[k], 128);
+      if (m >= 2) {
+        long_doc[j] = k;
+        long_m[j] = m;
+        j++;
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- phase B: before[c] = number of items with cost > c (suffix sums over the histogram)
+  {
+    const int per_c = ceil_div(max_cost, NT);
+    // thread tid covers costs c in (max_cost - (tid+1)*per_c, max_cost - tid*per_c]
+    const int chi = max_cost - tid * per_c, clo = max(chi - per_c, 0);
+    int local = 0;
+    for (int c = chi; c > clo; --c) local += hist[c];
+    int total;
+    int run = wg_exclusive_scan(local, scratch, &total);
+    for (int c = chi; c > clo; --c) {
+      before[c] = run;
+      run += hist[c];
+    }
+    if (tid == 0) {
+      list[0] = total;
+      list[1] = KIND;
+      list[2] = n_docs;
+      list[3] = 0;
+    }
+  }
+  __syncthreads();
+
+  int4* items = reinterpret_cast<int4*>(list + 4);
+  // ---- phase C1: cost-1 items, placed by document order
+  {
+    int r = base1;
+    const int b1 = before[1];
+    for (int k = k0; k < k1; ++k) {
+      const int m = ceil_div(cu[k + 1] - cu[k], 128);
+      if (KIND == 0 ? (m == 1) : (m >= 1)) {
+        const int pos = b1 + r;
+        items[pos] = make_int4(k, KIND == 0 ? 0 : m - 1, 1, serpentine(pos, G));
+        r++;
+      }
+    }
+  }
+  // ---- phase C2: items of cost >= 2, one thread per cost walking the long documents in order
+  for (int c = 2 + tid; c <= max_cost; c += NT) {
+    if (hist[c] == 0) continue;
+    int r = before[c];
+    for (int j = 0; j < totl; ++j) {
+      const int m = long_m[j];
+      if (has_cost<KIND>(m, c)) {
+        const int blk = (KIND == 0) ? ((c == m) ? ceil_div(m, 2) - 1 : c / 2 - 1) : (m - c);
+        items[r] = make_int4(long_doc[j], blk, c, serpentine(r, G));
+        r++;
+      }
+    }
+  }
+}
+
+}  // namespace
+
+size_t worklist_lds_bytes(int T) {
+  const int max_cost = (T + 127) / 128 + 1;
+  const int max_long = T / 129 + 2;
+  return sizeof(int) * (2 * (max_cost + 2) + 2 * max_long + NT / 64 + 1);
+}
+
+hipError_t launch_worklist(const int32_t* cu, int n_docs, int T, int kind, int n_workers, int32_t* list,
+                           hipStream_t s) {
+  const int max_cost = (T + 127) / 128 + 1;
+  const int max_long = T / 129 + 2;
+  const size_t lds = worklist_lds_bytes(T);
+  hipError_t e;
+  if (kind == 0) {
+    e = hipFuncSetAttribute((const void*)worklist_kernel<0>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(worklist_kernel<0>, dim3(1), dim3(NT), lds, s, cu, n_docs, max_cost, max_long, n_workers, list);
+  } else {
+    e = hipFuncSetAttribute((const void*)worklist_kernel<1>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(worklist_kernel<1>, dim3(1), dim3(NT), lds, s, cu, n_docs, max_cost, max_long, n_workers, list);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace flamia

@@ -1,0 +1,69 @@
+"""The C-ABI library loads and exports every entry point declared in include/flamia.h, and
+its host-side argument checks return the documented statuses.  No kernel is launched."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import precision_causal_attention_token_amd as fl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "flamia.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(flamia_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(fl.LIB_PATH):
+        pytest.fail("libflamia.so is not built; run __graft_entry__.build()")
+    return fl.load_library()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared()
+    assert set(names) >= {"flamia_quantize", "flamia_fwd", "flamia_bwd", "flamia_build_worklist"}
+    for nm in names:
+        assert hasattr(lib, nm), nm
+    assert set(fl.EXPORTED_SYMBOLS) <= set(names)
+
+
+def test_status_strings(lib):
+    for s, txt in ((0, b"ok"), (1, b"null pointer"), (4, b"buffer too small")):
+        assert lib.flamia_status_str(s) == txt
+
+
+def test_size_queries(lib):
+    assert lib.flamia_worklist_bytes(3, 1000, 0) == 16 + 16 * (8 + 3)
+    assert lib.flamia_worklist_bytes(-1, 10, 0) == 0
+    T, Hq = 1000, 4
+    assert lib.flamia_bwd_workspace_bytes(T, Hq) >= T * Hq * 6
+
+
+def test_host_validation_errors(lib):
+    # null argument blocks
+    assert lib.flamia_fwd(None, None) == 1
+    assert lib.flamia_bwd(None, None) == 1
+    assert lib.flamia_build_worklist(None, 1, 10, 0, 4, None, 0, None) == 1
+    # unsupported head dim / head ratio and small buffers are rejected before any launch
+    fake = 1 << 20  # never dereferenced: validation fails first
+    a = fl._FwdArgs(fake, fake, fake, fake, fake, fake, 100, 4, 3, 128, 0.0, fake, 1, fake, fake, 512, 128, fake)
+    assert lib.flamia_fwd(ctypes.byref(a), None) == 3          # Hq % Hkv != 0
+    a.Hkv, a.d = 2, 96
+    assert lib.flamia_fwd(ctypes.byref(a), None) == 3          # d not in {64, 128}
+    a.d, a.o_stride_t = 128, 3
+    assert lib.flamia_fwd(ctypes.byref(a), None) == 2          # misaligned output stride
+    assert lib.flamia_build_worklist(fake, 1, 1000, 0, 4, fake, 16, None) == 4
+    assert lib.flamia_build_worklist(fake, 1, 1 << 21, 0, 4, fake, 1 << 30, None) == 3
+    b = fl._BwdArgs()
+    for f, _ in fl._BwdArgs._fields_:
+        if f in ("q", "k", "v", "dO", "sq", "sk", "sv", "sdO", "lse", "D", "cu_seqlens", "bwd_list", "dq", "dk",
+                 "dv", "workspace"):
+            setattr(b, f, fake)
+    b.T, b.Hq, b.Hkv, b.d, b.n_docs = 100, 4, 2, 64, 1
+    b.workspace_bytes = 16
+    assert lib.flamia_bwd(ctypes.byref(b), None) == 4          # workspace too small

@@ -1,0 +1,129 @@
+"""GPU parity, bit-exact parts: the token-block quantiser (codes, scale bytes; D of the dO pass
+within FP32 rounding) and the GPU work lists, against the oracle on the same inputs."""
+import numpy as np
+import pytest
+import torch
+
+import precision_causal_attention_token_amd as fl
+from precision_causal_attention_token_amd import workloads
+from tests.gpu_common import say
+from tests.helpers import bf16_bits
+
+pytestmark = pytest.mark.gpu
+
+
+def _quant_case(orc, x, cu):
+    cu = np.asarray(cu, np.int32)
+    cu_d = torch.as_tensor(cu).cuda()
+    (codes, scales), = fl.quantize([x.cuda()], cu_d)
+    rc, rs = orc.quantize(bf16_bits(x), cu)
+    gc, gs = codes.cpu().numpy(), scales.cpu().numpy()
+    nbad = int((gc != rc).sum()) + int((gs != rs).sum())
+    say("  quantize T=%d H=%d d=%d docs=%d: mismatches %d" % (x.shape[0], x.shape[1], x.shape[2], len(cu) - 1, nbad))
+    assert np.array_equal(gs, rs)
+    assert np.array_equal(gc, rc)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_quantize_small_cases(orc, d):
+    say("quantize small cases d=%d" % d)
+    T = 1000
+    for seed, cu in enumerate([[0, T], [0, 1, 2, 40, 41, 300, 301, 999, T], [7, 100, 100, 650, 990],
+                               [0, 31, 32, 33, 64, 65, 97, 500, T]]):
+        q, k, v, do = workloads.tensors(T, 3, 3, d, seed=200 + seed, outlier_channels=2)
+        _quant_case(orc, k, cu)
+
+
+def test_quantize_all_bf16_patterns_and_scales(orc):
+    """Every BF16 bit pattern, inside blocks whose maxima span the exponent range, so the
+    hardware conversion and the exponent logic are checked against the oracle on all inputs,
+    subnormals included."""
+    say("quantize: all BF16 patterns")
+    pats = np.arange(65536, dtype=np.uint32)
+    e = (pats >> 7) & 0xFF
+    pats = pats[e != 0xFF].astype(np.uint16)          # finite values only
+    d = 128
+    rng = np.random.default_rng(5)
+    rng.shuffle(pats)
+    T = (len(pats) + d - 1) // d
+    x = np.zeros(T * d, np.uint16)
+    x[:len(pats)] = pats
+    x = x.reshape(T, 1, d)
+    xt = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16)
+    lens = workloads.random_lengths(T, 1, 40, seed=9)
+    _quant_case(orc, xt, workloads.cu_seqlens(lens))
+
+
+def test_quantize_subnormal_and_zero_blocks(orc):
+    say("quantize: subnormal / zero blocks")
+    T, d = 96, 64
+    x = np.zeros((T, 2, d), np.uint16)
+    x[:32, 0, :] = np.arange(32 * d).reshape(32, d) % 127 + 1          # subnormal BF16
+    x[32:64, 1, 5] = 0x8001                                            # -2^-133
+    xt = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16)
+    _quant_case(orc, xt, [0, 64, T])
+
+
+@pytest.mark.parametrize("name", ["lognormal", "gqa", "long"])
+def test_quantize_full_workloads(orc, name):
+    """Full-size inputs of the measured workloads (Q, K, V in one launch), bit-exact."""
+    say("quantize full workload %s" % name)
+    cu, shp, (q, k, v, do) = workloads.workload(name)
+    cu_d = torch.as_tensor(cu).cuda()
+    outs = fl.quantize([q.cuda(), k.cuda(), v.cuda()], cu_d)
+    for (codes, scales), x, nm in zip(outs, (q, k, v), "qkv"):
+        rc, rs = orc.quantize(bf16_bits(x), cu)
+        assert np.array_equal(scales.cpu().numpy(), rs), nm
+        assert np.array_equal(codes.cpu().numpy(), rc), nm
+        say("  %s ok" % nm)
+
+
+def test_quantize_do_and_D(orc):
+    say("dO pass + D")
+    T, H, d = 700, 4, 128
+    cu = np.array([0, 5, 300, 650], np.int32)
+    q, k, v, do = workloads.tensors(T, H, H, d, seed=31)
+    o = q  # any BF16 tensor stands in for the forward output here
+    cu_d = torch.as_tensor(cu).cuda()
+    codes, scales, D = fl.quantize_do(do.cuda(), o.cuda(), cu_d)
+    rc, rs, rD = orc.quantize_do(bf16_bits(do), bf16_bits(o), cu)
+    assert np.array_equal(scales.cpu().numpy(), rs)
+    assert np.array_equal(codes.cpu().numpy(), rc)
+    gD = D.cpu().numpy()
+    tol = 1e-5 * np.abs(rD).max()
+    say("  D max|diff| %.3e (tol %.3e)" % (np.abs(gD - rD).max(), tol))
+    assert np.abs(gD - rD).max() <= tol
+    assert not gD[:, 650:].any()
+
+
+def _list_case(orc, cu, G=None):
+    cu = np.asarray(cu, np.int32)
+    T = int(cu[-1])
+    cu_d = torch.as_tensor(cu).cuda()
+    G = G or fl.num_workers()
+    for kind in (0, 1):
+        buf = fl.build_worklist(cu_d, T, kind, G)
+        n, items = fl.worklist_items(buf)
+        ref = orc.worklist(cu, kind, G)
+        assert n == len(ref), (kind, n, len(ref))
+        assert np.array_equal(items.cpu().numpy(), ref), kind
+        assert int(buf[1].item()) == kind and int(buf[2].item()) == len(cu) - 1
+    say("  work lists ok: docs=%d T=%d" % (len(cu) - 1, T))
+
+
+def test_worklist_random(orc):
+    say("work lists: random")
+    for seed in range(6):
+        lens = workloads.random_lengths(5000 + 997 * seed, 1, 1500, seed=300 + seed)
+        if seed % 2:
+            lens[2] = 0
+            lens.insert(0, 0)
+        _list_case(orc, workloads.cu_seqlens(lens), G=7 + seed)
+    _list_case(orc, [0], G=3)           # no documents
+    _list_case(orc, [0, 0, 0], G=3)     # empty documents only
+
+
+@pytest.mark.parametrize("name", ["single", "lognormal", "gqa", "long", "tokens", "onedoc"])
+def test_worklist_workloads(orc, name):
+    say("work lists: %s" % name)
+    _list_case(orc, workloads.cu_seqlens(workloads.doc_lengths(name)))
