@@ -52,6 +52,76 @@ __device__ __forceinline__ uint32_t pack_half2(_Float16 a, _Float16 b) {
 __device__ __forceinline__ _Float16 half_lo(uint32_t w) { return __builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFF)); }
 __device__ __forceinline__ _Float16 half_hi(uint32_t w) { return __builtin_bit_cast(_Float16, (uint16_t)(w >> 16)); }
 
+// One step's Q / dO rows and row statistics, held in registers between the global loads
+// (issued one step ahead) and the LDS stores.
+template <int D>
+struct StepRegs {
+  static constexpr int CH = QT * D / 16 / BWD_THREADS;  // 16-byte chunks per tensor per thread
+  uint4 q[CH], dO[CH];
+  float lse, dd;
+  int pi, sq, sdo;
+  int q0;
+};
+
+template <int D>
+__device__ __forceinline__ void load_step(StepRegs<D>& r, const BwdParams& p, int doc_start, int L, int h, int qt) {
+  const int tid = threadIdx.x;
+  constexpr int CPR = D / 16;
+  const int q0 = QT * qt;
+  r.q0 = q0;
+#pragma unroll
+  for (int i = 0; i < StepRegs<D>::CH; ++i) {
+    const int chunk = tid + i * BWD_THREADS;
+    const int row = chunk / CPR, col = (chunk % CPR) * 16;
+    const int qr = q0 + row;
+    r.q[i] = make_uint4(0, 0, 0, 0);
+    r.dO[i] = make_uint4(0, 0, 0, 0);
+    if (qr < L) {
+      const int64_t off = ((int64_t)(doc_start + qr) * p.Hq + h) * D + col;
+      r.q[i] = *reinterpret_cast<const uint4*>(p.q + off);
+      r.dO[i] = *reinterpret_cast<const uint4*>(p.dO + off);
+    }
+  }
+  r.lse = 0.f; r.dd = 0.f; r.pi = 0; r.sq = 127; r.sdo = 127;
+  if (tid < QT) {
+    const int qr = q0 + tid;
+    if (qr < L) {
+      const int64_t ti = (int64_t)h * p.T + doc_start + qr;
+      r.lse = p.lse[ti];
+      r.dd = p.Dv[ti];
+      r.pi = p.pi[ti];
+    }
+  } else if (tid < QT + 2) {
+    const int qr = q0 + 32 * (tid - QT);
+    if (qr < L) {
+      const int64_t ti = (int64_t)h * p.T + doc_start + qr;
+      r.sq = p.sq[ti];
+      r.sdo = p.sdo[ti];
+    }
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void store_step(const StepRegs<D>& r, BwdSmem<D>& sm) {
+  const int tid = threadIdx.x;
+  constexpr int CPR = D / 16;
+#pragma unroll
+  for (int i = 0; i < StepRegs<D>::CH; ++i) {
+    const int chunk = tid + i * BWD_THREADS;
+    const int row = chunk / CPR, col = (chunk % CPR) * 16;
+    *reinterpret_cast<uint4*>(&sm.q[lds_off<D>(row, col)]) = r.q[i];
+    *reinterpret_cast<uint4*>(&sm.dO[lds_off<D>(row, col)]) = r.dO[i];
+  }
+  if (tid < QT) {
+    sm.lse[tid] = r.lse;
+    sm.dd[tid] = r.dd;
+    sm.pi[tid] = r.pi;
+  } else if (tid < QT + 2) {
+    sm.sq[tid - QT] = r.sq;
+    sm.sdo[tid - QT] = r.sdo;
+  }
+}
+
 template <int D>
 __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
   constexpr int NC = D / 64;
@@ -122,181 +192,186 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
 #pragma unroll
     for (int db = 0; db < NDB; ++db) { dkacc[db] = v16f{}; dvacc[db] = v16f{}; }
 
-    for (int hi = 0; hi < grp; ++hi) {
+    // Steps run over (query head of the group, 64-query tile from the diagonal to the
+    // document end).  The next step's Q / dO tiles and row statistics are loaded into
+    // registers while the current step computes.
+    const int n_qt = (L + QT - 1) / QT - 2 * kappa;  // query tiles per head
+    const int n_steps = grp * n_qt;
+    StepRegs<D> pre;
+    load_step<D>(pre, p, doc_start, L, g * grp, 2 * kappa);
+    for (int st = 0; st < n_steps; ++st) {
+      const int hi = st / n_qt;
       const int h = g * grp + hi;
-      for (int qt = 2 * kappa; QT * qt < L; ++qt) {
-        const int q0 = QT * qt;
-        __syncthreads();  // previous step's LDS readers are done
-        // ---- stage Q, dO tiles and per-row statistics
-        {
-          constexpr int CPR = D / 16;
-          for (int chunk = tid; chunk < QT * CPR; chunk += BWD_THREADS) {
-            const int row = chunk / CPR, col = (chunk % CPR) * 16;
-            const int qr = q0 + row;
-            uint4 a = make_uint4(0, 0, 0, 0), b = make_uint4(0, 0, 0, 0);
-            if (qr < L) {
-              const int64_t off = ((int64_t)(doc_start + qr) * p.Hq + h) * D + col;
-              a = *reinterpret_cast<const uint4*>(p.q + off);
-              b = *reinterpret_cast<const uint4*>(p.dO + off);
+      const int qt = 2 * kappa + (st - hi * n_qt);
+      const int q0 = QT * qt;
+      __syncthreads();  // previous step's LDS readers are done
+      store_step<D>(pre, sm);
+      __syncthreads();
+      if (st + 1 < n_steps) {
+        const int hn = (st + 1) / n_qt;
+        load_step<D>(pre, p, doc_start, L, g * grp + hn, 2 * kappa + (st + 1 - hn * n_qt));
+      }
+      {
+          // ---- S and dP for this wave's 32 keys x 64 queries
+          v16f sacc[2], pacc[2];
+  #pragma unroll
+          for (int qb = 0; qb < 2; ++qb) {
+            sacc[qb] = v16f{};
+            pacc[qb] = v16f{};
+  #pragma unroll
+            for (int cc = 0; cc < NC; ++cc) {
+              const v8i aq = lds_read_row32<D>(sm.q, 32 * qb + n, 64 * cc + 32 * hh);
+              sacc[qb] = mfma_scaled(aq, kop[cc], sacc[qb], sm.sq[qb], k_scale);
+              const v8i ad = lds_read_row32<D>(sm.dO, 32 * qb + n, 64 * cc + 32 * hh);
+              pacc[qb] = mfma_scaled(ad, vop[cc], pacc[qb], sm.sdo[qb], v_scale);
             }
-            *reinterpret_cast<uint4*>(&sm.q[lds_off<D>(row, col)]) = a;
-            *reinterpret_cast<uint4*>(&sm.dO[lds_off<D>(row, col)]) = b;
+            mfma_drain(sacc[qb]);
+            mfma_drain(pacc[qb]);
           }
-          if (tid < QT) {
-            const int qr = q0 + tid;
-            const bool ok = qr < L;
-            const int64_t ti = (int64_t)h * T + doc_start + qr;
-            sm.lse[tid] = ok ? p.lse[ti] : 0.f;
-            sm.dd[tid] = ok ? p.Dv[ti] : 0.f;
-            sm.pi[tid] = ok ? (int)p.pi[ti] : 0;
-          } else if (tid < QT + 2) {
-            const int qb = tid - QT, qr = q0 + 32 * qb;
-            const int64_t ti = (int64_t)h * T + doc_start + qr;
-            sm.sq[qb] = qr < L ? p.sq[ti] : 127;
-            sm.sdo[qb] = qr < L ? p.sdo[ti] : 127;
+          // ---- P, dS, block exponents, E4M3 operands
+          int pp[8], pd[8];
+          int sp[2], sds[2];
+  #pragma unroll
+          for (int qb = 0; qb < 2; ++qb) {
+            float pmax = 0.f, dmax = 0.f;
+  #pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const int qr = q0 + 32 * qb + acc_row(i, hh);
+              const bool vis = key_rel <= qr && qr < L;
+              const int qi = 32 * qb + acc_row(i, hh);
+              const float pv = vis ? __builtin_amdgcn_exp2f(fmaf(sacc[qb][i], c, -sm.lse[qi])) : 0.f;
+              const float dsv = pv * (pacc[qb][i] - sm.dd[qi]);
+              sacc[qb][i] = pv;
+              pacc[qb][i] = dsv;
+              pmax = fmaxf(pmax, pv);
+              dmax = fmaxf(dmax, fabsf(dsv));
+            }
+            sp[qb] = e8m0_roundup(wave_max(pmax));
+            sds[qb] = e8m0_roundup(wave_max(dmax));
+            const float fp = exp2i_neg(sp[qb]), fd = exp2i_neg(sds[qb]);
+  #pragma unroll
+            for (int w4 = 0; w4 < 4; ++w4) {
+              pp[4 * qb + w4] = pack4_fp8(sacc[qb][4 * w4] * fp, sacc[qb][4 * w4 + 1] * fp, sacc[qb][4 * w4 + 2] * fp,
+                                          sacc[qb][4 * w4 + 3] * fp);
+              pd[4 * qb + w4] = pack4_fp8(pacc[qb][4 * w4] * fd, pacc[qb][4 * w4 + 1] * fd, pacc[qb][4 * w4 + 2] * fd,
+                                          pacc[qb][4 * w4 + 3] * fd);
+              // dS codes to LDS as [key][query]: 4 consecutive queries per dword
+              const int qcol = 32 * qb + 8 * w4 + 4 * hh;
+              *reinterpret_cast<int*>(&sm.ds[lds_off<QT>(32 * wave + n, qcol)]) = pd[4 * qb + w4];
+            }
+            if (lane == 0) sm.ds_scale[qb][wave] = sds[qb] + 127;
           }
-        }
-        __syncthreads();
-
-        // ---- S and dP for this wave's 32 keys x 64 queries
-        v16f sacc[2], pacc[2];
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          sacc[qb] = v16f{};
-          pacc[qb] = v16f{};
-#pragma unroll
-          for (int cc = 0; cc < NC; ++cc) {
-            const v8i aq = lds_read_row32<D>(sm.q, 32 * qb + n, 64 * cc + 32 * hh);
-            sacc[qb] = mfma_scaled(aq, kop[cc], sacc[qb], sm.sq[qb], k_scale);
-            const v8i ad = lds_read_row32<D>(sm.dO, 32 * qb + n, 64 * cc + 32 * hh);
-            pacc[qb] = mfma_scaled(ad, vop[cc], pacc[qb], sm.sdo[qb], v_scale);
-          }
-        }
-        // ---- P, dS, block exponents, E4M3 operands
-        int pp[8], pd[8];
-        int sp[2], sds[2];
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          float pmax = 0.f, dmax = 0.f;
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int qr = q0 + 32 * qb + acc_row(i, hh);
-            const bool vis = key_rel <= qr && qr < L;
-            const int qi = 32 * qb + acc_row(i, hh);
-            const float pv = vis ? __builtin_amdgcn_exp2f(fmaf(sacc[qb][i], c, -sm.lse[qi])) : 0.f;
-            const float dsv = pv * (pacc[qb][i] - sm.dd[qi]);
-            sacc[qb][i] = pv;
-            pacc[qb][i] = dsv;
-            pmax = fmaxf(pmax, pv);
-            dmax = fmaxf(dmax, fabsf(dsv));
-          }
-          sp[qb] = e8m0_roundup(wave_max(pmax));
-          sds[qb] = e8m0_roundup(wave_max(dmax));
-          const float fp = exp2i_neg(sp[qb]), fd = exp2i_neg(sds[qb]);
-#pragma unroll
-          for (int w4 = 0; w4 < 4; ++w4) {
-            pp[4 * qb + w4] = pack4_fp8(sacc[qb][4 * w4] * fp, sacc[qb][4 * w4 + 1] * fp, sacc[qb][4 * w4 + 2] * fp,
-                                        sacc[qb][4 * w4 + 3] * fp);
-            pd[4 * qb + w4] = pack4_fp8(pacc[qb][4 * w4] * fd, pacc[qb][4 * w4 + 1] * fd, pacc[qb][4 * w4 + 2] * fd,
-                                        pacc[qb][4 * w4 + 3] * fd);
-            // dS codes to LDS as [key][query]: 4 consecutive queries per dword
-            const int qcol = 32 * qb + 8 * w4 + 4 * hh;
-            *reinterpret_cast<int*>(&sm.ds[lds_off<QT>(32 * wave + n, qcol)]) = pd[4 * qb + w4];
-          }
-          if (lane == 0) sm.ds_scale[qb][wave] = sds[qb] + 127;
-        }
-        // ---- dV^T += dO^T Phat, dK^T += Q^T dShat
-        {
-          v8i bp, bd;
-#pragma unroll
-          for (int w = 0; w < 8; ++w) { bp[w] = pp[w]; bd[w] = pd[w]; }
-          const int sdo_h = sm.sdo[hh], sq_h = sm.sq[hh];
-          const int sp_h = (hh ? sp[1] : sp[0]) + 127, sds_h = (hh ? sds[1] : sds[0]) + 127;
-#pragma unroll
-          for (int db = 0; db < NDB; ++db) {
-            const v8i ado = lds_read_tr32<D>(sm.dO, 0, 32 * db, lane);
-            dvacc[db] = mfma_scaled(ado, bp, dvacc[db], sdo_h, sp_h);
-            const v8i aq = lds_read_tr32<D>(sm.q, 0, 32 * db, lane);
-            dkacc[db] = mfma_scaled(aq, bd, dkacc[db], sq_h, sds_h);
-          }
-        }
-        __syncthreads();  // dShat tile and its exponents are complete
-
-        // ---- dQ^T = K^T dShat^T for this wave's slice
-        constexpr int NQB = (D == 128) ? 2 : 1;
-        const int dblk = (D == 128) ? wave : (wave & 1);
-        const int qb0 = (D == 128) ? 0 : (wave >> 1);
-        v16f dq[NQB];
-#pragma unroll
-        for (int x = 0; x < NQB; ++x) {
-          const int qb = qb0 + x;
-          dq[x] = v16f{};
-#pragma unroll
-          for (int ci = 0; ci < 2; ++ci) {
-            const v8i ak = lds_read_tr32<D>(sm.k, 64 * ci, 32 * dblk, lane);
-            const v8i bs = lds_read_tr32<QT>(sm.ds, 64 * ci, 32 * qb, lane);
-            dq[x] = mfma_scaled(ak, bs, dq[x], sm.sk[64 * ci + 32 * hh], sm.ds_scale[qb][2 * ci + hh]);
-          }
-        }
-
-        // ---- ordered FP16 accumulation of the partial sums (ascending key tiles)
-        int32_t* cnt = p.counters + (int64_t)h * T + doc_start + q0;
-        if (tid == 0 && kappa > 0) {
-          int spins = 0;
-          while (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != kappa) {
-            __builtin_amdgcn_s_sleep(4);
-            // give up after the limit, or at once if another wait already gave up
-            if (++spins > SPIN_LIMIT || __hip_atomic_load(p.status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
-              atomicOr(p.status, 1);
-              break;
+          // ---- dV^T += dO^T Phat, dK^T += Q^T dShat
+          {
+            v8i bp, bd;
+  #pragma unroll
+            for (int w = 0; w < 8; ++w) { bp[w] = pp[w]; bd[w] = pd[w]; }
+            const int sdo_h = sm.sdo[hh], sq_h = sm.sq[hh];
+            const int sp_h = (hh ? sp[1] : sp[0]) + 127, sds_h = (hh ? sds[1] : sds[0]) + 127;
+  #pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+              const v8i ado = lds_read_tr32<D>(sm.dO, 0, 32 * db, lane);
+              dvacc[db] = mfma_scaled(ado, bp, dvacc[db], sdo_h, sp_h);
+              const v8i aq = lds_read_tr32<D>(sm.q, 0, 32 * db, lane);
+              dkacc[db] = mfma_scaled(aq, bd, dkacc[db], sq_h, sds_h);
             }
           }
-        }
-        if (tid == 0) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-        __syncthreads();
-        const bool last = (kappa == qt / 2);
-#pragma unroll
-        for (int x = 0; x < NQB; ++x) {
-          const int qb = qb0 + x;
-          const int qi = 32 * qb + n;
-          const int qr = q0 + qi;
-          if (qr < L) {
-            const int pi = sm.pi[qi];
-            const float up = exp2i(pi), down = exp2i(-pi) * p.softmax_scale;
-            uint16_t* row = p.dq + (int64_t)(doc_start + qr) * p.dqst + (int64_t)h * p.dqsh;
-#pragma unroll
+          __syncthreads();  // dShat tile and its exponents are complete
+
+          // ---- dQ^T = K^T dShat^T for this wave's slice
+          constexpr int NQB = (D == 128) ? 2 : 1;
+          const int dblk = (D == 128) ? wave : (wave & 1);
+          const int qb0 = (D == 128) ? 0 : (wave >> 1);
+          v16f dq[NQB];
+  #pragma unroll
+          for (int x = 0; x < NQB; ++x) {
+            const int qb = qb0 + x;
+            dq[x] = v16f{};
+  #pragma unroll
+            for (int ci = 0; ci < 2; ++ci) {
+              const v8i ak = lds_read_tr32<D>(sm.k, 64 * ci, 32 * dblk, lane);
+              const v8i bs = lds_read_tr32<QT>(sm.ds, 64 * ci, 32 * qb, lane);
+              dq[x] = mfma_scaled(ak, bs, dq[x], sm.sk[64 * ci + 32 * hh], sm.ds_scale[qb][2 * ci + hh]);
+            }
+            mfma_drain(dq[x]);
+          }
+
+          // ---- ordered FP16 accumulation of the partial sums (ascending key tiles)
+          int32_t* cnt = p.counters + (int64_t)h * T + doc_start + q0;
+          if (tid == 0 && kappa > 0) {
+            int spins = 0;
+            while (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != kappa) {
+              __builtin_amdgcn_s_sleep(4);
+              // give up after the limit, or at once if another wait already gave up
+              if (++spins > SPIN_LIMIT || __hip_atomic_load(p.status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
+                atomicOr(p.status, 1);
+                break;
+              }
+            }
+          }
+          __syncthreads();
+          const bool last = (kappa == qt / 2);
+          // read all previous sums first (one memory round trip), then add and store
+          uint64_t old[NQB][4];
+  #pragma unroll
+          for (int x = 0; x < NQB; ++x) {
+            const int qr = q0 + 32 * (qb0 + x) + n;
+  #pragma unroll
             for (int j = 0; j < 4; ++j) {
-              const int d0 = 32 * dblk + 8 * j + 4 * hh;
-              uint64_t* ptr = reinterpret_cast<uint64_t*>(row + d0);
-              _Float16 a0 = (_Float16)(dq[x][4 * j + 0] * up), a1 = (_Float16)(dq[x][4 * j + 1] * up);
-              _Float16 a2 = (_Float16)(dq[x][4 * j + 2] * up), a3 = (_Float16)(dq[x][4 * j + 3] * up);
-              if (kappa > 0) {
-                const uint64_t old = __hip_atomic_load(ptr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                const uint32_t lo = (uint32_t)old, hi = (uint32_t)(old >> 32);
-                a0 = half_lo(lo) + a0;
-                a1 = half_hi(lo) + a1;
-                a2 = half_lo(hi) + a2;
-                a3 = half_hi(hi) + a3;
-              }
-              if (last) {
-                uint2 w;
-                w.x = pack_bf16((float)a0 * down, (float)a1 * down);
-                w.y = pack_bf16((float)a2 * down, (float)a3 * down);
-                *reinterpret_cast<uint2*>(ptr) = w;
-              } else {
-                const uint64_t nw = (uint64_t)pack_half2(a0, a1) | ((uint64_t)pack_half2(a2, a3) << 32);
-                __hip_atomic_store(ptr, nw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              old[x][j] = 0;
+              if (kappa > 0 && qr < L) {
+                const uint16_t* row = p.dq + (int64_t)(doc_start + qr) * p.dqst + (int64_t)h * p.dqsh;
+                old[x][j] = __hip_atomic_load(reinterpret_cast<const uint64_t*>(row + 32 * dblk + 8 * j + 4 * hh),
+                                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
               }
             }
           }
-        }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-        __syncthreads();
-        if (tid == 0 && !last) __hip_atomic_store(cnt, kappa + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+  #pragma unroll
+          for (int x = 0; x < NQB; ++x) {
+            const int qb = qb0 + x;
+            const int qi = 32 * qb + n;
+            const int qr = q0 + qi;
+            if (qr < L) {
+              const int pi = sm.pi[qi];
+              const float up = exp2i(pi), down = exp2i(-pi) * p.softmax_scale;
+              uint16_t* row = p.dq + (int64_t)(doc_start + qr) * p.dqst + (int64_t)h * p.dqsh;
+  #pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                const int d0 = 32 * dblk + 8 * j + 4 * hh;
+                uint64_t* ptr = reinterpret_cast<uint64_t*>(row + d0);
+                _Float16 a0 = (_Float16)(dq[x][4 * j + 0] * up), a1 = (_Float16)(dq[x][4 * j + 1] * up);
+                _Float16 a2 = (_Float16)(dq[x][4 * j + 2] * up), a3 = (_Float16)(dq[x][4 * j + 3] * up);
+                if (kappa > 0) {
+                  const uint32_t lo = (uint32_t)old[x][j], hi2 = (uint32_t)(old[x][j] >> 32);
+                  a0 = half_lo(lo) + a0;
+                  a1 = half_hi(lo) + a1;
+                  a2 = half_lo(hi2) + a2;
+                  a3 = half_hi(hi2) + a3;
+                }
+                if (last) {
+                  uint2 w;
+                  w.x = pack_bf16((float)a0 * down, (float)a1 * down);
+                  w.y = pack_bf16((float)a2 * down, (float)a3 * down);
+                  *reinterpret_cast<uint2*>(ptr) = w;
+                } else {
+                  const uint64_t nw = (uint64_t)pack_half2(a0, a1) | ((uint64_t)pack_half2(a2, a3) << 32);
+                  __hip_atomic_store(ptr, nw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
+              }
+            }
+          }
+          // The partial sums are device-coherent atomics (loads and stores bypass the non-coherent
+          // cache levels), so no cache-wide write-back or invalidation is needed: the turn is
+          // handed on once every lane's stores have completed.
+          __builtin_amdgcn_s_waitcnt(0);
+          __syncthreads();
+          if (tid == 0 && !last) __hip_atomic_store(cnt, kappa + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
 
     // ---- dK, dV of this wave's keys
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) { mfma_drain(dkacc[db]); mfma_drain(dvacc[db]); }
     if (key_valid) {
       uint16_t* krow = p.dk + (int64_t)(doc_start + key_rel) * p.dkst + (int64_t)g * p.dksh;
       uint16_t* vrow = p.dv + (int64_t)(doc_start + key_rel) * p.dvst + (int64_t)g * p.dvsh;
