@@ -36,6 +36,9 @@ def parse():
     ap.add_argument("--causal-dq", action="store_true", help="causal dQ prescale option")
     ap.add_argument("--cpu-pairs", type=float, default=2.0e7, help="query-key pairs in the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibration-copy-mb", type=int, default=0,
+                    help="before warmup, run one plain device-to-device copy of this many MiB (reference "
+                         "kernel of known traffic for hardware byte counters)")
     return ap.parse_args()
 
 
@@ -115,7 +118,7 @@ def main():
         e1.record()
         torch.cuda.synchronize()
         wl_ms.append(e0.elapsed_time(e1))
-    ws = torch.empty(fl.load_library().flamia_bwd_workspace_bytes(T, Hq), dtype=torch.uint8, device=dev)
+    ws = torch.empty(fl.bwd_workspace_bytes(cu, T, Hq), dtype=torch.uint8, device=dev)
 
     stage_names = ("quantize_qkv", "fwd", "quantize_do", "bwd")
 
@@ -127,14 +130,24 @@ def main():
         if evs: evs[2].record()
         dc, dsc, D = fl.quantize_do(do, o, cu_d)
         if evs: evs[3].record()
-        out = fl.bwd(qz, kz, vz, (dc, dsc), lse, D, cu_d, lists.bwd, None, args.causal_dq, workspace=ws)
+        out = fl.bwd(qz, kz, vz, (dc, dsc), lse, D, cu_d, lists, None, args.causal_dq, workspace=ws)
         if evs: evs[4].record()
         return out
+
+    if args.calibration_copy_mb > 0:
+        n = args.calibration_copy_mb << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print("bench: calibration copy of %d bytes done" % n, file=sys.stderr, flush=True)
+        del src, dst
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    assert fl.bwd_status(ws, T, Hq) == 0
+    assert fl.bwd_status(ws) == 0
 
     # timed region: exactly K steps, bracketed by device synchronisation
     all_evs = [[ev() for _ in range(5)] for _ in range(args.steps)]
@@ -146,7 +159,7 @@ def main():
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     stages = {nm: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in all_evs])) for j, nm in enumerate(stage_names)}
-    assert fl.bwd_status(ws, T, Hq) == 0
+    assert fl.bwd_status(ws) == 0
 
     value = flop / (ms_per_step * 1e-3) / 1e12
     fwd_flop, bwd_flop = 4.0 * d * Hq * pairs, 10.0 * d * Hq * pairs

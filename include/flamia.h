@@ -168,11 +168,18 @@ flamia_status flamia_fwd(const flamia_fwd_args* args, void* stream);
  *   causal_dq_scale = 1: e(dO_i) of the row's own block and maxima of e(V), e(K) over the row's
  *                        document up to and including its own block, so no later token
  *                        changes the rounding of earlier rows.
- * The FP16 accumulation is done in place in the dq buffer (which must therefore hold d
- * contiguous elements per (row, head)); the ascending order is enforced by per-(head, query
- * tile) turn counters, which makes results bit-reproducible.
- * Work comes from a FLAMIA_LIST_BWD list; each (item, KV head) unit runs all query heads of
- * its group, so dK and dV are written once.
+ * Reduction of dQ: a document with a single 128-key tile has one contribution per row, which
+ * the key-tile pass turns into dQ directly.  For longer documents the key-tile pass stores
+ * the dShat codes and exponents of every visited (64-query tile, key tile, query head) in the
+ * workspace, and a query-tile pass (driven by the forward work list) reads them back in
+ * ascending key-tile order and keeps acc16 in registers.  The order of every sum is fixed, so
+ * results are bit-reproducible, and no workgroup waits for another.
+ * Work comes from a FLAMIA_LIST_BWD list (key-tile pass; each (item, KV head) unit runs all
+ * query heads of its group, so dK and dV are written once) and a FLAMIA_LIST_FWD list (dQ
+ * pass), both built for the same cu_seqlens.
+ * Device-side error: if the workspace cannot hold the dShat store, the status word (the first
+ * int32 of the workspace) is set to 2 and dQ, dK, dV of the rows inside documents are left
+ * unwritten; otherwise it is 0 once the backward has run.
  * ------------------------------------------------------------------------------------------ */
 typedef struct {
   const uint8_t *q, *k, *v, *dO;      /* codes (dO: [T, Hq, d], from the dO quantiser pass) */
@@ -182,20 +189,26 @@ typedef struct {
   float softmax_scale;                /* must equal the forward's (<= 0: 1 / sqrt(d)) */
   const int32_t* cu_seqlens;
   int32_t n_docs;
+  const void* fwd_list;               /* FLAMIA_LIST_FWD list for cu_seqlens */
   const void* bwd_list;               /* FLAMIA_LIST_BWD list for cu_seqlens */
   void *dq, *dk, *dv;                 /* out: bf16; dq [T, Hq, d], dk, dv [T, Hkv, d] */
   int64_t dq_stride_t, dq_stride_h, dk_stride_t, dk_stride_h, dv_stride_t, dv_stride_h;
-  void* workspace;                    /* flamia_bwd_workspace_bytes(T, Hq) bytes, any contents */
+  void* workspace;                    /* flamia_bwd_workspace_bytes(...) bytes, 256-byte aligned,
+                                         any contents */
   size_t workspace_bytes;
   int32_t causal_dq_scale;            /* 0: sequence-wide prescale (default); 1: causal */
   int16_t* dq_exp_out;                /* optional out: pi as int16 [Hq, T] (0 on invalid rows) */
 } flamia_bwd_args;
 
-/* Host.  Workspace bytes for T tokens and Hq query heads (pi table, turn counters, a status
- * word).  The dQ FP16 accumulator lives in the dq output itself. */
-size_t flamia_bwd_workspace_bytes(int32_t T, int32_t Hq);
+/* Host.  Workspace bytes of a backward over these documents: a status word, pi [Hq, T],
+ * n_docs + 1 block offsets and, per query head, 8200 bytes for each 64-query x 128-key block
+ * on or below the diagonal of every document longer than 128 tokens.  cu_seqlens_host is a
+ * HOST copy of cu_seqlens (may be NULL only when n_docs == 0).  Returns 0 on bad arguments. */
+size_t flamia_bwd_workspace_bytes(const int32_t* cu_seqlens_host, int32_t n_docs, int32_t T, int32_t Hq);
 
-/* Errors: NULL pointers, sizes, d, head ratio, small workspace. */
+/* Errors: NULL pointers, sizes, d, head ratio, workspace smaller than its fixed part (status
+ * word, pi table, block offsets).  A dShat store that does not fit is reported on the device
+ * (status word 2, see above). */
 flamia_status flamia_bwd(const flamia_bwd_args* args, void* stream);
 
 /* Host.  Number of compute units of the current device, the persistent grid used by

@@ -45,7 +45,8 @@ class _BwdArgs(ctypes.Structure):
                 ("lse", ctypes.c_void_p), ("D", ctypes.c_void_p),
                 ("T", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32), ("d", ctypes.c_int32),
                 ("softmax_scale", ctypes.c_float), ("cu_seqlens", ctypes.c_void_p), ("n_docs", ctypes.c_int32),
-                ("bwd_list", ctypes.c_void_p), ("dq", ctypes.c_void_p), ("dk", ctypes.c_void_p), ("dv", ctypes.c_void_p),
+                ("fwd_list", ctypes.c_void_p), ("bwd_list", ctypes.c_void_p),
+                ("dq", ctypes.c_void_p), ("dk", ctypes.c_void_p), ("dv", ctypes.c_void_p),
                 ("dq_stride_t", ctypes.c_int64), ("dq_stride_h", ctypes.c_int64),
                 ("dk_stride_t", ctypes.c_int64), ("dk_stride_h", ctypes.c_int64),
                 ("dv_stride_t", ctypes.c_int64), ("dv_stride_h", ctypes.c_int64),
@@ -81,7 +82,7 @@ def load_library(path=LIB_PATH):
     lib.flamia_bwd.restype = ctypes.c_int
     lib.flamia_bwd.argtypes = [ctypes.POINTER(_BwdArgs), ctypes.c_void_p]
     lib.flamia_bwd_workspace_bytes.restype = ctypes.c_size_t
-    lib.flamia_bwd_workspace_bytes.argtypes = [ctypes.c_int32, ctypes.c_int32]
+    lib.flamia_bwd_workspace_bytes.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
     lib.flamia_num_workers.restype = ctypes.c_int32
     lib.flamia_num_workers.argtypes = []
     _lib = lib
@@ -195,9 +196,20 @@ def fwd(q, k, v, cu_seqlens, fwd_list, softmax_scale=None, out=None):
     return o, lse
 
 
-def bwd(q, k, v, do, lse, D, cu_seqlens, bwd_list, softmax_scale=None, causal_dq_scale=False, want_pi=False,
+def bwd_workspace_bytes(cu_seqlens_host, T, Hq):
+    """Workspace bytes of a backward (cu_seqlens_host: host int32 array or CPU tensor)."""
+    import numpy as np
+    cu = np.ascontiguousarray(np.asarray(cu_seqlens_host, dtype=np.int32))
+    n_docs = cu.size - 1
+    ptr = cu.ctypes.data_as(ctypes.c_void_p) if n_docs > 0 else None
+    return int(load_library().flamia_bwd_workspace_bytes(ptr, n_docs, int(T), int(Hq)))
+
+
+def bwd(q, k, v, do, lse, D, cu_seqlens, lists, softmax_scale=None, causal_dq_scale=False, want_pi=False,
         workspace=None):
-    """Backward on quantised operands.  q, k, v, do are (codes, scales) pairs; lse, D f32 [Hq, T].
+    """Backward on quantised operands.  q, k, v, do are (codes, scales) pairs; lse, D f32 [Hq, T];
+    lists: the micro-batch's Lists.  workspace: a uint8 CUDA tensor of at least
+    bwd_workspace_bytes(...) bytes, or None to allocate one.
     Returns (dq, dk, dv) BF16, plus the prescale exponents pi int16 [Hq, T] if want_pi."""
     lib = load_library()
     n_docs = _check_cu(cu_seqlens)
@@ -208,13 +220,13 @@ def bwd(q, k, v, do, lse, D, cu_seqlens, bwd_list, softmax_scale=None, causal_dq
     dq = torch.empty((T, Hq, d), dtype=torch.bfloat16, device=dev)
     dk = torch.empty((T, Hkv, d), dtype=torch.bfloat16, device=dev)
     dv = torch.empty((T, Hkv, d), dtype=torch.bfloat16, device=dev)
-    nbytes = lib.flamia_bwd_workspace_bytes(T, Hq)
-    if workspace is None or workspace.numel() < nbytes:
-        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    if workspace is None:
+        workspace = torch.empty(bwd_workspace_bytes(lists.cu_host, T, Hq), dtype=torch.uint8, device=dev)
     pi = torch.empty((Hq, T), dtype=torch.int16, device=dev) if want_pi else None
     a = _BwdArgs(qc.data_ptr(), kc.data_ptr(), vc.data_ptr(), dc.data_ptr(),
                  qs.data_ptr(), ks.data_ptr(), vs.data_ptr(), dsc.data_ptr(), lse.data_ptr(), D.data_ptr(),
-                 T, Hq, Hkv, d, float(softmax_scale or 0.0), cu_seqlens.data_ptr(), n_docs, bwd_list.data_ptr(),
+                 T, Hq, Hkv, d, float(softmax_scale or 0.0), cu_seqlens.data_ptr(), n_docs,
+                 lists.fwd.data_ptr(), lists.bwd.data_ptr(),
                  dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), dq.stride(0), dq.stride(1), dk.stride(0), dk.stride(1),
                  dv.stride(0), dv.stride(1), workspace.data_ptr(), workspace.numel(), int(bool(causal_dq_scale)),
                  pi.data_ptr() if pi is not None else None)
@@ -222,19 +234,20 @@ def bwd(q, k, v, do, lse, D, cu_seqlens, bwd_list, softmax_scale=None, causal_dq
     return (dq, dk, dv, pi) if want_pi else (dq, dk, dv)
 
 
-def bwd_status(workspace, T, Hq):
-    """Status word of the last backward that used `workspace` (0 = ok; bit 0 = a turn wait gave up)."""
-    pi_bytes = (T * Hq * 2 + 255) // 256 * 256
-    cnt_bytes = (T * Hq * 4 + 255) // 256 * 256
-    return int(workspace[pi_bytes + cnt_bytes:pi_bytes + cnt_bytes + 4].view(torch.int32).item())
+def bwd_status(workspace):
+    """Status word of the last backward that used `workspace` (0 = ok; 2 = the dShat store did
+    not fit the workspace)."""
+    return int(workspace[:4].view(torch.int32).item())
 
 
 class Lists:
-    """Forward and backward work lists of one micro-batch (built once, reused by every layer)."""
+    """Forward and backward work lists of one micro-batch (built once, reused by every layer),
+    and a host copy of cu_seqlens for sizing the backward workspace."""
 
     def __init__(self, cu_seqlens, T):
         self.fwd = build_worklist(cu_seqlens, T, FLAMIA_LIST_FWD)
         self.bwd = build_worklist(cu_seqlens, T, FLAMIA_LIST_BWD)
+        self.cu_host = cu_seqlens.cpu().numpy()
 
 
 def training_call(q, k, v, do, cu_seqlens, lists=None, softmax_scale=None, causal_dq_scale=False):
@@ -246,5 +259,5 @@ def training_call(q, k, v, do, cu_seqlens, lists=None, softmax_scale=None, causa
     qz, kz, vz = quantize([q, k, v], cu_seqlens)
     o, lse = fwd(qz, kz, vz, cu_seqlens, lists.fwd, softmax_scale)
     dc, dsc, D = quantize_do(do, o, cu_seqlens)
-    dq, dk, dv = bwd(qz, kz, vz, (dc, dsc), lse, D, cu_seqlens, lists.bwd, softmax_scale, causal_dq_scale)
+    dq, dk, dv = bwd(qz, kz, vz, (dc, dsc), lse, D, cu_seqlens, lists, softmax_scale, causal_dq_scale)
     return dict(o=o, lse=lse, dq=dq, dk=dk, dv=dv)

@@ -3,24 +3,37 @@
 //  §3.3 recomputation with the same quantised operands and block-scaled dS, §3.4 backward pass,
 //  packed documents and work scheduling).
 //
-// Prologue (one workgroup per query head): the dQ prescale exponent pi of every row, zeroed
-// turn counters, zero gradients on rows outside every document.
+// Three launches.
 //
-// Main kernel: persistent grid, one 256-thread workgroup per compute unit.  A work unit is
-// (backward item = 128-key tile of a document, KV head).  Wave w owns keys 32w..32w+31; K^T and
-// V for those keys stay in registers as MFMA operands, dK^T and dV^T accumulate in registers
-// over all query heads of the group and all 64-query steps from the diagonal to the document
-// end.  Per step:
+// Prologue: one workgroup per query head computes the dQ prescale exponent pi of every row and
+// zeroes the gradients of rows outside every document; one more workgroup lays out the dShat
+// store (a prefix sum over documents) and checks that it fits the workspace.
+//
+// Key-stationary kernel (dK, dV, dShat): persistent grid, one 256-thread workgroup per compute
+// unit.  A work unit is (backward item = 128-key tile kappa of a document, KV head).  Wave w owns
+// keys 32w..32w+31; K^T and V for those keys stay in registers as MFMA operands, dK^T and dV^T
+// accumulate in registers over all query heads of the group and all 64-query steps from the
+// diagonal to the document end.  Per step:
 //   S  (queries x keys) = Q K^T  and  dP = dO V^T          (A from the row-major Q / dO tiles)
 //     -> the score t is bit-identical to the forward's: same codes, scales, instruction and
 //        K ordering (the instruction gives identical results with its operands swapped);
 //   P = 2^(t - LSE), dS = P (dP - D); each wave's 32x32 blocks of P and dS get a round-up E8M0
 //     exponent from a wave-wide amax and E4M3 codes, already in operand order;
 //   dV^T += dO^T Phat,  dK^T += Q^T dShat                   (A via transpose reads of the tiles)
-//   dQ^T  = K^T dShat^T over the 128 keys                   (dShat staged in LDS [key][query])
-//   dQ partial -> FP16 (x 2^pi), added in place in the dq buffer in ascending key-tile order,
-//     enforced by a per-(head, query tile) turn counter; the diagonal tile's unit is the last
-//     contributor and writes the BF16 result.
+//   dShat codes and exponents -> workspace, one 8 KiB block per (64-query tile, key tile, head).
+// Steps whose 64 x 128 pairs are all visible skip the mask.  The Q / dO tiles of the next step
+// are loaded while the current one computes (two LDS buffers, one barrier per step).
+// A document with a single key tile has only one dQ contribution per row: its unit computes
+// dQ = K^T dShat^T itself (dShat staged in LDS) and writes it, and nothing is stored.
+//
+// Query-stationary kernel (dQ of documents with two or more key tiles): a work unit is
+// (forward item = 256 queries of a document, query head); wave w owns 32 queries.  Over the key
+// tiles kappa = 0, 1, ... in ascending order it reads the stored dShat blocks and the K tile,
+// forms partial = K^T dShat^T (FP32) and accumulates acc16 = FP16(acc16 + FP16(2^pi partial))
+// in registers; at the end dQ = BF16(softmax_scale 2^-pi acc16).  The reduction order is fixed,
+// so results are bit-reproducible, and no workgroup waits for another.
+#include <type_traits>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -29,28 +42,38 @@ namespace flamia {
 namespace {
 
 constexpr int BWD_THREADS = 256;
-constexpr int QT = 64;  // queries per step
-constexpr int SPIN_LIMIT = 1 << 20;  // polls (~0.1 s) before a turn wait gives up and flags an error
+constexpr int QT = 64;                 // queries per step / per stored dShat block
+constexpr int DS_BLOCK = KV_TILE * QT;  // bytes of one stored dShat block
+constexpr int DQ_WAVES = 8;
+constexpr int DQ_THREADS = 64 * DQ_WAVES;
+
+// Stored dShat block of (key tile kappa, query tile qt >= 2 kappa) of a document with n_qt query
+// tiles whose blocks start at `base`: blocks are ordered by key tile, then query tile.
+__device__ __forceinline__ int64_t ds_block(int64_t base, int kappa, int n_qt, int qt) {
+  return base + (int64_t)kappa * n_qt - (int64_t)kappa * (kappa - 1) + (qt - 2 * kappa);
+}
+
+// Query offset (within a 64-query tile) held at byte position pos of a stored dShat row: the
+// row of key j holds, for lane group hh of the wave that owns j, the 32 bytes of its P-operand
+// register order (query 32 qb + 8 w4 + 4 hh + e in byte 4 (4 qb + w4) + e).
+__device__ __forceinline__ int ds_pos_query(int pos) {
+  const int s = pos >> 5, n = pos & 31;
+  return 32 * (n >> 4) + 8 * ((n >> 2) & 3) + 4 * s + (n & 3);
+}
 
 template <int D>
 struct BwdSmem {
+  uint8_t q[2][QT * D];
+  uint8_t dO[2][QT * D];
   uint8_t k[KV_TILE * D];
-  uint8_t q[QT * D];
-  uint8_t dO[QT * D];
-  uint8_t ds[KV_TILE * QT];
+  uint8_t ds[KV_TILE * QT];  // dShat [key][query], single-tile documents only
   uint8_t sk[KV_TILE];
-  float lse[QT];
-  float dd[QT];
-  int pi[QT];
-  int sq[2], sdo[2];
+  float lse[2][QT];
+  float dd[2][QT];
+  int pi[2][QT];
+  int sq[2][2], sdo[2][2];
   int ds_scale[2][4];
 };
-
-__device__ __forceinline__ uint32_t pack_half2(_Float16 a, _Float16 b) {
-  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
-}
-__device__ __forceinline__ _Float16 half_lo(uint32_t w) { return __builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFF)); }
-__device__ __forceinline__ _Float16 half_hi(uint32_t w) { return __builtin_bit_cast(_Float16, (uint16_t)(w >> 16)); }
 
 // One step's Q / dO rows and row statistics, held in registers between the global loads
 // (issued one step ahead) and the LDS stores.
@@ -60,7 +83,6 @@ struct StepRegs {
   uint4 q[CH], dO[CH];
   float lse, dd;
   int pi, sq, sdo;
-  int q0;
 };
 
 template <int D>
@@ -68,7 +90,6 @@ __device__ __forceinline__ void load_step(StepRegs<D>& r, const BwdParams& p, in
   const int tid = threadIdx.x;
   constexpr int CPR = D / 16;
   const int q0 = QT * qt;
-  r.q0 = q0;
 #pragma unroll
   for (int i = 0; i < StepRegs<D>::CH; ++i) {
     const int chunk = tid + i * BWD_THREADS;
@@ -102,23 +123,23 @@ __device__ __forceinline__ void load_step(StepRegs<D>& r, const BwdParams& p, in
 }
 
 template <int D>
-__device__ __forceinline__ void store_step(const StepRegs<D>& r, BwdSmem<D>& sm) {
+__device__ __forceinline__ void store_step(const StepRegs<D>& r, BwdSmem<D>& sm, int b) {
   const int tid = threadIdx.x;
   constexpr int CPR = D / 16;
 #pragma unroll
   for (int i = 0; i < StepRegs<D>::CH; ++i) {
     const int chunk = tid + i * BWD_THREADS;
     const int row = chunk / CPR, col = (chunk % CPR) * 16;
-    *reinterpret_cast<uint4*>(&sm.q[lds_off<D>(row, col)]) = r.q[i];
-    *reinterpret_cast<uint4*>(&sm.dO[lds_off<D>(row, col)]) = r.dO[i];
+    *reinterpret_cast<uint4*>(&sm.q[b][lds_off<D>(row, col)]) = r.q[i];
+    *reinterpret_cast<uint4*>(&sm.dO[b][lds_off<D>(row, col)]) = r.dO[i];
   }
   if (tid < QT) {
-    sm.lse[tid] = r.lse;
-    sm.dd[tid] = r.dd;
-    sm.pi[tid] = r.pi;
+    sm.lse[b][tid] = r.lse;
+    sm.dd[b][tid] = r.dd;
+    sm.pi[b][tid] = r.pi;
   } else if (tid < QT + 2) {
-    sm.sq[tid - QT] = r.sq;
-    sm.sdo[tid - QT] = r.sdo;
+    sm.sq[b][tid - QT] = r.sq;
+    sm.sdo[b][tid - QT] = r.sdo;
   }
 }
 
@@ -128,6 +149,7 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
   constexpr int NDB = D / 32;
   __shared__ BwdSmem<D> sm;
 
+  if (*p.status) return;  // the dShat store does not fit the workspace
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int n = lane & 31, hh = lane >> 5;
@@ -147,11 +169,21 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
     const int doc = it.x, kappa = it.y;
     const int doc_start = p.cu[doc];
     const int L = p.cu[doc + 1] - doc_start;
+    const int n_qt = (L + QT - 1) / QT;
+    const bool store_ds = L > KV_TILE;  // two or more key tiles: dQ in the query-stationary kernel
+    const int64_t ds_base = store_ds ? p.doc_base[doc] : 0;
     const int key_rel = KV_TILE * kappa + 32 * wave + n;
     const bool key_valid = key_rel < L;
 
-    // ---- K tile into LDS, stationary K / V operands into registers
+    // Steps run over (query head of the group, 64-query tile from the diagonal to the
+    // document end).
+    const int nq = n_qt - 2 * kappa;  // query tiles per head
+    const int n_steps = grp * nq;
+
+    // ---- K tile and the first step's tiles into LDS
     __syncthreads();  // the previous unit no longer reads LDS
+    StepRegs<D> pre;
+    load_step<D>(pre, p, doc_start, L, g * grp, 2 * kappa);
     {
       constexpr int CPR = D / 16;
       for (int chunk = tid; chunk < KV_TILE * CPR; chunk += BWD_THREADS) {
@@ -166,6 +198,7 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
         sm.sk[tid] = key < L ? p.sk[(int64_t)g * T + doc_start + key] : (uint8_t)127;
       }
     }
+    store_step<D>(pre, sm, 0);
     __syncthreads();
     v8i kop[NC], vop[NC];
     const int k_scale = sm.sk[32 * wave + n];
@@ -192,181 +225,144 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
 #pragma unroll
     for (int db = 0; db < NDB; ++db) { dkacc[db] = v16f{}; dvacc[db] = v16f{}; }
 
-    // Steps run over (query head of the group, 64-query tile from the diagonal to the
-    // document end).  The next step's Q / dO tiles and row statistics are loaded into
-    // registers while the current step computes.
-    const int n_qt = (L + QT - 1) / QT - 2 * kappa;  // query tiles per head
-    const int n_steps = grp * n_qt;
-    StepRegs<D> pre;
-    load_step<D>(pre, p, doc_start, L, g * grp, 2 * kappa);
     for (int st = 0; st < n_steps; ++st) {
-      const int hi = st / n_qt;
+      const int b = st & 1;
+      const int hi = st / nq;
       const int h = g * grp + hi;
-      const int qt = 2 * kappa + (st - hi * n_qt);
+      const int qt = 2 * kappa + (st - hi * nq);
       const int q0 = QT * qt;
-      __syncthreads();  // previous step's LDS readers are done
-      store_step<D>(pre, sm);
-      __syncthreads();
       if (st + 1 < n_steps) {
-        const int hn = (st + 1) / n_qt;
-        load_step<D>(pre, p, doc_start, L, g * grp + hn, 2 * kappa + (st + 1 - hn * n_qt));
+        const int hn = (st + 1) / nq;
+        load_step<D>(pre, p, doc_start, L, g * grp + hn, 2 * kappa + (st + 1 - hn * nq));
       }
+
+      // ---- S, dP, P, dS and the E4M3 operands of this wave's 32 keys x 64 queries
+      int pp[8], pd[8];
+      int sp[2], sds[2];
+      auto scores = [&](auto masked) {
+        constexpr bool MASK = decltype(masked)::value;
+        v16f sacc[2], pacc[2];
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          sacc[qb] = v16f{};
+          pacc[qb] = v16f{};
+#pragma unroll
+          for (int cc = 0; cc < NC; ++cc) {
+            const v8i aq = lds_read_row32<D>(sm.q[b], 32 * qb + n, 64 * cc + 32 * hh);
+            sacc[qb] = mfma_scaled(aq, kop[cc], sacc[qb], sm.sq[b][qb], k_scale);
+            const v8i ad = lds_read_row32<D>(sm.dO[b], 32 * qb + n, 64 * cc + 32 * hh);
+            pacc[qb] = mfma_scaled(ad, vop[cc], pacc[qb], sm.sdo[b][qb], v_scale);
+          }
+          mfma_drain(sacc[qb]);
+          mfma_drain(pacc[qb]);
+        }
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          float pmax = 0.f, dmax = 0.f;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int qi = 32 * qb + acc_row(i, hh);
+            float pv = __builtin_amdgcn_exp2f(fmaf(sacc[qb][i], c, -sm.lse[b][qi]));
+            if constexpr (MASK) {
+              const int qr = q0 + qi;
+              pv = (key_rel <= qr && qr < L) ? pv : 0.f;
+            }
+            const float dsv = pv * (pacc[qb][i] - sm.dd[b][qi]);
+            sacc[qb][i] = pv;
+            pacc[qb][i] = dsv;
+            pmax = fmaxf(pmax, pv);
+            dmax = fmaxf(dmax, fabsf(dsv));
+          }
+          sp[qb] = e8m0_roundup(wave_max(pmax));
+          sds[qb] = e8m0_roundup(wave_max(dmax));
+          const float fp = exp2i_neg(sp[qb]), fd = exp2i_neg(sds[qb]);
+#pragma unroll
+          for (int w4 = 0; w4 < 4; ++w4) {
+            pp[4 * qb + w4] = pack4_fp8(sacc[qb][4 * w4] * fp, sacc[qb][4 * w4 + 1] * fp, sacc[qb][4 * w4 + 2] * fp,
+                                        sacc[qb][4 * w4 + 3] * fp);
+            pd[4 * qb + w4] = pack4_fp8(pacc[qb][4 * w4] * fd, pacc[qb][4 * w4 + 1] * fd, pacc[qb][4 * w4 + 2] * fd,
+                                        pacc[qb][4 * w4 + 3] * fd);
+          }
+        }
+      };
+      // all 64 x 128 pairs visible: the query tile lies wholly below the key tile and inside
+      // the document (then every key of the tile is inside it too)
+      if (qt >= 2 * kappa + 2 && q0 + QT <= L) scores(std::false_type{});
+      else scores(std::true_type{});
+
+      // ---- dV^T += dO^T Phat, dK^T += Q^T dShat
       {
-          // ---- S and dP for this wave's 32 keys x 64 queries
-          v16f sacc[2], pacc[2];
-  #pragma unroll
-          for (int qb = 0; qb < 2; ++qb) {
-            sacc[qb] = v16f{};
-            pacc[qb] = v16f{};
-  #pragma unroll
-            for (int cc = 0; cc < NC; ++cc) {
-              const v8i aq = lds_read_row32<D>(sm.q, 32 * qb + n, 64 * cc + 32 * hh);
-              sacc[qb] = mfma_scaled(aq, kop[cc], sacc[qb], sm.sq[qb], k_scale);
-              const v8i ad = lds_read_row32<D>(sm.dO, 32 * qb + n, 64 * cc + 32 * hh);
-              pacc[qb] = mfma_scaled(ad, vop[cc], pacc[qb], sm.sdo[qb], v_scale);
-            }
-            mfma_drain(sacc[qb]);
-            mfma_drain(pacc[qb]);
-          }
-          // ---- P, dS, block exponents, E4M3 operands
-          int pp[8], pd[8];
-          int sp[2], sds[2];
-  #pragma unroll
-          for (int qb = 0; qb < 2; ++qb) {
-            float pmax = 0.f, dmax = 0.f;
-  #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int qr = q0 + 32 * qb + acc_row(i, hh);
-              const bool vis = key_rel <= qr && qr < L;
-              const int qi = 32 * qb + acc_row(i, hh);
-              const float pv = vis ? __builtin_amdgcn_exp2f(fmaf(sacc[qb][i], c, -sm.lse[qi])) : 0.f;
-              const float dsv = pv * (pacc[qb][i] - sm.dd[qi]);
-              sacc[qb][i] = pv;
-              pacc[qb][i] = dsv;
-              pmax = fmaxf(pmax, pv);
-              dmax = fmaxf(dmax, fabsf(dsv));
-            }
-            sp[qb] = e8m0_roundup(wave_max(pmax));
-            sds[qb] = e8m0_roundup(wave_max(dmax));
-            const float fp = exp2i_neg(sp[qb]), fd = exp2i_neg(sds[qb]);
-  #pragma unroll
-            for (int w4 = 0; w4 < 4; ++w4) {
-              pp[4 * qb + w4] = pack4_fp8(sacc[qb][4 * w4] * fp, sacc[qb][4 * w4 + 1] * fp, sacc[qb][4 * w4 + 2] * fp,
-                                          sacc[qb][4 * w4 + 3] * fp);
-              pd[4 * qb + w4] = pack4_fp8(pacc[qb][4 * w4] * fd, pacc[qb][4 * w4 + 1] * fd, pacc[qb][4 * w4 + 2] * fd,
-                                          pacc[qb][4 * w4 + 3] * fd);
-              // dS codes to LDS as [key][query]: 4 consecutive queries per dword
-              const int qcol = 32 * qb + 8 * w4 + 4 * hh;
-              *reinterpret_cast<int*>(&sm.ds[lds_off<QT>(32 * wave + n, qcol)]) = pd[4 * qb + w4];
-            }
-            if (lane == 0) sm.ds_scale[qb][wave] = sds[qb] + 127;
-          }
-          // ---- dV^T += dO^T Phat, dK^T += Q^T dShat
-          {
-            v8i bp, bd;
-  #pragma unroll
-            for (int w = 0; w < 8; ++w) { bp[w] = pp[w]; bd[w] = pd[w]; }
-            const int sdo_h = sm.sdo[hh], sq_h = sm.sq[hh];
-            const int sp_h = (hh ? sp[1] : sp[0]) + 127, sds_h = (hh ? sds[1] : sds[0]) + 127;
-  #pragma unroll
-            for (int db = 0; db < NDB; ++db) {
-              const v8i ado = lds_read_tr32<D>(sm.dO, 0, 32 * db, lane);
-              dvacc[db] = mfma_scaled(ado, bp, dvacc[db], sdo_h, sp_h);
-              const v8i aq = lds_read_tr32<D>(sm.q, 0, 32 * db, lane);
-              dkacc[db] = mfma_scaled(aq, bd, dkacc[db], sq_h, sds_h);
-            }
-          }
-          __syncthreads();  // dShat tile and its exponents are complete
-
-          // ---- dQ^T = K^T dShat^T for this wave's slice
-          constexpr int NQB = (D == 128) ? 2 : 1;
-          const int dblk = (D == 128) ? wave : (wave & 1);
-          const int qb0 = (D == 128) ? 0 : (wave >> 1);
-          v16f dq[NQB];
-  #pragma unroll
-          for (int x = 0; x < NQB; ++x) {
-            const int qb = qb0 + x;
-            dq[x] = v16f{};
-  #pragma unroll
-            for (int ci = 0; ci < 2; ++ci) {
-              const v8i ak = lds_read_tr32<D>(sm.k, 64 * ci, 32 * dblk, lane);
-              const v8i bs = lds_read_tr32<QT>(sm.ds, 64 * ci, 32 * qb, lane);
-              dq[x] = mfma_scaled(ak, bs, dq[x], sm.sk[64 * ci + 32 * hh], sm.ds_scale[qb][2 * ci + hh]);
-            }
-            mfma_drain(dq[x]);
-          }
-
-          // ---- ordered FP16 accumulation of the partial sums (ascending key tiles)
-          int32_t* cnt = p.counters + (int64_t)h * T + doc_start + q0;
-          if (tid == 0 && kappa > 0) {
-            int spins = 0;
-            while (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != kappa) {
-              __builtin_amdgcn_s_sleep(4);
-              // give up after the limit, or at once if another wait already gave up
-              if (++spins > SPIN_LIMIT || __hip_atomic_load(p.status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
-                atomicOr(p.status, 1);
-                break;
-              }
-            }
-          }
-          __syncthreads();
-          const bool last = (kappa == qt / 2);
-          // read all previous sums first (one memory round trip), then add and store
-          uint64_t old[NQB][4];
-  #pragma unroll
-          for (int x = 0; x < NQB; ++x) {
-            const int qr = q0 + 32 * (qb0 + x) + n;
-  #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              old[x][j] = 0;
-              if (kappa > 0 && qr < L) {
-                const uint16_t* row = p.dq + (int64_t)(doc_start + qr) * p.dqst + (int64_t)h * p.dqsh;
-                old[x][j] = __hip_atomic_load(reinterpret_cast<const uint64_t*>(row + 32 * dblk + 8 * j + 4 * hh),
-                                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-              }
-            }
-          }
-  #pragma unroll
-          for (int x = 0; x < NQB; ++x) {
-            const int qb = qb0 + x;
-            const int qi = 32 * qb + n;
-            const int qr = q0 + qi;
-            if (qr < L) {
-              const int pi = sm.pi[qi];
-              const float up = exp2i(pi), down = exp2i(-pi) * p.softmax_scale;
-              uint16_t* row = p.dq + (int64_t)(doc_start + qr) * p.dqst + (int64_t)h * p.dqsh;
-  #pragma unroll
-              for (int j = 0; j < 4; ++j) {
-                const int d0 = 32 * dblk + 8 * j + 4 * hh;
-                uint64_t* ptr = reinterpret_cast<uint64_t*>(row + d0);
-                _Float16 a0 = (_Float16)(dq[x][4 * j + 0] * up), a1 = (_Float16)(dq[x][4 * j + 1] * up);
-                _Float16 a2 = (_Float16)(dq[x][4 * j + 2] * up), a3 = (_Float16)(dq[x][4 * j + 3] * up);
-                if (kappa > 0) {
-                  const uint32_t lo = (uint32_t)old[x][j], hi2 = (uint32_t)(old[x][j] >> 32);
-                  a0 = half_lo(lo) + a0;
-                  a1 = half_hi(lo) + a1;
-                  a2 = half_lo(hi2) + a2;
-                  a3 = half_hi(hi2) + a3;
-                }
-                if (last) {
-                  uint2 w;
-                  w.x = pack_bf16((float)a0 * down, (float)a1 * down);
-                  w.y = pack_bf16((float)a2 * down, (float)a3 * down);
-                  *reinterpret_cast<uint2*>(ptr) = w;
-                } else {
-                  const uint64_t nw = (uint64_t)pack_half2(a0, a1) | ((uint64_t)pack_half2(a2, a3) << 32);
-                  __hip_atomic_store(ptr, nw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                }
-              }
-            }
-          }
-          // The partial sums are device-coherent atomics (loads and stores bypass the non-coherent
-          // cache levels), so no cache-wide write-back or invalidation is needed: the turn is
-          // handed on once every lane's stores have completed.
-          __builtin_amdgcn_s_waitcnt(0);
-          __syncthreads();
-          if (tid == 0 && !last) __hip_atomic_store(cnt, kappa + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        v8i bp, bd;
+#pragma unroll
+        for (int w = 0; w < 8; ++w) { bp[w] = pp[w]; bd[w] = pd[w]; }
+        const int sdo_h = sm.sdo[b][hh], sq_h = sm.sq[b][hh];
+        const int sp_h = (hh ? sp[1] : sp[0]) + 127, sds_h = (hh ? sds[1] : sds[0]) + 127;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const v8i ado = lds_read_tr32<D>(sm.dO[b], 0, 32 * db, lane);
+          dvacc[db] = mfma_scaled(ado, bp, dvacc[db], sdo_h, sp_h);
+          const v8i aq = lds_read_tr32<D>(sm.q[b], 0, 32 * db, lane);
+          dkacc[db] = mfma_scaled(aq, bd, dkacc[db], sq_h, sds_h);
+        }
       }
+
+      if (store_ds) {
+        // ---- dShat block: key row j holds 64 bytes, lane group hh's 32 bytes at 32 hh
+        const int64_t blk = ds_block(ds_base, kappa, n_qt, qt) * p.Hq + h;
+        uint4* dst = reinterpret_cast<uint4*>(p.ds_codes + blk * DS_BLOCK + (32 * wave + n) * QT + 32 * hh);
+        dst[0] = make_uint4(pd[0], pd[1], pd[2], pd[3]);
+        dst[1] = make_uint4(pd[4], pd[5], pd[6], pd[7]);
+        if (lane == 0) {
+          p.ds_scales[blk * 8 + wave] = (uint8_t)(sds[0] + 127);
+          p.ds_scales[blk * 8 + 4 + wave] = (uint8_t)(sds[1] + 127);
+        }
+      } else {
+        // ---- single key tile: dQ^T = K^T dShat^T here, the only contribution of its rows
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+#pragma unroll
+          for (int w4 = 0; w4 < 4; ++w4) {
+            const int qcol = 32 * qb + 8 * w4 + 4 * hh;
+            *reinterpret_cast<int*>(&sm.ds[lds_off<QT>(32 * wave + n, qcol)]) = pd[4 * qb + w4];
+          }
+          if (lane == 0) sm.ds_scale[qb][wave] = sds[qb] + 127;
+        }
+        __syncthreads();  // dShat tile and its exponents are complete
+        constexpr int NQB = (D == 128) ? 2 : 1;
+        const int dblk = (D == 128) ? wave : (wave & 1);
+        const int qb0 = (D == 128) ? 0 : (wave >> 1);
+#pragma unroll
+        for (int x = 0; x < NQB; ++x) {
+          const int qb = qb0 + x;
+          v16f dq = v16f{};
+#pragma unroll
+          for (int ci = 0; ci < 2; ++ci) {
+            const v8i ak = lds_read_tr32<D>(sm.k, 64 * ci, 32 * dblk, lane);
+            const v8i bs = lds_read_tr32<QT>(sm.ds, 64 * ci, 32 * qb, lane);
+            dq = mfma_scaled(ak, bs, dq, sm.sk[64 * ci + 32 * hh], sm.ds_scale[qb][2 * ci + hh]);
+          }
+          mfma_drain(dq);
+          const int qi = 32 * qb + n;
+          const int qr = q0 + qi;
+          if (qr < L) {
+            const int pi = sm.pi[b][qi];
+            const float up = exp2i(pi), down = exp2i(-pi) * p.softmax_scale;
+            uint16_t* row = p.dq + (int64_t)(doc_start + qr) * p.dqst + (int64_t)h * p.dqsh;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const _Float16 a0 = (_Float16)(dq[4 * j + 0] * up), a1 = (_Float16)(dq[4 * j + 1] * up);
+              const _Float16 a2 = (_Float16)(dq[4 * j + 2] * up), a3 = (_Float16)(dq[4 * j + 3] * up);
+              uint2 w;
+              w.x = pack_bf16((float)a0 * down, (float)a1 * down);
+              w.y = pack_bf16((float)a2 * down, (float)a3 * down);
+              *reinterpret_cast<uint2*>(row + 32 * dblk + 8 * j + 4 * hh) = w;
+            }
+          }
+        }
+      }
+
+      if (st + 1 < n_steps) store_step<D>(pre, sm, b ^ 1);
+      __syncthreads();  // this step's LDS readers are done; the next step's tiles are stored
     }
 
     // ---- dK, dV of this wave's keys
@@ -394,7 +390,189 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
 }
 
 // ------------------------------------------------------------------------------------------
-// Prologue: pi per (head, row), zeroed turn counters, zero rows outside every document.
+// Query-stationary dQ.
+template <int D>
+struct DqSmem {
+  uint8_t k[2][KV_TILE * D];
+  uint8_t ds[2][4][DS_BLOCK];
+  uint8_t sk[2][KV_TILE];
+  uint8_t dsc[2][4][8];
+};
+
+// The next key tile's K rows, dShat blocks and exponents, in registers between the global loads
+// and the LDS stores.
+template <int D>
+struct DqRegs {
+  static constexpr int KCH = KV_TILE * D / 16 / DQ_THREADS;  // K chunks per thread
+  static constexpr int SCH = 4 * DS_BLOCK / 16 / DQ_THREADS;  // dShat chunks per thread
+  uint4 k[KCH], s[SCH];
+  uint2 sc;       // threads 0..3: exponents of query tile `tid`
+  uint32_t skb;   // threads 0..127: K scale byte of key `tid`
+};
+
+template <int D>
+__device__ __forceinline__ void dq_load(DqRegs<D>& r, const BwdParams& p, int doc_start, int L, int n_qt,
+                                        int64_t base, int qt0, int g, int h, int kappa) {
+  const int tid = threadIdx.x;
+  constexpr int CPR = D / 16;
+#pragma unroll
+  for (int i = 0; i < DqRegs<D>::KCH; ++i) {
+    const int chunk = tid + i * DQ_THREADS;
+    const int row = chunk / CPR, col = (chunk % CPR) * 16;
+    const int key = KV_TILE * kappa + row;
+    r.k[i] = make_uint4(0, 0, 0, 0);
+    if (key < L) r.k[i] = *reinterpret_cast<const uint4*>(p.k + ((int64_t)(doc_start + key) * p.Hkv + g) * D + col);
+  }
+#pragma unroll
+  for (int i = 0; i < DqRegs<D>::SCH; ++i) {
+    const int chunk = tid + i * DQ_THREADS;
+    const int t4 = chunk / (DS_BLOCK / 16), within = chunk % (DS_BLOCK / 16);
+    const int qt = qt0 + t4;
+    r.s[i] = make_uint4(0, 0, 0, 0);
+    if (qt < n_qt && qt >= 2 * kappa) {
+      const int64_t blk = ds_block(base, kappa, n_qt, qt) * p.Hq + h;
+      r.s[i] = reinterpret_cast<const uint4*>(p.ds_codes + blk * DS_BLOCK)[within];
+    }
+  }
+  r.sc = make_uint2(0x7F7F7F7Fu, 0x7F7F7F7Fu);
+  if (tid < 4) {
+    const int qt = qt0 + tid;
+    if (qt < n_qt && qt >= 2 * kappa) {
+      const int64_t blk = ds_block(base, kappa, n_qt, qt) * p.Hq + h;
+      r.sc = *reinterpret_cast<const uint2*>(p.ds_scales + blk * 8);
+    }
+  }
+  r.skb = 127;
+  if (tid < KV_TILE) {
+    const int key = KV_TILE * kappa + tid;
+    if (key < L) r.skb = p.sk[(int64_t)g * p.T + doc_start + key];
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void dq_store(const DqRegs<D>& r, DqSmem<D>& sm, int b) {
+  const int tid = threadIdx.x;
+  constexpr int CPR = D / 16;
+#pragma unroll
+  for (int i = 0; i < DqRegs<D>::KCH; ++i) {
+    const int chunk = tid + i * DQ_THREADS;
+    const int row = chunk / CPR, col = (chunk % CPR) * 16;
+    *reinterpret_cast<uint4*>(&sm.k[b][lds_off<D>(row, col)]) = r.k[i];
+  }
+#pragma unroll
+  for (int i = 0; i < DqRegs<D>::SCH; ++i) {
+    const int chunk = tid + i * DQ_THREADS;
+    const int t4 = chunk / (DS_BLOCK / 16), within = chunk % (DS_BLOCK / 16);
+    const int row = within / (QT / 16), col = (within % (QT / 16)) * 16;
+    *reinterpret_cast<uint4*>(&sm.ds[b][t4][lds_off<QT>(row, col)]) = r.s[i];
+  }
+  if (tid < 4) *reinterpret_cast<uint2*>(&sm.dsc[b][tid][0]) = r.sc;
+  if (tid < KV_TILE) sm.sk[b][tid] = (uint8_t)r.skb;
+}
+
+template <int D>
+__global__ __launch_bounds__(DQ_THREADS) void dq_kernel(BwdParams p) {
+  constexpr int NDB = D / 32;
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  __shared__ DqSmem<D> sm;
+
+  if (*p.status) return;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 31, hh = lane >> 5;
+  const int n_items = p.fwd_list[0];
+  const int4* items = reinterpret_cast<const int4*>(p.fwd_list + 4);
+  const int n_units = n_items * p.Hq;
+  const int G = gridDim.x, wg = blockIdx.x;
+  const int grp = p.Hq / p.Hkv;
+  const int t4 = wave >> 1, s = wave & 1;     // query tile of the item, byte-position half
+  const int qrow = ds_pos_query(32 * s + n);  // query offset in the tile held by this lane
+  const int qb_l = n >> 4;                    // its 32-query block
+
+  for (int round = 0;; ++round) {
+    const int u = round * G + ((round & 1) ? (G - 1 - wg) : wg);
+    if (u >= n_units) break;
+    const int4 it = items[u / p.Hq];
+    if (it.z < 2) break;  // single key tile from here on (the list is sorted by cost)
+    const int h = u % p.Hq, g = h / grp;
+    const int doc = it.x, item = it.y;
+    const int doc_start = p.cu[doc];
+    const int L = p.cu[doc + 1] - doc_start;
+    const int n_qt = (L + QT - 1) / QT;
+    const int64_t base = p.doc_base[doc];
+    const int qt0 = (ITEM_Q / QT) * item;
+    const int qt = qt0 + t4;
+    const bool active = qt < n_qt;
+    const int last_qt = min(qt0 + ITEM_Q / QT, n_qt) - 1;
+    const int kappa_hi = last_qt / 2;
+    const int q_rel = QT * qt + qrow;
+    const bool row_valid = q_rel < L;
+    int pi = 0;
+    if (row_valid) pi = p.pi[(int64_t)h * p.T + doc_start + q_rel];
+    const float up = exp2i(pi);
+
+    h2 acc16[NDB][8];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc16[db][j] = h2{0, 0};
+
+    DqRegs<D> pre;
+    __syncthreads();  // the previous unit no longer reads LDS
+    dq_load<D>(pre, p, doc_start, L, n_qt, base, qt0, g, h, 0);
+    dq_store<D>(pre, sm, 0);
+    __syncthreads();
+    for (int kappa = 0; kappa <= kappa_hi; ++kappa) {
+      const int b = kappa & 1;
+      if (kappa < kappa_hi) dq_load<D>(pre, p, doc_start, L, n_qt, base, qt0, g, h, kappa + 1);
+      if (active && qt >= 2 * kappa) {
+        v8i bs[2];
+        int sb[2];
+#pragma unroll
+        for (int ci = 0; ci < 2; ++ci) {
+          bs[ci] = lds_read_tr32<QT>(sm.ds[b][t4], 64 * ci, 32 * s, lane);
+          sb[ci] = sm.dsc[b][t4][4 * qb_l + 2 * ci + hh];
+        }
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          v16f part = v16f{};
+#pragma unroll
+          for (int ci = 0; ci < 2; ++ci) {
+            const v8i ak = lds_read_tr32<D>(sm.k[b], 64 * ci, 32 * db, lane);
+            part = mfma_scaled(ak, bs[ci], part, sm.sk[b][64 * ci + 32 * hh], sb[ci]);
+          }
+          mfma_drain(part);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const h2 x = h2{(_Float16)(part[2 * j] * up), (_Float16)(part[2 * j + 1] * up)};
+            acc16[db][j] = acc16[db][j] + x;
+          }
+        }
+      }
+      if (kappa < kappa_hi) dq_store<D>(pre, sm, b ^ 1);
+      __syncthreads();
+    }
+
+    if (active && row_valid) {
+      const float down = exp2i(-pi) * p.softmax_scale;
+      uint16_t* row = p.dq + (int64_t)(doc_start + q_rel) * p.dqst + (int64_t)h * p.dqsh;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const h2 lo = acc16[db][2 * j], hi2 = acc16[db][2 * j + 1];
+          uint2 w;
+          w.x = pack_bf16((float)lo[0] * down, (float)lo[1] * down);
+          w.y = pack_bf16((float)hi2[0] * down, (float)hi2[1] * down);
+          *reinterpret_cast<uint2*>(row + 32 * db + 8 * j + 4 * hh) = w;
+        }
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// Prologue: pi per (head, row) and zero rows outside every document (workgroups 0..Hq-1);
+// dShat store layout and capacity check (workgroup Hq).
 constexpr int PRO_THREADS = 1024;
 constexpr int PRO_CHUNK = 4 * PRO_THREADS;
 
@@ -405,6 +583,40 @@ __device__ __forceinline__ Seg seg_op(Seg a, Seg b) {
   return Seg{a.f | b.f, b.f ? b.v : max(a.v, b.v), b.f ? b.k : max(a.k, b.k)};
 }
 
+// Stored dShat blocks of a document of length L (none with a single key tile).
+__device__ __forceinline__ int64_t doc_blocks(int L) {
+  const int64_t n_kt = (L + KV_TILE - 1) / KV_TILE, n_qt = (L + QT - 1) / QT;
+  return n_kt >= 2 ? n_kt * n_qt - n_kt * (n_kt - 1) : 0;
+}
+
+__device__ void layout_ds_store(const BwdParams& p) {
+  __shared__ int64_t part[PRO_THREADS];
+  const int tid = threadIdx.x;
+  const int nd = p.n_docs;
+  const int per = (nd + PRO_THREADS - 1) / PRO_THREADS;
+  const int lo = min(nd, tid * per), hi = min(nd, lo + per);
+  int64_t sum = 0;
+  for (int k = lo; k < hi; ++k) sum += doc_blocks(p.cu[k + 1] - p.cu[k]);
+  part[tid] = sum;
+  __syncthreads();
+  for (int off = 1; off < PRO_THREADS; off <<= 1) {  // inclusive scan
+    const int64_t add = tid >= off ? part[tid - off] : 0;
+    __syncthreads();
+    part[tid] += add;
+    __syncthreads();
+  }
+  int64_t run = part[tid] - sum;
+  for (int k = lo; k < hi; ++k) {
+    p.doc_base[k] = run;
+    run += doc_blocks(p.cu[k + 1] - p.cu[k]);
+  }
+  if (tid == PRO_THREADS - 1) {
+    const int64_t total = part[tid];
+    p.doc_base[nd] = total;
+    *p.status = (total * p.Hq > p.ds_capacity) ? 2 : 0;
+  }
+}
+
 template <int D>
 __global__ __launch_bounds__(PRO_THREADS) void bwd_prologue(BwdParams p) {
   __shared__ uint8_t flags[PRO_CHUNK];
@@ -413,6 +625,10 @@ __global__ __launch_bounds__(PRO_THREADS) void bwd_prologue(BwdParams p) {
   __shared__ int kstart;
   __shared__ Seg carry_sh;
 
+  if ((int)blockIdx.x == p.Hq) {
+    layout_ds_store(p);
+    return;
+  }
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = blockIdx.x, grp = p.Hq / p.Hkv, g = h / grp;
   const int T = p.T;
@@ -424,9 +640,7 @@ __global__ __launch_bounds__(PRO_THREADS) void bwd_prologue(BwdParams p) {
   const uint8_t* sk = p.sk + (int64_t)g * T;
   int16_t* pi = p.pi + (int64_t)h * T;
 
-  // zero rows outside every document, zero the turn counters and the status word
-  if (h == 0 && tid == 0) *p.status = 0;
-  for (int t = tid; t < T; t += PRO_THREADS) p.counters[(int64_t)h * T + t] = 0;
+  // zero rows outside every document
   {
     const int n_out = c_lo + (T - c_hi);
     for (int x = tid; x < n_out * D; x += PRO_THREADS) {
@@ -529,11 +743,13 @@ __global__ __launch_bounds__(PRO_THREADS) void bwd_prologue(BwdParams p) {
 
 hipError_t launch_bwd(const BwdParams& p, int d, int grid, hipStream_t s) {
   if (d == 128) {
-    hipLaunchKernelGGL(bwd_prologue<128>, dim3(p.Hq), dim3(PRO_THREADS), 0, s, p);
+    hipLaunchKernelGGL(bwd_prologue<128>, dim3(p.Hq + 1), dim3(PRO_THREADS), 0, s, p);
     hipLaunchKernelGGL(bwd_kernel<128>, dim3(grid), dim3(BWD_THREADS), 0, s, p);
+    hipLaunchKernelGGL(dq_kernel<128>, dim3(grid), dim3(DQ_THREADS), 0, s, p);
   } else {
-    hipLaunchKernelGGL(bwd_prologue<64>, dim3(p.Hq), dim3(PRO_THREADS), 0, s, p);
+    hipLaunchKernelGGL(bwd_prologue<64>, dim3(p.Hq + 1), dim3(PRO_THREADS), 0, s, p);
     hipLaunchKernelGGL(bwd_kernel<64>, dim3(grid), dim3(BWD_THREADS), 0, s, p);
+    hipLaunchKernelGGL(dq_kernel<64>, dim3(grid), dim3(DQ_THREADS), 0, s, p);
   }
   return hipGetLastError();
 }

@@ -31,6 +31,22 @@ int num_cus() {
 
 }  // namespace
 
+namespace {
+// Backward workspace: status word, pi [Hq, T], per-document block offsets, then the dShat store
+// (8 KiB of codes and 8 exponent bytes per (block, query head)).
+constexpr size_t DS_BLOCK_BYTES = 128 * 64;
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+size_t bwd_fixed_bytes(int32_t T, int32_t Hq, int32_t n_docs) {
+  return 256 + align256((size_t)T * Hq * 2) + align256(((size_t)n_docs + 1) * 8);
+}
+// Stored dShat blocks of a document of length L: one per (128-key tile kappa, 64-query tile
+// qt >= 2 kappa), none when the document has a single key tile.
+int64_t doc_blocks(int64_t L) {
+  const int64_t n_kt = (L + 127) / 128, n_qt = (L + 63) / 64;
+  return n_kt >= 2 ? n_kt * n_qt - n_kt * (n_kt - 1) : 0;
+}
+}  // namespace
+
 extern "C" {
 
 const char* flamia_status_str(flamia_status s) {
@@ -131,30 +147,32 @@ flamia_status flamia_fwd(const flamia_fwd_args* a, void* stream) {
   return e == hipSuccess ? FLAMIA_OK : FLAMIA_ERR_HIP;
 }
 
-size_t flamia_bwd_workspace_bytes(int32_t T, int32_t Hq) {
-  if (T < 0 || Hq < 0) return 0;
-  const size_t pi = ((size_t)T * Hq * 2 + 255) / 256 * 256;
-  const size_t cnt = ((size_t)T * Hq * 4 + 255) / 256 * 256;
-  return pi + cnt + 256;
+
+size_t flamia_bwd_workspace_bytes(const int32_t* cu_seqlens_host, int32_t n_docs, int32_t T, int32_t Hq) {
+  if (T < 0 || Hq < 0 || n_docs < 0 || (n_docs > 0 && !cu_seqlens_host)) return 0;
+  int64_t blocks = 0;
+  for (int32_t k = 0; k < n_docs; ++k) blocks += doc_blocks((int64_t)cu_seqlens_host[k + 1] - cu_seqlens_host[k]);
+  return bwd_fixed_bytes(T, Hq, n_docs) + (size_t)blocks * Hq * (DS_BLOCK_BYTES + 8);
 }
 
 flamia_status flamia_bwd(const flamia_bwd_args* a, void* stream) {
   if (!a) return FLAMIA_ERR_NULL;
   if (!a->q || !a->k || !a->v || !a->dO || !a->sq || !a->sk || !a->sv || !a->sdO || !a->lse || !a->D ||
-      !a->cu_seqlens || !a->bwd_list || !a->dq || !a->dk || !a->dv || !a->workspace)
+      !a->cu_seqlens || !a->fwd_list || !a->bwd_list || !a->dq || !a->dk || !a->dv || !a->workspace)
     return FLAMIA_ERR_NULL;
   if (a->T < 0 || a->Hq < 1 || a->Hkv < 1 || a->n_docs < 0) return FLAMIA_ERR_SHAPE;
   if (a->d != 64 && a->d != 128) return FLAMIA_ERR_UNSUPPORTED;
   if (a->Hq % a->Hkv) return FLAMIA_ERR_UNSUPPORTED;
   if (a->T > FLAMIA_MAX_T) return FLAMIA_ERR_UNSUPPORTED;
-  if (a->workspace_bytes < flamia_bwd_workspace_bytes(a->T, a->Hq)) return FLAMIA_ERR_WORKSPACE;
+  const size_t fixed = bwd_fixed_bytes(a->T, a->Hq, a->n_docs);
+  if (a->workspace_bytes < fixed) return FLAMIA_ERR_WORKSPACE;
   const int64_t st[6] = {a->dq_stride_t, a->dq_stride_h, a->dk_stride_t, a->dk_stride_h, a->dv_stride_t, a->dv_stride_h};
   for (int i = 0; i < 6; ++i)
     if (st[i] < 0 || (st[i] % 4)) return FLAMIA_ERR_SHAPE;
   if (!aligned(a->dq, 8) || !aligned(a->dk, 8) || !aligned(a->dv, 8) || !aligned(a->workspace, 256))
     return FLAMIA_ERR_SHAPE;
   if (!aligned(a->q, 16) || !aligned(a->k, 16) || !aligned(a->v, 16) || !aligned(a->dO, 16) ||
-      !aligned(a->bwd_list, 16))
+      !aligned(a->fwd_list, 16) || !aligned(a->bwd_list, 16))
     return FLAMIA_ERR_SHAPE;
   const int grid = num_cus();
   if (grid <= 0) return FLAMIA_ERR_HIP;
@@ -167,16 +185,23 @@ flamia_status flamia_bwd(const flamia_bwd_args* a, void* stream) {
   p.softmax_scale = resolved_scale(a->softmax_scale, a->d);
   p.cu = a->cu_seqlens; p.n_docs = a->n_docs;
   p.list = static_cast<const int32_t*>(a->bwd_list);
+  p.fwd_list = static_cast<const int32_t*>(a->fwd_list);
   p.dq = static_cast<uint16_t*>(a->dq); p.dk = static_cast<uint16_t*>(a->dk); p.dv = static_cast<uint16_t*>(a->dv);
   p.dqst = a->dq_stride_t; p.dqsh = a->dq_stride_h;
   p.dkst = a->dk_stride_t; p.dksh = a->dk_stride_h;
   p.dvst = a->dv_stride_t; p.dvsh = a->dv_stride_h;
   uint8_t* ws = static_cast<uint8_t*>(a->workspace);
-  const size_t pi_bytes = ((size_t)a->T * a->Hq * 2 + 255) / 256 * 256;
-  const size_t cnt_bytes = ((size_t)a->T * a->Hq * 4 + 255) / 256 * 256;
-  p.pi = reinterpret_cast<int16_t*>(ws);
-  p.counters = reinterpret_cast<int32_t*>(ws + pi_bytes);
-  p.status = reinterpret_cast<int32_t*>(ws + pi_bytes + cnt_bytes);
+  size_t off = 0;
+  p.status = reinterpret_cast<int32_t*>(ws);
+  off += 256;
+  p.pi = reinterpret_cast<int16_t*>(ws + off);
+  off += align256((size_t)a->T * a->Hq * 2);
+  p.doc_base = reinterpret_cast<int64_t*>(ws + off);
+  off += align256(((size_t)a->n_docs + 1) * 8);
+  const size_t cap = (a->workspace_bytes - off) / (DS_BLOCK_BYTES + 8);
+  p.ds_codes = ws + off;
+  p.ds_scales = ws + off + cap * DS_BLOCK_BYTES;
+  p.ds_capacity = (int64_t)cap;
   p.pi_out = a->dq_exp_out;
   p.causal = a->causal_dq_scale ? 1 : 0;
   hipError_t e = launch_bwd(p, a->d, grid, static_cast<hipStream_t>(stream));

@@ -45,13 +45,17 @@ struct BwdParams {
   float softmax_scale;
   const int32_t* cu;
   int32_t n_docs;
-  const int32_t* list;
+  const int32_t* list;      // backward list (128-key tiles)
+  const int32_t* fwd_list;  // forward list (256-query items), drives the dQ kernel
   uint16_t *dq, *dk, *dv;
   int64_t dqst, dqsh, dkst, dksh, dvst, dvsh;
-  int16_t* pi;          // workspace: [Hq, T]
-  int32_t* counters;    // workspace: [Hq, T]
-  int32_t* status;      // workspace: error word(s)
-  int16_t* pi_out;      // optional copy of pi
+  int32_t* status;          // workspace: 0, or 2 when the dShat store does not fit
+  int16_t* pi;              // workspace: [Hq, T]
+  int64_t* doc_base;        // workspace: first stored dShat block of each document, [n_docs + 1]
+  uint8_t* ds_codes;        // workspace: dShat blocks, 8 KiB per (block, query head)
+  uint8_t* ds_scales;       // workspace: their 8 exponent bytes
+  int64_t ds_capacity;      // (block, query head) pairs that fit
+  int16_t* pi_out;          // optional copy of pi
   int32_t causal;
 };
 

@@ -4,6 +4,8 @@ import ctypes
 import os
 import re
 
+import numpy as np
+
 import pytest
 
 import precision_causal_attention_token_amd as fl
@@ -41,7 +43,14 @@ def test_size_queries(lib):
     assert lib.flamia_worklist_bytes(3, 1000, 0) == 16 + 16 * (8 + 3)
     assert lib.flamia_worklist_bytes(-1, 10, 0) == 0
     T, Hq = 1000, 4
-    assert lib.flamia_bwd_workspace_bytes(T, Hq) >= T * Hq * 6
+    cu = np.array([0, 100, 100, 612, 1000], np.int32)       # lengths 100, 0, 512, 388
+    blocks = 0 + 0 + (4 * 8 - 4 * 3) + (4 * 7 - 4 * 3)     # n_kt n_qt - n_kt (n_kt - 1), 1-tile docs: 0
+    got = lib.flamia_bwd_workspace_bytes(cu.ctypes.data_as(ctypes.c_void_p), 4, T, Hq)
+    fixed = lib.flamia_bwd_workspace_bytes(None, 0, T, Hq)
+    assert fixed >= 256 + T * Hq * 2
+    assert got - fixed == blocks * Hq * (8192 + 8)             # block offsets fit the same 256 bytes
+    assert lib.flamia_bwd_workspace_bytes(None, 3, T, Hq) == 0    # host cu_seqlens required
+    assert fl.bwd_workspace_bytes(cu, T, Hq) == got
 
 
 def test_host_validation_errors(lib):
@@ -61,8 +70,8 @@ def test_host_validation_errors(lib):
     assert lib.flamia_build_worklist(fake, 1, 1 << 21, 0, 4, fake, 1 << 30, None) == 3
     b = fl._BwdArgs()
     for f, _ in fl._BwdArgs._fields_:
-        if f in ("q", "k", "v", "dO", "sq", "sk", "sv", "sdO", "lse", "D", "cu_seqlens", "bwd_list", "dq", "dk",
-                 "dv", "workspace"):
+        if f in ("q", "k", "v", "dO", "sq", "sk", "sv", "sdO", "lse", "D", "cu_seqlens", "fwd_list", "bwd_list",
+                 "dq", "dk", "dv", "workspace"):
             setattr(b, f, fake)
     b.T, b.Hq, b.Hkv, b.d, b.n_docs = 100, 4, 2, 64, 1
     b.workspace_bytes = 16

@@ -10,7 +10,8 @@ from precision_causal_attention_token_amd import build
 from tests import isa_waits
 
 KERNELS = [("attn_fwd.hip", r"_ZN6flamia12_GLOBAL__N_110fwd_kernelI\w+"),
-           ("attn_bwd.hip", r"_ZN6flamia12_GLOBAL__N_110bwd_kernelI\w+")]
+           ("attn_bwd.hip", r"_ZN6flamia12_GLOBAL__N_110bwd_kernelI\w+"),
+           ("attn_bwd.hip", r"_ZN6flamia12_GLOBAL__N_19dq_kernelI\w+")]
 
 
 @pytest.mark.skipif(not os.path.exists(build.HIPCC), reason="hipcc not installed")
