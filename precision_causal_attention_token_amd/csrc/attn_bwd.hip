@@ -66,6 +66,7 @@ struct BwdSmem {
   uint8_t q[2][QT * D];
   uint8_t dO[2][QT * D];
   uint8_t k[KV_TILE * D];
+  uint8_t v[KV_TILE * D];
   uint8_t ds[KV_TILE * QT];  // dShat [key][query], single-tile documents only
   uint8_t sk[KV_TILE];
   float lse[2][QT];
@@ -189,9 +190,14 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
       for (int chunk = tid; chunk < KV_TILE * CPR; chunk += BWD_THREADS) {
         const int row = chunk / CPR, col = (chunk % CPR) * 16;
         const int key = KV_TILE * kappa + row;
-        uint4 v4 = make_uint4(0, 0, 0, 0);
-        if (key < L) v4 = *reinterpret_cast<const uint4*>(p.k + ((int64_t)(doc_start + key) * p.Hkv + g) * D + col);
-        *reinterpret_cast<uint4*>(&sm.k[lds_off<D>(row, col)]) = v4;
+        uint4 k4 = make_uint4(0, 0, 0, 0), v4 = make_uint4(0, 0, 0, 0);
+        if (key < L) {
+          const int64_t off = ((int64_t)(doc_start + key) * p.Hkv + g) * D + col;
+          k4 = *reinterpret_cast<const uint4*>(p.k + off);
+          v4 = *reinterpret_cast<const uint4*>(p.v + off);
+        }
+        *reinterpret_cast<uint4*>(&sm.k[lds_off<D>(row, col)]) = k4;
+        *reinterpret_cast<uint4*>(&sm.v[lds_off<D>(row, col)]) = v4;
       }
       if (tid < KV_TILE) {
         const int key = KV_TILE * kappa + tid;
@@ -200,26 +206,10 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
     }
     store_step<D>(pre, sm, 0);
     __syncthreads();
-    v8i kop[NC], vop[NC];
+    // K and V of this wave's keys are the B operands of S and dP in every step; they are read
+    // from the LDS tiles each time (registers are the scarce resource here).
     const int k_scale = sm.sk[32 * wave + n];
-    int v_scale = 127;
-    {
-      const int64_t ka = (int64_t)(doc_start + key_rel);
-#pragma unroll
-      for (int cc = 0; cc < NC; ++cc) {
-        kop[cc] = lds_read_row32<D>(sm.k, 32 * wave + n, 64 * cc + 32 * hh);
-        if (key_valid) {
-          const uint4* src = reinterpret_cast<const uint4*>(p.v + (ka * p.Hkv + g) * D + 64 * cc + 32 * hh);
-          const uint4 a = src[0], b = src[1];
-          vop[cc][0] = a.x; vop[cc][1] = a.y; vop[cc][2] = a.z; vop[cc][3] = a.w;
-          vop[cc][4] = b.x; vop[cc][5] = b.y; vop[cc][6] = b.z; vop[cc][7] = b.w;
-        } else {
-#pragma unroll
-          for (int i = 0; i < 8; ++i) vop[cc][i] = 0;
-        }
-      }
-      if (key_valid) v_scale = p.sv[(int64_t)g * T + doc_start + key_rel];
-    }
+    const int v_scale = key_valid ? p.sv[(int64_t)g * T + doc_start + key_rel] : 127;
 
     v16f dkacc[NDB], dvacc[NDB];
 #pragma unroll
@@ -248,10 +238,12 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
           pacc[qb] = v16f{};
 #pragma unroll
           for (int cc = 0; cc < NC; ++cc) {
+            const v8i kop = lds_read_row32<D>(sm.k, 32 * wave + n, 64 * cc + 32 * hh);
             const v8i aq = lds_read_row32<D>(sm.q[b], 32 * qb + n, 64 * cc + 32 * hh);
-            sacc[qb] = mfma_scaled(aq, kop[cc], sacc[qb], sm.sq[b][qb], k_scale);
+            sacc[qb] = mfma_scaled(aq, kop, sacc[qb], sm.sq[b][qb], k_scale);
+            const v8i vop = lds_read_row32<D>(sm.v, 32 * wave + n, 64 * cc + 32 * hh);
             const v8i ad = lds_read_row32<D>(sm.dO[b], 32 * qb + n, 64 * cc + 32 * hh);
-            pacc[qb] = mfma_scaled(ad, vop[cc], pacc[qb], sm.sdo[b][qb], v_scale);
+            pacc[qb] = mfma_scaled(ad, vop, pacc[qb], sm.sdo[b][qb], v_scale);
           }
           mfma_drain(sacc[qb]);
           mfma_drain(pacc[qb]);
@@ -259,15 +251,23 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
           float pmax = 0.f, dmax = 0.f;
+          float4 lse4[4], dd4[4];  // rows acc_row(4 j + e, hh) = 32 qb + 8 j + 4 hh + e
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            lse4[j] = *reinterpret_cast<const float4*>(&sm.lse[b][32 * qb + 8 * j + 4 * hh]);
+            dd4[j] = *reinterpret_cast<const float4*>(&sm.dd[b][32 * qb + 8 * j + 4 * hh]);
+          }
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            const int qi = 32 * qb + acc_row(i, hh);
-            float pv = __builtin_amdgcn_exp2f(fmaf(sacc[qb][i], c, -sm.lse[b][qi]));
+            const float lse_i = i % 4 == 0 ? lse4[i / 4].x : i % 4 == 1 ? lse4[i / 4].y : i % 4 == 2 ? lse4[i / 4].z : lse4[i / 4].w;
+            const float dd_i = i % 4 == 0 ? dd4[i / 4].x : i % 4 == 1 ? dd4[i / 4].y : i % 4 == 2 ? dd4[i / 4].z : dd4[i / 4].w;
+            float arg = fmaf(sacc[qb][i], c, -lse_i);
             if constexpr (MASK) {
-              const int qr = q0 + qi;
-              pv = (key_rel <= qr && qr < L) ? pv : 0.f;
+              const int qr = q0 + 32 * qb + acc_row(i, hh);
+              arg = (key_rel <= qr && qr < L) ? arg : -__builtin_inff();  // 2^-inf = +0
             }
-            const float dsv = pv * (pacc[qb][i] - sm.dd[b][qi]);
+            const float pv = __builtin_amdgcn_exp2f(arg);
+            const float dsv = pv * (pacc[qb][i] - dd_i);
             sacc[qb][i] = pv;
             pacc[qb][i] = dsv;
             pmax = fmaxf(pmax, pv);
@@ -367,7 +367,7 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
 
     // ---- dK, dV of this wave's keys
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) { mfma_drain(dkacc[db]); mfma_drain(dvacc[db]); }
+    for (int db = 0; db < NDB; ++db) { mfma_drain_acc(dkacc[db]); mfma_drain_acc(dvacc[db]); }
     if (key_valid) {
       uint16_t* krow = p.dk + (int64_t)(doc_start + key_rel) * p.dkst + (int64_t)g * p.dksh;
       uint16_t* vrow = p.dv + (int64_t)(doc_start + key_rel) * p.dvst + (int64_t)g * p.dvsh;
@@ -413,6 +413,7 @@ struct DqRegs {
 template <int D>
 __device__ __forceinline__ void dq_load(DqRegs<D>& r, const BwdParams& p, int doc_start, int L, int n_qt,
                                         int64_t base, int qt0, int g, int h, int kappa) {
+  static_assert(DqRegs<D>::SCH == 4, "one 16-byte chunk of each of the four blocks per thread");
   const int tid = threadIdx.x;
   constexpr int CPR = D / 16;
 #pragma unroll
@@ -423,24 +424,19 @@ __device__ __forceinline__ void dq_load(DqRegs<D>& r, const BwdParams& p, int do
     r.k[i] = make_uint4(0, 0, 0, 0);
     if (key < L) r.k[i] = *reinterpret_cast<const uint4*>(p.k + ((int64_t)(doc_start + key) * p.Hkv + g) * D + col);
   }
+  // block of query tile qt0 + t; the four tiles' blocks of one key tile are consecutive
+  const int64_t blk0 = ds_block(base, kappa, n_qt, qt0);
 #pragma unroll
-  for (int i = 0; i < DqRegs<D>::SCH; ++i) {
-    const int chunk = tid + i * DQ_THREADS;
-    const int t4 = chunk / (DS_BLOCK / 16), within = chunk % (DS_BLOCK / 16);
-    const int qt = qt0 + t4;
-    r.s[i] = make_uint4(0, 0, 0, 0);
-    if (qt < n_qt && qt >= 2 * kappa) {
-      const int64_t blk = ds_block(base, kappa, n_qt, qt) * p.Hq + h;
-      r.s[i] = reinterpret_cast<const uint4*>(p.ds_codes + blk * DS_BLOCK)[within];
-    }
+  for (int t = 0; t < 4; ++t) {
+    const int qt = qt0 + t;
+    r.s[t] = make_uint4(0, 0, 0, 0);
+    if (qt < n_qt && qt >= 2 * kappa)
+      r.s[t] = reinterpret_cast<const uint4*>(p.ds_codes + ((blk0 + t) * p.Hq + h) * DS_BLOCK)[tid];
   }
   r.sc = make_uint2(0x7F7F7F7Fu, 0x7F7F7F7Fu);
   if (tid < 4) {
     const int qt = qt0 + tid;
-    if (qt < n_qt && qt >= 2 * kappa) {
-      const int64_t blk = ds_block(base, kappa, n_qt, qt) * p.Hq + h;
-      r.sc = *reinterpret_cast<const uint2*>(p.ds_scales + blk * 8);
-    }
+    if (qt < n_qt && qt >= 2 * kappa) r.sc = *reinterpret_cast<const uint2*>(p.ds_scales + ((blk0 + tid) * p.Hq + h) * 8);
   }
   r.skb = 127;
   if (tid < KV_TILE) {
@@ -459,13 +455,9 @@ __device__ __forceinline__ void dq_store(const DqRegs<D>& r, DqSmem<D>& sm, int 
     const int row = chunk / CPR, col = (chunk % CPR) * 16;
     *reinterpret_cast<uint4*>(&sm.k[b][lds_off<D>(row, col)]) = r.k[i];
   }
+  const int off = lds_off<QT>(tid / (QT / 16), (tid % (QT / 16)) * 16);
 #pragma unroll
-  for (int i = 0; i < DqRegs<D>::SCH; ++i) {
-    const int chunk = tid + i * DQ_THREADS;
-    const int t4 = chunk / (DS_BLOCK / 16), within = chunk % (DS_BLOCK / 16);
-    const int row = within / (QT / 16), col = (within % (QT / 16)) * 16;
-    *reinterpret_cast<uint4*>(&sm.ds[b][t4][lds_off<QT>(row, col)]) = r.s[i];
-  }
+  for (int t = 0; t < 4; ++t) *reinterpret_cast<uint4*>(&sm.ds[b][t][off]) = r.s[t];
   if (tid < 4) *reinterpret_cast<uint2*>(&sm.dsc[b][tid][0]) = r.sc;
   if (tid < KV_TILE) sm.sk[b][tid] = (uint8_t)r.skb;
 }

@@ -34,13 +34,15 @@ __device__ __forceinline__ v16f mfma_scaled(const v8i& a, const v8i& b, const v1
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
 }
 
-// End of an accumulation chain whose result the vector ALU reads next.  The scaled FP8
-// instruction writes its last accumulator registers late; the compiler's padding before the
-// first read has been seen to fall one wait state short when scalar instructions fill the
-// gap.  This no-op block is tied to the accumulator, so it sits between the last instruction
-// of the chain and every read of the result and adds a fixed margin to whatever padding the
-// compiler places.  "a": the accumulator is kept in the matrix-core registers.
-__device__ __forceinline__ void mfma_drain(v16f& acc) { asm volatile("s_nop 3" : "+a"(acc)); }
+// End of an accumulation chain whose result is read next.  The scaled FP8 instruction writes
+// its last accumulator registers late; the compiler's padding before the first read has been
+// seen to fall one wait state short when scalar instructions fill the gap.  This no-op block is
+// tied to the accumulator, so it sits between the last instruction of the chain and every read
+// of the result and adds a fixed margin to whatever padding the compiler places.
+// mfma_drain: the result is read by vector instructions, so it is kept in (arch) VGPRs;
+// mfma_drain_acc: a long-lived accumulator kept in the matrix-core registers (AGPRs).
+__device__ __forceinline__ void mfma_drain(v16f& acc) { asm volatile("s_nop 3" : "+v"(acc)); }
+__device__ __forceinline__ void mfma_drain_acc(v16f& acc) { asm volatile("s_nop 3" : "+a"(acc)); }
 
 // Accumulator row held by register i of lane group h.
 __device__ __forceinline__ int acc_row(int i, int h) { return 8 * (i >> 2) + 4 * h + (i & 3); }
