@@ -49,13 +49,23 @@ __device__ __forceinline__ int acc_row(int i, int h) { return 8 * (i >> 2) + 4 *
 
 // ---------------------------------------------------------------------------------------------
 // LDS tiles: [rows][COLS] bytes, COLS in {64, 128}, with the 16-byte chunks of each row permuted
-// by an XOR.  The permutation keeps two access patterns free of bank conflicts: 32 contiguous
-// bytes per lane of consecutive rows (row-major operand reads) and 8 rows
-// {4h..4h+3, 8+4h..8+4h+3} x 16 bytes (transpose reads).
+// by an XOR with a function of the row.  Taking the LDS as 64 banks of 4 bytes (256 bytes per
+// cycle), the permutation keeps both access patterns free of bank conflicts:
+//   row-major operand reads: 16 consecutive lanes read the same 16-byte chunk of 16 consecutive
+//     rows, which land in 16 distinct 16-byte bank groups;
+//   transpose reads: 32 lanes read rows {b..b+3, b+8..b+11} (b = 0 or 4 mod 16) at two adjacent
+//     chunks, again 16 distinct bank groups.
+// COLS = 128 (two rows per 256 bytes): chunk ^ g(m), m = (row >> 1) & 7, g a permutation of 0..7
+//   with g(m) >> 1 distinct over m in {0, 1, 4, 5} and over m in {2, 3, 6, 7};
+// COLS = 64 (four rows per 256 bytes): chunk ^ ((row >> 2) & 3).
 template <int COLS>
 __device__ __forceinline__ int lds_swizzle(int row) {
-  if constexpr (COLS == 128) return (row & 3) | ((((row >> 2) ^ (row >> 3)) & 1) << 2);
-  else return ((row >> 1) & 1) | ((((row >> 2) ^ (row >> 3)) & 1) << 1);
+  if constexpr (COLS == 128) {
+    const int m = (row >> 1) & 7;
+    return 2 * ((m & 1) | (((m >> 2) & 1) << 1)) + ((m >> 1) & 1);
+  } else {
+    return (row >> 2) & 3;
+  }
 }
 template <int COLS>
 __device__ __forceinline__ int lds_off(int row, int col) {
