@@ -273,15 +273,14 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
             pmax = fmaxf(pmax, pv);
             dmax = fmaxf(dmax, fabsf(dsv));
           }
-          sp[qb] = e8m0_roundup(wave_max(pmax));
-          sds[qb] = e8m0_roundup(wave_max(dmax));
-          const float fp = exp2i_neg(sp[qb]), fd = exp2i_neg(sds[qb]);
+          sp[qb] = e8m0_roundup(wave_max_nonneg(pmax));
+          sds[qb] = e8m0_roundup(wave_max_nonneg(dmax));
 #pragma unroll
           for (int w4 = 0; w4 < 4; ++w4) {
-            pp[4 * qb + w4] = pack4_fp8(sacc[qb][4 * w4] * fp, sacc[qb][4 * w4 + 1] * fp, sacc[qb][4 * w4 + 2] * fp,
-                                        sacc[qb][4 * w4 + 3] * fp);
-            pd[4 * qb + w4] = pack4_fp8(pacc[qb][4 * w4] * fd, pacc[qb][4 * w4 + 1] * fd, pacc[qb][4 * w4 + 2] * fd,
-                                        pacc[qb][4 * w4 + 3] * fd);
+            pp[4 * qb + w4] = pack4_fp8_scaled(sacc[qb][4 * w4], sacc[qb][4 * w4 + 1], sacc[qb][4 * w4 + 2],
+                                               sacc[qb][4 * w4 + 3], sp[qb]);
+            pd[4 * qb + w4] = pack4_fp8_scaled(pacc[qb][4 * w4], pacc[qb][4 * w4 + 1], pacc[qb][4 * w4 + 2],
+                                               pacc[qb][4 * w4 + 3], sds[qb]);
           }
         }
       };

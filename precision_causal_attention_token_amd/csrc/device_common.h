@@ -132,6 +132,19 @@ __device__ __forceinline__ int pack4_fp8(float a0, float a1, float a2, float a3)
   return __builtin_amdgcn_cvt_pk_fp8_f32(a2, a3, r, true);
 }
 
+// Four floats -> one dword of E4M3 codes of x * 2^-s (round to nearest even), s in [-127, 127].
+// The scaled conversion instruction divides by the power of two whose float exponent field is
+// s + 127 (the field alone is used, so +0.0 stands for 2^-127); on gfx950 it gives exactly the
+// codes of the multiply-then-convert sequence, ties, subnormal and saturating results included
+// (checked on the hardware for every exponent).
+typedef short v2s __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ int pack4_fp8_scaled(float a0, float a1, float a2, float a3, int s) {
+  const float scale = __uint_as_float((uint32_t)(127 + s) << 23);
+  const v2s lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(v2s{0, 0}, a0, a1, scale, false);
+  const v2s r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lo, a2, a3, scale, true);
+  return __builtin_bit_cast(int, r);
+}
+
 // ---------------------------------------------------------------------------------------------
 // Wave reductions (64 lanes): DPP within rows of 16, then permlane swaps across rows.
 template <int CTRL>
@@ -147,6 +160,19 @@ __device__ __forceinline__ float wave_max(float x) {
   x = fmaxf(__int_as_float((int)a[0]), __int_as_float((int)a[1]));
   auto b = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
   return fmaxf(__int_as_float((int)b[0]), __int_as_float((int)b[1]));
+}
+// Maximum over the wave of a non-negative float, as an unsigned maximum of the bit patterns
+// (the same order for non-negative floats; each DPP step is one instruction).
+__device__ __forceinline__ float wave_max_nonneg(float x) {
+  uint32_t u = __float_as_uint(x);
+  u = max(u, (uint32_t)__builtin_amdgcn_mov_dpp((int)u, 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
+  u = max(u, (uint32_t)__builtin_amdgcn_mov_dpp((int)u, 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
+  u = max(u, (uint32_t)__builtin_amdgcn_mov_dpp((int)u, 0x124, 0xF, 0xF, false));  // row_ror:4
+  u = max(u, (uint32_t)__builtin_amdgcn_mov_dpp((int)u, 0x128, 0xF, 0xF, false));  // row_ror:8
+  auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  u = max((uint32_t)a[0], (uint32_t)a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float(max((uint32_t)b[0], (uint32_t)b[1]));
 }
 // Combine the two lane groups (l and l ^ 32).
 __device__ __forceinline__ float halves_max(float x) {
