@@ -26,6 +26,13 @@ METRIC = "causal MXFP8 attn fwd+bwd TFLOPS incl. quantize; % of MI355X MXFP8 pea
 PEAK_FP8_TFLOPS = 5000.0     # MI355X dense FP8 / MXFP8 matrix peak
 PEAK_HBM_GBPS = 8000.0       # MI355X HBM3E
 
+# HBM bytes per flamia_bwd call (prologue + key-tile + dQ kernels) on the `long` workload, from
+# the FETCH_SIZE / WRITE_SIZE passes summarised in profiles/flamia_long_hbm_traffic.md (FETCH
+# scaled by 2.000 and WRITE by 1.000, the factors a 1 GiB copy gives).  Valid only for the
+# backward sources it was measured on (sha256 prefix over attn_bwd.hip, device_common.h,
+# kernels.h); any other build reports null.
+BWD_TRAFFIC = {"workload": "long", "src": "2d72e94548b16a83", "read_bytes": 17.83e9, "write_bytes": 12.95e9}
+
 
 def parse():
     ap = argparse.ArgumentParser()
@@ -40,6 +47,15 @@ def parse():
                     help="before warmup, run one plain device-to-device copy of this many MiB (reference "
                          "kernel of known traffic for hardware byte counters)")
     return ap.parse_args()
+
+
+def bwd_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("attn_bwd.hip", "device_common.h", "kernels.h"):
+        with open(os.path.join(ROOT, "precision_causal_attention_token_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 
 
 def cpu_baseline(workload_name, pairs_budget):
@@ -166,9 +182,13 @@ def main():
     dom = "bwd" if stages["bwd"] >= stages["fwd"] else "fwd"
     dom_flop = bwd_flop if dom == "bwd" else fwd_flop
     achieved = dom_flop / (stages[dom] * 1e-3) / 1e12
-    roofline = {"bound": "mfma", "kernel": "flamia_bwd (prologue + main kernel)" if dom == "bwd" else "flamia_fwd",
+    traffic = None
+    if dom == "bwd" and args.workload == BWD_TRAFFIC["workload"] and bwd_source_hash() == BWD_TRAFFIC["src"]:
+        traffic = BWD_TRAFFIC["read_bytes"] + BWD_TRAFFIC["write_bytes"]
+    roofline = {"bound": "mfma",
+                "kernel": "flamia_bwd (bwd_prologue + bwd_kernel + dq_kernel)" if dom == "bwd" else "flamia_fwd",
                 "achieved": achieved, "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_FP8_TFLOPS,
-                "traffic": None}
+                "traffic": traffic, "traffic_unit": "bytes per launch"}
     n_qkv = T * (Hq + 2 * Hkv) * d
     qkv_bytes = 3 * n_qkv + T * (Hq + 2 * Hkv)
     do_bytes = 5 * T * Hq * d + 5 * T * Hq
