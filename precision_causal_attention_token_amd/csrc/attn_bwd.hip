@@ -41,7 +41,8 @@ namespace flamia {
 
 namespace {
 
-constexpr int BWD_THREADS = 256;
+constexpr int BWD_WAVES = 8;   // 4 producer + 4 consumer waves, one of each per SIMD
+constexpr int BWD_THREADS = 64 * BWD_WAVES;
 constexpr int QT = 64;                 // queries per step / per stored dShat block
 constexpr int DS_BLOCK = KV_TILE * QT;  // bytes of one stored dShat block
 constexpr int DQ_WAVES = 8;
@@ -63,24 +64,27 @@ __device__ __forceinline__ int ds_pos_query(int pos) {
 
 template <int D>
 struct BwdSmem {
-  uint8_t q[2][QT * D];
-  uint8_t dO[2][QT * D];
+  uint8_t q[3][QT * D];       // step s in buffer s % 3: producers read step k, consumers k - 1,
+  uint8_t dO[3][QT * D];      // the loader fills k + 1
   uint8_t k[KV_TILE * D];
   uint8_t v[KV_TILE * D];
-  uint8_t ds[KV_TILE * QT];  // dShat [key][query], single-tile documents only
+  int4 xp[2][4][2][64];       // Phat operand of (key group) in lane order, 2 x 16 bytes per lane
+  int4 xd[2][4][2][64];       // dShat operand
+  uint8_t ds[2][KV_TILE * QT];  // dShat [key][query], single-tile documents only
   uint8_t sk[KV_TILE];
-  float lse[2][QT];
-  float dd[2][QT];
-  int pi[2][QT];
-  int sq[2][2], sdo[2][2];
-  int ds_scale[2][4];
+  float lse[3][QT];
+  float dd[3][QT];
+  int pi[3][QT];
+  int sq[3][2], sdo[3][2];
+  int xs_p[2][2][4], xs_d[2][2][4];  // block exponent bytes of (query block, key group)
 };
 
 // One step's Q / dO rows and row statistics, held in registers between the global loads
-// (issued one step ahead) and the LDS stores.
+// (issued one phase ahead) and the LDS stores.
 template <int D>
 struct StepRegs {
-  static constexpr int CH = QT * D / 16 / BWD_THREADS;  // 16-byte chunks per tensor per thread
+  static constexpr int TOTAL = QT * D / 16;                          // 16-byte chunks per tensor
+  static constexpr int CH = (TOTAL + BWD_THREADS - 1) / BWD_THREADS;  // per thread
   uint4 q[CH], dO[CH];
   float lse, dd;
   int pi, sq, sdo;
@@ -98,7 +102,7 @@ __device__ __forceinline__ void load_step(StepRegs<D>& r, const BwdParams& p, in
     const int qr = q0 + row;
     r.q[i] = make_uint4(0, 0, 0, 0);
     r.dO[i] = make_uint4(0, 0, 0, 0);
-    if (qr < L) {
+    if (chunk < StepRegs<D>::TOTAL && qr < L) {
       const int64_t off = ((int64_t)(doc_start + qr) * p.Hq + h) * D + col;
       r.q[i] = *reinterpret_cast<const uint4*>(p.q + off);
       r.dO[i] = *reinterpret_cast<const uint4*>(p.dO + off);
@@ -130,9 +134,11 @@ __device__ __forceinline__ void store_step(const StepRegs<D>& r, BwdSmem<D>& sm,
 #pragma unroll
   for (int i = 0; i < StepRegs<D>::CH; ++i) {
     const int chunk = tid + i * BWD_THREADS;
-    const int row = chunk / CPR, col = (chunk % CPR) * 16;
-    *reinterpret_cast<uint4*>(&sm.q[b][lds_off<D>(row, col)]) = r.q[i];
-    *reinterpret_cast<uint4*>(&sm.dO[b][lds_off<D>(row, col)]) = r.dO[i];
+    if (chunk < StepRegs<D>::TOTAL) {
+      const int row = chunk / CPR, col = (chunk % CPR) * 16;
+      *reinterpret_cast<uint4*>(&sm.q[b][lds_off<D>(row, col)]) = r.q[i];
+      *reinterpret_cast<uint4*>(&sm.dO[b][lds_off<D>(row, col)]) = r.dO[i];
+    }
   }
   if (tid < QT) {
     sm.lse[b][tid] = r.lse;
@@ -144,6 +150,12 @@ __device__ __forceinline__ void store_step(const StepRegs<D>& r, BwdSmem<D>& sm,
   }
 }
 
+// Key-stationary pass.  Producer wave w (0..3) owns keys 32 w .. 32 w + 31 of the tile: per
+// 64-query step it forms S and dP, the softmax terms, and the E4M3 Phat / dShat operands with
+// their 32 x 32 block exponents, hands them over in LDS and stores dShat.  Consumer wave 4 + w
+// holds dK^T and dV^T of the same keys and runs the gradient products one step behind, so its
+// matrix instructions overlap the producer's vector work on the same SIMD.  Phase k: producers
+// on step k, consumers on step k - 1, every thread loads step k + 1; one barrier per phase.
 template <int D>
 __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
   constexpr int NC = D / 64;
@@ -154,6 +166,8 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int n = lane & 31, hh = lane >> 5;
+  const bool producer = wave < 4;
+  const int kw = wave & 3;  // key group of both roles
   const int n_items = p.list[0];
   const int4* items = reinterpret_cast<const int4*>(p.list + 4);
   const int n_units = n_items * p.Hkv;
@@ -173,7 +187,7 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
     const int n_qt = (L + QT - 1) / QT;
     const bool store_ds = L > KV_TILE;  // two or more key tiles: dQ in the query-stationary kernel
     const int64_t ds_base = store_ds ? p.doc_base[doc] : 0;
-    const int key_rel = KV_TILE * kappa + 32 * wave + n;
+    const int key_rel = KV_TILE * kappa + 32 * kw + n;
     const bool key_valid = key_rel < L;
 
     // Steps run over (query head of the group, 64-query tile from the diagonal to the
@@ -181,7 +195,7 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
     const int nq = n_qt - 2 * kappa;  // query tiles per head
     const int n_steps = grp * nq;
 
-    // ---- K tile and the first step's tiles into LDS
+    // ---- K / V tiles and the first step's tiles into LDS
     __syncthreads();  // the previous unit no longer reads LDS
     StepRegs<D> pre;
     load_step<D>(pre, p, doc_start, L, g * grp, 2 * kappa);
@@ -206,184 +220,219 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
     }
     store_step<D>(pre, sm, 0);
     __syncthreads();
-    // K and V of this wave's keys are the B operands of S and dP in every step; they are read
-    // from the LDS tiles each time (registers are the scarce resource here).
-    const int k_scale = sm.sk[32 * wave + n];
+    const int k_scale = sm.sk[32 * kw + n];
     const int v_scale = key_valid ? p.sv[(int64_t)g * T + doc_start + key_rel] : 127;
 
-    v16f dkacc[NDB], dvacc[NDB];
+    // Each role runs its own phase loop (the same number of barriers in both), so the
+    // consumers' accumulators are not live in the producers' code.
+    if (producer) {
+      int b3 = 0;  // phase % 3
+      for (int ph = 0; ph <= n_steps; ++ph) {
+        const int b3n = b3 == 2 ? 0 : b3 + 1;  // (phase + 1) % 3
+        const int x2 = ph & 1;                 // operand hand-over buffer of step ph
+        if (ph + 1 < n_steps) {
+          const int hn = (ph + 1) / nq;
+          load_step<D>(pre, p, doc_start, L, g * grp + hn, 2 * kappa + (ph + 1 - hn * nq));
+        }
+        if (ph < n_steps) {
+          const int hi = ph / nq;
+          const int h = g * grp + hi;
+          const int qt = 2 * kappa + (ph - hi * nq);
+          const int q0 = QT * qt;
+          const int b = b3;
+          int pp[8], pd[8];
+          int sp[2], sds[2];
+          auto scores = [&](auto masked) {
+            constexpr bool MASK = decltype(masked)::value;
+            // both query blocks' products are issued first, so the matrix cores work on block 1
+            // while the vector unit processes block 0
+            v16f sacc2[2], pacc2[2];
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) { dkacc[db] = v16f{}; dvacc[db] = v16f{}; }
+            for (int cc = 0; cc < NC; ++cc) {
+              const v8i kop = lds_read_row32<D>(sm.k, 32 * kw + n, 64 * cc + 32 * hh);
+              const v8i vop = lds_read_row32<D>(sm.v, 32 * kw + n, 64 * cc + 32 * hh);
+#pragma unroll
+              for (int qb = 0; qb < 2; ++qb) {
+                const v8i aq = lds_read_row32<D>(sm.q[b], 32 * qb + n, 64 * cc + 32 * hh);
+                sacc2[qb] = mfma_scaled(aq, kop, cc ? sacc2[qb] : v16f{}, sm.sq[b][qb], k_scale);
+                const v8i ad = lds_read_row32<D>(sm.dO[b], 32 * qb + n, 64 * cc + 32 * hh);
+                pacc2[qb] = mfma_scaled(ad, vop, cc ? pacc2[qb] : v16f{}, sm.sdo[b][qb], v_scale);
+              }
+            }
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) {
+              v16f sacc = sacc2[qb], pacc = pacc2[qb];
+              mfma_drain(sacc);
+              mfma_drain(pacc);
+              float pmax = 0.f, dmax = 0.f;
+              float4 lse4[4], dd4[4];  // rows acc_row(4 j + e, hh) = 32 qb + 8 j + 4 hh + e
+#pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                lse4[j] = *reinterpret_cast<const float4*>(&sm.lse[b][32 * qb + 8 * j + 4 * hh]);
+                dd4[j] = *reinterpret_cast<const float4*>(&sm.dd[b][32 * qb + 8 * j + 4 * hh]);
+              }
+#pragma unroll
+              for (int i = 0; i < 16; ++i) {
+                const float lse_i = i % 4 == 0 ? lse4[i / 4].x : i % 4 == 1 ? lse4[i / 4].y : i % 4 == 2 ? lse4[i / 4].z : lse4[i / 4].w;
+                const float dd_i = i % 4 == 0 ? dd4[i / 4].x : i % 4 == 1 ? dd4[i / 4].y : i % 4 == 2 ? dd4[i / 4].z : dd4[i / 4].w;
+                float arg = fmaf(sacc[i], c, -lse_i);
+                if constexpr (MASK) {
+                  const int qr = q0 + 32 * qb + acc_row(i, hh);
+                  arg = (key_rel <= qr && qr < L) ? arg : -__builtin_inff();  // 2^-inf = +0
+                }
+                const float pv = __builtin_amdgcn_exp2f(arg);
+                const float dsv = pv * (pacc[i] - dd_i);
+                sacc[i] = pv;
+                pacc[i] = dsv;
+                pmax = fmaxf(pmax, pv);
+                dmax = fmaxf(dmax, fabsf(dsv));
+              }
+              sp[qb] = e8m0_roundup(wave_max_nonneg(pmax));
+              sds[qb] = e8m0_roundup(wave_max_nonneg(dmax));
+#pragma unroll
+              for (int w4 = 0; w4 < 4; ++w4) {
+                pp[4 * qb + w4] = pack4_fp8_scaled(sacc[4 * w4], sacc[4 * w4 + 1], sacc[4 * w4 + 2], sacc[4 * w4 + 3], sp[qb]);
+                pd[4 * qb + w4] = pack4_fp8_scaled(pacc[4 * w4], pacc[4 * w4 + 1], pacc[4 * w4 + 2], pacc[4 * w4 + 3], sds[qb]);
+              }
+            }
+          };
+          // all 64 x 128 pairs visible: the query tile lies wholly below the key tile and inside
+          // the document (then every key of the tile is inside it too)
+          if (qt >= 2 * kappa + 2 && q0 + QT <= L) scores(std::false_type{});
+          else scores(std::true_type{});
 
-    for (int st = 0; st < n_steps; ++st) {
-      const int b = st & 1;
-      const int hi = st / nq;
-      const int h = g * grp + hi;
-      const int qt = 2 * kappa + (st - hi * nq);
-      const int q0 = QT * qt;
-      if (st + 1 < n_steps) {
-        const int hn = (st + 1) / nq;
-        load_step<D>(pre, p, doc_start, L, g * grp + hn, 2 * kappa + (st + 1 - hn * nq));
+          // ---- hand over the operands and exponents; store dShat
+          sm.xp[x2][kw][0][lane] = make_int4(pp[0], pp[1], pp[2], pp[3]);
+          sm.xp[x2][kw][1][lane] = make_int4(pp[4], pp[5], pp[6], pp[7]);
+          sm.xd[x2][kw][0][lane] = make_int4(pd[0], pd[1], pd[2], pd[3]);
+          sm.xd[x2][kw][1][lane] = make_int4(pd[4], pd[5], pd[6], pd[7]);
+          if (lane == 0) {
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) {
+              sm.xs_p[x2][qb][kw] = sp[qb] + 127;
+              sm.xs_d[x2][qb][kw] = sds[qb] + 127;
+            }
+          }
+          if (store_ds) {
+            // dShat block: key row j holds 64 bytes, lane group hh's 32 bytes at 32 hh
+            const int64_t blk = ds_block(ds_base, kappa, n_qt, qt) * p.Hq + h;
+            int4* dst = reinterpret_cast<int4*>(p.ds_codes + blk * DS_BLOCK + (32 * kw + n) * QT + 32 * hh);
+            dst[0] = make_int4(pd[0], pd[1], pd[2], pd[3]);
+            dst[1] = make_int4(pd[4], pd[5], pd[6], pd[7]);
+            if (lane == 0) {
+              p.ds_scales[blk * 8 + kw] = (uint8_t)(sds[0] + 127);
+              p.ds_scales[blk * 8 + 4 + kw] = (uint8_t)(sds[1] + 127);
+            }
+          } else {
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+              for (int w4 = 0; w4 < 4; ++w4) {
+                const int qcol = 32 * qb + 8 * w4 + 4 * hh;
+                *reinterpret_cast<int*>(&sm.ds[x2][lds_off<QT>(32 * kw + n, qcol)]) = pd[4 * qb + w4];
+              }
+          }
+        }
+        if (ph + 1 < n_steps) store_step<D>(pre, sm, b3n);
+        __syncthreads();  // phase done: operands handed over, the next step's tiles stored
+        b3 = b3n;
+      }
+    } else {
+      v16f dkacc[NDB], dvacc[NDB];
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) { dkacc[db] = v16f{}; dvacc[db] = v16f{}; }
+      int b3 = 0;  // phase % 3
+      for (int ph = 0; ph <= n_steps; ++ph) {
+        const int b3p = b3 == 0 ? 2 : b3 - 1;  // (phase - 1) % 3
+        const int b3n = b3 == 2 ? 0 : b3 + 1;  // (phase + 1) % 3
+        if (ph + 1 < n_steps) {
+          const int hn = (ph + 1) / nq;
+          load_step<D>(pre, p, doc_start, L, g * grp + hn, 2 * kappa + (ph + 1 - hn * nq));
+        }
+        if (ph >= 1) {
+          // ---- gradient products of step ph - 1
+          const int st = ph - 1;
+          const int b = b3p, xb = (ph & 1) ^ 1;
+          {
+            const int4 p0 = sm.xp[xb][kw][0][lane], p1 = sm.xp[xb][kw][1][lane];
+            const int4 d0 = sm.xd[xb][kw][0][lane], d1 = sm.xd[xb][kw][1][lane];
+            const v8i bp = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+            const v8i bd = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+            const int sdo_h = sm.sdo[b][hh], sq_h = sm.sq[b][hh];
+            const int sp_h = sm.xs_p[xb][hh][kw], sds_h = sm.xs_d[xb][hh][kw];
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+              const v8i ado = lds_read_tr32<D>(sm.dO[b], 0, 32 * db, lane);
+              dvacc[db] = mfma_scaled(ado, bp, dvacc[db], sdo_h, sp_h);
+              const v8i aq = lds_read_tr32<D>(sm.q[b], 0, 32 * db, lane);
+              dkacc[db] = mfma_scaled(aq, bd, dkacc[db], sq_h, sds_h);
+            }
+          }
+          if (!store_ds) {
+            // single key tile: dQ^T = K^T dShat^T here, the only contribution of its rows;
+            // consumer w computes d-block w (d = 128) or w % 2 (d = 64) of its query blocks
+            const int hi = st / nq;
+            const int h = g * grp + hi;
+            const int q0 = QT * (2 * kappa + (st - hi * nq));
+            constexpr int NQB = (D == 128) ? 2 : 1;
+            const int dblk = (D == 128) ? kw : (kw & 1);
+            const int qb0 = (D == 128) ? 0 : (kw >> 1);
+#pragma unroll
+            for (int x = 0; x < NQB; ++x) {
+              const int qb = qb0 + x;
+              v16f dq = v16f{};
+#pragma unroll
+              for (int ci = 0; ci < 2; ++ci) {
+                const v8i ak = lds_read_tr32<D>(sm.k, 64 * ci, 32 * dblk, lane);
+                const v8i bs = lds_read_tr32<QT>(sm.ds[xb], 64 * ci, 32 * qb, lane);
+                dq = mfma_scaled(ak, bs, dq, sm.sk[64 * ci + 32 * hh], sm.xs_d[xb][qb][2 * ci + hh]);
+              }
+              mfma_drain(dq);
+              const int qi = 32 * qb + n;
+              const int qr = q0 + qi;
+              if (qr < L) {
+                const int pi = sm.pi[b][qi];
+                const float up = exp2i(pi), down = exp2i(-pi) * p.softmax_scale;
+                uint16_t* row = p.dq + (int64_t)(doc_start + qr) * p.dqst + (int64_t)h * p.dqsh;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                  const _Float16 a0 = (_Float16)(dq[4 * j + 0] * up), a1 = (_Float16)(dq[4 * j + 1] * up);
+                  const _Float16 a2 = (_Float16)(dq[4 * j + 2] * up), a3 = (_Float16)(dq[4 * j + 3] * up);
+                  uint2 w;
+                  w.x = pack_bf16((float)a0 * down, (float)a1 * down);
+                  w.y = pack_bf16((float)a2 * down, (float)a3 * down);
+                  *reinterpret_cast<uint2*>(row + 32 * dblk + 8 * j + 4 * hh) = w;
+                }
+              }
+            }
+          }
+        }
+        if (ph + 1 < n_steps) store_step<D>(pre, sm, b3n);
+        __syncthreads();  // phase done: operands consumed, the next step's tiles stored
+        b3 = b3n;
       }
 
-      // ---- S, dP, P, dS and the E4M3 operands of this wave's 32 keys x 64 queries
-      int pp[8], pd[8];
-      int sp[2], sds[2];
-      auto scores = [&](auto masked) {
-        constexpr bool MASK = decltype(masked)::value;
-        v16f sacc[2], pacc[2];
+      // ---- dK, dV of this consumer's keys
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          sacc[qb] = v16f{};
-          pacc[qb] = v16f{};
+      for (int db = 0; db < NDB; ++db) { mfma_drain(dkacc[db]); mfma_drain(dvacc[db]); }
+      if (key_valid) {
+        uint16_t* krow = p.dk + (int64_t)(doc_start + key_rel) * p.dkst + (int64_t)g * p.dksh;
+        uint16_t* vrow = p.dv + (int64_t)(doc_start + key_rel) * p.dvst + (int64_t)g * p.dvsh;
+        const float ss = p.softmax_scale;
 #pragma unroll
-          for (int cc = 0; cc < NC; ++cc) {
-            const v8i kop = lds_read_row32<D>(sm.k, 32 * wave + n, 64 * cc + 32 * hh);
-            const v8i aq = lds_read_row32<D>(sm.q[b], 32 * qb + n, 64 * cc + 32 * hh);
-            sacc[qb] = mfma_scaled(aq, kop, sacc[qb], sm.sq[b][qb], k_scale);
-            const v8i vop = lds_read_row32<D>(sm.v, 32 * wave + n, 64 * cc + 32 * hh);
-            const v8i ad = lds_read_row32<D>(sm.dO[b], 32 * qb + n, 64 * cc + 32 * hh);
-            pacc[qb] = mfma_scaled(ad, vop, pacc[qb], sm.sdo[b][qb], v_scale);
-          }
-          mfma_drain(sacc[qb]);
-          mfma_drain(pacc[qb]);
-        }
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          float pmax = 0.f, dmax = 0.f;
-          float4 lse4[4], dd4[4];  // rows acc_row(4 j + e, hh) = 32 qb + 8 j + 4 hh + e
+        for (int db = 0; db < NDB; ++db)
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            lse4[j] = *reinterpret_cast<const float4*>(&sm.lse[b][32 * qb + 8 * j + 4 * hh]);
-            dd4[j] = *reinterpret_cast<const float4*>(&sm.dd[b][32 * qb + 8 * j + 4 * hh]);
+            const int d0 = 32 * db + 8 * j + 4 * hh;
+            uint2 wk, wv;
+            wk.x = pack_bf16(dkacc[db][4 * j] * ss, dkacc[db][4 * j + 1] * ss);
+            wk.y = pack_bf16(dkacc[db][4 * j + 2] * ss, dkacc[db][4 * j + 3] * ss);
+            wv.x = pack_bf16(dvacc[db][4 * j], dvacc[db][4 * j + 1]);
+            wv.y = pack_bf16(dvacc[db][4 * j + 2], dvacc[db][4 * j + 3]);
+            *reinterpret_cast<uint2*>(krow + d0) = wk;
+            *reinterpret_cast<uint2*>(vrow + d0) = wv;
           }
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const float lse_i = i % 4 == 0 ? lse4[i / 4].x : i % 4 == 1 ? lse4[i / 4].y : i % 4 == 2 ? lse4[i / 4].z : lse4[i / 4].w;
-            const float dd_i = i % 4 == 0 ? dd4[i / 4].x : i % 4 == 1 ? dd4[i / 4].y : i % 4 == 2 ? dd4[i / 4].z : dd4[i / 4].w;
-            float arg = fmaf(sacc[qb][i], c, -lse_i);
-            if constexpr (MASK) {
-              const int qr = q0 + 32 * qb + acc_row(i, hh);
-              arg = (key_rel <= qr && qr < L) ? arg : -__builtin_inff();  // 2^-inf = +0
-            }
-            const float pv = __builtin_amdgcn_exp2f(arg);
-            const float dsv = pv * (pacc[qb][i] - dd_i);
-            sacc[qb][i] = pv;
-            pacc[qb][i] = dsv;
-            pmax = fmaxf(pmax, pv);
-            dmax = fmaxf(dmax, fabsf(dsv));
-          }
-          sp[qb] = e8m0_roundup(wave_max_nonneg(pmax));
-          sds[qb] = e8m0_roundup(wave_max_nonneg(dmax));
-#pragma unroll
-          for (int w4 = 0; w4 < 4; ++w4) {
-            pp[4 * qb + w4] = pack4_fp8_scaled(sacc[qb][4 * w4], sacc[qb][4 * w4 + 1], sacc[qb][4 * w4 + 2],
-                                               sacc[qb][4 * w4 + 3], sp[qb]);
-            pd[4 * qb + w4] = pack4_fp8_scaled(pacc[qb][4 * w4], pacc[qb][4 * w4 + 1], pacc[qb][4 * w4 + 2],
-                                               pacc[qb][4 * w4 + 3], sds[qb]);
-          }
-        }
-      };
-      // all 64 x 128 pairs visible: the query tile lies wholly below the key tile and inside
-      // the document (then every key of the tile is inside it too)
-      if (qt >= 2 * kappa + 2 && q0 + QT <= L) scores(std::false_type{});
-      else scores(std::true_type{});
-
-      // ---- dV^T += dO^T Phat, dK^T += Q^T dShat
-      {
-        v8i bp, bd;
-#pragma unroll
-        for (int w = 0; w < 8; ++w) { bp[w] = pp[w]; bd[w] = pd[w]; }
-        const int sdo_h = sm.sdo[b][hh], sq_h = sm.sq[b][hh];
-        const int sp_h = (hh ? sp[1] : sp[0]) + 127, sds_h = (hh ? sds[1] : sds[0]) + 127;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const v8i ado = lds_read_tr32<D>(sm.dO[b], 0, 32 * db, lane);
-          dvacc[db] = mfma_scaled(ado, bp, dvacc[db], sdo_h, sp_h);
-          const v8i aq = lds_read_tr32<D>(sm.q[b], 0, 32 * db, lane);
-          dkacc[db] = mfma_scaled(aq, bd, dkacc[db], sq_h, sds_h);
-        }
       }
-
-      if (store_ds) {
-        // ---- dShat block: key row j holds 64 bytes, lane group hh's 32 bytes at 32 hh
-        const int64_t blk = ds_block(ds_base, kappa, n_qt, qt) * p.Hq + h;
-        uint4* dst = reinterpret_cast<uint4*>(p.ds_codes + blk * DS_BLOCK + (32 * wave + n) * QT + 32 * hh);
-        dst[0] = make_uint4(pd[0], pd[1], pd[2], pd[3]);
-        dst[1] = make_uint4(pd[4], pd[5], pd[6], pd[7]);
-        if (lane == 0) {
-          p.ds_scales[blk * 8 + wave] = (uint8_t)(sds[0] + 127);
-          p.ds_scales[blk * 8 + 4 + wave] = (uint8_t)(sds[1] + 127);
-        }
-      } else {
-        // ---- single key tile: dQ^T = K^T dShat^T here, the only contribution of its rows
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-#pragma unroll
-          for (int w4 = 0; w4 < 4; ++w4) {
-            const int qcol = 32 * qb + 8 * w4 + 4 * hh;
-            *reinterpret_cast<int*>(&sm.ds[lds_off<QT>(32 * wave + n, qcol)]) = pd[4 * qb + w4];
-          }
-          if (lane == 0) sm.ds_scale[qb][wave] = sds[qb] + 127;
-        }
-        __syncthreads();  // dShat tile and its exponents are complete
-        constexpr int NQB = (D == 128) ? 2 : 1;
-        const int dblk = (D == 128) ? wave : (wave & 1);
-        const int qb0 = (D == 128) ? 0 : (wave >> 1);
-#pragma unroll
-        for (int x = 0; x < NQB; ++x) {
-          const int qb = qb0 + x;
-          v16f dq = v16f{};
-#pragma unroll
-          for (int ci = 0; ci < 2; ++ci) {
-            const v8i ak = lds_read_tr32<D>(sm.k, 64 * ci, 32 * dblk, lane);
-            const v8i bs = lds_read_tr32<QT>(sm.ds, 64 * ci, 32 * qb, lane);
-            dq = mfma_scaled(ak, bs, dq, sm.sk[64 * ci + 32 * hh], sm.ds_scale[qb][2 * ci + hh]);
-          }
-          mfma_drain(dq);
-          const int qi = 32 * qb + n;
-          const int qr = q0 + qi;
-          if (qr < L) {
-            const int pi = sm.pi[b][qi];
-            const float up = exp2i(pi), down = exp2i(-pi) * p.softmax_scale;
-            uint16_t* row = p.dq + (int64_t)(doc_start + qr) * p.dqst + (int64_t)h * p.dqsh;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const _Float16 a0 = (_Float16)(dq[4 * j + 0] * up), a1 = (_Float16)(dq[4 * j + 1] * up);
-              const _Float16 a2 = (_Float16)(dq[4 * j + 2] * up), a3 = (_Float16)(dq[4 * j + 3] * up);
-              uint2 w;
-              w.x = pack_bf16((float)a0 * down, (float)a1 * down);
-              w.y = pack_bf16((float)a2 * down, (float)a3 * down);
-              *reinterpret_cast<uint2*>(row + 32 * dblk + 8 * j + 4 * hh) = w;
-            }
-          }
-        }
-      }
-
-      if (st + 1 < n_steps) store_step<D>(pre, sm, b ^ 1);
-      __syncthreads();  // this step's LDS readers are done; the next step's tiles are stored
-    }
-
-    // ---- dK, dV of this wave's keys
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) { mfma_drain_acc(dkacc[db]); mfma_drain_acc(dvacc[db]); }
-    if (key_valid) {
-      uint16_t* krow = p.dk + (int64_t)(doc_start + key_rel) * p.dkst + (int64_t)g * p.dksh;
-      uint16_t* vrow = p.dv + (int64_t)(doc_start + key_rel) * p.dvst + (int64_t)g * p.dvsh;
-      const float ss = p.softmax_scale;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int d0 = 32 * db + 8 * j + 4 * hh;
-          uint2 wk, wv;
-          wk.x = pack_bf16(dkacc[db][4 * j] * ss, dkacc[db][4 * j + 1] * ss);
-          wk.y = pack_bf16(dkacc[db][4 * j + 2] * ss, dkacc[db][4 * j + 3] * ss);
-          wv.x = pack_bf16(dvacc[db][4 * j], dvacc[db][4 * j + 1]);
-          wv.y = pack_bf16(dvacc[db][4 * j + 2], dvacc[db][4 * j + 3]);
-          *reinterpret_cast<uint2*>(krow + d0) = wk;
-          *reinterpret_cast<uint2*>(vrow + d0) = wv;
-        }
     }
   }
 }
