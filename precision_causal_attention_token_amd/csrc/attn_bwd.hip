@@ -44,7 +44,8 @@ namespace {
 constexpr int BWD_WAVES = 8;   // 4 producer + 4 consumer waves, one of each per SIMD
 constexpr int BWD_THREADS = 64 * BWD_WAVES;
 constexpr int QT = 64;                 // queries per step / per stored dShat block
-constexpr int DS_BLOCK = KV_TILE * QT;  // bytes of one stored dShat block
+constexpr int DS_BLOCK = KV_TILE * QT;  // code bytes of one stored dShat block
+constexpr int DS_STRIDE = DS_BLOCK + 16;  // codes, then the 8 exponent bytes (and 8 spare)
 constexpr int DQ_WAVES = 8;
 constexpr int DQ_THREADS = 64 * DQ_WAVES;
 
@@ -72,6 +73,7 @@ struct BwdSmem {
   int4 xd[2][4][2][64];       // dShat operand
   uint8_t ds[2][KV_TILE * QT];  // dShat [key][query], single-tile documents only
   uint8_t sk[KV_TILE];
+  uint8_t sv[KV_TILE];
   float lse[3][QT];
   float dd[3][QT];
   int pi[3][QT];
@@ -80,12 +82,16 @@ struct BwdSmem {
 };
 
 // One step's Q / dO rows and row statistics, held in registers between the global loads
-// (issued one phase ahead) and the LDS stores.
+// (issued one phase ahead) and the LDS stores.  The loads are unconditional (rows past the
+// document end read its last row, which always exists) and validity is applied when the
+// registers are stored, so no register is written while its load may still be in flight.
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+
 template <int D>
 struct StepRegs {
   static constexpr int TOTAL = QT * D / 16;                          // 16-byte chunks per tensor
   static constexpr int CH = (TOTAL + BWD_THREADS - 1) / BWD_THREADS;  // per thread
-  uint4 q[CH], dO[CH];
+  v4u q[CH], dO[CH];
   float lse, dd;
   int pi, sq, sdo;
 };
@@ -97,38 +103,31 @@ __device__ __forceinline__ void load_step(StepRegs<D>& r, const BwdParams& p, in
   const int q0 = QT * qt;
 #pragma unroll
   for (int i = 0; i < StepRegs<D>::CH; ++i) {
-    const int chunk = tid + i * BWD_THREADS;
+    const int chunk = min(tid + i * BWD_THREADS, StepRegs<D>::TOTAL - 1);
     const int row = chunk / CPR, col = (chunk % CPR) * 16;
-    const int qr = q0 + row;
-    r.q[i] = make_uint4(0, 0, 0, 0);
-    r.dO[i] = make_uint4(0, 0, 0, 0);
-    if (chunk < StepRegs<D>::TOTAL && qr < L) {
-      const int64_t off = ((int64_t)(doc_start + qr) * p.Hq + h) * D + col;
-      r.q[i] = *reinterpret_cast<const uint4*>(p.q + off);
-      r.dO[i] = *reinterpret_cast<const uint4*>(p.dO + off);
-    }
+    const int qr = min(q0 + row, L - 1);
+    const int64_t off = ((int64_t)(doc_start + qr) * p.Hq + h) * D + col;
+    r.q[i] = *reinterpret_cast<const v4u*>(p.q + off);
+    r.dO[i] = *reinterpret_cast<const v4u*>(p.dO + off);
   }
-  r.lse = 0.f; r.dd = 0.f; r.pi = 0; r.sq = 127; r.sdo = 127;
+  // row statistics: threads 0..63 one row each, threads 64, 65 the two 32-row blocks' scales
+  // (registers of other threads keep stale values, never stored)
   if (tid < QT) {
-    const int qr = q0 + tid;
-    if (qr < L) {
-      const int64_t ti = (int64_t)h * p.T + doc_start + qr;
-      r.lse = p.lse[ti];
-      r.dd = p.Dv[ti];
-      r.pi = p.pi[ti];
-    }
+    const int qr = min(q0 + tid, L - 1);
+    const int64_t ti = (int64_t)h * p.T + doc_start + qr;
+    r.lse = p.lse[ti];
+    r.dd = p.Dv[ti];
+    r.pi = p.pi[ti];
   } else if (tid < QT + 2) {
-    const int qr = q0 + 32 * (tid - QT);
-    if (qr < L) {
-      const int64_t ti = (int64_t)h * p.T + doc_start + qr;
-      r.sq = p.sq[ti];
-      r.sdo = p.sdo[ti];
-    }
+    const int qr = min(q0 + 32 * (tid - QT), L - 1);
+    const int64_t ti = (int64_t)h * p.T + doc_start + qr;
+    r.sq = p.sq[ti];
+    r.sdo = p.sdo[ti];
   }
 }
 
 template <int D>
-__device__ __forceinline__ void store_step(const StepRegs<D>& r, BwdSmem<D>& sm, int b) {
+__device__ __forceinline__ void store_step(const StepRegs<D>& r, BwdSmem<D>& sm, int b, int q0, int L) {
   const int tid = threadIdx.x;
   constexpr int CPR = D / 16;
 #pragma unroll
@@ -136,17 +135,20 @@ __device__ __forceinline__ void store_step(const StepRegs<D>& r, BwdSmem<D>& sm,
     const int chunk = tid + i * BWD_THREADS;
     if (chunk < StepRegs<D>::TOTAL) {
       const int row = chunk / CPR, col = (chunk % CPR) * 16;
-      *reinterpret_cast<uint4*>(&sm.q[b][lds_off<D>(row, col)]) = r.q[i];
-      *reinterpret_cast<uint4*>(&sm.dO[b][lds_off<D>(row, col)]) = r.dO[i];
+      const unsigned keep = q0 + row < L ? ~0u : 0u;
+      *reinterpret_cast<v4u*>(&sm.q[b][lds_off<D>(row, col)]) = r.q[i] & keep;
+      *reinterpret_cast<v4u*>(&sm.dO[b][lds_off<D>(row, col)]) = r.dO[i] & keep;
     }
   }
   if (tid < QT) {
-    sm.lse[b][tid] = r.lse;
-    sm.dd[b][tid] = r.dd;
-    sm.pi[b][tid] = r.pi;
+    const bool valid = q0 + tid < L;
+    sm.lse[b][tid] = valid ? r.lse : 0.f;
+    sm.dd[b][tid] = valid ? r.dd : 0.f;
+    sm.pi[b][tid] = valid ? r.pi : 0;
   } else if (tid < QT + 2) {
-    sm.sq[b][tid - QT] = r.sq;
-    sm.sdo[b][tid - QT] = r.sdo;
+    const bool valid = q0 + 32 * (tid - QT) < L;
+    sm.sq[b][tid - QT] = valid ? r.sq : 127;
+    sm.sdo[b][tid - QT] = valid ? r.sdo : 127;
   }
 }
 
@@ -196,8 +198,9 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
     const int n_steps = grp * nq;
 
     // ---- K / V tiles and the first step's tiles into LDS
-    __syncthreads();  // the previous unit no longer reads LDS
+    lds_barrier();  // the previous unit no longer reads LDS
     StepRegs<D> pre;
+    pre.lse = 0.f; pre.dd = 0.f; pre.pi = 0; pre.sq = 127; pre.sdo = 127;
     load_step<D>(pre, p, doc_start, L, g * grp, 2 * kappa);
     {
       constexpr int CPR = D / 16;
@@ -216,12 +219,13 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
       if (tid < KV_TILE) {
         const int key = KV_TILE * kappa + tid;
         sm.sk[tid] = key < L ? p.sk[(int64_t)g * T + doc_start + key] : (uint8_t)127;
+        sm.sv[tid] = key < L ? p.sv[(int64_t)g * T + doc_start + key] : (uint8_t)127;
       }
     }
-    store_step<D>(pre, sm, 0);
-    __syncthreads();
+    store_step<D>(pre, sm, 0, QT * 2 * kappa, L);
+    lds_barrier();
     const int k_scale = sm.sk[32 * kw + n];
-    const int v_scale = key_valid ? p.sv[(int64_t)g * T + doc_start + key_rel] : 127;
+    const int v_scale = sm.sv[32 * kw + n];
 
     // Each role runs its own phase loop (the same number of barriers in both), so the
     // consumers' accumulators are not live in the producers' code.
@@ -230,9 +234,12 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
       for (int ph = 0; ph <= n_steps; ++ph) {
         const int b3n = b3 == 2 ? 0 : b3 + 1;  // (phase + 1) % 3
         const int x2 = ph & 1;                 // operand hand-over buffer of step ph
+        int q0n = 0;  // first query of step ph + 1
         if (ph + 1 < n_steps) {
           const int hn = (ph + 1) / nq;
-          load_step<D>(pre, p, doc_start, L, g * grp + hn, 2 * kappa + (ph + 1 - hn * nq));
+          const int qtn = 2 * kappa + (ph + 1 - hn * nq);
+          q0n = QT * qtn;
+          load_step<D>(pre, p, doc_start, L, g * grp + hn, qtn);
         }
         if (ph < n_steps) {
           const int hi = ph / nq;
@@ -313,17 +320,7 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
               sm.xs_d[x2][qb][kw] = sds[qb] + 127;
             }
           }
-          if (store_ds) {
-            // dShat block: key row j holds 64 bytes, lane group hh's 32 bytes at 32 hh
-            const int64_t blk = ds_block(ds_base, kappa, n_qt, qt) * p.Hq + h;
-            int4* dst = reinterpret_cast<int4*>(p.ds_codes + blk * DS_BLOCK + (32 * kw + n) * QT + 32 * hh);
-            dst[0] = make_int4(pd[0], pd[1], pd[2], pd[3]);
-            dst[1] = make_int4(pd[4], pd[5], pd[6], pd[7]);
-            if (lane == 0) {
-              p.ds_scales[blk * 8 + kw] = (uint8_t)(sds[0] + 127);
-              p.ds_scales[blk * 8 + 4 + kw] = (uint8_t)(sds[1] + 127);
-            }
-          } else {
+          if (!store_ds) {
 #pragma unroll
             for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
@@ -333,8 +330,8 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
               }
           }
         }
-        if (ph + 1 < n_steps) store_step<D>(pre, sm, b3n);
-        __syncthreads();  // phase done: operands handed over, the next step's tiles stored
+        if (ph + 1 < n_steps) store_step<D>(pre, sm, b3n, q0n, L);
+        lds_barrier();  // phase done: operands handed over, the next step's tiles stored
         b3 = b3n;
       }
     } else {
@@ -345,9 +342,30 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
       for (int ph = 0; ph <= n_steps; ++ph) {
         const int b3p = b3 == 0 ? 2 : b3 - 1;  // (phase - 1) % 3
         const int b3n = b3 == 2 ? 0 : b3 + 1;  // (phase + 1) % 3
+        // The dShat block of step ph - 1 goes to the workspace first: issued before this phase's
+        // tile loads, the stores retire while the phase runs instead of holding up the wait for
+        // those loads (loads and stores share one in-order counter).
+        if (ph >= 1 && store_ds) {
+          const int st = ph - 1, xb = (ph & 1) ^ 1;
+          const int hi = st / nq;
+          const int qt = 2 * kappa + (st - hi * nq);
+          const int64_t blk = ds_block(ds_base, kappa, n_qt, qt) * p.Hq + g * grp + hi;
+          uint8_t* bbase = p.ds_store + blk * DS_STRIDE;
+          // key row j holds 64 bytes: lane group hh's 32 bytes of the dShat operand at 32 hh
+          int4* dst = reinterpret_cast<int4*>(bbase + (32 * kw + n) * QT + 32 * hh);
+          dst[0] = sm.xd[xb][kw][0][lane];
+          dst[1] = sm.xd[xb][kw][1][lane];
+          if (lane == 0) {
+            bbase[DS_BLOCK + kw] = (uint8_t)sm.xs_d[xb][0][kw];
+            bbase[DS_BLOCK + 4 + kw] = (uint8_t)sm.xs_d[xb][1][kw];
+          }
+        }
+        int q0n = 0;  // first query of step ph + 1
         if (ph + 1 < n_steps) {
           const int hn = (ph + 1) / nq;
-          load_step<D>(pre, p, doc_start, L, g * grp + hn, 2 * kappa + (ph + 1 - hn * nq));
+          const int qtn = 2 * kappa + (ph + 1 - hn * nq);
+          q0n = QT * qtn;
+          load_step<D>(pre, p, doc_start, L, g * grp + hn, qtn);
         }
         if (ph >= 1) {
           // ---- gradient products of step ph - 1
@@ -407,8 +425,8 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
             }
           }
         }
-        if (ph + 1 < n_steps) store_step<D>(pre, sm, b3n);
-        __syncthreads();  // phase done: operands consumed, the next step's tiles stored
+        if (ph + 1 < n_steps) store_step<D>(pre, sm, b3n, q0n, L);
+        lds_barrier();  // phase done: operands consumed, the next step's tiles stored
         b3 = b3n;
       }
 
@@ -479,12 +497,13 @@ __device__ __forceinline__ void dq_load(DqRegs<D>& r, const BwdParams& p, int do
     const int qt = qt0 + t;
     r.s[t] = make_uint4(0, 0, 0, 0);
     if (qt < n_qt && qt >= 2 * kappa)
-      r.s[t] = reinterpret_cast<const uint4*>(p.ds_codes + ((blk0 + t) * p.Hq + h) * DS_BLOCK)[tid];
+      r.s[t] = reinterpret_cast<const uint4*>(p.ds_store + ((blk0 + t) * p.Hq + h) * DS_STRIDE)[tid];
   }
   r.sc = make_uint2(0x7F7F7F7Fu, 0x7F7F7F7Fu);
   if (tid < 4) {
     const int qt = qt0 + tid;
-    if (qt < n_qt && qt >= 2 * kappa) r.sc = *reinterpret_cast<const uint2*>(p.ds_scales + ((blk0 + tid) * p.Hq + h) * 8);
+    if (qt < n_qt && qt >= 2 * kappa)
+      r.sc = *reinterpret_cast<const uint2*>(p.ds_store + ((blk0 + tid) * p.Hq + h) * DS_STRIDE + DS_BLOCK);
   }
   r.skb = 127;
   if (tid < KV_TILE) {
@@ -558,10 +577,10 @@ __global__ __launch_bounds__(DQ_THREADS) void dq_kernel(BwdParams p) {
       for (int j = 0; j < 8; ++j) acc16[db][j] = h2{0, 0};
 
     DqRegs<D> pre;
-    __syncthreads();  // the previous unit no longer reads LDS
+    lds_barrier();  // the previous unit no longer reads LDS
     dq_load<D>(pre, p, doc_start, L, n_qt, base, qt0, g, h, 0);
     dq_store<D>(pre, sm, 0);
-    __syncthreads();
+    lds_barrier();
     for (int kappa = 0; kappa <= kappa_hi; ++kappa) {
       const int b = kappa & 1;
       if (kappa < kappa_hi) dq_load<D>(pre, p, doc_start, L, n_qt, base, qt0, g, h, kappa + 1);
@@ -590,7 +609,7 @@ __global__ __launch_bounds__(DQ_THREADS) void dq_kernel(BwdParams p) {
         }
       }
       if (kappa < kappa_hi) dq_store<D>(pre, sm, b ^ 1);
-      __syncthreads();
+      lds_barrier();
     }
 
     if (active && row_valid) {

@@ -143,9 +143,9 @@ __global__ __launch_bounds__(FWD_THREADS) void fwd_kernel(FwdParams p) {
 
     TileRegs<D> pre;
     load_tile<D>(pre, p, g, doc_start, L, kappa_hi);
-    __syncthreads();  // previous unit's readers are done with both buffers
+    lds_barrier();  // previous unit's readers are done with both buffers
     store_tile<D>(pre, sm, 0);
-    __syncthreads();
+    lds_barrier();
     int buf = 0;
     for (int kappa = kappa_hi; kappa >= 0; --kappa) {
       if (kappa > 0) load_tile<D>(pre, p, g, doc_start, L, kappa - 1);
@@ -221,7 +221,7 @@ __global__ __launch_bounds__(FWD_THREADS) void fwd_kernel(FwdParams p) {
       }
       if (kappa > 0) {
         store_tile<D>(pre, sm, buf ^ 1);
-        __syncthreads();
+        lds_barrier();
         buf ^= 1;
       }
     }

@@ -44,6 +44,16 @@ __device__ __forceinline__ v16f mfma_scaled(const v8i& a, const v8i& b, const v1
 __device__ __forceinline__ void mfma_drain(v16f& acc) { asm volatile("s_nop 3" : "+v"(acc)); }
 __device__ __forceinline__ void mfma_drain_acc(v16f& acc) { asm volatile("s_nop 3" : "+a"(acc)); }
 
+// Workgroup barrier for LDS hand-offs.  The fences cover LDS only, so global loads still in
+// flight (prefetches, waited for where their registers are used) and global stores (results no
+// wave of this workgroup reads back) do not hold the barrier up; __syncthreads() would wait for
+// every outstanding global access at each barrier.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Accumulator row held by register i of lane group h.
 __device__ __forceinline__ int acc_row(int i, int h) { return 8 * (i >> 2) + 4 * h + (i & 3); }
 

@@ -33,8 +33,9 @@ int num_cus() {
 
 namespace {
 // Backward workspace: status word, pi [Hq, T], per-document block offsets, then the dShat store
-// (8 KiB of codes and 8 exponent bytes per (block, query head)).
-constexpr size_t DS_BLOCK_BYTES = 128 * 64;
+// (per (block, query head): 8 KiB of codes, 8 exponent bytes, 8 spare, so blocks stay 16-byte
+// aligned).
+constexpr size_t DS_BLOCK_BYTES = 128 * 64 + 16;
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 size_t bwd_fixed_bytes(int32_t T, int32_t Hq, int32_t n_docs) {
   return 256 + align256((size_t)T * Hq * 2) + align256(((size_t)n_docs + 1) * 8);
@@ -152,7 +153,7 @@ size_t flamia_bwd_workspace_bytes(const int32_t* cu_seqlens_host, int32_t n_docs
   if (T < 0 || Hq < 0 || n_docs < 0 || (n_docs > 0 && !cu_seqlens_host)) return 0;
   int64_t blocks = 0;
   for (int32_t k = 0; k < n_docs; ++k) blocks += doc_blocks((int64_t)cu_seqlens_host[k + 1] - cu_seqlens_host[k]);
-  return bwd_fixed_bytes(T, Hq, n_docs) + (size_t)blocks * Hq * (DS_BLOCK_BYTES + 8);
+  return bwd_fixed_bytes(T, Hq, n_docs) + (size_t)blocks * Hq * DS_BLOCK_BYTES;
 }
 
 flamia_status flamia_bwd(const flamia_bwd_args* a, void* stream) {
@@ -198,9 +199,8 @@ flamia_status flamia_bwd(const flamia_bwd_args* a, void* stream) {
   off += align256((size_t)a->T * a->Hq * 2);
   p.doc_base = reinterpret_cast<int64_t*>(ws + off);
   off += align256(((size_t)a->n_docs + 1) * 8);
-  const size_t cap = (a->workspace_bytes - off) / (DS_BLOCK_BYTES + 8);
-  p.ds_codes = ws + off;
-  p.ds_scales = ws + off + cap * DS_BLOCK_BYTES;
+  const size_t cap = (a->workspace_bytes - off) / DS_BLOCK_BYTES;
+  p.ds_store = ws + off;
   p.ds_capacity = (int64_t)cap;
   p.pi_out = a->dq_exp_out;
   p.causal = a->causal_dq_scale ? 1 : 0;
