@@ -76,79 +76,41 @@ struct BwdSmem {
   uint8_t sv[KV_TILE];
   float lse[3][QT];
   float dd[3][QT];
-  int pi[3][QT];
   int sq[3][2], sdo[3][2];
   int xs_p[2][2][4], xs_d[2][2][4];  // block exponent bytes of (query block, key group)
 };
 
-// One step's Q / dO rows and row statistics, held in registers between the global loads
-// (issued one phase ahead) and the LDS stores.  The loads are unconditional (rows past the
-// document end read its last row, which always exists) and validity is applied when the
-// registers are stored, so no register is written while its load may still be in flight.
-typedef unsigned v4u __attribute__((ext_vector_type(4)));
+// Step tiles go from global memory straight into LDS (16-byte direct loads: lane l of a wave
+// writes bytes 16 l .. 16 l + 15 of the wave's 1 KiB LDS block), issued by the four consumer
+// waves one phase ahead.  Each lane fetches the global chunk that belongs at its LDS position
+// under the tile's swizzle.  Rows past the document end repeat its last row: every use of those
+// rows is masked to zero, and the repeated values are finite.
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
 
 template <int D>
-struct StepRegs {
-  static constexpr int TOTAL = QT * D / 16;                          // 16-byte chunks per tensor
-  static constexpr int CH = (TOTAL + BWD_THREADS - 1) / BWD_THREADS;  // per thread
-  v4u q[CH], dO[CH];
-  float lse, dd;
-  int pi, sq, sdo;
-};
-
-template <int D>
-__device__ __forceinline__ void load_step(StepRegs<D>& r, const BwdParams& p, int doc_start, int L, int h, int qt) {
-  const int tid = threadIdx.x;
-  constexpr int CPR = D / 16;
+__device__ __forceinline__ void issue_step_loads(const BwdParams& p, BwdSmem<D>& sm, int b, int doc_start, int L,
+                                                 int h, int qt, int cw, int lane) {
+  constexpr int CPR = D / 16;                    // 16-byte chunks per row
+  constexpr int BLOCKS = QT * D / 1024;          // 1 KiB wave blocks per tile (4 or 8)
+  constexpr int PER_WAVE = 2 * BLOCKS / 4;       // Q and dO blocks per consumer wave
   const int q0 = QT * qt;
 #pragma unroll
-  for (int i = 0; i < StepRegs<D>::CH; ++i) {
-    const int chunk = min(tid + i * BWD_THREADS, StepRegs<D>::TOTAL - 1);
-    const int row = chunk / CPR, col = (chunk % CPR) * 16;
+  for (int i = 0; i < PER_WAVE; ++i) {
+    const int wb = cw * PER_WAVE + i;            // 0 .. 2 BLOCKS - 1: Q blocks, then dO blocks
+    const bool is_do = wb >= BLOCKS;
+    const int blk = is_do ? wb - BLOCKS : wb;
+    const int pos = blk * 64 + lane;             // 16-byte chunk position in the tile
+    const int row = pos / CPR, pc = pos % CPR;
+    const int lc = pc ^ lds_swizzle<D>(row);     // logical chunk stored at this position
     const int qr = min(q0 + row, L - 1);
-    const int64_t off = ((int64_t)(doc_start + qr) * p.Hq + h) * D + col;
-    r.q[i] = *reinterpret_cast<const v4u*>(p.q + off);
-    r.dO[i] = *reinterpret_cast<const v4u*>(p.dO + off);
+    const uint8_t* src = (is_do ? p.dO : p.q) + ((int64_t)(doc_start + qr) * p.Hq + h) * D + 16 * lc;
+    uint8_t* dst = (is_do ? sm.dO[b] : sm.q[b]) + blk * 1024;
+    __builtin_amdgcn_global_load_lds(src, (lds_void_ptr)dst, 16, 0, 0);
   }
-  // row statistics: threads 0..63 one row each, threads 64, 65 the two 32-row blocks' scales
-  // (registers of other threads keep stale values, never stored)
-  if (tid < QT) {
-    const int qr = min(q0 + tid, L - 1);
-    const int64_t ti = (int64_t)h * p.T + doc_start + qr;
-    r.lse = p.lse[ti];
-    r.dd = p.Dv[ti];
-    r.pi = p.pi[ti];
-  } else if (tid < QT + 2) {
-    const int qr = min(q0 + 32 * (tid - QT), L - 1);
-    const int64_t ti = (int64_t)h * p.T + doc_start + qr;
-    r.sq = p.sq[ti];
-    r.sdo = p.sdo[ti];
-  }
-}
-
-template <int D>
-__device__ __forceinline__ void store_step(const StepRegs<D>& r, BwdSmem<D>& sm, int b, int q0, int L) {
-  const int tid = threadIdx.x;
-  constexpr int CPR = D / 16;
-#pragma unroll
-  for (int i = 0; i < StepRegs<D>::CH; ++i) {
-    const int chunk = tid + i * BWD_THREADS;
-    if (chunk < StepRegs<D>::TOTAL) {
-      const int row = chunk / CPR, col = (chunk % CPR) * 16;
-      const unsigned keep = q0 + row < L ? ~0u : 0u;
-      *reinterpret_cast<v4u*>(&sm.q[b][lds_off<D>(row, col)]) = r.q[i] & keep;
-      *reinterpret_cast<v4u*>(&sm.dO[b][lds_off<D>(row, col)]) = r.dO[i] & keep;
-    }
-  }
-  if (tid < QT) {
-    const bool valid = q0 + tid < L;
-    sm.lse[b][tid] = valid ? r.lse : 0.f;
-    sm.dd[b][tid] = valid ? r.dd : 0.f;
-    sm.pi[b][tid] = valid ? r.pi : 0;
-  } else if (tid < QT + 2) {
-    const bool valid = q0 + 32 * (tid - QT) < L;
-    sm.sq[b][tid - QT] = valid ? r.sq : 127;
-    sm.sdo[b][tid - QT] = valid ? r.sdo : 127;
+  if (cw < 2) {  // row statistics: one float per lane
+    const int qr = min(q0 + lane, L - 1);
+    const float* src = (cw == 0 ? p.lse : p.Dv) + (int64_t)h * p.T + doc_start + qr;
+    __builtin_amdgcn_global_load_lds(src, (lds_void_ptr)(cw == 0 ? sm.lse[b] : sm.dd[b]), 4, 0, 0);
   }
 }
 
@@ -199,9 +161,29 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
 
     // ---- K / V tiles and the first step's tiles into LDS
     lds_barrier();  // the previous unit no longer reads LDS
-    StepRegs<D> pre;
-    pre.lse = 0.f; pre.dd = 0.f; pre.pi = 0; pre.sq = 127; pre.sdo = 127;
-    load_step<D>(pre, p, doc_start, L, g * grp, 2 * kappa);
+    const int cw = wave - 4;  // consumer index (loads)
+    // block scales of the two 32-row query blocks of a step: two lanes of consumer 2 load them
+    // into registers and store them to LDS at the end of the phase
+    auto scale_loads = [&](int h, int qt, int& rsq, int& rsdo) {
+      if (cw == 2 && lane < 2) {
+        const int qr = min(QT * qt + 32 * lane, L - 1);
+        const int64_t ti = (int64_t)h * T + doc_start + qr;
+        rsq = p.sq[ti];
+        rsdo = p.sdo[ti];
+      }
+    };
+    auto scale_store = [&](int b, int qt, int rsq, int rsdo) {
+      if (cw == 2 && lane < 2) {
+        const bool valid = QT * qt + 32 * lane < L;
+        sm.sq[b][lane] = valid ? rsq : 127;
+        sm.sdo[b][lane] = valid ? rsdo : 127;
+      }
+    };
+    int rsq = 127, rsdo = 127;
+    if (!producer) {
+      issue_step_loads<D>(p, sm, 0, doc_start, L, g * grp, 2 * kappa, cw, lane);
+      scale_loads(g * grp, 2 * kappa, rsq, rsdo);
+    }
     {
       constexpr int CPR = D / 16;
       for (int chunk = tid; chunk < KV_TILE * CPR; chunk += BWD_THREADS) {
@@ -222,7 +204,10 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
         sm.sv[tid] = key < L ? p.sv[(int64_t)g * T + doc_start + key] : (uint8_t)127;
       }
     }
-    store_step<D>(pre, sm, 0, QT * 2 * kappa, L);
+    if (!producer) {
+      __builtin_amdgcn_s_waitcnt(0);  // the direct loads have landed
+      scale_store(0, 2 * kappa, rsq, rsdo);
+    }
     lds_barrier();
     const int k_scale = sm.sk[32 * kw + n];
     const int v_scale = sm.sv[32 * kw + n];
@@ -234,13 +219,6 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
       for (int ph = 0; ph <= n_steps; ++ph) {
         const int b3n = b3 == 2 ? 0 : b3 + 1;  // (phase + 1) % 3
         const int x2 = ph & 1;                 // operand hand-over buffer of step ph
-        int q0n = 0;  // first query of step ph + 1
-        if (ph + 1 < n_steps) {
-          const int hn = (ph + 1) / nq;
-          const int qtn = 2 * kappa + (ph + 1 - hn * nq);
-          q0n = QT * qtn;
-          load_step<D>(pre, p, doc_start, L, g * grp + hn, qtn);
-        }
         if (ph < n_steps) {
           const int hi = ph / nq;
           const int h = g * grp + hi;
@@ -330,7 +308,6 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
               }
           }
         }
-        if (ph + 1 < n_steps) store_step<D>(pre, sm, b3n, q0n, L);
         lds_barrier();  // phase done: operands handed over, the next step's tiles stored
         b3 = b3n;
       }
@@ -360,12 +337,12 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
             bbase[DS_BLOCK + 4 + kw] = (uint8_t)sm.xs_d[xb][1][kw];
           }
         }
-        int q0n = 0;  // first query of step ph + 1
-        if (ph + 1 < n_steps) {
+        int qtn = 0;
+        if (ph + 1 < n_steps) {  // step ph + 1's tiles, straight into LDS
           const int hn = (ph + 1) / nq;
-          const int qtn = 2 * kappa + (ph + 1 - hn * nq);
-          q0n = QT * qtn;
-          load_step<D>(pre, p, doc_start, L, g * grp + hn, qtn);
+          qtn = 2 * kappa + (ph + 1 - hn * nq);
+          issue_step_loads<D>(p, sm, b3n, doc_start, L, g * grp + hn, qtn, cw, lane);
+          scale_loads(g * grp + hn, qtn, rsq, rsdo);
         }
         if (ph >= 1) {
           // ---- gradient products of step ph - 1
@@ -409,7 +386,7 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
               const int qi = 32 * qb + n;
               const int qr = q0 + qi;
               if (qr < L) {
-                const int pi = sm.pi[b][qi];
+                const int pi = p.pi[(int64_t)h * T + doc_start + qr];
                 const float up = exp2i(pi), down = exp2i(-pi) * p.softmax_scale;
                 uint16_t* row = p.dq + (int64_t)(doc_start + qr) * p.dqst + (int64_t)h * p.dqsh;
 #pragma unroll
@@ -425,7 +402,10 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
             }
           }
         }
-        if (ph + 1 < n_steps) store_step<D>(pre, sm, b3n, q0n, L);
+        if (ph + 1 < n_steps) {
+          __builtin_amdgcn_s_waitcnt(0);  // the direct loads have landed
+          scale_store(b3n, qtn, rsq, rsdo);
+        }
         lds_barrier();  // phase done: operands consumed, the next step's tiles stored
         b3 = b3n;
       }
