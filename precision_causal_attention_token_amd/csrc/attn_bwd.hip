@@ -194,6 +194,9 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
           const int64_t off = ((int64_t)(doc_start + key) * p.Hkv + g) * D + col;
           k4 = *reinterpret_cast<const uint4*>(p.k + off);
           v4 = *reinterpret_cast<const uint4*>(p.v + off);
+          // V is kept negated (E4M3 sign bits flipped, exact): the dP products then come out as
+          // D - dP on top of an accumulator that starts at D
+          v4.x ^= 0x80808080u; v4.y ^= 0x80808080u; v4.z ^= 0x80808080u; v4.w ^= 0x80808080u;
         }
         *reinterpret_cast<uint4*>(&sm.k[lds_off<D>(row, col)]) = k4;
         *reinterpret_cast<uint4*>(&sm.v[lds_off<D>(row, col)]) = v4;
@@ -215,6 +218,13 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
     // Each role runs its own phase loop (the same number of barriers in both), so the
     // consumers' accumulators are not live in the producers' code.
     if (producer) {
+      // this wave's K and (negated) V operand rows, the same in every step of the unit
+      v8i kreg[NC], vreg[NC];
+#pragma unroll
+      for (int cc = 0; cc < NC; ++cc) {
+        kreg[cc] = lds_read_row32<D>(sm.k, 32 * kw + n, 64 * cc + 32 * hh);
+        vreg[cc] = lds_read_row32<D>(sm.v, 32 * kw + n, 64 * cc + 32 * hh);
+      }
       int b3 = 0;  // phase % 3
       for (int ph = 0; ph <= n_steps; ++ph) {
         const int b3n = b3 == 2 ? 0 : b3 + 1;  // (phase + 1) % 3
@@ -232,17 +242,26 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
             // both query blocks' products are issued first, so the matrix cores work on block 1
             // while the vector unit processes block 0
             v16f sacc2[2], pacc2[2];
+            // the dP accumulators start at D of their rows: accumulator register 4 j + e holds
+            // row 32 qb + 8 j + 4 hh + e, the float4 at that row
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                const float4 d4 = *reinterpret_cast<const float4*>(&sm.dd[b][32 * qb + 8 * j + 4 * hh]);
+                pacc2[qb][4 * j] = d4.x; pacc2[qb][4 * j + 1] = d4.y;
+                pacc2[qb][4 * j + 2] = d4.z; pacc2[qb][4 * j + 3] = d4.w;
+              }
 #pragma unroll
             for (int cc = 0; cc < NC; ++cc) {
-              const v8i kop = lds_read_row32<D>(sm.k, 32 * kw + n, 64 * cc + 32 * hh);
-              const v8i vop = lds_read_row32<D>(sm.v, 32 * kw + n, 64 * cc + 32 * hh);
 #pragma unroll
               for (int qb = 0; qb < 2; ++qb) {
                 const v8i aq = lds_read_row32<D>(sm.q[b], 32 * qb + n, 64 * cc + 32 * hh);
-                sacc2[qb] = mfma_scaled(aq, kop, cc ? sacc2[qb] : v16f{}, sm.sq[b][qb], k_scale);
+                sacc2[qb] = mfma_scaled(aq, kreg[cc], cc ? sacc2[qb] : v16f{}, sm.sq[b][qb], k_scale);
                 const v8i ad = lds_read_row32<D>(sm.dO[b], 32 * qb + n, 64 * cc + 32 * hh);
-                pacc2[qb] = mfma_scaled(ad, vop, cc ? pacc2[qb] : v16f{}, sm.sdo[b][qb], v_scale);
+                pacc2[qb] = mfma_scaled(ad, vreg[cc], pacc2[qb], sm.sdo[b][qb], v_scale);  // D - dP
               }
+              __builtin_amdgcn_sched_barrier(0);  // one column chunk of operands live at a time
             }
 #pragma unroll
             for (int qb = 0; qb < 2; ++qb) {
@@ -250,23 +269,20 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
               mfma_drain(sacc);
               mfma_drain(pacc);
               float pmax = 0.f, dmax = 0.f;
-              float4 lse4[4], dd4[4];  // rows acc_row(4 j + e, hh) = 32 qb + 8 j + 4 hh + e
+              float4 lse4[4];  // rows acc_row(4 j + e, hh) = 32 qb + 8 j + 4 hh + e
 #pragma unroll
-              for (int j = 0; j < 4; ++j) {
+              for (int j = 0; j < 4; ++j)
                 lse4[j] = *reinterpret_cast<const float4*>(&sm.lse[b][32 * qb + 8 * j + 4 * hh]);
-                dd4[j] = *reinterpret_cast<const float4*>(&sm.dd[b][32 * qb + 8 * j + 4 * hh]);
-              }
 #pragma unroll
               for (int i = 0; i < 16; ++i) {
                 const float lse_i = i % 4 == 0 ? lse4[i / 4].x : i % 4 == 1 ? lse4[i / 4].y : i % 4 == 2 ? lse4[i / 4].z : lse4[i / 4].w;
-                const float dd_i = i % 4 == 0 ? dd4[i / 4].x : i % 4 == 1 ? dd4[i / 4].y : i % 4 == 2 ? dd4[i / 4].z : dd4[i / 4].w;
                 float arg = fmaf(sacc[i], c, -lse_i);
                 if constexpr (MASK) {
                   const int qr = q0 + 32 * qb + acc_row(i, hh);
                   arg = (key_rel <= qr && qr < L) ? arg : -__builtin_inff();  // 2^-inf = +0
                 }
                 const float pv = __builtin_amdgcn_exp2f(arg);
-                const float dsv = pv * (pacc[i] - dd_i);
+                const float dsv = -(pv * pacc[i]);  // P (dP - D)
                 sacc[i] = pv;
                 pacc[i] = dsv;
                 pmax = fmaxf(pmax, pv);

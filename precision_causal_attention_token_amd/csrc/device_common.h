@@ -150,7 +150,8 @@ __device__ __forceinline__ int pack4_fp8(float a0, float a1, float a2, float a3)
 typedef short v2s __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ int pack4_fp8_scaled(float a0, float a1, float a2, float a3, int s) {
   const float scale = __uint_as_float((uint32_t)(127 + s) << 23);
-  const v2s lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(v2s{0, 0}, a0, a1, scale, false);
+  // the first conversion's upper half is overwritten by the second: any value will do there
+  const v2s lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(__builtin_bit_cast(v2s, a0), a0, a1, scale, false);
   const v2s r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lo, a2, a3, scale, true);
   return __builtin_bit_cast(int, r);
 }
@@ -172,17 +173,19 @@ __device__ __forceinline__ float wave_max(float x) {
   return fmaxf(__int_as_float((int)b[0]), __int_as_float((int)b[1]));
 }
 // Maximum over the wave of a non-negative float, as an unsigned maximum of the bit patterns
-// (the same order for non-negative floats; each DPP step is one instruction).
+// (the same order for non-negative floats).  Four DPP steps give every lane its row's maximum;
+// row_bcast:15 then row_bcast:31 carry the row maxima up to the last row, and lane 63 holds the
+// wave's maximum, returned as a wave-uniform value (so what follows can run on the scalar unit).
+// Each step is one vector instruction: the DPP move folds into the maximum.
 __device__ __forceinline__ float wave_max_nonneg(float x) {
   uint32_t u = __float_as_uint(x);
-  u = max(u, (uint32_t)__builtin_amdgcn_mov_dpp((int)u, 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
-  u = max(u, (uint32_t)__builtin_amdgcn_mov_dpp((int)u, 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
-  u = max(u, (uint32_t)__builtin_amdgcn_mov_dpp((int)u, 0x124, 0xF, 0xF, false));  // row_ror:4
-  u = max(u, (uint32_t)__builtin_amdgcn_mov_dpp((int)u, 0x128, 0xF, 0xF, false));  // row_ror:8
-  auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-  u = max((uint32_t)a[0], (uint32_t)a[1]);
-  auto b = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  return __uint_as_float(max((uint32_t)b[0], (uint32_t)b[1]));
+  u = max(u, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
+  u = max(u, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
+  u = max(u, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, 0x124, 0xF, 0xF, false));  // row_ror:4
+  u = max(u, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, 0x128, 0xF, 0xF, false));  // row_ror:8
+  u = max(u, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, 0x142, 0xA, 0xF, false));  // row_bcast:15, rows 1, 3
+  u = max(u, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, 0x143, 0xC, 0xF, false));  // row_bcast:31, rows 2, 3
+  return __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)u, 63));
 }
 // Combine the two lane groups (l and l ^ 32).
 __device__ __forceinline__ float halves_max(float x) {
