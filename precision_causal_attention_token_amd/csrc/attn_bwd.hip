@@ -45,6 +45,7 @@ constexpr int BWD_WAVES = 8;   // 4 producer + 4 consumer waves, one of each per
 constexpr int BWD_THREADS = 64 * BWD_WAVES;
 constexpr int QT = 64;                 // queries per step / per stored dShat block
 constexpr int DS_BLOCK = KV_TILE * QT;  // code bytes of one stored dShat block
+constexpr int NBUF = 4;                 // step tile buffers of the key-stationary pass
 constexpr int DS_STRIDE = DS_BLOCK + 16;  // codes, then the 8 exponent bytes (and 8 spare)
 constexpr int DQ_WAVES = 8;
 constexpr int DQ_THREADS = 64 * DQ_WAVES;
@@ -65,8 +66,8 @@ __device__ __forceinline__ int ds_pos_query(int pos) {
 
 template <int D>
 struct BwdSmem {
-  uint8_t q[3][QT * D];       // step s in buffer s % 3: producers read step k, consumers k - 1,
-  uint8_t dO[3][QT * D];      // the loader fills k + 1
+  uint8_t q[NBUF][QT * D];    // step s in buffer s % 4: in phase k producers form the products of
+  uint8_t dO[NBUF][QT * D];   // step k + 1, consumers read step k - 1, the loads fill step k + 2
   uint8_t k[KV_TILE * D];
   uint8_t v[KV_TILE * D];
   int4 xp[2][4][2][64];       // Phat operand of (key group) in lane order, 2 x 16 bytes per lane
@@ -74,15 +75,15 @@ struct BwdSmem {
   uint8_t ds[2][KV_TILE * QT];  // dShat [key][query], single-tile documents only
   uint8_t sk[KV_TILE];
   uint8_t sv[KV_TILE];
-  float lse[3][QT];
-  float dd[3][QT];
-  int sq[3][2], sdo[3][2];
+  float lse[NBUF][QT];
+  float dd[NBUF][QT];
+  int sq[NBUF][2], sdo[NBUF][2];
   int xs_p[2][2][4], xs_d[2][2][4];  // block exponent bytes of (query block, key group)
 };
 
 // Step tiles go from global memory straight into LDS (16-byte direct loads: lane l of a wave
 // writes bytes 16 l .. 16 l + 15 of the wave's 1 KiB LDS block), issued by the four consumer
-// waves one phase ahead.  Each lane fetches the global chunk that belongs at its LDS position
+// waves two phases ahead.  Each lane fetches the global chunk that belongs at its LDS position
 // under the tile's swizzle.  Rows past the document end repeat its last row: every use of those
 // rows is masked to zero, and the repeated values are finite.
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
@@ -116,10 +117,12 @@ __device__ __forceinline__ void issue_step_loads(const BwdParams& p, BwdSmem<D>&
 
 // Key-stationary pass.  Producer wave w (0..3) owns keys 32 w .. 32 w + 31 of the tile: per
 // 64-query step it forms S and dP, the softmax terms, and the E4M3 Phat / dShat operands with
-// their 32 x 32 block exponents, hands them over in LDS and stores dShat.  Consumer wave 4 + w
-// holds dK^T and dV^T of the same keys and runs the gradient products one step behind, so its
-// matrix instructions overlap the producer's vector work on the same SIMD.  Phase k: producers
-// on step k, consumers on step k - 1, every thread loads step k + 1; one barrier per phase.
+// their 32 x 32 block exponents, hands them over in LDS and stores dShat from its registers.
+// Its matrix products run one query block ahead of its softmax terms, so the two overlap.
+// Consumer wave 4 + w holds dK^T and dV^T of the same keys and runs the gradient products one
+// step behind, so its matrix instructions overlap the producer's vector work on the same SIMD.
+// Phase k: producers finish step k and form the products of step k + 1, consumers work on step
+// k - 1 and load step k + 2; one barrier per phase.
 template <int D>
 __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
   constexpr int NC = D / 64;
@@ -128,7 +131,8 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
 
   if (*p.status) return;  // the dShat store does not fit the workspace
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  // the wave index is uniform: in a scalar register, everything derived from it stays scalar
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 31, hh = lane >> 5;
   const bool producer = wave < 4;
   const int kw = wave & 3;  // key group of both roles
@@ -145,12 +149,19 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
     if (u >= n_units) break;
     const int4 it = items[u / p.Hkv];
     const int g = u % p.Hkv;
-    const int doc = it.x, kappa = it.y;
-    const int doc_start = p.cu[doc];
-    const int L = p.cu[doc + 1] - doc_start;
+    // unit values are the same in every lane: kept in scalar registers (vector loads would
+    // leave them in vector registers for the whole unit)
+    const int doc = __builtin_amdgcn_readfirstlane(it.x), kappa = __builtin_amdgcn_readfirstlane(it.y);
+    const int doc_start = __builtin_amdgcn_readfirstlane(p.cu[doc]);
+    const int L = __builtin_amdgcn_readfirstlane(p.cu[doc + 1]) - doc_start;
     const int n_qt = (L + QT - 1) / QT;
     const bool store_ds = L > KV_TILE;  // two or more key tiles: dQ in the query-stationary kernel
-    const int64_t ds_base = store_ds ? p.doc_base[doc] : 0;
+    int64_t ds_base = 0;
+    if (store_ds) {
+      const int64_t v = p.doc_base[doc];
+      ds_base = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(v >> 32)) << 32) |
+                          (uint32_t)__builtin_amdgcn_readfirstlane((int)v));
+    }
     const int key_rel = KV_TILE * kappa + 32 * kw + n;
     const bool key_valid = key_rel < L;
 
@@ -179,14 +190,27 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
         sm.sdo[b][lane] = valid ? rsdo : 127;
       }
     };
-    int rsq = 127, rsdo = 127;
+    // query head and 64-query tile of step st
+    auto step_qt = [&](int st, int& h) {
+      const int hi = st / nq;
+      h = g * grp + hi;
+      return 2 * kappa + (st - hi * nq);
+    };
+    int rsq = 127, rsdo = 127, rsq1 = 127, rsdo1 = 127;
     if (!producer) {
       issue_step_loads<D>(p, sm, 0, doc_start, L, g * grp, 2 * kappa, cw, lane);
       scale_loads(g * grp, 2 * kappa, rsq, rsdo);
+      if (n_steps > 1) {
+        int h1;
+        const int qt1 = step_qt(1, h1);
+        issue_step_loads<D>(p, sm, 1, doc_start, L, h1, qt1, cw, lane);
+        scale_loads(h1, qt1, rsq1, rsdo1);
+      }
     }
     {
       constexpr int CPR = D / 16;
-      for (int chunk = tid; chunk < KV_TILE * CPR; chunk += BWD_THREADS) {
+      // consumer threads only: the producers' dShat stores stay outside the wait for these loads
+      for (int chunk = tid - BWD_THREADS / 2; chunk >= 0 && chunk < KV_TILE * CPR; chunk += BWD_THREADS / 2) {
         const int row = chunk / CPR, col = (chunk % CPR) * 16;
         const int key = KV_TILE * kappa + row;
         uint4 k4 = make_uint4(0, 0, 0, 0), v4 = make_uint4(0, 0, 0, 0);
@@ -201,15 +225,20 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
         *reinterpret_cast<uint4*>(&sm.k[lds_off<D>(row, col)]) = k4;
         *reinterpret_cast<uint4*>(&sm.v[lds_off<D>(row, col)]) = v4;
       }
-      if (tid < KV_TILE) {
-        const int key = KV_TILE * kappa + tid;
-        sm.sk[tid] = key < L ? p.sk[(int64_t)g * T + doc_start + key] : (uint8_t)127;
-        sm.sv[tid] = key < L ? p.sv[(int64_t)g * T + doc_start + key] : (uint8_t)127;
+      if (tid >= BWD_THREADS / 2 && tid < BWD_THREADS / 2 + KV_TILE) {
+        const int r = tid - BWD_THREADS / 2;
+        const int key = KV_TILE * kappa + r;
+        sm.sk[r] = key < L ? p.sk[(int64_t)g * T + doc_start + key] : (uint8_t)127;
+        sm.sv[r] = key < L ? p.sv[(int64_t)g * T + doc_start + key] : (uint8_t)127;
       }
     }
     if (!producer) {
       __builtin_amdgcn_s_waitcnt(0);  // the direct loads have landed
       scale_store(0, 2 * kappa, rsq, rsdo);
+      if (n_steps > 1) {
+        int h1;
+        scale_store(1, step_qt(1, h1), rsq1, rsdo1);
+      }
     }
     lds_barrier();
     const int k_scale = sm.sk[32 * kw + n];
@@ -218,6 +247,13 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
     // Each role runs its own phase loop (the same number of barriers in both), so the
     // consumers' accumulators are not live in the producers' code.
     if (producer) {
+      // lane-dependent values re-derived from an opaque copy of the lane index: addresses
+      // built from them are local to this role instead of shared with (and kept alive
+      // through) the other role's code
+      int lane_r = lane;
+      asm volatile("" : "+v"(lane_r));
+      const int lane = lane_r, n = lane_r & 31, hh = lane_r >> 5;
+      const int key_rel = KV_TILE * kappa + 32 * kw + n;
       // this wave's K and (negated) V operand rows, the same in every step of the unit
       v8i kreg[NC], vreg[NC];
 #pragma unroll
@@ -225,145 +261,171 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
         kreg[cc] = lds_read_row32<D>(sm.k, 32 * kw + n, 64 * cc + 32 * hh);
         vreg[cc] = lds_read_row32<D>(sm.v, 32 * kw + n, 64 * cc + 32 * hh);
       }
-      int b3 = 0;  // phase % 3
-      for (int ph = 0; ph <= n_steps; ++ph) {
-        const int b3n = b3 == 2 ? 0 : b3 + 1;  // (phase + 1) % 3
-        const int x2 = ph & 1;                 // operand hand-over buffer of step ph
-        if (ph < n_steps) {
-          const int hi = ph / nq;
-          const int h = g * grp + hi;
-          const int qt = 2 * kappa + (ph - hi * nq);
-          const int q0 = QT * qt;
-          const int b = b3;
-          int pp[8], pd[8];
-          int sp[2], sds[2];
-          auto scores = [&](auto masked) {
-            constexpr bool MASK = decltype(masked)::value;
-            // both query blocks' products are issued first, so the matrix cores work on block 1
-            // while the vector unit processes block 0
-            v16f sacc2[2], pacc2[2];
-            // the dP accumulators start at D of their rows: accumulator register 4 j + e holds
-            // row 32 qb + 8 j + 4 hh + e, the float4 at that row
+      // S and D - dP of query block qb of step st (tiles in buffer st % 4).  The dP accumulator
+      // starts at D of its rows: accumulator register 4 j + e holds row 32 qb + 8 j + 4 hh + e,
+      // the float4 at that row.
+      auto products = [&](int st, int qb, v16f& sa, v16f& pa) {
+        const int bb = st & (NBUF - 1);
 #pragma unroll
-            for (int qb = 0; qb < 2; ++qb)
+        for (int j = 0; j < 4; ++j) {
+          const float4 d4 = *reinterpret_cast<const float4*>(&sm.dd[bb][32 * qb + 8 * j + 4 * hh]);
+          pa[4 * j] = d4.x; pa[4 * j + 1] = d4.y; pa[4 * j + 2] = d4.z; pa[4 * j + 3] = d4.w;
+        }
 #pragma unroll
-              for (int j = 0; j < 4; ++j) {
-                const float4 d4 = *reinterpret_cast<const float4*>(&sm.dd[b][32 * qb + 8 * j + 4 * hh]);
-                pacc2[qb][4 * j] = d4.x; pacc2[qb][4 * j + 1] = d4.y;
-                pacc2[qb][4 * j + 2] = d4.z; pacc2[qb][4 * j + 3] = d4.w;
-              }
+        for (int cc = 0; cc < NC; ++cc) {
+          const v8i aq = lds_read_row32<D>(sm.q[bb], 32 * qb + n, 64 * cc + 32 * hh);
+          sa = mfma_scaled(aq, kreg[cc], cc ? sa : v16f{}, sm.sq[bb][qb], k_scale);
+          const v8i ad = lds_read_row32<D>(sm.dO[bb], 32 * qb + n, 64 * cc + 32 * hh);
+          pa = mfma_scaled(ad, vreg[cc], pa, sm.sdo[bb][qb], v_scale);
+        }
+      };
+      // One block's softmax terms fused with another block's products.  Softmax of query block
+      // qs of step ss from (sa, pa): P = 2^(c S - LSE), dS = P (dP - D), the 32 x 32 block
+      // exponents and the E4M3 codes (four words each).  Products of query block qp of step sp
+      // into (ns, np).  The code runs in chunks fenced off from each other: each chunk issues
+      // one matrix instruction, the operand read of the next one and a slice of the softmax
+      // elements, so the matrix unit works while the vector unit does, and only one operand is
+      // in flight at a time.
+      auto fused = [&](int sp_st, int qp, v16f& ns, v16f& np, int ss, int qs, int q0, v16f& sa, v16f& pa,
+                       int* pp4, int* pd4, int& sp, int& sds, auto masked) {
+        constexpr bool MASK = decltype(masked)::value;
+        constexpr int NM = 2 * NC;     // matrix instructions of the products
+        constexpr int EPM = 16 / NM;   // softmax elements per chunk
+        const int bp = sp_st & (NBUF - 1), bs = ss & (NBUF - 1);
+        float4 lse4[4];  // rows acc_row(4 j + e, hh) = 32 qs + 8 j + 4 hh + e
 #pragma unroll
-            for (int cc = 0; cc < NC; ++cc) {
+        for (int j = 0; j < 4; ++j)
+          lse4[j] = *reinterpret_cast<const float4*>(&sm.lse[bs][32 * qs + 8 * j + 4 * hh]);
 #pragma unroll
-              for (int qb = 0; qb < 2; ++qb) {
-                const v8i aq = lds_read_row32<D>(sm.q[b], 32 * qb + n, 64 * cc + 32 * hh);
-                sacc2[qb] = mfma_scaled(aq, kreg[cc], cc ? sacc2[qb] : v16f{}, sm.sq[b][qb], k_scale);
-                const v8i ad = lds_read_row32<D>(sm.dO[b], 32 * qb + n, 64 * cc + 32 * hh);
-                pacc2[qb] = mfma_scaled(ad, vreg[cc], pacc2[qb], sm.sdo[b][qb], v_scale);  // D - dP
-              }
-              __builtin_amdgcn_sched_barrier(0);  // one column chunk of operands live at a time
-            }
+        for (int j = 0; j < 4; ++j) {
+          const float4 d4 = *reinterpret_cast<const float4*>(&sm.dd[bp][32 * qp + 8 * j + 4 * hh]);
+          np[4 * j] = d4.x; np[4 * j + 1] = d4.y; np[4 * j + 2] = d4.z; np[4 * j + 3] = d4.w;
+        }
+        const int sq_s = sm.sq[bp][qp], sdo_s = sm.sdo[bp][qp];
+        v8i opnd = lds_read_row32<D>(sm.q[bp], 32 * qp + n, 32 * hh);
+        __builtin_amdgcn_sched_barrier(0);
+        float pmax = 0.f, dmax = 0.f;
+        // element i sits in row 32 qs + 4 hh + r_i (r_i = 8 (i / 4) + i % 4, a constant): it is
+        // visible when lo <= r_i < hi
+        const int lo = key_rel - (q0 + 32 * qs + 4 * hh), hi = L - (q0 + 32 * qs + 4 * hh);
 #pragma unroll
-            for (int qb = 0; qb < 2; ++qb) {
-              v16f sacc = sacc2[qb], pacc = pacc2[qb];
-              mfma_drain(sacc);
-              mfma_drain(pacc);
-              float pmax = 0.f, dmax = 0.f;
-              float4 lse4[4];  // rows acc_row(4 j + e, hh) = 32 qb + 8 j + 4 hh + e
-#pragma unroll
-              for (int j = 0; j < 4; ++j)
-                lse4[j] = *reinterpret_cast<const float4*>(&sm.lse[b][32 * qb + 8 * j + 4 * hh]);
-#pragma unroll
-              for (int i = 0; i < 16; ++i) {
-                const float lse_i = i % 4 == 0 ? lse4[i / 4].x : i % 4 == 1 ? lse4[i / 4].y : i % 4 == 2 ? lse4[i / 4].z : lse4[i / 4].w;
-                float arg = fmaf(sacc[i], c, -lse_i);
-                if constexpr (MASK) {
-                  const int qr = q0 + 32 * qb + acc_row(i, hh);
-                  arg = (key_rel <= qr && qr < L) ? arg : -__builtin_inff();  // 2^-inf = +0
-                }
-                const float pv = __builtin_amdgcn_exp2f(arg);
-                const float dsv = -(pv * pacc[i]);  // P (dP - D)
-                sacc[i] = pv;
-                pacc[i] = dsv;
-                pmax = fmaxf(pmax, pv);
-                dmax = fmaxf(dmax, fabsf(dsv));
-              }
-              sp[qb] = e8m0_roundup(wave_max_nonneg(pmax));
-              sds[qb] = e8m0_roundup(wave_max_nonneg(dmax));
-#pragma unroll
-              for (int w4 = 0; w4 < 4; ++w4) {
-                pp[4 * qb + w4] = pack4_fp8_scaled(sacc[4 * w4], sacc[4 * w4 + 1], sacc[4 * w4 + 2], sacc[4 * w4 + 3], sp[qb]);
-                pd[4 * qb + w4] = pack4_fp8_scaled(pacc[4 * w4], pacc[4 * w4 + 1], pacc[4 * w4 + 2], pacc[4 * w4 + 3], sds[qb]);
-              }
-            }
-          };
-          // all 64 x 128 pairs visible: the query tile lies wholly below the key tile and inside
-          // the document (then every key of the tile is inside it too)
-          if (qt >= 2 * kappa + 2 && q0 + QT <= L) scores(std::false_type{});
-          else scores(std::true_type{});
-
-          // ---- hand over the operands and exponents; store dShat
-          sm.xp[x2][kw][0][lane] = make_int4(pp[0], pp[1], pp[2], pp[3]);
-          sm.xp[x2][kw][1][lane] = make_int4(pp[4], pp[5], pp[6], pp[7]);
-          sm.xd[x2][kw][0][lane] = make_int4(pd[0], pd[1], pd[2], pd[3]);
-          sm.xd[x2][kw][1][lane] = make_int4(pd[4], pd[5], pd[6], pd[7]);
-          if (lane == 0) {
-#pragma unroll
-            for (int qb = 0; qb < 2; ++qb) {
-              sm.xs_p[x2][qb][kw] = sp[qb] + 127;
-              sm.xs_d[x2][qb][kw] = sds[qb] + 127;
-            }
+        for (int m = 0; m < NM; ++m) {
+          const int cc = m / 2;
+          if (m % 2 == 0) {
+            ns = mfma_scaled(opnd, kreg[cc], cc ? ns : v16f{}, sq_s, k_scale);
+            opnd = lds_read_row32<D>(sm.dO[bp], 32 * qp + n, 64 * cc + 32 * hh);
+          } else {
+            np = mfma_scaled(opnd, vreg[cc], np, sdo_s, v_scale);  // D - dP
+            if (cc + 1 < NC) opnd = lds_read_row32<D>(sm.q[bp], 32 * qp + n, 64 * (cc + 1) + 32 * hh);
           }
-          if (!store_ds) {
 #pragma unroll
-            for (int qb = 0; qb < 2; ++qb)
+          for (int i = m * EPM; i < (m + 1) * EPM; ++i) {
+            const float lse_i = i % 4 == 0 ? lse4[i / 4].x : i % 4 == 1 ? lse4[i / 4].y : i % 4 == 2 ? lse4[i / 4].z : lse4[i / 4].w;
+            float arg = fmaf(sa[i], c, -lse_i);
+            if constexpr (MASK) {
+              const int r = 8 * (i / 4) + i % 4;  // unrolled: an immediate
+              arg = (lo <= r && r < hi) ? arg : -__builtin_inff();  // 2^-inf = +0
+            }
+            const float pv = __builtin_amdgcn_exp2f(arg);
+            const float dsv = -(pv * pa[i]);  // P (dP - D)
+            sa[i] = pv;
+            pa[i] = dsv;
+            pmax = fmaxf(pmax, pv);
+            dmax = fmaxf(dmax, fabsf(dsv));
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        sp = e8m0_roundup(wave_max_nonneg(pmax));
+        sds = e8m0_roundup(wave_max_nonneg(dmax));
 #pragma unroll
-              for (int w4 = 0; w4 < 4; ++w4) {
-                const int qcol = 32 * qb + 8 * w4 + 4 * hh;
-                *reinterpret_cast<int*>(&sm.ds[x2][lds_off<QT>(32 * kw + n, qcol)]) = pd[4 * qb + w4];
-              }
+        for (int w4 = 0; w4 < 4; ++w4) {
+          pp4[w4] = pack4_fp8_scaled(sa[4 * w4], sa[4 * w4 + 1], sa[4 * w4 + 2], sa[4 * w4 + 3], sp);
+          pd4[w4] = pack4_fp8_scaled(pa[4 * w4], pa[4 * w4 + 1], pa[4 * w4 + 2], pa[4 * w4 + 3], sds);
+        }
+      };
+      // Phase ph works on step ph.  Block 0's products were made in the phase before (cs, cp);
+      // block 1's are issued while block 0's softmax terms are formed, and block 0 of the next
+      // step while block 1's are.  The last step has no successor: it recomputes its own
+      // block 0, which is not used.
+      v16f cs, cp, xs, xq;
+      auto phase_body = [&](int ph, int q0, auto masked) {
+        const int x2 = ph & 1;
+        int pp[8], pd[8], sp[2], sds[2];
+        fused(ph, 1, xs, xq, ph, 0, q0, cs, cp, pp, pd, sp[0], sds[0], masked);
+        fused(min(ph + 1, n_steps - 1), 0, cs, cp, ph, 1, q0, xs, xq, pp + 4, pd + 4, sp[1], sds[1], masked);
+        // an empty use of the next step's products: keeps their matrix instructions here, among
+        // the vector work, instead of sunk to the end of the phase next to their next use
+        asm volatile("" ::"v"(cs), "v"(cp));
+        sm.xp[x2][kw][0][lane] = make_int4(pp[0], pp[1], pp[2], pp[3]);
+        sm.xp[x2][kw][1][lane] = make_int4(pp[4], pp[5], pp[6], pp[7]);
+        sm.xd[x2][kw][0][lane] = make_int4(pd[0], pd[1], pd[2], pd[3]);
+        sm.xd[x2][kw][1][lane] = make_int4(pd[4], pd[5], pd[6], pd[7]);
+        if (lane == 0) {
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb) {
+            sm.xs_p[x2][qb][kw] = sp[qb] + 127;
+            sm.xs_d[x2][qb][kw] = sds[qb] + 127;
           }
         }
-        lds_barrier();  // phase done: operands handed over, the next step's tiles stored
-        b3 = b3n;
+        if (store_ds) {
+          // dShat of the step to the workspace, straight from registers: key row 32 kw + n holds
+          // 64 bytes, lane group hh's 32 operand bytes at 32 hh
+          int h;
+          const int qt = step_qt(ph, h);
+          uint8_t* bbase = p.ds_store + (ds_block(ds_base, kappa, n_qt, qt) * p.Hq + h) * DS_STRIDE;
+          int4* dst = reinterpret_cast<int4*>(bbase + (32 * kw + n) * QT + 32 * hh);
+          dst[0] = make_int4(pd[0], pd[1], pd[2], pd[3]);
+          dst[1] = make_int4(pd[4], pd[5], pd[6], pd[7]);
+          if (lane == 0) {
+            bbase[DS_BLOCK + kw] = (uint8_t)(sds[0] + 127);
+            bbase[DS_BLOCK + 4 + kw] = (uint8_t)(sds[1] + 127);
+          }
+        } else {
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+            for (int w4 = 0; w4 < 4; ++w4) {
+              const int qcol = 32 * qb + 8 * w4 + 4 * hh;
+              *reinterpret_cast<int*>(&sm.ds[x2][lds_off<QT>(32 * kw + n, qcol)]) = pd[4 * qb + w4];
+            }
+        }
+      };
+      products(0, 0, cs, cp);
+      for (int ph = 0; ph <= n_steps; ++ph) {
+        if (ph < n_steps) {
+          int h;
+          const int q0 = QT * step_qt(ph, h);
+          // all 64 x 128 pairs visible: the query tile lies wholly below the key tile and
+          // inside the document (then every key of the tile is inside it too)
+          if (q0 >= QT * (2 * kappa + 2) && q0 + QT <= L) phase_body(ph, q0, std::false_type{});
+          else phase_body(ph, q0, std::true_type{});
+        }
+        lds_barrier();  // phase done: operands handed over, the next tiles in place
       }
     } else {
+      // lane-dependent values re-derived from an opaque copy of the lane index: addresses
+      // built from them are local to this role instead of shared with (and kept alive
+      // through) the other role's code
+      int lane_r = lane;
+      asm volatile("" : "+v"(lane_r));
+      const int lane = lane_r, n = lane_r & 31, hh = lane_r >> 5;
+      const int key_rel = KV_TILE * kappa + 32 * kw + n;
       v16f dkacc[NDB], dvacc[NDB];
 #pragma unroll
       for (int db = 0; db < NDB; ++db) { dkacc[db] = v16f{}; dvacc[db] = v16f{}; }
-      int b3 = 0;  // phase % 3
       for (int ph = 0; ph <= n_steps; ++ph) {
-        const int b3p = b3 == 0 ? 2 : b3 - 1;  // (phase - 1) % 3
-        const int b3n = b3 == 2 ? 0 : b3 + 1;  // (phase + 1) % 3
-        // The dShat block of step ph - 1 goes to the workspace first: issued before this phase's
-        // tile loads, the stores retire while the phase runs instead of holding up the wait for
-        // those loads (loads and stores share one in-order counter).
-        if (ph >= 1 && store_ds) {
-          const int st = ph - 1, xb = (ph & 1) ^ 1;
-          const int hi = st / nq;
-          const int qt = 2 * kappa + (st - hi * nq);
-          const int64_t blk = ds_block(ds_base, kappa, n_qt, qt) * p.Hq + g * grp + hi;
-          uint8_t* bbase = p.ds_store + blk * DS_STRIDE;
-          // key row j holds 64 bytes: lane group hh's 32 bytes of the dShat operand at 32 hh
-          int4* dst = reinterpret_cast<int4*>(bbase + (32 * kw + n) * QT + 32 * hh);
-          dst[0] = sm.xd[xb][kw][0][lane];
-          dst[1] = sm.xd[xb][kw][1][lane];
-          if (lane == 0) {
-            bbase[DS_BLOCK + kw] = (uint8_t)sm.xs_d[xb][0][kw];
-            bbase[DS_BLOCK + 4 + kw] = (uint8_t)sm.xs_d[xb][1][kw];
-          }
-        }
         int qtn = 0;
-        if (ph + 1 < n_steps) {  // step ph + 1's tiles, straight into LDS
-          const int hn = (ph + 1) / nq;
-          qtn = 2 * kappa + (ph + 1 - hn * nq);
-          issue_step_loads<D>(p, sm, b3n, doc_start, L, g * grp + hn, qtn, cw, lane);
-          scale_loads(g * grp + hn, qtn, rsq, rsdo);
+        const int bn = (ph + 2) & (NBUF - 1);
+        if (ph + 2 < n_steps) {  // step ph + 2's tiles, straight into LDS
+          int hn;
+          qtn = step_qt(ph + 2, hn);
+          issue_step_loads<D>(p, sm, bn, doc_start, L, hn, qtn, cw, lane);
+          scale_loads(hn, qtn, rsq, rsdo);
         }
         if (ph >= 1) {
           // ---- gradient products of step ph - 1
           const int st = ph - 1;
-          const int b = b3p, xb = (ph & 1) ^ 1;
+          const int b = st & (NBUF - 1), xb = st & 1;
           {
             const int4 p0 = sm.xp[xb][kw][0][lane], p1 = sm.xp[xb][kw][1][lane];
             const int4 d0 = sm.xd[xb][kw][0][lane], d1 = sm.xd[xb][kw][1][lane];
@@ -371,12 +433,22 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
             const v8i bd = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
             const int sdo_h = sm.sdo[b][hh], sq_h = sm.sq[b][hh];
             const int sp_h = sm.xs_p[xb][hh][kw], sds_h = sm.xs_d[xb][hh][kw];
+            // Operand k (dO^T for even k, Q^T for odd k, d-block k / 2) is read AHEAD matrix
+            // instructions early, so each one finds its operand in registers instead of waiting
+            // out an LDS round trip; at most 4 AHEAD reads are outstanding, within the range of
+            // the LDS wait counter.
+            constexpr int NOP = 2 * NDB, AHEAD = 3;
+            auto read_op = [&](int k) { return lds_read_tr32<D>((k & 1) ? sm.q[b] : sm.dO[b], 0, 32 * (k >> 1), lane); };
+            v8i ring[AHEAD];
 #pragma unroll
-            for (int db = 0; db < NDB; ++db) {
-              const v8i ado = lds_read_tr32<D>(sm.dO[b], 0, 32 * db, lane);
-              dvacc[db] = mfma_scaled(ado, bp, dvacc[db], sdo_h, sp_h);
-              const v8i aq = lds_read_tr32<D>(sm.q[b], 0, 32 * db, lane);
-              dkacc[db] = mfma_scaled(aq, bd, dkacc[db], sq_h, sds_h);
+            for (int k = 0; k < AHEAD; ++k) ring[k] = read_op(k);
+#pragma unroll
+            for (int k = 0; k < NOP; ++k) {
+              const v8i a = ring[k % AHEAD];
+              if (k & 1) dkacc[k >> 1] = mfma_scaled(a, bd, dkacc[k >> 1], sq_h, sds_h);
+              else dvacc[k >> 1] = mfma_scaled(a, bp, dvacc[k >> 1], sdo_h, sp_h);
+              if (k + AHEAD < NOP) ring[k % AHEAD] = read_op(k + AHEAD);
+              __builtin_amdgcn_sched_barrier(0);
             }
           }
           if (!store_ds) {
@@ -418,12 +490,11 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
             }
           }
         }
-        if (ph + 1 < n_steps) {
+        if (ph + 2 < n_steps) {
           __builtin_amdgcn_s_waitcnt(0);  // the direct loads have landed
-          scale_store(b3n, qtn, rsq, rsdo);
+          scale_store(bn, qtn, rsq, rsdo);
         }
         lds_barrier();  // phase done: operands consumed, the next step's tiles stored
-        b3 = b3n;
       }
 
       // ---- dK, dV of this consumer's keys
