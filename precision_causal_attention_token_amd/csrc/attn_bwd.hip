@@ -88,6 +88,22 @@ struct BwdSmem {
 // rows is masked to zero, and the repeated values are finite.
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
 
+// The direct loads are issued as inline assembly, out of the compiler's sight: it cannot tell
+// that they write other buffers than the ones being read, and would otherwise wait for them
+// (for the whole global-memory round trip) before every LDS read that follows.  The kernel
+// waits for them itself, at the end of the phase (s_waitcnt), before the barrier that publishes
+// the buffer.  M0 holds the LDS address of the wave's block; one wait state separates its
+// write from the load.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)__builtin_amdgcn_readfirstlane((int)(uintptr_t)(lds_void_ptr)p);
+}
+__device__ __forceinline__ void dma_load16(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(g) : "memory", "m0");
+}
+__device__ __forceinline__ void dma_load4(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off" ::"s"(lds), "v"(g) : "memory", "m0");
+}
+
 template <int D>
 __device__ __forceinline__ void issue_step_loads(const BwdParams& p, BwdSmem<D>& sm, int b, int doc_start, int L,
                                                  int h, int qt, int cw, int lane) {
@@ -106,12 +122,12 @@ __device__ __forceinline__ void issue_step_loads(const BwdParams& p, BwdSmem<D>&
     const int qr = min(q0 + row, L - 1);
     const uint8_t* src = (is_do ? p.dO : p.q) + ((int64_t)(doc_start + qr) * p.Hq + h) * D + 16 * lc;
     uint8_t* dst = (is_do ? sm.dO[b] : sm.q[b]) + blk * 1024;
-    __builtin_amdgcn_global_load_lds(src, (lds_void_ptr)dst, 16, 0, 0);
+    dma_load16(src, lds_addr(dst));
   }
   if (cw < 2) {  // row statistics: one float per lane
     const int qr = min(q0 + lane, L - 1);
     const float* src = (cw == 0 ? p.lse : p.Dv) + (int64_t)h * p.T + doc_start + qr;
-    __builtin_amdgcn_global_load_lds(src, (lds_void_ptr)(cw == 0 ? sm.lse[b] : sm.dd[b]), 4, 0, 0);
+    dma_load4(src, lds_addr(cw == 0 ? sm.lse[b] : sm.dd[b]));
   }
 }
 
