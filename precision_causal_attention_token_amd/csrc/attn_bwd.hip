@@ -201,9 +201,11 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
     };
     auto scale_store = [&](int b, int qt, int rsq, int rsdo) {
       if (cw == 2 && lane < 2) {
-        const bool valid = QT * qt + 32 * lane < L;
-        sm.sq[b][lane] = valid ? rsq : 127;
-        sm.sdo[b][lane] = valid ? rsdo : 127;
+        int l = lane;
+        asm volatile("" : "+v"(l));  // address formed here, not kept in a register all along
+        const bool valid = QT * qt + 32 * l < L;
+        sm.sq[b][l] = valid ? rsq : 127;
+        sm.sdo[b][l] = valid ? rsdo : 127;
       }
     };
     // query head and 64-query tile of step st
@@ -364,7 +366,8 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
       // step while block 1's are.  The last step has no successor: it recomputes its own
       // block 0, which is not used.
       v16f cs, cp, xs, xq;
-      auto phase_body = [&](int ph, int q0, auto masked) {
+      auto phase_body = [&](int ph, int h, int qt, auto masked) {
+        const int q0 = QT * qt;
         const int x2 = ph & 1;
         int pp[8], pd[8], sp[2], sds[2];
         fused(ph, 1, xs, xq, ph, 0, q0, cs, cp, pp, pd, sp[0], sds[0], masked);
@@ -386,8 +389,6 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
         if (store_ds) {
           // dShat of the step to the workspace, straight from registers: key row 32 kw + n holds
           // 64 bytes, lane group hh's 32 operand bytes at 32 hh
-          int h;
-          const int qt = step_qt(ph, h);
           uint8_t* bbase = p.ds_store + (ds_block(ds_base, kappa, n_qt, qt) * p.Hq + h) * DS_STRIDE;
           int4* dst = reinterpret_cast<int4*>(bbase + (32 * kw + n) * QT + 32 * hh);
           dst[0] = make_int4(pd[0], pd[1], pd[2], pd[3]);
@@ -407,14 +408,17 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
         }
       };
       products(0, 0, cs, cp);
+      int cur_h = g * grp, cur_qt = 2 * kappa;  // head and query tile of step ph
       for (int ph = 0; ph <= n_steps; ++ph) {
         if (ph < n_steps) {
-          int h;
-          const int q0 = QT * step_qt(ph, h);
           // all 64 x 128 pairs visible: the query tile lies wholly below the key tile and
           // inside the document (then every key of the tile is inside it too)
-          if (q0 >= QT * (2 * kappa + 2) && q0 + QT <= L) phase_body(ph, q0, std::false_type{});
-          else phase_body(ph, q0, std::true_type{});
+          if (cur_qt >= 2 * kappa + 2 && QT * cur_qt + QT <= L) phase_body(ph, cur_h, cur_qt, std::false_type{});
+          else phase_body(ph, cur_h, cur_qt, std::true_type{});
+          if (++cur_qt == n_qt) {
+            cur_qt = 2 * kappa;
+            ++cur_h;
+          }
         }
         lds_barrier();  // phase done: operands handed over, the next tiles in place
       }
@@ -429,14 +433,18 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
       v16f dkacc[NDB], dvacc[NDB];
 #pragma unroll
       for (int db = 0; db < NDB; ++db) { dkacc[db] = v16f{}; dvacc[db] = v16f{}; }
+      int ld_h = 0, ld_qt = 0;  // head and query tile of step ph + 2 (the next to load)
+      if (n_steps > 2) ld_qt = step_qt(2, ld_h);
       for (int ph = 0; ph <= n_steps; ++ph) {
-        int qtn = 0;
+        const int qtn = ld_qt;
         const int bn = (ph + 2) & (NBUF - 1);
         if (ph + 2 < n_steps) {  // step ph + 2's tiles, straight into LDS
-          int hn;
-          qtn = step_qt(ph + 2, hn);
-          issue_step_loads<D>(p, sm, bn, doc_start, L, hn, qtn, cw, lane);
-          scale_loads(hn, qtn, rsq, rsdo);
+          issue_step_loads<D>(p, sm, bn, doc_start, L, ld_h, qtn, cw, lane);
+          scale_loads(ld_h, qtn, rsq, rsdo);
+          if (++ld_qt == n_qt) {
+            ld_qt = 2 * kappa;
+            ++ld_h;
+          }
         }
         if (ph >= 1) {
           // ---- gradient products of step ph - 1

@@ -125,10 +125,11 @@ __device__ __forceinline__ v8i lds_read_tr32(const uint8_t* tile, int row0, int 
 // s = E - 8 + (f > 0.75).
 __device__ __forceinline__ int e8m0_roundup(float amax) {
   const uint32_t b = __float_as_uint(amax) & 0x7FFFFFFFu;
-  const int E = (int)(b >> 23);
-  if (E == 255) return 128;
-  if (E == 0) return -127;
-  const int s = (E - 127) - 8 + ((b & 0x7FFFFFu) > 0x600000u ? 1 : 0);
+  if (b >= 0x7F800000u) return 128;  // infinity or NaN
+  // 448 = 1.75 * 2^8: adding 2^21 - 1 carries into the exponent field exactly when the mantissa
+  // exceeds 0.75, which is when amax / 2^(E - 127 - 8) exceeds 448; zero and subnormal amax
+  // land below -127 and clamp there
+  const int s = (int)((b + 0x1FFFFFu) >> 23) - 135;
   return s < -127 ? -127 : s;
 }
 // 2^-s as a float, for s in [-127, 127].
