@@ -320,7 +320,13 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
           np[4 * j] = d4.x; np[4 * j + 1] = d4.y; np[4 * j + 2] = d4.z; np[4 * j + 3] = d4.w;
         }
         const int sq_s = sm.sq[bp][qp], sdo_s = sm.sdo[bp][qp];
-        v8i opnd = lds_read_row32<D>(sm.q[bp], 32 * qp + n, 32 * hh);
+        // operand m: Q rows (m even) or dO rows (m odd) of column chunk m / 2; two in flight
+        auto read_op = [&](int m) {
+          return lds_read_row32<D>((m & 1) ? sm.dO[bp] : sm.q[bp], 32 * qp + n, 64 * (m >> 1) + 32 * hh);
+        };
+        v8i opnd[2];
+        opnd[0] = read_op(0);
+        opnd[1] = read_op(1);
         __builtin_amdgcn_sched_barrier(0);
         float pmax = 0.f, dmax = 0.f;
         // element i sits in row 32 qs + 4 hh + r_i (r_i = 8 (i / 4) + i % 4, a constant): it is
@@ -329,13 +335,9 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
 #pragma unroll
         for (int m = 0; m < NM; ++m) {
           const int cc = m / 2;
-          if (m % 2 == 0) {
-            ns = mfma_scaled(opnd, kreg[cc], cc ? ns : v16f{}, sq_s, k_scale);
-            opnd = lds_read_row32<D>(sm.dO[bp], 32 * qp + n, 64 * cc + 32 * hh);
-          } else {
-            np = mfma_scaled(opnd, vreg[cc], np, sdo_s, v_scale);  // D - dP
-            if (cc + 1 < NC) opnd = lds_read_row32<D>(sm.q[bp], 32 * qp + n, 64 * (cc + 1) + 32 * hh);
-          }
+          if (m % 2 == 0) ns = mfma_scaled(opnd[0], kreg[cc], cc ? ns : v16f{}, sq_s, k_scale);
+          else np = mfma_scaled(opnd[1], vreg[cc], np, sdo_s, v_scale);  // D - dP
+          if (m + 2 < NM) opnd[m & 1] = read_op(m + 2);
 #pragma unroll
           for (int i = m * EPM; i < (m + 1) * EPM; ++i) {
             const float lse_i = i % 4 == 0 ? lse4[i / 4].x : i % 4 == 1 ? lse4[i / 4].y : i % 4 == 2 ? lse4[i / 4].z : lse4[i / 4].w;
@@ -398,12 +400,15 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
             bbase[DS_BLOCK + 4 + kw] = (uint8_t)(sds[1] + 127);
           }
         } else {
+          int l = lane;
+          asm volatile("" : "+v"(l));  // addresses formed here, not kept in registers all along
+          const int nl = l & 31, hl = l >> 5;
 #pragma unroll
           for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
             for (int w4 = 0; w4 < 4; ++w4) {
-              const int qcol = 32 * qb + 8 * w4 + 4 * hh;
-              *reinterpret_cast<int*>(&sm.ds[x2][lds_off<QT>(32 * kw + n, qcol)]) = pd[4 * qb + w4];
+              const int qcol = 32 * qb + 8 * w4 + 4 * hl;
+              *reinterpret_cast<int*>(&sm.ds[x2][lds_off<QT>(32 * kw + nl, qcol)]) = pd[4 * qb + w4];
             }
         }
       };
