@@ -563,15 +563,21 @@ struct DqSmem {
 
 // The next key tile's K rows, dShat blocks and exponents, in registers between the global loads
 // and the LDS stores.
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));  // plain vector: stays in registers
 template <int D>
 struct DqRegs {
   static constexpr int KCH = KV_TILE * D / 16 / DQ_THREADS;  // K chunks per thread
   static constexpr int SCH = 4 * DS_BLOCK / 16 / DQ_THREADS;  // dShat chunks per thread
-  uint4 k[KCH], s[SCH];
+  v4u k[KCH], s[SCH];
   uint2 sc;       // threads 0..3: exponents of query tile `tid`
   uint32_t skb;   // threads 0..127: K scale byte of key `tid`
+  int nkeys;      // keys of the tile inside the document (scale 127 beyond)
 };
 
+// Every thread issues the same loads whatever the tile (rows past the document end repeat its
+// last row, tiles outside the item's range re-read a block that exists and are not used), so
+// the number of loads in flight is the same on every path and the wait before the LDS store
+// can leave the following tile's loads outstanding.
 template <int D>
 __device__ __forceinline__ void dq_load(DqRegs<D>& r, const BwdParams& p, int doc_start, int L, int n_qt,
                                         int64_t base, int qt0, int g, int h, int kappa) {
@@ -582,30 +588,19 @@ __device__ __forceinline__ void dq_load(DqRegs<D>& r, const BwdParams& p, int do
   for (int i = 0; i < DqRegs<D>::KCH; ++i) {
     const int chunk = tid + i * DQ_THREADS;
     const int row = chunk / CPR, col = (chunk % CPR) * 16;
-    const int key = KV_TILE * kappa + row;
-    r.k[i] = make_uint4(0, 0, 0, 0);
-    if (key < L) r.k[i] = *reinterpret_cast<const uint4*>(p.k + ((int64_t)(doc_start + key) * p.Hkv + g) * D + col);
+    const int key = min(KV_TILE * kappa + row, L - 1);
+    r.k[i] = *reinterpret_cast<const v4u*>(p.k + ((int64_t)(doc_start + key) * p.Hkv + g) * D + col);
   }
-  // block of query tile qt0 + t; the four tiles' blocks of one key tile are consecutive
-  const int64_t blk0 = ds_block(base, kappa, n_qt, qt0);
+  // block of query tile qt0 + t (clamped into the key tile's range [2 kappa, n_qt - 1])
+  auto block = [&](int t) {
+    const int qt = min(max(qt0 + t, 2 * kappa), n_qt - 1);
+    return p.ds_store + ((int64_t)ds_block(base, kappa, n_qt, qt) * p.Hq + h) * DS_STRIDE;
+  };
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const int qt = qt0 + t;
-    r.s[t] = make_uint4(0, 0, 0, 0);
-    if (qt < n_qt && qt >= 2 * kappa)
-      r.s[t] = reinterpret_cast<const uint4*>(p.ds_store + ((blk0 + t) * p.Hq + h) * DS_STRIDE)[tid];
-  }
-  r.sc = make_uint2(0x7F7F7F7Fu, 0x7F7F7F7Fu);
-  if (tid < 4) {
-    const int qt = qt0 + tid;
-    if (qt < n_qt && qt >= 2 * kappa)
-      r.sc = *reinterpret_cast<const uint2*>(p.ds_store + ((blk0 + tid) * p.Hq + h) * DS_STRIDE + DS_BLOCK);
-  }
-  r.skb = 127;
-  if (tid < KV_TILE) {
-    const int key = KV_TILE * kappa + tid;
-    if (key < L) r.skb = p.sk[(int64_t)g * p.T + doc_start + key];
-  }
+  for (int t = 0; t < 4; ++t) r.s[t] = reinterpret_cast<const v4u*>(block(t))[tid];
+  r.sc = *reinterpret_cast<const uint2*>(block(tid & 3) + DS_BLOCK);  // used by threads 0..3
+  r.skb = p.sk[(int64_t)g * p.T + doc_start + min(KV_TILE * kappa + (tid & (KV_TILE - 1)), L - 1)];
+  r.nkeys = L - KV_TILE * kappa;  // the value is tested at the store, not here: no wait for it
 }
 
 template <int D>
@@ -616,13 +611,13 @@ __device__ __forceinline__ void dq_store(const DqRegs<D>& r, DqSmem<D>& sm, int 
   for (int i = 0; i < DqRegs<D>::KCH; ++i) {
     const int chunk = tid + i * DQ_THREADS;
     const int row = chunk / CPR, col = (chunk % CPR) * 16;
-    *reinterpret_cast<uint4*>(&sm.k[b][lds_off<D>(row, col)]) = r.k[i];
+    *reinterpret_cast<v4u*>(&sm.k[b][lds_off<D>(row, col)]) = r.k[i];
   }
   const int off = lds_off<QT>(tid / (QT / 16), (tid % (QT / 16)) * 16);
 #pragma unroll
-  for (int t = 0; t < 4; ++t) *reinterpret_cast<uint4*>(&sm.ds[b][t][off]) = r.s[t];
+  for (int t = 0; t < 4; ++t) *reinterpret_cast<v4u*>(&sm.ds[b][t][off]) = r.s[t];
   if (tid < 4) *reinterpret_cast<uint2*>(&sm.dsc[b][tid][0]) = r.sc;
-  if (tid < KV_TILE) sm.sk[b][tid] = (uint8_t)r.skb;
+  if (tid < KV_TILE) sm.sk[b][tid] = tid < r.nkeys ? (uint8_t)r.skb : (uint8_t)127;
 }
 
 template <int D>
@@ -672,14 +667,11 @@ __global__ __launch_bounds__(DQ_THREADS) void dq_kernel(BwdParams p) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) acc16[db][j] = h2{0, 0};
 
-    DqRegs<D> pre;
-    lds_barrier();  // the previous unit no longer reads LDS
-    dq_load<D>(pre, p, doc_start, L, n_qt, base, qt0, g, h, 0);
-    dq_store<D>(pre, sm, 0);
-    lds_barrier();
-    for (int kappa = 0; kappa <= kappa_hi; ++kappa) {
+    // Key tile kappa's operands go global -> registers two tiles ahead and registers -> LDS one
+    // tile ahead (two register sets, two LDS buffers), so each load has a whole tile's compute
+    // to arrive.
+    auto compute = [&](int kappa) __attribute__((always_inline)) {
       const int b = kappa & 1;
-      if (kappa < kappa_hi) dq_load<D>(pre, p, doc_start, L, n_qt, base, qt0, g, h, kappa + 1);
       if (active && qt >= 2 * kappa) {
         v8i bs[2];
         int sb[2];
@@ -688,24 +680,57 @@ __global__ __launch_bounds__(DQ_THREADS) void dq_kernel(BwdParams p) {
           bs[ci] = lds_read_tr32<QT>(sm.ds[b][t4], 64 * ci, 32 * s, lane);
           sb[ci] = sm.dsc[b][t4][4 * qb_l + 2 * ci + hh];
         }
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          v16f part = v16f{};
-#pragma unroll
-          for (int ci = 0; ci < 2; ++ci) {
-            const v8i ak = lds_read_tr32<D>(sm.k[b], 64 * ci, 32 * db, lane);
-            part = mfma_scaled(ak, bs[ci], part, sm.sk[b][64 * ci + 32 * hh], sb[ci]);
-          }
+        // K^T operand k (d-block k / 2, key half k % 2) read three products ahead; the partial
+        // of d-block db is added to the FP16 sums while the products of d-block db + 1 run
+        constexpr int NOP = 2 * NDB, AHEAD = 3;
+        auto read_k = [&](int k) { return lds_read_tr32<D>(sm.k[b], 64 * (k & 1), 32 * (k >> 1), lane); };
+        auto add_partial = [&](v16f& part, int db) {
           mfma_drain(part);
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
             const h2 x = h2{(_Float16)(part[2 * j] * up), (_Float16)(part[2 * j + 1] * up)};
             acc16[db][j] = acc16[db][j] + x;
           }
+        };
+        v8i ring[AHEAD];
+#pragma unroll
+        for (int k = 0; k < AHEAD; ++k) ring[k] = read_k(k);
+        v16f part[2];
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+          for (int ci = 0; ci < 2; ++ci) {
+            const int k = 2 * db + ci;
+            part[db & 1] = mfma_scaled(ring[k % AHEAD], bs[ci], ci ? part[db & 1] : v16f{},
+                                       sm.sk[b][64 * ci + 32 * hh], sb[ci]);
+            if (k + AHEAD < NOP) ring[k % AHEAD] = read_k(k + AHEAD);
+          }
+          if (db >= 1) add_partial(part[(db - 1) & 1], db - 1);
+          __builtin_amdgcn_sched_barrier(0);
         }
+        add_partial(part[(NDB - 1) & 1], NDB - 1);
       }
-      if (kappa < kappa_hi) dq_store<D>(pre, sm, b ^ 1);
+    };
+    // one tile: loads of kappa + 2 into `spare`, compute kappa, `next` (kappa + 1) into LDS.  The
+    // loads are issued on every tile (the last two re-read tile kappa_hi, unused) so that the
+    // count of loads in flight does not depend on the path.
+    auto tile = [&](int kappa, DqRegs<D>& next, DqRegs<D>& spare) __attribute__((always_inline)) {
+      dq_load<D>(spare, p, doc_start, L, n_qt, base, qt0, g, h, min(kappa + 2, kappa_hi));
+      compute(kappa);
+      if (kappa + 1 <= kappa_hi) dq_store<D>(next, sm, (kappa + 1) & 1);
       lds_barrier();
+    };
+    DqRegs<D> ra, rb;
+    lds_barrier();  // the previous unit no longer reads LDS
+    dq_load<D>(ra, p, doc_start, L, n_qt, base, qt0, g, h, 0);
+    dq_load<D>(rb, p, doc_start, L, n_qt, base, qt0, g, h, min(1, kappa_hi));
+    dq_store<D>(ra, sm, 0);
+    lds_barrier();
+    for (int kappa = 0;; kappa += 2) {  // two tiles per trip: the register sets trade roles
+      tile(kappa, rb, ra);
+      if (kappa + 1 > kappa_hi) break;
+      tile(kappa + 1, ra, rb);
+      if (kappa + 2 > kappa_hi) break;
     }
 
     if (active && row_valid) {
