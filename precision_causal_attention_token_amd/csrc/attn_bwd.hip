@@ -86,24 +86,6 @@ struct BwdSmem {
 // waves two phases ahead.  Each lane fetches the global chunk that belongs at its LDS position
 // under the tile's swizzle.  Rows past the document end repeat its last row: every use of those
 // rows is masked to zero, and the repeated values are finite.
-typedef __attribute__((address_space(3))) void* lds_void_ptr;
-
-// The direct loads are issued as inline assembly, out of the compiler's sight: it cannot tell
-// that they write other buffers than the ones being read, and would otherwise wait for them
-// (for the whole global-memory round trip) before every LDS read that follows.  The kernel
-// waits for them itself, at the end of the phase (s_waitcnt), before the barrier that publishes
-// the buffer.  M0 holds the LDS address of the wave's block; one wait state separates its
-// write from the load.
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)__builtin_amdgcn_readfirstlane((int)(uintptr_t)(lds_void_ptr)p);
-}
-__device__ __forceinline__ void dma_load16(const void* g, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(g) : "memory", "m0");
-}
-__device__ __forceinline__ void dma_load4(const void* g, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off" ::"s"(lds), "v"(g) : "memory", "m0");
-}
-
 template <int D>
 __device__ __forceinline__ void issue_step_loads(const BwdParams& p, BwdSmem<D>& sm, int b, int doc_start, int L,
                                                  int h, int qt, int cw, int lane) {

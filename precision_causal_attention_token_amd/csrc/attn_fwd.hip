@@ -27,60 +27,51 @@ constexpr int FWD_THREADS = 64 * FWD_WAVES;
 template <int D>
 struct FwdSmem {
   uint8_t k[2][KV_TILE * D];
-  uint8_t v[2][KV_TILE * D];
+  uint8_t v[3][KV_TILE * D];
   uint8_t sk[2][KV_TILE];
-  uint8_t sv[2][KV_TILE];
+  uint8_t sv[3][KV_TILE];
 };
 
-// Prefetch of one K/V tile into registers: each thread moves 16-byte chunks.
+// Tile i of a unit (key tile kappa_hi - i) sits in K buffer i % 2 and V buffer i % 3: while tile
+// i is current, the staggered waves still read tile i - 1's V and tile i + 1 is being loaded.
+// K and V rows go global -> LDS with direct loads, each lane fetching the 16-byte chunk that
+// belongs at its LDS position under the tile's swizzle; rows past the document end repeat its
+// last row (their scores are masked, their probabilities are zero, and the values are finite).
+// The scale bytes go through a register, returned here and stored by store_scales: thread
+// t < 128 holds the K scale of key t, 128 <= t < 256 the V scale of key t - 128.
 template <int D>
-struct TileRegs {
-  static constexpr int CHUNKS = KV_TILE * D / 16 / FWD_THREADS;  // per tensor per thread
-  uint4 k[CHUNKS], v[CHUNKS];
-  uint32_t sc;  // thread t < 128: sk byte of key t; 128 <= t < 256: sv byte of key t-128
-};
-
-template <int D>
-__device__ __forceinline__ void load_tile(TileRegs<D>& r, const FwdParams& p, int g, int doc_start, int L, int kappa) {
-  const int tid = threadIdx.x;
-  constexpr int CPR = D / 16;  // chunks per row
+__device__ __forceinline__ uint32_t issue_tile(const FwdParams& p, FwdSmem<D>& sm, int kb, int vb, int g,
+                                               int doc_start, int L, int kappa, int wave, int lane) {
+  constexpr int CPR = D / 16;                        // 16-byte chunks per row
+  constexpr int BLOCKS = KV_TILE * D / 1024;         // 1 KiB wave blocks per tensor
+  constexpr int PER_WAVE = 2 * BLOCKS / FWD_WAVES;   // K and V blocks per wave
+  static_assert(PER_WAVE * FWD_WAVES == 2 * BLOCKS, "blocks split evenly over the waves");
 #pragma unroll
-  for (int i = 0; i < TileRegs<D>::CHUNKS; ++i) {
-    const int chunk = tid + i * FWD_THREADS;
-    const int row = chunk / CPR, col = (chunk % CPR) * 16;
-    const int key = 128 * kappa + row;
-    if (key < L) {
-      const int64_t off = ((int64_t)(doc_start + key) * p.Hkv + g) * D + col;
-      r.k[i] = *reinterpret_cast<const uint4*>(p.k + off);
-      r.v[i] = *reinterpret_cast<const uint4*>(p.v + off);
-    } else {
-      r.k[i] = make_uint4(0, 0, 0, 0);
-      r.v[i] = make_uint4(0, 0, 0, 0);
-    }
+  for (int i = 0; i < PER_WAVE; ++i) {
+    const int wb = wave * PER_WAVE + i;              // K blocks, then V blocks
+    const bool is_v = wb >= BLOCKS;
+    const int blk = is_v ? wb - BLOCKS : wb;
+    const int pos = blk * 64 + lane;                 // chunk position in the tile
+    const int row = pos / CPR, pc = pos % CPR;
+    const int lc = pc ^ lds_swizzle<D>(row);         // logical chunk stored there
+    const int key = min(KV_TILE * kappa + row, L - 1);
+    const uint8_t* src = (is_v ? p.v : p.k) + ((int64_t)(doc_start + key) * p.Hkv + g) * D + 16 * lc;
+    dma_load16(src, lds_addr((is_v ? sm.v[vb] : sm.k[kb]) + blk * 1024));
   }
-  r.sc = 127;
+  const int tid = threadIdx.x;
+  uint32_t sc = 127;
   if (tid < 2 * KV_TILE) {
-    const int key = 128 * kappa + (tid & 127);
-    if (key < L) {
-      const uint8_t* tab = tid < KV_TILE ? p.sk : p.sv;
-      r.sc = tab[(int64_t)g * p.T + doc_start + key];
-    }
+    const int key = KV_TILE * kappa + (tid & (KV_TILE - 1));
+    if (key < L) sc = (tid < KV_TILE ? p.sk : p.sv)[(int64_t)g * p.T + doc_start + key];
   }
+  return sc;
 }
 
 template <int D>
-__device__ __forceinline__ void store_tile(const TileRegs<D>& r, FwdSmem<D>& sm, int buf) {
+__device__ __forceinline__ void store_scales(FwdSmem<D>& sm, int kb, int vb, uint32_t sc) {
   const int tid = threadIdx.x;
-  constexpr int CPR = D / 16;
-#pragma unroll
-  for (int i = 0; i < TileRegs<D>::CHUNKS; ++i) {
-    const int chunk = tid + i * FWD_THREADS;
-    const int row = chunk / CPR, col = (chunk % CPR) * 16;
-    *reinterpret_cast<uint4*>(&sm.k[buf][lds_off<D>(row, col)]) = r.k[i];
-    *reinterpret_cast<uint4*>(&sm.v[buf][lds_off<D>(row, col)]) = r.v[i];
-  }
-  if (tid < KV_TILE) sm.sk[buf][tid] = (uint8_t)r.sc;
-  else if (tid < 2 * KV_TILE) sm.sv[buf][tid - KV_TILE] = (uint8_t)r.sc;
+  if (tid < KV_TILE) sm.sk[kb][tid] = (uint8_t)sc;
+  else if (tid < 2 * KV_TILE) sm.sv[vb][tid - KV_TILE] = (uint8_t)sc;
 }
 
 template <int D>
@@ -141,45 +132,76 @@ __global__ __launch_bounds__(FWD_THREADS) void fwd_kernel(FwdParams p) {
     float m = -__builtin_inff();  // running max, score units
     float l = 0.f;                // this lane's share of the row sum of 2^8 p
 
-    TileRegs<D> pre;
-    load_tile<D>(pre, p, g, doc_start, L, kappa_hi);
-    lds_barrier();  // previous unit's readers are done with both buffers
-    store_tile<D>(pre, sm, 0);
+    // O^T += V^T P^T for the P codes pk of the tile whose V sits in buffer vb
+    int pk[4][4];
+    auto pv_product = [&](int vb) {
+      const uint8_t* vt = sm.v[vb];
+#pragma unroll
+      for (int ci = 0; ci < 2; ++ci) {
+        v8i pop;
+#pragma unroll
+        for (int w = 0; w < 8; ++w) pop[w] = pk[2 * ci + (w >> 2)][w & 3];
+        const int vs = sm.sv[vb][64 * ci + 32 * hh];
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const v8i a = lds_read_tr32<D>(vt, 64 * ci, 32 * db, lane);
+          oacc[db] = mfma_scaled(a, pop, oacc[db], vs, 127 - P_SHIFT);
+        }
+      }
+    };
+    // The four upper waves run each tile's PV product at the start of the next tile: on every
+    // SIMD one wave of each kind, so one wave's score products and softmax terms meet the other
+    // wave's PV products and the vector and matrix units both have work.
+    const bool late = wave >= FWD_WAVES / 2;
+    bool pending = false;
+
+    lds_barrier();  // the previous unit's readers are done with every buffer
+    {
+      const uint32_t sc = issue_tile<D>(p, sm, 0, 0, g, doc_start, L, kappa_hi, wave, lane);
+      __builtin_amdgcn_s_waitcnt(0);  // this wave's direct loads have landed
+      store_scales<D>(sm, 0, 0, sc);
+    }
     lds_barrier();
-    int buf = 0;
-    for (int kappa = kappa_hi; kappa >= 0; --kappa) {
-      if (kappa > 0) load_tile<D>(pre, p, g, doc_start, L, kappa - 1);
+    int vb = 0;  // V buffer of the current tile (tile index mod 3)
+    for (int kappa = kappa_hi, it = 0; kappa >= 0; --kappa, ++it) {
+      const int kb = it & 1;
+      const int vbn = vb == 2 ? 0 : vb + 1, vbp = vb == 0 ? 2 : vb - 1;
+      uint32_t scn = 127;
+      if (kappa > 0) scn = issue_tile<D>(p, sm, kb ^ 1, vbn, g, doc_start, L, kappa - 1, wave, lane);
+      if (pending) {  // late waves: the previous tile's PV product
+        pv_product(vbp);
+        pending = false;
+      }
       if (wave_active && kappa <= kd) {
-        const uint8_t* kt = sm.k[buf];
-        const uint8_t* vt = sm.v[buf];
+        const uint8_t* kt = sm.k[kb];
         // ---- S^T for the 4 key blocks of the tile
         v16f s[4];
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-          s[kb] = v16f{};
-          const int ks = sm.sk[buf][32 * kb + n];
+        for (int kb4 = 0; kb4 < 4; ++kb4) {
+          s[kb4] = v16f{};
+          const int ks = sm.sk[kb][32 * kb4 + n];
 #pragma unroll
           for (int cc = 0; cc < NC; ++cc) {
-            const v8i a = lds_read_row32<D>(kt, 32 * kb + n, 64 * cc + 32 * hh);
-            s[kb] = mfma_scaled(a, qop[cc], s[kb], ks, q_scale);
+            const v8i a = lds_read_row32<D>(kt, 32 * kb4 + n, 64 * cc + 32 * hh);
+            s[kb4] = mfma_scaled(a, qop[cc], s[kb4], ks, q_scale);
           }
         }
         // ---- causal mask on the diagonal tile (keys after the query)
         if (kappa == kd) {
 #pragma unroll
-          for (int kb = 0; kb < 4; ++kb)
+          for (int kb4 = 0; kb4 < 4; ++kb4)
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-              const int key = KV_TILE * kappa + 32 * kb + acc_row(i, hh);
-              if (key > q_rel) s[kb][i] = -__builtin_inff();
+              const int key = KV_TILE * kappa + 32 * kb4 + acc_row(i, hh);
+              if (key > q_rel) s[kb4][i] = -__builtin_inff();
             }
         }
         // ---- running max (raw accumulator units, then scaled once)
         float mx = -__builtin_inff();
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
+        for (int kb4 = 0; kb4 < 4; ++kb4)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
+          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb4][i]);
         mx = halves_max(mx);
         const float m_new = fmaxf(m, mx * c);
         const float alpha = __builtin_amdgcn_exp2f(m - m_new);
@@ -193,38 +215,28 @@ __global__ __launch_bounds__(FWD_THREADS) void fwd_kernel(FwdParams p) {
         m = m_new;
         // ---- p = 2^(t - m), scaled by 2^8 for the E4M3 operand; packed into operand order
         const float bias = (float)P_SHIFT - m_new;
-        int pk[4][4];
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
+        for (int kb4 = 0; kb4 < 4; ++kb4)
 #pragma unroll
           for (int w4 = 0; w4 < 4; ++w4) {
-            const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][4 * w4 + 0], c, bias));
-            const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][4 * w4 + 1], c, bias));
-            const float p2 = __builtin_amdgcn_exp2f(fmaf(s[kb][4 * w4 + 2], c, bias));
-            const float p3 = __builtin_amdgcn_exp2f(fmaf(s[kb][4 * w4 + 3], c, bias));
+            const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb4][4 * w4 + 0], c, bias));
+            const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb4][4 * w4 + 1], c, bias));
+            const float p2 = __builtin_amdgcn_exp2f(fmaf(s[kb4][4 * w4 + 2], c, bias));
+            const float p3 = __builtin_amdgcn_exp2f(fmaf(s[kb4][4 * w4 + 3], c, bias));
             l += (p0 + p1) + (p2 + p3);
-            pk[kb][w4] = pack4_fp8(p0, p1, p2, p3);
+            pk[kb4][w4] = pack4_fp8(p0, p1, p2, p3);
           }
-        // ---- O^T += V^T P^T, two 64-key chunks
-#pragma unroll
-        for (int ci = 0; ci < 2; ++ci) {
-          v8i pop;
-#pragma unroll
-          for (int w = 0; w < 8; ++w) pop[w] = pk[2 * ci + (w >> 2)][w & 3];
-          const int vs = sm.sv[buf][64 * ci + 32 * hh];
-#pragma unroll
-          for (int db = 0; db < NDB; ++db) {
-            const v8i a = lds_read_tr32<D>(vt, 64 * ci, 32 * db, lane);
-            oacc[db] = mfma_scaled(a, pop, oacc[db], vs, 127 - P_SHIFT);
-          }
-        }
+        if (late) pending = true;
+        else pv_product(vb);
       }
       if (kappa > 0) {
-        store_tile<D>(pre, sm, buf ^ 1);
+        __builtin_amdgcn_s_waitcnt(0);  // this wave's direct loads have landed
+        store_scales<D>(sm, kb ^ 1, vbn, scn);
         lds_barrier();
-        buf ^= 1;
       }
+      vb = vbn;
     }
+    if (pending) pv_product(vb == 0 ? 2 : vb - 1);  // the last tile's V buffer
 
     // ---- epilogue: O = acc / l, LSE = m + log2 l (l in units of 2^-8)
     if (wave_active) {

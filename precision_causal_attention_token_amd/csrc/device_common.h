@@ -118,6 +118,25 @@ __device__ __forceinline__ v8i lds_read_tr32(const uint8_t* tile, int row0, int 
 }
 
 // ---------------------------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+
+// Direct global -> LDS loads (lane l writes bytes 16 l .. 16 l + 15, or 4 l .. 4 l + 3, of the
+// block at the LDS address), issued as inline assembly, out of the compiler's sight: it cannot tell
+// that they write other buffers than the ones being read, and would otherwise wait for them
+// (for the whole global-memory round trip) before every LDS read that follows.  The kernels
+// wait for them explicitly (s_waitcnt) before the barrier that publishes the buffer.  M0 holds
+// the LDS address of the wave's block; one wait state separates its write from the load.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)__builtin_amdgcn_readfirstlane((int)(uintptr_t)(lds_void_ptr)p);
+}
+__device__ __forceinline__ void dma_load16(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(g) : "memory", "m0");
+}
+__device__ __forceinline__ void dma_load4(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off" ::"s"(lds), "v"(g) : "memory", "m0");
+}
+
+// ---------------------------------------------------------------------------------------------
 // E8M0 / E4M3 helpers.
 
 // Smallest s with amax <= 448 * 2^s, clamped to >= -127 (amax = 0 or subnormal gives -127);
