@@ -354,44 +354,45 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
         const int q0 = QT * qt;
         const int x2 = ph & 1;
         int pp[8], pd[8], sp[2], sds[2];
+        uint8_t* bbase = p.ds_store + (ds_block(ds_base, kappa, n_qt, qt) * p.Hq + h) * DS_STRIDE;
+        // hand over query block qb's operands (and store its dShat half) as soon as they exist,
+        // so the writes retire under the next block's work instead of before the barrier
+        auto hand_over = [&](int qb) {
+          sm.xp[x2][kw][qb][lane] = make_int4(pp[4 * qb], pp[4 * qb + 1], pp[4 * qb + 2], pp[4 * qb + 3]);
+          sm.xd[x2][kw][qb][lane] = make_int4(pd[4 * qb], pd[4 * qb + 1], pd[4 * qb + 2], pd[4 * qb + 3]);
+          if (store_ds) {
+            // dShat to the workspace, straight from registers: key row 32 kw + n holds 64 bytes,
+            // lane group hh's 32 operand bytes at 32 hh, query block qb's 16 of them at 16 qb
+            *reinterpret_cast<int4*>(bbase + (32 * kw + n) * QT + 32 * hh + 16 * qb) =
+                make_int4(pd[4 * qb], pd[4 * qb + 1], pd[4 * qb + 2], pd[4 * qb + 3]);
+          } else {
+            int l = lane;
+            asm volatile("" : "+v"(l));  // addresses formed here, not kept in registers all along
+            const int nl = l & 31, hl = l >> 5;
+#pragma unroll
+            for (int w4 = 0; w4 < 4; ++w4) {
+              const int qcol = 32 * qb + 8 * w4 + 4 * hl;
+              *reinterpret_cast<int*>(&sm.ds[x2][lds_off<QT>(32 * kw + nl, qcol)]) = pd[4 * qb + w4];
+            }
+          }
+        };
         fused(ph, 1, xs, xq, ph, 0, q0, cs, cp, pp, pd, sp[0], sds[0], masked);
+        hand_over(0);
         fused(min(ph + 1, n_steps - 1), 0, cs, cp, ph, 1, q0, xs, xq, pp + 4, pd + 4, sp[1], sds[1], masked);
         // an empty use of the next step's products: keeps their matrix instructions here, among
         // the vector work, instead of sunk to the end of the phase next to their next use
         asm volatile("" ::"v"(cs), "v"(cp));
-        sm.xp[x2][kw][0][lane] = make_int4(pp[0], pp[1], pp[2], pp[3]);
-        sm.xp[x2][kw][1][lane] = make_int4(pp[4], pp[5], pp[6], pp[7]);
-        sm.xd[x2][kw][0][lane] = make_int4(pd[0], pd[1], pd[2], pd[3]);
-        sm.xd[x2][kw][1][lane] = make_int4(pd[4], pd[5], pd[6], pd[7]);
+        hand_over(1);
         if (lane == 0) {
 #pragma unroll
           for (int qb = 0; qb < 2; ++qb) {
             sm.xs_p[x2][qb][kw] = sp[qb] + 127;
             sm.xs_d[x2][qb][kw] = sds[qb] + 127;
           }
-        }
-        if (store_ds) {
-          // dShat of the step to the workspace, straight from registers: key row 32 kw + n holds
-          // 64 bytes, lane group hh's 32 operand bytes at 32 hh
-          uint8_t* bbase = p.ds_store + (ds_block(ds_base, kappa, n_qt, qt) * p.Hq + h) * DS_STRIDE;
-          int4* dst = reinterpret_cast<int4*>(bbase + (32 * kw + n) * QT + 32 * hh);
-          dst[0] = make_int4(pd[0], pd[1], pd[2], pd[3]);
-          dst[1] = make_int4(pd[4], pd[5], pd[6], pd[7]);
-          if (lane == 0) {
+          if (store_ds) {
             bbase[DS_BLOCK + kw] = (uint8_t)(sds[0] + 127);
             bbase[DS_BLOCK + 4 + kw] = (uint8_t)(sds[1] + 127);
           }
-        } else {
-          int l = lane;
-          asm volatile("" : "+v"(l));  // addresses formed here, not kept in registers all along
-          const int nl = l & 31, hl = l >> 5;
-#pragma unroll
-          for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-            for (int w4 = 0; w4 < 4; ++w4) {
-              const int qcol = 32 * qb + 8 * w4 + 4 * hl;
-              *reinterpret_cast<int*>(&sm.ds[x2][lds_off<QT>(32 * kw + nl, qcol)]) = pd[4 * qb + w4];
-            }
         }
       };
       products(0, 0, cs, cp);

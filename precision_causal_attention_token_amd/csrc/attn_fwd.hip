@@ -13,7 +13,10 @@
 //   P operand                      : E4M3(2^8 p) from the score registers, which already are in
 //                                    the MFMA operand order (no data movement between lanes);
 //   O^T += V^T P^T                 : A = V^T read from the row-major V tile with transpose reads.
-// One E4M3 copy of K and V serves both products; only the LDS read instruction differs.
+// One E4M3 copy of K and V serves both products; only the LDS read instruction differs.  K/V
+// tiles arrive by direct global-to-LDS loads one tile ahead (two K, three V buffers), and the
+// upper four waves run each tile's PV product at the start of the next tile, so the two waves
+// sharing a SIMD are out of phase: one's matrix products overlap the other's softmax terms.
 #include "device_common.h"
 #include "kernels.h"
 
