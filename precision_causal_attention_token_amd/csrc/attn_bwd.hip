@@ -84,8 +84,9 @@ struct BwdSmem {
 // Step tiles go from global memory straight into LDS (16-byte direct loads: lane l of a wave
 // writes bytes 16 l .. 16 l + 15 of the wave's 1 KiB LDS block), issued by the four consumer
 // waves two phases ahead.  Each lane fetches the global chunk that belongs at its LDS position
-// under the tile's swizzle.  Rows past the document end repeat its last row: every use of those
-// rows is masked to zero, and the repeated values are finite.
+// under the tile's swizzle.  Rows past the document end repeat its last row, and 1 KiB blocks
+// wholly past it are zero-filled instead of loaded: every use of those rows is masked to zero,
+// and the values are finite.
 template <int D>
 __device__ __forceinline__ void issue_step_loads(const BwdParams& p, BwdSmem<D>& sm, int b, int doc_start, int L,
                                                  int h, int qt, int cw, int lane) {
@@ -101,10 +102,15 @@ __device__ __forceinline__ void issue_step_loads(const BwdParams& p, BwdSmem<D>&
     const int pos = blk * 64 + lane;             // 16-byte chunk position in the tile
     const int row = pos / CPR, pc = pos % CPR;
     const int lc = pc ^ lds_swizzle<D>(row);     // logical chunk stored at this position
-    const int qr = min(q0 + row, L - 1);
-    const uint8_t* src = (is_do ? p.dO : p.q) + ((int64_t)(doc_start + qr) * p.Hq + h) * D + 16 * lc;
     uint8_t* dst = (is_do ? sm.dO[b] : sm.q[b]) + blk * 1024;
-    dma_load16(src, lds_addr(dst));
+    if (q0 + blk * (1024 / D) < L) {
+      const int qr = min(q0 + row, L - 1);
+      const uint8_t* src = (is_do ? p.dO : p.q) + ((int64_t)(doc_start + qr) * p.Hq + h) * D + 16 * lc;
+      dma_load16(src, lds_addr(dst));
+    } else {
+      // a block wholly past the document end: zeros (its rows only need to be finite)
+      *reinterpret_cast<uint4*>(dst + 16 * lane) = make_uint4(0, 0, 0, 0);
+    }
   }
   if (cw < 2) {  // row statistics: one float per lane
     const int qr = min(q0 + lane, L - 1);

@@ -57,9 +57,16 @@ __device__ __forceinline__ uint32_t issue_tile(const FwdParams& p, FwdSmem<D>& s
     const int pos = blk * 64 + lane;                 // chunk position in the tile
     const int row = pos / CPR, pc = pos % CPR;
     const int lc = pc ^ lds_swizzle<D>(row);         // logical chunk stored there
-    const int key = min(KV_TILE * kappa + row, L - 1);
-    const uint8_t* src = (is_v ? p.v : p.k) + ((int64_t)(doc_start + key) * p.Hkv + g) * D + 16 * lc;
-    dma_load16(src, lds_addr((is_v ? sm.v[vb] : sm.k[kb]) + blk * 1024));
+    uint8_t* dst = (is_v ? sm.v[vb] : sm.k[kb]) + blk * 1024;
+    if (KV_TILE * kappa + blk * (1024 / D) < L) {
+      const int key = min(KV_TILE * kappa + row, L - 1);
+      const uint8_t* src = (is_v ? p.v : p.k) + ((int64_t)(doc_start + key) * p.Hkv + g) * D + 16 * lc;
+      dma_load16(src, lds_addr(dst));
+    } else if (is_v) {
+      // a block wholly past the document end: its V rows meet zero probabilities and only need
+      // to be finite; its K rows are masked and are not loaded at all
+      *reinterpret_cast<uint4*>(dst + 16 * lane) = make_uint4(0, 0, 0, 0);
+    }
   }
   const int tid = threadIdx.x;
   uint32_t sc = 127;
