@@ -383,10 +383,11 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
           }
         };
         fused(ph, 1, xs, xq, ph, 0, q0, cs, cp, pp, pd, sp[0], sds[0], masked);
+        // empty uses of freshly issued products keep their matrix instructions among the vector
+        // work they overlap, instead of sunk past the hand-over towards their next use
+        asm volatile("" ::"v"(xs), "v"(xq));
         hand_over(0);
         fused(min(ph + 1, n_steps - 1), 0, cs, cp, ph, 1, q0, xs, xq, pp + 4, pd + 4, sp[1], sds[1], masked);
-        // an empty use of the next step's products: keeps their matrix instructions here, among
-        // the vector work, instead of sunk to the end of the phase next to their next use
         asm volatile("" ::"v"(cs), "v"(cp));
         hand_over(1);
         if (lane == 0) {
