@@ -137,7 +137,7 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
   const int tid = threadIdx.x;
   // the wave index is uniform: in a scalar register, everything derived from it stays scalar
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int n = lane & 31, hh = lane >> 5;
+  const int n = lane & 31;
   const bool producer = wave < 4;
   const int kw = wave & 3;  // key group of both roles
   const int n_items = p.list[0];

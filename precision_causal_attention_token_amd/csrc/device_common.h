@@ -125,7 +125,9 @@ typedef __attribute__((address_space(3))) void* lds_void_ptr;
 // that they write other buffers than the ones being read, and would otherwise wait for them
 // (for the whole global-memory round trip) before every LDS read that follows.  The kernels
 // wait for them explicitly (s_waitcnt) before the barrier that publishes the buffer.  M0 holds
-// the LDS address of the wave's block; one wait state separates its write from the load.
+// the LDS address of the wave's block; one wait state separates its write from the load.  M0 is
+// a reserved register, so the compiler does not honour its clobber here: these kernels must not
+// use M0 for anything else, which a host-side check of their assembly verifies.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)__builtin_amdgcn_readfirstlane((int)(uintptr_t)(lds_void_ptr)p);
 }

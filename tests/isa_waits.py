@@ -117,3 +117,36 @@ def close_reads(asm, symbol, need=NEED):
         if best is not None:
             found.append((i, best[0], best[1]))
     return found, n_mfma
+
+
+def m0_uses(asm, symbol):
+    """Instructions of `symbol` that read or write M0, as (index, text).  The kernels set M0 only
+    for their direct global-to-LDS loads, in the fixed sequence s_mov_b32 m0 / s_nop 0 /
+    global_load_lds_*; anything else touching M0 would be the compiler's, and could be clobbered
+    by that sequence (the inline assembly's M0 clobber is not honoured: M0 is reserved)."""
+    ins = _instructions(asm, symbol)
+    out = []
+    for i, (op, ops) in enumerate(ins):
+        if op == "LABEL":
+            continue
+        if any(o.strip().split()[0] == "m0" for o in ops if o.strip()) or op.startswith("global_load_lds"):
+            out.append((i, op, ops))
+    return ins, out
+
+
+def stray_m0_uses(asm, symbol):
+    """M0 uses outside the direct-load sequence: [] when the kernel is safe."""
+    ins, uses = m0_uses(asm, symbol)
+    bad = []
+    k = 0
+    while k < len(uses):
+        i, op, ops = uses[k]
+        ok = (op == "s_mov_b32" and ops[0].strip() == "m0" and i + 2 < len(ins)
+              and ins[i + 1][0] == "s_nop" and ins[i + 2][0].startswith("global_load_lds")
+              and k + 1 < len(uses) and uses[k + 1][0] == i + 2)
+        if ok:
+            k += 2
+            continue
+        bad.append("%s %s" % (op, ", ".join(ops)))
+        k += 1
+    return bad

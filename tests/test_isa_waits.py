@@ -44,3 +44,22 @@ def test_checker_flags_a_short_distance():
     branchy = mf + "\ts_cbranch_scc1 .LBB0_1\n" + "\ts_nop 15\n\ts_nop 7\n" + ".LBB0_1:\n" + read
     res, _ = isa_waits.close_reads(kern(branchy), "k")
     assert [r[1] for r in res] == [1]
+
+
+@pytest.mark.skipif(not os.path.exists(build.HIPCC), reason="hipcc not installed")
+@pytest.mark.parametrize("src,pattern", KERNELS)
+def test_m0_only_in_direct_load_sequences(tmp_path, src, pattern):
+    """M0 is written only by the direct-load sequence, which always writes it right before its
+    load: no compiler-placed M0 value can be live across it."""
+    asm = isa_waits.compile_to_asm(os.path.join(build.CSRC, src), str(tmp_path / (src + ".s")), build.HIPCC,
+                                   build.FLAGS)
+    for sym in isa_waits.kernel_symbols(asm, pattern):
+        assert isa_waits.stray_m0_uses(asm, sym) == [], sym
+
+
+def test_m0_checker_flags_a_stray_use():
+    k = lambda body: "k:\n" + body + "\ts_endpgm\n.Lfunc_end0:\n"
+    good = "\ts_mov_b32 m0, s4\n\ts_nop 0\n\tglobal_load_lds_dwordx4 v[0:1], off\n"
+    assert isa_waits.stray_m0_uses(k(good), "k") == []
+    assert isa_waits.stray_m0_uses(k("\ts_mov_b32 m0, s5\n" + good), "k") != []
+    assert isa_waits.stray_m0_uses(k("\ts_mov_b32 m0, s4\n\tglobal_load_lds_dwordx4 v[0:1], off\n"), "k") != []
