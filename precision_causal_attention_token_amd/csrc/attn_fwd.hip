@@ -77,6 +77,48 @@ __device__ __forceinline__ uint32_t issue_tile(const FwdParams& p, FwdSmem<D>& s
   return sc;
 }
 
+// A tile wholly inside the document (every tile after a unit's first): no row needs clamping,
+// so each of the wave's blocks is one wave-uniform base address plus a per-lane offset. Within a
+// wave the blocks are consecutive and of one tensor; block i sits 64 i / CPR rows below block 0,
+// and since the swizzle is a bit permutation of row bits below that step, its chunk differs
+// from block 0's by the swizzle of that row step alone, whatever the lane.
+template <int D>
+__device__ __forceinline__ uint32_t issue_full_tile(const FwdParams& p, FwdSmem<D>& sm, int kb, int vb, int g,
+                                                    int doc_start, int kappa, int wave, uint32_t voff0) {
+  constexpr int CPR = D / 16;
+  constexpr int BLOCKS = KV_TILE * D / 1024;
+  constexpr int PER_WAVE = 2 * BLOCKS / FWD_WAVES;
+  static_assert(BLOCKS % PER_WAVE == 0, "no wave's blocks span both tensors");
+  static_assert(16 * CPR <= D && (D & (D - 1)) == 0, "chunk offsets stay below the row stride");
+  const bool is_v = wave * PER_WAVE >= BLOCKS;
+  const int blk0 = wave * PER_WAVE - (is_v ? BLOCKS : 0);
+  uint8_t* dst = (is_v ? sm.v[vb] : sm.k[kb]) + blk0 * 1024;
+  // the base address from the wave index read as a scalar (the LDS address above keeps the
+  // per-lane form, which the compiler turns into a scalar itself)
+  const int ws = __builtin_amdgcn_readfirstlane(wave);
+  const bool vs = ws * PER_WAVE >= BLOCKS;
+  const uint8_t* base =
+      (vs ? p.v : p.k) + ((int64_t)(doc_start + KV_TILE * kappa + (ws * PER_WAVE - (vs ? BLOCKS : 0)) * (64 / CPR)) * p.Hkv + g) * D;
+#pragma unroll
+  for (int i = 0; i < PER_WAVE; ++i) {
+    const uint32_t dsw = 16 * lds_swizzle<D>(i * (64 / CPR));
+    dma_load16_sv(base + (int64_t)i * (64 / CPR) * p.Hkv * D, voff0 ^ dsw, lds_addr(dst + i * 1024));
+  }
+  const int tid = threadIdx.x;
+  uint32_t sc = 127;
+  if (tid < 2 * KV_TILE)
+    sc = (tid < KV_TILE ? p.sk : p.sv)[(int64_t)g * p.T + doc_start + KV_TILE * kappa + (tid & (KV_TILE - 1))];
+  return sc;
+}
+// Per-lane byte offset, from its first row, of the chunk the lane fetches in the wave's first
+// block of a full tile.
+template <int D>
+__device__ __forceinline__ uint32_t tile_offset(const FwdParams& p, int lane) {
+  constexpr int CPR = D / 16;
+  const int row = lane / CPR, pc = lane % CPR;
+  return (uint32_t)(row * p.Hkv * D + 16 * (pc ^ lds_swizzle<D>(row)));
+}
+
 template <int D>
 __device__ __forceinline__ void store_scales(FwdSmem<D>& sm, int kb, int vb, uint32_t sc) {
   const int tid = threadIdx.x;
@@ -99,6 +141,7 @@ __global__ __launch_bounds__(FWD_THREADS) void fwd_kernel(FwdParams p) {
   const int G = gridDim.x, wg = blockIdx.x;
   const int grp = p.Hq / p.Hkv;
   const float c = p.c;
+  const uint32_t voff0 = tile_offset<D>(p, lane);
 
   for (int round = 0;; ++round) {
     const int u = round * G + ((round & 1) ? (G - 1 - wg) : wg);
@@ -177,7 +220,7 @@ __global__ __launch_bounds__(FWD_THREADS) void fwd_kernel(FwdParams p) {
       const int kb = it & 1;
       const int vbn = vb == 2 ? 0 : vb + 1, vbp = vb == 0 ? 2 : vb - 1;
       uint32_t scn = 127;
-      if (kappa > 0) scn = issue_tile<D>(p, sm, kb ^ 1, vbn, g, doc_start, L, kappa - 1, wave, lane);
+      if (kappa > 0) scn = issue_full_tile<D>(p, sm, kb ^ 1, vbn, g, doc_start, kappa - 1, wave, voff0);
       if (pending) {  // late waves: the previous tile's PV product
         pv_product(vbp);
         pending = false;
