@@ -94,6 +94,22 @@ __device__ __forceinline__ void issue_step_loads(const BwdParams& p, BwdSmem<D>&
   constexpr int BLOCKS = QT * D / 1024;          // 1 KiB wave blocks per tile (4 or 8)
   constexpr int PER_WAVE = 2 * BLOCKS / 4;       // Q and dO blocks per consumer wave
   const int q0 = QT * qt;
+  if (q0 + QT <= L) {
+    // a tile wholly inside the document: no row clamp, so the wave's blocks (consecutive, of one
+    // tensor) are one scalar base each plus the lane's fixed offset; block i sits 64 i / CPR rows
+    // below block 0, and the swizzle, a bit permutation of row bits below that step, moves its
+    // chunk by the swizzle of the row step alone
+    static_assert(BLOCKS % PER_WAVE == 0, "no wave's blocks span both tensors");
+    const bool is_do = cw * PER_WAVE >= BLOCKS;
+    const int blk0 = cw * PER_WAVE - (is_do ? BLOCKS : 0);
+    const uint8_t* base = (is_do ? p.dO : p.q) + ((int64_t)(doc_start + q0 + blk0 * (64 / CPR)) * p.Hq + h) * D;
+    const uint32_t voff0 = (uint32_t)((lane / CPR) * p.Hq * D + 16 * ((lane % CPR) ^ lds_swizzle<D>(lane / CPR)));
+    uint8_t* dst = (is_do ? sm.dO[b] : sm.q[b]) + blk0 * 1024;
+#pragma unroll
+    for (int i = 0; i < PER_WAVE; ++i)
+      dma_load16_sv(base + (int64_t)i * (64 / CPR) * p.Hq * D, voff0 ^ (16 * lds_swizzle<D>(i * (64 / CPR))),
+                    lds_addr(dst + i * 1024));
+  } else {
 #pragma unroll
   for (int i = 0; i < PER_WAVE; ++i) {
     const int wb = cw * PER_WAVE + i;            // 0 .. 2 BLOCKS - 1: Q blocks, then dO blocks
@@ -111,6 +127,7 @@ __device__ __forceinline__ void issue_step_loads(const BwdParams& p, BwdSmem<D>&
       // a block wholly past the document end: zeros (its rows only need to be finite)
       *reinterpret_cast<uint4*>(dst + 16 * lane) = make_uint4(0, 0, 0, 0);
     }
+  }
   }
   if (cw < 2) {  // row statistics: one float per lane
     const int qr = min(q0 + lane, L - 1);
