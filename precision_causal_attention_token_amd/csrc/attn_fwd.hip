@@ -241,13 +241,17 @@ __global__ __launch_bounds__(FWD_THREADS) void fwd_kernel(FwdParams p) {
         }
         // ---- causal mask on the diagonal tile (keys after the query)
         if (kappa == kd) {
+          // key 128 kappa + 32 kb4 + acc_row(i, hh) lies after the query when the constant part
+          // 32 kb4 + acc_row(i, 0) exceeds lim; lim is formed here, opaque to the compiler, so
+          // the 64 comparisons stay in this branch instead of held as lane masks in scalar
+          // registers across the loop
+          int lim = q_rel - KV_TILE * kappa - 4 * hh;
+          asm volatile("" : "+v"(lim));
 #pragma unroll
           for (int kb4 = 0; kb4 < 4; ++kb4)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int key = KV_TILE * kappa + 32 * kb4 + acc_row(i, hh);
-              if (key > q_rel) s[kb4][i] = -__builtin_inff();
-            }
+            for (int i = 0; i < 16; ++i)
+              if (32 * kb4 + acc_row(i, 0) > lim) s[kb4][i] = -__builtin_inff();
         }
         // ---- running max (raw accumulator units, then scaled once)
         float mx = -__builtin_inff();
