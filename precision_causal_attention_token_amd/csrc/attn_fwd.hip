@@ -14,9 +14,9 @@
 //                                    the MFMA operand order (no data movement between lanes);
 //   O^T += V^T P^T                 : A = V^T read from the row-major V tile with transpose reads.
 // One E4M3 copy of K and V serves both products; only the LDS read instruction differs.  K/V
-// tiles arrive by direct global-to-LDS loads one tile ahead (two K, three V buffers), and the
-// upper four waves run each tile's PV product at the start of the next tile, so the two waves
-// sharing a SIMD are out of phase: one's matrix products overlap the other's softmax terms.
+// tiles arrive by direct global-to-LDS loads one tile ahead (two buffers each).  A wave issues
+// its instructions one at a time, so the PV product's matrix instructions are spread between
+// the vector instructions of the exponentials and the row sum, where they run underneath them.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -30,13 +30,13 @@ constexpr int FWD_THREADS = 64 * FWD_WAVES;
 template <int D>
 struct FwdSmem {
   uint8_t k[2][KV_TILE * D];
-  uint8_t v[3][KV_TILE * D];
+  uint8_t v[2][KV_TILE * D];
   uint8_t sk[2][KV_TILE];
-  uint8_t sv[3][KV_TILE];
+  uint8_t sv[2][KV_TILE];
 };
 
-// Tile i of a unit (key tile kappa_hi - i) sits in K buffer i % 2 and V buffer i % 3: while tile
-// i is current, the staggered waves still read tile i - 1's V and tile i + 1 is being loaded.
+// Tile i of a unit (key tile kappa_hi - i) sits in K and V buffers i % 2: while tile i is current,
+// tile i + 1 is being loaded.
 // K and V rows go global -> LDS with direct loads, each lane fetching the 16-byte chunk that
 // belongs at its LDS position under the tile's swizzle; rows past the document end repeat its
 // last row (their scores are masked, their probabilities are zero, and the values are finite).
@@ -185,29 +185,6 @@ __global__ __launch_bounds__(FWD_THREADS) void fwd_kernel(FwdParams p) {
     float m = -__builtin_inff();  // running max, score units
     float l = 0.f;                // this lane's share of the row sum of 2^8 p
 
-    // O^T += V^T P^T for the P codes pk of the tile whose V sits in buffer vb
-    int pk[4][4];
-    auto pv_product = [&](int vb) {
-      const uint8_t* vt = sm.v[vb];
-#pragma unroll
-      for (int ci = 0; ci < 2; ++ci) {
-        v8i pop;
-#pragma unroll
-        for (int w = 0; w < 8; ++w) pop[w] = pk[2 * ci + (w >> 2)][w & 3];
-        const int vs = sm.sv[vb][64 * ci + 32 * hh];
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const v8i a = lds_read_tr32<D>(vt, 64 * ci, 32 * db, lane);
-          oacc[db] = mfma_scaled(a, pop, oacc[db], vs, 127 - P_SHIFT);
-        }
-      }
-    };
-    // The four upper waves run each tile's PV product at the start of the next tile: on every
-    // SIMD one wave of each kind, so one wave's score products and softmax terms meet the other
-    // wave's PV products and the vector and matrix units both have work.
-    const bool late = wave >= FWD_WAVES / 2;
-    bool pending = false;
-
     lds_barrier();  // the previous unit's readers are done with every buffer
     {
       const uint32_t sc = issue_tile<D>(p, sm, 0, 0, g, doc_start, L, kappa_hi, wave, lane);
@@ -215,16 +192,10 @@ __global__ __launch_bounds__(FWD_THREADS) void fwd_kernel(FwdParams p) {
       store_scales<D>(sm, 0, 0, sc);
     }
     lds_barrier();
-    int vb = 0;  // V buffer of the current tile (tile index mod 3)
     for (int kappa = kappa_hi, it = 0; kappa >= 0; --kappa, ++it) {
       const int kb = it & 1;
-      const int vbn = vb == 2 ? 0 : vb + 1, vbp = vb == 0 ? 2 : vb - 1;
       uint32_t scn = 127;
-      if (kappa > 0) scn = issue_full_tile<D>(p, sm, kb ^ 1, vbn, g, doc_start, kappa - 1, wave, voff0);
-      if (pending) {  // late waves: the previous tile's PV product
-        pv_product(vbp);
-        pending = false;
-      }
+      if (kappa > 0) scn = issue_full_tile<D>(p, sm, kb ^ 1, kb ^ 1, g, doc_start, kappa - 1, wave, voff0);
       if (wave_active && kappa <= kd) {
         const uint8_t* kt = sm.k[kb];
         // ---- S^T for the 4 key blocks of the tile
@@ -270,10 +241,28 @@ __global__ __launch_bounds__(FWD_THREADS) void fwd_kernel(FwdParams p) {
           l *= alpha;
         }
         m = m_new;
-        // ---- p = 2^(t - m), scaled by 2^8 for the E4M3 operand; packed into operand order
+        // ---- p = 2^(t - m), scaled by 2^8 for the E4M3 operand, packed into operand order;
+        // O^T += V^T P^T in two halves of 64 keys.  A wave issues one instruction at a time, so
+        // the eight matrix instructions are spread between vector instructions instead of
+        // issued in a burst: the first half's run between the exponentials of key blocks 2 and
+        // 3 (the probabilities overwrite their scores), the second half's between those blocks'
+        // additions to the row sum, which come last (the order of the additions is unchanged).
         const float bias = (float)P_SHIFT - m_new;
+        const uint8_t* vt = sm.v[kb];
+        v8i pop[2];
+        int vs[2];
 #pragma unroll
-        for (int kb4 = 0; kb4 < 4; ++kb4)
+        for (int ci = 0; ci < 2; ++ci) vs[ci] = sm.sv[kb][64 * ci + 32 * hh];
+        auto read_v = [&](int k) { return lds_read_tr32<D>(vt, 64 * (k / NDB), 32 * (k % NDB), lane); };
+        constexpr int NPV = 2 * NDB;  // matrix instructions: (64-key half ci, d-block db)
+        v8i ring[2];
+        auto pv_step = [&](int k) {
+          oacc[k % NDB] = mfma_scaled(ring[k & 1], pop[k / NDB], oacc[k % NDB], vs[k / NDB], 127 - P_SHIFT);
+          if (k + 2 < NPV) ring[k & 1] = read_v(k + 2);
+        };
+        // blocks 0, 1: probabilities, row sum, codes
+#pragma unroll
+        for (int kb4 = 0; kb4 < 2; ++kb4)
 #pragma unroll
           for (int w4 = 0; w4 < 4; ++w4) {
             const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb4][4 * w4 + 0], c, bias));
@@ -281,19 +270,49 @@ __global__ __launch_bounds__(FWD_THREADS) void fwd_kernel(FwdParams p) {
             const float p2 = __builtin_amdgcn_exp2f(fmaf(s[kb4][4 * w4 + 2], c, bias));
             const float p3 = __builtin_amdgcn_exp2f(fmaf(s[kb4][4 * w4 + 3], c, bias));
             l += (p0 + p1) + (p2 + p3);
-            pk[kb4][w4] = pack4_fp8(p0, p1, p2, p3);
+            pop[0][4 * kb4 + w4] = pack4_fp8(p0, p1, p2, p3);
           }
-        if (late) pending = true;
-        else pv_product(vb);
+        ring[0] = read_v(0);
+        ring[1] = read_v(1);
+        asm volatile("" : "+v"(l));  // this part of the row sum formed here, not sunk below
+        __builtin_amdgcn_sched_barrier(0);
+        // blocks 2, 3: probabilities (in place) and codes, one matrix instruction per half block
+#pragma unroll
+        for (int kb4 = 2; kb4 < 4; ++kb4)
+#pragma unroll
+          for (int hb = 0; hb < 2; ++hb) {
+#pragma unroll
+            for (int w4 = 2 * hb; w4 < 2 * hb + 2; ++w4) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) s[kb4][4 * w4 + e] = __builtin_amdgcn_exp2f(fmaf(s[kb4][4 * w4 + e], c, bias));
+              pop[1][4 * (kb4 - 2) + w4] =
+                  pack4_fp8(s[kb4][4 * w4], s[kb4][4 * w4 + 1], s[kb4][4 * w4 + 2], s[kb4][4 * w4 + 3]);
+            }
+            // first half, instructions 0 .. NDB - 1, spread over the four half blocks
+            const int j = 2 * (kb4 - 2) + hb;
+            if ((j + 1) * NDB / 4 > j * NDB / 4) pv_step(j * NDB / 4);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        // second half's instructions between the remaining row-sum additions
+#pragma unroll
+        for (int k = NDB; k < NPV; ++k) {
+          pv_step(k);
+#pragma unroll
+          for (int j = 0; j < 8 / NDB; ++j) {
+            const int w = (k - NDB) * (8 / NDB) + j;  // word 0..7 of blocks 2, 3
+            const int kb4 = 2 + w / 4, w4 = w % 4;
+            l += (s[kb4][4 * w4] + s[kb4][4 * w4 + 1]) + (s[kb4][4 * w4 + 2] + s[kb4][4 * w4 + 3]);
+          }
+          asm volatile("" : "+v"(l));
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
       if (kappa > 0) {
         __builtin_amdgcn_s_waitcnt(0);  // this wave's direct loads have landed
-        store_scales<D>(sm, kb ^ 1, vbn, scn);
+        store_scales<D>(sm, kb ^ 1, kb ^ 1, scn);
         lds_barrier();
       }
-      vb = vbn;
     }
-    if (pending) pv_product(vb == 0 ? 2 : vb - 1);  // the last tile's V buffer
 
     // ---- epilogue: O = acc / l, LSE = m + log2 l (l in units of 2^-8)
     if (wave_active) {

@@ -165,8 +165,12 @@ __device__ __forceinline__ float exp2i(int s) { return __uint_as_float((uint32_t
 
 // E4M3 conversion: round to nearest even, hardware instruction.
 // Four floats -> one dword of E4M3 bytes (a0 lowest).
+// The first conversion's upper half is overwritten by the second, so its starting value is left
+// undefined (no instruction clears the register first).
 __device__ __forceinline__ int pack4_fp8(float a0, float a1, float a2, float a3) {
-  const int r = __builtin_amdgcn_cvt_pk_fp8_f32(a0, a1, 0, false);
+  int u;
+  asm volatile("" : "=v"(u));  // an undefined register, formed by no instruction
+  const int r = __builtin_amdgcn_cvt_pk_fp8_f32(a0, a1, u, false);
   return __builtin_amdgcn_cvt_pk_fp8_f32(a2, a3, r, true);
 }
 

@@ -26,9 +26,11 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantParams p) {
   __shared__ int16_t bexp[ROWS];        // exponent for every owned row
 
   const int tid = threadIdx.x;
-  const int W0 = blockIdx.x * WIN;
-  const int h = blockIdx.y;
-  const QTensorDev& X = p.t[blockIdx.z];
+  // heads vary fastest over the grid, so the workgroups running at one time read whole token
+  // rows ([T, H, d] packs a token's heads together) rather than one head's slice of many rows
+  const int h = blockIdx.x % p.maxH;
+  const int W0 = (blockIdx.x / p.maxH) * WIN;
+  const QTensorDev& X = p.t[blockIdx.y];
   if (h >= X.H) return;
   const int T = p.T;
 
@@ -88,9 +90,14 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantParams p) {
   // ---- block exponents (thread per block start)
   for (int r = tid; r < ROWS; r += 256) {
     if (own_start[r] == r) {
+      // all 32 reads issued at once (independent, one wait), rows past the block masked off
       float m = 0.f;
       const int len = blk_len[r];
-      for (int i = 0; i < len; ++i) m = fmaxf(m, rmax[r + i]);
+#pragma unroll
+      for (int i = 0; i < BLK; ++i) {
+        const float x = rmax[min(r + i, ROWS - 1)];
+        m = i < len ? fmaxf(m, x) : m;
+      }
       bexp[r] = (int16_t)e8m0_roundup(m);
     }
   }
@@ -164,7 +171,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantParams p) {
 
 hipError_t launch_quantize(const QuantParams& p, int d, hipStream_t s) {
   if (p.T == 0) return hipSuccess;
-  dim3 grid((p.T + WIN - 1) / WIN, p.maxH, p.n_tensors);
+  dim3 grid(p.maxH * ((p.T + WIN - 1) / WIN), p.n_tensors);  // (window, head) with the head fastest
   if (d == 128) hipLaunchKernelGGL(quantize_kernel<128>, grid, dim3(256), 0, s, p);
   else hipLaunchKernelGGL(quantize_kernel<64>, grid, dim3(256), 0, s, p);
   return hipGetLastError();
