@@ -138,10 +138,13 @@ __device__ __forceinline__ void issue_step_loads(const BwdParams& p, BwdSmem<D>&
 
 // Key-stationary pass.  Producer wave w (0..3) owns keys 32 w .. 32 w + 31 of the tile: per
 // 64-query step it forms S and dP, the softmax terms, and the E4M3 Phat / dShat operands with
-// their 32 x 32 block exponents, hands them over in LDS and stores dShat from its registers.
-// Its matrix products run one query block ahead of its softmax terms, so the two overlap.
+// their 32 x 32 block exponents and hands them over in LDS.  Its matrix products run one query
+// block ahead of its softmax terms, so the two overlap.
 // Consumer wave 4 + w holds dK^T and dV^T of the same keys and runs the gradient products one
-// step behind, so its matrix instructions overlap the producer's vector work on the same SIMD.
+// step behind, so its matrix instructions overlap the producer's vector work on the same SIMD;
+// it also stores the step's dShat codes and exponents to the workspace.  A wave issues one
+// instruction at a time, and the producer's stream is the longer one (it sets the phase
+// length), so work that either role can do is given to the consumer.
 // Phase k: producers finish step k and form the products of step k + 1, consumers work on step
 // k - 1 and load step k + 2; one barrier per phase.
 template <int D>
@@ -377,18 +380,13 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
         const int q0 = QT * qt;
         const int x2 = ph & 1;
         int pp[8], pd[8], sp[2], sds[2];
-        uint8_t* bbase = p.ds_store + (ds_block(ds_base, kappa, n_qt, qt) * p.Hq + h) * DS_STRIDE;
-        // hand over query block qb's operands (and store its dShat half) as soon as they exist,
-        // so the writes retire under the next block's work instead of before the barrier
+        // hand over query block qb's operands as soon as they exist, so the writes retire under
+        // the next block's work instead of before the barrier (the consumer stores dShat to the
+        // workspace)
         auto hand_over = [&](int qb) {
           sm.xp[x2][kw][qb][lane] = make_int4(pp[4 * qb], pp[4 * qb + 1], pp[4 * qb + 2], pp[4 * qb + 3]);
           sm.xd[x2][kw][qb][lane] = make_int4(pd[4 * qb], pd[4 * qb + 1], pd[4 * qb + 2], pd[4 * qb + 3]);
-          if (store_ds) {
-            // dShat to the workspace, straight from registers: key row 32 kw + n holds 64 bytes,
-            // lane group hh's 32 operand bytes at 32 hh, query block qb's 16 of them at 16 qb
-            *reinterpret_cast<int4*>(bbase + (32 * kw + n) * QT + 32 * hh + 16 * qb) =
-                make_int4(pd[4 * qb], pd[4 * qb + 1], pd[4 * qb + 2], pd[4 * qb + 3]);
-          } else {
+          if (!store_ds) {
             int l = lane;
             asm volatile("" : "+v"(l));  // addresses formed here, not kept in registers all along
             const int nl = l & 31, hl = l >> 5;
@@ -412,10 +410,6 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
           for (int qb = 0; qb < 2; ++qb) {
             sm.xs_p[x2][qb][kw] = sp[qb] + 127;
             sm.xs_d[x2][qb][kw] = sds[qb] + 127;
-          }
-          if (store_ds) {
-            bbase[DS_BLOCK + kw] = (uint8_t)(sds[0] + 127);
-            bbase[DS_BLOCK + 4 + kw] = (uint8_t)(sds[1] + 127);
           }
         }
       };
@@ -447,6 +441,7 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
       for (int db = 0; db < NDB; ++db) { dkacc[db] = v16f{}; dvacc[db] = v16f{}; }
       int ld_h = 0, ld_qt = 0;  // head and query tile of step ph + 2 (the next to load)
       if (n_steps > 2) ld_qt = step_qt(2, ld_h);
+      int st_h = g * grp, st_qt = 2 * kappa;  // head and query tile of step ph - 1
       for (int ph = 0; ph <= n_steps; ++ph) {
         const int qtn = ld_qt;
         const int bn = (ph + 2) & (NBUF - 1);
@@ -465,6 +460,23 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
           {
             const int4 p0 = sm.xp[xb][kw][0][lane], p1 = sm.xp[xb][kw][1][lane];
             const int4 d0 = sm.xd[xb][kw][0][lane], d1 = sm.xd[xb][kw][1][lane];
+            if (store_ds) {
+              // dShat codes and block exponents of step ph - 1 to the workspace, from the operand
+              // registers (the producer's wave stream is the longer one): key row 32 kw + n
+              // holds 64 bytes, lane group hh's 32 operand bytes at 32 hh
+              uint8_t* bbase = p.ds_store + (ds_block(ds_base, kappa, n_qt, st_qt) * p.Hq + st_h) * DS_STRIDE;
+              int4* dst = reinterpret_cast<int4*>(bbase + (32 * kw + n) * QT + 32 * hh);
+              dst[0] = d0;
+              dst[1] = d1;
+              if (lane == 0) {
+                bbase[DS_BLOCK + kw] = (uint8_t)sm.xs_d[xb][0][kw];
+                bbase[DS_BLOCK + 4 + kw] = (uint8_t)sm.xs_d[xb][1][kw];
+              }
+            }
+            if (++st_qt == n_qt) {
+              st_qt = 2 * kappa;
+              ++st_h;
+            }
             const v8i bp = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
             const v8i bd = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
             const int sdo_h = sm.sdo[b][hh], sq_h = sm.sq[b][hh];
@@ -688,34 +700,49 @@ __global__ __launch_bounds__(DQ_THREADS) void dq_kernel(BwdParams p) {
           sb[ci] = sm.dsc[b][t4][4 * qb_l + 2 * ci + hh];
         }
         // K^T operand k (d-block k / 2, key half k % 2) read three products ahead; the partial
-        // of d-block db is added to the FP16 sums while the products of d-block db + 1 run
+        // of d-block db is added to the FP16 sums while the products of d-block db + 1 run.
+        // The prescale 2^pi of the lane's query is folded into the dShat operand's scale byte
+        // when every such byte stays a finite E8M0 exponent: the instruction then returns
+        // partial * 2^pi itself (a power-of-two scale commutes with the rounding; the results
+        // are far inside the normal range, |partial * 2^pi| <= 2^15), and no multiply is needed.
+        // Otherwise (a rare block exponent near either end of the range) the partial is
+        // multiplied by 2^pi as it stands.
         constexpr int NOP = 2 * NDB, AHEAD = 3;
         auto read_k = [&](int k) { return lds_read_tr32<D>(sm.k[b], 64 * (k & 1), 32 * (k >> 1), lane); };
-        auto add_partial = [&](v16f& part, int db) {
-          mfma_drain(part);
+        const int f0 = sb[0] + pi, f1 = sb[1] + pi;
+        const bool fold_ok = (unsigned)f0 <= 254u && (unsigned)f1 <= 254u;
+        auto run = [&](auto fold) {
+          constexpr bool FOLD = decltype(fold)::value;
+          const int sc[2] = {FOLD ? f0 : sb[0], FOLD ? f1 : sb[1]};
+          auto add_partial = [&](v16f& part, int db) {
+            mfma_drain(part);
 #pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const h2 x = h2{(_Float16)(part[2 * j] * up), (_Float16)(part[2 * j + 1] * up)};
-            acc16[db][j] = acc16[db][j] + x;
+            for (int j = 0; j < 8; ++j) {
+              const h2 x = FOLD ? h2{(_Float16)part[2 * j], (_Float16)part[2 * j + 1]}
+                                : h2{(_Float16)(part[2 * j] * up), (_Float16)(part[2 * j + 1] * up)};
+              acc16[db][j] = acc16[db][j] + x;
+            }
+          };
+          v8i ring[AHEAD];
+#pragma unroll
+          for (int k = 0; k < AHEAD; ++k) ring[k] = read_k(k);
+          v16f part[2];
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+            for (int ci = 0; ci < 2; ++ci) {
+              const int k = 2 * db + ci;
+              part[db & 1] = mfma_scaled(ring[k % AHEAD], bs[ci], ci ? part[db & 1] : v16f{},
+                                         sm.sk[b][64 * ci + 32 * hh], sc[ci]);
+              if (k + AHEAD < NOP) ring[k % AHEAD] = read_k(k + AHEAD);
+            }
+            if (db >= 1) add_partial(part[(db - 1) & 1], db - 1);
+            __builtin_amdgcn_sched_barrier(0);
           }
+          add_partial(part[(NDB - 1) & 1], NDB - 1);
         };
-        v8i ring[AHEAD];
-#pragma unroll
-        for (int k = 0; k < AHEAD; ++k) ring[k] = read_k(k);
-        v16f part[2];
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-#pragma unroll
-          for (int ci = 0; ci < 2; ++ci) {
-            const int k = 2 * db + ci;
-            part[db & 1] = mfma_scaled(ring[k % AHEAD], bs[ci], ci ? part[db & 1] : v16f{},
-                                       sm.sk[b][64 * ci + 32 * hh], sb[ci]);
-            if (k + AHEAD < NOP) ring[k % AHEAD] = read_k(k + AHEAD);
-          }
-          if (db >= 1) add_partial(part[(db - 1) & 1], db - 1);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        add_partial(part[(NDB - 1) & 1], NDB - 1);
+        if (__all(fold_ok)) run(std::true_type{});
+        else run(std::false_type{});
       }
     };
     // one tile: loads of kappa + 2 into `spare`, compute kappa, `next` (kappa + 1) into LDS.  The
