@@ -463,14 +463,16 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
             if (store_ds) {
               // dShat codes and block exponents of step ph - 1 to the workspace, from the operand
               // registers (the producer's wave stream is the longer one): key row 32 kw + n
-              // holds 64 bytes, lane group hh's 32 operand bytes at 32 hh
+              // holds 64 bytes, lane group hh's 32 operand bytes at 32 hh.  Non-temporal: the
+              // store is read back once, by another kernel, and would otherwise push the step
+              // tiles (re-read once per key tile) out of L2
               uint8_t* bbase = p.ds_store + (ds_block(ds_base, kappa, n_qt, st_qt) * p.Hq + st_h) * DS_STRIDE;
-              int4* dst = reinterpret_cast<int4*>(bbase + (32 * kw + n) * QT + 32 * hh);
-              dst[0] = d0;
-              dst[1] = d1;
+              v4i* dst = reinterpret_cast<v4i*>(bbase + (32 * kw + n) * QT + 32 * hh);
+              __builtin_nontemporal_store(v4i{d0.x, d0.y, d0.z, d0.w}, dst);
+              __builtin_nontemporal_store(v4i{d1.x, d1.y, d1.z, d1.w}, dst + 1);
               if (lane == 0) {
-                bbase[DS_BLOCK + kw] = (uint8_t)sm.xs_d[xb][0][kw];
-                bbase[DS_BLOCK + 4 + kw] = (uint8_t)sm.xs_d[xb][1][kw];
+                __builtin_nontemporal_store((uint8_t)sm.xs_d[xb][0][kw], bbase + DS_BLOCK + kw);
+                __builtin_nontemporal_store((uint8_t)sm.xs_d[xb][1][kw], bbase + DS_BLOCK + 4 + kw);
               }
             }
             if (++st_qt == n_qt) {
