@@ -313,7 +313,7 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
       // elements, so the matrix unit works while the vector unit does, and only one operand is
       // in flight at a time.
       auto fused = [&](int sp_st, int qp, v16f& ns, v16f& np, int ss, int qs, int q0, v16f& sa, v16f& pa,
-                       int* pp4, int* pd4, int& sp, int& sds, auto masked) {
+                       int* pp4, int* pd4, uint32_t& sp, uint32_t& sds, auto masked) {
         constexpr bool MASK = decltype(masked)::value;
         constexpr int NM = 2 * NC;     // matrix instructions of the products
         constexpr int EPM = 16 / NM;   // softmax elements per chunk
@@ -363,8 +363,8 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
           }
           __builtin_amdgcn_sched_barrier(0);
         }
-        sp = e8m0_roundup(wave_max_nonneg(pmax));
-        sds = e8m0_roundup(wave_max_nonneg(dmax));
+        sp = e8m0_byte_nonneg(wave_max_nonneg(pmax));  // E8M0 bytes of the block exponents
+        sds = e8m0_byte_nonneg(wave_max_nonneg(dmax));
 #pragma unroll
         for (int w4 = 0; w4 < 4; ++w4) {
           pp4[w4] = pack4_fp8_scaled(sa[4 * w4], sa[4 * w4 + 1], sa[4 * w4 + 2], sa[4 * w4 + 3], sp);
@@ -379,7 +379,8 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
       auto phase_body = [&](int ph, int h, int qt, auto masked) {
         const int q0 = QT * qt;
         const int x2 = ph & 1;
-        int pp[8], pd[8], sp[2], sds[2];
+        int pp[8], pd[8];
+        uint32_t sp[2], sds[2];  // E8M0 bytes
         // hand over query block qb's operands as soon as they exist, so the writes retire under
         // the next block's work instead of before the barrier (the consumer stores dShat to the
         // workspace)
@@ -408,8 +409,8 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
         if (lane == 0) {
 #pragma unroll
           for (int qb = 0; qb < 2; ++qb) {
-            sm.xs_p[x2][qb][kw] = sp[qb] + 127;
-            sm.xs_d[x2][qb][kw] = sds[qb] + 127;
+            sm.xs_p[x2][qb][kw] = sp[qb];
+            sm.xs_d[x2][qb][kw] = sds[qb];
           }
         }
       };

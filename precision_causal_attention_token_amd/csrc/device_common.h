@@ -159,6 +159,13 @@ __device__ __forceinline__ int e8m0_roundup(float amax) {
   const int s = (int)((b + 0x1FFFFFu) >> 23) - 135;
   return s < -127 ? -127 : s;
 }
+// The same exponent as its E8M0 byte s + 127 (255 for NaN / infinity), for amax >= +0 (sign bit
+// clear), in fewer steps: max((b + 2^21 - 1) >> 23, 8) - 8 is the clamped s + 127.
+__device__ __forceinline__ uint32_t e8m0_byte_nonneg(float amax) {
+  const uint32_t b = __float_as_uint(amax);
+  if (b >= 0x7F800000u) return 255;  // infinity or NaN
+  return max((b + 0x1FFFFFu) >> 23, 8u) - 8u;
+}
 // 2^-s as a float, for s in [-127, 127].
 __device__ __forceinline__ float exp2i_neg(int s) { return __uint_as_float((uint32_t)(127 - s) << 23); }
 __device__ __forceinline__ float exp2i(int s) { return __uint_as_float((uint32_t)(127 + s) << 23); }
@@ -179,9 +186,10 @@ __device__ __forceinline__ int pack4_fp8(float a0, float a1, float a2, float a3)
 // s + 127 (the field alone is used, so +0.0 stands for 2^-127); on gfx950 it gives exactly the
 // codes of the multiply-then-convert sequence, ties, subnormal and saturating results included
 // (checked on the hardware for every exponent).
+// The scale is given as its E8M0 byte s + 127.
 typedef short v2s __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ int pack4_fp8_scaled(float a0, float a1, float a2, float a3, int s) {
-  const float scale = __uint_as_float((uint32_t)(127 + s) << 23);
+__device__ __forceinline__ int pack4_fp8_scaled(float a0, float a1, float a2, float a3, uint32_t sbyte) {
+  const float scale = __uint_as_float(sbyte << 23);
   // the first conversion's upper half is overwritten by the second: any value will do there
   const v2s lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(__builtin_bit_cast(v2s, a0), a0, a1, scale, false);
   const v2s r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lo, a2, a3, scale, true);
