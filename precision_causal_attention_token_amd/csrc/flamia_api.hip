@@ -117,7 +117,7 @@ flamia_status flamia_quantize(const flamia_qtensor* tensors, int32_t n_tensors, 
     p.osh = o_stride_h;
     p.D = D;
   }
-  if ((int64_t)p.maxH * ((T + 255) / 256) > 0x7FFFFFFF) return FLAMIA_ERR_UNSUPPORTED;  // grid size
+  if ((int64_t)p.maxH * ((T + 127) / 128) > 0x7FFFFFFF) return FLAMIA_ERR_UNSUPPORTED;  // grid size
   hipError_t e = launch_quantize(p, d, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FLAMIA_OK : FLAMIA_ERR_HIP;
 }
