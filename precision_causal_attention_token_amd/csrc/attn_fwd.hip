@@ -198,16 +198,25 @@ __global__ __launch_bounds__(FWD_THREADS) void fwd_kernel(FwdParams p) {
       if (kappa > 0) scn = issue_full_tile<D>(p, sm, kb ^ 1, kb ^ 1, g, doc_start, kappa - 1, wave, voff0);
       if (wave_active && kappa <= kd) {
         const uint8_t* kt = sm.k[kb];
-        // ---- S^T for the 4 key blocks of the tile
+        // ---- S^T for the 4 key blocks of the tile.  K operand k (key block k / NC, d chunk
+        // k % NC) is read SAHEAD matrix instructions early into a ring of registers, so each
+        // instruction finds its operand loaded instead of waiting out an LDS round trip.
         v16f s[4];
+        {
+          constexpr int NS = 4 * NC, SAHEAD = 3;
+          auto read_k = [&](int k) { return lds_read_row32<D>(kt, 32 * (k / NC) + n, 64 * (k % NC) + 32 * hh); };
+          v8i kring[SAHEAD];
 #pragma unroll
-        for (int kb4 = 0; kb4 < 4; ++kb4) {
-          s[kb4] = v16f{};
-          const int ks = sm.sk[kb][32 * kb4 + n];
+          for (int k = 0; k < SAHEAD; ++k) kring[k] = read_k(k);
+          int ks[4];
 #pragma unroll
-          for (int cc = 0; cc < NC; ++cc) {
-            const v8i a = lds_read_row32<D>(kt, 32 * kb4 + n, 64 * cc + 32 * hh);
-            s[kb4] = mfma_scaled(a, qop[cc], s[kb4], ks, q_scale);
+          for (int kb4 = 0; kb4 < 4; ++kb4) ks[kb4] = sm.sk[kb][32 * kb4 + n];
+#pragma unroll
+          for (int k = 0; k < NS; ++k) {
+            const int kb4 = k / NC, cc = k % NC;
+            s[kb4] = mfma_scaled(kring[k % SAHEAD], qop[cc], cc ? s[kb4] : v16f{}, ks[kb4], q_scale);
+            if (k + SAHEAD < NS) kring[k % SAHEAD] = read_k(k + SAHEAD);
+            __builtin_amdgcn_sched_barrier(0);
           }
         }
         // ---- causal mask on the diagonal tile (keys after the query)
