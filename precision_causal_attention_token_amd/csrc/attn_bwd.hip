@@ -56,9 +56,9 @@ __device__ __forceinline__ int64_t ds_block(int64_t base, int kappa, int n_qt, i
   return base + (int64_t)kappa * n_qt - (int64_t)kappa * (kappa - 1) + (qt - 2 * kappa);
 }
 
-// Query offset (within a 64-query tile) held at byte position pos of a stored dShat row: the
-// row of key j holds, for lane group hh of the wave that owns j, the 32 bytes of its P-operand
-// register order (query 32 qb + 8 w4 + 4 hh + e in byte 4 (4 qb + w4) + e).
+// Query offset (within a 64-query tile) held at byte position pos of a dShat row as assembled in
+// LDS by the dQ pass: the row of key j holds, for lane group hh of the wave that owns j, the 32
+// bytes of its P-operand register order (query 32 qb + 8 w4 + 4 hh + e in byte 4 (4 qb + w4) + e).
 __device__ __forceinline__ int ds_pos_query(int pos) {
   const int s = pos >> 5, n = pos & 31;
   return 32 * (n >> 4) + 8 * ((n >> 2) & 3) + 4 * s + (n & 3);
@@ -463,14 +463,15 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
             const int4 d0 = sm.xd[xb][kw][0][lane], d1 = sm.xd[xb][kw][1][lane];
             if (store_ds) {
               // dShat codes and block exponents of step ph - 1 to the workspace, from the operand
-              // registers (the producer's wave stream is the longer one): key row 32 kw + n
-              // holds 64 bytes, lane group hh's 32 operand bytes at 32 hh.  Non-temporal: the
+              // registers (the producer's wave stream is the longer one).  Stored layout: the
+              // 2 KiB of key group kw hold query block qb's operand bytes at 1 KiB qb, lane by
+              // lane, so each store instruction writes 1 KiB contiguously.  Non-temporal: the
               // store is read back once, by another kernel, and would otherwise push the step
               // tiles (re-read once per key tile) out of L2
               uint8_t* bbase = p.ds_store + (ds_block(ds_base, kappa, n_qt, st_qt) * p.Hq + st_h) * DS_STRIDE;
-              v4i* dst = reinterpret_cast<v4i*>(bbase + (32 * kw + n) * QT + 32 * hh);
+              v4i* dst = reinterpret_cast<v4i*>(bbase + 2048 * kw + 16 * lane);
               __builtin_nontemporal_store(v4i{d0.x, d0.y, d0.z, d0.w}, dst);
-              __builtin_nontemporal_store(v4i{d1.x, d1.y, d1.z, d1.w}, dst + 1);
+              __builtin_nontemporal_store(v4i{d1.x, d1.y, d1.z, d1.w}, dst + 64);
               if (lane == 0) {
                 __builtin_nontemporal_store((uint8_t)sm.xs_d[xb][0][kw], bbase + DS_BLOCK + kw);
                 __builtin_nontemporal_store((uint8_t)sm.xs_d[xb][1][kw], bbase + DS_BLOCK + 4 + kw);
@@ -635,7 +636,9 @@ __device__ __forceinline__ void dq_store(const DqRegs<D>& r, DqSmem<D>& sm, int 
     const int row = chunk / CPR, col = (chunk % CPR) * 16;
     *reinterpret_cast<v4u*>(&sm.k[b][lds_off<D>(row, col)]) = r.k[i];
   }
-  const int off = lds_off<QT>(tid / (QT / 16), (tid % (QT / 16)) * 16);
+  // stored chunk tid (key group kw = tid / 128, query block qb, producer lane (n, hh)) is the
+  // 16-byte piece of key row 32 kw + n at byte 32 hh + 16 qb
+  const int off = lds_off<QT>(32 * (tid >> 7) + (tid & 31), 32 * ((tid >> 5) & 1) + 16 * ((tid >> 6) & 1));
 #pragma unroll
   for (int t = 0; t < 4; ++t) *reinterpret_cast<v4u*>(&sm.ds[b][t][off]) = r.s[t];
   if (tid < 4) *reinterpret_cast<uint2*>(&sm.dsc[b][tid][0]) = r.sc;
