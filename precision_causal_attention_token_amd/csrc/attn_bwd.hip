@@ -77,7 +77,7 @@ struct BwdSmem {
   uint8_t sv[KV_TILE];
   float lse[NBUF][QT];
   float dd[NBUF][QT];
-  int sq[NBUF][2], sdo[NBUF][2];
+  int2 sqdo[NBUF][2];           // block scale bytes {Q, dO} of the step's two query blocks
   int xs_p[2][2][4], xs_d[2][2][4];  // block exponent bytes of (query block, key group)
 };
 
@@ -212,8 +212,7 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
         int l = lane;
         asm volatile("" : "+v"(l));  // address formed here, not kept in a register all along
         const bool valid = QT * qt + 32 * l < L;
-        sm.sq[b][l] = valid ? rsq : 127;
-        sm.sdo[b][l] = valid ? rsdo : 127;
+        sm.sqdo[b][l] = make_int2(valid ? rsq : 127, valid ? rsdo : 127);
       }
     };
     // query head and 64-query tile of step st
@@ -300,9 +299,9 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
 #pragma unroll
         for (int cc = 0; cc < NC; ++cc) {
           const v8i aq = lds_read_row32<D>(sm.q[bb], 32 * qb + n, 64 * cc + 32 * hh);
-          sa = mfma_scaled(aq, kreg[cc], cc ? sa : v16f{}, sm.sq[bb][qb], k_scale);
+          sa = mfma_scaled(aq, kreg[cc], cc ? sa : v16f{}, sm.sqdo[bb][qb].x, k_scale);
           const v8i ad = lds_read_row32<D>(sm.dO[bb], 32 * qb + n, 64 * cc + 32 * hh);
-          pa = mfma_scaled(ad, vreg[cc], pa, sm.sdo[bb][qb], v_scale);
+          pa = mfma_scaled(ad, vreg[cc], pa, sm.sqdo[bb][qb].y, v_scale);
         }
       };
       // One block's softmax terms fused with another block's products.  Softmax of query block
@@ -327,7 +326,8 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
           const float4 d4 = *reinterpret_cast<const float4*>(&sm.dd[bp][32 * qp + 8 * j + 4 * hh]);
           np[4 * j] = d4.x; np[4 * j + 1] = d4.y; np[4 * j + 2] = d4.z; np[4 * j + 3] = d4.w;
         }
-        const int sq_s = sm.sq[bp][qp], sdo_s = sm.sdo[bp][qp];
+        const int2 sqdo = sm.sqdo[bp][qp];  // one 8-byte read
+        const int sq_s = sqdo.x, sdo_s = sqdo.y;
         // operand m: Q rows (m even) or dO rows (m odd) of column chunk m / 2; two in flight
         auto read_op = [&](int m) {
           return lds_read_row32<D>((m & 1) ? sm.dO[bp] : sm.q[bp], 32 * qp + n, 64 * (m >> 1) + 32 * hh);
@@ -483,7 +483,8 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
             }
             const v8i bp = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
             const v8i bd = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
-            const int sdo_h = sm.sdo[b][hh], sq_h = sm.sq[b][hh];
+            const int2 sqdo_h = sm.sqdo[b][hh];
+            const int sdo_h = sqdo_h.y, sq_h = sqdo_h.x;
             const int sp_h = sm.xs_p[xb][hh][kw], sds_h = sm.xs_d[xb][hh][kw];
             // Operand k (dO^T for even k, Q^T for odd k, d-block k / 2) is read AHEAD matrix
             // instructions early, so each one finds its operand in registers instead of waiting
