@@ -15,7 +15,7 @@ import torch
 
 from precision_causal_attention_token_amd import workloads
 from tests.gpu_common import check_cosine, gpu_call, oracle_call, say, stage_check, token_mask
-from tests.helpers import bits_to_f64, cosine, exact_attention
+from tests.helpers import bits_to_f64, cosine, dequant, exact_attention
 
 pytestmark = pytest.mark.gpu
 
@@ -72,14 +72,15 @@ def test_single_workload_against_exact():
     assert c >= 0.998
 
 
-@pytest.mark.parametrize("name", ["lognormal", "gqa", "long"])
-def test_full_size_sampled_documents(orc, name):
-    """Full-size workload on the GPU (the configuration the benchmark runs for `long`); the
-    oracle recomputes a sample of documents (the three shortest and one of median length,
-    each at most 4096 tokens) for two KV heads."""
+@pytest.mark.parametrize("name,causal_dq", [("lognormal", True), ("gqa", True), ("gqa", False), ("long", True)])
+def test_full_size_sampled_documents(orc, name, causal_dq):
+    """Full-size workload on the GPU; the oracle recomputes a sample of documents (the three
+    shortest and one of median length, each at most 4096 tokens) for two KV heads.  The GQA
+    workload runs with the causal dQ prescale off and on."""
     cu, shp, (q, k, v, do) = workloads.workload(name)
-    say("full-size %s T=%d Hq=%d Hkv=%d d=%d docs=%d" % (name, shp.T, shp.Hq, shp.Hkv, shp.d, len(cu) - 1))
-    g = gpu_call(q, k, v, do, cu, causal_dq=True)
+    say("full-size %s T=%d Hq=%d Hkv=%d d=%d docs=%d causal_dq=%s" % (name, shp.T, shp.Hq, shp.Hkv, shp.d,
+                                                                   len(cu) - 1, causal_dq))
+    g = gpu_call(q, k, v, do, cu, causal_dq=causal_dq)
     L = np.diff(cu)
     order = [i for i in np.argsort(L, kind="stable") if L[i] <= 4096]
     docs = sorted(set(order[:3] + [order[len(order) // 2]]))
@@ -87,5 +88,38 @@ def test_full_size_sampled_documents(orc, name):
     grp = shp.Hq // shp.Hkv
     qh = [h for h in range(shp.Hq) if h // grp in kv]
     say("  sampled docs %s (lengths %s), kv heads %s" % (docs, L[docs].tolist(), kv))
-    stage_check(orc, g, cu, True, docs=docs, kv_heads=kv, q_heads=qh)
-    _chain(orc, g, q, k, v, do, cu, True, docs=docs, kv_heads=kv, q_heads=qh)
+    stage_check(orc, g, cu, causal_dq, docs=docs, kv_heads=kv, q_heads=qh)
+    _chain(orc, g, q, k, v, do, cu, causal_dq, docs=docs, kv_heads=kv, q_heads=qh)
+
+
+def test_long_document_forward_bench_configuration(orc):
+    """The 65536-token workload in the benchmark's configuration (default dQ prescale), checked
+    on its shortest long document (16853 tokens: 132 key tiles of the multi-tile forward) for
+    the last head: the oracle's forward on the GPU's (bit-exact) codes gives O to the north-star
+    cosine bar and LSE to the FP8 accumulation scale of the scores.  (The oracle's backward and
+    tolerance allowances for a document this long take minutes on the host; the backward's
+    multi-tile paths are checked at full size on the 8192-token workload's documents.)"""
+    cu, shp, (q, k, v, do) = workloads.workload("long")
+    L = np.diff(np.asarray(cu, np.int64))
+    doc = int(np.argmin(np.where(L > 4096, L, np.iinfo(np.int64).max)))
+    h = shp.Hkv - 1
+    qh = list(range(h * (shp.Hq // shp.Hkv), (h + 1) * (shp.Hq // shp.Hkv)))
+    say("long document %d (%d tokens), kv head %d, default prescale" % (doc, L[doc], h))
+    g = gpu_call(q, k, v, do, cu, causal_dq=False)
+    o, lse, _ = orc.fwd(g["q"], g["sq"], g["k"], g["sk"], g["v"], g["sv"], cu, None, docs=[doc], kv_heads=[h])
+    m = token_mask(cu, shp.T, [doc])
+    check_cosine("O", g["o"][m][:, qh], o[m][:, qh])
+    # LSE (log2 units) moves by at most the largest score error, and the FP8 instruction's
+    # accumulation error is below 2^-10 of the sum of the absolute products (the accumulation
+    # reading the stage allowances use): per row, 2^-10 c max_j sum_c |q_ic k_jc|
+    a, b = int(cu[doc]), int(cu[doc + 1])
+    c = np.log2(np.e) / np.sqrt(shp.d)
+    kd = np.abs(dequant(g["k"][a:b, h:h + 1], g["sk"][h:h + 1, a:b])[:, 0])
+    for hq in qh:
+        qd = np.abs(dequant(g["q"][a:b, hq:hq + 1], g["sq"][hq:hq + 1, a:b])[:, 0])
+        # (+ a few FP32 ulps of the stored LSE on both sides)
+        bound = np.concatenate([2.0 ** -10 * c * (qd[r:r + 2048] @ kd.T).max(axis=1) for r in range(0, b - a, 2048)])
+        bound += 1e-5
+        lerr = np.abs(g["lse"][hq, a:b].astype(np.float64) - lse[hq, a:b])
+        say("  LSE head %d max|diff| %.3e  max diff/bound %.3f" % (hq, lerr.max(), (lerr / bound).max()))
+        assert np.all(lerr <= bound)
