@@ -186,11 +186,12 @@ class _Dbg(ctypes.Structure):
 
 
 def bwd(q, sq, k, sk, v, sv, do, sdo, lse, D, cu, softmax_scale=None, causal_dq=False, exact=0,
-        want64=False, debug=False, docs=None, kv_heads=None, want_flip=False):
+        want64=False, debug=False, docs=None, kv_heads=None, want_flip=False, tail_blocks=0):
     """Returns dict with dq, dk, dv (u16 BF16 bits), pi (i16 [Hq,T]) and optionally the
     double-precision values (dq64, dk64, dv64) and, for single-document calls, the block
     exponents/codes of the P and dS operands (p_scale, ds_scale [Hq,nb,nb]; p_code,
-    ds_code [Hq,L,L])."""
+    ds_code [Hq,L,L]).  tail_blocks > 0 restricts the work to the last tail_blocks 32-query
+    blocks of each document: only those rows' dQ and those keys' dK, dV are complete."""
     q, k, v, do = (_c(a, np.uint8) for a in (q, k, v, do))
     sq, sk, sv, sdo = (_c(a, np.uint8) for a in (sq, sk, sv, sdo))
     lse, D = _c(lse, np.float32), _c(D, np.float32)
@@ -221,7 +222,8 @@ def bwd(q, sq, k, sk, v, sv, do, sdo, lse, D, cu, softmax_scale=None, causal_dq=
                   _p(out["dq64"]) if want64 else None, _p(out["dk64"]) if want64 else None,
                   _p(out["dv64"]) if want64 else None, ctypes.byref(dbg) if dbg is not None else None,
                   _p(sd) if sd is not None else None, _p(sk_) if sk_ is not None else None,
-                  *((_p(out["dq_flip"]), _p(out["dk_flip"]), _p(out["dv_flip"])) if want_flip else (None, None, None)))
+                  *((_p(out["dq_flip"]), _p(out["dk_flip"]), _p(out["dv_flip"])) if want_flip else (None, None, None)),
+                  int(tail_blocks))
     return out
 
 

@@ -490,6 +490,11 @@ void orc_dq_exponents(const uint8_t* sk, const uint8_t* sv, const uint8_t* sdo, 
  * computed for the whole call.  d?_flip (optional; all three or none) receive per element
  * the largest change one Phat / dShat code moving to a neighbouring code would cause (the
  * tests' allowance for rounding decisions that two implementations may take differently).
+ * tail_blocks > 0 (a work restriction for sampling long documents, no change to what is
+ * computed): only the last tail_blocks 32-query blocks of each document are visited.  dQ of
+ * those rows is then complete (every key block up to theirs is visited), and so are dK and dV
+ * of the keys in those blocks (only queries at or after a key see it); the gradients of earlier
+ * keys hold partial sums and must not be read.
  * ---------------------------------------------------------------------------------- */
 typedef struct {
   uint8_t* p_scale;
@@ -505,7 +510,7 @@ void orc_bwd(const uint8_t* q, const uint8_t* sq, const uint8_t* k, const uint8_
              uint16_t* dq, uint16_t* dk, uint16_t* dv, int16_t* pi_out,
              double* dq64, double* dk64, double* dv64, const orc_bwd_debug* dbg,
              const uint8_t* sel_docs, const uint8_t* sel_kv, double* dq_flip, double* dk_flip,
-             double* dv_flip) {
+             double* dv_flip, int tail_blocks) {
   const int group = Hq / Hkv;
   const double c_scale = softmax_scale * 1.4426950408889634074;
   int16_t* pi = (int16_t*)malloc(sizeof(int16_t) * (size_t)Hq * T + 2);
@@ -548,7 +553,7 @@ void orc_bwd(const uint8_t* q, const uint8_t* sq, const uint8_t* k, const uint8_
       dv_fl = (double*)calloc((size_t)L * d, sizeof(double));
     }
     for (hq = g * group; hq < (g + 1) * group; ++hq) {
-      for (bq = 0; bq < nb; ++bq) {
+      for (bq = (tail_blocks > 0 && nb > tail_blocks) ? nb - tail_blocks : 0; bq < nb; ++bq) {
         int i0 = bq * BLK, i1 = i0 + BLK < L ? i0 + BLK : L;
         int kappa, kappa_last = (i1 - 1) / KV_TILE;
         for (z = 0; z < (size_t)BLK * d; ++z) acc16[z] = 0.0;

@@ -92,13 +92,15 @@ def test_full_size_sampled_documents(orc, name, causal_dq):
     _chain(orc, g, q, k, v, do, cu, causal_dq, docs=docs, kv_heads=kv, q_heads=qh)
 
 
-def test_long_document_forward_bench_configuration(orc):
+def test_long_document_bench_configuration(orc):
     """The 65536-token workload in the benchmark's configuration (default dQ prescale), checked
-    on its shortest long document (16853 tokens: 132 key tiles of the multi-tile forward) for
-    the last head: the oracle's forward on the GPU's (bit-exact) codes gives O to the north-star
-    cosine bar and LSE to the FP8 accumulation scale of the scores.  (The oracle's backward and
-    tolerance allowances for a document this long take minutes on the host; the backward's
-    multi-tile paths are checked at full size on the 8192-token workload's documents.)"""
+    on its shortest long document (16853 tokens, 132 key tiles) for the last head, against the
+    oracle on the GPU's (bit-exact) codes and the GPU's own LSE and D:
+      forward: O to the north-star cosine bar, LSE within the accumulation bound of the scores;
+      backward: dQ of the last 128 query rows (its FP16 sum runs over all 132 key-tile partials)
+      and dK, dV of the last 128 keys, to the cosine bar, with the oracle's backward restricted
+      to those rows (its full backward and tolerance allowances for a document this long take
+      minutes on the host)."""
     cu, shp, (q, k, v, do) = workloads.workload("long")
     L = np.diff(np.asarray(cu, np.int64))
     doc = int(np.argmin(np.where(L > 4096, L, np.iinfo(np.int64).max)))
@@ -123,3 +125,12 @@ def test_long_document_forward_bench_configuration(orc):
         lerr = np.abs(g["lse"][hq, a:b].astype(np.float64) - lse[hq, a:b])
         say("  LSE head %d max|diff| %.3e  max diff/bound %.3f" % (hq, lerr.max(), (lerr / bound).max()))
         assert np.all(lerr <= bound)
+    # backward tail
+    tail = 4  # 32-query blocks: the last 128 rows and keys
+    r = orc.bwd(g["q"], g["sq"], g["k"], g["sk"], g["v"], g["sv"], g["do"], g["sdo"], g["lse"], g["D"], cu,
+                causal_dq=False, docs=[doc], kv_heads=[h], tail_blocks=tail)
+    assert np.array_equal(g["pi"], r["pi"]), "pi"
+    t0 = a + 32 * ((b - a + 31) // 32 - tail)
+    check_cosine("dQ", g["dq"][t0:b][:, qh], r["dq"][t0:b][:, qh])
+    check_cosine("dK", g["dk"][t0:b][:, [h]], r["dk"][t0:b][:, [h]])
+    check_cosine("dV", g["dv"][t0:b][:, [h]], r["dv"][t0:b][:, [h]])

@@ -308,3 +308,33 @@ def test_leakage_probe(orc, b0):
         assert np.array_equal(c0[n][keep], c1[n][keep]), n
     assert np.array_equal(c0["pi"][:, keep], c1["pi"][:, keep])
     assert not np.array_equal(d0["pi"][:, keep], d1["pi"][:, keep])
+
+
+@pytest.mark.parametrize("causal_dq", [False, True])
+def test_backward_tail_restriction_is_exact(orc, causal_dq):
+    """The oracle's tail_blocks work restriction (used to sample long documents on the GPU)
+    visits only the last query blocks of each document: dQ of those rows and dK, dV of the
+    keys in those blocks equal the unrestricted backward bit for bit (ragged documents, a
+    partial last block, GQA, several key tiles)."""
+    T, Hq, Hkv, d = 900, 4, 2, 64
+    cu = np.array([0, 611, 640, 900], np.int32)
+    q, k, v, do = workloads.tensors(T, Hq, Hkv, d, seed=123)
+    Qz = _quantize_all(orc, q, k, v, cu)
+    o, lse, _ = orc.fwd(Qz["q"], Qz["sq"], Qz["k"], Qz["sk"], Qz["v"], Qz["sv"], cu)
+    dc, dsc, D = orc.quantize_do(bf16_bits(do), o, cu)
+    args = (Qz["q"], Qz["sq"], Qz["k"], Qz["sk"], Qz["v"], Qz["sv"], dc, dsc, lse, D, cu)
+    full = orc.bwd(*args, causal_dq=causal_dq, want64=True)
+    tail_blocks = 5
+    part = orc.bwd(*args, causal_dq=causal_dq, want64=True, tail_blocks=tail_blocks)
+    assert np.array_equal(full["pi"], part["pi"])
+    covered = 0
+    for a, b in zip(cu[:-1], cu[1:]):
+        L = b - a
+        nb = (L + 31) // 32
+        t0 = a + 32 * max(nb - tail_blocks, 0)   # first row / key of the complete tail
+        for name in ("dq", "dk", "dv", "dq64", "dk64", "dv64"):
+            assert np.array_equal(full[name][t0:b], part[name][t0:b]), (name, a, b)
+        covered += b - t0
+        if t0 > a:  # earlier keys hold partial sums: the restriction really skipped work
+            assert not np.array_equal(full["dk64"][a:t0], part["dk64"][a:t0])
+    assert covered < T
