@@ -134,10 +134,11 @@ def _sel(mask, n):
 
 
 def fwd(q, sq, k, sk, v, sv, cu, softmax_scale=None, p_shift=8, exact_p=False, want_o64=False,
-        docs=None, kv_heads=None, want_flip=False):
+        docs=None, kv_heads=None, want_flip=False, tail_rows=0):
     """Returns (O bits u16 [T,Hq,d], LSE f32 [Hq,T] in log2 units, O64 or None), plus the
     one-flip allowance of O if want_flip.  ``docs`` / ``kv_heads`` (index lists) restrict the
-    work to those documents / KV heads; other rows are zero (O) or NaN (LSE)."""
+    work to those documents / KV heads, and tail_rows > 0 to the last tail_rows rows of each
+    document; other rows are zero (O) or NaN (LSE)."""
     q, k, v = _c(q, np.uint8), _c(k, np.uint8), _c(v, np.uint8)
     sq, sk, sv = _c(sq, np.uint8), _c(sk, np.uint8), _c(sv, np.uint8)
     T, Hq, d = q.shape
@@ -153,7 +154,7 @@ def fwd(q, sq, k, sk, v, sv, cu, softmax_scale=None, p_shift=8, exact_p=False, w
     lib().orc_fwd(_p(q), _p(sq), _p(k), _p(sk), _p(v), _p(sv), T, Hq, Hkv, d, ctypes.c_double(softmax_scale),
                   _p(cu), len(cu) - 1, int(p_shift), int(bool(exact_p)), _p(o), _p(lse),
                   _p(o64) if o64 is not None else None, _p(sd) if sd is not None else None,
-                  _p(sk_) if sk_ is not None else None, _p(flip) if flip is not None else None)
+                  _p(sk_) if sk_ is not None else None, _p(flip) if flip is not None else None, int(tail_rows))
     if want_flip:
         return o, lse, o64, flip
     return o, lse, o64

@@ -306,12 +306,15 @@ int orc_worklist(const int32_t* cu, int n_docs, int kind, int n_workers, int32_t
  * tests sample large calls).  o_flip (optional) receives, per output element, the largest
  * change one Phat code moving to a neighbouring code would cause (a test allowance for
  * rounding decisions taken on values that differ by rounding between implementations).
+ * tail_rows > 0 (a work restriction for sampling long documents, no change to what is
+ * computed): only the last tail_rows rows of each document are computed; the outputs of the
+ * other rows are left as they were.
  * ---------------------------------------------------------------------------------- */
 void orc_fwd(const uint8_t* q, const uint8_t* sq, const uint8_t* k, const uint8_t* sk,
              const uint8_t* v, const uint8_t* sv, int T, int Hq, int Hkv, int d,
              double softmax_scale, const int32_t* cu, int n_docs, int p_shift, int exact_p,
              uint16_t* o, float* lse, double* o64, const uint8_t* sel_docs, const uint8_t* sel_kv,
-             double* o_flip) {
+             double* o_flip, int tail_rows) {
   const int group = Hq / Hkv;
   const double c_scale = softmax_scale * 1.4426950408889634074; /* log2(e) */
   double* Qd = deq_all(q, sq, T, Hq, d);
@@ -336,6 +339,7 @@ void orc_fwd(const uint8_t* q, const uint8_t* sq, const uint8_t* k, const uint8_
       continue;
     }
     if ((sel_docs && !sel_docs[doc]) || (sel_kv && !sel_kv[g])) continue;
+    if (tail_rows > 0 && row < cu[doc + 1] - tail_rows) continue;
     for (cc = 0; cc < d; ++cc) acc[cc] = flip[cc] = 0.0;
     {
       int start = cu[doc], r = row - start;

@@ -134,3 +134,34 @@ def test_long_document_bench_configuration(orc):
     check_cosine("dQ", g["dq"][t0:b][:, qh], r["dq"][t0:b][:, qh])
     check_cosine("dK", g["dk"][t0:b][:, [h]], r["dk"][t0:b][:, [h]])
     check_cosine("dV", g["dv"][t0:b][:, [h]], r["dv"][t0:b][:, [h]])
+
+
+def test_single_long_document_tail(orc):
+    """Extreme packing, one 131072-token document (1024 key tiles), default dQ prescale: the
+    last 128 rows of the last head against the oracle on the GPU's codes and the GPU's own LSE
+    and D (the oracle's forward and backward restricted to that tail): O, dQ (an FP16 sum over
+    1024 key-tile partials), dK, dV to the cosine bar, LSE within the accumulation bound."""
+    cu, shp, (q, k, v, do) = workloads.workload("onedoc")
+    h = shp.Hkv - 1
+    grp = shp.Hq // shp.Hkv
+    qh = list(range(h * grp, (h + 1) * grp))
+    T, tail = shp.T, 128
+    say("single %d-token document, kv head %d, last %d rows" % (T, h, tail))
+    g = gpu_call(q, k, v, do, cu, causal_dq=False)
+    o, lse, _ = orc.fwd(g["q"], g["sq"], g["k"], g["sk"], g["v"], g["sv"], cu, None, kv_heads=[h], tail_rows=tail)
+    t0 = T - tail
+    check_cosine("O", g["o"][t0:][:, qh], o[t0:][:, qh])
+    c = np.log2(np.e) / np.sqrt(shp.d)
+    kd = np.abs(dequant(g["k"][:, h:h + 1], g["sk"][h:h + 1])[:, 0])
+    for hq in qh:
+        qd = np.abs(dequant(g["q"][t0:, hq:hq + 1], g["sq"][hq:hq + 1, t0:])[:, 0])
+        bound = 2.0 ** -10 * c * (qd @ kd.T).max(axis=1) + 1e-5  # as in the 65536-token test
+        lerr = np.abs(g["lse"][hq, t0:].astype(np.float64) - lse[hq, t0:])
+        say("  LSE head %d max|diff| %.3e  max diff/bound %.3f" % (hq, lerr.max(), (lerr / bound).max()))
+        assert np.all(lerr <= bound)
+    r = orc.bwd(g["q"], g["sq"], g["k"], g["sk"], g["v"], g["sv"], g["do"], g["sdo"], g["lse"], g["D"], cu,
+                causal_dq=False, kv_heads=[h], tail_blocks=tail // 32)
+    assert np.array_equal(g["pi"], r["pi"]), "pi"
+    check_cosine("dQ", g["dq"][t0:][:, qh], r["dq"][t0:][:, qh])
+    check_cosine("dK", g["dk"][t0:][:, [h]], r["dk"][t0:][:, [h]])
+    check_cosine("dV", g["dv"][t0:][:, [h]], r["dv"][t0:][:, [h]])

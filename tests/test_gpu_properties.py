@@ -1,7 +1,7 @@
 """GPU properties that hold at any size: causal leakage exactly zero (jaehun.me review §4.5,
 read per the design notes: perturbation from a 32-token block boundary on, dO zeroed there,
 causal dQ scale), document isolation, run-to-run bit reproducibility, one-token documents
-(O = BF16(deq V) and dV = BF16(deq dO) bit-exactly)."""
+(O = BF16(0 + deq V) and dV = BF16(0 + deq dO) bit-exactly)."""
 import numpy as np
 import pytest
 import torch
@@ -71,15 +71,34 @@ def test_bitwise_reproducible():
         assert np.array_equal(r1[nm], r2[nm]), nm
 
 
+def _check_one_token_closed_form(g):
+    """O = BF16(0 + deq V) and dV = BF16(0 + deq dO), bit for bit.  The sums start from +0, so
+    an E4M3 negative zero (code 0x80) contributes -0 and leaves +0 (IEEE addition), as in the
+    oracle."""
+    vd = dequant(g["v"], g["sv"]) + 0.0
+    assert np.array_equal(g["o"], bf16_bits(torch.from_numpy(vd).to(torch.bfloat16)))
+    dod = dequant(g["do"], g["sdo"]) + 0.0
+    assert np.array_equal(g["dv"], bf16_bits(torch.from_numpy(dod).to(torch.bfloat16)))
+
+
 def test_one_token_documents(orc):
-    """O = BF16(deq V) and dV = BF16(deq dO) bit-exactly; dQ and dK are zero in exact
+    """O = BF16(0 + deq V) and dV = BF16(0 + deq dO) bit-exactly; dQ and dK are zero in exact
     arithmetic (D = dP) and stay within the stage bar (accumulation-level values)."""
     T, H, d = 512, 2, 128
     cu = workloads.cu_seqlens([1] * T)
     q, k, v, do = workloads.tensors(T, H, H, d, seed=720)
     g = gpu_call(q, k, v, do, cu)
-    vd = dequant(g["v"], g["sv"])
-    assert np.array_equal(g["o"], bf16_bits(torch.from_numpy(vd).to(torch.bfloat16)))
-    dod = dequant(g["do"], g["sdo"])
-    assert np.array_equal(g["dv"], bf16_bits(torch.from_numpy(dod).to(torch.bfloat16)))
+    _check_one_token_closed_form(g)
     stage_check(orc, g, cu, zero_in_exact=("dQ", "dK"))
+
+
+def test_one_token_documents_full_size(orc):
+    """Extreme packing at full size, 131072 one-token documents x 8 heads: O = BF16(0 + deq V)
+    and dV = BF16(0 + deq dO) bit-exactly for every token; the stage bar (dQ, dK zero in exact
+    arithmetic) on a sample of 4096 documents spread over the call."""
+    cu, shp, (q, k, v, do) = workloads.workload("tokens")
+    say("one-token documents: T=%d H=%d d=%d" % (shp.T, shp.Hq, shp.d))
+    g = gpu_call(q, k, v, do, cu)
+    _check_one_token_closed_form(g)
+    docs = list(range(0, len(cu) - 1, (len(cu) - 1) // 4096))
+    stage_check(orc, g, cu, docs=docs, zero_in_exact=("dQ", "dK"))

@@ -201,23 +201,24 @@ def test_query_zero_closed_form(orc):
 
 
 def test_one_token_documents(orc):
-    """A4: every document is a single token: O = BF16(deq V), dV = BF16(deq dO) bit-exactly,
-    LSE = t_ii.  dS = P (dP - D) vanishes up to the FP32 storage of LSE and D (P = 1 and
-    D = dP in exact arithmetic), so dQ and dK are at rounding level."""
+    """A4: every document is a single token: O = BF16(deq V), dV = BF16(deq dO) bit-exactly
+    (as sums from +0: an E4M3 negative zero gives +0), LSE = t_ii.  dS = P (dP - D) vanishes up
+    to the FP32 storage of LSE and D (P = 1 and D = dP in exact arithmetic), so dQ and dK are
+    at rounding level."""
     T, H, d = 96, 2, 128
     cu = workloads.cu_seqlens([1] * T)
     q, k, v, do = workloads.tensors(T, H, H, d, seed=91)
     Qz = _quantize_all(orc, q, k, v, cu)
     ss = 1.0 / np.sqrt(d)
     o, lse, _ = orc.fwd(Qz["q"], Qz["sq"], Qz["k"], Qz["sk"], Qz["v"], Qz["sv"], cu, ss)
-    vd = dequant(Qz["v"], Qz["sv"])
+    vd = dequant(Qz["v"], Qz["sv"]) + 0.0
     assert np.array_equal(o, bf16_bits(torch.from_numpy(vd).to(torch.bfloat16)))
     qd, kd = dequant(Qz["q"], Qz["sq"]), dequant(Qz["k"], Qz["sk"])
     t = (qd * kd).sum(-1).T * ss * LOG2E
     assert np.allclose(lse, t, rtol=1e-6, atol=1e-6)
     dc, dsc, D = orc.quantize_do(bf16_bits(do), o, cu)
     g = orc.bwd(Qz["q"], Qz["sq"], Qz["k"], Qz["sk"], Qz["v"], Qz["sv"], dc, dsc, lse, D, cu, ss)
-    assert np.array_equal(g["dv"], bf16_bits(torch.from_numpy(dequant(dc, dsc)).to(torch.bfloat16)))
+    assert np.array_equal(g["dv"], bf16_bits(torch.from_numpy(dequant(dc, dsc) + 0.0).to(torch.bfloat16)))
     dv_max = np.abs(bits_to_f64(g["dv"])).max()
     assert np.abs(bits_to_f64(g["dq"])).max() <= 1e-5 * dv_max
     assert np.abs(bits_to_f64(g["dk"])).max() <= 1e-5 * dv_max
@@ -338,3 +339,22 @@ def test_backward_tail_restriction_is_exact(orc, causal_dq):
         if t0 > a:  # earlier keys hold partial sums: the restriction really skipped work
             assert not np.array_equal(full["dk64"][a:t0], part["dk64"][a:t0])
     assert covered < T
+
+
+def test_forward_tail_restriction_is_exact(orc):
+    """The oracle's tail_rows work restriction (used to sample long documents on the GPU)
+    computes the last rows of each document exactly as the unrestricted forward does."""
+    T, Hq, Hkv, d = 900, 4, 2, 64
+    cu = np.array([0, 611, 640, 900], np.int32)
+    q, k, v, _ = workloads.tensors(T, Hq, Hkv, d, seed=124)
+    Qz = _quantize_all(orc, q, k, v, cu)
+    args = (Qz["q"], Qz["sq"], Qz["k"], Qz["sk"], Qz["v"], Qz["sv"], cu)
+    o, lse, o64 = orc.fwd(*args, want_o64=True)
+    tail = 70
+    o2, lse2, o642 = orc.fwd(*args, want_o64=True, tail_rows=tail)
+    for a, b in zip(cu[:-1], cu[1:]):
+        t0 = max(a, b - tail)
+        assert np.array_equal(o[t0:b], o2[t0:b]) and np.array_equal(o64[t0:b], o642[t0:b])
+        assert np.array_equal(lse[:, t0:b], lse2[:, t0:b])
+        if t0 > a:  # earlier rows were skipped
+            assert np.all(np.isnan(lse2[:, a:t0]))
