@@ -201,7 +201,7 @@ typedef struct {
 } flamia_bwd_args;
 
 /* Host.  Workspace bytes of a backward over these documents: a status word, pi [Hq, T],
- * n_docs + 1 block offsets and, per query head, 8208 bytes for each 64-query x 128-key block
+ * n_docs + 1 block offsets and, per query head, 8320 bytes for each 64-query x 128-key block
  * on or below the diagonal of every document longer than 128 tokens.  cu_seqlens_host is a
  * HOST copy of cu_seqlens (may be NULL only when n_docs == 0).  Returns 0 on bad arguments. */
 size_t flamia_bwd_workspace_bytes(const int32_t* cu_seqlens_host, int32_t n_docs, int32_t T, int32_t Hq);

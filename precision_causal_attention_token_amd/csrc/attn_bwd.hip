@@ -46,7 +46,9 @@ constexpr int BWD_THREADS = 64 * BWD_WAVES;
 constexpr int QT = 64;                 // queries per step / per stored dShat block
 constexpr int DS_BLOCK = KV_TILE * QT;  // code bytes of one stored dShat block
 constexpr int NBUF = 4;                 // step tile buffers of the key-stationary pass
-constexpr int DS_STRIDE = DS_BLOCK + 16;  // codes, then the 8 exponent bytes (and 8 spare)
+// codes, then the 8 exponent bytes in a 128-byte line of their own: every block starts on a cache
+// line, so its 1 KiB stores and loads cover whole lines
+constexpr int DS_STRIDE = DS_BLOCK + 128;
 constexpr int DQ_WAVES = 8;
 constexpr int DQ_THREADS = 64 * DQ_WAVES;
 
@@ -621,7 +623,8 @@ __device__ __forceinline__ void dq_load(DqRegs<D>& r, const BwdParams& p, int do
     return p.ds_store + ((int64_t)ds_block(base, kappa, n_qt, qt) * p.Hq + h) * DS_STRIDE;
   };
 #pragma unroll
-  for (int t = 0; t < 4; ++t) r.s[t] = reinterpret_cast<const v4u*>(block(t))[tid];
+  for (int t = 0; t < 4; ++t)  // read once: non-temporal, so L2 keeps the K tiles
+    r.s[t] = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(block(t)) + tid);
   r.sc = *reinterpret_cast<const uint2*>(block(tid & 3) + DS_BLOCK);  // used by threads 0..3
   r.skb = p.sk[(int64_t)g * p.T + doc_start + min(KV_TILE * kappa + (tid & (KV_TILE - 1)), L - 1)];
   r.nkeys = L - KV_TILE * kappa;  // the value is tested at the store, not here: no wait for it

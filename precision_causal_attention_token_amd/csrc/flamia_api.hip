@@ -33,9 +33,9 @@ int num_cus() {
 
 namespace {
 // Backward workspace: status word, pi [Hq, T], per-document block offsets, then the dShat store
-// (per (block, query head): 8 KiB of codes, 8 exponent bytes, 8 spare, so blocks stay 16-byte
-// aligned).
-constexpr size_t DS_BLOCK_BYTES = 128 * 64 + 16;
+// (per (block, query head): 8 KiB of codes, then 8 exponent bytes padded to a 128-byte line, so
+// every block starts on a cache line).
+constexpr size_t DS_BLOCK_BYTES = 128 * 64 + 128;
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 size_t bwd_fixed_bytes(int32_t T, int32_t Hq, int32_t n_docs) {
   return 256 + align256((size_t)T * Hq * 2) + align256(((size_t)n_docs + 1) * 8);

@@ -53,7 +53,7 @@ struct BwdParams {
   int16_t* pi;              // workspace: [Hq, T]
   int64_t* doc_base;        // workspace: first stored dShat block of each document, [n_docs + 1]
   uint8_t* ds_store;        // workspace: dShat blocks, per (block, query head) 8 KiB of codes and
-                            // 8 exponent bytes, 8208 bytes apart
+                            // 8 exponent bytes, 8320 bytes apart
   int64_t ds_capacity;      // (block, query head) pairs that fit
   int16_t* pi_out;          // optional copy of pi
   int32_t causal;
