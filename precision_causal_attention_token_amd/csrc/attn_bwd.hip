@@ -537,8 +537,8 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
                   const _Float16 a0 = (_Float16)(dq[4 * j + 0] * up), a1 = (_Float16)(dq[4 * j + 1] * up);
                   const _Float16 a2 = (_Float16)(dq[4 * j + 2] * up), a3 = (_Float16)(dq[4 * j + 3] * up);
                   uint2 w;
-                  w.x = pack_bf16((float)a0 * down, (float)a1 * down);
-                  w.y = pack_bf16((float)a2 * down, (float)a3 * down);
+                  w.x = pack_bf16_int((float)a0 * down, (float)a1 * down);
+                  w.y = pack_bf16_int((float)a2 * down, (float)a3 * down);
                   *reinterpret_cast<uint2*>(row + 32 * dblk + 8 * j + 4 * hh) = w;
                 }
               }

@@ -252,15 +252,27 @@ __device__ __forceinline__ float row16_sum(float x) {
   return x;
 }
 
-// bf16 helpers (round to nearest even; inputs here are finite).
+// bf16 helpers: conversions round to nearest even.
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+// Rounding in integer arithmetic: the same results as pack_bf16 below (NaN stays NaN, its
+// payload may differ).  Used where the packed instruction changes the register allocation of a
+// whole kernel (the key-tile pass's dQ for one-tile documents: with it the compiler spills 83
+// registers); the branches it compiles to cost little there.
 __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
   uint32_t u = __float_as_uint(f);
   if ((u & 0x7F800000u) == 0x7F800000u) return (u >> 16) | ((u & 0xFFFFu) ? 0x40u : 0u);
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
-__device__ __forceinline__ uint32_t pack_bf16(float a, float b) { return f32_to_bf16(a) | (f32_to_bf16(b) << 16); }
+__device__ __forceinline__ uint32_t pack_bf16_int(float a, float b) { return f32_to_bf16(a) | (f32_to_bf16(b) << 16); }
+// Two floats to BF16 (a in the low half) with one packed conversion instruction, rounding to
+// nearest even; NaN stays NaN.  Branch-free: epilogues that convert a whole tile run it once
+// per two values.
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{a, b}, b2));
+}
 
 // Document containing token t: the k with cu[k] <= t < cu[k+1], or -1.
 __device__ __forceinline__ int find_doc(const int32_t* __restrict__ cu, int n_docs, int t) {
