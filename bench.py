@@ -31,7 +31,7 @@ PEAK_HBM_GBPS = 8000.0       # MI355X HBM3E
 # scaled by 2.000 and WRITE by 1.000, the factors a 1 GiB copy gives).  Valid only for the
 # backward sources it was measured on (sha256 prefix over attn_bwd.hip, device_common.h,
 # kernels.h); any other build reports null.
-BWD_TRAFFIC = {"workload": "long", "src": "31a47f33619b393e", "read_bytes": 17.63e9, "write_bytes": 13.02e9}
+BWD_TRAFFIC = {"workload": "long", "src": "d350c2342591160a", "read_bytes": 19.73e9, "write_bytes": 13.02e9}
 
 
 def parse():

@@ -27,7 +27,9 @@
 // dQ = K^T dShat^T itself (dShat staged in LDS) and writes it, and nothing is stored.
 //
 // Query-stationary kernel (dQ of documents with two or more key tiles): a work unit is
-// (forward item = 256 queries of a document, query head); wave w owns 32 queries.  Over the key
+// (half of a forward item = 128 queries of a document, query head), two workgroups of four
+// waves per CU (twice the loads in flight of one larger workgroup); wave w owns 32 queries.
+// Over the key
 // tiles kappa = 0, 1, ... in ascending order it reads the stored dShat blocks and the K tile,
 // forms partial = K^T dShat^T (FP32) and accumulates acc16 = FP16(acc16 + FP16(2^pi partial))
 // in registers; at the end dQ = BF16(softmax_scale 2^-pi acc16).  The reduction order is fixed,
@@ -49,7 +51,8 @@ constexpr int NBUF = 4;                 // step tile buffers of the key-stationa
 // codes, then the 8 exponent bytes in a 128-byte line of their own: every block starts on a cache
 // line, so its 1 KiB stores and loads cover whole lines
 constexpr int DS_STRIDE = DS_BLOCK + 128;
-constexpr int DQ_WAVES = 8;
+constexpr int DQ_QT = 2;               // 64-query tiles per dQ workgroup (two workgroups per CU)
+constexpr int DQ_WAVES = 2 * DQ_QT;
 constexpr int DQ_THREADS = 64 * DQ_WAVES;
 
 // Stored dShat block of (key tile kappa, query tile qt >= 2 kappa) of a document with n_qt query
@@ -582,9 +585,9 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
 template <int D>
 struct DqSmem {
   uint8_t k[2][KV_TILE * D];
-  uint8_t ds[2][4][DS_BLOCK];
+  uint8_t ds[2][DQ_QT][DS_BLOCK];
   uint8_t sk[2][KV_TILE];
-  uint8_t dsc[2][4][8];
+  uint8_t dsc[2][DQ_QT][8];
 };
 
 // The next key tile's K rows, dShat blocks and exponents, in registers between the global loads
@@ -593,9 +596,10 @@ typedef unsigned int v4u __attribute__((ext_vector_type(4)));  // plain vector: 
 template <int D>
 struct DqRegs {
   static constexpr int KCH = KV_TILE * D / 16 / DQ_THREADS;  // K chunks per thread
-  static constexpr int SCH = 4 * DS_BLOCK / 16 / DQ_THREADS;  // dShat chunks per thread
-  v4u k[KCH], s[SCH];
-  uint2 sc;       // threads 0..3: exponents of query tile `tid`
+  static constexpr int CPB = DS_BLOCK / 16 / DQ_THREADS;    // chunks of one dShat block per thread
+  static_assert(CPB * DQ_THREADS * 16 == DS_BLOCK && (DQ_QT & (DQ_QT - 1)) == 0, "dQ tiling");
+  v4u k[KCH], s[DQ_QT * CPB];
+  uint2 sc;       // threads 0..DQ_QT-1: exponents of query tile `tid`
   uint32_t skb;   // threads 0..127: K scale byte of key `tid`
   int nkeys;      // keys of the tile inside the document (scale 127 beyond)
 };
@@ -607,7 +611,6 @@ struct DqRegs {
 template <int D>
 __device__ __forceinline__ void dq_load(DqRegs<D>& r, const BwdParams& p, int doc_start, int L, int n_qt,
                                         int64_t base, int qt0, int g, int h, int kappa) {
-  static_assert(DqRegs<D>::SCH == 4, "one 16-byte chunk of each of the four blocks per thread");
   const int tid = threadIdx.x;
   constexpr int CPR = D / 16;
 #pragma unroll
@@ -623,9 +626,11 @@ __device__ __forceinline__ void dq_load(DqRegs<D>& r, const BwdParams& p, int do
     return p.ds_store + ((int64_t)ds_block(base, kappa, n_qt, qt) * p.Hq + h) * DS_STRIDE;
   };
 #pragma unroll
-  for (int t = 0; t < 4; ++t)  // read once: non-temporal, so L2 keeps the K tiles
-    r.s[t] = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(block(t)) + tid);
-  r.sc = *reinterpret_cast<const uint2*>(block(tid & 3) + DS_BLOCK);  // used by threads 0..3
+  for (int t = 0; t < DQ_QT; ++t)  // read once: non-temporal, so L2 keeps the K tiles
+#pragma unroll
+    for (int j = 0; j < DqRegs<D>::CPB; ++j)
+      r.s[t * DqRegs<D>::CPB + j] = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(block(t)) + tid + j * DQ_THREADS);
+  r.sc = *reinterpret_cast<const uint2*>(block(tid & (DQ_QT - 1)) + DS_BLOCK);  // used by threads 0..DQ_QT-1
   r.skb = p.sk[(int64_t)g * p.T + doc_start + min(KV_TILE * kappa + (tid & (KV_TILE - 1)), L - 1)];
   r.nkeys = L - KV_TILE * kappa;  // the value is tested at the store, not here: no wait for it
 }
@@ -642,15 +647,19 @@ __device__ __forceinline__ void dq_store(const DqRegs<D>& r, DqSmem<D>& sm, int 
   }
   // stored chunk tid (key group kw = tid / 128, query block qb, producer lane (n, hh)) is the
   // 16-byte piece of key row 32 kw + n at byte 32 hh + 16 qb
-  const int off = lds_off<QT>(32 * (tid >> 7) + (tid & 31), 32 * ((tid >> 5) & 1) + 16 * ((tid >> 6) & 1));
 #pragma unroll
-  for (int t = 0; t < 4; ++t) *reinterpret_cast<v4u*>(&sm.ds[b][t][off]) = r.s[t];
-  if (tid < 4) *reinterpret_cast<uint2*>(&sm.dsc[b][tid][0]) = r.sc;
+  for (int j = 0; j < DqRegs<D>::CPB; ++j) {
+    const int c = tid + j * DQ_THREADS;
+    const int off = lds_off<QT>(32 * (c >> 7) + (c & 31), 32 * ((c >> 5) & 1) + 16 * ((c >> 6) & 1));
+#pragma unroll
+    for (int t = 0; t < DQ_QT; ++t) *reinterpret_cast<v4u*>(&sm.ds[b][t][off]) = r.s[t * DqRegs<D>::CPB + j];
+  }
+  if (tid < DQ_QT) *reinterpret_cast<uint2*>(&sm.dsc[b][tid][0]) = r.sc;
   if (tid < KV_TILE) sm.sk[b][tid] = tid < r.nkeys ? (uint8_t)r.skb : (uint8_t)127;
 }
 
 template <int D>
-__global__ __launch_bounds__(DQ_THREADS) void dq_kernel(BwdParams p) {
+__global__ __launch_bounds__(DQ_THREADS, 2) void dq_kernel(BwdParams p) {  // two workgroups per CU
   constexpr int NDB = D / 32;
   typedef _Float16 h2 __attribute__((ext_vector_type(2)));
   __shared__ DqSmem<D> sm;
@@ -661,28 +670,30 @@ __global__ __launch_bounds__(DQ_THREADS) void dq_kernel(BwdParams p) {
   const int n = lane & 31, hh = lane >> 5;
   const int n_items = p.fwd_list[0];
   const int4* items = reinterpret_cast<const int4*>(p.fwd_list + 4);
-  const int n_units = n_items * p.Hq;
+  constexpr int PARTS = ITEM_Q / (QT * DQ_QT);  // workgroup units per work item and head
+  const int n_units = n_items * PARTS * p.Hq;
   const int G = gridDim.x, wg = blockIdx.x;
   const int grp = p.Hq / p.Hkv;
-  const int t4 = wave >> 1, s = wave & 1;     // query tile of the item, byte-position half
+  const int t4 = wave >> 1, s = wave & 1;     // query tile of the unit, byte-position half
   const int qrow = ds_pos_query(32 * s + n);  // query offset in the tile held by this lane
   const int qb_l = n >> 4;                    // its 32-query block
 
   for (int round = 0;; ++round) {
     const int u = round * G + ((round & 1) ? (G - 1 - wg) : wg);
     if (u >= n_units) break;
-    const int4 it = items[u / p.Hq];
+    const int4 it = items[u / (PARTS * p.Hq)];
     if (it.z < 2) break;  // single key tile from here on (the list is sorted by cost)
-    const int h = u % p.Hq, g = h / grp;
+    const int h = u % p.Hq, g = h / grp, part = (u / p.Hq) % PARTS;
     const int doc = it.x, item = it.y;
     const int doc_start = p.cu[doc];
     const int L = p.cu[doc + 1] - doc_start;
     const int n_qt = (L + QT - 1) / QT;
     const int64_t base = p.doc_base[doc];
-    const int qt0 = (ITEM_Q / QT) * item;
+    const int qt0 = (ITEM_Q / QT) * item + DQ_QT * part;
+    if (qt0 >= n_qt) continue;  // the item ends before this part (uniform over the workgroup)
     const int qt = qt0 + t4;
     const bool active = qt < n_qt;
-    const int last_qt = min(qt0 + ITEM_Q / QT, n_qt) - 1;
+    const int last_qt = min(qt0 + DQ_QT, n_qt) - 1;
     const int kappa_hi = last_qt / 2;
     const int q_rel = QT * qt + qrow;
     const bool row_valid = q_rel < L;
@@ -969,11 +980,11 @@ hipError_t launch_bwd(const BwdParams& p, int d, int grid, hipStream_t s) {
   if (d == 128) {
     hipLaunchKernelGGL(bwd_prologue<128>, dim3(p.Hq + 1), dim3(PRO_THREADS), 0, s, p);
     hipLaunchKernelGGL(bwd_kernel<128>, dim3(grid), dim3(BWD_THREADS), 0, s, p);
-    hipLaunchKernelGGL(dq_kernel<128>, dim3(grid), dim3(DQ_THREADS), 0, s, p);
+    hipLaunchKernelGGL(dq_kernel<128>, dim3(2 * grid), dim3(DQ_THREADS), 0, s, p);
   } else {
     hipLaunchKernelGGL(bwd_prologue<64>, dim3(p.Hq + 1), dim3(PRO_THREADS), 0, s, p);
     hipLaunchKernelGGL(bwd_kernel<64>, dim3(grid), dim3(BWD_THREADS), 0, s, p);
-    hipLaunchKernelGGL(dq_kernel<64>, dim3(grid), dim3(DQ_THREADS), 0, s, p);
+    hipLaunchKernelGGL(dq_kernel<64>, dim3(2 * grid), dim3(DQ_THREADS), 0, s, p);
   }
   return hipGetLastError();
 }
