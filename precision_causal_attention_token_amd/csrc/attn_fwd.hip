@@ -24,8 +24,11 @@ namespace flamia {
 
 namespace {
 
-constexpr int FWD_WAVES = 8;
-constexpr int FWD_THREADS = 64 * FWD_WAVES;
+// Workgroup shapes: W = 8 waves (a 256-query unit, one workgroup per CU) for long documents, or
+// W = 4 (a 128-query unit, two workgroups per CU, whose barriers and loads interleave) where
+// documents are short and a unit covers few key tiles.  Both compute the same values.
+template <int W>
+constexpr int fwd_threads() { return 64 * W; }
 
 template <int D>
 struct FwdSmem {
@@ -42,13 +45,13 @@ struct FwdSmem {
 // last row (their scores are masked, their probabilities are zero, and the values are finite).
 // The scale bytes go through a register, returned here and stored by store_scales: thread
 // t < 128 holds the K scale of key t, 128 <= t < 256 the V scale of key t - 128.
-template <int D>
+template <int D, int W>
 __device__ __forceinline__ uint32_t issue_tile(const FwdParams& p, FwdSmem<D>& sm, int kb, int vb, int g,
                                                int doc_start, int L, int kappa, int wave, int lane) {
   constexpr int CPR = D / 16;                        // 16-byte chunks per row
   constexpr int BLOCKS = KV_TILE * D / 1024;         // 1 KiB wave blocks per tensor
-  constexpr int PER_WAVE = 2 * BLOCKS / FWD_WAVES;   // K and V blocks per wave
-  static_assert(PER_WAVE * FWD_WAVES == 2 * BLOCKS, "blocks split evenly over the waves");
+  constexpr int PER_WAVE = 2 * BLOCKS / W;           // K and V blocks per wave
+  static_assert(PER_WAVE * W == 2 * BLOCKS, "blocks split evenly over the waves");
 #pragma unroll
   for (int i = 0; i < PER_WAVE; ++i) {
     const int wb = wave * PER_WAVE + i;              // K blocks, then V blocks
@@ -82,12 +85,12 @@ __device__ __forceinline__ uint32_t issue_tile(const FwdParams& p, FwdSmem<D>& s
 // wave the blocks are consecutive and of one tensor; block i sits 64 i / CPR rows below block 0,
 // and since the swizzle is a bit permutation of row bits below that step, its chunk differs
 // from block 0's by the swizzle of that row step alone, whatever the lane.
-template <int D>
+template <int D, int W>
 __device__ __forceinline__ uint32_t issue_full_tile(const FwdParams& p, FwdSmem<D>& sm, int kb, int vb, int g,
                                                     int doc_start, int kappa, int wave, uint32_t voff0) {
   constexpr int CPR = D / 16;
   constexpr int BLOCKS = KV_TILE * D / 1024;
-  constexpr int PER_WAVE = 2 * BLOCKS / FWD_WAVES;
+  constexpr int PER_WAVE = 2 * BLOCKS / W;
   static_assert(BLOCKS % PER_WAVE == 0, "no wave's blocks span both tensors");
   static_assert(16 * CPR <= D && (D & (D - 1)) == 0, "chunk offsets stay below the row stride");
   const bool is_v = wave * PER_WAVE >= BLOCKS;
@@ -126,8 +129,9 @@ __device__ __forceinline__ void store_scales(FwdSmem<D>& sm, int kb, int vb, uin
   else if (tid < 2 * KV_TILE) sm.sv[vb][tid - KV_TILE] = (uint8_t)sc;
 }
 
-template <int D>
-__global__ __launch_bounds__(FWD_THREADS) void fwd_kernel(FwdParams p) {
+template <int D, int W>
+__global__ __launch_bounds__(fwd_threads<W>(), 8 / W) void fwd_kernel(FwdParams p) {
+  constexpr int FWD_THREADS = fwd_threads<W>();
   constexpr int NC = D / 64;   // 64-wide d chunks of the score contraction
   constexpr int NDB = D / 32;  // 32-wide d blocks of the output
   __shared__ FwdSmem<D> sm;
@@ -137,7 +141,9 @@ __global__ __launch_bounds__(FWD_THREADS) void fwd_kernel(FwdParams p) {
   const int n = lane & 31, hh = lane >> 5;
   const int n_items = p.list[0];
   const int4* items = reinterpret_cast<const int4*>(p.list + 4);
-  const int n_units = n_items * p.Hq;
+  constexpr int QU = 32 * W;                 // queries per workgroup unit
+  constexpr int PARTS = ITEM_Q / QU;         // units per work item and head
+  const int n_units = n_items * PARTS * p.Hq;
   const int G = gridDim.x, wg = blockIdx.x;
   const int grp = p.Hq / p.Hkv;
   const float c = p.c;
@@ -146,17 +152,19 @@ __global__ __launch_bounds__(FWD_THREADS) void fwd_kernel(FwdParams p) {
   for (int round = 0;; ++round) {
     const int u = round * G + ((round & 1) ? (G - 1 - wg) : wg);
     if (u >= n_units) break;
-    const int4 it = items[u / p.Hq];
-    const int h = u % p.Hq, g = h / grp;
+    const int4 it = items[u / (PARTS * p.Hq)];
+    const int h = u % p.Hq, g = h / grp, part = (u / p.Hq) % PARTS;
     const int doc = it.x, b = it.y;
     const int doc_start = p.cu[doc];
     const int L = p.cu[doc + 1] - doc_start;
-    const int q_wave = ITEM_Q * b + 32 * wave;         // first query (document offset) of this wave
+    const int q0 = ITEM_Q * b + QU * part;             // first query (document offset) of the unit
+    if (q0 >= L) continue;                              // the item ends before this part (uniform)
+    const int q_wave = q0 + 32 * wave;                  // first query of this wave
     const bool wave_active = q_wave < L;
     const int q_rel = q_wave + n;
     const bool row_valid = q_rel < L;
     const int kd = q_wave / KV_TILE;                    // this wave's diagonal tile
-    const int last_row = min(ITEM_Q * b + ITEM_Q, L) - 1;
+    const int last_row = min(q0 + QU, L) - 1;
     const int kappa_hi = last_row / KV_TILE;
 
     // Q operand (B of S^T): lane (n, hh) holds d = 64c + 32hh .. +31 of query n.
@@ -187,7 +195,7 @@ __global__ __launch_bounds__(FWD_THREADS) void fwd_kernel(FwdParams p) {
 
     lds_barrier();  // the previous unit's readers are done with every buffer
     {
-      const uint32_t sc = issue_tile<D>(p, sm, 0, 0, g, doc_start, L, kappa_hi, wave, lane);
+      const uint32_t sc = issue_tile<D, W>(p, sm, 0, 0, g, doc_start, L, kappa_hi, wave, lane);
       __builtin_amdgcn_s_waitcnt(0);  // this wave's direct loads have landed
       store_scales<D>(sm, 0, 0, sc);
     }
@@ -195,7 +203,7 @@ __global__ __launch_bounds__(FWD_THREADS) void fwd_kernel(FwdParams p) {
     for (int kappa = kappa_hi, it = 0; kappa >= 0; --kappa, ++it) {
       const int kb = it & 1;
       uint32_t scn = 127;
-      if (kappa > 0) scn = issue_full_tile<D>(p, sm, kb ^ 1, kb ^ 1, g, doc_start, kappa - 1, wave, voff0);
+      if (kappa > 0) scn = issue_full_tile<D, W>(p, sm, kb ^ 1, kb ^ 1, g, doc_start, kappa - 1, wave, voff0);
       if (wave_active && kappa <= kd) {
         const uint8_t* kt = sm.k[kb];
         // ---- S^T for the 4 key blocks of the tile.  K operand k (key block k / NC, d chunk
@@ -362,8 +370,15 @@ __global__ __launch_bounds__(FWD_THREADS) void fwd_kernel(FwdParams p) {
 }  // namespace
 
 hipError_t launch_fwd(const FwdParams& p, int d, int grid, hipStream_t s) {
-  if (d == 128) hipLaunchKernelGGL(fwd_kernel<128>, dim3(grid), dim3(FWD_THREADS), 0, s, p);
-  else hipLaunchKernelGGL(fwd_kernel<64>, dim3(grid), dim3(FWD_THREADS), 0, s, p);
+  // documents of fewer than 4096 tokens on average: 128-query units, two workgroups per CU
+  const bool short_docs = (int64_t)p.n_docs * 4096 > (int64_t)p.T;
+  if (short_docs) {
+    if (d == 128) hipLaunchKernelGGL((fwd_kernel<128, 4>), dim3(2 * grid), dim3(fwd_threads<4>()), 0, s, p);
+    else hipLaunchKernelGGL((fwd_kernel<64, 4>), dim3(2 * grid), dim3(fwd_threads<4>()), 0, s, p);
+  } else {
+    if (d == 128) hipLaunchKernelGGL((fwd_kernel<128, 8>), dim3(grid), dim3(fwd_threads<8>()), 0, s, p);
+    else hipLaunchKernelGGL((fwd_kernel<64, 8>), dim3(grid), dim3(fwd_threads<8>()), 0, s, p);
+  }
   return hipGetLastError();
 }
 

@@ -9,18 +9,20 @@ import pytest
 from precision_causal_attention_token_amd import build
 from tests import isa_waits
 
-KERNELS = [("attn_fwd.hip", r"_ZN6flamia12_GLOBAL__N_110fwd_kernelI\w+"),
-           ("attn_bwd.hip", r"_ZN6flamia12_GLOBAL__N_110bwd_kernelI\w+"),
-           ("attn_bwd.hip", r"_ZN6flamia12_GLOBAL__N_19dq_kernelI\w+")]
+# (source, symbol pattern, instantiations: head dims 64 and 128, times the forward's two
+# workgroup shapes)
+KERNELS = [("attn_fwd.hip", r"_ZN6flamia12_GLOBAL__N_110fwd_kernelI\w+", 4),
+           ("attn_bwd.hip", r"_ZN6flamia12_GLOBAL__N_110bwd_kernelI\w+", 2),
+           ("attn_bwd.hip", r"_ZN6flamia12_GLOBAL__N_19dq_kernelI\w+", 2)]
 
 
 @pytest.mark.skipif(not os.path.exists(build.HIPCC), reason="hipcc not installed")
-@pytest.mark.parametrize("src,pattern", KERNELS)
-def test_matrix_results_read_after_full_latency(tmp_path, src, pattern):
+@pytest.mark.parametrize("src,pattern,count", KERNELS)
+def test_matrix_results_read_after_full_latency(tmp_path, src, pattern, count):
     asm = isa_waits.compile_to_asm(os.path.join(build.CSRC, src), str(tmp_path / (src + ".s")), build.HIPCC,
                                    build.FLAGS)
     syms = isa_waits.kernel_symbols(asm, pattern)
-    assert len(syms) == 2, syms  # head dims 64 and 128
+    assert len(syms) == count, syms
     for sym in syms:
         close, n = isa_waits.close_reads(asm, sym)
         assert n > 0, sym
@@ -47,8 +49,8 @@ def test_checker_flags_a_short_distance():
 
 
 @pytest.mark.skipif(not os.path.exists(build.HIPCC), reason="hipcc not installed")
-@pytest.mark.parametrize("src,pattern", KERNELS)
-def test_m0_only_in_direct_load_sequences(tmp_path, src, pattern):
+@pytest.mark.parametrize("src,pattern,count", KERNELS)
+def test_m0_only_in_direct_load_sequences(tmp_path, src, pattern, count):
     """M0 is written only by the direct-load sequence, which always writes it right before its
     load: no compiler-placed M0 value can be live across it."""
     asm = isa_waits.compile_to_asm(os.path.join(build.CSRC, src), str(tmp_path / (src + ".s")), build.HIPCC,
