@@ -125,6 +125,37 @@ def worklist(cu, kind, n_workers):
     return out[:n].copy()
 
 
+class _Window(ctypes.Structure):
+    _fields_ = [("row_lo", ctypes.c_int), ("row_hi", ctypes.c_int), ("key_lo", ctypes.c_int),
+                ("key_hi", ctypes.c_int), ("head_lo", ctypes.c_int), ("head_hi", ctypes.c_int),
+                ("fwd_s", ctypes.c_void_p), ("fwd_m", ctypes.c_void_p), ("fwd_p", ctypes.c_void_p),
+                ("bwd_dp", ctypes.c_void_p), ("bwd_p", ctypes.c_void_p), ("bwd_ps", ctypes.c_void_p),
+                ("bwd_ds", ctypes.c_void_p), ("bwd_dss", ctypes.c_void_p)]
+
+
+def window_shape(win):
+    """(heads, rows, keys) of a window dict {row_lo, row_hi, key_lo, key_hi, head_lo, head_hi}."""
+    return (win["head_hi"] - win["head_lo"], win["row_hi"] - win["row_lo"], win["key_hi"] - win["key_lo"])
+
+
+def _window(win, arrays):
+    w = _Window(win["row_lo"], win["row_hi"], win["key_lo"], win["key_hi"], win["head_lo"], win["head_hi"])
+    for name, a in arrays.items():
+        setattr(w, name, a.ctypes.data if a is not None else None)
+    return w
+
+
+def _dump_arrays(win, names):
+    shp = window_shape(win)
+    out = {}
+    for n in names:
+        if n in ("fwd_s", "fwd_m", "bwd_dp"):
+            out[n] = np.full(shp, np.nan, np.float64)
+        else:
+            out[n] = np.full(shp, 0xFF, np.uint8)
+    return out
+
+
 def _sel(mask, n):
     if mask is None:
         return None
@@ -134,11 +165,13 @@ def _sel(mask, n):
 
 
 def fwd(q, sq, k, sk, v, sv, cu, softmax_scale=None, p_shift=8, exact_p=False, want_o64=False,
-        docs=None, kv_heads=None, want_flip=False, tail_rows=0):
+        docs=None, kv_heads=None, want_flip=False, tail_rows=0, window=None):
     """Returns (O bits u16 [T,Hq,d], LSE f32 [Hq,T] in log2 units, O64 or None), plus the
-    one-flip allowance of O if want_flip.  ``docs`` / ``kv_heads`` (index lists) restrict the
-    work to those documents / KV heads, and tail_rows > 0 to the last tail_rows rows of each
-    document; other rows are zero (O) or NaN (LSE)."""
+    one-flip allowance of O if want_flip, plus (with ``window``, a dict of row/key/head bounds)
+    a dict of the per-pair dumps fwd_s (score accumulator), fwd_m (running maximum), fwd_p
+    (E4M3 codes), [heads][rows][keys], NaN / 0xFF where not visited.  ``docs`` / ``kv_heads``
+    (index lists) restrict the work to those documents / KV heads, and tail_rows > 0 to the last
+    tail_rows rows of each document; other rows are zero (O) or NaN (LSE)."""
     q, k, v = _c(q, np.uint8), _c(k, np.uint8), _c(v, np.uint8)
     sq, sk, sv = _c(sq, np.uint8), _c(sk, np.uint8), _c(sv, np.uint8)
     T, Hq, d = q.shape
@@ -151,13 +184,15 @@ def fwd(q, sq, k, sk, v, sv, cu, softmax_scale=None, p_shift=8, exact_p=False, w
     o64 = np.zeros((T, Hq, d), np.float64) if want_o64 else None
     sd, sk_ = _sel(docs, len(cu) - 1), _sel(kv_heads, Hkv)
     flip = np.zeros((T, Hq, d), np.float64) if want_flip else None
+    dumps = _dump_arrays(window, ("fwd_s", "fwd_m", "fwd_p")) if window is not None else None
+    w = _window(window, dumps) if window is not None else None
     lib().orc_fwd(_p(q), _p(sq), _p(k), _p(sk), _p(v), _p(sv), T, Hq, Hkv, d, ctypes.c_double(softmax_scale),
                   _p(cu), len(cu) - 1, int(p_shift), int(bool(exact_p)), _p(o), _p(lse),
                   _p(o64) if o64 is not None else None, _p(sd) if sd is not None else None,
-                  _p(sk_) if sk_ is not None else None, _p(flip) if flip is not None else None, int(tail_rows))
-    if want_flip:
-        return o, lse, o64, flip
-    return o, lse, o64
+                  _p(sk_) if sk_ is not None else None, _p(flip) if flip is not None else None, int(tail_rows),
+                  ctypes.byref(w) if w is not None else None)
+    res = (o, lse, o64) + ((flip,) if want_flip else ()) + ((dumps,) if window is not None else ())
+    return res
 
 
 def quantize_do(do_bits, o_bits, cu):
@@ -187,12 +222,14 @@ class _Dbg(ctypes.Structure):
 
 
 def bwd(q, sq, k, sk, v, sv, do, sdo, lse, D, cu, softmax_scale=None, causal_dq=False, exact=0,
-        want64=False, debug=False, docs=None, kv_heads=None, want_flip=False, tail_blocks=0):
+        want64=False, debug=False, docs=None, kv_heads=None, want_flip=False, tail_blocks=0, window=None):
     """Returns dict with dq, dk, dv (u16 BF16 bits), pi (i16 [Hq,T]) and optionally the
     double-precision values (dq64, dk64, dv64) and, for single-document calls, the block
     exponents/codes of the P and dS operands (p_scale, ds_scale [Hq,nb,nb]; p_code,
     ds_code [Hq,L,L]).  tail_blocks > 0 restricts the work to the last tail_blocks 32-query
-    blocks of each document: only those rows' dQ and those keys' dK, dV are complete."""
+    blocks of each document: only those rows' dQ and those keys' dK, dV are complete.  With
+    ``window`` (row/key/head bounds), out["dumps"] holds the per-pair bwd_dp (D - dP), bwd_p,
+    bwd_ps (Phat code, block exponent byte), bwd_ds, bwd_dss (dShat), [heads][rows][keys]."""
     q, k, v, do = (_c(a, np.uint8) for a in (q, k, v, do))
     sq, sk, sv, sdo = (_c(a, np.uint8) for a in (sq, sk, sv, sdo))
     lse, D = _c(lse, np.float32), _c(D, np.float32)
@@ -217,6 +254,10 @@ def bwd(q, sq, k, sk, v, sv, do, sdo, lse, D, cu, softmax_scale=None, causal_dq=
                    p_code=np.zeros((Hq, L, L), np.uint8), ds_code=np.zeros((Hq, L, L), np.uint8))
         dbg = _Dbg(out["p_scale"].ctypes.data, out["ds_scale"].ctypes.data,
                    out["p_code"].ctypes.data, out["ds_code"].ctypes.data)
+    dumps = _dump_arrays(window, ("bwd_dp", "bwd_p", "bwd_ps", "bwd_ds", "bwd_dss")) if window is not None else None
+    w = _window(window, dumps) if window is not None else None
+    if dumps is not None:
+        out["dumps"] = dumps
     lib().orc_bwd(_p(q), _p(sq), _p(k), _p(sk), _p(v), _p(sv), _p(do), _p(sdo), _p(lse), _p(D),
                   T, Hq, Hkv, d, ctypes.c_double(softmax_scale), _p(cu), len(cu) - 1, int(bool(causal_dq)),
                   int(exact), _p(out["dq"]), _p(out["dk"]), _p(out["dv"]), _p(out["pi"]),
@@ -224,7 +265,48 @@ def bwd(q, sq, k, sk, v, sv, do, sdo, lse, D, cu, softmax_scale=None, causal_dq=
                   _p(out["dv64"]) if want64 else None, ctypes.byref(dbg) if dbg is not None else None,
                   _p(sd) if sd is not None else None, _p(sk_) if sk_ is not None else None,
                   *((_p(out["dq_flip"]), _p(out["dk_flip"]), _p(out["dv_flip"])) if want_flip else (None, None, None)),
-                  int(tail_blocks))
+                  int(tail_blocks), ctypes.byref(w) if w is not None else None)
+    return out
+
+
+def fwd_replay(v, sv, cu, window, S, M, P, Hq, c_scale, p_shift=8):
+    """Forward products from given per-pair decisions (score accumulator S, running maximum M,
+    codes P, [heads][rows][keys] over ``window``).  Returns (O64 [heads][rows][d], LSE64
+    [heads][rows]), NaN for rows not replayed.  c_scale = softmax_scale * log2(e) as used."""
+    v, sv = _c(v, np.uint8), _c(sv, np.uint8)
+    T, Hkv, d = v.shape
+    cu = _c(cu, np.int32)
+    S, M, P = _c(S, np.float64), _c(M, np.float64), _c(P, np.uint8)
+    nh, nr, nk = window_shape(window)
+    assert S.shape == M.shape == P.shape == (nh, nr, nk)
+    o64 = np.empty((nh, nr, d))
+    lse64 = np.empty((nh, nr))
+    w = _window(window, {})
+    lib().orc_fwd_replay(_p(v), _p(sv), T, int(Hq), Hkv, d, ctypes.c_double(c_scale), _p(cu), len(cu) - 1,
+                         int(p_shift), ctypes.byref(w), _p(S), _p(M), _p(P), _p(o64), _p(lse64))
+    return o64, lse64
+
+
+def bwd_replay(q, sq, k, sk, do, sdo, cu, pi, window, P, PS, DS, DSS, softmax_scale=None):
+    """Backward products from given Phat / dShat codes and block exponent bytes ([heads][rows]
+    [keys] over ``window``).  Returns dict dq64 [heads][rows][d] (window heads and rows), dk64,
+    dv64 [Hkv][rows][d] (keys = the window's rows), NaN where not computed."""
+    q, k, do = _c(q, np.uint8), _c(k, np.uint8), _c(do, np.uint8)
+    sq, sk, sdo = _c(sq, np.uint8), _c(sk, np.uint8), _c(sdo, np.uint8)
+    T, Hq, d = q.shape
+    Hkv = k.shape[1]
+    if softmax_scale is None:
+        softmax_scale = 1.0 / np.sqrt(d)
+    cu = _c(cu, np.int32)
+    pi = _c(pi, np.int16)
+    P, PS, DS, DSS = (_c(a, np.uint8) for a in (P, PS, DS, DSS))
+    nh, nr, nk = window_shape(window)
+    assert P.shape == PS.shape == DS.shape == DSS.shape == (nh, nr, nk)
+    out = dict(dq64=np.empty((nh, nr, d)), dk64=np.empty((Hkv, nr, d)), dv64=np.empty((Hkv, nr, d)))
+    w = _window(window, {})
+    lib().orc_bwd_replay(_p(q), _p(sq), _p(k), _p(sk), _p(do), _p(sdo), T, Hq, Hkv, d,
+                         ctypes.c_double(softmax_scale), _p(cu), len(cu) - 1, _p(pi), ctypes.byref(w), _p(P), _p(PS),
+                         _p(DS), _p(DSS), _p(out["dq64"]), _p(out["dk64"]), _p(out["dv64"]))
     return out
 
 

@@ -290,6 +290,33 @@ int orc_worklist(const int32_t* cu, int n_docs, int kind, int n_workers, int32_t
 }
 
 /* ------------------------------------------------------------------------------------
+ * Intermediate dumps (test infrastructure): the forward and backward below can copy the
+ * per-pair values they form into caller arrays laid out [heads][rows][keys] over a window of
+ * query heads, absolute rows and absolute keys, so that the tests can compare decisions one by
+ * one and replay the products from given decisions (orc_fwd_replay, orc_bwd_replay).  Only
+ * visible pairs (same document, key <= row) are written.  NULL arrays are skipped.
+ * ---------------------------------------------------------------------------------- */
+typedef struct {
+  int row_lo, row_hi, key_lo, key_hi, head_lo, head_hi;
+  double* fwd_s;   /* forward: score accumulator sum_c deq(Q_ic) deq(K_jc) */
+  double* fwd_m;   /* forward: running maximum (score units) the pair's probability used */
+  uint8_t* fwd_p;  /* forward: E4M3 code of 2^p_shift 2^(t - m) */
+  double* bwd_dp;  /* backward: D_i - dP_ij */
+  uint8_t* bwd_p;  /* backward: Phat code and block exponent byte */
+  uint8_t* bwd_ps;
+  uint8_t* bwd_ds; /* backward: dShat code and block exponent byte */
+  uint8_t* bwd_dss;
+} orc_window;
+
+static long long win_index(const orc_window* w, int h, int row, int key) {
+  if (!w || h < w->head_lo || h >= w->head_hi || row < w->row_lo || row >= w->row_hi || key < w->key_lo ||
+      key >= w->key_hi)
+    return -1;
+  return ((long long)(h - w->head_lo) * (w->row_hi - w->row_lo) + (row - w->row_lo)) * (w->key_hi - w->key_lo) +
+         (key - w->key_lo);
+}
+
+/* ------------------------------------------------------------------------------------
  * Forward (jaehun.me §1.2 and §3.1; online softmax of the FlashAttention family)
  *
  * Scores in the base-2 domain: t_ij = softmax_scale * log2(e) * sum_c deq(Q_ic) deq(K_jc)
@@ -308,13 +335,13 @@ int orc_worklist(const int32_t* cu, int n_docs, int kind, int n_workers, int32_t
  * rounding decisions taken on values that differ by rounding between implementations).
  * tail_rows > 0 (a work restriction for sampling long documents, no change to what is
  * computed): only the last tail_rows rows of each document are computed; the outputs of the
- * other rows are left as they were.
+ * other rows are left as they were.  win (optional): intermediate dumps, see orc_window.
  * ---------------------------------------------------------------------------------- */
 void orc_fwd(const uint8_t* q, const uint8_t* sq, const uint8_t* k, const uint8_t* sk,
              const uint8_t* v, const uint8_t* sv, int T, int Hq, int Hkv, int d,
              double softmax_scale, const int32_t* cu, int n_docs, int p_shift, int exact_p,
              uint16_t* o, float* lse, double* o64, const uint8_t* sel_docs, const uint8_t* sel_kv,
-             double* o_flip, int tail_rows) {
+             double* o_flip, int tail_rows, const orc_window* win) {
   const int group = Hq / Hkv;
   const double c_scale = softmax_scale * 1.4426950408889634074; /* log2(e) */
   double* Qd = deq_all(q, sq, T, Hq, d);
@@ -328,7 +355,7 @@ void orc_fwd(const uint8_t* q, const uint8_t* sq, const uint8_t* k, const uint8_
     int doc = dm[row], kappa, j, cc;
     double m = -INFINITY, l = 0.0;
     double acc[256], flip[256];
-    double t_tile[KV_TILE];
+    double t_tile[KV_TILE], dot_tile[KV_TILE];
     const double* qi = Qd + ((size_t)row * Hq + hh) * d;
     if (doc < 0) {
       lse[(size_t)hh * T + row] = INFINITY;
@@ -351,6 +378,7 @@ void orc_fwd(const uint8_t* q, const uint8_t* sq, const uint8_t* k, const uint8_
           const double* kj = Kd + ((size_t)(start + j) * Hkv + g) * d;
           double dot = 0.0;
           for (cc = 0; cc < d; ++cc) dot += qi[cc] * kj[cc];
+          dot_tile[j - j0] = dot;
           t_tile[j - j0] = dot * c_scale;
           if (t_tile[j - j0] > mt) mt = t_tile[j - j0];
         }
@@ -362,6 +390,12 @@ void orc_fwd(const uint8_t* q, const uint8_t* sq, const uint8_t* k, const uint8_
           double p = exp2(t_tile[j - j0] - m_new);
           double ph = exact_p ? p : ldexp(orc_e4m3_decode(orc_e4m3_rne(ldexp(p, p_shift))), -p_shift);
           double qp = ldexp(e4m3_quantum(ldexp(p, p_shift)), -p_shift);
+          long long wi = win_index(win, hh, row, start + j);
+          if (wi >= 0) {
+            if (win->fwd_s) win->fwd_s[wi] = dot_tile[j - j0];
+            if (win->fwd_m) win->fwd_m[wi] = m_new;
+            if (win->fwd_p) win->fwd_p[wi] = orc_e4m3_rne(ldexp(p, p_shift));
+          }
           sum += p;
           for (cc = 0; cc < d; ++cc) {
             acc[cc] += ph * vj[cc];
@@ -514,7 +548,7 @@ void orc_bwd(const uint8_t* q, const uint8_t* sq, const uint8_t* k, const uint8_
              uint16_t* dq, uint16_t* dk, uint16_t* dv, int16_t* pi_out,
              double* dq64, double* dk64, double* dv64, const orc_bwd_debug* dbg,
              const uint8_t* sel_docs, const uint8_t* sel_kv, double* dq_flip, double* dk_flip,
-             double* dv_flip, int tail_blocks) {
+             double* dv_flip, int tail_blocks, const orc_window* win) {
   const int group = Hq / Hkv;
   const double c_scale = softmax_scale * 1.4426950408889634074;
   int16_t* pi = (int16_t*)malloc(sizeof(int16_t) * (size_t)Hq * T + 2);
@@ -544,7 +578,7 @@ void orc_bwd(const uint8_t* q, const uint8_t* sq, const uint8_t* k, const uint8_
     double* dv_acc;
     double* dk_fl = NULL;
     double* dv_fl = NULL;
-    double P[BLK][BLK], dS[BLK][BLK], qP[BLK][BLK], qdS[BLK][BLK];
+    double P[BLK][BLK], dS[BLK][BLK], qP[BLK][BLK], qdS[BLK][BLK], dPv[BLK][BLK];
     uint8_t Pc[BLK][BLK], dSc[BLK][BLK];
     double part[BLK * 256];
     double acc16[BLK * 256];
@@ -582,6 +616,7 @@ void orc_bwd(const uint8_t* q, const uint8_t* sq, const uint8_t* k, const uint8_
                 }
                 p = exp2(dot * c_scale - (double)lse[(size_t)hq * T + start + ii]);
                 P[ii - i0][jj - j0] = p;
+                dPv[ii - i0][jj - j0] = dp;
                 dS[ii - i0][jj - j0] = p * (dp - (double)D[(size_t)hq * T + start + ii]);
                 if (fabs(p) > pmax) pmax = fabs(p);
                 if (fabs(dS[ii - i0][jj - j0]) > dsmax) dsmax = fabs(dS[ii - i0][jj - j0]);
@@ -599,6 +634,15 @@ void orc_bwd(const uint8_t* q, const uint8_t* sq, const uint8_t* k, const uint8_
                 if (!(exact & 1)) P[ii - i0][jj - j0] = ldexp(orc_e4m3_decode(Pc[ii - i0][jj - j0]), sp);
                 if (!(exact & 2)) dS[ii - i0][jj - j0] = ldexp(orc_e4m3_decode(dSc[ii - i0][jj - j0]), sds);
               }
+            if (win)
+              for (ii = i0; ii < i1; ++ii)
+                for (jj = j0; jj < j1 && jj <= ii; ++jj) {
+                  long long wi = win_index(win, hq, start + ii, start + jj);
+                  if (wi < 0) continue;
+                  if (win->bwd_dp) win->bwd_dp[wi] = (double)D[(size_t)hq * T + start + ii] - dPv[ii - i0][jj - j0];
+                  if (win->bwd_p) { win->bwd_p[wi] = Pc[ii - i0][jj - j0]; win->bwd_ps[wi] = (uint8_t)(sp + 127); }
+                  if (win->bwd_ds) { win->bwd_ds[wi] = dSc[ii - i0][jj - j0]; win->bwd_dss[wi] = (uint8_t)(sds + 127); }
+                }
             if (dbg && n_docs == 1) {
               size_t bi = ((size_t)hq * nb + bq) * nb + bk;
               if (dbg->p_scale) dbg->p_scale[bi] = (uint8_t)(sp + 127);
@@ -673,6 +717,161 @@ void orc_bwd(const uint8_t* q, const uint8_t* sq, const uint8_t* k, const uint8_
   }
   free(pi);
   free(Qd); free(Kd); free(Vd); free(dOd);
+}
+
+/* ------------------------------------------------------------------------------------
+ * Replays (test infrastructure): the method's products computed from GIVEN per-pair
+ * decisions instead of the oracle's own, in the same order and arithmetic as orc_fwd and
+ * orc_bwd.  Fed the oracle's own dumps (orc_window) they reproduce its outputs bit for bit;
+ * fed the GPU's decisions, each checked separately against the method's definition, they
+ * give what the GPU's products should be up to the FP8 instruction's accumulation and the
+ * final rounding.  The decision arrays are laid out [heads][rows][keys] over `win`.
+ *
+ * Forward replay (jaehun.me §1.2, §3.1): for every (query head, row) of the window whose
+ * document's keys up to the row lie in the key window, key tiles from the diagonal tile down
+ * to tile 0; per tile the running maximum m is read from M (at the tile's first key),
+ * alpha = 2^(m_prev - m) (0 at the first tile), acc = alpha acc + sum_j 2^-p_shift deq(P_ij) V_j,
+ * l = alpha l + sum_j 2^(c S_ij - m).  o64 [nh][nr][d] = acc / l and lse64 [nh][nr] = m + log2 l,
+ * NaN for rows not replayed.  c_scale = softmax_scale log2(e) as the caller gives it.
+ * ---------------------------------------------------------------------------------- */
+void orc_fwd_replay(const uint8_t* v, const uint8_t* sv, int T, int Hq, int Hkv, int d, double c_scale,
+                    const int32_t* cu, int n_docs, int p_shift, const orc_window* win, const double* S,
+                    const double* M, const uint8_t* P, double* o64, double* lse64) {
+  const int group = Hq / Hkv;
+  const int nh = win->head_hi - win->head_lo, nr = win->row_hi - win->row_lo;
+  double* Vd = deq_all(v, sv, T, Hkv, d);
+  int* dm = doc_map(cu, n_docs, T);
+  long long task;
+#pragma omp parallel for schedule(dynamic, 16)
+  for (task = 0; task < (long long)nh * nr; ++task) {
+    int hh = win->head_lo + (int)(task / nr), row = win->row_lo + (int)(task % nr), g = hh / group;
+    int doc = (row >= 0 && row < T) ? dm[row] : -1, kappa, j, cc;
+    double acc[256], m = -INFINITY, l = 0.0;
+    double* o = o64 + (size_t)task * d;
+    lse64[task] = NAN;
+    for (cc = 0; cc < d; ++cc) o[cc] = NAN;
+    if (doc < 0 || cu[doc] < win->key_lo || row >= win->key_hi) continue;
+    for (cc = 0; cc < d; ++cc) acc[cc] = 0.0;
+    {
+      int start = cu[doc], r = row - start;
+      for (kappa = r / KV_TILE; kappa >= 0; --kappa) {
+        int j0 = kappa * KV_TILE, j1 = (kappa + 1) * KV_TILE;
+        double m_new, alpha, sum = 0.0;
+        if (j1 > r + 1) j1 = r + 1;
+        m_new = M[win_index(win, hh, row, start + j0)];
+        alpha = (m == -INFINITY) ? 0.0 : exp2(m - m_new);
+        for (cc = 0; cc < d; ++cc) acc[cc] *= alpha;
+        for (j = j0; j < j1; ++j) {
+          long long wi = win_index(win, hh, row, start + j);
+          const double* vj = Vd + ((size_t)(start + j) * Hkv + g) * d;
+          double ph = ldexp(orc_e4m3_decode(P[wi]), -p_shift);
+          sum += exp2(S[wi] * c_scale - m_new);
+          for (cc = 0; cc < d; ++cc) acc[cc] += ph * vj[cc];
+        }
+        l = alpha * l + sum;
+        m = m_new;
+      }
+      for (cc = 0; cc < d; ++cc) o[cc] = acc[cc] / l;
+      lse64[task] = m + log2(l);
+    }
+  }
+  free(Vd); free(dm);
+}
+
+/* Backward replay (jaehun.me §1.2, §3.1, §3.2): dQ of every (query head, row) of the window,
+ * and dK, dV of every key in [row_lo, row_hi) for the KV heads whose whole query-head group lies
+ * in the head window, from the given Phat / dShat codes and block exponent bytes (PS, DSS hold
+ * exponent + 127 per pair):
+ *   dV_j = sum_{h in group} sum_i 2^ps deq(P_ij) deq(dO_i),
+ *   dK_j = softmax_scale sum_{h in group} sum_i 2^dss deq(DS_ij) deq(Q_i),
+ *   dQ_i: 128-key tiles ascending, part = sum_j 2^dss deq(DS_ij) deq(K_j),
+ *         acc16 = f16(acc16 + f16(2^pi part)), dQ = softmax_scale 2^-pi acc16.
+ * Each document is replayed from the 32-query block that contains the window's first row (the
+ * window must start on a block of the document, or before it); all visible pairs from there to
+ * the document end must be in the dump, keys from the document start.  Order of every sum as in
+ * orc_bwd.  dq64 [nh][nr][d]; dk64, dv64 [Hkv][nr][d] (key rows of the row window); NaN where
+ * not computed. */
+void orc_bwd_replay(const uint8_t* q, const uint8_t* sq, const uint8_t* k, const uint8_t* sk, const uint8_t* dO,
+                    const uint8_t* sdo, int T, int Hq, int Hkv, int d, double softmax_scale, const int32_t* cu,
+                    int n_docs, const int16_t* pi, const orc_window* win, const uint8_t* P, const uint8_t* PS,
+                    const uint8_t* DS, const uint8_t* DSS, double* dq64, double* dk64, double* dv64) {
+  const int group = Hq / Hkv;
+  const int nr = win->row_hi - win->row_lo;
+  long long task, n_tasks = (long long)n_docs * Hkv;
+  size_t z;
+  double* Qd = deq_all(q, sq, T, Hq, d);
+  double* Kd = deq_all(k, sk, T, Hkv, d);
+  double* dOd = deq_all(dO, sdo, T, Hq, d);
+  for (z = 0; z < (size_t)(win->head_hi - win->head_lo) * nr * d; ++z) dq64[z] = NAN;
+  for (z = 0; z < (size_t)Hkv * nr * d; ++z) { dk64[z] = NAN; dv64[z] = NAN; }
+#pragma omp parallel for schedule(dynamic, 1)
+  for (task = 0; task < n_tasks; ++task) {
+    int doc = (int)(task / Hkv), g = (int)(task % Hkv);
+    int start = cu[doc], L = cu[doc + 1] - start, hq, bq, bk, ii, jj, cc, bq0, kv_ok;
+    int nb = (L + BLK - 1) / BLK;
+    double *dk_acc, *dv_acc, part[BLK * 256], acc16[BLK * 256];
+    if (L <= 0 || cu[doc + 1] <= win->row_lo || start >= win->row_hi) continue;
+    kv_ok = g * group >= win->head_lo && (g + 1) * group <= win->head_hi;
+    bq0 = win->row_lo > start ? (win->row_lo - start) / BLK : 0;
+    dk_acc = (double*)calloc((size_t)L * d, sizeof(double));
+    dv_acc = (double*)calloc((size_t)L * d, sizeof(double));
+    for (hq = g * group; hq < (g + 1) * group; ++hq) {
+      int in_heads = hq >= win->head_lo && hq < win->head_hi;
+      if (!in_heads) continue;
+      for (bq = bq0; bq < nb; ++bq) {
+        int i0 = bq * BLK, i1 = i0 + BLK < L ? i0 + BLK : L;
+        int kappa, kappa_last = (i1 - 1) / KV_TILE;
+        for (z = 0; z < (size_t)BLK * d; ++z) acc16[z] = 0.0;
+        for (kappa = 0; kappa <= kappa_last; ++kappa) {
+          for (z = 0; z < (size_t)BLK * d; ++z) part[z] = 0.0;
+          for (bk = kappa * (KV_TILE / BLK); bk < (kappa + 1) * (KV_TILE / BLK) && bk <= bq; ++bk) {
+            int j0 = bk * BLK, j1 = j0 + BLK < L ? j0 + BLK : L;
+            for (ii = i0; ii < i1; ++ii)
+              for (jj = j0; jj < j1 && jj <= ii; ++jj) {
+                long long wi = win_index(win, hq, start + ii, start + jj);
+                double ph = ldexp(orc_e4m3_decode(P[wi]), (int)PS[wi] - 127);
+                double dsh = ldexp(orc_e4m3_decode(DS[wi]), (int)DSS[wi] - 127);
+                const double* qi = Qd + ((size_t)(start + ii) * Hq + hq) * d;
+                const double* doi = dOd + ((size_t)(start + ii) * Hq + hq) * d;
+                const double* kj = Kd + ((size_t)(start + jj) * Hkv + g) * d;
+                for (cc = 0; cc < d; ++cc) {
+                  dv_acc[(size_t)jj * d + cc] += ph * doi[cc];
+                  dk_acc[(size_t)jj * d + cc] += dsh * qi[cc];
+                  part[(size_t)(ii - i0) * d + cc] += dsh * kj[cc];
+                }
+              }
+          }
+          for (ii = i0; ii < i1; ++ii) {
+            int p = pi[(size_t)hq * T + start + ii];
+            for (cc = 0; cc < d; ++cc) {
+              double x = ldexp(part[(size_t)(ii - i0) * d + cc], p);
+              double* a = &acc16[(size_t)(ii - i0) * d + cc];
+              *a = orc_f16_decode(orc_f16_rne(*a + orc_f16_decode(orc_f16_rne(x))));
+            }
+          }
+        }
+        for (ii = i0; ii < i1; ++ii) {
+          int p = pi[(size_t)hq * T + start + ii], row = start + ii;
+          if (row < win->row_lo || row >= win->row_hi) continue;
+          for (cc = 0; cc < d; ++cc)
+            dq64[((size_t)(hq - win->head_lo) * nr + (row - win->row_lo)) * d + cc] =
+                softmax_scale * ldexp(acc16[(size_t)(ii - i0) * d + cc], -p);
+        }
+      }
+    }
+    if (kv_ok)
+      for (jj = 0; jj < L; ++jj) {
+        int key = start + jj;
+        if (key < win->row_lo || key >= win->row_hi || jj < bq0 * BLK) continue;
+        for (cc = 0; cc < d; ++cc) {
+          dk64[((size_t)g * nr + (key - win->row_lo)) * d + cc] = softmax_scale * dk_acc[(size_t)jj * d + cc];
+          dv64[((size_t)g * nr + (key - win->row_lo)) * d + cc] = dv_acc[(size_t)jj * d + cc];
+        }
+      }
+    free(dk_acc);
+    free(dv_acc);
+  }
+  free(Qd); free(Kd); free(dOd);
 }
 
 int orc_num_threads(void) {
