@@ -1,4 +1,8 @@
-"""Build libflamia.so (all HIP sources, gfx950) in place, next to this file."""
+"""Build libflamia.so (all HIP sources, gfx950) in place, next to this file.
+
+`build(debug=True)` builds the test variant instead (FLAMIA_DEBUG_DUMP: the same kernels plus
+copies of their intermediates into caller buffers, see include/flamia_debug.h) into
+tests/_build/libflamia_debug.so; the product never loads it."""
 import os
 import subprocess
 import sys
@@ -6,6 +10,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libflamia.so")
+DEBUG_LIB = os.path.join(os.path.dirname(HERE), "tests", "_build", "libflamia_debug.so")
 SOURCES = ["flamia_api.hip", "quantize.hip", "worklist.hip", "attn_fwd.hip", "attn_bwd.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -17,19 +22,21 @@ FLAGS = [
 ]
 
 
-def build(verbose=False):
+def build(verbose=False, debug=False):
+    out_lib = DEBUG_LIB if debug else LIB
+    os.makedirs(os.path.dirname(out_lib), exist_ok=True)
     srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC] + FLAGS + srcs + ["-o", tmp]
+    tmp = out_lib + ".tmp%d" % os.getpid()
+    cmd = [HIPCC] + FLAGS + (["-DFLAMIA_DEBUG_DUMP"] if debug else []) + srcs + ["-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     out = "\n".join(l for l in (res.stdout + res.stderr).splitlines() if "packed-fp32-ops" not in l)
     if res.returncode != 0:
         raise RuntimeError("hipcc failed:\n" + out)
     if verbose and out.strip():
         print(out, file=sys.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out_lib)
+    return out_lib
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    print(build(verbose=True, debug="--debug" in sys.argv))

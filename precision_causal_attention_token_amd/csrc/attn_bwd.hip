@@ -316,7 +316,7 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
       // one matrix instruction, the operand read of the next one and a slice of the softmax
       // elements, so the matrix unit works while the vector unit does, and only one operand is
       // in flight at a time.
-      auto fused = [&](int sp_st, int qp, v16f& ns, v16f& np, int ss, int qs, int q0, v16f& sa, v16f& pa,
+      auto fused = [&](int sp_st, int qp, v16f& ns, v16f& np, int ss, int qs, int q0, int sh, v16f& sa, v16f& pa,
                        int* pp4, int* pd4, uint32_t& sp, uint32_t& sds, auto masked) {
         constexpr bool MASK = decltype(masked)::value;
         constexpr int NM = 2 * NC;     // matrix instructions of the products
@@ -359,6 +359,17 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
               const int r = 8 * (i / 4) + i % 4;  // unrolled: an immediate
               arg = (lo <= r && r < hi) ? arg : -__builtin_inff();  // 2^-inf = +0
             }
+#ifdef FLAMIA_DEBUG_DUMP
+            if (p.dbg.bwd_s || p.dbg.bwd_dp) {  // test builds: the two accumulators, masked as used
+              const int r = 8 * (i / 4) + i % 4, row_rel = q0 + 32 * qs + 4 * hh + r;
+              const int64_t x = (row_rel < L && key_rel < L)
+                                    ? dbg_index(p.dbg, sh, doc_start + row_rel, doc_start + key_rel) : -1;
+              if (x >= 0) {
+                if (p.dbg.bwd_s) p.dbg.bwd_s[x] = (MASK && !(lo <= r && r < hi)) ? -__builtin_inff() : sa[i];
+                if (p.dbg.bwd_dp) p.dbg.bwd_dp[x] = pa[i];
+              }
+            }
+#endif
             const float pv = __builtin_amdgcn_exp2f(arg);
             const float dsv = -(pv * pa[i]);  // P (dP - D)
             sa[i] = pv;
@@ -375,6 +386,19 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
           pp4[w4] = pack4_fp8_scaled(sa[4 * w4], sa[4 * w4 + 1], sa[4 * w4 + 2], sa[4 * w4 + 3], sp);
           pd4[w4] = pack4_fp8_scaled(pa[4 * w4], pa[4 * w4 + 1], pa[4 * w4 + 2], pa[4 * w4 + 3], sds);
         }
+#ifdef FLAMIA_DEBUG_DUMP
+        if (p.dbg.bwd_p || p.dbg.bwd_ds) {  // test builds: codes and block exponent bytes
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int row_rel = q0 + 32 * qs + acc_row(i, hh);
+            const int64_t x = (row_rel < L && key_rel < L)
+                                  ? dbg_index(p.dbg, sh, doc_start + row_rel, doc_start + key_rel) : -1;
+            if (x < 0) continue;
+            if (p.dbg.bwd_p) { p.dbg.bwd_p[x] = (uint8_t)(pp4[i / 4] >> (8 * (i % 4))); p.dbg.bwd_ps[x] = (uint8_t)sp; }
+            if (p.dbg.bwd_ds) { p.dbg.bwd_ds[x] = (uint8_t)(pd4[i / 4] >> (8 * (i % 4))); p.dbg.bwd_dss[x] = (uint8_t)sds; }
+          }
+        }
+#endif
       };
       // Phase ph works on step ph.  Block 0's products were made in the phase before (cs, cp);
       // block 1's are issued while block 0's softmax terms are formed, and block 0 of the next
@@ -403,12 +427,12 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
             }
           }
         };
-        fused(ph, 1, xs, xq, ph, 0, q0, cs, cp, pp, pd, sp[0], sds[0], masked);
+        fused(ph, 1, xs, xq, ph, 0, q0, h, cs, cp, pp, pd, sp[0], sds[0], masked);
         // empty uses of freshly issued products keep their matrix instructions among the vector
         // work they overlap, instead of sunk past the hand-over towards their next use
         asm volatile("" ::"v"(xs), "v"(xq));
         hand_over(0);
-        fused(min(ph + 1, n_steps - 1), 0, cs, cp, ph, 1, q0, xs, xq, pp + 4, pd + 4, sp[1], sds[1], masked);
+        fused(min(ph + 1, n_steps - 1), 0, cs, cp, ph, 1, q0, h, xs, xq, pp + 4, pd + 4, sp[1], sds[1], masked);
         asm volatile("" ::"v"(cs), "v"(cp));
         hand_over(1);
         if (lane == 0) {
@@ -534,11 +558,23 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
               if (qr < L) {
                 const int pi = p.pi[(int64_t)h * T + doc_start + qr];
                 const float up = exp2i(pi), down = exp2i(-pi) * p.softmax_scale;
+#ifdef FLAMIA_DEBUG_DUMP
+                if (p.dbg.dq_part) {  // test builds: the partial as converted to FP16 (key tile 0)
+                  const int64_t x = dbg_row(p.dbg, h, doc_start + qr);
+                  if (x >= 0)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i)
+                      p.dbg.dq_part[(x * p.dbg.n_tiles) * D + 32 * dblk + acc_row(i, hh)] = dq[i] * up;
+                }
+#endif
                 uint16_t* row = p.dq + (int64_t)(doc_start + qr) * p.dqst + (int64_t)h * p.dqsh;
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                  const _Float16 a0 = (_Float16)(dq[4 * j + 0] * up), a1 = (_Float16)(dq[4 * j + 1] * up);
-                  const _Float16 a2 = (_Float16)(dq[4 * j + 2] * up), a3 = (_Float16)(dq[4 * j + 3] * up);
+                  // the FP16 sum of one partial: acc16 = +0 + FP16(partial), so a partial that
+                  // rounds to -0 gives +0, as the sums of longer documents do
+                  const _Float16 z = 0;
+                  const _Float16 a0 = z + (_Float16)(dq[4 * j + 0] * up), a1 = z + (_Float16)(dq[4 * j + 1] * up);
+                  const _Float16 a2 = z + (_Float16)(dq[4 * j + 2] * up), a3 = z + (_Float16)(dq[4 * j + 3] * up);
                   uint2 w;
                   w.x = pack_bf16_int((float)a0 * down, (float)a1 * down);
                   w.y = pack_bf16_int((float)a2 * down, (float)a3 * down);
@@ -737,6 +773,15 @@ __global__ __launch_bounds__(DQ_THREADS, 2) void dq_kernel(BwdParams p) {  // tw
           const int sc[2] = {FOLD ? f0 : sb[0], FOLD ? f1 : sb[1]};
           auto add_partial = [&](v16f& part, int db) {
             mfma_drain(part);
+#ifdef FLAMIA_DEBUG_DUMP
+            if (p.dbg.dq_part && row_valid) {  // test builds: the partial as converted to FP16
+              const int64_t x = dbg_row(p.dbg, h, doc_start + q_rel);
+              if (x >= 0 && kappa < p.dbg.n_tiles)
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                  p.dbg.dq_part[(x * p.dbg.n_tiles + kappa) * D + 32 * db + acc_row(i, hh)] = FOLD ? part[i] : part[i] * up;
+            }
+#endif
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
               const h2 x = FOLD ? h2{(_Float16)part[2 * j], (_Float16)part[2 * j + 1]}

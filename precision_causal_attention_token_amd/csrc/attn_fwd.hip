@@ -241,6 +241,18 @@ __global__ __launch_bounds__(fwd_threads<W>(), 8 / W) void fwd_kernel(FwdParams 
             for (int i = 0; i < 16; ++i)
               if (32 * kb4 + acc_row(i, 0) > lim) s[kb4][i] = -__builtin_inff();
         }
+#ifdef FLAMIA_DEBUG_DUMP
+        if (row_valid && p.dbg.fwd_s) {  // test builds: the score accumulator after the mask
+#pragma unroll
+          for (int kb4 = 0; kb4 < 4; ++kb4)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const int key_rel = KV_TILE * kappa + 32 * kb4 + acc_row(i, hh);
+              const int64_t x = key_rel < L ? dbg_index(p.dbg, h, doc_start + q_rel, doc_start + key_rel) : -1;
+              if (x >= 0) p.dbg.fwd_s[x] = s[kb4][i];
+            }
+        }
+#endif
         // ---- running max (raw accumulator units, then scaled once)
         float mx = -__builtin_inff();
 #pragma unroll
@@ -323,6 +335,21 @@ __global__ __launch_bounds__(fwd_threads<W>(), 8 / W) void fwd_kernel(FwdParams 
           asm volatile("" : "+v"(l));
           __builtin_amdgcn_sched_barrier(0);
         }
+#ifdef FLAMIA_DEBUG_DUMP
+        if (row_valid && (p.dbg.fwd_p || p.dbg.fwd_m)) {  // test builds: codes and the running max
+#pragma unroll
+          for (int kb4 = 0; kb4 < 4; ++kb4)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const int key_rel = KV_TILE * kappa + 32 * kb4 + acc_row(i, hh);
+              const int64_t x = key_rel < L ? dbg_index(p.dbg, h, doc_start + q_rel, doc_start + key_rel) : -1;
+              if (x < 0) continue;
+              const int word = pop[kb4 >> 1][4 * (kb4 & 1) + i / 4];
+              if (p.dbg.fwd_p) p.dbg.fwd_p[x] = (uint8_t)(word >> (8 * (i % 4)));
+              if (p.dbg.fwd_m) p.dbg.fwd_m[x] = m_new;
+            }
+        }
+#endif
       }
       if (kappa > 0) {
         __builtin_amdgcn_s_waitcnt(0);  // this wave's direct loads have landed

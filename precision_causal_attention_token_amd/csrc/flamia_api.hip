@@ -5,8 +5,28 @@
 
 #include "../../include/flamia.h"
 #include "kernels.h"
+#ifdef FLAMIA_DEBUG_DUMP
+#include "../../include/flamia_debug.h"
+#endif
 
 using namespace flamia;
+
+#ifdef FLAMIA_DEBUG_DUMP
+namespace {
+DebugDump g_dbg{};  // all-NULL: nothing dumped
+}
+extern "C" flamia_status flamia_debug_set_dump(const flamia_debug_dump* d) {
+  if (!d) {
+    g_dbg = DebugDump{};
+    return FLAMIA_OK;
+  }
+  if (d->row_hi <= d->row_lo || d->key_hi <= d->key_lo || d->head_hi <= d->head_lo) return FLAMIA_ERR_SHAPE;
+  g_dbg = DebugDump{d->row_lo, d->row_hi, d->key_lo, d->key_hi, d->head_lo, d->head_hi, d->fwd_s, d->fwd_m,
+                    d->fwd_p, d->bwd_s, d->bwd_dp, d->bwd_p, d->bwd_ps, d->bwd_ds, d->bwd_dss, d->dq_part,
+                    d->n_tiles};
+  return FLAMIA_OK;
+}
+#endif
 
 namespace {
 
@@ -144,6 +164,9 @@ flamia_status flamia_fwd(const flamia_fwd_args* a, void* stream) {
   p.list = static_cast<const int32_t*>(a->fwd_list);
   p.o = static_cast<uint16_t*>(a->o); p.ost = a->o_stride_t; p.osh = a->o_stride_h;
   p.lse = a->lse;
+#ifdef FLAMIA_DEBUG_DUMP
+  p.dbg = g_dbg;
+#endif
   hipError_t e = launch_fwd(p, a->d, grid, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FLAMIA_OK : FLAMIA_ERR_HIP;
 }
@@ -204,6 +227,9 @@ flamia_status flamia_bwd(const flamia_bwd_args* a, void* stream) {
   p.ds_capacity = (int64_t)cap;
   p.pi_out = a->dq_exp_out;
   p.causal = a->causal_dq_scale ? 1 : 0;
+#ifdef FLAMIA_DEBUG_DUMP
+  p.dbg = g_dbg;
+#endif
   hipError_t e = launch_bwd(p, a->d, grid, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FLAMIA_OK : FLAMIA_ERR_HIP;
 }

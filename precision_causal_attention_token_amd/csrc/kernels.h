@@ -6,6 +6,39 @@
 
 namespace flamia {
 
+#ifdef FLAMIA_DEBUG_DUMP
+// Test builds only (the library variant the parity tests build with FLAMIA_DEBUG_DUMP): where the
+// attention kernels copy the intermediates they compute.  Every array is [heads][rows][keys] over
+// the window [head_lo, head_hi) x [row_lo, row_hi) x [key_lo, key_hi) (query heads, absolute rows
+// and keys); only visited (row, key) pairs of one document are written; NULL arrays are skipped.
+struct DebugDump {
+  int32_t row_lo, row_hi, key_lo, key_hi, head_lo, head_hi;
+  float* fwd_s;       // forward score accumulator after the causal mask (-inf where masked)
+  float* fwd_m;       // running maximum (score units) the pair's probability was formed against
+  uint8_t* fwd_p;     // E4M3 code of 2^8 p
+  float* bwd_s;       // backward score accumulator after the mask
+  float* bwd_dp;      // the D - dP accumulator
+  uint8_t* bwd_p;     // Phat code and its block exponent byte
+  uint8_t* bwd_ps;
+  uint8_t* bwd_ds;    // dShat code and its block exponent byte
+  uint8_t* bwd_dss;
+  float* dq_part;     // [heads][rows][n_tiles][d]: each key tile's dQ partial times 2^pi, as converted to FP16
+  int32_t n_tiles;
+};
+// Position of (query head, row) in the window's rows, or -1 outside it.
+__device__ __forceinline__ int64_t dbg_row(const DebugDump& g, int h, int row) {
+  if (h < g.head_lo || h >= g.head_hi || row < g.row_lo || row >= g.row_hi) return -1;
+  return (int64_t)(h - g.head_lo) * (g.row_hi - g.row_lo) + (row - g.row_lo);
+}
+// Position of (query head, row, key) in the dump window, or -1 outside it.
+__device__ __forceinline__ int64_t dbg_index(const DebugDump& g, int h, int row, int key) {
+  if (h < g.head_lo || h >= g.head_hi || row < g.row_lo || row >= g.row_hi || key < g.key_lo || key >= g.key_hi)
+    return -1;
+  return ((int64_t)(h - g.head_lo) * (g.row_hi - g.row_lo) + (row - g.row_lo)) * (g.key_hi - g.key_lo) +
+         (key - g.key_lo);
+}
+#endif
+
 struct QTensorDev {
   const uint16_t* x;
   int64_t st, sh;   // element strides
@@ -35,6 +68,9 @@ struct FwdParams {
   uint16_t* o;
   int64_t ost, osh;
   float* lse;
+#ifdef FLAMIA_DEBUG_DUMP
+  DebugDump dbg;
+#endif
 };
 
 struct BwdParams {
@@ -57,6 +93,9 @@ struct BwdParams {
   int64_t ds_capacity;      // (block, query head) pairs that fit
   int16_t* pi_out;          // optional copy of pi
   int32_t causal;
+#ifdef FLAMIA_DEBUG_DUMP
+  DebugDump dbg;
+#endif
 };
 
 hipError_t launch_quantize(const QuantParams& p, int d, hipStream_t s);

@@ -8,7 +8,7 @@ import torch
 
 import precision_causal_attention_token_amd as fl
 from precision_causal_attention_token_amd import workloads
-from tests.gpu_common import gpu_call, say, stage_check, token_mask
+from tests.gpu_common import full_window, gpu_call, say, stage_and_chain, token_mask
 from tests.helpers import bf16_bits, bits_to_f64, dequant
 
 pytestmark = pytest.mark.gpu
@@ -89,16 +89,17 @@ def test_one_token_documents(orc):
     q, k, v, do = workloads.tensors(T, H, H, d, seed=720)
     g = gpu_call(q, k, v, do, cu)
     _check_one_token_closed_form(g)
-    stage_check(orc, g, cu, zero_in_exact=("dQ", "dK"))
+    stage_and_chain(orc, q, k, v, do, cu, full_window(T, H), release=g, zero_in_exact=("dQ", "dK"))
 
 
 def test_one_token_documents_full_size(orc):
     """Extreme packing at full size, 131072 one-token documents x 8 heads: O = BF16(0 + deq V)
-    and dV = BF16(0 + deq dO) bit-exactly for every token; the stage bar (dQ, dK zero in exact
-    arithmetic) on a sample of 4096 documents spread over the call."""
+    and dV = BF16(0 + deq dO) bit-exactly for every token; stage and chain checks (dQ, dK zero in
+    exact arithmetic) on 1024 consecutive documents in the middle of the call, all heads."""
     cu, shp, (q, k, v, do) = workloads.workload("tokens")
     say("one-token documents: T=%d H=%d d=%d" % (shp.T, shp.Hq, shp.d))
     g = gpu_call(q, k, v, do, cu)
     _check_one_token_closed_form(g)
-    docs = list(range(0, len(cu) - 1, (len(cu) - 1) // 4096))
-    stage_check(orc, g, cu, docs=docs, zero_in_exact=("dQ", "dK"))
+    a = shp.T // 2
+    win = dict(row_lo=a, row_hi=a + 1024, key_lo=a, key_hi=a + 1024, head_lo=0, head_hi=shp.Hq)
+    stage_and_chain(orc, q, k, v, do, cu, win, release=g, zero_in_exact=("dQ", "dK"))
