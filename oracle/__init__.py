@@ -165,9 +165,9 @@ def _sel(mask, n):
 
 
 def fwd(q, sq, k, sk, v, sv, cu, softmax_scale=None, p_shift=8, exact_p=False, want_o64=False,
-        docs=None, kv_heads=None, want_flip=False, tail_rows=0, window=None):
-    """Returns (O bits u16 [T,Hq,d], LSE f32 [Hq,T] in log2 units, O64 or None), plus the
-    one-flip allowance of O if want_flip, plus (with ``window``, a dict of row/key/head bounds)
+        docs=None, kv_heads=None, tail_rows=0, window=None):
+    """Returns (O bits u16 [T,Hq,d], LSE f32 [Hq,T] in log2 units, O64 or None), plus (with
+    ``window``, a dict of row/key/head bounds)
     a dict of the per-pair dumps fwd_s (score accumulator), fwd_m (running maximum), fwd_p
     (E4M3 codes), [heads][rows][keys], NaN / 0xFF where not visited.  ``docs`` / ``kv_heads``
     (index lists) restrict the work to those documents / KV heads, and tail_rows > 0 to the last
@@ -183,16 +183,13 @@ def fwd(q, sq, k, sk, v, sv, cu, softmax_scale=None, p_shift=8, exact_p=False, w
     lse = np.full((Hq, T), np.nan, np.float32)
     o64 = np.zeros((T, Hq, d), np.float64) if want_o64 else None
     sd, sk_ = _sel(docs, len(cu) - 1), _sel(kv_heads, Hkv)
-    flip = np.zeros((T, Hq, d), np.float64) if want_flip else None
     dumps = _dump_arrays(window, ("fwd_s", "fwd_m", "fwd_p")) if window is not None else None
     w = _window(window, dumps) if window is not None else None
     lib().orc_fwd(_p(q), _p(sq), _p(k), _p(sk), _p(v), _p(sv), T, Hq, Hkv, d, ctypes.c_double(softmax_scale),
                   _p(cu), len(cu) - 1, int(p_shift), int(bool(exact_p)), _p(o), _p(lse),
                   _p(o64) if o64 is not None else None, _p(sd) if sd is not None else None,
-                  _p(sk_) if sk_ is not None else None, _p(flip) if flip is not None else None, int(tail_rows),
-                  ctypes.byref(w) if w is not None else None)
-    res = (o, lse, o64) + ((flip,) if want_flip else ()) + ((dumps,) if window is not None else ())
-    return res
+                  _p(sk_) if sk_ is not None else None, int(tail_rows), ctypes.byref(w) if w is not None else None)
+    return (o, lse, o64) + ((dumps,) if window is not None else ())
 
 
 def quantize_do(do_bits, o_bits, cu):
@@ -222,7 +219,7 @@ class _Dbg(ctypes.Structure):
 
 
 def bwd(q, sq, k, sk, v, sv, do, sdo, lse, D, cu, softmax_scale=None, causal_dq=False, exact=0,
-        want64=False, debug=False, docs=None, kv_heads=None, want_flip=False, tail_blocks=0, window=None):
+        want64=False, debug=False, docs=None, kv_heads=None, tail_blocks=0, window=None):
     """Returns dict with dq, dk, dv (u16 BF16 bits), pi (i16 [Hq,T]) and optionally the
     double-precision values (dq64, dk64, dv64) and, for single-document calls, the block
     exponents/codes of the P and dS operands (p_scale, ds_scale [Hq,nb,nb]; p_code,
@@ -242,8 +239,6 @@ def bwd(q, sq, k, sk, v, sv, do, sdo, lse, D, cu, softmax_scale=None, causal_dq=
                dv=np.empty((T, Hkv, d), np.uint16), pi=np.empty((Hq, T), np.int16))
     if want64:
         out.update(dq64=np.empty((T, Hq, d)), dk64=np.empty((T, Hkv, d)), dv64=np.empty((T, Hkv, d)))
-    if want_flip:
-        out.update(dq_flip=np.empty((T, Hq, d)), dk_flip=np.empty((T, Hkv, d)), dv_flip=np.empty((T, Hkv, d)))
     sd, sk_ = _sel(docs, len(cu) - 1), _sel(kv_heads, Hkv)
     dbg = None
     if debug:
@@ -264,7 +259,6 @@ def bwd(q, sq, k, sk, v, sv, do, sdo, lse, D, cu, softmax_scale=None, causal_dq=
                   _p(out["dq64"]) if want64 else None, _p(out["dk64"]) if want64 else None,
                   _p(out["dv64"]) if want64 else None, ctypes.byref(dbg) if dbg is not None else None,
                   _p(sd) if sd is not None else None, _p(sk_) if sk_ is not None else None,
-                  *((_p(out["dq_flip"]), _p(out["dk_flip"]), _p(out["dv_flip"])) if want_flip else (None, None, None)),
                   int(tail_blocks), ctypes.byref(w) if w is not None else None)
     return out
 
@@ -307,28 +301,4 @@ def bwd_replay(q, sq, k, sk, do, sdo, cu, pi, window, P, PS, DS, DSS, softmax_sc
     lib().orc_bwd_replay(_p(q), _p(sq), _p(k), _p(sk), _p(do), _p(sdo), T, Hq, Hkv, d,
                          ctypes.c_double(softmax_scale), _p(cu), len(cu) - 1, _p(pi), ctypes.byref(w), _p(P), _p(PS),
                          _p(DS), _p(DSS), _p(out["dq64"]), _p(out["dk64"]), _p(out["dv64"]))
-    return out
-
-
-def allowance(q, sq, k, sk, v, sv, do, sdo, lse, D, o64, o_flip, pi, cu, softmax_scale=None, docs=None,
-              kv_heads=None, shared_stats=True):
-    """First-order bound, per output element, of the effect of the FP8 matrix instruction's
-    accumulation precision (test tolerance derivation, not the method).  Returns dict with
-    lse_a [Hq,T], o_a, dq_a [T,Hq,d], dk_a, dv_a [T,Hkv,d]."""
-    q, k, v, do = (_c(a, np.uint8) for a in (q, k, v, do))
-    sq, sk, sv, sdo = (_c(a, np.uint8) for a in (sq, sk, sv, sdo))
-    lse, D = _c(lse, np.float32), _c(D, np.float32)
-    o64, o_flip, pi = _c(o64, np.float64), _c(o_flip, np.float64), _c(pi, np.int16)
-    T, Hq, d = q.shape
-    Hkv = k.shape[1]
-    if softmax_scale is None:
-        softmax_scale = 1.0 / np.sqrt(d)
-    cu = _c(cu, np.int32)
-    out = dict(lse_a=np.empty((Hq, T)), o_a=np.empty((T, Hq, d)), dq_a=np.empty((T, Hq, d)),
-               dk_a=np.empty((T, Hkv, d)), dv_a=np.empty((T, Hkv, d)))
-    sd, sk_ = _sel(docs, len(cu) - 1), _sel(kv_heads, Hkv)
-    lib().orc_allowance(_p(q), _p(sq), _p(k), _p(sk), _p(v), _p(sv), _p(do), _p(sdo), _p(lse), _p(D), _p(o64),
-                        _p(o_flip), T, Hq, Hkv, d, ctypes.c_double(softmax_scale), _p(cu), len(cu) - 1, _p(pi),
-                        _p(sd) if sd is not None else None, _p(sk_) if sk_ is not None else None,
-                        int(bool(shared_stats)), _p(out["lse_a"]), _p(out["o_a"]), _p(out["dq_a"]), _p(out["dk_a"]), _p(out["dv_a"]))
     return out

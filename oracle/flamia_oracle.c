@@ -152,16 +152,6 @@ double orc_f16_decode(uint16_t h) {
   return s ? -v : v;
 }
 
-/* Spacing of E4M3 values at |y| (y in the code domain): 2^-9 below the normal range, else
- * 2^(floor(log2|y|) - 3).  Used only for the one-flip error allowances the tests derive. */
-static double e4m3_quantum(double y) {
-  int e;
-  double a = fabs(y);
-  if (a < ldexp(1.0, -6)) return ldexp(1.0, -9);
-  frexp(a, &e);
-  return ldexp(1.0, (e - 1) - 3);
-}
-
 /* ------------------------------------------------------------------------------------
  * Token-block quantiser (jaehun.me §3.1, §3.2, §3.4 "Packed documents"; agihunt.info)
  *
@@ -330,9 +320,7 @@ static long long win_index(const orc_window* w, int h, int row, int key) {
  * o64 (optional) receives acc / l in double.  GQA: query head h reads KV head
  * h / (Hq / Hkv).  sel_docs / sel_kv (optional, one byte per document / KV head): rows of
  * unselected documents or heads are skipped and their outputs left as they were (lets the
- * tests sample large calls).  o_flip (optional) receives, per output element, the largest
- * change one Phat code moving to a neighbouring code would cause (a test allowance for
- * rounding decisions taken on values that differ by rounding between implementations).
+ * tests sample large calls).
  * tail_rows > 0 (a work restriction for sampling long documents, no change to what is
  * computed): only the last tail_rows rows of each document are computed; the outputs of the
  * other rows are left as they were.  win (optional): intermediate dumps, see orc_window.
@@ -341,7 +329,7 @@ void orc_fwd(const uint8_t* q, const uint8_t* sq, const uint8_t* k, const uint8_
              const uint8_t* v, const uint8_t* sv, int T, int Hq, int Hkv, int d,
              double softmax_scale, const int32_t* cu, int n_docs, int p_shift, int exact_p,
              uint16_t* o, float* lse, double* o64, const uint8_t* sel_docs, const uint8_t* sel_kv,
-             double* o_flip, int tail_rows, const orc_window* win) {
+             int tail_rows, const orc_window* win) {
   const int group = Hq / Hkv;
   const double c_scale = softmax_scale * 1.4426950408889634074; /* log2(e) */
   double* Qd = deq_all(q, sq, T, Hq, d);
@@ -354,7 +342,7 @@ void orc_fwd(const uint8_t* q, const uint8_t* sq, const uint8_t* k, const uint8_
     int row = (int)(task / Hq), hh = (int)(task % Hq), g = hh / group;
     int doc = dm[row], kappa, j, cc;
     double m = -INFINITY, l = 0.0;
-    double acc[256], flip[256];
+    double acc[256];
     double t_tile[KV_TILE], dot_tile[KV_TILE];
     const double* qi = Qd + ((size_t)row * Hq + hh) * d;
     if (doc < 0) {
@@ -367,7 +355,7 @@ void orc_fwd(const uint8_t* q, const uint8_t* sq, const uint8_t* k, const uint8_
     }
     if ((sel_docs && !sel_docs[doc]) || (sel_kv && !sel_kv[g])) continue;
     if (tail_rows > 0 && row < cu[doc + 1] - tail_rows) continue;
-    for (cc = 0; cc < d; ++cc) acc[cc] = flip[cc] = 0.0;
+    for (cc = 0; cc < d; ++cc) acc[cc] = 0.0;
     {
       int start = cu[doc], r = row - start;
       for (kappa = r / KV_TILE; kappa >= 0; --kappa) {
@@ -384,12 +372,11 @@ void orc_fwd(const uint8_t* q, const uint8_t* sq, const uint8_t* k, const uint8_
         }
         m_new = m > mt ? m : mt;
         alpha = (m == -INFINITY) ? 0.0 : exp2(m - m_new);
-        for (cc = 0; cc < d; ++cc) { acc[cc] *= alpha; flip[cc] *= alpha; }
+        for (cc = 0; cc < d; ++cc) acc[cc] *= alpha;
         for (j = j0; j < j1; ++j) {
           const double* vj = Vd + ((size_t)(start + j) * Hkv + g) * d;
           double p = exp2(t_tile[j - j0] - m_new);
           double ph = exact_p ? p : ldexp(orc_e4m3_decode(orc_e4m3_rne(ldexp(p, p_shift))), -p_shift);
-          double qp = ldexp(e4m3_quantum(ldexp(p, p_shift)), -p_shift);
           long long wi = win_index(win, hh, row, start + j);
           if (wi >= 0) {
             if (win->fwd_s) win->fwd_s[wi] = dot_tile[j - j0];
@@ -397,10 +384,7 @@ void orc_fwd(const uint8_t* q, const uint8_t* sq, const uint8_t* k, const uint8_
             if (win->fwd_p) win->fwd_p[wi] = orc_e4m3_rne(ldexp(p, p_shift));
           }
           sum += p;
-          for (cc = 0; cc < d; ++cc) {
-            acc[cc] += ph * vj[cc];
-            if (o_flip && qp * fabs(vj[cc]) > flip[cc]) flip[cc] = qp * fabs(vj[cc]);
-          }
+          for (cc = 0; cc < d; ++cc) acc[cc] += ph * vj[cc];
         }
         l = alpha * l + sum;
         m = m_new;
@@ -408,7 +392,6 @@ void orc_fwd(const uint8_t* q, const uint8_t* sq, const uint8_t* k, const uint8_
       for (cc = 0; cc < d; ++cc) {
         o[((size_t)row * Hq + hh) * d + cc] = orc_bf16_rne(acc[cc] / l);
         if (o64) o64[((size_t)row * Hq + hh) * d + cc] = acc[cc] / l;
-        if (o_flip) o_flip[((size_t)row * Hq + hh) * d + cc] = flip[cc] / l;
       }
       lse[(size_t)hh * T + row] = (float)(m + log2(l));
     }
@@ -525,9 +508,7 @@ void orc_dq_exponents(const uint8_t* sk, const uint8_t* sv, const uint8_t* sdo, 
  * calls only) receive the P and dS block exponent bytes [Hq][nb][nb] and codes
  * [Hq][L][L] (0 for invisible entries).  sel_docs / sel_kv as in the forward: unselected
  * (document, KV head) pairs are skipped and their gradient rows stay zero; pi is always
- * computed for the whole call.  d?_flip (optional; all three or none) receive per element
- * the largest change one Phat / dShat code moving to a neighbouring code would cause (the
- * tests' allowance for rounding decisions that two implementations may take differently).
+ * computed for the whole call.
  * tail_blocks > 0 (a work restriction for sampling long documents, no change to what is
  * computed): only the last tail_blocks 32-query blocks of each document are visited.  dQ of
  * those rows is then complete (every key block up to theirs is visited), and so are dK and dV
@@ -547,8 +528,7 @@ void orc_bwd(const uint8_t* q, const uint8_t* sq, const uint8_t* k, const uint8_
              double softmax_scale, const int32_t* cu, int n_docs, int causal_dq, int exact,
              uint16_t* dq, uint16_t* dk, uint16_t* dv, int16_t* pi_out,
              double* dq64, double* dk64, double* dv64, const orc_bwd_debug* dbg,
-             const uint8_t* sel_docs, const uint8_t* sel_kv, double* dq_flip, double* dk_flip,
-             double* dv_flip, int tail_blocks, const orc_window* win) {
+             const uint8_t* sel_docs, const uint8_t* sel_kv, int tail_blocks, const orc_window* win) {
   const int group = Hq / Hkv;
   const double c_scale = softmax_scale * 1.4426950408889634074;
   int16_t* pi = (int16_t*)malloc(sizeof(int16_t) * (size_t)Hq * T + 2);
@@ -560,13 +540,11 @@ void orc_bwd(const uint8_t* q, const uint8_t* sq, const uint8_t* k, const uint8_
   double* dOd = deq_all(dO, sdo, T, Hq, d);
   orc_dq_exponents(sk, sv, sdo, T, Hq, Hkv, d, cu, n_docs, causal_dq, pi);
   if (pi_out) memcpy(pi_out, pi, sizeof(int16_t) * (size_t)Hq * T);
-  for (z = 0; z < n_q; ++z) { dq[z] = 0; if (dq64) dq64[z] = 0.0; if (dq_flip) dq_flip[z] = 0.0; }
+  for (z = 0; z < n_q; ++z) { dq[z] = 0; if (dq64) dq64[z] = 0.0; }
   for (z = 0; z < n_kv; ++z) {
     dk[z] = 0; dv[z] = 0;
     if (dk64) dk64[z] = 0.0;
     if (dv64) dv64[z] = 0.0;
-    if (dk_flip) dk_flip[z] = 0.0;
-    if (dv_flip) dv_flip[z] = 0.0;
   }
 
 #pragma omp parallel for schedule(dynamic, 1)
@@ -576,9 +554,7 @@ void orc_bwd(const uint8_t* q, const uint8_t* sq, const uint8_t* k, const uint8_
     int nb = (L + BLK - 1) / BLK, hq, bq, bk, ii, jj, cc;
     double* dk_acc;
     double* dv_acc;
-    double* dk_fl = NULL;
-    double* dv_fl = NULL;
-    double P[BLK][BLK], dS[BLK][BLK], qP[BLK][BLK], qdS[BLK][BLK], dPv[BLK][BLK];
+    double P[BLK][BLK], dS[BLK][BLK], dPv[BLK][BLK];
     uint8_t Pc[BLK][BLK], dSc[BLK][BLK];
     double part[BLK * 256];
     double acc16[BLK * 256];
@@ -586,10 +562,6 @@ void orc_bwd(const uint8_t* q, const uint8_t* sq, const uint8_t* k, const uint8_
     if ((sel_docs && !sel_docs[doc]) || (sel_kv && !sel_kv[g])) continue;
     dk_acc = (double*)calloc((size_t)L * d, sizeof(double));
     dv_acc = (double*)calloc((size_t)L * d, sizeof(double));
-    if (dq_flip) {
-      dk_fl = (double*)calloc((size_t)L * d, sizeof(double));
-      dv_fl = (double*)calloc((size_t)L * d, sizeof(double));
-    }
     for (hq = g * group; hq < (g + 1) * group; ++hq) {
       for (bq = (tail_blocks > 0 && nb > tail_blocks) ? nb - tail_blocks : 0; bq < nb; ++bq) {
         int i0 = bq * BLK, i1 = i0 + BLK < L ? i0 + BLK : L;
@@ -629,8 +601,6 @@ void orc_bwd(const uint8_t* q, const uint8_t* sq, const uint8_t* k, const uint8_
                 if (jj > ii) { Pc[ii - i0][jj - j0] = 0; dSc[ii - i0][jj - j0] = 0; continue; }
                 Pc[ii - i0][jj - j0] = orc_e4m3_rne(ldexp(P[ii - i0][jj - j0], -sp));
                 dSc[ii - i0][jj - j0] = orc_e4m3_rne(ldexp(dS[ii - i0][jj - j0], -sds));
-                qP[ii - i0][jj - j0] = ldexp(e4m3_quantum(ldexp(P[ii - i0][jj - j0], -sp)), sp);
-                qdS[ii - i0][jj - j0] = ldexp(e4m3_quantum(ldexp(dS[ii - i0][jj - j0], -sds)), sds);
                 if (!(exact & 1)) P[ii - i0][jj - j0] = ldexp(orc_e4m3_decode(Pc[ii - i0][jj - j0]), sp);
                 if (!(exact & 2)) dS[ii - i0][jj - j0] = ldexp(orc_e4m3_decode(dSc[ii - i0][jj - j0]), sds);
               }
@@ -666,17 +636,6 @@ void orc_bwd(const uint8_t* q, const uint8_t* sq, const uint8_t* k, const uint8_
                   dk_acc[(size_t)jj * d + cc] += dsh * qi[cc];
                   part[(size_t)(ii - i0) * d + cc] += dsh * kj[cc];
                 }
-                if (dq_flip) {
-                  const double qp = qP[ii - i0][jj - j0], qd = qdS[ii - i0][jj - j0];
-                  for (cc = 0; cc < d; ++cc) {
-                    double* fv = &dv_fl[(size_t)jj * d + cc];
-                    double* fk = &dk_fl[(size_t)jj * d + cc];
-                    double* fq = &dq_flip[((size_t)(start + ii) * Hq + hq) * d + cc];
-                    if (qp * fabs(doi[cc]) > *fv) *fv = qp * fabs(doi[cc]);
-                    if (softmax_scale * qd * fabs(qi[cc]) > *fk) *fk = softmax_scale * qd * fabs(qi[cc]);
-                    if (softmax_scale * qd * fabs(kj[cc]) > *fq) *fq = softmax_scale * qd * fabs(kj[cc]);
-                  }
-                }
               }
           }
           /* FP16 accumulation of this key tile's partial sums, in ascending tile order */
@@ -707,13 +666,9 @@ void orc_bwd(const uint8_t* q, const uint8_t* sq, const uint8_t* k, const uint8_
         dv[((size_t)(start + jj) * Hkv + g) * d + cc] = orc_bf16_rne(vval);
         if (dk64) dk64[((size_t)(start + jj) * Hkv + g) * d + cc] = kval;
         if (dv64) dv64[((size_t)(start + jj) * Hkv + g) * d + cc] = vval;
-        if (dk_flip) dk_flip[((size_t)(start + jj) * Hkv + g) * d + cc] = dk_fl[(size_t)jj * d + cc];
-        if (dv_flip) dv_flip[((size_t)(start + jj) * Hkv + g) * d + cc] = dv_fl[(size_t)jj * d + cc];
       }
     free(dk_acc);
     free(dv_acc);
-    free(dk_fl);
-    free(dv_fl);
   }
   free(pi);
   free(Qd); free(Kd); free(Vd); free(dOd);
@@ -888,136 +843,3 @@ void orc_e4m3_decode_array(const uint8_t* c, double* out, long n) { long i; for 
 void orc_bf16_rne_array(const double* y, uint16_t* out, long n) { long i; for (i = 0; i < n; ++i) out[i] = orc_bf16_rne(y[i]); }
 void orc_f16_rne_array(const double* y, uint16_t* out, long n) { long i; for (i = 0; i < n; ++i) out[i] = orc_f16_rne(y[i]); }
 void orc_e8m0_roundup_array(const double* a, int32_t* out, long n) { long i; for (i = 0; i < n; ++i) out[i] = orc_e8m0_roundup(a[i]); }
-
-/* ------------------------------------------------------------------------------------
- * Test tolerance derivation (not part of the method).
- *
- * The GPU computes every product with the FP8 matrix instruction, whose accumulation keeps
- * only about 11-12 bits below the largest product of each 64-term instruction (measured on
- * the hardware: worst error 2^-11.4 of the largest product over 32K random dot products).
- * The pages fix no accumulation precision, so this is the kernel's precision.  Its effect
- * on the outputs is bounded here to first order, per output element, from the oracle's own
- * quantities; the parity tests add it to the spec bar.  Inputs: decoded operands via
- * codes/scales, the oracle's LSE, D, O (double) and O flip allowance.  Outputs (all
- * optional): lse_a [Hq][T], o_a [T][Hq][d] (score error -> softmax weights, PV accumulation),
- * dq_a, dk_a, dv_a (score, dP, D errors -> P and dS -> gradient products; product and FP16
- * accumulation errors).  ACC is the relative accumulation bound used (2^-10, a margin over
- * the measured 2^-11.4).  shared_stats = 1: the backward being checked used the same LSE and
- * D as the oracle's backward (stage-wise check), so only its own score and dP errors count.
- * ---------------------------------------------------------------------------------- */
-#define ACC_REL 9.765625e-4 /* 2^-10 */
-#define F32_REL 2.384185791015625e-07 /* 2^-22: a few FP32 roundings */
-
-static double chunk_max_sum(const double* a, const double* b, int d) {
-  /* sum over 64-wide chunks of max_c |a_c b_c| */
-  double s = 0.0;
-  int c0, c;
-  for (c0 = 0; c0 < d; c0 += 64) {
-    double m = 0.0;
-    for (c = c0; c < c0 + 64 && c < d; ++c) {
-      double x = fabs(a[c] * b[c]);
-      if (x > m) m = x;
-    }
-    s += m;
-  }
-  return s;
-}
-
-void orc_allowance(const uint8_t* q, const uint8_t* sq, const uint8_t* k, const uint8_t* sk,
-                   const uint8_t* v, const uint8_t* sv, const uint8_t* dO, const uint8_t* sdo,
-                   const float* lse, const float* D, const double* o64, const double* o_flip,
-                   int T, int Hq, int Hkv, int d, double softmax_scale, const int32_t* cu, int n_docs,
-                   const int16_t* pi, const uint8_t* sel_docs, const uint8_t* sel_kv, int shared_stats,
-                   double* lse_a, double* o_a, double* dq_a, double* dk_a, double* dv_a) {
-  const int group = Hq / Hkv;
-  const double c_scale = softmax_scale * 1.4426950408889634074, LN2 = 0.6931471805599453;
-  double* Qd = deq_all(q, sq, T, Hq, d);
-  double* Kd = deq_all(k, sk, T, Hkv, d);
-  double* Vd = deq_all(v, sv, T, Hkv, d);
-  double* dOd = deq_all(dO, sdo, T, Hq, d);
-  size_t z;
-  long long task, n_tasks = (long long)n_docs * Hkv;
-  for (z = 0; z < (size_t)T * Hq * d; ++z) { o_a[z] = 0.0; dq_a[z] = 0.0; }
-  for (z = 0; z < (size_t)T * Hkv * d; ++z) { dk_a[z] = 0.0; dv_a[z] = 0.0; }
-  for (z = 0; z < (size_t)T * Hq; ++z) lse_a[z] = 0.0;
-#pragma omp parallel for schedule(dynamic, 1)
-  for (task = 0; task < n_tasks; ++task) {
-    int doc = (int)(task / Hkv), g = (int)(task % Hkv);
-    int start = cu[doc], L = cu[doc + 1] - start, hq, i, j, cc;
-    double *P, *eps, *dkA, *dvA;
-    if (L <= 0) continue;
-    if ((sel_docs && !sel_docs[doc]) || (sel_kv && !sel_kv[g])) continue;
-    P = (double*)malloc(sizeof(double) * L);
-    eps = (double*)malloc(sizeof(double) * L);
-    dkA = (double*)calloc((size_t)L * d, sizeof(double));
-    dvA = (double*)calloc((size_t)L * d, sizeof(double));
-    for (hq = g * group; hq < (g + 1) * group; ++hq) {
-      for (i = 0; i < L; ++i) {
-        const size_t ri = (size_t)(start + i) * Hq + hq;
-        const double* qi = Qd + ri * d;
-        const double* doi = dOd + ri * d;
-        const double* oi = o64 + ri * d;
-        const double Li = (double)lse[(size_t)hq * T + start + i], Di = (double)D[(size_t)hq * T + start + i];
-        double emax = 0.0, ebar = 0.0, dD = 0.0, oA[256], dqA[256], cum[256], fp16[256];
-        const double scale_pi = ldexp(1.0, pi[(size_t)hq * T + start + i]);
-        for (j = 0; j <= i; ++j) {
-          const double* kj = Kd + ((size_t)(start + j) * Hkv + g) * d;
-          double dot = 0.0;
-          for (cc = 0; cc < d; ++cc) dot += qi[cc] * kj[cc];
-          P[j] = exp2(dot * c_scale - Li);
-          eps[j] = c_scale * (ACC_REL * chunk_max_sum(qi, kj, d)) + F32_REL * fabs(dot * c_scale);
-          if (eps[j] > emax) emax = eps[j];
-          ebar += P[j] * eps[j];
-        }
-        lse_a[(size_t)hq * T + start + i] = emax + F32_REL * (fabs(Li) + 8.0);
-        /* O: softmax-weight perturbation + PV accumulation per 64-key chunk */
-        for (cc = 0; cc < d; ++cc) {
-          double s = 0.0, pv = 0.0, cm = 0.0;
-          for (j = 0; j <= i; ++j) {
-            const double vjc = Vd[((size_t)(start + j) * Hkv + g) * d + cc];
-            double x = P[j] * fabs(vjc);
-            s += P[j] * (eps[j] + ebar) * fabs(vjc - oi[cc]);
-            if (x > cm) cm = x;
-            if ((j % 64) == 63 || j == i) { pv += cm; cm = 0.0; }
-          }
-          oA[cc] = LN2 * s + ACC_REL * pv + F32_REL * fabs(oi[cc]);
-          o_a[ri * d + cc] = oA[cc];
-        }
-        /* D: the GPU's D uses its own (BF16) O */
-        for (cc = 0; cc < d && !shared_stats; ++cc) {
-          double ob = fabs(oi[cc]);
-          int e;
-          frexp(ob > 1e-300 ? ob : 1e-300, &e);
-          dD += fabs(doi[cc]) * (oA[cc] + o_flip[ri * d + cc] + ldexp(1.0, e - 8)) + F32_REL * fabs(doi[cc] * oi[cc]);
-        }
-        for (cc = 0; cc < d; ++cc) { dqA[cc] = 0.0; cum[cc] = 0.0; fp16[cc] = 0.0; }
-        for (j = 0; j <= i; ++j) {
-          const double* kj = Kd + ((size_t)(start + j) * Hkv + g) * d;
-          const double* vj = Vd + ((size_t)(start + j) * Hkv + g) * d;
-          double dp = 0.0, edp, dP_, dS_;
-          for (cc = 0; cc < d; ++cc) dp += doi[cc] * vj[cc];
-          edp = ACC_REL * chunk_max_sum(doi, vj, d) + F32_REL * fabs(dp);
-          dP_ = P[j] * LN2 * (eps[j] + (shared_stats ? 0.0 : lse_a[(size_t)hq * T + start + i]));
-          dS_ = dP_ * fabs(dp - Di) + P[j] * (edp + dD);
-          for (cc = 0; cc < d; ++cc) {
-            const double ds = P[j] * (dp - Di);
-            dvA[(size_t)j * d + cc] += dP_ * fabs(doi[cc]) + ACC_REL * P[j] * fabs(doi[cc]);
-            dkA[(size_t)j * d + cc] += softmax_scale * (dS_ * fabs(qi[cc]) + ACC_REL * fabs(ds * qi[cc]));
-            dqA[cc] += softmax_scale * (dS_ * fabs(kj[cc]) + ACC_REL * fabs(ds * kj[cc]));
-            cum[cc] += ds * kj[cc];
-          }
-          if ((j % KV_TILE) == KV_TILE - 1 || j == i)  /* FP16 accumulation after each key tile */
-            for (cc = 0; cc < d; ++cc) fp16[cc] += 2.0 * ldexp(1.0, -11) * fabs(cum[cc]) + ldexp(1.0, -24) / scale_pi;
-        }
-        for (cc = 0; cc < d; ++cc) dq_a[ri * d + cc] = dqA[cc] + softmax_scale * fp16[cc];
-      }
-    }
-    for (j = 0; j < L; ++j)
-      for (cc = 0; cc < d; ++cc) {
-        dk_a[((size_t)(start + j) * Hkv + g) * d + cc] = dkA[(size_t)j * d + cc];
-        dv_a[((size_t)(start + j) * Hkv + g) * d + cc] = dvA[(size_t)j * d + cc];
-      }
-    free(P); free(eps); free(dkA); free(dvA);
-  }
-  free(Qd); free(Kd); free(Vd); free(dOd);
-}
