@@ -171,15 +171,17 @@ flamia_status flamia_fwd(const flamia_fwd_args* args, void* stream);
  * Reduction of dQ: a document with a single 128-key tile has one contribution per row, which
  * the key-tile pass turns into dQ directly.  For longer documents the key-tile pass stores
  * the dShat codes and exponents of every visited (64-query tile, key tile, query head) in the
- * workspace, and a query-tile pass (driven by the forward work list) reads them back in
- * ascending key-tile order and keeps acc16 in registers.  The order of every sum is fixed, so
- * results are bit-reproducible, and no workgroup waits for another.
+ * workspace's store, and a query-tile pass (driven by the forward work list) reads them back
+ * in ascending key-tile order and keeps acc16 in registers.  When the store cannot hold every
+ * block of the call, the backward list is cut into consecutive chunks that each fit (laid out
+ * on the GPU from cu_seqlens, no host synchronisation); each chunk runs both passes, and rows
+ * whose key tiles continue in a later chunk leave their FP16 sums in the dQ output rows until
+ * then.  The backward list visits each document's key tiles in ascending order, so the sums
+ * are the same whatever the chunking.  The order of every sum is fixed, so results are
+ * bit-reproducible, and no workgroup waits for another.
  * Work comes from a FLAMIA_LIST_BWD list (key-tile pass; each (item, KV head) unit runs all
  * query heads of its group, so dK and dV are written once) and a FLAMIA_LIST_FWD list (dQ
  * pass), both built for the same cu_seqlens.
- * Device-side error: if the workspace cannot hold the dShat store, the status word (the first
- * int32 of the workspace) is set to 2 and dQ, dK, dV of the rows inside documents are left
- * unwritten; otherwise it is 0 once the backward has run.
  * ------------------------------------------------------------------------------------------ */
 typedef struct {
   const uint8_t *q, *k, *v, *dO;      /* codes (dO: [T, Hq, d], from the dO quantiser pass) */
@@ -193,22 +195,34 @@ typedef struct {
   const void* bwd_list;               /* FLAMIA_LIST_BWD list for cu_seqlens */
   void *dq, *dk, *dv;                 /* out: bf16; dq [T, Hq, d], dk, dv [T, Hkv, d] */
   int64_t dq_stride_t, dq_stride_h, dk_stride_t, dk_stride_h, dv_stride_t, dv_stride_h;
-  void* workspace;                    /* flamia_bwd_workspace_bytes(...) bytes, 256-byte aligned,
-                                         any contents */
+  void* workspace;                    /* at least flamia_bwd_workspace_bytes(n_docs, T, Hq, d, 0)
+                                         bytes, 256-byte aligned, any contents; every byte beyond
+                                         that enlarges the dShat store (fewer, larger chunks) */
   size_t workspace_bytes;
   int32_t causal_dq_scale;            /* 0: sequence-wide prescale (default); 1: causal */
   int16_t* dq_exp_out;                /* optional out: pi as int16 [Hq, T] (0 on invalid rows) */
 } flamia_bwd_args;
 
-/* Host.  Workspace bytes of a backward over these documents: a status word, pi [Hq, T],
- * n_docs + 1 block offsets and, per query head, 8320 bytes for each 64-query x 128-key block
- * on or below the diagonal of every document longer than 128 tokens.  cu_seqlens_host is a
- * HOST copy of cu_seqlens (may be NULL only when n_docs == 0).  Returns 0 on bad arguments. */
-size_t flamia_bwd_workspace_bytes(const int32_t* cu_seqlens_host, int32_t n_docs, int32_t T, int32_t Hq);
+/* Host.  Backward workspace for n_docs documents of total length T: a header, pi [Hq, T], the
+ * chunk layout tables (n_docs + ceil(T / 128) entries) and a dShat store of about store_budget
+ * bytes, clamped between twice the largest single key tile (ceil(T / 64) blocks of 8320 bytes
+ * per query head: store_budget = 0 gives the smallest workspace the backward accepts) and what
+ * one chunk of any documents of total length T needs.  Depends on the sizes only, never on the
+ * document lengths, so sizing needs no copy of cu_seqlens on the host.  A smaller store runs the
+ * backward in more chunks (more launches, the FP16 dQ sums carried between them).  Returns 0 on
+ * bad arguments. */
+size_t flamia_bwd_workspace_bytes(int32_t n_docs, int32_t T, int32_t Hq, int32_t d, size_t store_budget);
 
-/* Errors: NULL pointers, sizes, d, head ratio, workspace smaller than its fixed part (status
- * word, pi table, block offsets).  A dShat store that does not fit is reported on the device
- * (status word 2, see above). */
+/* Host.  Workspace with which a backward over these documents runs as one chunk (the fastest):
+ * the store holds every dShat block of the call.  For callers that already hold the document
+ * lengths on the host (cu_seqlens_host: HOST int32 [n_docs + 1]; NULL only when n_docs == 0).
+ * Returns 0 on bad arguments. */
+size_t flamia_bwd_workspace_bytes_for(const int32_t* cu_seqlens_host, int32_t n_docs, int32_t T, int32_t Hq,
+                                      int32_t d);
+
+/* Errors: NULL pointers, sizes, d, head ratio, a workspace smaller than
+ * flamia_bwd_workspace_bytes(n_docs, T, Hq, d, 0) (FLAMIA_ERR_WORKSPACE).  The status word (first
+ * int32 of the workspace) is 0 once the backward has run. */
 flamia_status flamia_bwd(const flamia_bwd_args* args, void* stream);
 
 /* Host.  Number of compute units of the current device, the persistent grid used by

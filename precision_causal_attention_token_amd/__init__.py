@@ -21,8 +21,14 @@ FLAMIA_LIST_BWD = 1
 
 EXPORTED_SYMBOLS = (
     "flamia_status_str", "flamia_worklist_bytes", "flamia_build_worklist", "flamia_quantize",
-    "flamia_fwd", "flamia_bwd", "flamia_bwd_workspace_bytes", "flamia_num_workers",
+    "flamia_fwd", "flamia_bwd", "flamia_bwd_workspace_bytes", "flamia_bwd_workspace_bytes_for",
+    "flamia_num_workers",
 )
+
+# Default dShat store of a backward whose caller passes no workspace: large enough that calls up
+# to the 65536-token, 16-head workloads run in a few chunks; the store never grows past what one
+# chunk of any documents of the call's total length needs.
+DEFAULT_STORE_BYTES = 4 << 30
 
 
 class _QTensor(ctypes.Structure):
@@ -82,7 +88,11 @@ def load_library(path=LIB_PATH):
     lib.flamia_bwd.restype = ctypes.c_int
     lib.flamia_bwd.argtypes = [ctypes.POINTER(_BwdArgs), ctypes.c_void_p]
     lib.flamia_bwd_workspace_bytes.restype = ctypes.c_size_t
-    lib.flamia_bwd_workspace_bytes.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
+    lib.flamia_bwd_workspace_bytes.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                               ctypes.c_size_t]
+    lib.flamia_bwd_workspace_bytes_for.restype = ctypes.c_size_t
+    lib.flamia_bwd_workspace_bytes_for.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                                   ctypes.c_int32]
     lib.flamia_num_workers.restype = ctypes.c_int32
     lib.flamia_num_workers.argtypes = []
     _lib = lib
@@ -196,20 +206,28 @@ def fwd(q, k, v, cu_seqlens, fwd_list, softmax_scale=None, out=None):
     return o, lse
 
 
-def bwd_workspace_bytes(cu_seqlens_host, T, Hq):
-    """Workspace bytes of a backward (cu_seqlens_host: host int32 array or CPU tensor)."""
+def bwd_workspace_bytes(n_docs, T, Hq, d, store_budget=DEFAULT_STORE_BYTES):
+    """Backward workspace bytes for n_docs documents of total length T (sizes only; a store of
+    about store_budget bytes, 0 for the smallest accepted)."""
+    return int(load_library().flamia_bwd_workspace_bytes(int(n_docs), int(T), int(Hq), int(d), int(store_budget)))
+
+
+def bwd_workspace_bytes_for(cu_seqlens_host, T, Hq, d):
+    """Workspace with which a backward over these documents runs as one chunk (cu_seqlens_host:
+    a host int32 array the caller already holds)."""
     import numpy as np
     cu = np.ascontiguousarray(np.asarray(cu_seqlens_host, dtype=np.int32))
     n_docs = cu.size - 1
     ptr = cu.ctypes.data_as(ctypes.c_void_p) if n_docs > 0 else None
-    return int(load_library().flamia_bwd_workspace_bytes(ptr, n_docs, int(T), int(Hq)))
+    return int(load_library().flamia_bwd_workspace_bytes_for(ptr, n_docs, int(T), int(Hq), int(d)))
 
 
 def bwd(q, k, v, do, lse, D, cu_seqlens, lists, softmax_scale=None, causal_dq_scale=False, want_pi=False,
         workspace=None):
     """Backward on quantised operands.  q, k, v, do are (codes, scales) pairs; lse, D f32 [Hq, T];
     lists: the micro-batch's Lists.  workspace: a uint8 CUDA tensor of at least
-    bwd_workspace_bytes(...) bytes, or None to allocate one.
+    bwd_workspace_bytes(n_docs, T, Hq, d, 0) bytes, or None to allocate one with the default
+    store (DEFAULT_STORE_BYTES).
     Returns (dq, dk, dv) BF16, plus the prescale exponents pi int16 [Hq, T] if want_pi."""
     lib = load_library()
     n_docs = _check_cu(cu_seqlens)
@@ -221,7 +239,7 @@ def bwd(q, k, v, do, lse, D, cu_seqlens, lists, softmax_scale=None, causal_dq_sc
     dk = torch.empty((T, Hkv, d), dtype=torch.bfloat16, device=dev)
     dv = torch.empty((T, Hkv, d), dtype=torch.bfloat16, device=dev)
     if workspace is None:
-        workspace = torch.empty(bwd_workspace_bytes(lists.cu_host, T, Hq), dtype=torch.uint8, device=dev)
+        workspace = torch.empty(bwd_workspace_bytes(n_docs, T, Hq, d), dtype=torch.uint8, device=dev)
     pi = torch.empty((Hq, T), dtype=torch.int16, device=dev) if want_pi else None
     a = _BwdArgs(qc.data_ptr(), kc.data_ptr(), vc.data_ptr(), dc.data_ptr(),
                  qs.data_ptr(), ks.data_ptr(), vs.data_ptr(), dsc.data_ptr(), lse.data_ptr(), D.data_ptr(),
@@ -235,19 +253,19 @@ def bwd(q, k, v, do, lse, D, cu_seqlens, lists, softmax_scale=None, causal_dq_sc
 
 
 def bwd_status(workspace):
-    """Status word of the last backward that used `workspace` (0 = ok; 2 = the dShat store did
-    not fit the workspace)."""
-    return int(workspace[:4].view(torch.int32).item())
+    """Header of the last backward that used `workspace`: (status, key-tile chunks run); status
+    0 once the backward has laid out its chunks (synchronises)."""
+    h = workspace[:8].view(torch.int32).cpu()
+    return int(h[0]), int(h[1])
 
 
 class Lists:
-    """Forward and backward work lists of one micro-batch (built once, reused by every layer),
-    and a host copy of cu_seqlens for sizing the backward workspace."""
+    """Forward and backward work lists of one micro-batch (built on the GPU once, reused by every
+    layer; nothing is copied to the host)."""
 
     def __init__(self, cu_seqlens, T):
         self.fwd = build_worklist(cu_seqlens, T, FLAMIA_LIST_FWD)
         self.bwd = build_worklist(cu_seqlens, T, FLAMIA_LIST_BWD)
-        self.cu_host = cu_seqlens.cpu().numpy()
 
 
 def training_call(q, k, v, do, cu_seqlens, lists=None, softmax_scale=None, causal_dq_scale=False):

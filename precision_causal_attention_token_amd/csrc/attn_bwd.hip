@@ -55,12 +55,6 @@ constexpr int DQ_QT = 2;               // 64-query tiles per dQ workgroup (two w
 constexpr int DQ_WAVES = 2 * DQ_QT;
 constexpr int DQ_THREADS = 64 * DQ_WAVES;
 
-// Stored dShat block of (key tile kappa, query tile qt >= 2 kappa) of a document with n_qt query
-// tiles whose blocks start at `base`: blocks are ordered by key tile, then query tile.
-__device__ __forceinline__ int64_t ds_block(int64_t base, int kappa, int n_qt, int qt) {
-  return base + (int64_t)kappa * n_qt - (int64_t)kappa * (kappa - 1) + (qt - 2 * kappa);
-}
-
 // Query offset (within a 64-query tile) held at byte position pos of a dShat row as assembled in
 // LDS by the dQ pass: the row of key j holds, for lane group hh of the wave that owns j, the 32
 // bytes of its P-operand register order (query 32 qb + 8 w4 + 4 hh + e in byte 4 (4 qb + w4) + e).
@@ -158,16 +152,17 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
   constexpr int NDB = D / 32;
   __shared__ BwdSmem<D> sm;
 
-  if (*p.status) return;  // the dShat store does not fit the workspace
+  if (p.status[0] || p.chunk >= p.status[1]) return;  // not laid out, or a chunk past the last
   const int tid = threadIdx.x;
   // the wave index is uniform: in a scalar register, everything derived from it stays scalar
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 31;
   const bool producer = wave < 4;
   const int kw = wave & 3;  // key group of both roles
-  const int n_items = p.list[0];
-  const int4* items = reinterpret_cast<const int4*>(p.list + 4);
-  const int n_units = n_items * p.Hkv;
+  // this chunk's items: a contiguous range of the backward list
+  const int u_lo = p.chunk_start[p.chunk], u_hi = p.chunk_start[p.chunk + 1];
+  const int4* items = reinterpret_cast<const int4*>(p.list + 4) + u_lo;
+  const int n_units = (u_hi - u_lo) * p.Hkv;
   const int G = gridDim.x, wg = blockIdx.x;
   const int grp = p.Hq / p.Hkv;
   const float c = p.c;
@@ -185,9 +180,9 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
     const int L = __builtin_amdgcn_readfirstlane(p.cu[doc + 1]) - doc_start;
     const int n_qt = (L + QT - 1) / QT;
     const bool store_ds = L > KV_TILE;  // two or more key tiles: dQ in the query-stationary kernel
-    int64_t ds_base = 0;
+    int64_t ds_base = 0;  // the item's first block in the chunk's store
     if (store_ds) {
-      const int64_t v = p.doc_base[doc];
+      const int64_t v = p.kv_off[__builtin_amdgcn_readfirstlane(p.tile_base[doc]) + kappa];
       ds_base = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(v >> 32)) << 32) |
                           (uint32_t)__builtin_amdgcn_readfirstlane((int)v));
     }
@@ -497,7 +492,7 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
               // lane, so each store instruction writes 1 KiB contiguously.  Non-temporal: the
               // store is read back once, by another kernel, and would otherwise push the step
               // tiles (re-read once per key tile) out of L2
-              uint8_t* bbase = p.ds_store + (ds_block(ds_base, kappa, n_qt, st_qt) * p.Hq + st_h) * DS_STRIDE;
+              uint8_t* bbase = p.ds_store + ((ds_base + (st_qt - 2 * kappa)) * p.Hq + st_h) * DS_STRIDE;
               v4i* dst = reinterpret_cast<v4i*>(bbase + 2048 * kw + 16 * lane);
               __builtin_nontemporal_store(v4i{d0.x, d0.y, d0.z, d0.w}, dst);
               __builtin_nontemporal_store(v4i{d1.x, d1.y, d1.z, d1.w}, dst + 64);
@@ -656,10 +651,11 @@ __device__ __forceinline__ void dq_load(DqRegs<D>& r, const BwdParams& p, int do
     const int key = min(KV_TILE * kappa + row, L - 1);
     r.k[i] = *reinterpret_cast<const v4u*>(p.k + ((int64_t)(doc_start + key) * p.Hkv + g) * D + col);
   }
-  // block of query tile qt0 + t (clamped into the key tile's range [2 kappa, n_qt - 1])
+  // block of query tile qt0 + t (clamped into the key tile's range [2 kappa, n_qt - 1]); `base` is
+  // the key tile's first block in the chunk's store
   auto block = [&](int t) {
     const int qt = min(max(qt0 + t, 2 * kappa), n_qt - 1);
-    return p.ds_store + ((int64_t)ds_block(base, kappa, n_qt, qt) * p.Hq + h) * DS_STRIDE;
+    return p.ds_store + ((base + (qt - 2 * kappa)) * p.Hq + h) * DS_STRIDE;
   };
 #pragma unroll
   for (int t = 0; t < DQ_QT; ++t)  // read once: non-temporal, so L2 keeps the K tiles
@@ -700,7 +696,8 @@ __global__ __launch_bounds__(DQ_THREADS, 2) void dq_kernel(BwdParams p) {  // tw
   typedef _Float16 h2 __attribute__((ext_vector_type(2)));
   __shared__ DqSmem<D> sm;
 
-  if (*p.status) return;
+  if (p.status[0] || p.chunk >= p.status[1]) return;  // not laid out, or a chunk past the last
+  const int chunk = p.chunk;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int n = lane & 31, hh = lane >> 5;
@@ -724,24 +721,61 @@ __global__ __launch_bounds__(DQ_THREADS, 2) void dq_kernel(BwdParams p) {  // tw
     const int doc_start = p.cu[doc];
     const int L = p.cu[doc + 1] - doc_start;
     const int n_qt = (L + QT - 1) / QT;
-    const int64_t base = p.doc_base[doc];
     const int qt0 = (ITEM_Q / QT) * item + DQ_QT * part;
     if (qt0 >= n_qt) continue;  // the item ends before this part (uniform over the workgroup)
+    // This unit's key tiles in this chunk: the key tiles 0 .. K of the unit's last row have
+    // chunk numbers that do not decrease along the document, so the ones in this chunk are
+    // [k_lo, kappa_hi] with k_lo = #(chunk < this one) and kappa_hi + 1 = #(chunk <= this one).
+    // Rows whose last key tile lies in an earlier chunk are complete already.
+    const int tb = p.tile_base[doc];
+    const int last_qt = min(qt0 + DQ_QT, n_qt) - 1;
+    const int K = last_qt / 2;
+    if (p.kv_chunk[tb + K] < chunk) continue;  // (uniform over the workgroup)
+    int k_lo = 0, kappa_hi = -1;
+    for (int k0 = 0; k0 <= K; k0 += 64 * 8) {  // each lane reads up to 8 entries, all in flight
+      int ch[8];
+#pragma unroll
+      for (int x = 0; x < 8; ++x) {
+        const int kk = k0 + 64 * x + lane;
+        ch[x] = kk <= K ? p.kv_chunk[tb + kk] : 0x7FFFFFFF;
+      }
+#pragma unroll
+      for (int x = 0; x < 8; ++x) {
+        k_lo += __popcll(__ballot(ch[x] < chunk));
+        kappa_hi += __popcll(__ballot(ch[x] <= chunk));
+      }
+    }
+    if (k_lo > kappa_hi) continue;  // no key tile of this unit's rows in this chunk (uniform)
     const int qt = qt0 + t4;
     const bool active = qt < n_qt;
-    const int last_qt = min(qt0 + DQ_QT, n_qt) - 1;
-    const int kappa_hi = last_qt / 2;
     const int q_rel = QT * qt + qrow;
     const bool row_valid = q_rel < L;
+    // the wave's rows (one 64-query tile, whose last key tile is qt / 2) take part in this chunk
+    // when that tile is at or after k_lo, and are complete after it when it is at or before
+    // kappa_hi (the unit's last key tile in this chunk)
+    const bool w_on = active && row_valid && qt / 2 >= k_lo;
+    const bool w_final = qt / 2 <= kappa_hi;
     int pi = 0;
     if (row_valid) pi = p.pi[(int64_t)h * p.T + doc_start + q_rel];
     const float up = exp2i(pi);
+    uint16_t* const row = p.dq + (int64_t)(doc_start + q_rel) * p.dqst + (int64_t)h * p.dqsh;
 
+    // the FP16 sums: from +0, or as an earlier chunk left them (kept in the dQ output rows)
     h2 acc16[NDB][8];
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int j = 0; j < 8; ++j) acc16[db][j] = h2{0, 0};
+    if (w_on && k_lo > 0) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint2 w = *reinterpret_cast<const uint2*>(row + 32 * db + 8 * j + 4 * hh);
+          acc16[db][2 * j] = __builtin_bit_cast(h2, w.x);
+          acc16[db][2 * j + 1] = __builtin_bit_cast(h2, w.y);
+        }
+    }
 
     // Key tile kappa's operands go global -> registers two tiles ahead and registers -> LDS one
     // tile ahead (two register sets, two LDS buffers), so each load has a whole tile's compute
@@ -814,28 +848,32 @@ __global__ __launch_bounds__(DQ_THREADS, 2) void dq_kernel(BwdParams p) {  // tw
     // one tile: loads of kappa + 2 into `spare`, compute kappa, `next` (kappa + 1) into LDS.  The
     // loads are issued on every tile (the last two re-read tile kappa_hi, unused) so that the
     // count of loads in flight does not depend on the path.
+    // The store offset of the tile loaded next (kappa + 2) is read one tile earlier, so the loads'
+    // addresses never wait for it.
+    int64_t off_n = 0;
     auto tile = [&](int kappa, DqRegs<D>& next, DqRegs<D>& spare) __attribute__((always_inline)) {
-      dq_load<D>(spare, p, doc_start, L, n_qt, base, qt0, g, h, min(kappa + 2, kappa_hi));
+      dq_load<D>(spare, p, doc_start, L, n_qt, off_n, qt0, g, h, min(kappa + 2, kappa_hi));
+      off_n = p.kv_off[tb + min(kappa + 3, kappa_hi)];
       compute(kappa);
       if (kappa + 1 <= kappa_hi) dq_store<D>(next, sm, (kappa + 1) & 1);
       lds_barrier();
     };
     DqRegs<D> ra, rb;
     lds_barrier();  // the previous unit no longer reads LDS
-    dq_load<D>(ra, p, doc_start, L, n_qt, base, qt0, g, h, 0);
-    dq_load<D>(rb, p, doc_start, L, n_qt, base, qt0, g, h, min(1, kappa_hi));
-    dq_store<D>(ra, sm, 0);
+    dq_load<D>(ra, p, doc_start, L, n_qt, p.kv_off[tb + k_lo], qt0, g, h, k_lo);
+    dq_load<D>(rb, p, doc_start, L, n_qt, p.kv_off[tb + min(k_lo + 1, kappa_hi)], qt0, g, h, min(k_lo + 1, kappa_hi));
+    off_n = p.kv_off[tb + min(k_lo + 2, kappa_hi)];
+    dq_store<D>(ra, sm, k_lo & 1);
     lds_barrier();
-    for (int kappa = 0;; kappa += 2) {  // two tiles per trip: the register sets trade roles
+    for (int kappa = k_lo;; kappa += 2) {  // two tiles per trip: the register sets trade roles
       tile(kappa, rb, ra);
       if (kappa + 1 > kappa_hi) break;
       tile(kappa + 1, ra, rb);
       if (kappa + 2 > kappa_hi) break;
     }
 
-    if (active && row_valid) {
+    if (w_on && w_final) {
       const float down = exp2i(-pi) * p.softmax_scale;
-      uint16_t* row = p.dq + (int64_t)(doc_start + q_rel) * p.dqst + (int64_t)h * p.dqsh;
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -844,6 +882,16 @@ __global__ __launch_bounds__(DQ_THREADS, 2) void dq_kernel(BwdParams p) {  // tw
           uint2 w;
           w.x = pack_bf16((float)lo[0] * down, (float)lo[1] * down);
           w.y = pack_bf16((float)hi2[0] * down, (float)hi2[1] * down);
+          *reinterpret_cast<uint2*>(row + 32 * db + 8 * j + 4 * hh) = w;
+        }
+    } else if (w_on) {  // rows continued in a later chunk: the FP16 sums wait in the dQ rows
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          uint2 w;
+          w.x = __builtin_bit_cast(uint32_t, acc16[db][2 * j]);
+          w.y = __builtin_bit_cast(uint32_t, acc16[db][2 * j + 1]);
           *reinterpret_cast<uint2*>(row + 32 * db + 8 * j + 4 * hh) = w;
         }
     }
@@ -863,38 +911,135 @@ __device__ __forceinline__ Seg seg_op(Seg a, Seg b) {
   return Seg{a.f | b.f, b.f ? b.v : max(a.v, b.v), b.f ? b.k : max(a.k, b.k)};
 }
 
-// Stored dShat blocks of a document of length L (none with a single key tile).
-__device__ __forceinline__ int64_t doc_blocks(int L) {
-  const int64_t n_kt = (L + KV_TILE - 1) / KV_TILE, n_qt = (L + QT - 1) / QT;
-  return n_kt >= 2 ? n_kt * n_qt - n_kt * (n_kt - 1) : 0;
+// Stored dShat blocks (per query head) of the backward item (document of length L, key tile
+// kappa): one per 64-query tile from the key tile's diagonal to the document end; none for a
+// document of a single key tile (its dQ is formed in the key-tile pass).
+__device__ __forceinline__ int64_t item_blocks(int L, int kappa) {
+  return L > KV_TILE ? (int64_t)((L + QT - 1) / QT - 2 * kappa) : 0;
 }
 
-__device__ void layout_ds_store(const BwdParams& p) {
-  __shared__ int64_t part[PRO_THREADS];
+// Inclusive scan of part[0 .. PRO_THREADS) in place (all threads take part).
+__device__ __forceinline__ void block_scan(int64_t* part) {
   const int tid = threadIdx.x;
-  const int nd = p.n_docs;
-  const int per = (nd + PRO_THREADS - 1) / PRO_THREADS;
-  const int lo = min(nd, tid * per), hi = min(nd, lo + per);
-  int64_t sum = 0;
-  for (int k = lo; k < hi; ++k) sum += doc_blocks(p.cu[k + 1] - p.cu[k]);
-  part[tid] = sum;
-  __syncthreads();
-  for (int off = 1; off < PRO_THREADS; off <<= 1) {  // inclusive scan
+  for (int off = 1; off < PRO_THREADS; off <<= 1) {
     const int64_t add = tid >= off ? part[tid - off] : 0;
     __syncthreads();
     part[tid] += add;
     __syncthreads();
   }
-  int64_t run = part[tid] - sum;
-  for (int k = lo; k < hi; ++k) {
-    p.doc_base[k] = run;
-    run += doc_blocks(p.cu[k + 1] - p.cu[k]);
+}
+
+// Layout of the key-tile chunks (one workgroup).
+//  1. tile_base: exclusive prefix sum over the documents of their key tiles (the row of each
+//     document in the (document, key tile) tables);
+//  2. over the backward list (sorted by descending cost, so the key tiles of one document appear
+//     in ascending order): each item's stored blocks and their exclusive prefix P(u); item u
+//     belongs to the chunk of its last block, floor(max(P(u) + blocks(u) - 1, 0) / chunk_cap),
+//     so a chunk holds fewer than chunk_cap + (largest item) blocks and consecutive items differ
+//     by at most one chunk; chunk_start / chunk_first record each chunk's first item and prefix;
+//  3. each item's chunk and its first block within the chunk's store, P(u) - chunk_first, go into
+//     the (document, key tile) tables.
+// Chunks run in list order, so every query row still meets its key tiles in ascending order and
+// the dQ sums are the same as with one chunk.
+__device__ void layout_chunks(const BwdParams& p) {
+  __shared__ int64_t part[PRO_THREADS];
+  const int tid = threadIdx.x;
+  {
+    const int nd = p.n_docs;
+    const int per = (nd + PRO_THREADS - 1) / PRO_THREADS;
+    const int lo = min(nd, tid * per), hi = min(nd, lo + per);
+    int64_t sum = 0;
+    for (int k = lo; k < hi; ++k) sum += (p.cu[k + 1] - p.cu[k] + KV_TILE - 1) / KV_TILE;
+    part[tid] = sum;
+    __syncthreads();
+    block_scan(part);
+    int64_t run = part[tid] - sum;
+    for (int k = lo; k < hi; ++k) {
+      p.tile_base[k] = (int32_t)run;
+      run += (p.cu[k + 1] - p.cu[k] + KV_TILE - 1) / KV_TILE;
+    }
+    if (tid == PRO_THREADS - 1) p.tile_base[nd] = (int32_t)part[tid];
+    __syncthreads();
   }
-  if (tid == PRO_THREADS - 1) {
-    const int64_t total = part[tid];
-    p.doc_base[nd] = total;
-    *p.status = (total * p.Hq > p.ds_capacity) ? 2 : 0;
+  const int n_items = p.list[0];
+  const int4* items = reinterpret_cast<const int4*>(p.list + 4);
+  auto blocks_of = [&](int u) {
+    const int4 it = items[u];
+    return item_blocks(p.cu[it.x + 1] - p.cu[it.x], it.y);
+  };
+  auto chunk_of = [&](int64_t P, int64_t b) {
+    const int64_t last = P + b - 1;
+    return (int)(last > 0 ? last / p.chunk_cap : 0);
+  };
+  const int per = (n_items + PRO_THREADS - 1) / PRO_THREADS;
+  const int lo = min(n_items, tid * per), hi = min(n_items, lo + per);
+  int64_t sum = 0;
+  for (int u = lo; u < hi; ++u) sum += blocks_of(u);
+  part[tid] = sum;
+  __syncthreads();
+  block_scan(part);
+  const int64_t base = part[tid] - sum;  // prefix of item lo
+  __shared__ int any_bad;
+  if (tid == 0) any_bad = 0;
+  __syncthreads();
+  int bad = 0;
+  {
+    int64_t P = base;
+    int prev = -1;
+    if (lo > 0 && lo < hi) {
+      const int64_t bp = blocks_of(lo - 1);
+      prev = chunk_of(P - bp, bp);
+    }
+    for (int u = lo; u < hi; ++u) {
+      const int64_t b = blocks_of(u);
+      const int c = chunk_of(P, b);
+      if (c >= p.max_chunks) {  // more blocks than any documents of T tokens have: bad cu_seqlens
+        bad = 1;
+        break;
+      }
+      if (c != prev) {
+        p.chunk_start[c] = u;
+        p.chunk_first[c] = P;
+      }
+      if (u == n_items - 1) {  // the last item: the chunk count, and empty chunks start at the end
+        p.status[1] = c + 1;
+        for (int x = c + 1; x <= p.max_chunks; ++x) p.chunk_start[x] = n_items;
+      }
+      prev = c;
+      P += b;
+    }
   }
+  if (n_items == 0 && tid == 0) {
+    p.status[1] = 0;
+    for (int x = 0; x <= p.max_chunks; ++x) p.chunk_start[x] = 0;
+  }
+  {
+    // table rows of this thread's items (documents longer than the tables allow: bad cu_seqlens)
+    for (int u = lo; u < hi && !bad; ++u) {
+      const int4 it = items[u];
+      const int x = p.tile_base[it.x] + it.y;
+      if (x < 0 || x >= p.n_tab) bad = 1;
+    }
+    if (bad) any_bad = 1;
+  }
+  __syncthreads();  // chunk_first written, any_bad settled
+  if (any_bad) {
+    if (tid == 0) p.status[0] = 3;  // every later kernel of the backward exits
+    return;
+  }
+  {
+    int64_t P = base;
+    for (int u = lo; u < hi; ++u) {
+      const int64_t b = blocks_of(u);
+      const int c = chunk_of(P, b);
+      const int4 it = items[u];
+      const int x = p.tile_base[it.x] + it.y;
+      p.kv_chunk[x] = c;
+      p.kv_off[x] = P - p.chunk_first[c];
+      P += b;
+    }
+  }
+  if (tid == 0) p.status[0] = 0;
 }
 
 template <int D>
@@ -906,7 +1051,7 @@ __global__ __launch_bounds__(PRO_THREADS) void bwd_prologue(BwdParams p) {
   __shared__ Seg carry_sh;
 
   if ((int)blockIdx.x == p.Hq) {
-    layout_ds_store(p);
+    layout_chunks(p);
     return;
   }
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -922,9 +1067,9 @@ __global__ __launch_bounds__(PRO_THREADS) void bwd_prologue(BwdParams p) {
 
   // zero rows outside every document
   {
-    const int n_out = c_lo + (T - c_hi);
-    for (int x = tid; x < n_out * D; x += PRO_THREADS) {
-      const int r = x / D, dd = x % D;
+    const int64_t n_out = (int64_t)c_lo + (T - c_hi);
+    for (int64_t x = tid; x < n_out * D; x += PRO_THREADS) {
+      const int r = (int)(x / D), dd = (int)(x % D);
       const int t = r < c_lo ? r : c_hi + (r - c_lo);
       p.dq[(int64_t)t * p.dqst + (int64_t)h * p.dqsh + dd] = 0;
       if (h % grp == 0) {
@@ -1022,14 +1167,20 @@ __global__ __launch_bounds__(PRO_THREADS) void bwd_prologue(BwdParams p) {
 }  // namespace
 
 hipError_t launch_bwd(const BwdParams& p, int d, int grid, hipStream_t s) {
-  if (d == 128) {
-    hipLaunchKernelGGL(bwd_prologue<128>, dim3(p.Hq + 1), dim3(PRO_THREADS), 0, s, p);
-    hipLaunchKernelGGL(bwd_kernel<128>, dim3(grid), dim3(BWD_THREADS), 0, s, p);
-    hipLaunchKernelGGL(dq_kernel<128>, dim3(2 * grid), dim3(DQ_THREADS), 0, s, p);
-  } else {
-    hipLaunchKernelGGL(bwd_prologue<64>, dim3(p.Hq + 1), dim3(PRO_THREADS), 0, s, p);
-    hipLaunchKernelGGL(bwd_kernel<64>, dim3(grid), dim3(BWD_THREADS), 0, s, p);
-    hipLaunchKernelGGL(dq_kernel<64>, dim3(2 * grid), dim3(DQ_THREADS), 0, s, p);
+  // the prologue lays out the chunks; then each chunk's key-tile pass fills the store and its
+  // dQ pass consumes it (stream order keeps the two apart and the chunks in sequence)
+  if (d == 128) hipLaunchKernelGGL(bwd_prologue<128>, dim3(p.Hq + 1), dim3(PRO_THREADS), 0, s, p);
+  else hipLaunchKernelGGL(bwd_prologue<64>, dim3(p.Hq + 1), dim3(PRO_THREADS), 0, s, p);
+  for (int c = 0; c < p.max_chunks; ++c) {
+    BwdParams q = p;
+    q.chunk = c;
+    if (d == 128) {
+      hipLaunchKernelGGL(bwd_kernel<128>, dim3(grid), dim3(BWD_THREADS), 0, s, q);
+      hipLaunchKernelGGL(dq_kernel<128>, dim3(2 * grid), dim3(DQ_THREADS), 0, s, q);
+    } else {
+      hipLaunchKernelGGL(bwd_kernel<64>, dim3(grid), dim3(BWD_THREADS), 0, s, q);
+      hipLaunchKernelGGL(dq_kernel<64>, dim3(2 * grid), dim3(DQ_THREADS), 0, s, q);
+    }
   }
   return hipGetLastError();
 }

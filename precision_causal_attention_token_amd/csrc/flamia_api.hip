@@ -3,6 +3,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "../../include/flamia.h"
 #include "kernels.h"
 #ifdef FLAMIA_DEBUG_DUMP
@@ -52,19 +54,45 @@ int num_cus() {
 }  // namespace
 
 namespace {
-// Backward workspace: status word, pi [Hq, T], per-document block offsets, then the dShat store
-// (per (block, query head): 8 KiB of codes, then 8 exponent bytes padded to a 128-byte line, so
-// every block starts on a cache line).
+// Backward workspace: a 256-byte header (status, chunk count), pi [Hq, T], the chunk layout
+// tables, then the dShat store (per (block, query head): 8 KiB of codes, then 8 exponent bytes
+// padded to a 128-byte line, so every block starts on a cache line).
 constexpr size_t DS_BLOCK_BYTES = 128 * 64 + 128;
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
-size_t bwd_fixed_bytes(int32_t T, int32_t Hq, int32_t n_docs) {
-  return 256 + align256((size_t)T * Hq * 2) + align256(((size_t)n_docs + 1) * 8);
+// (document, key tile) table entries: at most ceil(T / 128) + n_docs tiles.
+int64_t n_tiles(int32_t n_docs, int32_t T) { return ((int64_t)T + 127) / 128 + n_docs; }
+// entries of the per-chunk tables (a bound on the chunk count + 2)
+int64_t n_chunk_entries(int32_t T) { return ((int64_t)T + 127) / 128 + 8; }
+struct BwdLayout {
+  size_t pi, tile_base, kv_chunk, kv_off, chunk_start, chunk_first, store;  // byte offsets
+};
+BwdLayout bwd_layout(int32_t n_docs, int32_t T, int32_t Hq) {
+  BwdLayout l{};
+  size_t off = 256;
+  l.pi = off;          off += align256((size_t)T * Hq * 2);
+  l.tile_base = off;   off += align256(((size_t)n_docs + 1) * 4);
+  l.kv_chunk = off;    off += align256((size_t)n_tiles(n_docs, T) * 4);
+  l.kv_off = off;      off += align256((size_t)n_tiles(n_docs, T) * 8);
+  l.chunk_start = off; off += align256((size_t)n_chunk_entries(T) * 4);
+  l.chunk_first = off; off += align256((size_t)n_chunk_entries(T) * 8);
+  l.store = off;
+  return l;
 }
-// Stored dShat blocks of a document of length L: one per (128-key tile kappa, 64-query tile
-// qt >= 2 kappa), none when the document has a single key tile.
+// Stored blocks (per query head) of the largest single backward item: the query tiles of a
+// T-token document.
+int64_t max_item_blocks(int32_t T) { return std::max<int64_t>(1, ((int64_t)T + 63) / 64); }
+// Stored blocks of a document of length L: one per (128-key tile kappa, 64-query tile qt >= 2 kappa),
+// none when the document has a single key tile.
 int64_t doc_blocks(int64_t L) {
   const int64_t n_kt = (L + 127) / 128, n_qt = (L + 63) / 64;
   return n_kt >= 2 ? n_kt * n_qt - n_kt * (n_kt - 1) : 0;
+}
+// An upper bound of the stored blocks of any documents of total length T: a document of length L
+// in (128 m, 128 (m + 1)] stores at most (m + 1)(m + 2) < (L / 128)(L / 128 + 3) + 2 blocks, at
+// most T / 129 documents store any, and sum L^2 <= T^2.
+int64_t worst_blocks(int32_t T) {
+  const int64_t t = T;
+  return (t * t) / 16384 + 5 * t / 128 + 3;
 }
 }  // namespace
 
@@ -172,11 +200,22 @@ flamia_status flamia_fwd(const flamia_fwd_args* a, void* stream) {
 }
 
 
-size_t flamia_bwd_workspace_bytes(const int32_t* cu_seqlens_host, int32_t n_docs, int32_t T, int32_t Hq) {
-  if (T < 0 || Hq < 0 || n_docs < 0 || (n_docs > 0 && !cu_seqlens_host)) return 0;
+size_t flamia_bwd_workspace_bytes(int32_t n_docs, int32_t T, int32_t Hq, int32_t d, size_t store_budget) {
+  if (T < 0 || Hq < 1 || n_docs < 0 || (d != 64 && d != 128)) return 0;
+  const int64_t lo = 2 * max_item_blocks(T);                      // the smallest store accepted
+  const int64_t hi = worst_blocks(T) + max_item_blocks(T);        // one chunk for any documents
+  const int64_t want = (int64_t)(store_budget / ((size_t)Hq * DS_BLOCK_BYTES));
+  const int64_t blocks = std::max(lo, std::min(want, hi));
+  return bwd_layout(n_docs, T, Hq).store + (size_t)blocks * Hq * DS_BLOCK_BYTES;
+}
+
+size_t flamia_bwd_workspace_bytes_for(const int32_t* cu_seqlens_host, int32_t n_docs, int32_t T, int32_t Hq,
+                                      int32_t d) {
+  if (T < 0 || Hq < 1 || n_docs < 0 || (n_docs > 0 && !cu_seqlens_host) || (d != 64 && d != 128)) return 0;
   int64_t blocks = 0;
   for (int32_t k = 0; k < n_docs; ++k) blocks += doc_blocks((int64_t)cu_seqlens_host[k + 1] - cu_seqlens_host[k]);
-  return bwd_fixed_bytes(T, Hq, n_docs) + (size_t)blocks * Hq * DS_BLOCK_BYTES;
+  const int64_t store = std::max<int64_t>(blocks, max_item_blocks(T)) + max_item_blocks(T);
+  return bwd_layout(n_docs, T, Hq).store + (size_t)store * Hq * DS_BLOCK_BYTES;
 }
 
 flamia_status flamia_bwd(const flamia_bwd_args* a, void* stream) {
@@ -188,8 +227,7 @@ flamia_status flamia_bwd(const flamia_bwd_args* a, void* stream) {
   if (a->d != 64 && a->d != 128) return FLAMIA_ERR_UNSUPPORTED;
   if (a->Hq % a->Hkv) return FLAMIA_ERR_UNSUPPORTED;
   if (a->T > FLAMIA_MAX_T) return FLAMIA_ERR_UNSUPPORTED;
-  const size_t fixed = bwd_fixed_bytes(a->T, a->Hq, a->n_docs);
-  if (a->workspace_bytes < fixed) return FLAMIA_ERR_WORKSPACE;
+  if (a->workspace_bytes < flamia_bwd_workspace_bytes(a->n_docs, a->T, a->Hq, a->d, 0)) return FLAMIA_ERR_WORKSPACE;
   const int64_t st[6] = {a->dq_stride_t, a->dq_stride_h, a->dk_stride_t, a->dk_stride_h, a->dv_stride_t, a->dv_stride_h};
   for (int i = 0; i < 6; ++i)
     if (st[i] < 0 || (st[i] % 4)) return FLAMIA_ERR_SHAPE;
@@ -215,16 +253,26 @@ flamia_status flamia_bwd(const flamia_bwd_args* a, void* stream) {
   p.dkst = a->dk_stride_t; p.dksh = a->dk_stride_h;
   p.dvst = a->dv_stride_t; p.dvsh = a->dv_stride_h;
   uint8_t* ws = static_cast<uint8_t*>(a->workspace);
-  size_t off = 0;
+  const BwdLayout lay = bwd_layout(a->n_docs, a->T, a->Hq);
   p.status = reinterpret_cast<int32_t*>(ws);
-  off += 256;
-  p.pi = reinterpret_cast<int16_t*>(ws + off);
-  off += align256((size_t)a->T * a->Hq * 2);
-  p.doc_base = reinterpret_cast<int64_t*>(ws + off);
-  off += align256(((size_t)a->n_docs + 1) * 8);
-  const size_t cap = (a->workspace_bytes - off) / DS_BLOCK_BYTES;
-  p.ds_store = ws + off;
-  p.ds_capacity = (int64_t)cap;
+  p.pi = reinterpret_cast<int16_t*>(ws + lay.pi);
+  p.tile_base = reinterpret_cast<int32_t*>(ws + lay.tile_base);
+  p.kv_chunk = reinterpret_cast<int32_t*>(ws + lay.kv_chunk);
+  p.kv_off = reinterpret_cast<int64_t*>(ws + lay.kv_off);
+  p.chunk_start = reinterpret_cast<int32_t*>(ws + lay.chunk_start);
+  p.chunk_first = reinterpret_cast<int64_t*>(ws + lay.chunk_first);
+  p.ds_store = ws + lay.store;
+  // Chunks: the store holds cap blocks per query head; a chunk spans chunk_cap = cap - (largest
+  // item) blocks of last-block positions, so it never overflows the store; the launches cover
+  // the most chunks any documents of total length T could need (those past the laid-out count
+  // exit at once).
+  const int64_t cap = (int64_t)((a->workspace_bytes - lay.store) / DS_BLOCK_BYTES) / a->Hq;
+  p.chunk_cap = cap - max_item_blocks(a->T);
+  if (p.chunk_cap < max_item_blocks(a->T)) return FLAMIA_ERR_WORKSPACE;
+  const int64_t max_chunks = (worst_blocks(a->T) - 1) / p.chunk_cap + 1;
+  if (max_chunks + 2 > n_chunk_entries(a->T)) return FLAMIA_ERR_WORKSPACE;
+  p.max_chunks = (int32_t)max_chunks;
+  p.n_tab = (int32_t)n_tiles(a->n_docs, a->T);
   p.pi_out = a->dq_exp_out;
   p.causal = a->causal_dq_scale ? 1 : 0;
 #ifdef FLAMIA_DEBUG_DUMP

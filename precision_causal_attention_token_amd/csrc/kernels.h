@@ -85,12 +85,21 @@ struct BwdParams {
   const int32_t* fwd_list;  // forward list (256-query items), drives the dQ kernel
   uint16_t *dq, *dk, *dv;
   int64_t dqst, dqsh, dkst, dksh, dvst, dvsh;
-  int32_t* status;          // workspace: 0, or 2 when the dShat store does not fit
+  int32_t* status;          // workspace header: [0] status (0 once laid out, 3 when cu_seqlens do
+                            // not fit the sizes the host gave), [1] key-tile chunks
   int16_t* pi;              // workspace: [Hq, T]
-  int64_t* doc_base;        // workspace: first stored dShat block of each document, [n_docs + 1]
-  uint8_t* ds_store;        // workspace: dShat blocks, per (block, query head) 8 KiB of codes and
-                            // 8 exponent bytes, 8320 bytes apart
-  int64_t ds_capacity;      // (block, query head) pairs that fit
+  int32_t* tile_base;       // workspace: first entry of each document in the key-tile tables, [n_docs + 1]
+  int32_t* kv_chunk;        // workspace: chunk of each (document, key tile), [tiles]
+  int64_t* kv_off;          // workspace: its first dShat block within the chunk's store, [tiles]
+  int32_t* chunk_start;     // workspace: first backward-list item of each chunk, [tiles + 2]
+  int64_t* chunk_first;     // workspace: block prefix of each chunk's first item, [tiles + 2]
+  uint8_t* ds_store;        // workspace: dShat blocks of the current chunk, per (block, query head)
+                            // 8 KiB of codes and 8 exponent bytes, 8320 bytes apart
+  int64_t chunk_cap;        // a chunk holds the items whose last block (per query head) falls in
+                            // one span of chunk_cap blocks; with the largest item it fits the store
+  int32_t max_chunks;       // chunk launches of the call (chunks past the laid-out count exit)
+  int32_t n_tab;            // entries of the (document, key tile) tables
+  int32_t chunk;            // the chunk a launch works on
   int16_t* pi_out;          // optional copy of pi
   int32_t causal;
 #ifdef FLAMIA_DEBUG_DUMP

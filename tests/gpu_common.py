@@ -103,10 +103,12 @@ DUMP_F32 = ("fwd_s", "fwd_m", "bwd_s", "bwd_dp")
 DUMP_U8 = ("fwd_p", "bwd_p", "bwd_ps", "bwd_ds", "bwd_dss")
 
 
-def gpu_call(q, k, v, do, cu, causal_dq=False, softmax_scale=None, window=None):
+def gpu_call(q, k, v, do, cu, causal_dq=False, softmax_scale=None, window=None, store_budget=None):
     """Full training call on the GPU through the C ABI; returns numpy arrays (BF16 outputs as
     bit patterns).  With `window` (row/key/head bounds) the call runs the debug variant and the
-    result also holds its per-pair dumps under "dumps" ([heads][rows][keys])."""
+    result also holds its per-pair dumps under "dumps" ([heads][rows][keys]).  store_budget: the
+    backward's dShat store (default: the binding's default; 0: the smallest accepted, many
+    chunks); the key-tile chunks run are returned under "chunks"."""
     dev = torch.device("cuda:0")
     cu_d = torch.as_tensor(np.asarray(cu, np.int32)).to(dev)
     T = q.shape[0]
@@ -128,20 +130,23 @@ def gpu_call(q, k, v, do, cu, causal_dq=False, softmax_scale=None, window=None):
             qz, kz, vz = fl.quantize([qd, kd, vd], cu_d)
             o, lse = fl.fwd(qz, kz, vz, cu_d, lists.fwd, softmax_scale)
             dc, dsc, D = fl.quantize_do(dod, o, cu_d)
-            Hq = q.shape[1]
-            ws = torch.empty(fl.bwd_workspace_bytes(cu, T, Hq), dtype=torch.uint8, device=dev)
+            Hq, d = q.shape[1], q.shape[2]
+            budget = fl.DEFAULT_STORE_BYTES if store_budget is None else store_budget
+            ws = torch.empty(fl.bwd_workspace_bytes(len(cu) - 1, T, Hq, d, budget), dtype=torch.uint8, device=dev)
             ws.fill_(0xA5)  # the workspace may hold anything on entry
             dq, dk, dv, pi = fl.bwd(qz, kz, vz, (dc, dsc), lse, D, cu_d, lists, softmax_scale, causal_dq,
                                     want_pi=True, workspace=ws)
             torch.cuda.synchronize()
-            assert fl.bwd_status(ws) == 0, 'backward workspace status'
+            status, chunks = fl.bwd_status(ws)
+            assert status == 0, 'backward workspace status'
         finally:
             if window is not None:
                 lib.flamia_debug_set_dump(None)
     b = lambda t: t.cpu().view(torch.int16).numpy().view(np.uint16)
     n = lambda t: t.cpu().numpy()
     out = dict(q=n(qz[0]), sq=n(qz[1]), k=n(kz[0]), sk=n(kz[1]), v=n(vz[0]), sv=n(vz[1]),
-               do=n(dc), sdo=n(dsc), D=n(D), o=b(o), lse=n(lse), dq=b(dq), dk=b(dk), dv=b(dv), pi=n(pi))
+               do=n(dc), sdo=n(dsc), D=n(D), o=b(o), lse=n(lse), dq=b(dq), dk=b(dk), dv=b(dv), pi=n(pi),
+               chunks=chunks)
     if bufs is not None:
         out["dumps"] = {k_: n(t) for k_, t in bufs.items()}
         out["window"] = dict(window)

@@ -42,15 +42,26 @@ def test_status_strings(lib):
 def test_size_queries(lib):
     assert lib.flamia_worklist_bytes(3, 1000, 0) == 16 + 16 * (8 + 3)
     assert lib.flamia_worklist_bytes(-1, 10, 0) == 0
-    T, Hq = 1000, 4
+    T, Hq, d = 1000, 4, 64
+    blk = 8192 + 128
+    # the smallest workspace depends on the sizes only: tables plus twice the largest key tile
+    lo = lib.flamia_bwd_workspace_bytes(4, T, Hq, d, 0)
+    assert lo >= 256 + T * Hq * 2 + 2 * ((T + 63) // 64) * Hq * blk
+    assert lib.flamia_bwd_workspace_bytes(4, T, Hq, d, 10 * Hq * blk) == lo           # clamped up
+    mid = lib.flamia_bwd_workspace_bytes(4, T, Hq, d, 100 * Hq * blk)
+    assert mid - lo == (100 - 2 * 16) * Hq * blk                                      # budget honoured
+    hi = lib.flamia_bwd_workspace_bytes(4, T, Hq, d, 1 << 40)
+    worst = (T * T) // 16384 + 5 * T // 128 + 3 + (T + 63) // 64
+    assert hi - lo == (worst - 2 * 16) * Hq * blk                                     # clamped down
+    assert lib.flamia_bwd_workspace_bytes(4, T, Hq, 96, 0) == 0                       # bad d
+    # one chunk for known lengths: the call's stored blocks plus the largest key tile
     cu = np.array([0, 100, 100, 612, 1000], np.int32)       # lengths 100, 0, 512, 388
     blocks = 0 + 0 + (4 * 8 - 4 * 3) + (4 * 7 - 4 * 3)     # n_kt n_qt - n_kt (n_kt - 1), 1-tile docs: 0
-    got = lib.flamia_bwd_workspace_bytes(cu.ctypes.data_as(ctypes.c_void_p), 4, T, Hq)
-    fixed = lib.flamia_bwd_workspace_bytes(None, 0, T, Hq)
-    assert fixed >= 256 + T * Hq * 2
-    assert got - fixed == blocks * Hq * (8192 + 128)             # block offsets fit the same 256 bytes
-    assert lib.flamia_bwd_workspace_bytes(None, 3, T, Hq) == 0    # host cu_seqlens required
-    assert fl.bwd_workspace_bytes(cu, T, Hq) == got
+    got = lib.flamia_bwd_workspace_bytes_for(cu.ctypes.data_as(ctypes.c_void_p), 4, T, Hq, d)
+    assert got - (lo - 2 * 16 * Hq * blk) == (blocks + 16) * Hq * blk
+    assert lib.flamia_bwd_workspace_bytes_for(None, 3, T, Hq, d) == 0                  # host lengths required
+    assert fl.bwd_workspace_bytes_for(cu, T, Hq, d) == got
+    assert fl.bwd_workspace_bytes(4, T, Hq, d, 0) == lo
 
 
 def test_host_validation_errors(lib):
@@ -76,3 +87,5 @@ def test_host_validation_errors(lib):
     b.T, b.Hq, b.Hkv, b.d, b.n_docs = 100, 4, 2, 64, 1
     b.workspace_bytes = 16
     assert lib.flamia_bwd(ctypes.byref(b), None) == 4          # workspace too small
+    b.workspace_bytes = lib.flamia_bwd_workspace_bytes(1, 100, 4, 64, 0) - 1
+    assert lib.flamia_bwd(ctypes.byref(b), None) == 4          # one byte short of the smallest

@@ -103,3 +103,32 @@ def test_one_token_documents_full_size(orc):
     a = shp.T // 2
     win = dict(row_lo=a, row_hi=a + 1024, key_lo=a, key_hi=a + 1024, head_lo=0, head_hi=shp.Hq)
     stage_and_chain(orc, q, k, v, do, cu, win, release=g, zero_in_exact=("dQ", "dK"))
+
+
+@pytest.mark.parametrize("causal_dq", [False, True])
+def test_chunked_backward_bit_identical(causal_dq):
+    """A backward whose dShat store holds only two of the largest key tiles (the smallest
+    workspace: many chunks, FP16 dQ sums carried between them in the dQ rows) gives the same
+    bits as one chunk: the backward list keeps each document's key tiles in ascending order
+    across chunks, so every FP16 sum adds the same partials in the same order."""
+    T, Hq, Hkv, d = 4096, 4, 2, 128
+    cu = np.array([0, 1500, 1501, 1700, 3000, 4096], np.int32)
+    q, k, v, do = workloads.tensors(T, Hq, Hkv, d, seed=730)
+    one = gpu_call(q, k, v, do, cu, causal_dq, store_budget=1 << 40)
+    many = gpu_call(q, k, v, do, cu, causal_dq, store_budget=0)
+    say("chunked backward: %d chunk(s) vs %d chunks" % (one["chunks"], many["chunks"]))
+    assert one["chunks"] == 1 and many["chunks"] >= 4
+    for nm in ("dq", "dk", "dv", "pi"):
+        assert np.array_equal(one[nm], many[nm]), nm
+
+
+def test_chunked_backward_long_document():
+    """The 65536-token workload's documents with a 1 GiB store (several chunks, one 29368-token
+    document spread over them) against one chunk: dQ, dK, dV bit-identical."""
+    cu, shp, (q, k, v, do) = workloads.workload("long")
+    one = gpu_call(q, k, v, do, cu, False, store_budget=1 << 40)
+    many = gpu_call(q, k, v, do, cu, False, store_budget=1 << 30)
+    say("long workload: %d chunk(s) vs %d chunks" % (one["chunks"], many["chunks"]))
+    assert one["chunks"] == 1 and many["chunks"] >= 8
+    for nm in ("dq", "dk", "dv"):
+        assert np.array_equal(one[nm], many[nm]), nm
