@@ -46,7 +46,8 @@ typedef enum {
   FLAMIA_ERR_SHAPE = 2,       /* negative or inconsistent sizes, bad strides */
   FLAMIA_ERR_UNSUPPORTED = 3, /* d not in {64, 128}, Hq % Hkv != 0, T or n_docs beyond limits */
   FLAMIA_ERR_WORKSPACE = 4,   /* a caller buffer is smaller than its *_bytes query */
-  FLAMIA_ERR_HIP = 5          /* a HIP call or kernel launch failed */
+  FLAMIA_ERR_HIP = 5,         /* a HIP call or kernel launch failed */
+  FLAMIA_ERR_SCRATCH = 6      /* flamia_bwd_static: the call needs more than the static scratch */
 } flamia_status;
 
 /* Host.  Static string naming a status. */
@@ -224,6 +225,25 @@ size_t flamia_bwd_workspace_bytes_for(const int32_t* cu_seqlens_host, int32_t n_
  * flamia_bwd_workspace_bytes(n_docs, T, Hq, d, 0) (FLAMIA_ERR_WORKSPACE).  The status word (first
  * int32 of the workspace) is 0 once the backward has run. */
 flamia_status flamia_bwd(const flamia_bwd_args* args, void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * Backward that allocates nothing, for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ *
+ * The same as flamia_bwd, except that args->workspace and args->workspace_bytes are ignored: the
+ * workspace is a static device array of FLAMIA_STATIC_SCRATCH_BYTES held by the library on every
+ * GPU it runs on until the process ends (its address on the current device is looked up on the
+ * first call there).  All of it becomes the backward's workspace, so calls whose smallest
+ * workspace, flamia_bwd_workspace_bytes(n_docs, T, Hq, d, 0), exceeds it are rejected with
+ * FLAMIA_ERR_SCRATCH (roughly T * Hq up to 2^17 at T = 16384, Hq = 8); larger calls need
+ * flamia_bwd.  No hipMalloc, hipFree or allocating library call is made.  The array's contents
+ * on entry do not matter (the backward writes everything it reads).  Every call on one GPU
+ * shares that GPU's array: calls that overlap in time on one GPU (other streams, other host
+ * threads) race and must be serialised by the caller.  Errors: as flamia_bwd, plus
+ * FLAMIA_ERR_SCRATCH.
+ * ------------------------------------------------------------------------------------------ */
+#define FLAMIA_STATIC_SCRATCH_BYTES (64u << 20)
+flamia_status flamia_bwd_static(const flamia_bwd_args* args, void* stream);
 
 /* Host.  Number of compute units of the current device, the persistent grid used by
  * flamia_fwd / flamia_bwd (one workgroup per compute unit). */

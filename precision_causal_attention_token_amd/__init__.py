@@ -22,7 +22,7 @@ FLAMIA_LIST_BWD = 1
 EXPORTED_SYMBOLS = (
     "flamia_status_str", "flamia_worklist_bytes", "flamia_build_worklist", "flamia_quantize",
     "flamia_fwd", "flamia_bwd", "flamia_bwd_workspace_bytes", "flamia_bwd_workspace_bytes_for",
-    "flamia_num_workers",
+    "flamia_bwd_static", "flamia_num_workers",
 )
 
 # Default dShat store of a backward whose caller passes no workspace: large enough that calls up
@@ -87,6 +87,8 @@ def load_library(path=LIB_PATH):
     lib.flamia_fwd.argtypes = [ctypes.POINTER(_FwdArgs), ctypes.c_void_p]
     lib.flamia_bwd.restype = ctypes.c_int
     lib.flamia_bwd.argtypes = [ctypes.POINTER(_BwdArgs), ctypes.c_void_p]
+    lib.flamia_bwd_static.restype = ctypes.c_int
+    lib.flamia_bwd_static.argtypes = [ctypes.POINTER(_BwdArgs), ctypes.c_void_p]
     lib.flamia_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.flamia_bwd_workspace_bytes.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                                ctypes.c_size_t]
@@ -223,11 +225,13 @@ def bwd_workspace_bytes_for(cu_seqlens_host, T, Hq, d):
 
 
 def bwd(q, k, v, do, lse, D, cu_seqlens, lists, softmax_scale=None, causal_dq_scale=False, want_pi=False,
-        workspace=None):
+        workspace=None, static_scratch=False):
     """Backward on quantised operands.  q, k, v, do are (codes, scales) pairs; lse, D f32 [Hq, T];
     lists: the micro-batch's Lists.  workspace: a uint8 CUDA tensor of at least
     bwd_workspace_bytes(n_docs, T, Hq, d, 0) bytes, or None to allocate one with the default
     store (DEFAULT_STORE_BYTES).
+    static_scratch=True calls flamia_bwd_static instead (the library's static device scratch; no
+    workspace is allocated or passed).
     Returns (dq, dk, dv) BF16, plus the prescale exponents pi int16 [Hq, T] if want_pi."""
     lib = load_library()
     n_docs = _check_cu(cu_seqlens)
@@ -238,7 +242,7 @@ def bwd(q, k, v, do, lse, D, cu_seqlens, lists, softmax_scale=None, causal_dq_sc
     dq = torch.empty((T, Hq, d), dtype=torch.bfloat16, device=dev)
     dk = torch.empty((T, Hkv, d), dtype=torch.bfloat16, device=dev)
     dv = torch.empty((T, Hkv, d), dtype=torch.bfloat16, device=dev)
-    if workspace is None:
+    if workspace is None and not static_scratch:
         workspace = torch.empty(bwd_workspace_bytes(n_docs, T, Hq, d), dtype=torch.uint8, device=dev)
     pi = torch.empty((Hq, T), dtype=torch.int16, device=dev) if want_pi else None
     a = _BwdArgs(qc.data_ptr(), kc.data_ptr(), vc.data_ptr(), dc.data_ptr(),
@@ -246,9 +250,10 @@ def bwd(q, k, v, do, lse, D, cu_seqlens, lists, softmax_scale=None, causal_dq_sc
                  T, Hq, Hkv, d, float(softmax_scale or 0.0), cu_seqlens.data_ptr(), n_docs,
                  lists.fwd.data_ptr(), lists.bwd.data_ptr(),
                  dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), dq.stride(0), dq.stride(1), dk.stride(0), dk.stride(1),
-                 dv.stride(0), dv.stride(1), workspace.data_ptr(), workspace.numel(), int(bool(causal_dq_scale)),
+                 dv.stride(0), dv.stride(1), workspace.data_ptr() if workspace is not None else None,
+                 workspace.numel() if workspace is not None else 0, int(bool(causal_dq_scale)),
                  pi.data_ptr() if pi is not None else None)
-    _check(lib.flamia_bwd(ctypes.byref(a), _stream()))
+    _check((lib.flamia_bwd_static if static_scratch else lib.flamia_bwd)(ctypes.byref(a), _stream()))
     return (dq, dk, dv, pi) if want_pi else (dq, dk, dv)
 
 

@@ -4,6 +4,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "../../include/flamia.h"
 #include "kernels.h"
@@ -106,6 +107,7 @@ const char* flamia_status_str(flamia_status s) {
     case FLAMIA_ERR_UNSUPPORTED: return "unsupported size";
     case FLAMIA_ERR_WORKSPACE: return "buffer too small";
     case FLAMIA_ERR_HIP: return "HIP error";
+    case FLAMIA_ERR_SCRATCH: return "call too large for the static scratch";
   }
   return "unknown status";
 }
@@ -280,6 +282,38 @@ flamia_status flamia_bwd(const flamia_bwd_args* a, void* stream) {
 #endif
   hipError_t e = launch_bwd(p, a->d, grid, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FLAMIA_OK : FLAMIA_ERR_HIP;
+}
+
+// ------------------------------------------------------------------------------------------
+// Backward without allocation: the workspace is a file-scope device array.  In host code the
+// array's name is only a stand-in: its device address, different on every GPU, is looked up
+// once per device with hipGetSymbolAddress and cached; kernels receive that address.
+static __device__ __align__(256) uint8_t scratch[FLAMIA_STATIC_SCRATCH_BYTES];
+
+namespace {
+constexpr int MAX_DEVICES = 64;
+std::once_flag scratch_once[MAX_DEVICES];
+void* scratch_ptr[MAX_DEVICES];
+hipError_t scratch_err[MAX_DEVICES];
+}  // namespace
+
+flamia_status flamia_bwd_static(const flamia_bwd_args* a, void* stream) {
+  if (!a) return FLAMIA_ERR_NULL;
+  if (a->T < 0 || a->Hq < 1 || a->n_docs < 0) return FLAMIA_ERR_SHAPE;
+  if (a->d != 64 && a->d != 128) return FLAMIA_ERR_UNSUPPORTED;
+  const size_t need = flamia_bwd_workspace_bytes(a->n_docs, a->T, a->Hq, a->d, 0);
+  if (need == 0) return FLAMIA_ERR_SHAPE;
+  if (need > FLAMIA_STATIC_SCRATCH_BYTES) return FLAMIA_ERR_SCRATCH;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return FLAMIA_ERR_HIP;
+  std::call_once(scratch_once[dev], [dev] {
+    scratch_err[dev] = hipGetSymbolAddress(&scratch_ptr[dev], HIP_SYMBOL(scratch));
+  });
+  if (scratch_err[dev] != hipSuccess || !scratch_ptr[dev]) return FLAMIA_ERR_HIP;
+  flamia_bwd_args b = *a;
+  b.workspace = scratch_ptr[dev];
+  b.workspace_bytes = FLAMIA_STATIC_SCRATCH_BYTES;
+  return flamia_bwd(&b, stream);
 }
 
 }  // extern "C"
