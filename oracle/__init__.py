@@ -115,7 +115,8 @@ def quantize(x_bits, cu, floor_rule=False):
 
 
 def worklist(cu, kind, n_workers):
-    """Sorted work list: int32 [n_items, 4] rows {doc, blk, cost, worker}; kind 0 = fwd, 1 = bwd."""
+    """Sorted work list: int32 [n_items, 4] rows {doc, blk, cost, worker}; kind 0 = fwd, 1 = bwd,
+    2 = non-causal fwd, 3 = non-causal bwd (every item of a document costs its key-tile count)."""
     cu = _c(cu, np.int32)
     n_docs = len(cu) - 1
     cap = int(sum((int(cu[k + 1] - cu[k]) + 127) // 128 for k in range(n_docs))) + 1
@@ -165,8 +166,9 @@ def _sel(mask, n):
 
 
 def fwd(q, sq, k, sk, v, sv, cu, softmax_scale=None, p_shift=8, exact_p=False, want_o64=False,
-        docs=None, kv_heads=None, tail_rows=0, window=None):
-    """Returns (O bits u16 [T,Hq,d], LSE f32 [Hq,T] in log2 units, O64 or None), plus (with
+        docs=None, kv_heads=None, tail_rows=0, window=None, causal=True):
+    """causal=False: every key of the row's document is visible (key tiles from the document's
+    last down to tile 0).  Returns (O bits u16 [T,Hq,d], LSE f32 [Hq,T] in log2 units, O64 or None), plus (with
     ``window``, a dict of row/key/head bounds)
     a dict of the per-pair dumps fwd_s (score accumulator), fwd_m (running maximum), fwd_p
     (E4M3 codes), [heads][rows][keys], NaN / 0xFF where not visited.  ``docs`` / ``kv_heads``
@@ -188,7 +190,8 @@ def fwd(q, sq, k, sk, v, sv, cu, softmax_scale=None, p_shift=8, exact_p=False, w
     lib().orc_fwd(_p(q), _p(sq), _p(k), _p(sk), _p(v), _p(sv), T, Hq, Hkv, d, ctypes.c_double(softmax_scale),
                   _p(cu), len(cu) - 1, int(p_shift), int(bool(exact_p)), _p(o), _p(lse),
                   _p(o64) if o64 is not None else None, _p(sd) if sd is not None else None,
-                  _p(sk_) if sk_ is not None else None, int(tail_rows), ctypes.byref(w) if w is not None else None)
+                  _p(sk_) if sk_ is not None else None, int(tail_rows), ctypes.byref(w) if w is not None else None,
+                  int(bool(causal)))
     return (o, lse, o64) + ((dumps,) if window is not None else ())
 
 
@@ -219,14 +222,17 @@ class _Dbg(ctypes.Structure):
 
 
 def bwd(q, sq, k, sk, v, sv, do, sdo, lse, D, cu, softmax_scale=None, causal_dq=False, exact=0,
-        want64=False, debug=False, docs=None, kv_heads=None, tail_blocks=0, window=None):
+        want64=False, debug=False, docs=None, kv_heads=None, tail_blocks=0, window=None, causal=True):
     """Returns dict with dq, dk, dv (u16 BF16 bits), pi (i16 [Hq,T]) and optionally the
     double-precision values (dq64, dk64, dv64) and, for single-document calls, the block
     exponents/codes of the P and dS operands (p_scale, ds_scale [Hq,nb,nb]; p_code,
     ds_code [Hq,L,L]).  tail_blocks > 0 restricts the work to the last tail_blocks 32-query
     blocks of each document: only those rows' dQ and those keys' dK, dV are complete.  With
     ``window`` (row/key/head bounds), out["dumps"] holds the per-pair bwd_dp (D - dP), bwd_p,
-    bwd_ps (Phat code, block exponent byte), bwd_ds, bwd_dss (dShat), [heads][rows][keys]."""
+    bwd_ps (Phat code, block exponent byte), bwd_ds, bwd_dss (dShat), [heads][rows][keys].
+    causal=False: every key of the row's document is visible (default dQ prescale only)."""
+    if not causal and causal_dq:
+        raise ValueError("the causal dQ prescale applies to causal attention")
     q, k, v, do = (_c(a, np.uint8) for a in (q, k, v, do))
     sq, sk, sv, sdo = (_c(a, np.uint8) for a in (sq, sk, sv, sdo))
     lse, D = _c(lse, np.float32), _c(D, np.float32)
@@ -259,11 +265,11 @@ def bwd(q, sq, k, sk, v, sv, do, sdo, lse, D, cu, softmax_scale=None, causal_dq=
                   _p(out["dq64"]) if want64 else None, _p(out["dk64"]) if want64 else None,
                   _p(out["dv64"]) if want64 else None, ctypes.byref(dbg) if dbg is not None else None,
                   _p(sd) if sd is not None else None, _p(sk_) if sk_ is not None else None,
-                  int(tail_blocks), ctypes.byref(w) if w is not None else None)
+                  int(tail_blocks), ctypes.byref(w) if w is not None else None, int(bool(causal)))
     return out
 
 
-def fwd_replay(v, sv, cu, window, S, M, P, Hq, c_scale, p_shift=8):
+def fwd_replay(v, sv, cu, window, S, M, P, Hq, c_scale, p_shift=8, causal=True):
     """Forward products from given per-pair decisions (score accumulator S, running maximum M,
     codes P, [heads][rows][keys] over ``window``).  Returns (O64 [heads][rows][d], LSE64
     [heads][rows]), NaN for rows not replayed.  c_scale = softmax_scale * log2(e) as used."""
@@ -277,11 +283,11 @@ def fwd_replay(v, sv, cu, window, S, M, P, Hq, c_scale, p_shift=8):
     lse64 = np.empty((nh, nr))
     w = _window(window, {})
     lib().orc_fwd_replay(_p(v), _p(sv), T, int(Hq), Hkv, d, ctypes.c_double(c_scale), _p(cu), len(cu) - 1,
-                         int(p_shift), ctypes.byref(w), _p(S), _p(M), _p(P), _p(o64), _p(lse64))
+                         int(p_shift), ctypes.byref(w), _p(S), _p(M), _p(P), _p(o64), _p(lse64), int(bool(causal)))
     return o64, lse64
 
 
-def bwd_replay(q, sq, k, sk, do, sdo, cu, pi, window, P, PS, DS, DSS, softmax_scale=None):
+def bwd_replay(q, sq, k, sk, do, sdo, cu, pi, window, P, PS, DS, DSS, softmax_scale=None, causal=True):
     """Backward products from given Phat / dShat codes and block exponent bytes ([heads][rows]
     [keys] over ``window``).  Returns dict dq64 [heads][rows][d] (window heads and rows), dk64,
     dv64 [Hkv][rows][d] (keys = the window's rows), NaN where not computed."""
@@ -300,5 +306,5 @@ def bwd_replay(q, sq, k, sk, do, sdo, cu, pi, window, P, PS, DS, DSS, softmax_sc
     w = _window(window, {})
     lib().orc_bwd_replay(_p(q), _p(sq), _p(k), _p(sk), _p(do), _p(sdo), T, Hq, Hkv, d,
                          ctypes.c_double(softmax_scale), _p(cu), len(cu) - 1, _p(pi), ctypes.byref(w), _p(P), _p(PS),
-                         _p(DS), _p(DSS), _p(out["dq64"]), _p(out["dk64"]), _p(out["dv64"]))
+                         _p(DS), _p(DSS), _p(out["dq64"]), _p(out["dk64"]), _p(out["dv64"]), int(bool(causal)))
     return out

@@ -244,17 +244,19 @@ int orc_worklist(const int32_t* cu, int n_docs, int kind, int n_workers, int32_t
   int32_t* tmp;
   for (k = 0; k < n_docs; ++k) {
     int L = cu[k + 1] - cu[k];
-    n += kind == 0 ? (L + 255) / 256 : (L + 127) / 128;
+    n += (kind % 2 == 0) ? (L + 255) / 256 : (L + 127) / 128;
   }
   if (n > cap) return -1;
   tmp = (int32_t*)malloc(sizeof(int32_t) * 4 * (n > 0 ? n : 1));
   n = 0;
   for (k = 0; k < n_docs; ++k) {
     int L = cu[k + 1] - cu[k], b;
-    int nb = kind == 0 ? (L + 255) / 256 : (L + 127) / 128;
+    int nb = (kind % 2 == 0) ? (L + 255) / 256 : (L + 127) / 128;
     for (b = 0; b < nb; ++b) {
       int cost;
-      if (kind == 0) {
+      if (kind >= 2) {
+        cost = (L + 127) / 128; /* non-causal: every item visits / serves all key or query tiles */
+      } else if (kind == 0) {
         int hi = 256 * (b + 1) < L ? 256 * (b + 1) : L;
         cost = (hi + 127) / 128;
       } else {
@@ -329,7 +331,7 @@ void orc_fwd(const uint8_t* q, const uint8_t* sq, const uint8_t* k, const uint8_
              const uint8_t* v, const uint8_t* sv, int T, int Hq, int Hkv, int d,
              double softmax_scale, const int32_t* cu, int n_docs, int p_shift, int exact_p,
              uint16_t* o, float* lse, double* o64, const uint8_t* sel_docs, const uint8_t* sel_kv,
-             int tail_rows, const orc_window* win) {
+             int tail_rows, const orc_window* win, int causal) {
   const int group = Hq / Hkv;
   const double c_scale = softmax_scale * 1.4426950408889634074; /* log2(e) */
   double* Qd = deq_all(q, sq, T, Hq, d);
@@ -357,11 +359,12 @@ void orc_fwd(const uint8_t* q, const uint8_t* sq, const uint8_t* k, const uint8_
     if (tail_rows > 0 && row < cu[doc + 1] - tail_rows) continue;
     for (cc = 0; cc < d; ++cc) acc[cc] = 0.0;
     {
-      int start = cu[doc], r = row - start;
-      for (kappa = r / KV_TILE; kappa >= 0; --kappa) {
+      int start = cu[doc], r = row - start, L = cu[doc + 1] - start;
+      for (kappa = (causal ? r : L - 1) / KV_TILE; kappa >= 0; --kappa) {
         int j0 = kappa * KV_TILE, j1 = (kappa + 1) * KV_TILE;
         double mt = -INFINITY, m_new, alpha, sum = 0.0;
-        if (j1 > r + 1) j1 = r + 1; /* causal: keys j <= i only */
+        if (causal && j1 > r + 1) j1 = r + 1; /* causal: keys j <= i only */
+        if (j1 > L) j1 = L;
         for (j = j0; j < j1; ++j) {
           const double* kj = Kd + ((size_t)(start + j) * Hkv + g) * d;
           double dot = 0.0;
@@ -528,7 +531,8 @@ void orc_bwd(const uint8_t* q, const uint8_t* sq, const uint8_t* k, const uint8_
              double softmax_scale, const int32_t* cu, int n_docs, int causal_dq, int exact,
              uint16_t* dq, uint16_t* dk, uint16_t* dv, int16_t* pi_out,
              double* dq64, double* dk64, double* dv64, const orc_bwd_debug* dbg,
-             const uint8_t* sel_docs, const uint8_t* sel_kv, int tail_blocks, const orc_window* win) {
+             const uint8_t* sel_docs, const uint8_t* sel_kv, int tail_blocks, const orc_window* win,
+             int causal) {
   const int group = Hq / Hkv;
   const double c_scale = softmax_scale * 1.4426950408889634074;
   int16_t* pi = (int16_t*)malloc(sizeof(int16_t) * (size_t)Hq * T + 2);
@@ -565,11 +569,12 @@ void orc_bwd(const uint8_t* q, const uint8_t* sq, const uint8_t* k, const uint8_
     for (hq = g * group; hq < (g + 1) * group; ++hq) {
       for (bq = (tail_blocks > 0 && nb > tail_blocks) ? nb - tail_blocks : 0; bq < nb; ++bq) {
         int i0 = bq * BLK, i1 = i0 + BLK < L ? i0 + BLK : L;
-        int kappa, kappa_last = (i1 - 1) / KV_TILE;
+        int kappa, kappa_last = (causal ? i1 - 1 : L - 1) / KV_TILE;
         for (z = 0; z < (size_t)BLK * d; ++z) acc16[z] = 0.0;
         for (kappa = 0; kappa <= kappa_last; ++kappa) {
           for (z = 0; z < (size_t)BLK * d; ++z) part[z] = 0.0;
-          for (bk = kappa * (KV_TILE / BLK); bk < (kappa + 1) * (KV_TILE / BLK) && bk <= bq; ++bk) {
+          for (bk = kappa * (KV_TILE / BLK); bk < (kappa + 1) * (KV_TILE / BLK) && bk < nb && (!causal || bk <= bq);
+               ++bk) {
             int j0 = bk * BLK, j1 = j0 + BLK < L ? j0 + BLK : L;
             double pmax = 0.0, dsmax = 0.0;
             int sp, sds;
@@ -577,7 +582,7 @@ void orc_bwd(const uint8_t* q, const uint8_t* sq, const uint8_t* k, const uint8_
             for (ii = i0; ii < i1; ++ii)
               for (jj = j0; jj < j1; ++jj) {
                 double dot = 0.0, dp = 0.0, p;
-                if (jj > ii) { P[ii - i0][jj - j0] = 0.0; dS[ii - i0][jj - j0] = 0.0; continue; }
+                if (causal && jj > ii) { P[ii - i0][jj - j0] = 0.0; dS[ii - i0][jj - j0] = 0.0; continue; }
                 const double* qi = Qd + ((size_t)(start + ii) * Hq + hq) * d;
                 const double* doi = dOd + ((size_t)(start + ii) * Hq + hq) * d;
                 const double* kj = Kd + ((size_t)(start + jj) * Hkv + g) * d;
@@ -598,7 +603,7 @@ void orc_bwd(const uint8_t* q, const uint8_t* sq, const uint8_t* k, const uint8_
             sds = orc_e8m0_roundup(dsmax);
             for (ii = i0; ii < i1; ++ii)
               for (jj = j0; jj < j1; ++jj) {
-                if (jj > ii) { Pc[ii - i0][jj - j0] = 0; dSc[ii - i0][jj - j0] = 0; continue; }
+                if (causal && jj > ii) { Pc[ii - i0][jj - j0] = 0; dSc[ii - i0][jj - j0] = 0; continue; }
                 Pc[ii - i0][jj - j0] = orc_e4m3_rne(ldexp(P[ii - i0][jj - j0], -sp));
                 dSc[ii - i0][jj - j0] = orc_e4m3_rne(ldexp(dS[ii - i0][jj - j0], -sds));
                 if (!(exact & 1)) P[ii - i0][jj - j0] = ldexp(orc_e4m3_decode(Pc[ii - i0][jj - j0]), sp);
@@ -606,7 +611,7 @@ void orc_bwd(const uint8_t* q, const uint8_t* sq, const uint8_t* k, const uint8_
               }
             if (win)
               for (ii = i0; ii < i1; ++ii)
-                for (jj = j0; jj < j1 && jj <= ii; ++jj) {
+                for (jj = j0; jj < j1 && (!causal || jj <= ii); ++jj) {
                   long long wi = win_index(win, hq, start + ii, start + jj);
                   if (wi < 0) continue;
                   if (win->bwd_dp) win->bwd_dp[wi] = (double)D[(size_t)hq * T + start + ii] - dPv[ii - i0][jj - j0];
@@ -626,7 +631,7 @@ void orc_bwd(const uint8_t* q, const uint8_t* sq, const uint8_t* k, const uint8_
             }
             /* the three gradient products of this block */
             for (ii = i0; ii < i1; ++ii)
-              for (jj = j0; jj < j1 && jj <= ii; ++jj) {
+              for (jj = j0; jj < j1 && (!causal || jj <= ii); ++jj) {
                 double ph = P[ii - i0][jj - j0], dsh = dS[ii - i0][jj - j0];
                 const double* qi = Qd + ((size_t)(start + ii) * Hq + hq) * d;
                 const double* doi = dOd + ((size_t)(start + ii) * Hq + hq) * d;
@@ -691,7 +696,7 @@ void orc_bwd(const uint8_t* q, const uint8_t* sq, const uint8_t* k, const uint8_
  * ---------------------------------------------------------------------------------- */
 void orc_fwd_replay(const uint8_t* v, const uint8_t* sv, int T, int Hq, int Hkv, int d, double c_scale,
                     const int32_t* cu, int n_docs, int p_shift, const orc_window* win, const double* S,
-                    const double* M, const uint8_t* P, double* o64, double* lse64) {
+                    const double* M, const uint8_t* P, double* o64, double* lse64, int causal) {
   const int group = Hq / Hkv;
   const int nh = win->head_hi - win->head_lo, nr = win->row_hi - win->row_lo;
   double* Vd = deq_all(v, sv, T, Hkv, d);
@@ -705,14 +710,15 @@ void orc_fwd_replay(const uint8_t* v, const uint8_t* sv, int T, int Hq, int Hkv,
     double* o = o64 + (size_t)task * d;
     lse64[task] = NAN;
     for (cc = 0; cc < d; ++cc) o[cc] = NAN;
-    if (doc < 0 || cu[doc] < win->key_lo || row >= win->key_hi) continue;
+    if (doc < 0 || cu[doc] < win->key_lo || (causal ? row : cu[doc + 1] - 1) >= win->key_hi) continue;
     for (cc = 0; cc < d; ++cc) acc[cc] = 0.0;
     {
-      int start = cu[doc], r = row - start;
-      for (kappa = r / KV_TILE; kappa >= 0; --kappa) {
+      int start = cu[doc], r = row - start, L = cu[doc + 1] - start;
+      for (kappa = (causal ? r : L - 1) / KV_TILE; kappa >= 0; --kappa) {
         int j0 = kappa * KV_TILE, j1 = (kappa + 1) * KV_TILE;
         double m_new, alpha, sum = 0.0;
-        if (j1 > r + 1) j1 = r + 1;
+        if (causal && j1 > r + 1) j1 = r + 1;
+        if (j1 > L) j1 = L;
         m_new = M[win_index(win, hh, row, start + j0)];
         alpha = (m == -INFINITY) ? 0.0 : exp2(m - m_new);
         for (cc = 0; cc < d; ++cc) acc[cc] *= alpha;
@@ -749,7 +755,7 @@ void orc_fwd_replay(const uint8_t* v, const uint8_t* sv, int T, int Hq, int Hkv,
 void orc_bwd_replay(const uint8_t* q, const uint8_t* sq, const uint8_t* k, const uint8_t* sk, const uint8_t* dO,
                     const uint8_t* sdo, int T, int Hq, int Hkv, int d, double softmax_scale, const int32_t* cu,
                     int n_docs, const int16_t* pi, const orc_window* win, const uint8_t* P, const uint8_t* PS,
-                    const uint8_t* DS, const uint8_t* DSS, double* dq64, double* dk64, double* dv64) {
+                    const uint8_t* DS, const uint8_t* DSS, double* dq64, double* dk64, double* dv64, int causal) {
   const int group = Hq / Hkv;
   const int nr = win->row_hi - win->row_lo;
   long long task, n_tasks = (long long)n_docs * Hkv;
@@ -766,8 +772,10 @@ void orc_bwd_replay(const uint8_t* q, const uint8_t* sq, const uint8_t* k, const
     int nb = (L + BLK - 1) / BLK;
     double *dk_acc, *dv_acc, part[BLK * 256], acc16[BLK * 256];
     if (L <= 0 || cu[doc + 1] <= win->row_lo || start >= win->row_hi) continue;
-    kv_ok = g * group >= win->head_lo && (g + 1) * group <= win->head_hi;
     bq0 = win->row_lo > start ? (win->row_lo - start) / BLK : 0;
+    /* dK, dV of a key need every row that sees it: all of them here only when the window's rows
+       start at the document start or, causally, at or before the key */
+    kv_ok = g * group >= win->head_lo && (g + 1) * group <= win->head_hi && (causal || bq0 == 0);
     dk_acc = (double*)calloc((size_t)L * d, sizeof(double));
     dv_acc = (double*)calloc((size_t)L * d, sizeof(double));
     for (hq = g * group; hq < (g + 1) * group; ++hq) {
@@ -775,14 +783,15 @@ void orc_bwd_replay(const uint8_t* q, const uint8_t* sq, const uint8_t* k, const
       if (!in_heads) continue;
       for (bq = bq0; bq < nb; ++bq) {
         int i0 = bq * BLK, i1 = i0 + BLK < L ? i0 + BLK : L;
-        int kappa, kappa_last = (i1 - 1) / KV_TILE;
+        int kappa, kappa_last = (causal ? i1 - 1 : L - 1) / KV_TILE;
         for (z = 0; z < (size_t)BLK * d; ++z) acc16[z] = 0.0;
         for (kappa = 0; kappa <= kappa_last; ++kappa) {
           for (z = 0; z < (size_t)BLK * d; ++z) part[z] = 0.0;
-          for (bk = kappa * (KV_TILE / BLK); bk < (kappa + 1) * (KV_TILE / BLK) && bk <= bq; ++bk) {
+          for (bk = kappa * (KV_TILE / BLK); bk < (kappa + 1) * (KV_TILE / BLK) && bk < nb && (!causal || bk <= bq);
+               ++bk) {
             int j0 = bk * BLK, j1 = j0 + BLK < L ? j0 + BLK : L;
             for (ii = i0; ii < i1; ++ii)
-              for (jj = j0; jj < j1 && jj <= ii; ++jj) {
+              for (jj = j0; jj < j1 && (!causal || jj <= ii); ++jj) {
                 long long wi = win_index(win, hq, start + ii, start + jj);
                 double ph = ldexp(orc_e4m3_decode(P[wi]), (int)PS[wi] - 127);
                 double dsh = ldexp(orc_e4m3_decode(DS[wi]), (int)DSS[wi] - 127);

@@ -33,8 +33,9 @@ def dequant(codes, scales):
     return v * np.exp2(e.astype(np.float64))
 
 
-def exact_attention(q, k, v, cu, softmax_scale, do=None):
-    """Causal softmax attention per document, FP64, GQA by contiguous head groups.
+def exact_attention(q, k, v, cu, softmax_scale, do=None, causal=True):
+    """Softmax attention per document (causal, or every key of the document), FP64, GQA by
+    contiguous head groups.
     q [T,Hq,d], k, v [T,Hkv,d] (numpy float64).  Returns O, and (dQ, dK, dV, dS-per-doc)
     when the output gradient ``do`` is given."""
     T, Hq, d = q.shape
@@ -58,7 +59,9 @@ def exact_attention(q, k, v, cu, softmax_scale, do=None):
         if do is not None:
             s.retain_grad()
         L = b - a
-        mask = torch.ones(L, L, dtype=torch.bool).tril()
+        mask = torch.ones(L, L, dtype=torch.bool)
+        if causal:
+            mask = mask.tril()
         p = torch.softmax(s.masked_fill(~mask, float("-inf")), dim=-1)
         od = torch.matmul(p, vv).permute(1, 0, 2)
         pieces.append((a, b, od))
