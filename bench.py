@@ -6,7 +6,8 @@ resident in HBM: quantise Q, K, V -> forward -> quantise dO (+ D) -> backward.  
 are built once per micro-batch (jaehun.me review §3.4) and are timed separately.
 
 value = algorithmic FLOP per step / step time, with the causal FLOP count
-14 * d * Hq * sum_docs L (L + 1) / 2 (forward 4d, backward 10d per visible query-key pair).
+14 * d * Hq * sum_docs L (L + 1) / 2 (forward 4d, backward 10d per visible query-key pair);
+--non-causal times the non-causal variant instead (14 * d * Hq * sum_docs L^2).
 
 Prints one JSON line.  Extra objects: `roofline` (dominant kernel vs the MI355X dense FP8
 peak, timed with HIP events on the launch stream), `quantize` (HBM roofline of the quantiser
@@ -23,6 +24,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "causal MXFP8 attn fwd+bwd TFLOPS incl. quantize; % of MI355X MXFP8 peak"
+METRIC_NC = "non-causal MXFP8 attn fwd+bwd TFLOPS incl. quantize; % of MI355X MXFP8 peak"
 PEAK_FP8_TFLOPS = 5000.0     # MI355X dense FP8 / MXFP8 matrix peak
 PEAK_HBM_GBPS = 8000.0       # MI355X HBM3E
 
@@ -41,6 +43,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="long")
     ap.add_argument("--causal-dq", action="store_true", help="causal dQ prescale option")
+    ap.add_argument("--non-causal", action="store_true",
+                    help="time the non-causal variant (every key of a row's document visible)")
     ap.add_argument("--store-gb", type=float, default=None,
                     help="cap the backward's dShat store at this many GiB (chunked backward); default: one chunk")
     ap.add_argument("--cpu-pairs", type=float, default=2.0e7, help="query-key pairs in the CPU-oracle sample")
@@ -104,6 +108,9 @@ def cpu_baseline(workload_name, pairs_budget):
 
 def main():
     args = parse()
+    if args.non_causal and args.causal_dq:
+        print("bench.py: the causal dQ prescale applies to causal attention only", file=sys.stderr)
+        sys.exit(2)
     if args.gpus != 1:
         print("bench.py measures one GPU: the path has no multi-GPU component (--gpus %d refused)" % args.gpus,
               file=sys.stderr)
@@ -118,7 +125,8 @@ def main():
     torch.cuda.set_device(dev)
     cu, shp, (q, k, v, do) = workloads.workload(args.workload)
     T, Hq, Hkv, d = shp.T, shp.Hq, shp.Hkv, shp.d
-    pairs = workloads.visible_pairs(cu)
+    causal = not args.non_causal
+    pairs = workloads.visible_pairs(cu, causal)
     flop = 14.0 * d * Hq * pairs
     q, k, v, do = (x.to(dev) for x in (q, k, v, do))
     cu_d = torch.as_tensor(cu).to(dev)
@@ -132,14 +140,14 @@ def main():
     for _ in range(5):
         e0, e1 = ev(), ev()
         e0.record()
-        lists = fl.Lists(cu_d, T)
+        lists = fl.Lists(cu_d, T, causal)
         e1.record()
         torch.cuda.synchronize()
         wl_ms.append(e0.elapsed_time(e1))
     # backward workspace: one key-tile chunk for this micro-batch's documents (sized from the
     # lengths the data loader holds on the host; --store-gb caps the store instead)
     if args.store_gb is None:
-        ws_bytes = fl.bwd_workspace_bytes_for(cu, T, Hq, d)
+        ws_bytes = fl.bwd_workspace_bytes_for(cu, T, Hq, d, causal)
     else:
         ws_bytes = fl.bwd_workspace_bytes(len(cu) - 1, T, Hq, d, int(args.store_gb * (1 << 30)))
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
@@ -150,11 +158,11 @@ def main():
         if evs: evs[0].record()
         qz, kz, vz = fl.quantize([q, k, v], cu_d)
         if evs: evs[1].record()
-        o, lse = fl.fwd(qz, kz, vz, cu_d, lists.fwd)
+        o, lse = fl.fwd(qz, kz, vz, cu_d, lists.fwd, causal=causal)
         if evs: evs[2].record()
         dc, dsc, D = fl.quantize_do(do, o, cu_d)
         if evs: evs[3].record()
-        out = fl.bwd(qz, kz, vz, (dc, dsc), lse, D, cu_d, lists, None, args.causal_dq, workspace=ws)
+        out = fl.bwd(qz, kz, vz, (dc, dsc), lse, D, cu_d, lists, None, args.causal_dq, workspace=ws, causal=causal)
         if evs: evs[4].record()
         return out
 
@@ -192,7 +200,7 @@ def main():
     dom_flop = bwd_flop if dom == "bwd" else fwd_flop
     achieved = dom_flop / (stages[dom] * 1e-3) / 1e12
     traffic = None
-    if dom == "bwd" and args.workload == BWD_TRAFFIC["workload"] and bwd_source_hash() == BWD_TRAFFIC["src"]:
+    if dom == "bwd" and causal and args.workload == BWD_TRAFFIC["workload"] and bwd_source_hash() == BWD_TRAFFIC["src"]:
         traffic = BWD_TRAFFIC["read_bytes"] + BWD_TRAFFIC["write_bytes"]
     roofline = {"bound": "mfma",
                 "kernel": "flamia_bwd (bwd_prologue + bwd_kernel + dq_kernel)" if dom == "bwd" else "flamia_fwd",
@@ -207,11 +215,12 @@ def main():
     quant["do_frac"] = quant["do_GBps"] / PEAK_HBM_GBPS
 
     res = {
-        "metric": METRIC, "value": value, "unit": "TFLOPS", "n_gpus": 1, "steps": args.steps,
+        "metric": METRIC if causal else METRIC_NC, "value": value, "unit": "TFLOPS", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "mxfp8_e4m3", "data": "synthetic",
         "config": {"workload": args.workload, "T": T, "Hq": Hq, "Hkv": Hkv, "d": d, "docs": len(cu) - 1,
-                   "visible_pairs": pairs, "flop_per_step": flop, "causal_dq_scale": bool(args.causal_dq)},
+                   "visible_pairs": pairs, "flop_per_step": flop, "causal_dq_scale": bool(args.causal_dq),
+                   "causal": causal},
         "frac_of_peak": value / PEAK_FP8_TFLOPS,
         "roofline": roofline,
         "quantize": quant,
@@ -220,7 +229,7 @@ def main():
         "peak_mem_GB": torch.cuda.max_memory_allocated() / 1e9,
         "bwd_workspace_GB": ws_bytes / 1e9, "bwd_chunks": chunks,
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and causal:
         res["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_pairs)
     print(json.dumps(res), flush=True)
 

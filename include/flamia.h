@@ -67,6 +67,9 @@ const char* flamia_status_str(flamia_status s);
  *   ceil(min(256(b+1), L) / 128).
  * FLAMIA_LIST_BWD: one item per 128-key tile kappa of a document; cost = number of 128-query
  *   tiles at or after it, ceil((L - 128 kappa) / 128).
+ * FLAMIA_LIST_FWD_NC, FLAMIA_LIST_BWD_NC: the same items for non-causal attention, where every
+ *   item of a document visits (serves) all of its ceil(L / 128) key (query) tiles: that is the
+ *   cost of each of them, so a document's items stay together in block order.
  * Items are enumerated by (document, block) and stably sorted by descending cost; `worker`
  * tags them in alternating (serpentine) order over n_workers: for list index i, with
  * r = i / n_workers, worker = i % n_workers if r is even, else n_workers - 1 - i % n_workers.
@@ -82,7 +85,7 @@ typedef struct {
   int32_t worker; /* serpentine tag over n_workers */
 } flamia_work_item;
 
-typedef enum { FLAMIA_LIST_FWD = 0, FLAMIA_LIST_BWD = 1 } flamia_list_kind;
+typedef enum { FLAMIA_LIST_FWD = 0, FLAMIA_LIST_BWD = 1, FLAMIA_LIST_FWD_NC = 2, FLAMIA_LIST_BWD_NC = 3 } flamia_list_kind;
 
 /* Host.  Bytes needed for a list over n_docs documents of total length T (an upper bound:
  * 16 + 16 * (ceil(T / 128) + n_docs)). */
@@ -135,6 +138,11 @@ flamia_status flamia_quantize(const flamia_qtensor* tensors, int32_t n_tensors, 
  * O_i = BF16(acc / l) is written into the packed output; LSE_i = m + log2 l.
  * Work comes from a FLAMIA_LIST_FWD list built for the same cu_seqlens; (item, head) units are
  * spread over a persistent grid in list order.  Invalid rows get O = 0 and LSE = +inf.
+ * Non-causal attention (non_causal = 1; [J] §3.4 "Backward pass", §4.8): every key of the
+ * row's document is visible; the key tiles are visited from the document's last one down to
+ * tile 0.  Batched attention is the special case of documents of equal length.  Either list kind
+ * gives the same results (the items are the same); FLAMIA_LIST_FWD_NC orders them by the
+ * non-causal costs.
  * ------------------------------------------------------------------------------------------ */
 typedef struct {
   const uint8_t *q, *k, *v;       /* codes: q [T, Hq, d]; k, v [T, Hkv, d] */
@@ -147,6 +155,7 @@ typedef struct {
   void* o;                        /* out: bf16 [T, Hq, d], element strides below */
   int64_t o_stride_t, o_stride_h;
   float* lse;                     /* out: float32 [Hq, T], log2 units */
+  int32_t non_causal;             /* 0: causal (j <= i); 1: every key of the document */
 } flamia_fwd_args;
 
 /* Errors: NULL pointers, sizes, d, head ratio. */
@@ -202,6 +211,10 @@ typedef struct {
   size_t workspace_bytes;
   int32_t causal_dq_scale;            /* 0: sequence-wide prescale (default); 1: causal */
   int16_t* dq_exp_out;                /* optional out: pi as int16 [Hq, T] (0 on invalid rows) */
+  int32_t non_causal;                 /* as in the forward (must match it); the non-causal
+                                         backward visits every (query tile, key tile) pair of a
+                                         document and takes the sequence-wide prescale only
+                                         (causal_dq_scale = 1 is FLAMIA_ERR_UNSUPPORTED) */
 } flamia_bwd_args;
 
 /* Host.  Backward workspace for n_docs documents of total length T: a header, pi [Hq, T], the
@@ -215,11 +228,12 @@ typedef struct {
 size_t flamia_bwd_workspace_bytes(int32_t n_docs, int32_t T, int32_t Hq, int32_t d, size_t store_budget);
 
 /* Host.  Workspace with which a backward over these documents runs as one chunk (the fastest):
- * the store holds every dShat block of the call.  For callers that already hold the document
+ * the store holds every dShat block of the call (non_causal != 0: of the non-causal backward,
+ * which stores every (query tile, key tile) pair).  For callers that already hold the document
  * lengths on the host (cu_seqlens_host: HOST int32 [n_docs + 1]; NULL only when n_docs == 0).
  * Returns 0 on bad arguments. */
 size_t flamia_bwd_workspace_bytes_for(const int32_t* cu_seqlens_host, int32_t n_docs, int32_t T, int32_t Hq,
-                                      int32_t d);
+                                      int32_t d, int32_t non_causal);
 
 /* Errors: NULL pointers, sizes, d, head ratio, a workspace smaller than
  * flamia_bwd_workspace_bytes(n_docs, T, Hq, d, 0) (FLAMIA_ERR_WORKSPACE).  The status word (first

@@ -18,6 +18,8 @@ LIB_PATH = os.path.join(_HERE, "libflamia.so")
 
 FLAMIA_LIST_FWD = 0
 FLAMIA_LIST_BWD = 1
+FLAMIA_LIST_FWD_NC = 2
+FLAMIA_LIST_BWD_NC = 3
 
 EXPORTED_SYMBOLS = (
     "flamia_status_str", "flamia_worklist_bytes", "flamia_build_worklist", "flamia_quantize",
@@ -42,7 +44,7 @@ class _FwdArgs(ctypes.Structure):
                 ("T", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32), ("d", ctypes.c_int32),
                 ("softmax_scale", ctypes.c_float), ("cu_seqlens", ctypes.c_void_p), ("n_docs", ctypes.c_int32),
                 ("fwd_list", ctypes.c_void_p), ("o", ctypes.c_void_p), ("o_stride_t", ctypes.c_int64),
-                ("o_stride_h", ctypes.c_int64), ("lse", ctypes.c_void_p)]
+                ("o_stride_h", ctypes.c_int64), ("lse", ctypes.c_void_p), ("non_causal", ctypes.c_int32)]
 
 
 class _BwdArgs(ctypes.Structure):
@@ -57,7 +59,8 @@ class _BwdArgs(ctypes.Structure):
                 ("dk_stride_t", ctypes.c_int64), ("dk_stride_h", ctypes.c_int64),
                 ("dv_stride_t", ctypes.c_int64), ("dv_stride_h", ctypes.c_int64),
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
-                ("causal_dq_scale", ctypes.c_int32), ("dq_exp_out", ctypes.c_void_p)]
+                ("causal_dq_scale", ctypes.c_int32), ("dq_exp_out", ctypes.c_void_p),
+                ("non_causal", ctypes.c_int32)]
 
 
 _lib = None
@@ -94,7 +97,7 @@ def load_library(path=LIB_PATH):
                                                ctypes.c_size_t]
     lib.flamia_bwd_workspace_bytes_for.restype = ctypes.c_size_t
     lib.flamia_bwd_workspace_bytes_for.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
-                                                   ctypes.c_int32]
+                                                   ctypes.c_int32, ctypes.c_int32]
     lib.flamia_num_workers.restype = ctypes.c_int32
     lib.flamia_num_workers.argtypes = []
     _lib = lib
@@ -191,9 +194,9 @@ def quantize_do(do, o, cu_seqlens):
     return codes, scales, D
 
 
-def fwd(q, k, v, cu_seqlens, fwd_list, softmax_scale=None, out=None):
-    """Forward on quantised operands.  q, k, v are (codes, scales) pairs.
-    Returns (O bf16 [T, Hq, d], LSE f32 [Hq, T] in log2 units)."""
+def fwd(q, k, v, cu_seqlens, fwd_list, softmax_scale=None, out=None, causal=True):
+    """Forward on quantised operands.  q, k, v are (codes, scales) pairs; causal=False lets every
+    row see every key of its document.  Returns (O bf16 [T, Hq, d], LSE f32 [Hq, T] in log2 units)."""
     lib = load_library()
     n_docs = _check_cu(cu_seqlens)
     (qc, qs), (kc, ks), (vc, vs) = q, k, v
@@ -203,7 +206,7 @@ def fwd(q, k, v, cu_seqlens, fwd_list, softmax_scale=None, out=None):
     lse = torch.empty((Hq, T), dtype=torch.float32, device=qc.device)
     a = _FwdArgs(qc.data_ptr(), kc.data_ptr(), vc.data_ptr(), qs.data_ptr(), ks.data_ptr(), vs.data_ptr(),
                  T, Hq, Hkv, d, float(softmax_scale or 0.0), cu_seqlens.data_ptr(), n_docs, fwd_list.data_ptr(),
-                 o.data_ptr(), o.stride(0), o.stride(1), lse.data_ptr())
+                 o.data_ptr(), o.stride(0), o.stride(1), lse.data_ptr(), int(not causal))
     _check(lib.flamia_fwd(ctypes.byref(a), _stream()))
     return o, lse
 
@@ -214,18 +217,19 @@ def bwd_workspace_bytes(n_docs, T, Hq, d, store_budget=DEFAULT_STORE_BYTES):
     return int(load_library().flamia_bwd_workspace_bytes(int(n_docs), int(T), int(Hq), int(d), int(store_budget)))
 
 
-def bwd_workspace_bytes_for(cu_seqlens_host, T, Hq, d):
+def bwd_workspace_bytes_for(cu_seqlens_host, T, Hq, d, causal=True):
     """Workspace with which a backward over these documents runs as one chunk (cu_seqlens_host:
     a host int32 array the caller already holds)."""
     import numpy as np
     cu = np.ascontiguousarray(np.asarray(cu_seqlens_host, dtype=np.int32))
     n_docs = cu.size - 1
     ptr = cu.ctypes.data_as(ctypes.c_void_p) if n_docs > 0 else None
-    return int(load_library().flamia_bwd_workspace_bytes_for(ptr, n_docs, int(T), int(Hq), int(d)))
+    return int(load_library().flamia_bwd_workspace_bytes_for(ptr, n_docs, int(T), int(Hq), int(d),
+                                                                      int(not causal)))
 
 
 def bwd(q, k, v, do, lse, D, cu_seqlens, lists, softmax_scale=None, causal_dq_scale=False, want_pi=False,
-        workspace=None, static_scratch=False):
+        workspace=None, static_scratch=False, causal=True):
     """Backward on quantised operands.  q, k, v, do are (codes, scales) pairs; lse, D f32 [Hq, T];
     lists: the micro-batch's Lists.  workspace: a uint8 CUDA tensor of at least
     bwd_workspace_bytes(n_docs, T, Hq, d, 0) bytes, or None to allocate one with the default
@@ -252,7 +256,7 @@ def bwd(q, k, v, do, lse, D, cu_seqlens, lists, softmax_scale=None, causal_dq_sc
                  dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), dq.stride(0), dq.stride(1), dk.stride(0), dk.stride(1),
                  dv.stride(0), dv.stride(1), workspace.data_ptr() if workspace is not None else None,
                  workspace.numel() if workspace is not None else 0, int(bool(causal_dq_scale)),
-                 pi.data_ptr() if pi is not None else None)
+                 pi.data_ptr() if pi is not None else None, int(not causal))
     _check((lib.flamia_bwd_static if static_scratch else lib.flamia_bwd)(ctypes.byref(a), _stream()))
     return (dq, dk, dv, pi) if want_pi else (dq, dk, dv)
 
@@ -266,21 +270,22 @@ def bwd_status(workspace):
 
 class Lists:
     """Forward and backward work lists of one micro-batch (built on the GPU once, reused by every
-    layer; nothing is copied to the host)."""
+    layer; nothing is copied to the host); causal=False builds the non-causal kinds."""
 
-    def __init__(self, cu_seqlens, T):
-        self.fwd = build_worklist(cu_seqlens, T, FLAMIA_LIST_FWD)
-        self.bwd = build_worklist(cu_seqlens, T, FLAMIA_LIST_BWD)
+    def __init__(self, cu_seqlens, T, causal=True):
+        self.fwd = build_worklist(cu_seqlens, T, FLAMIA_LIST_FWD if causal else FLAMIA_LIST_FWD_NC)
+        self.bwd = build_worklist(cu_seqlens, T, FLAMIA_LIST_BWD if causal else FLAMIA_LIST_BWD_NC)
 
 
-def training_call(q, k, v, do, cu_seqlens, lists=None, softmax_scale=None, causal_dq_scale=False):
+def training_call(q, k, v, do, cu_seqlens, lists=None, softmax_scale=None, causal_dq_scale=False, causal=True):
     """One attention training call: quantise Q, K, V -> forward -> quantise dO (+ D) -> backward.
     Returns dict with o, lse, dq, dk, dv."""
     T = q.shape[0]
     if lists is None:
-        lists = Lists(cu_seqlens, T)
+        lists = Lists(cu_seqlens, T, causal)
     qz, kz, vz = quantize([q, k, v], cu_seqlens)
-    o, lse = fwd(qz, kz, vz, cu_seqlens, lists.fwd, softmax_scale)
+    o, lse = fwd(qz, kz, vz, cu_seqlens, lists.fwd, softmax_scale, causal=causal)
     dc, dsc, D = quantize_do(do, o, cu_seqlens)
-    dq, dk, dv = bwd(qz, kz, vz, (dc, dsc), lse, D, cu_seqlens, lists, softmax_scale, causal_dq_scale)
+    dq, dk, dv = bwd(qz, kz, vz, (dc, dsc), lse, D, cu_seqlens, lists, softmax_scale, causal_dq_scale,
+                     causal=causal)
     return dict(o=o, lse=lse, dq=dq, dk=dk, dv=dv)

@@ -191,7 +191,9 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
 
     // Steps run over (query head of the group, 64-query tile from the diagonal to the
     // document end).
-    const int nq = n_qt - 2 * kappa;  // query tiles per head
+    // query tiles that see this key tile: from its diagonal on (causal) or all of them
+    const int qt_first = p.causal_mask ? 2 * kappa : 0;
+    const int nq = n_qt - qt_first;  // query tiles per head
     const int n_steps = grp * nq;
 
     // ---- K / V tiles and the first step's tiles into LDS
@@ -219,12 +221,12 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
     auto step_qt = [&](int st, int& h) {
       const int hi = st / nq;
       h = g * grp + hi;
-      return 2 * kappa + (st - hi * nq);
+      return qt_first + (st - hi * nq);
     };
     int rsq = 127, rsdo = 127, rsq1 = 127, rsdo1 = 127;
     if (!producer) {
-      issue_step_loads<D>(p, sm, 0, doc_start, L, g * grp, 2 * kappa, cw, lane);
-      scale_loads(g * grp, 2 * kappa, rsq, rsdo);
+      issue_step_loads<D>(p, sm, 0, doc_start, L, g * grp, qt_first, cw, lane);
+      scale_loads(g * grp, qt_first, rsq, rsdo);
       if (n_steps > 1) {
         int h1;
         const int qt1 = step_qt(1, h1);
@@ -259,7 +261,7 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
     }
     if (!producer) {
       __builtin_amdgcn_s_waitcnt(0);  // the direct loads have landed
-      scale_store(0, 2 * kappa, rsq, rsdo);
+      scale_store(0, qt_first, rsq, rsdo);
       if (n_steps > 1) {
         int h1;
         scale_store(1, step_qt(1, h1), rsq1, rsdo1);
@@ -338,8 +340,9 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
         __builtin_amdgcn_sched_barrier(0);
         float pmax = 0.f, dmax = 0.f;
         // element i sits in row 32 qs + 4 hh + r_i (r_i = 8 (i / 4) + i % 4, a constant): it is
-        // visible when lo <= r_i < hi
-        const int lo = key_rel - (q0 + 32 * qs + 4 * hh), hi = L - (q0 + 32 * qs + 4 * hh);
+        // visible when lo <= r_i < hi (non-causally every row is when the key is in the document)
+        const int lo = p.causal_mask ? key_rel - (q0 + 32 * qs + 4 * hh) : (key_rel < L ? -QT : QT);
+        const int hi = L - (q0 + 32 * qs + 4 * hh);
 #pragma unroll
         for (int m = 0; m < NM; ++m) {
           const int cc = m / 2;
@@ -439,15 +442,20 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
         }
       };
       products(0, 0, cs, cp);
-      int cur_h = g * grp, cur_qt = 2 * kappa;  // head and query tile of step ph
+      int cur_h = g * grp, cur_qt = qt_first;  // head and query tile of step ph
+      // all 64 x 128 pairs of a step are visible when the query tile lies wholly inside the
+      // document and, causally, below the key tile (then every key of the tile is inside the
+      // document too) or, non-causally, when the key tile is wholly inside it as well
+      const bool keys_full = !p.causal_mask && KV_TILE * kappa + KV_TILE <= L;
       for (int ph = 0; ph <= n_steps; ++ph) {
         if (ph < n_steps) {
           // all 64 x 128 pairs visible: the query tile lies wholly below the key tile and
           // inside the document (then every key of the tile is inside it too)
-          if (cur_qt >= 2 * kappa + 2 && QT * cur_qt + QT <= L) phase_body(ph, cur_h, cur_qt, std::false_type{});
+          if ((p.causal_mask ? cur_qt >= 2 * kappa + 2 : keys_full) && QT * cur_qt + QT <= L)
+            phase_body(ph, cur_h, cur_qt, std::false_type{});
           else phase_body(ph, cur_h, cur_qt, std::true_type{});
           if (++cur_qt == n_qt) {
-            cur_qt = 2 * kappa;
+            cur_qt = qt_first;
             ++cur_h;
           }
         }
@@ -466,7 +474,7 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
       for (int db = 0; db < NDB; ++db) { dkacc[db] = v16f{}; dvacc[db] = v16f{}; }
       int ld_h = 0, ld_qt = 0;  // head and query tile of step ph + 2 (the next to load)
       if (n_steps > 2) ld_qt = step_qt(2, ld_h);
-      int st_h = g * grp, st_qt = 2 * kappa;  // head and query tile of step ph - 1
+      int st_h = g * grp, st_qt = qt_first;  // head and query tile of step ph - 1
       for (int ph = 0; ph <= n_steps; ++ph) {
         const int qtn = ld_qt;
         const int bn = (ph + 2) & (NBUF - 1);
@@ -474,7 +482,7 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
           issue_step_loads<D>(p, sm, bn, doc_start, L, ld_h, qtn, cw, lane);
           scale_loads(ld_h, qtn, rsq, rsdo);
           if (++ld_qt == n_qt) {
-            ld_qt = 2 * kappa;
+            ld_qt = qt_first;
             ++ld_h;
           }
         }
@@ -492,7 +500,7 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
               // lane, so each store instruction writes 1 KiB contiguously.  Non-temporal: the
               // store is read back once, by another kernel, and would otherwise push the step
               // tiles (re-read once per key tile) out of L2
-              uint8_t* bbase = p.ds_store + ((ds_base + (st_qt - 2 * kappa)) * p.Hq + st_h) * DS_STRIDE;
+              uint8_t* bbase = p.ds_store + ((ds_base + (st_qt - qt_first)) * p.Hq + st_h) * DS_STRIDE;
               v4i* dst = reinterpret_cast<v4i*>(bbase + 2048 * kw + 16 * lane);
               __builtin_nontemporal_store(v4i{d0.x, d0.y, d0.z, d0.w}, dst);
               __builtin_nontemporal_store(v4i{d1.x, d1.y, d1.z, d1.w}, dst + 64);
@@ -502,7 +510,7 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
               }
             }
             if (++st_qt == n_qt) {
-              st_qt = 2 * kappa;
+              st_qt = qt_first;
               ++st_h;
             }
             const v8i bp = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
@@ -533,7 +541,7 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
             // consumer w computes d-block w (d = 128) or w % 2 (d = 64) of its query blocks
             const int hi = st / nq;
             const int h = g * grp + hi;
-            const int q0 = QT * (2 * kappa + (st - hi * nq));
+            const int q0 = QT * (qt_first + (st - hi * nq));
             constexpr int NQB = (D == 128) ? 2 : 1;
             const int dblk = (D == 128) ? kw : (kw & 1);
             const int qb0 = (D == 128) ? 0 : (kw >> 1);
@@ -651,11 +659,13 @@ __device__ __forceinline__ void dq_load(DqRegs<D>& r, const BwdParams& p, int do
     const int key = min(KV_TILE * kappa + row, L - 1);
     r.k[i] = *reinterpret_cast<const v4u*>(p.k + ((int64_t)(doc_start + key) * p.Hkv + g) * D + col);
   }
-  // block of query tile qt0 + t (clamped into the key tile's range [2 kappa, n_qt - 1]); `base` is
-  // the key tile's first block in the chunk's store
+  // block of query tile qt0 + t (clamped into the key tile's range [qt_lo, n_qt - 1], qt_lo its
+  // diagonal query tile, or 0 non-causally); `base` is the key tile's first block in the chunk's
+  // store
+  const int qt_lo = p.causal_mask ? 2 * kappa : 0;
   auto block = [&](int t) {
-    const int qt = min(max(qt0 + t, 2 * kappa), n_qt - 1);
-    return p.ds_store + ((base + (qt - 2 * kappa)) * p.Hq + h) * DS_STRIDE;
+    const int qt = min(max(qt0 + t, qt_lo), n_qt - 1);
+    return p.ds_store + ((base + (qt - qt_lo)) * p.Hq + h) * DS_STRIDE;
   };
 #pragma unroll
   for (int t = 0; t < DQ_QT; ++t)  // read once: non-temporal, so L2 keeps the K tiles
@@ -729,7 +739,9 @@ __global__ __launch_bounds__(DQ_THREADS, 2) void dq_kernel(BwdParams p) {  // tw
     // Rows whose last key tile lies in an earlier chunk are complete already.
     const int tb = p.tile_base[doc];
     const int last_qt = min(qt0 + DQ_QT, n_qt) - 1;
-    const int K = last_qt / 2;
+    // the last key tile the unit's rows see: that of its last query tile, or non-causally the
+    // document's last one
+    const int K = p.causal_mask ? last_qt / 2 : (L - 1) / KV_TILE;
     if (p.kv_chunk[tb + K] < chunk) continue;  // (uniform over the workgroup)
     int k_lo = 0, kappa_hi = -1;
     for (int k0 = 0; k0 <= K; k0 += 64 * 8) {  // each lane reads up to 8 entries, all in flight
@@ -750,11 +762,12 @@ __global__ __launch_bounds__(DQ_THREADS, 2) void dq_kernel(BwdParams p) {  // tw
     const bool active = qt < n_qt;
     const int q_rel = QT * qt + qrow;
     const bool row_valid = q_rel < L;
-    // the wave's rows (one 64-query tile, whose last key tile is qt / 2) take part in this chunk
-    // when that tile is at or after k_lo, and are complete after it when it is at or before
-    // kappa_hi (the unit's last key tile in this chunk)
-    const bool w_on = active && row_valid && qt / 2 >= k_lo;
-    const bool w_final = qt / 2 <= kappa_hi;
+    // the wave's rows (one 64-query tile, whose last key tile is qt / 2, or K non-causally) take
+    // part in this chunk when that tile is at or after k_lo, and are complete after it when it
+    // is at or before kappa_hi (the unit's last key tile in this chunk)
+    const int w_last = p.causal_mask ? qt / 2 : K;
+    const bool w_on = active && row_valid && w_last >= k_lo;
+    const bool w_final = w_last <= kappa_hi;
     int pi = 0;
     if (row_valid) pi = p.pi[(int64_t)h * p.T + doc_start + q_rel];
     const float up = exp2i(pi);
@@ -782,7 +795,7 @@ __global__ __launch_bounds__(DQ_THREADS, 2) void dq_kernel(BwdParams p) {  // tw
     // to arrive.
     auto compute = [&](int kappa) __attribute__((always_inline)) {
       const int b = kappa & 1;
-      if (active && qt >= 2 * kappa) {
+      if (active && (!p.causal_mask || qt >= 2 * kappa)) {
         v8i bs[2];
         int sb[2];
 #pragma unroll
@@ -914,8 +927,8 @@ __device__ __forceinline__ Seg seg_op(Seg a, Seg b) {
 // Stored dShat blocks (per query head) of the backward item (document of length L, key tile
 // kappa): one per 64-query tile from the key tile's diagonal to the document end; none for a
 // document of a single key tile (its dQ is formed in the key-tile pass).
-__device__ __forceinline__ int64_t item_blocks(int L, int kappa) {
-  return L > KV_TILE ? (int64_t)((L + QT - 1) / QT - 2 * kappa) : 0;
+__device__ __forceinline__ int64_t item_blocks(int L, int kappa, int causal_mask) {
+  return L > KV_TILE ? (int64_t)((L + QT - 1) / QT - (causal_mask ? 2 * kappa : 0)) : 0;
 }
 
 // Inclusive scan of part[0 .. PRO_THREADS) in place (all threads take part).
@@ -965,7 +978,7 @@ __device__ void layout_chunks(const BwdParams& p) {
   const int4* items = reinterpret_cast<const int4*>(p.list + 4);
   auto blocks_of = [&](int u) {
     const int4 it = items[u];
-    return item_blocks(p.cu[it.x + 1] - p.cu[it.x], it.y);
+    return item_blocks(p.cu[it.x + 1] - p.cu[it.x], it.y, p.causal_mask);
   };
   auto chunk_of = [&](int64_t P, int64_t b) {
     const int64_t last = P + b - 1;

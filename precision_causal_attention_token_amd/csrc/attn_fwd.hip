@@ -163,9 +163,11 @@ __global__ __launch_bounds__(fwd_threads<W>(), 8 / W) void fwd_kernel(FwdParams 
     const bool wave_active = q_wave < L;
     const int q_rel = q_wave + n;
     const bool row_valid = q_rel < L;
-    const int kd = q_wave / KV_TILE;                    // this wave's diagonal tile
+    // this wave's first (diagonal) tile: causal, the tile of its queries; non-causal, the
+    // document's last key tile, the one every row starts from
+    const int kd = p.causal ? q_wave / KV_TILE : (L - 1) / KV_TILE;
     const int last_row = min(q0 + QU, L) - 1;
-    const int kappa_hi = last_row / KV_TILE;
+    const int kappa_hi = p.causal ? last_row / KV_TILE : (L - 1) / KV_TILE;
 
     // Q operand (B of S^T): lane (n, hh) holds d = 64c + 32hh .. +31 of query n.
     v8i qop[NC];
@@ -227,13 +229,14 @@ __global__ __launch_bounds__(fwd_threads<W>(), 8 / W) void fwd_kernel(FwdParams 
             __builtin_amdgcn_sched_barrier(0);
           }
         }
-        // ---- causal mask on the diagonal tile (keys after the query)
+        // ---- mask on the first tile: keys after the query (causal) or past the document end
+        // (non-causal; causally those lie after the query too)
         if (kappa == kd) {
-          // key 128 kappa + 32 kb4 + acc_row(i, hh) lies after the query when the constant part
+          // key 128 kappa + 32 kb4 + acc_row(i, hh) is masked when the constant part
           // 32 kb4 + acc_row(i, 0) exceeds lim; lim is formed here, opaque to the compiler, so
           // the 64 comparisons stay in this branch instead of held as lane masks in scalar
           // registers across the loop
-          int lim = q_rel - KV_TILE * kappa - 4 * hh;
+          int lim = (p.causal ? q_rel : L - 1) - KV_TILE * kappa - 4 * hh;
           asm volatile("" : "+v"(lim));
 #pragma unroll
           for (int kb4 = 0; kb4 < 4; ++kb4)

@@ -63,7 +63,7 @@ size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 // (document, key tile) table entries: at most ceil(T / 128) + n_docs tiles.
 int64_t n_tiles(int32_t n_docs, int32_t T) { return ((int64_t)T + 127) / 128 + n_docs; }
 // entries of the per-chunk tables (a bound on the chunk count + 2)
-int64_t n_chunk_entries(int32_t T) { return ((int64_t)T + 127) / 128 + 8; }
+int64_t n_chunk_entries(int32_t T) { return ((int64_t)T + 63) / 64 + 16; }
 struct BwdLayout {
   size_t pi, tile_base, kv_chunk, kv_off, chunk_start, chunk_first, store;  // byte offsets
 };
@@ -82,11 +82,12 @@ BwdLayout bwd_layout(int32_t n_docs, int32_t T, int32_t Hq) {
 // Stored blocks (per query head) of the largest single backward item: the query tiles of a
 // T-token document.
 int64_t max_item_blocks(int32_t T) { return std::max<int64_t>(1, ((int64_t)T + 63) / 64); }
-// Stored blocks of a document of length L: one per (128-key tile kappa, 64-query tile qt >= 2 kappa),
-// none when the document has a single key tile.
-int64_t doc_blocks(int64_t L) {
+// Stored blocks of a document of length L: one per (128-key tile kappa, 64-query tile qt >= 2 kappa)
+// (non-causal: every 64-query tile), none when the document has a single key tile.
+int64_t doc_blocks(int64_t L, bool non_causal) {
   const int64_t n_kt = (L + 127) / 128, n_qt = (L + 63) / 64;
-  return n_kt >= 2 ? n_kt * n_qt - n_kt * (n_kt - 1) : 0;
+  if (n_kt < 2) return 0;
+  return non_causal ? n_kt * n_qt : n_kt * n_qt - n_kt * (n_kt - 1);
 }
 // An upper bound of the stored blocks of any documents of total length T: a document of length L
 // in (128 m, 128 (m + 1)] stores at most (m + 1)(m + 2) < (L / 128)(L / 128 + 3) + 2 blocks, at
@@ -94,6 +95,12 @@ int64_t doc_blocks(int64_t L) {
 int64_t worst_blocks(int32_t T) {
   const int64_t t = T;
   return (t * t) / 16384 + 5 * t / 128 + 3;
+}
+// The same for non-causal attention, whose documents store every (query tile, key tile) pair:
+// (m + 1)(2m + 2) < 2 (L / 128)(L / 128 + 3) + 2 blocks for L in (128 m, 128 (m + 1)].
+int64_t worst_blocks_nc(int32_t T) {
+  const int64_t t = T;
+  return (t * t) / 8192 + 5 * t / 64 + 3;
 }
 }  // namespace
 
@@ -123,7 +130,7 @@ size_t flamia_worklist_bytes(int32_t n_docs, int32_t T, int32_t kind) {
 flamia_status flamia_build_worklist(const int32_t* cu_seqlens, int32_t n_docs, int32_t T, int32_t kind,
                                     int32_t n_workers, void* list, size_t list_bytes, void* stream) {
   if (!cu_seqlens || !list) return FLAMIA_ERR_NULL;
-  if (n_docs < 0 || T < 0 || n_workers < 1 || (kind != FLAMIA_LIST_FWD && kind != FLAMIA_LIST_BWD))
+  if (n_docs < 0 || T < 0 || n_workers < 1 || kind < FLAMIA_LIST_FWD || kind > FLAMIA_LIST_BWD_NC)
     return FLAMIA_ERR_SHAPE;
   if (T > FLAMIA_MAX_T_WORKLIST) return FLAMIA_ERR_UNSUPPORTED;
   if (list_bytes < flamia_worklist_bytes(n_docs, T, kind)) return FLAMIA_ERR_WORKSPACE;
@@ -194,6 +201,7 @@ flamia_status flamia_fwd(const flamia_fwd_args* a, void* stream) {
   p.list = static_cast<const int32_t*>(a->fwd_list);
   p.o = static_cast<uint16_t*>(a->o); p.ost = a->o_stride_t; p.osh = a->o_stride_h;
   p.lse = a->lse;
+  p.causal = a->non_causal ? 0 : 1;
 #ifdef FLAMIA_DEBUG_DUMP
   p.dbg = g_dbg;
 #endif
@@ -205,17 +213,17 @@ flamia_status flamia_fwd(const flamia_fwd_args* a, void* stream) {
 size_t flamia_bwd_workspace_bytes(int32_t n_docs, int32_t T, int32_t Hq, int32_t d, size_t store_budget) {
   if (T < 0 || Hq < 1 || n_docs < 0 || (d != 64 && d != 128)) return 0;
   const int64_t lo = 2 * max_item_blocks(T);                      // the smallest store accepted
-  const int64_t hi = worst_blocks(T) + max_item_blocks(T);        // one chunk for any documents
+  const int64_t hi = worst_blocks_nc(T) + max_item_blocks(T);     // one chunk for any documents
   const int64_t want = (int64_t)(store_budget / ((size_t)Hq * DS_BLOCK_BYTES));
   const int64_t blocks = std::max(lo, std::min(want, hi));
   return bwd_layout(n_docs, T, Hq).store + (size_t)blocks * Hq * DS_BLOCK_BYTES;
 }
 
 size_t flamia_bwd_workspace_bytes_for(const int32_t* cu_seqlens_host, int32_t n_docs, int32_t T, int32_t Hq,
-                                      int32_t d) {
+                                      int32_t d, int32_t non_causal) {
   if (T < 0 || Hq < 1 || n_docs < 0 || (n_docs > 0 && !cu_seqlens_host) || (d != 64 && d != 128)) return 0;
   int64_t blocks = 0;
-  for (int32_t k = 0; k < n_docs; ++k) blocks += doc_blocks((int64_t)cu_seqlens_host[k + 1] - cu_seqlens_host[k]);
+  for (int32_t k = 0; k < n_docs; ++k) blocks += doc_blocks((int64_t)cu_seqlens_host[k + 1] - cu_seqlens_host[k], non_causal != 0);
   const int64_t store = std::max<int64_t>(blocks, max_item_blocks(T)) + max_item_blocks(T);
   return bwd_layout(n_docs, T, Hq).store + (size_t)store * Hq * DS_BLOCK_BYTES;
 }
@@ -229,6 +237,7 @@ flamia_status flamia_bwd(const flamia_bwd_args* a, void* stream) {
   if (a->d != 64 && a->d != 128) return FLAMIA_ERR_UNSUPPORTED;
   if (a->Hq % a->Hkv) return FLAMIA_ERR_UNSUPPORTED;
   if (a->T > FLAMIA_MAX_T) return FLAMIA_ERR_UNSUPPORTED;
+  if (a->non_causal && a->causal_dq_scale) return FLAMIA_ERR_UNSUPPORTED;
   if (a->workspace_bytes < flamia_bwd_workspace_bytes(a->n_docs, a->T, a->Hq, a->d, 0)) return FLAMIA_ERR_WORKSPACE;
   const int64_t st[6] = {a->dq_stride_t, a->dq_stride_h, a->dk_stride_t, a->dk_stride_h, a->dv_stride_t, a->dv_stride_h};
   for (int i = 0; i < 6; ++i)
@@ -271,12 +280,13 @@ flamia_status flamia_bwd(const flamia_bwd_args* a, void* stream) {
   const int64_t cap = (int64_t)((a->workspace_bytes - lay.store) / DS_BLOCK_BYTES) / a->Hq;
   p.chunk_cap = cap - max_item_blocks(a->T);
   if (p.chunk_cap < max_item_blocks(a->T)) return FLAMIA_ERR_WORKSPACE;
-  const int64_t max_chunks = (worst_blocks(a->T) - 1) / p.chunk_cap + 1;
+  const int64_t max_chunks = ((a->non_causal ? worst_blocks_nc(a->T) : worst_blocks(a->T)) - 1) / p.chunk_cap + 1;
   if (max_chunks + 2 > n_chunk_entries(a->T)) return FLAMIA_ERR_WORKSPACE;
   p.max_chunks = (int32_t)max_chunks;
   p.n_tab = (int32_t)n_tiles(a->n_docs, a->T);
   p.pi_out = a->dq_exp_out;
   p.causal = a->causal_dq_scale ? 1 : 0;
+  p.causal_mask = a->non_causal ? 0 : 1;
 #ifdef FLAMIA_DEBUG_DUMP
   p.dbg = g_dbg;
 #endif

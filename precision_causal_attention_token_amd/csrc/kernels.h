@@ -68,6 +68,7 @@ struct FwdParams {
   uint16_t* o;
   int64_t ost, osh;
   float* lse;
+  int32_t causal;  // 1: keys j <= i; 0: every key of the document
 #ifdef FLAMIA_DEBUG_DUMP
   DebugDump dbg;
 #endif
@@ -101,7 +102,8 @@ struct BwdParams {
   int32_t n_tab;            // entries of the (document, key tile) tables
   int32_t chunk;            // the chunk a launch works on
   int16_t* pi_out;          // optional copy of pi
-  int32_t causal;
+  int32_t causal;           // causal dQ prescale option
+  int32_t causal_mask;      // 1: keys j <= i; 0: every key of the document
 #ifdef FLAMIA_DEBUG_DUMP
   DebugDump dbg;
 #endif

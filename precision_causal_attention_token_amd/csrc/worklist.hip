@@ -10,6 +10,9 @@
 //   BWD: key tile kappa costs m - kappa, so the costs are exactly 1..m.
 // Hence the position of item (document k, cost c) is
 //   #items of cost > c  +  #documents k' < k that have an item of cost c.
+// Non-causal lists (kinds 2 = FWD, 3 = BWD): every item of a document costs m, so a document's
+// items (n = ceil(L/256), or m) sit together, in block order, at
+//   #items of cost > m  +  #items of documents k' < k of cost m.
 // Cost-1 items come from documents with m == 1 (FWD) or m >= 1 (BWD) and are placed by a
 // prefix count over documents.  Items of cost >= 2 exist only in "long" documents (m >= 2,
 // at most T/129 of them), which are listed in LDS; for every cost c one thread walks that
@@ -61,7 +64,13 @@ __device__ __forceinline__ int serpentine(int i, int G) {
 template <int KIND>
 __device__ __forceinline__ bool has_cost(int m, int c) {
   if constexpr (KIND == 0) return ((c & 1) == 0 && c <= m) || c == m;
-  else return c <= m;
+  else if constexpr (KIND == 1) return c <= m;
+  else return c == m;
+}
+// Items of a document of length L (m key tiles) in a list of this kind.
+template <int KIND>
+__device__ __forceinline__ int n_items_of(int L, int m) {
+  return (KIND % 2 == 0) ? ceil_div(L, 256) : m;
 }
 
 template <int KIND>
@@ -85,15 +94,17 @@ __global__ __launch_bounds__(NT) void worklist_kernel(const int32_t* __restrict_
   for (int k = k0; k < k1; ++k) {
     const int L = cu[k + 1] - cu[k];
     const int m = ceil_div(L, 128);
-    if (KIND == 0 ? (m == 1) : (m >= 1)) n1++;
+    if (KIND == 1 ? (m >= 1) : (m == 1)) n1++;
     if (m >= 2) {
       nl++;
       if (KIND == 0) {
         const int n = ceil_div(L, 256);
         for (int b = 0; b + 1 < n; ++b) atomicAdd(&hist[2 * b + 2], 1);
         atomicAdd(&hist[m], 1);
-      } else {
+      } else if (KIND == 1) {
         for (int c = 2; c <= m; ++c) atomicAdd(&hist[c], 1);
+      } else {
+        atomicAdd(&hist[m], n_items_of<KIND>(L, m));
       }
     }
   }
@@ -143,9 +154,9 @@ __global__ __launch_bounds__(NT) void worklist_kernel(const int32_t* __restrict_
     const int b1 = before[1];
     for (int k = k0; k < k1; ++k) {
       const int m = ceil_div(cu[k + 1] - cu[k], 128);
-      if (KIND == 0 ? (m == 1) : (m >= 1)) {
+      if (KIND == 1 ? (m >= 1) : (m == 1)) {
         const int pos = b1 + r;
-        items[pos] = make_int4(k, KIND == 0 ? 0 : m - 1, 1, serpentine(pos, G));
+        items[pos] = make_int4(k, KIND == 1 ? m - 1 : 0, 1, serpentine(pos, G));
         r++;
       }
     }
@@ -157,9 +168,15 @@ __global__ __launch_bounds__(NT) void worklist_kernel(const int32_t* __restrict_
     for (int j = 0; j < totl; ++j) {
       const int m = long_m[j];
       if (has_cost<KIND>(m, c)) {
-        const int blk = (KIND == 0) ? ((c == m) ? ceil_div(m, 2) - 1 : c / 2 - 1) : (m - c);
-        items[r] = make_int4(long_doc[j], blk, c, serpentine(r, G));
-        r++;
+        if constexpr (KIND >= 2) {  // non-causal: all of the document's items, in block order
+          const int k = long_doc[j];
+          const int n = n_items_of<KIND>(cu[k + 1] - cu[k], m);
+          for (int b = 0; b < n; ++b, ++r) items[r] = make_int4(k, b, c, serpentine(r, G));
+        } else {
+          const int blk = (KIND == 0) ? ((c == m) ? ceil_div(m, 2) - 1 : c / 2 - 1) : (m - c);
+          items[r] = make_int4(long_doc[j], blk, c, serpentine(r, G));
+          r++;
+        }
       }
     }
   }
@@ -178,17 +195,18 @@ hipError_t launch_worklist(const int32_t* cu, int n_docs, int T, int kind, int n
   const int max_cost = (T + 127) / 128 + 1;
   const int max_long = T / 129 + 2;
   const size_t lds = worklist_lds_bytes(T);
-  hipError_t e;
-  if (kind == 0) {
-    e = hipFuncSetAttribute((const void*)worklist_kernel<0>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  auto go = [&](auto kern) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(worklist_kernel<0>, dim3(1), dim3(NT), lds, s, cu, n_docs, max_cost, max_long, n_workers, list);
-  } else {
-    e = hipFuncSetAttribute((const void*)worklist_kernel<1>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(worklist_kernel<1>, dim3(1), dim3(NT), lds, s, cu, n_docs, max_cost, max_long, n_workers, list);
+    hipLaunchKernelGGL(kern, dim3(1), dim3(NT), lds, s, cu, n_docs, max_cost, max_long, n_workers, list);
+    return hipGetLastError();
+  };
+  switch (kind) {
+    case 0: return go(worklist_kernel<0>);
+    case 1: return go(worklist_kernel<1>);
+    case 2: return go(worklist_kernel<2>);
+    default: return go(worklist_kernel<3>);
   }
-  return hipGetLastError();
 }
 
 }  // namespace flamia

@@ -134,7 +134,7 @@ def random_lengths(total, lo, hi, seed):
     return _fill_row(total, lambda: rng.integers(lo, hi + 1))
 
 
-def visible_pairs(cu):
-    """Number of (query, key) pairs a causal packed call visits: sum L(L+1)/2."""
+def visible_pairs(cu, causal=True):
+    """Number of (query, key) pairs a packed call visits: sum L(L+1)/2 (causal) or sum L^2."""
     L = np.diff(np.asarray(cu, np.int64))
-    return int((L * (L + 1) // 2).sum())
+    return int((L * (L + 1) // 2).sum()) if causal else int((L * L).sum())

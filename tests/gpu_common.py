@@ -103,9 +103,10 @@ DUMP_F32 = ("fwd_s", "fwd_m", "bwd_s", "bwd_dp")
 DUMP_U8 = ("fwd_p", "bwd_p", "bwd_ps", "bwd_ds", "bwd_dss")
 
 
-def gpu_call(q, k, v, do, cu, causal_dq=False, softmax_scale=None, window=None, store_budget=None):
+def gpu_call(q, k, v, do, cu, causal_dq=False, softmax_scale=None, window=None, store_budget=None, causal=True,
+             static_scratch=False):
     """Full training call on the GPU through the C ABI; returns numpy arrays (BF16 outputs as
-    bit patterns).  With `window` (row/key/head bounds) the call runs the debug variant and the
+    bit patterns).  causal=False: non-causal attention within each document.  With `window` (row/key/head bounds) the call runs the debug variant and the
     result also holds its per-pair dumps under "dumps" ([heads][rows][keys]).  store_budget: the
     backward's dShat store (default: the binding's default; 0: the smallest accepted, many
     chunks); the key-tile chunks run are returned under "chunks"."""
@@ -126,18 +127,24 @@ def gpu_call(q, k, v, do, cu, causal_dq=False, softmax_scale=None, window=None, 
             st = lib.flamia_debug_set_dump(ctypes.byref(_dump_struct(window, bufs)))
             assert st == 0, st
         try:
-            lists = fl.Lists(cu_d, T)
+            lists = fl.Lists(cu_d, T, causal)
             qz, kz, vz = fl.quantize([qd, kd, vd], cu_d)
-            o, lse = fl.fwd(qz, kz, vz, cu_d, lists.fwd, softmax_scale)
+            o, lse = fl.fwd(qz, kz, vz, cu_d, lists.fwd, softmax_scale, causal=causal)
             dc, dsc, D = fl.quantize_do(dod, o, cu_d)
             Hq, d = q.shape[1], q.shape[2]
             budget = fl.DEFAULT_STORE_BYTES if store_budget is None else store_budget
             ws = torch.empty(fl.bwd_workspace_bytes(len(cu) - 1, T, Hq, d, budget), dtype=torch.uint8, device=dev)
             ws.fill_(0xA5)  # the workspace may hold anything on entry
-            dq, dk, dv, pi = fl.bwd(qz, kz, vz, (dc, dsc), lse, D, cu_d, lists, softmax_scale, causal_dq,
-                                    want_pi=True, workspace=ws)
-            torch.cuda.synchronize()
-            status, chunks = fl.bwd_status(ws)
+            if static_scratch:
+                dq, dk, dv, pi = fl.bwd(qz, kz, vz, (dc, dsc), lse, D, cu_d, lists, softmax_scale, causal_dq,
+                                        want_pi=True, static_scratch=True, causal=causal)
+                torch.cuda.synchronize()
+                status, chunks = 0, None
+            else:
+                dq, dk, dv, pi = fl.bwd(qz, kz, vz, (dc, dsc), lse, D, cu_d, lists, softmax_scale, causal_dq,
+                                        want_pi=True, workspace=ws, causal=causal)
+                torch.cuda.synchronize()
+                status, chunks = fl.bwd_status(ws)
             assert status == 0, 'backward workspace status'
         finally:
             if window is not None:
@@ -146,7 +153,7 @@ def gpu_call(q, k, v, do, cu, causal_dq=False, softmax_scale=None, window=None, 
     n = lambda t: t.cpu().numpy()
     out = dict(q=n(qz[0]), sq=n(qz[1]), k=n(kz[0]), sk=n(kz[1]), v=n(vz[0]), sv=n(vz[1]),
                do=n(dc), sdo=n(dsc), D=n(D), o=b(o), lse=n(lse), dq=b(dq), dk=b(dk), dv=b(dv), pi=n(pi),
-               chunks=chunks)
+               chunks=chunks, causal=bool(causal))
     if bufs is not None:
         out["dumps"] = {k_: n(t) for k_, t in bufs.items()}
         out["window"] = dict(window)
@@ -160,7 +167,7 @@ def same_outputs(a, b):
 
 
 def oracle_call(orc, q, k, v, do, cu, causal_dq=False, softmax_scale=None, docs=None, kv_heads=None,
-                tail_rows=0, tail_blocks=0):
+                tail_rows=0, tail_blocks=0, causal=True):
     """The oracle's own end-to-end chain on the BF16 inputs."""
     cu = np.asarray(cu, np.int32)
     out = {}
@@ -168,10 +175,10 @@ def oracle_call(orc, q, k, v, do, cu, causal_dq=False, softmax_scale=None, docs=
         c, s = orc.quantize(bf16_bits(x), cu)
         out[name], out["s" + name] = c, s
     o, lse, _ = orc.fwd(out["q"], out["sq"], out["k"], out["sk"], out["v"], out["sv"], cu, softmax_scale,
-                        docs=docs, kv_heads=kv_heads, tail_rows=tail_rows)
+                        docs=docs, kv_heads=kv_heads, tail_rows=tail_rows, causal=causal)
     dc, dsc, D = orc.quantize_do(bf16_bits(do), o, cu)
     g = orc.bwd(out["q"], out["sq"], out["k"], out["sk"], out["v"], out["sv"], dc, dsc, lse, D, cu, softmax_scale,
-                causal_dq=causal_dq, docs=docs, kv_heads=kv_heads, tail_blocks=tail_blocks)
+                causal_dq=causal_dq, docs=docs, kv_heads=kv_heads, tail_blocks=tail_blocks, causal=causal)
     out.update(do=dc, sdo=dsc, D=D, o=o, lse=lse, dq=g["dq"], dk=g["dk"], dv=g["dv"], pi=g["pi"])
     return out
 
@@ -225,12 +232,15 @@ def doc_map(cu, T):
     return m
 
 
-def visible_mask(cu, T, win):
+def visible_mask(cu, T, win, causal=True):
+    """[rows, keys] of the window: the key belongs to the row's document (and, causal, is not
+    after the row)."""
     dm = doc_map(cu, T)
     rows = np.arange(win["row_lo"], win["row_hi"])
     keys = np.arange(win["key_lo"], win["key_hi"])
     dr, dk = dm[rows], dm[keys]
-    return (dr[:, None] == dk[None, :]) & (dr[:, None] >= 0) & (keys[None, :] <= rows[:, None])
+    same = (dr[:, None] == dk[None, :]) & (dr[:, None] >= 0)
+    return same & (keys[None, :] <= rows[:, None]) if causal else same
 
 
 def _chunk_max(x):
@@ -305,7 +315,8 @@ def validate_forward(orc, g, cu, softmax_scale=None):
     Hkv = g["k"].shape[1]
     grp = Hq // Hkv
     c32 = score_scale32(d, softmax_scale)
-    vis = visible_mask(cu, T, win)
+    causal = g.get("causal", True)
+    vis = visible_mask(cu, T, win, causal)
     hs = range(win["head_lo"], win["head_hi"])
     rows = slice(win["row_lo"], win["row_hi"])
     keys = slice(win["key_lo"], win["key_hi"])
@@ -328,7 +339,8 @@ def validate_forward(orc, g, cu, softmax_scale=None):
         assert (err <= bound).all(), "score beyond the accumulation bound"
     say("  scores vs exact dot products: max error / bound %.3f" % worst)
     # 3. running maxima, recomputed in FP32 from the GPU's own scores (per document, key tiles
-    # counted from its start, from the diagonal tile down)
+    # counted from its start, from the row's last visible tile down: the diagonal one, or the
+    # document's last without the causal mask)
     dm = doc_map(cu, T)
     n_m = 0
     for doc in sorted(set(dm[win["row_lo"]:win["row_hi"]]) - {-1}):
@@ -343,7 +355,7 @@ def validate_forward(orc, g, cu, softmax_scale=None):
         t = pad.reshape(s_doc.shape[:2] + (nkt, 128))
         with np.errstate(invalid="ignore"):
             mx = np.where(np.isnan(t), -np.inf, t).max(-1).astype(np.float32)          # [h, r, tiles]
-        diag = (np.arange(r0, r1) - a) // 128
+        diag = (np.arange(r0, r1) - a) // 128 if causal else np.full(r1 - r0, nkt - 1)
         above = np.arange(nkt)[None, :] > diag[:, None]                              # tiles not visited
         scaled = np.where(above[None], np.float32(-np.inf), (mx * c32).astype(np.float32))
         m_exp = np.maximum.accumulate(scaled[..., ::-1], axis=-1)[..., ::-1]         # from the diagonal down
@@ -362,7 +374,7 @@ def validate_forward(orc, g, cu, softmax_scale=None):
     say("  probability codes: %d / %d at a rounding boundary, the rest equal the oracle's rounding" % (nbad, ntot))
     # 5. products: O and LSE against the replay on the GPU's decisions
     o64, lse64 = orc.fwd_replay(g["v"], g["sv"], cu, win, S.astype(np.float64), M.astype(np.float64), P, Hq,
-                                float(c32))
+                                float(c32), causal=causal)
     rmask = dm[win["row_lo"]:win["row_hi"]] >= 0
     got_o = np.transpose(g["o"][rows][:, win["head_lo"]:win["head_hi"]], (1, 0, 2))
     beyond = bar_check("O", got_o[:, rmask], o64[:, rmask], orc)
@@ -387,7 +399,8 @@ def validate_backward(orc, g, cu, causal_dq=False, softmax_scale=None):
     grp = Hq // Hkv
     ss = 1.0 / np.sqrt(d) if not softmax_scale else softmax_scale
     c32 = score_scale32(d, softmax_scale)
-    vis = visible_mask(cu, T, win)
+    causal = g.get("causal", True)
+    vis = visible_mask(cu, T, win, causal)
     hs = list(range(win["head_lo"], win["head_hi"]))
     rows = slice(win["row_lo"], win["row_hi"])
     keys = slice(win["key_lo"], win["key_hi"])
@@ -436,7 +449,7 @@ def validate_backward(orc, g, cu, causal_dq=False, softmax_scale=None):
                                                                    counts["ds"][0], counts["ds"][1], counts["dse"]))
     # 5'. products against the replay on the GPU's decisions
     r = orc.bwd_replay(g["q"], g["sq"], g["k"], g["sk"], g["do"], g["sdo"], cu, pi, win, du["bwd_p"], du["bwd_ps"],
-                       du["bwd_ds"], du["bwd_dss"], ss)
+                       du["bwd_ds"], du["bwd_dss"], ss, causal=causal)
     rmask = dm[win["row_lo"]:win["row_hi"]] >= 0
     got_dq = np.transpose(g["dq"][rows][:, win["head_lo"]:win["head_hi"]], (1, 0, 2))
     dq16 = validate_dq_partials(orc, g, cu, pi, ss)
@@ -473,6 +486,7 @@ def validate_dq_partials(orc, g, cu, pi, ss):
     win, du = g["window"], g["dumps"]
     T, Hq, d = g["q"].shape
     grp = Hq // g["k"].shape[1]
+    causal = g.get("causal", True)
     parts = du["dq_part"]                                                    # [h, r, tiles, d]
     kd = dequant(g["k"], g["sk"])
     dm = doc_map(cu, T)
@@ -486,8 +500,8 @@ def validate_dq_partials(orc, g, cu, pi, ss):
         rs = slice(r0 - win["row_lo"], r1 - win["row_lo"])
         L = b - a
         nkt = -(-L // 128)
-        vis = visible_mask(cu, T, win)[rs, a - win["key_lo"]:b - win["key_lo"]]
-        last = (np.arange(r0, r1) - a) // 128                                 # last key tile of each row
+        vis = visible_mask(cu, T, win, causal)[rs, a - win["key_lo"]:b - win["key_lo"]]
+        last = (np.arange(r0, r1) - a) // 128 if causal else np.full(r1 - r0, nkt - 1)  # last key tile of each row
         for x, h in enumerate(range(win["head_lo"], win["head_hi"])):
             dsh = orc.e4m3_decode(du["bwd_ds"][x, rs, a - win["key_lo"]:b - win["key_lo"]]) * \
                 np.exp2(du["bwd_dss"][x, rs, a - win["key_lo"]:b - win["key_lo"]].astype(np.float64) - 127)
@@ -544,6 +558,9 @@ def chain_check(orc, g, ref, cu, fwd_val, bwd_val, zero_in_exact=()):
                   ("dV", g["dv"][rows][kmask][:, kv], ref["dv"][rows][kmask][:, kv],
                    np.transpose(bwd_val["replay"]["dv64"][kv], (1, 0, 2))[kmask])]
     for nm, gb, rb, rep in items:
+        if not gb.size:
+            say("  chain %-3s: no rows in the window (non-causal keys outside a document-start window)" % nm)
+            continue
         gv, rv = bits_to_f64(gb), bits_to_f64(rb)
         repv = bits_to_f64(orc.bf16_rne(rep))
         c = cosine(gv, rv)
@@ -590,14 +607,15 @@ def doc_window(cu, doc, heads, tail_blocks=0):
     return dict(row_lo=r0, row_hi=b, key_lo=a, key_hi=b, head_lo=heads[0], head_hi=heads[1])
 
 
-def stage_and_chain(orc, q, k, v, do, cu, window, causal_dq=False, release=None, tail=False, zero_in_exact=()):
+def stage_and_chain(orc, q, k, v, do, cu, window, causal_dq=False, release=None, tail=False, zero_in_exact=(),
+                    causal=True):
     """Debug run in `window` (compared bit for bit with the product library's run `release`, made
     here if not given), decision checks and replays (stage), then the oracle's own chain (its
     work restricted to the window's documents, KV heads and, with tail=True, document tail)."""
     cu = np.asarray(cu, np.int32)
     if release is None:
-        release = gpu_call(q, k, v, do, cu, causal_dq)
-    g = gpu_call(q, k, v, do, cu, causal_dq, window=window)
+        release = gpu_call(q, k, v, do, cu, causal_dq, causal=causal)
+    g = gpu_call(q, k, v, do, cu, causal_dq, window=window, causal=causal)
     same_outputs(g, release)
     say("  debug variant: outputs bit-identical to libflamia.so")
     fv = validate_forward(orc, g, cu)
@@ -611,7 +629,7 @@ def stage_and_chain(orc, q, k, v, do, cu, window, causal_dq=False, release=None,
     if tail:
         tr = window["row_hi"] - window["row_lo"]
         kw.update(tail_rows=tr, tail_blocks=-(-tr // 32))
-    ref = oracle_call(orc, q, k, v, do, cu, causal_dq, **kw)
+    ref = oracle_call(orc, q, k, v, do, cu, causal_dq, causal=causal, **kw)
     chain_check(orc, g, ref, cu, fv, bv, zero_in_exact)
     return g
 

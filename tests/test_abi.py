@@ -51,16 +51,20 @@ def test_size_queries(lib):
     mid = lib.flamia_bwd_workspace_bytes(4, T, Hq, d, 100 * Hq * blk)
     assert mid - lo == (100 - 2 * 16) * Hq * blk                                      # budget honoured
     hi = lib.flamia_bwd_workspace_bytes(4, T, Hq, d, 1 << 40)
-    worst = (T * T) // 16384 + 5 * T // 128 + 3 + (T + 63) // 64
-    assert hi - lo == (worst - 2 * 16) * Hq * blk                                     # clamped down
+    worst_nc = (T * T) // 8192 + 5 * T // 64 + 3 + (T + 63) // 64           # one chunk, non-causal bound
+    assert hi - lo == (worst_nc - 2 * 16) * Hq * blk                                  # clamped down
     assert lib.flamia_bwd_workspace_bytes(4, T, Hq, 96, 0) == 0                       # bad d
     # one chunk for known lengths: the call's stored blocks plus the largest key tile
     cu = np.array([0, 100, 100, 612, 1000], np.int32)       # lengths 100, 0, 512, 388
     blocks = 0 + 0 + (4 * 8 - 4 * 3) + (4 * 7 - 4 * 3)     # n_kt n_qt - n_kt (n_kt - 1), 1-tile docs: 0
-    got = lib.flamia_bwd_workspace_bytes_for(cu.ctypes.data_as(ctypes.c_void_p), 4, T, Hq, d)
+    got = lib.flamia_bwd_workspace_bytes_for(cu.ctypes.data_as(ctypes.c_void_p), 4, T, Hq, d, 0)
     assert got - (lo - 2 * 16 * Hq * blk) == (blocks + 16) * Hq * blk
-    assert lib.flamia_bwd_workspace_bytes_for(None, 3, T, Hq, d) == 0                  # host lengths required
+    blocks_nc = 0 + 0 + 4 * 8 + 4 * 7                        # non-causal: every (query tile, key tile) pair
+    got_nc = lib.flamia_bwd_workspace_bytes_for(cu.ctypes.data_as(ctypes.c_void_p), 4, T, Hq, d, 1)
+    assert got_nc - (lo - 2 * 16 * Hq * blk) == (blocks_nc + 16) * Hq * blk
+    assert lib.flamia_bwd_workspace_bytes_for(None, 3, T, Hq, d, 0) == 0               # host lengths required
     assert fl.bwd_workspace_bytes_for(cu, T, Hq, d) == got
+    assert fl.bwd_workspace_bytes_for(cu, T, Hq, d, causal=False) == got_nc
     assert fl.bwd_workspace_bytes(4, T, Hq, d, 0) == lo
 
 
@@ -89,3 +93,14 @@ def test_host_validation_errors(lib):
     assert lib.flamia_bwd(ctypes.byref(b), None) == 4          # workspace too small
     b.workspace_bytes = lib.flamia_bwd_workspace_bytes(1, 100, 4, 64, 0) - 1
     assert lib.flamia_bwd(ctypes.byref(b), None) == 4          # one byte short of the smallest
+    b.workspace_bytes = lib.flamia_bwd_workspace_bytes(1, 100, 4, 64, 0)
+    b.non_causal, b.causal_dq_scale = 1, 1
+    assert lib.flamia_bwd(ctypes.byref(b), None) == 3          # causal dQ prescale needs causal attention
+
+
+def test_list_kinds(lib):
+    fake = 1 << 20
+    for kind in (0, 1, 2, 3):      # causal and non-causal forward / backward lists
+        assert lib.flamia_build_worklist(fake, 1, 1000, kind, 4, fake, 16, None) == 4
+    assert lib.flamia_build_worklist(fake, 1, 1000, 4, 4, fake, 1 << 20, None) == 2   # unknown kind
+    assert lib.flamia_status_str(6) == b"call too large for the static scratch"

@@ -15,22 +15,24 @@ T, Hq, Hkv, d = 520, 2, 1, 64
 CU = np.array([0, 129, 257, 520], np.int32)
 
 
-def _fake_gpu(orc, causal_dq=False):
+def _fake_gpu(orc, causal_dq=False, causal=True):
     q, k, v, do = workloads.tensors(T, Hq, Hkv, d, seed=190)
-    r = gc.oracle_call(orc, q, k, v, do, CU, causal_dq)
+    r = gc.oracle_call(orc, q, k, v, do, CU, causal_dq, causal=causal)
     ss = 1.0 / np.sqrt(d)
     win = gc.full_window(T, Hq)
-    _, lse, _, dumps = orc.fwd(r["q"], r["sq"], r["k"], r["sk"], r["v"], r["sv"], CU, ss, want_o64=True, window=win)
+    _, lse, _, dumps = orc.fwd(r["q"], r["sq"], r["k"], r["sk"], r["v"], r["sv"], CU, ss, want_o64=True, window=win,
+                               causal=causal)
     b = orc.bwd(r["q"], r["sq"], r["k"], r["sk"], r["v"], r["sv"], r["do"], r["sdo"], lse, r["D"], CU, ss,
-                causal_dq=causal_dq, window=win)
+                causal_dq=causal_dq, window=win, causal=causal)
     S = dumps["fwd_s"].astype(np.float32)
     c32 = gc.score_scale32(d)
     M = np.full(S.shape, np.nan, np.float32)
     for a, e in zip(CU[:-1], CU[1:]):
         for i in range(a, e):
             run = np.float32(-np.inf)
-            for kt in range((i - a) // 128, -1, -1):
-                cols = slice(a + 128 * kt, min(e, a + 128 * kt + 128, i + 1))
+            last = i if causal else e - 1
+            for kt in range((last - a) // 128, -1, -1):
+                cols = slice(a + 128 * kt, min(e, a + 128 * kt + 128, last + 1))
                 run = np.maximum(run, (np.nanmax(S[:, i, cols], axis=1) * c32).astype(np.float32))
                 M[:, i, cols] = run[:, None]
     g = dict(r)
@@ -38,9 +40,10 @@ def _fake_gpu(orc, causal_dq=False):
                       bwd_dp=b["dumps"]["bwd_dp"].astype(np.float32),
                       **{n: b["dumps"][n] for n in ("bwd_p", "bwd_ps", "bwd_ds", "bwd_dss")})
     g["window"] = win
+    g["causal"] = causal
     # each key tile's dQ partial times 2^pi from the oracle's dShat codes, stored in FP32 as the
     # GPU converts it; dQ then follows from those partials as the method forms it
-    vis = gc.visible_mask(CU, T, win)
+    vis = gc.visible_mask(CU, T, win, causal)
     dsh = orc.e4m3_decode(g["dumps"]["bwd_ds"]) * np.exp2(g["dumps"]["bwd_dss"].astype(np.float64) - 127)
     dsh = np.where(vis[None], dsh, 0.0)
     kd = gc.dequant(r["k"], r["sk"])
@@ -49,7 +52,7 @@ def _fake_gpu(orc, causal_dq=False):
     for a, e in zip(CU[:-1], CU[1:]):
         for kt in range(-(-(e - a) // 128)):
             ks = slice(a + 128 * kt, min(e, a + 128 * kt + 128))
-            rows = slice(a + 128 * kt, e)
+            rows = slice(a + 128 * kt if causal else a, e)
             for h in range(Hq):
                 parts[h, rows, kt] = (dsh[h, rows, ks] @ kd[ks, h // (Hq // Hkv)]) * \
                     np.exp2(r["pi"][h, rows].astype(np.float64))[:, None]
@@ -64,9 +67,18 @@ def _run(orc, g, r):
     gc.chain_check(orc, g, r, CU, fv, bv)
 
 
-def test_gate_accepts_the_oracle_stand_in(orc):
-    g, r = _fake_gpu(orc)
+@pytest.mark.parametrize("causal", [True, False], ids=["causal", "non-causal"])
+def test_gate_accepts_the_oracle_stand_in(orc, causal):
+    g, r = _fake_gpu(orc, causal=causal)
     _run(orc, g, r)
+
+
+def test_gate_rejects_causal_decisions_for_non_causal_attention(orc):
+    """The non-causal gate needs the pairs above the diagonal: a causal run fails it."""
+    g, r = _fake_gpu(orc)
+    g["causal"] = False
+    with pytest.raises(AssertionError):
+        gc.validate_forward(orc, g, CU)
 
 
 def _far_from_boundary(orc, codes, values, vis):

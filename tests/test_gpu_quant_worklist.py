@@ -101,7 +101,7 @@ def _list_case(orc, cu, G=None):
     T = int(cu[-1])
     cu_d = torch.as_tensor(cu).cuda()
     G = G or fl.num_workers()
-    for kind in (0, 1):
+    for kind in (0, 1, 2, 3):      # causal and non-causal forward / backward lists
         buf = fl.build_worklist(cu_d, T, kind, G)
         n, items = fl.worklist_items(buf)
         ref = orc.worklist(cu, kind, G)
