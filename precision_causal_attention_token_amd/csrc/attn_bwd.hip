@@ -146,7 +146,8 @@ __device__ __forceinline__ void issue_step_loads(const BwdParams& p, BwdSmem<D>&
 // length), so work that either role can do is given to the consumer.
 // Phase k: producers finish step k and form the products of step k + 1, consumers work on step
 // k - 1 and load step k + 2; one barrier per phase.
-template <int D>
+// CAUSAL: keys after the query are masked (else every key of the document is visible).
+template <int D, bool CAUSAL>
 __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
   constexpr int NC = D / 64;
   constexpr int NDB = D / 32;
@@ -192,7 +193,7 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
     // Steps run over (query head of the group, 64-query tile from the diagonal to the
     // document end).
     // query tiles that see this key tile: from its diagonal on (causal) or all of them
-    const int qt_first = p.causal_mask ? 2 * kappa : 0;
+    const int qt_first = CAUSAL ? 2 * kappa : 0;
     const int nq = n_qt - qt_first;  // query tiles per head
     const int n_steps = grp * nq;
 
@@ -341,7 +342,7 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
         float pmax = 0.f, dmax = 0.f;
         // element i sits in row 32 qs + 4 hh + r_i (r_i = 8 (i / 4) + i % 4, a constant): it is
         // visible when lo <= r_i < hi (non-causally every row is when the key is in the document)
-        const int lo = p.causal_mask ? key_rel - (q0 + 32 * qs + 4 * hh) : (key_rel < L ? -QT : QT);
+        const int lo = CAUSAL ? key_rel - (q0 + 32 * qs + 4 * hh) : (key_rel < L ? -QT : QT);
         const int hi = L - (q0 + 32 * qs + 4 * hh);
 #pragma unroll
         for (int m = 0; m < NM; ++m) {
@@ -442,16 +443,20 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
         }
       };
       products(0, 0, cs, cp);
+      // once per unit: the loop's paths (a step-less one among them, never taken) may touch these
+      // registers soon after the products are issued
+      mfma_drain(cs);
+      mfma_drain(cp);
       int cur_h = g * grp, cur_qt = qt_first;  // head and query tile of step ph
       // all 64 x 128 pairs of a step are visible when the query tile lies wholly inside the
       // document and, causally, below the key tile (then every key of the tile is inside the
       // document too) or, non-causally, when the key tile is wholly inside it as well
-      const bool keys_full = !p.causal_mask && KV_TILE * kappa + KV_TILE <= L;
+      const bool keys_full = !CAUSAL && KV_TILE * kappa + KV_TILE <= L;
       for (int ph = 0; ph <= n_steps; ++ph) {
         if (ph < n_steps) {
           // all 64 x 128 pairs visible: the query tile lies wholly below the key tile and
           // inside the document (then every key of the tile is inside it too)
-          if ((p.causal_mask ? cur_qt >= 2 * kappa + 2 : keys_full) && QT * cur_qt + QT <= L)
+          if ((CAUSAL ? cur_qt >= 2 * kappa + 2 : keys_full) && QT * cur_qt + QT <= L)
             phase_body(ph, cur_h, cur_qt, std::false_type{});
           else phase_body(ph, cur_h, cur_qt, std::true_type{});
           if (++cur_qt == n_qt) {
@@ -700,6 +705,8 @@ __device__ __forceinline__ void dq_store(const DqRegs<D>& r, DqSmem<D>& sm, int 
   if (tid < KV_TILE) sm.sk[b][tid] = tid < r.nkeys ? (uint8_t)r.skb : (uint8_t)127;
 }
 
+// Causality is a run-time flag here (p.causal_mask): two instantiations allocate registers
+// differently enough that one keeps a spill reload inside the key-tile loop.
 template <int D>
 __global__ __launch_bounds__(DQ_THREADS, 2) void dq_kernel(BwdParams p) {  // two workgroups per CU
   constexpr int NDB = D / 32;
@@ -719,6 +726,8 @@ __global__ __launch_bounds__(DQ_THREADS, 2) void dq_kernel(BwdParams p) {  // tw
   const int grp = p.Hq / p.Hkv;
   const int t4 = wave >> 1, s = wave & 1;     // query tile of the unit, byte-position half
   const int qrow = ds_pos_query(32 * s + n);  // query offset in the tile held by this lane
+  int lane_zero;                              // 0, opaque: keeps a load's result in vector registers
+  asm volatile("v_mov_b32 %0, 0" : "=v"(lane_zero));
   const int qb_l = n >> 4;                    // its 32-query block
 
   for (int round = 0;; ++round) {
@@ -861,12 +870,16 @@ __global__ __launch_bounds__(DQ_THREADS, 2) void dq_kernel(BwdParams p) {  // tw
     // one tile: loads of kappa + 2 into `spare`, compute kappa, `next` (kappa + 1) into LDS.  The
     // loads are issued on every tile (the last two re-read tile kappa_hi, unused) so that the
     // count of loads in flight does not depend on the path.
-    // The store offset of the tile loaded next (kappa + 2) is read one tile earlier, so the loads'
-    // addresses never wait for it.
+    // The store offset of tile kappa + 3 is read one tile ahead of its loads and before this
+    // tile's loads, so waiting for it at the next tile leaves those in flight.  Its index goes
+    // through a register that differs per lane in the compiler's view (zero in every lane): a
+    // uniform value would be moved to scalar registers at once, which waits for every load
+    // issued before that point, this tile's included.
     int64_t off_n = 0;
     auto tile = [&](int kappa, DqRegs<D>& next, DqRegs<D>& spare) __attribute__((always_inline)) {
-      dq_load<D>(spare, p, doc_start, L, n_qt, off_n, qt0, g, h, min(kappa + 2, kappa_hi));
-      off_n = p.kv_off[tb + min(kappa + 3, kappa_hi)];
+      const int64_t off = off_n;
+      off_n = p.kv_off[tb + min(kappa + 3, kappa_hi) + lane_zero];
+      dq_load<D>(spare, p, doc_start, L, n_qt, off, qt0, g, h, min(kappa + 2, kappa_hi));
       compute(kappa);
       if (kappa + 1 <= kappa_hi) dq_store<D>(next, sm, (kappa + 1) & 1);
       lds_barrier();
@@ -875,7 +888,7 @@ __global__ __launch_bounds__(DQ_THREADS, 2) void dq_kernel(BwdParams p) {  // tw
     lds_barrier();  // the previous unit no longer reads LDS
     dq_load<D>(ra, p, doc_start, L, n_qt, p.kv_off[tb + k_lo], qt0, g, h, k_lo);
     dq_load<D>(rb, p, doc_start, L, n_qt, p.kv_off[tb + min(k_lo + 1, kappa_hi)], qt0, g, h, min(k_lo + 1, kappa_hi));
-    off_n = p.kv_off[tb + min(k_lo + 2, kappa_hi)];
+    off_n = p.kv_off[tb + min(k_lo + 2, kappa_hi) + lane_zero];
     dq_store<D>(ra, sm, k_lo & 1);
     lds_barrier();
     for (int kappa = k_lo;; kappa += 2) {  // two tiles per trip: the register sets trade roles
@@ -1184,16 +1197,20 @@ hipError_t launch_bwd(const BwdParams& p, int d, int grid, hipStream_t s) {
   // dQ pass consumes it (stream order keeps the two apart and the chunks in sequence)
   if (d == 128) hipLaunchKernelGGL(bwd_prologue<128>, dim3(p.Hq + 1), dim3(PRO_THREADS), 0, s, p);
   else hipLaunchKernelGGL(bwd_prologue<64>, dim3(p.Hq + 1), dim3(PRO_THREADS), 0, s, p);
-  for (int c = 0; c < p.max_chunks; ++c) {
-    BwdParams q = p;
-    q.chunk = c;
-    if (d == 128) {
-      hipLaunchKernelGGL(bwd_kernel<128>, dim3(grid), dim3(BWD_THREADS), 0, s, q);
-      hipLaunchKernelGGL(dq_kernel<128>, dim3(2 * grid), dim3(DQ_THREADS), 0, s, q);
-    } else {
-      hipLaunchKernelGGL(bwd_kernel<64>, dim3(grid), dim3(BWD_THREADS), 0, s, q);
-      hipLaunchKernelGGL(dq_kernel<64>, dim3(2 * grid), dim3(DQ_THREADS), 0, s, q);
+  auto chunks = [&](auto bk, auto dk) {
+    for (int c = 0; c < p.max_chunks; ++c) {
+      BwdParams q = p;
+      q.chunk = c;
+      hipLaunchKernelGGL(bk, dim3(grid), dim3(BWD_THREADS), 0, s, q);
+      hipLaunchKernelGGL(dk, dim3(2 * grid), dim3(DQ_THREADS), 0, s, q);
     }
+  };
+  if (d == 128) {
+    if (p.causal_mask) chunks(bwd_kernel<128, true>, dq_kernel<128>);
+    else chunks(bwd_kernel<128, false>, dq_kernel<128>);
+  } else {
+    if (p.causal_mask) chunks(bwd_kernel<64, true>, dq_kernel<64>);
+    else chunks(bwd_kernel<64, false>, dq_kernel<64>);
   }
   return hipGetLastError();
 }

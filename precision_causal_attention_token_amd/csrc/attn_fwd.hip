@@ -129,7 +129,8 @@ __device__ __forceinline__ void store_scales(FwdSmem<D>& sm, int kb, int vb, uin
   else if (tid < 2 * KV_TILE) sm.sv[vb][tid - KV_TILE] = (uint8_t)sc;
 }
 
-template <int D, int W>
+// CAUSAL: keys after the query are masked (else every key of the document is visible).
+template <int D, int W, bool CAUSAL>
 __global__ __launch_bounds__(fwd_threads<W>(), 8 / W) void fwd_kernel(FwdParams p) {
   constexpr int FWD_THREADS = fwd_threads<W>();
   constexpr int NC = D / 64;   // 64-wide d chunks of the score contraction
@@ -165,9 +166,9 @@ __global__ __launch_bounds__(fwd_threads<W>(), 8 / W) void fwd_kernel(FwdParams 
     const bool row_valid = q_rel < L;
     // this wave's first (diagonal) tile: causal, the tile of its queries; non-causal, the
     // document's last key tile, the one every row starts from
-    const int kd = p.causal ? q_wave / KV_TILE : (L - 1) / KV_TILE;
+    const int kd = CAUSAL ? q_wave / KV_TILE : (L - 1) / KV_TILE;
     const int last_row = min(q0 + QU, L) - 1;
-    const int kappa_hi = p.causal ? last_row / KV_TILE : (L - 1) / KV_TILE;
+    const int kappa_hi = CAUSAL ? last_row / KV_TILE : (L - 1) / KV_TILE;
 
     // Q operand (B of S^T): lane (n, hh) holds d = 64c + 32hh .. +31 of query n.
     v8i qop[NC];
@@ -236,8 +237,10 @@ __global__ __launch_bounds__(fwd_threads<W>(), 8 / W) void fwd_kernel(FwdParams 
           // 32 kb4 + acc_row(i, 0) exceeds lim; lim is formed here, opaque to the compiler, so
           // the 64 comparisons stay in this branch instead of held as lane masks in scalar
           // registers across the loop
-          int lim = (p.causal ? q_rel : L - 1) - KV_TILE * kappa - 4 * hh;
+          int lim = (CAUSAL ? q_rel : L - 1) - KV_TILE * kappa - 4 * hh;
           asm volatile("" : "+v"(lim));
+#pragma unroll
+          for (int kb4 = 0; kb4 < 4; ++kb4) mfma_drain(s[kb4]);  // the mask may follow the last product closely
 #pragma unroll
           for (int kb4 = 0; kb4 < 4; ++kb4)
 #pragma unroll
@@ -402,13 +405,18 @@ __global__ __launch_bounds__(fwd_threads<W>(), 8 / W) void fwd_kernel(FwdParams 
 hipError_t launch_fwd(const FwdParams& p, int d, int grid, hipStream_t s) {
   // documents of fewer than 4096 tokens on average: 128-query units, two workgroups per CU
   const bool short_docs = (int64_t)p.n_docs * 4096 > (int64_t)p.T;
-  if (short_docs) {
-    if (d == 128) hipLaunchKernelGGL((fwd_kernel<128, 4>), dim3(2 * grid), dim3(fwd_threads<4>()), 0, s, p);
-    else hipLaunchKernelGGL((fwd_kernel<64, 4>), dim3(2 * grid), dim3(fwd_threads<4>()), 0, s, p);
-  } else {
-    if (d == 128) hipLaunchKernelGGL((fwd_kernel<128, 8>), dim3(grid), dim3(fwd_threads<8>()), 0, s, p);
-    else hipLaunchKernelGGL((fwd_kernel<64, 8>), dim3(grid), dim3(fwd_threads<8>()), 0, s, p);
-  }
+  auto go = [&](auto c) {
+    constexpr bool C = decltype(c)::value;
+    if (short_docs) {
+      if (d == 128) hipLaunchKernelGGL((fwd_kernel<128, 4, C>), dim3(2 * grid), dim3(fwd_threads<4>()), 0, s, p);
+      else hipLaunchKernelGGL((fwd_kernel<64, 4, C>), dim3(2 * grid), dim3(fwd_threads<4>()), 0, s, p);
+    } else {
+      if (d == 128) hipLaunchKernelGGL((fwd_kernel<128, 8, C>), dim3(grid), dim3(fwd_threads<8>()), 0, s, p);
+      else hipLaunchKernelGGL((fwd_kernel<64, 8, C>), dim3(grid), dim3(fwd_threads<8>()), 0, s, p);
+    }
+  };
+  if (p.causal) go(std::true_type{});
+  else go(std::false_type{});
   return hipGetLastError();
 }
 

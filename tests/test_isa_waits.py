@@ -9,10 +9,10 @@ import pytest
 from precision_causal_attention_token_amd import build
 from tests import isa_waits
 
-# (source, symbol pattern, instantiations: head dims 64 and 128, times the forward's two
-# workgroup shapes)
-KERNELS = [("attn_fwd.hip", r"_ZN6flamia12_GLOBAL__N_110fwd_kernelI\w+", 4),
-           ("attn_bwd.hip", r"_ZN6flamia12_GLOBAL__N_110bwd_kernelI\w+", 2),
+# (source, symbol pattern, instantiations: head dims 64 and 128, times causal and non-causal for
+# the forward and key-tile kernels, times the forward's two workgroup shapes)
+KERNELS = [("attn_fwd.hip", r"_ZN6flamia12_GLOBAL__N_110fwd_kernelI\w+", 8),
+           ("attn_bwd.hip", r"_ZN6flamia12_GLOBAL__N_110bwd_kernelI\w+", 4),
            ("attn_bwd.hip", r"_ZN6flamia12_GLOBAL__N_19dq_kernelI\w+", 2)]
 
 
