@@ -33,7 +33,7 @@ PEAK_HBM_GBPS = 8000.0       # MI355X HBM3E
 # scaled by 2.000 and WRITE by 1.000, the factors a 1 GiB copy gives).  Valid only for the
 # backward sources it was measured on (sha256 prefix over attn_bwd.hip, device_common.h,
 # kernels.h); any other build reports null.
-BWD_TRAFFIC = {"workload": "long", "src": "d350c2342591160a", "read_bytes": 19.73e9, "write_bytes": 13.02e9}
+BWD_TRAFFIC = {"workload": "long", "src": "ddac0e7b57dff6a8", "read_bytes": 20.011e9, "write_bytes": 13.078e9}
 
 
 def parse():
@@ -47,7 +47,8 @@ def parse():
                     help="time the non-causal variant (every key of a row's document visible)")
     ap.add_argument("--store-gb", type=float, default=None,
                     help="cap the backward's dShat store at this many GiB (chunked backward); default: one chunk")
-    ap.add_argument("--cpu-pairs", type=float, default=2.0e7, help="query-key pairs in the CPU-oracle sample")
+    ap.add_argument("--cpu-pairs", type=float, default=1.5e8,
+                    help="query-key pairs (summed over heads) in the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibration-copy-mb", type=int, default=0,
                     help="before warmup, run one plain device-to-device copy of this many MiB (reference "
@@ -66,8 +67,9 @@ def bwd_source_hash():
 
 def cpu_baseline(workload_name, pairs_budget):
     """Time the oracle (test infrastructure, untuned) on a bounded sample: documents of the
-    workload in order, each truncated to 4096 tokens, one head, until pairs_budget
-    query-key pairs are covered."""
+    workload in order, each truncated to 4096 tokens, until pairs_budget query-key pairs per
+    head are covered; then the query heads of the first KV heads, whole groups, until
+    pairs_budget pairs in all (or every head)."""
     import numpy as np
     import torch
 
@@ -87,22 +89,25 @@ def cpu_baseline(workload_name, pairs_budget):
             break
     idx = np.concatenate([np.arange(a, b) for a, b in spans])
     cs = workloads.cu_seqlens(lens)
+    grp = shp.Hq // shp.Hkv
+    n_kv = min(shp.Hkv, max(1, -(-int(pairs_budget) // (pairs * grp))))
+    n_q = n_kv * grp
 
-    def bits(x):
-        return x[idx][:, :1].contiguous().view(torch.int16).numpy().view(np.uint16)
+    def bits(x, nh):
+        return x[idx][:, :nh].contiguous().view(torch.int16).numpy().view(np.uint16)
 
     oracle.lib()
     t0 = time.perf_counter()
-    qc = [oracle.quantize(bits(x), cs) for x in (q, k, v)]
+    qc = [oracle.quantize(bits(x, nh), cs) for x, nh in ((q, n_q), (k, n_kv), (v, n_kv))]
     o, lse, _ = oracle.fwd(*qc[0], *qc[1], *qc[2], cs)
-    dc, dsc, D = oracle.quantize_do(bits(do), o, cs)
+    dc, dsc, D = oracle.quantize_do(bits(do, n_q), o, cs)
     oracle.bwd(*qc[0], *qc[1], *qc[2], dc, dsc, lse, D, cs)
     dt = time.perf_counter() - t0
-    flop = 14.0 * shp.d * 1 * pairs
+    flop = 14.0 * shp.d * n_q * pairs
     return {"value": flop / dt / 1e12, "unit": "TFLOPS", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": "%s workload: first %d documents (each truncated to 4096 tokens, %d tokens), head 0 only, "
-                      "%d query-key pairs; quantise + forward + dO pass + backward in %.2f s"
-                      % (workload_name, len(lens), len(idx), pairs, dt),
+            "sample": "%s workload: first %d documents (each truncated to 4096 tokens, %d tokens), query heads "
+                      "0..%d (KV heads 0..%d), %d query-key pairs per head; quantise + forward + dO pass + "
+                      "backward in %.2f s" % (workload_name, len(lens), len(idx), n_q - 1, n_kv - 1, pairs, dt),
             "seconds": dt}
 
 
