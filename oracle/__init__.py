@@ -103,15 +103,38 @@ def e8m0_floor(a):
 
 # ---------------------------------------------------------------------------------------
 # the method
-def quantize(x_bits, cu, floor_rule=False):
-    """Token-block quantiser: returns (codes [T,H,d] u8, scales [H,T] u8)."""
+def quantize(x_bits, cu, floor_rule=False, hadamard=False):
+    """Token-block quantiser: returns (codes [T,H,d] u8, scales [H,T] u8).  hadamard=True rotates
+    each (token, head) row first (see hadamard())."""
     x = _c(x_bits, np.uint16)
     T, H, d = x.shape
     cu = _c(cu, np.int32)
     codes = np.empty((T, H, d), np.uint8)
     scales = np.empty((H, T), np.uint8)
-    lib().orc_quantize(_p(x), T, H, d, _p(cu), len(cu) - 1, _p(codes), _p(scales), int(bool(floor_rule)))
+    if hadamard:
+        assert not floor_rule
+        lib().orc_quantize_hadamard(_p(x), T, H, d, _p(cu), len(cu) - 1, _p(codes), _p(scales))
+    else:
+        lib().orc_quantize(_p(x), T, H, d, _p(cu), len(cu) - 1, _p(codes), _p(scales), int(bool(floor_rule)))
     return codes, scales
+
+
+def hadamard(x):
+    """Rows of the last axis (FP32) times H / sqrt(d): FP32 butterflies, strides 1, 2, ..., d/2,
+    then the FP32 multiply by RN32(1 / sqrt(d)).  Returns a new float32 array."""
+    x = np.array(x, dtype=np.float32, order="C", copy=True)
+    d = x.shape[-1]
+    lib().orc_hadamard(_p(x), ctypes.c_long(x.size // d), d)
+    return x
+
+
+def unrotate_bf16(bits):
+    """BF16 gradient rows (last axis d) back to the inputs' basis: BF16(hadamard(row))."""
+    b = _c(bits, np.uint16)
+    d = b.shape[-1]
+    out = np.empty(b.shape, np.uint16)
+    lib().orc_unrotate_bf16(_p(b), _p(out), ctypes.c_long(b.size // d), d)
+    return out
 
 
 def worklist(cu, kind, n_workers):

@@ -163,8 +163,9 @@ double orc_f16_decode(uint16_t h) {
  * Tokens outside every document get code 0 and scale byte 0.
  * floor_rule = 1 selects the leaking floor exponent (with clipping) as a test foil.
  * ---------------------------------------------------------------------------------- */
-void orc_quantize(const uint16_t* x, int T, int H, int d, const int32_t* cu, int n_docs,
-                  uint8_t* codes, uint8_t* scales, int floor_rule) {
+/* The block rule on decoded values v [T][H][d] (double). */
+static void quantize_values(const double* v, int T, int H, int d, const int32_t* cu, int n_docs,
+                            uint8_t* codes, uint8_t* scales, int floor_rule) {
   int k, h, t, c;
   memset(codes, 0, (size_t)T * H * d);
   memset(scales, 0, (size_t)H * T);
@@ -178,14 +179,14 @@ void orc_quantize(const uint16_t* x, int T, int H, int d, const int32_t* cu, int
         int s;
         for (t = t0; t < t1; ++t)
           for (c = 0; c < d; ++c) {
-            double a = fabs(orc_bf16_decode(x[((size_t)t * H + h) * d + c]));
+            double a = fabs(v[((size_t)t * H + h) * d + c]);
             if (a > amax || isnan(a)) amax = a;
           }
         s = floor_rule ? orc_e8m0_floor(amax) : orc_e8m0_roundup(amax);
         for (t = t0; t < t1; ++t) {
           scales[(size_t)h * T + t] = (uint8_t)(s + 127);
           for (c = 0; c < d; ++c) {
-            double y = ldexp(orc_bf16_decode(x[((size_t)t * H + h) * d + c]), -s);
+            double y = ldexp(v[((size_t)t * H + h) * d + c], -s);
             if (floor_rule) {
               if (y > E4M3_MAX) y = E4M3_MAX;
               if (y < -E4M3_MAX) y = -E4M3_MAX;
@@ -196,6 +197,75 @@ void orc_quantize(const uint16_t* x, int T, int H, int d, const int32_t* cu, int
       }
     }
   }
+}
+
+void orc_quantize(const uint16_t* x, int T, int H, int d, const int32_t* cu, int n_docs,
+                  uint8_t* codes, uint8_t* scales, int floor_rule) {
+  size_t n = (size_t)T * H * d, i;
+  double* v = (double*)malloc((n ? n : 1) * sizeof(double));
+  for (i = 0; i < n; ++i) v[i] = orc_bf16_decode(x[i]);
+  quantize_values(v, T, H, d, cu, n_docs, codes, scales, floor_rule);
+  free(v);
+}
+
+/* ------------------------------------------------------------------------------------
+ * Hadamard rotation of the head dimension (jaehun.me §3.4 "Hadamard rotation", "Quantization
+ * fusion"): each row x of d values becomes x H / sqrt(d), H the d x d Sylvester Hadamard
+ * matrix (H_1 = [1], H_2n = [[H_n, H_n], [H_n, -H_n]]), which is symmetric and, normalised,
+ * its own inverse.  The pages fix neither the precision nor the order of the arithmetic; the
+ * reading taken: FP32 throughout (the inputs are BF16, exact in FP32), the butterflies of the
+ * fast transform for strides 1, 2, 4, ..., d/2 in that order, each pair (a, b) at distance
+ * `stride` (lower index a) becoming (a + b, a - b) rounded to FP32, then every value multiplied
+ * by the FP32 value nearest 1 / sqrt(d) and rounded to FP32.  Each stage's pairs are
+ * independent, so the order within a stage does not matter.  Codes are decided on these FP32
+ * values, so both sides take that decision in the same precision.
+ * ---------------------------------------------------------------------------------- */
+void orc_hadamard(float* x, long n_rows, int d) {
+  const float c = (float)(1.0 / sqrt((double)d));
+  long r;
+  for (r = 0; r < n_rows; ++r) {
+    float* row = x + (size_t)r * d;
+    int stride, i, j;
+    for (stride = 1; stride < d; stride *= 2)
+      for (i = 0; i < d; i += 2 * stride)
+        for (j = i; j < i + stride; ++j) {
+          volatile float a = row[j], b = row[j + stride];
+          volatile float sum = a + b, diff = a - b;
+          row[j] = sum;
+          row[j + stride] = diff;
+        }
+    for (i = 0; i < d; ++i) {
+      volatile float y = row[i] * c;
+      row[i] = y;
+    }
+  }
+}
+
+/* Quantiser with the rotation: each (token, head) row rotated in FP32, then the block rule
+ * on the rotated values. */
+void orc_quantize_hadamard(const uint16_t* x, int T, int H, int d, const int32_t* cu, int n_docs,
+                           uint8_t* codes, uint8_t* scales) {
+  size_t n = (size_t)T * H * d, i;
+  float* f = (float*)malloc((n ? n : 1) * sizeof(float));
+  double* v = (double*)malloc((n ? n : 1) * sizeof(double));
+  for (i = 0; i < n; ++i) f[i] = (float)orc_bf16_decode(x[i]);
+  orc_hadamard(f, (long)T * H, d);
+  for (i = 0; i < n; ++i) v[i] = (double)f[i];
+  quantize_values(v, T, H, d, cu, n_docs, codes, scales, 0);
+  free(f);
+  free(v);
+}
+
+/* Gradients of rotated operands back to the inputs' basis: dX = dX_rot H / sqrt(d) (the
+ * transform is its own inverse), applied to the BF16 gradient rows the backward stores:
+ * FP32 rotation as above, then BF16 round-to-nearest-even. */
+void orc_unrotate_bf16(const uint16_t* in, uint16_t* out, long n_rows, int d) {
+  size_t n = (size_t)n_rows * d, i;
+  float* f = (float*)malloc((n ? n : 1) * sizeof(float));
+  for (i = 0; i < n; ++i) f[i] = (float)orc_bf16_decode(in[i]);
+  orc_hadamard(f, n_rows, d);
+  for (i = 0; i < n; ++i) out[i] = orc_bf16_rne((double)f[i]);
+  free(f);
 }
 
 /* Decoded copy of a whole quantised tensor, [T][H][d] in double (elementwise). */

@@ -167,12 +167,13 @@ def same_outputs(a, b):
 
 
 def oracle_call(orc, q, k, v, do, cu, causal_dq=False, softmax_scale=None, docs=None, kv_heads=None,
-                tail_rows=0, tail_blocks=0, causal=True):
-    """The oracle's own end-to-end chain on the BF16 inputs."""
+                tail_rows=0, tail_blocks=0, causal=True, hadamard=False):
+    """The oracle's own end-to-end chain on the BF16 inputs (hadamard: Q, K rotated before
+    quantisation, dQ, dK rotated back)."""
     cu = np.asarray(cu, np.int32)
     out = {}
     for name, x in (("q", q), ("k", k), ("v", v)):
-        c, s = orc.quantize(bf16_bits(x), cu)
+        c, s = orc.quantize(bf16_bits(x), cu, hadamard=hadamard and name in ("q", "k"))
         out[name], out["s" + name] = c, s
     o, lse, _ = orc.fwd(out["q"], out["sq"], out["k"], out["sk"], out["v"], out["sv"], cu, softmax_scale,
                         docs=docs, kv_heads=kv_heads, tail_rows=tail_rows, causal=causal)
@@ -180,6 +181,9 @@ def oracle_call(orc, q, k, v, do, cu, causal_dq=False, softmax_scale=None, docs=
     g = orc.bwd(out["q"], out["sq"], out["k"], out["sk"], out["v"], out["sv"], dc, dsc, lse, D, cu, softmax_scale,
                 causal_dq=causal_dq, docs=docs, kv_heads=kv_heads, tail_blocks=tail_blocks, causal=causal)
     out.update(do=dc, sdo=dsc, D=D, o=o, lse=lse, dq=g["dq"], dk=g["dk"], dv=g["dv"], pi=g["pi"])
+    if hadamard:
+        out["dq_rot"], out["dk_rot"] = out["dq"], out["dk"]
+        out["dq"], out["dk"] = orc.unrotate_bf16(g["dq"]), orc.unrotate_bf16(g["dk"])
     return out
 
 
