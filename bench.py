@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--causal-dq", action="store_true", help="causal dQ prescale option")
     ap.add_argument("--non-causal", action="store_true",
                     help="time the non-causal variant (every key of a row's document visible)")
+    ap.add_argument("--hadamard", action="store_true",
+                    help="rotate Q and K by H / sqrt(d) in the quantiser, dQ and dK back in the backward")
     ap.add_argument("--store-gb", type=float, default=None,
                     help="cap the backward's dShat store at this many GiB (chunked backward); default: one chunk")
     ap.add_argument("--cpu-pairs", type=float, default=1.5e8,
@@ -161,13 +163,14 @@ def main():
 
     def step(evs=None):
         if evs: evs[0].record()
-        qz, kz, vz = fl.quantize([q, k, v], cu_d)
+        qz, kz, vz = fl.quantize([q, k, v], cu_d, hadamard=(args.hadamard, args.hadamard, False))
         if evs: evs[1].record()
         o, lse = fl.fwd(qz, kz, vz, cu_d, lists.fwd, causal=causal)
         if evs: evs[2].record()
         dc, dsc, D = fl.quantize_do(do, o, cu_d)
         if evs: evs[3].record()
-        out = fl.bwd(qz, kz, vz, (dc, dsc), lse, D, cu_d, lists, None, args.causal_dq, workspace=ws, causal=causal)
+        out = fl.bwd(qz, kz, vz, (dc, dsc), lse, D, cu_d, lists, None, args.causal_dq, workspace=ws, causal=causal,
+                     hadamard=args.hadamard)
         if evs: evs[4].record()
         return out
 
@@ -205,7 +208,8 @@ def main():
     dom_flop = bwd_flop if dom == "bwd" else fwd_flop
     achieved = dom_flop / (stages[dom] * 1e-3) / 1e12
     traffic = None
-    if dom == "bwd" and causal and args.workload == BWD_TRAFFIC["workload"] and bwd_source_hash() == BWD_TRAFFIC["src"]:
+    if (dom == "bwd" and causal and not args.hadamard and args.workload == BWD_TRAFFIC["workload"]
+            and bwd_source_hash() == BWD_TRAFFIC["src"]):
         traffic = BWD_TRAFFIC["read_bytes"] + BWD_TRAFFIC["write_bytes"]
     roofline = {"bound": "mfma",
                 "kernel": "flamia_bwd (bwd_prologue + bwd_kernel + dq_kernel)" if dom == "bwd" else "flamia_fwd",
@@ -225,7 +229,7 @@ def main():
         "vs_baseline": None, "dtype": "mxfp8_e4m3", "data": "synthetic",
         "config": {"workload": args.workload, "T": T, "Hq": Hq, "Hkv": Hkv, "d": d, "docs": len(cu) - 1,
                    "visible_pairs": pairs, "flop_per_step": flop, "causal_dq_scale": bool(args.causal_dq),
-                   "causal": causal},
+                   "causal": causal, "hadamard": bool(args.hadamard)},
         "frac_of_peak": value / PEAK_FP8_TFLOPS,
         "roofline": roofline,
         "quantize": quant,
@@ -234,7 +238,7 @@ def main():
         "peak_mem_GB": torch.cuda.max_memory_allocated() / 1e9,
         "bwd_workspace_GB": ws_bytes / 1e9, "bwd_chunks": chunks,
     }
-    if not args.no_cpu_baseline and causal:
+    if not args.no_cpu_baseline and causal and not args.hadamard:
         res["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_pairs)
     print(json.dumps(res), flush=True)
 

@@ -112,6 +112,14 @@ flamia_status flamia_build_worklist(const int32_t* cu_seqlens, int32_t n_docs, i
  * dO pass: with `o` non-NULL, exactly one tensor (dO, H heads) is given, and D[h][t] =
  * sum_c deq(dO_{t,h,c}) * O_{t,h,c} is also written (float32 [H, T]); deq(x) = code * 2^s, the
  * same quantised dO that the backward's dP product reads ([J] §3.3).
+ *
+ * Hadamard rotation ([J] §3.4 "Hadamard rotation", "Quantization fusion"): with hadamard = 1 a
+ * tensor's (token, head) rows are first multiplied by H / sqrt(d), H the Sylvester Hadamard
+ * matrix, in FP32 with a fixed order: butterflies for strides 1, 2, ..., d/2 in turn, a pair
+ * (a, b) at that distance (a the lower index) becoming (a + b, a - b), then the multiply by
+ * RN32(1 / sqrt(d)); the block rule above then runs on those FP32 values.  Meant for Q and K
+ * together (scores are unchanged in exact arithmetic); the backward then rotates dQ and dK back
+ * (flamia_bwd_args.hadamard).  Not with the dO pass.
  * ------------------------------------------------------------------------------------------ */
 typedef struct {
   const void* x;              /* bf16 [T, H, d], element strides below, d contiguous */
@@ -119,10 +127,11 @@ typedef struct {
   int32_t H;                  /* heads of this tensor */
   uint8_t* codes;             /* out: u8 [T, H, d] contiguous */
   uint8_t* scales;            /* out: u8 [H, T] */
+  int32_t hadamard;           /* 1: rotate each row by H / sqrt(d) first (Q and K); 0: plain */
 } flamia_qtensor;
 
 /* Errors: NULL pointers, n_tensors not in [1, 3] (1 with `o`), H < 1, T < 0 or > FLAMIA_MAX_T,
- * d not in {64, 128}, n_docs < 0, D NULL when o is given. */
+ * d not in {64, 128}, n_docs < 0, D NULL when o is given, hadamard with o (UNSUPPORTED). */
 flamia_status flamia_quantize(const flamia_qtensor* tensors, int32_t n_tensors, int32_t T, int32_t d,
                               const int32_t* cu_seqlens, int32_t n_docs, const void* o, int64_t o_stride_t,
                               int64_t o_stride_h, float* D, void* stream);
@@ -215,6 +224,12 @@ typedef struct {
                                          backward visits every (query tile, key tile) pair of a
                                          document and takes the sequence-wide prescale only
                                          (causal_dq_scale = 1 is FLAMIA_ERR_UNSUPPORTED) */
+  int32_t hadamard;                   /* 1: Q and K were quantised with hadamard = 1; the
+                                         gradients of the rotated operands, as BF16 rows, are
+                                         rotated back in place (same FP32 arithmetic as the
+                                         quantiser, BF16 round to nearest even), so dq and dk are
+                                         the gradients of the unrotated inputs.  Needs dq, dk
+                                         16-byte aligned and their strides multiples of 8. */
 } flamia_bwd_args;
 
 /* Host.  Backward workspace for n_docs documents of total length T: a header, pi [Hq, T], the

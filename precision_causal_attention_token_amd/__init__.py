@@ -35,7 +35,8 @@ DEFAULT_STORE_BYTES = 4 << 30
 
 class _QTensor(ctypes.Structure):
     _fields_ = [("x", ctypes.c_void_p), ("stride_t", ctypes.c_int64), ("stride_h", ctypes.c_int64),
-                ("H", ctypes.c_int32), ("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p)]
+                ("H", ctypes.c_int32), ("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("hadamard", ctypes.c_int32)]
 
 
 class _FwdArgs(ctypes.Structure):
@@ -60,7 +61,7 @@ class _BwdArgs(ctypes.Structure):
                 ("dv_stride_t", ctypes.c_int64), ("dv_stride_h", ctypes.c_int64),
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
                 ("causal_dq_scale", ctypes.c_int32), ("dq_exp_out", ctypes.c_void_p),
-                ("non_causal", ctypes.c_int32)]
+                ("non_causal", ctypes.c_int32), ("hadamard", ctypes.c_int32)]
 
 
 _lib = None
@@ -156,14 +157,18 @@ def worklist_items(buf):
     return n, buf[4:4 + 4 * n].view(n, 4)
 
 
-def quantize(xs, cu_seqlens):
+def quantize(xs, cu_seqlens, hadamard=False):
     """Token-block MXFP8 quantisation of up to three BF16 tensors [T, H, d] in one launch.
-    Returns a list of (codes u8 [T, H, d], scales u8 [H, T])."""
+    hadamard: a bool for every tensor or one per tensor (rows rotated by H / sqrt(d) first; Q
+    and K of a training call).  Returns a list of (codes u8 [T, H, d], scales u8 [H, T])."""
     lib = load_library()
     n_docs = _check_cu(cu_seqlens)
     T, _, d = xs[0].shape
     arr = (_QTensor * len(xs))()
     outs = []
+    rot = [bool(hadamard)] * len(xs) if isinstance(hadamard, bool) else [bool(r) for r in hadamard]
+    if len(rot) != len(xs):
+        raise ValueError("one hadamard flag per tensor")
     for i, x in enumerate(xs):
         _check_bf16(x, "x")
         if x.shape[0] != T or x.shape[2] != d:
@@ -171,7 +176,7 @@ def quantize(xs, cu_seqlens):
         H = x.shape[1]
         codes = torch.empty((T, H, d), dtype=torch.uint8, device=x.device)
         scales = torch.empty((H, T), dtype=torch.uint8, device=x.device)
-        arr[i] = _QTensor(x.data_ptr(), x.stride(0), x.stride(1), H, codes.data_ptr(), scales.data_ptr())
+        arr[i] = _QTensor(x.data_ptr(), x.stride(0), x.stride(1), H, codes.data_ptr(), scales.data_ptr(), int(rot[i]))
         outs.append((codes, scales))
     _check(lib.flamia_quantize(arr, len(xs), T, d, _ptr(cu_seqlens), n_docs, None, 0, 0, None, _stream()))
     return outs
@@ -188,7 +193,7 @@ def quantize_do(do, o, cu_seqlens):
     scales = torch.empty((H, T), dtype=torch.uint8, device=do.device)
     D = torch.empty((H, T), dtype=torch.float32, device=do.device)
     arr = (_QTensor * 1)()
-    arr[0] = _QTensor(do.data_ptr(), do.stride(0), do.stride(1), H, codes.data_ptr(), scales.data_ptr())
+    arr[0] = _QTensor(do.data_ptr(), do.stride(0), do.stride(1), H, codes.data_ptr(), scales.data_ptr(), 0)
     _check(lib.flamia_quantize(arr, 1, T, d, _ptr(cu_seqlens), n_docs, _ptr(o), o.stride(0), o.stride(1),
                                _ptr(D), _stream()))
     return codes, scales, D
@@ -229,13 +234,14 @@ def bwd_workspace_bytes_for(cu_seqlens_host, T, Hq, d, causal=True):
 
 
 def bwd(q, k, v, do, lse, D, cu_seqlens, lists, softmax_scale=None, causal_dq_scale=False, want_pi=False,
-        workspace=None, static_scratch=False, causal=True):
+        workspace=None, static_scratch=False, causal=True, hadamard=False):
     """Backward on quantised operands.  q, k, v, do are (codes, scales) pairs; lse, D f32 [Hq, T];
     lists: the micro-batch's Lists.  workspace: a uint8 CUDA tensor of at least
     bwd_workspace_bytes(n_docs, T, Hq, d, 0) bytes, or None to allocate one with the default
     store (DEFAULT_STORE_BYTES).
     static_scratch=True calls flamia_bwd_static instead (the library's static device scratch; no
     workspace is allocated or passed).
+    hadamard=True: Q and K were quantised rotated; dq and dk are rotated back.
     Returns (dq, dk, dv) BF16, plus the prescale exponents pi int16 [Hq, T] if want_pi."""
     lib = load_library()
     n_docs = _check_cu(cu_seqlens)
@@ -256,7 +262,7 @@ def bwd(q, k, v, do, lse, D, cu_seqlens, lists, softmax_scale=None, causal_dq_sc
                  dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), dq.stride(0), dq.stride(1), dk.stride(0), dk.stride(1),
                  dv.stride(0), dv.stride(1), workspace.data_ptr() if workspace is not None else None,
                  workspace.numel() if workspace is not None else 0, int(bool(causal_dq_scale)),
-                 pi.data_ptr() if pi is not None else None, int(not causal))
+                 pi.data_ptr() if pi is not None else None, int(not causal), int(bool(hadamard)))
     _check((lib.flamia_bwd_static if static_scratch else lib.flamia_bwd)(ctypes.byref(a), _stream()))
     return (dq, dk, dv, pi) if want_pi else (dq, dk, dv)
 
@@ -277,15 +283,16 @@ class Lists:
         self.bwd = build_worklist(cu_seqlens, T, FLAMIA_LIST_BWD if causal else FLAMIA_LIST_BWD_NC)
 
 
-def training_call(q, k, v, do, cu_seqlens, lists=None, softmax_scale=None, causal_dq_scale=False, causal=True):
+def training_call(q, k, v, do, cu_seqlens, lists=None, softmax_scale=None, causal_dq_scale=False, causal=True,
+                  hadamard=False):
     """One attention training call: quantise Q, K, V -> forward -> quantise dO (+ D) -> backward.
     Returns dict with o, lse, dq, dk, dv."""
     T = q.shape[0]
     if lists is None:
         lists = Lists(cu_seqlens, T, causal)
-    qz, kz, vz = quantize([q, k, v], cu_seqlens)
+    qz, kz, vz = quantize([q, k, v], cu_seqlens, hadamard=(hadamard, hadamard, False))
     o, lse = fwd(qz, kz, vz, cu_seqlens, lists.fwd, softmax_scale, causal=causal)
     dc, dsc, D = quantize_do(do, o, cu_seqlens)
     dq, dk, dv = bwd(qz, kz, vz, (dc, dsc), lse, D, cu_seqlens, lists, softmax_scale, causal_dq_scale,
-                     causal=causal)
+                     causal=causal, hadamard=hadamard)
     return dict(o=o, lse=lse, dq=dq, dk=dk, dv=dv)

@@ -149,6 +149,7 @@ flamia_status flamia_quantize(const flamia_qtensor* tensors, int32_t n_tensors, 
   if (T > FLAMIA_MAX_T) return FLAMIA_ERR_UNSUPPORTED;
   if (d != 64 && d != 128) return FLAMIA_ERR_UNSUPPORTED;
   if (o && !D) return FLAMIA_ERR_NULL;
+  if (o && tensors[0].hadamard) return FLAMIA_ERR_UNSUPPORTED;  // dO is never rotated
   QuantParams p{};
   p.n_tensors = n_tensors;
   p.T = T;
@@ -163,7 +164,8 @@ flamia_status flamia_quantize(const flamia_qtensor* tensors, int32_t n_tensors, 
     if (!aligned(t.x, 16) || (t.stride_t % 8) || (t.stride_h % 8) || t.stride_t < 0 || t.stride_h < 0)
       return FLAMIA_ERR_SHAPE;
     if (!aligned(t.codes, 16)) return FLAMIA_ERR_SHAPE;
-    p.t[i] = QTensorDev{static_cast<const uint16_t*>(t.x), t.stride_t, t.stride_h, t.H, t.codes, t.scales};
+    p.t[i] = QTensorDev{static_cast<const uint16_t*>(t.x), t.stride_t, t.stride_h, t.H, t.codes, t.scales,
+                        t.hadamard ? 1 : 0};
     if (t.H > p.maxH) p.maxH = t.H;
   }
   if (o) {
@@ -247,6 +249,10 @@ flamia_status flamia_bwd(const flamia_bwd_args* a, void* stream) {
   if (!aligned(a->q, 16) || !aligned(a->k, 16) || !aligned(a->v, 16) || !aligned(a->dO, 16) ||
       !aligned(a->fwd_list, 16) || !aligned(a->bwd_list, 16))
     return FLAMIA_ERR_SHAPE;
+  // the un-rotation moves 16-byte pieces of 8 values
+  if (a->hadamard && (!aligned(a->dq, 16) || !aligned(a->dk, 16) || (a->dq_stride_t % 8) || (a->dq_stride_h % 8) ||
+                      (a->dk_stride_t % 8) || (a->dk_stride_h % 8)))
+    return FLAMIA_ERR_SHAPE;
   const int grid = num_cus();
   if (grid <= 0) return FLAMIA_ERR_HIP;
   BwdParams p{};
@@ -291,6 +297,11 @@ flamia_status flamia_bwd(const flamia_bwd_args* a, void* stream) {
   p.dbg = g_dbg;
 #endif
   hipError_t e = launch_bwd(p, a->d, grid, static_cast<hipStream_t>(stream));
+  if (e == hipSuccess && a->hadamard) {
+    e = launch_unrotate(p.dq, a->dq_stride_t, a->dq_stride_h, a->T, a->Hq, a->d, static_cast<hipStream_t>(stream));
+    if (e == hipSuccess)
+      e = launch_unrotate(p.dk, a->dk_stride_t, a->dk_stride_h, a->T, a->Hkv, a->d, static_cast<hipStream_t>(stream));
+  }
   return e == hipSuccess ? FLAMIA_OK : FLAMIA_ERR_HIP;
 }
 

@@ -45,6 +45,7 @@ struct QTensorDev {
   int32_t H;
   uint8_t* codes;
   uint8_t* scales;
+  int32_t hadamard;  // rows rotated by H / sqrt(d) before quantisation
 };
 
 struct QuantParams {
@@ -110,6 +111,9 @@ struct BwdParams {
 };
 
 hipError_t launch_quantize(const QuantParams& p, int d, hipStream_t s);
+// In-place rotation of BF16 rows [T, H, d] (element strides) by H / sqrt(d): gradients of
+// rotated operands back to the inputs' basis.
+hipError_t launch_unrotate(uint16_t* x, int64_t st, int64_t sh, int T, int H, int d, hipStream_t s);
 hipError_t launch_worklist(const int32_t* cu, int n_docs, int T, int kind, int n_workers, int32_t* list,
                            hipStream_t s);
 hipError_t launch_fwd(const FwdParams& p, int d, int grid, hipStream_t s);

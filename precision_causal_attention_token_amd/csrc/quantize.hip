@@ -17,6 +17,58 @@ namespace {
 constexpr int WIN = 128;            // window of block starts per workgroup
 constexpr int ROWS = WIN + BLK - 1; // rows a workgroup may touch
 
+// ---- Hadamard rotation of the head dimension (jaehun.me §3.4 "Hadamard rotation", "Quantization
+// fusion").  A row x of D values becomes x H / sqrt(D), H the Sylvester Hadamard matrix.  Fixed
+// arithmetic, so that codes decided on the rotated values are reproducible: FP32 butterflies
+// for strides 1, 2, ..., D/2 in that order, a pair (a, b) at distance `stride` (a the lower
+// index) becoming (a + b, a - b), then the multiply by RN32(1 / sqrt(D)).
+// The row is held 8 values per lane by D/8 consecutive lanes (lane lc: elements 8 lc .. 8 lc + 7),
+// so strides 1, 2, 4 stay in the lane and strides 8 .. D/2 pair lane lc with lane lc ^ (stride / 8).
+template <int M>
+__device__ __forceinline__ float xor_lane(float x) {
+  if constexpr (M == 1) return dpp<0xB1>(x);  // quad_perm [1,0,3,2]
+  else if constexpr (M == 2) return dpp<0x4E>(x);  // quad_perm [2,3,0,1]
+  else if constexpr (M == 4) return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x101F));
+  else return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x201F));  // lane ^ 8
+}
+template <int M>
+__device__ __forceinline__ void cross_stage(float (&v)[8], int lc) {
+  const bool upper = (lc & M) != 0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float other = xor_lane<M>(v[e]);
+    v[e] = upper ? __fsub_rn(other, v[e]) : __fadd_rn(v[e], other);
+  }
+}
+template <int D>
+__device__ __forceinline__ void hadamard_row(float (&v)[8], int lc) {
+#pragma unroll
+  for (int st = 1; st < 8; st *= 2)
+#pragma unroll
+    for (int i = 0; i < 8; i += 2 * st)
+#pragma unroll
+      for (int j = i; j < i + st; ++j) {
+        const float a = v[j], b = v[j + st];
+        v[j] = __fadd_rn(a, b);
+        v[j + st] = __fsub_rn(a, b);
+      }
+  cross_stage<1>(v, lc);
+  cross_stage<2>(v, lc);
+  cross_stage<4>(v, lc);
+  if constexpr (D == 128) cross_stage<8>(v, lc);
+  constexpr float c = (D == 128) ? 0x1.6a09e6p-4f : 0.125f;  // RN32(1 / sqrt(D))
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = __fmul_rn(v[e], c);
+}
+__device__ __forceinline__ void bf16x8_to_f32(const uint4& w, float (&v)[8]) {
+  const uint32_t a[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = bf16_lo(a[i]);
+    v[2 * i + 1] = bf16_hi(a[i]);
+  }
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void quantize_kernel(QuantParams p) {
   constexpr int LPR = D / 8;            // lanes per row
@@ -69,13 +121,21 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantParams p) {
     if (r < ROWS && own_start[r] >= 0) {
       const int64_t tau = W0 + r;
       vals[ps] = *reinterpret_cast<const uint4*>(X.x + tau * X.st + (int64_t)h * X.sh + 8 * lc);
-      const uint32_t w[4] = {vals[ps].x, vals[ps].y, vals[ps].z, vals[ps].w};
+      if (X.hadamard) {  // (uniform over the row's lanes, which exchange values)
+        float v[8];
+        bf16x8_to_f32(vals[ps], v);
+        hadamard_row<D>(v, lc);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) m = fmaxf(m, fmaxf(fabsf(bf16_lo(w[i])), fabsf(bf16_hi(w[i]))));
-      // a NaN element makes the block's exponent NaN (byte 0xFF)
+        for (int e = 0; e < 8; ++e) m = (fabsf(v[e]) <= 3.4028235e38f) ? fmaxf(m, fabsf(v[e])) : __int_as_float(0x7F800000);
+      } else {
+        const uint32_t w[4] = {vals[ps].x, vals[ps].y, vals[ps].z, vals[ps].w};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (((w[i] & 0x7F80u) == 0x7F80u) || ((w[i] & 0x7F800000u) == 0x7F800000u)) m = __int_as_float(0x7F800000);
+        for (int i = 0; i < 4; ++i) m = fmaxf(m, fmaxf(fabsf(bf16_lo(w[i])), fabsf(bf16_hi(w[i]))));
+        // a NaN element makes the block's exponent NaN (byte 0xFF)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (((w[i] & 0x7F80u) == 0x7F80u) || ((w[i] & 0x7F800000u) == 0x7F800000u)) m = __int_as_float(0x7F800000);
+        }
       }
     }
     if constexpr (LPR == 16) {
@@ -129,6 +189,13 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantParams p) {
       uint2 out;
       if (s == 128) {
         out = make_uint2(0x7F7F7F7Fu, 0x7F7F7F7Fu);
+      } else if (X.hadamard) {  // the rotation again (the same arithmetic), then the codes
+        const float f = exp2i_neg(s);
+        float v[8];
+        bf16x8_to_f32(vals[ps], v);
+        hadamard_row<D>(v, lc);
+        out.x = (uint32_t)pack4_fp8(v[0] * f, v[1] * f, v[2] * f, v[3] * f);
+        out.y = (uint32_t)pack4_fp8(v[4] * f, v[5] * f, v[6] * f, v[7] * f);
       } else {
         const float f = exp2i_neg(s);
         const uint32_t w[4] = {vals[ps].x, vals[ps].y, vals[ps].z, vals[ps].w};
@@ -169,7 +236,33 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantParams p) {
   }
 }
 
+// Rows of gradients of rotated operands back to the inputs' basis, in place: BF16 -> FP32, the
+// rotation above (its own inverse), BF16 round to nearest even.  One row per D/8 lanes.
+template <int D>
+__global__ __launch_bounds__(256) void unrotate_kernel(uint16_t* x, int64_t st, int64_t sh, int T, int H) {
+  constexpr int LPR = D / 8;
+  const int64_t row = (int64_t)blockIdx.x * (256 / LPR) + threadIdx.x / LPR;
+  const int lc = threadIdx.x % LPR;
+  if (row >= (int64_t)T * H) return;  // whole rows leave together: the exchanges stay within a row
+  const int64_t t = row / H, h = row % H;
+  uint4* ptr = reinterpret_cast<uint4*>(x + t * st + h * sh + 8 * lc);
+  float v[8];
+  bf16x8_to_f32(*ptr, v);
+  hadamard_row<D>(v, lc);
+  *ptr = make_uint4(pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]), pack_bf16(v[4], v[5]), pack_bf16(v[6], v[7]));
+}
+
 }  // namespace
+
+hipError_t launch_unrotate(uint16_t* x, int64_t st, int64_t sh, int T, int H, int d, hipStream_t s) {
+  const int64_t rows = (int64_t)T * H;
+  if (rows == 0) return hipSuccess;
+  const int rpb = 256 / (d / 8);  // rows per workgroup
+  const dim3 grid((unsigned)((rows + rpb - 1) / rpb));
+  if (d == 128) hipLaunchKernelGGL(unrotate_kernel<128>, grid, dim3(256), 0, s, x, st, sh, T, H);
+  else hipLaunchKernelGGL(unrotate_kernel<64>, grid, dim3(256), 0, s, x, st, sh, T, H);
+  return hipGetLastError();
+}
 
 hipError_t launch_quantize(const QuantParams& p, int d, hipStream_t s) {
   if (p.T == 0) return hipSuccess;

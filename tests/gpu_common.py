@@ -104,9 +104,11 @@ DUMP_U8 = ("fwd_p", "bwd_p", "bwd_ps", "bwd_ds", "bwd_dss")
 
 
 def gpu_call(q, k, v, do, cu, causal_dq=False, softmax_scale=None, window=None, store_budget=None, causal=True,
-             static_scratch=False):
+             static_scratch=False, hadamard=False):
     """Full training call on the GPU through the C ABI; returns numpy arrays (BF16 outputs as
-    bit patterns).  causal=False: non-causal attention within each document.  With `window` (row/key/head bounds) the call runs the debug variant and the
+    bit patterns).  causal=False: non-causal attention within each document.  hadamard=True: Q
+    and K quantised rotated; dQ and dK are returned in the rotated basis (the backward's own
+    un-rotation is checked on its own).  With `window` (row/key/head bounds) the call runs the debug variant and the
     result also holds its per-pair dumps under "dumps" ([heads][rows][keys]).  store_budget: the
     backward's dShat store (default: the binding's default; 0: the smallest accepted, many
     chunks); the key-tile chunks run are returned under "chunks"."""
@@ -128,7 +130,7 @@ def gpu_call(q, k, v, do, cu, causal_dq=False, softmax_scale=None, window=None, 
             assert st == 0, st
         try:
             lists = fl.Lists(cu_d, T, causal)
-            qz, kz, vz = fl.quantize([qd, kd, vd], cu_d)
+            qz, kz, vz = fl.quantize([qd, kd, vd], cu_d, hadamard=(hadamard, hadamard, False))
             o, lse = fl.fwd(qz, kz, vz, cu_d, lists.fwd, softmax_scale, causal=causal)
             dc, dsc, D = fl.quantize_do(dod, o, cu_d)
             Hq, d = q.shape[1], q.shape[2]
@@ -153,7 +155,7 @@ def gpu_call(q, k, v, do, cu, causal_dq=False, softmax_scale=None, window=None, 
     n = lambda t: t.cpu().numpy()
     out = dict(q=n(qz[0]), sq=n(qz[1]), k=n(kz[0]), sk=n(kz[1]), v=n(vz[0]), sv=n(vz[1]),
                do=n(dc), sdo=n(dsc), D=n(D), o=b(o), lse=n(lse), dq=b(dq), dk=b(dk), dv=b(dv), pi=n(pi),
-               chunks=chunks, causal=bool(causal))
+               chunks=chunks, causal=bool(causal), hadamard=bool(hadamard))
     if bufs is not None:
         out["dumps"] = {k_: n(t) for k_, t in bufs.items()}
         out["window"] = dict(window)
@@ -612,14 +614,14 @@ def doc_window(cu, doc, heads, tail_blocks=0):
 
 
 def stage_and_chain(orc, q, k, v, do, cu, window, causal_dq=False, release=None, tail=False, zero_in_exact=(),
-                    causal=True):
+                    causal=True, hadamard=False):
     """Debug run in `window` (compared bit for bit with the product library's run `release`, made
     here if not given), decision checks and replays (stage), then the oracle's own chain (its
     work restricted to the window's documents, KV heads and, with tail=True, document tail)."""
     cu = np.asarray(cu, np.int32)
     if release is None:
-        release = gpu_call(q, k, v, do, cu, causal_dq, causal=causal)
-    g = gpu_call(q, k, v, do, cu, causal_dq, window=window, causal=causal)
+        release = gpu_call(q, k, v, do, cu, causal_dq, causal=causal, hadamard=hadamard)
+    g = gpu_call(q, k, v, do, cu, causal_dq, window=window, causal=causal, hadamard=hadamard)
     same_outputs(g, release)
     say("  debug variant: outputs bit-identical to libflamia.so")
     fv = validate_forward(orc, g, cu)
@@ -633,7 +635,9 @@ def stage_and_chain(orc, q, k, v, do, cu, window, causal_dq=False, release=None,
     if tail:
         tr = window["row_hi"] - window["row_lo"]
         kw.update(tail_rows=tr, tail_blocks=-(-tr // 32))
-    ref = oracle_call(orc, q, k, v, do, cu, causal_dq, causal=causal, **kw)
+    ref = oracle_call(orc, q, k, v, do, cu, causal_dq, causal=causal, hadamard=hadamard, **kw)
+    if hadamard:  # the GPU run above returns dQ, dK in the rotated basis
+        ref["dq"], ref["dk"] = ref["dq_rot"], ref["dk_rot"]
     chain_check(orc, g, ref, cu, fv, bv, zero_in_exact)
     return g
 

@@ -96,6 +96,14 @@ def test_host_validation_errors(lib):
     b.workspace_bytes = lib.flamia_bwd_workspace_bytes(1, 100, 4, 64, 0)
     b.non_causal, b.causal_dq_scale = 1, 1
     assert lib.flamia_bwd(ctypes.byref(b), None) == 3          # causal dQ prescale needs causal attention
+    b.non_causal, b.causal_dq_scale, b.hadamard = 0, 0, 1
+    b.dq_stride_t, b.dq_stride_h = 4 * 64 + 4, 64               # 8-byte aligned, not a multiple of 8 elements
+    b.dk_stride_t, b.dk_stride_h, b.dv_stride_t, b.dv_stride_h = 128, 64, 128, 64
+    assert lib.flamia_bwd(ctypes.byref(b), None) == 2          # the un-rotation needs 16-byte rows
+    # the dO pass is never rotated
+    t = (fl._QTensor * 1)()
+    t[0] = fl._QTensor(fake, 512, 128, 4, fake, fake, 1)
+    assert lib.flamia_quantize(t, 1, 100, 128, fake, 1, fake, 512, 128, fake, None) == 3
 
 
 def test_list_kinds(lib):
