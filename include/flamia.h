@@ -200,7 +200,10 @@ flamia_status flamia_fwd(const flamia_fwd_args* args, void* stream);
  * bit-reproducible, and no workgroup waits for another.
  * Work comes from a FLAMIA_LIST_BWD list (key-tile pass; each (item, KV head) unit runs all
  * query heads of its group, so dK and dV are written once) and a FLAMIA_LIST_FWD list (dQ
- * pass), both built for the same cu_seqlens.
+ * pass), both built for the same cu_seqlens.  Both passes assign their units dynamically
+ * ([J] §3.4 "Work scheduling"): a workgroup takes the next unit of the list from a counter in
+ * the workspace (zeroed by the call itself) when it finishes one, so units run in list order
+ * (descending cost) on whichever compute unit is free.
  * ------------------------------------------------------------------------------------------ */
 typedef struct {
   const uint8_t *q, *k, *v, *dO;      /* codes (dO: [T, Hq, d], from the dO quantiser pass) */

@@ -169,9 +169,11 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
   const float c = p.c;
   const int T = p.T;
 
-  for (int round = 0;; ++round) {
-    const int u = round * G + ((round & 1) ? (G - 1 - wg) : wg);
-    if (u >= n_units) break;
+  // units (item, KV head) are taken dynamically: the list is sorted by descending cost, so the
+  // longest left go first to whichever workgroup is free
+  __shared__ int unit_slot;
+  int32_t* const counter = p.counters + 2 * p.chunk;
+  for (int u = wg; u < n_units; u = next_unit(counter, &unit_slot)) {
     const int4 it = items[u / p.Hkv];
     const int g = u % p.Hkv;
     // unit values are the same in every lane: kept in scalar registers (vector loads would
@@ -730,9 +732,9 @@ __global__ __launch_bounds__(DQ_THREADS, 2) void dq_kernel(BwdParams p) {  // tw
   asm volatile("v_mov_b32 %0, 0" : "=v"(lane_zero));
   const int qb_l = n >> 4;                    // its 32-query block
 
-  for (int round = 0;; ++round) {
-    const int u = round * G + ((round & 1) ? (G - 1 - wg) : wg);
-    if (u >= n_units) break;
+  __shared__ int unit_slot;
+  int32_t* const counter = p.counters + 2 * p.chunk + 1;
+  for (int u = wg; u < n_units; u = next_unit(counter, &unit_slot)) {  // dynamic, as in the key-tile pass
     const int4 it = items[u / (PARTS * p.Hq)];
     if (it.z < 2) break;  // single key tile from here on (the list is sorted by cost)
     const int h = u % p.Hq, g = h / grp, part = (u / p.Hq) % PARTS;
@@ -1077,6 +1079,7 @@ __global__ __launch_bounds__(PRO_THREADS) void bwd_prologue(BwdParams p) {
   __shared__ Seg carry_sh;
 
   if ((int)blockIdx.x == p.Hq) {
+    for (int x = threadIdx.x; x < 2 * (p.max_chunks + 1); x += PRO_THREADS) p.counters[x] = 0;
     layout_chunks(p);
     return;
   }

@@ -54,6 +54,18 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// Dynamic assignment of a persistent grid's units ([J] §3.4 "Work scheduling"): a workgroup
+// runs unit blockIdx.x first, then takes the next unit from an atomic counter (counted from
+// gridDim.x) when it has finished the current one, so no unit is reserved while its taker is
+// still busy.  Every thread of the workgroup calls this; the value is passed through LDS.
+__device__ __forceinline__ int next_unit(int32_t* counter, int* slot) {
+  if (threadIdx.x == 0) *slot = atomicAdd(counter, 1) + (int)gridDim.x;
+  lds_barrier();
+  const int u = *slot;
+  lds_barrier();  // every thread has read it before the next write
+  return u;
+}
+
 // Accumulator row held by register i of lane group h.
 __device__ __forceinline__ int acc_row(int i, int h) { return 8 * (i >> 2) + 4 * h + (i & 3); }
 

@@ -65,7 +65,7 @@ int64_t n_tiles(int32_t n_docs, int32_t T) { return ((int64_t)T + 127) / 128 + n
 // entries of the per-chunk tables (a bound on the chunk count + 2)
 int64_t n_chunk_entries(int32_t T) { return ((int64_t)T + 63) / 64 + 16; }
 struct BwdLayout {
-  size_t pi, tile_base, kv_chunk, kv_off, chunk_start, chunk_first, store;  // byte offsets
+  size_t pi, tile_base, kv_chunk, kv_off, chunk_start, chunk_first, counters, store;  // byte offsets
 };
 BwdLayout bwd_layout(int32_t n_docs, int32_t T, int32_t Hq) {
   BwdLayout l{};
@@ -76,6 +76,7 @@ BwdLayout bwd_layout(int32_t n_docs, int32_t T, int32_t Hq) {
   l.kv_off = off;      off += align256((size_t)n_tiles(n_docs, T) * 8);
   l.chunk_start = off; off += align256((size_t)n_chunk_entries(T) * 4);
   l.chunk_first = off; off += align256((size_t)n_chunk_entries(T) * 8);
+  l.counters = off;    off += align256((size_t)n_chunk_entries(T) * 8);
   l.store = off;
   return l;
 }
@@ -278,6 +279,7 @@ flamia_status flamia_bwd(const flamia_bwd_args* a, void* stream) {
   p.kv_off = reinterpret_cast<int64_t*>(ws + lay.kv_off);
   p.chunk_start = reinterpret_cast<int32_t*>(ws + lay.chunk_start);
   p.chunk_first = reinterpret_cast<int64_t*>(ws + lay.chunk_first);
+  p.counters = reinterpret_cast<int32_t*>(ws + lay.counters);
   p.ds_store = ws + lay.store;
   // Chunks: the store holds cap blocks per query head; a chunk spans chunk_cap = cap - (largest
   // item) blocks of last-block positions, so it never overflows the store; the launches cover
