@@ -67,6 +67,19 @@ def bwd_source_hash():
     return h.hexdigest()[:16]
 
 
+def cpu_model():
+    """The host CPU's model name (Linux /proc/cpuinfo), or the platform's processor string."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.lower().startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
 def cpu_baseline(workload_name, pairs_budget):
     """Time the oracle (test infrastructure, untuned) on a bounded sample: documents of the
     workload in order, each truncated to 4096 tokens, until pairs_budget query-key pairs per
@@ -107,6 +120,7 @@ def cpu_baseline(workload_name, pairs_budget):
     dt = time.perf_counter() - t0
     flop = 14.0 * shp.d * n_q * pairs
     return {"value": flop / dt / 1e12, "unit": "TFLOPS", "cores": oracle.num_threads(), "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": "%s workload: first %d documents (each truncated to 4096 tokens, %d tokens), query heads "
                       "0..%d (KV heads 0..%d), %d query-key pairs per head; quantise + forward + dO pass + "
                       "backward in %.2f s" % (workload_name, len(lens), len(idx), n_q - 1, n_kv - 1, pairs, dt),
