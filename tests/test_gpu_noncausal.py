@@ -74,3 +74,22 @@ def test_non_causal_long_document_tail(orc):
     cu = np.array([0, T], np.int32)
     q, k, v, do = workloads.tensors(T, Hq, Hkv, d, seed=970)
     stage_and_chain(orc, q, k, v, do, cu, doc_window(cu, 0, (1, 2), tail_blocks=4), tail=True, causal=False)
+
+
+def test_non_causal_with_hadamard_rotation(orc):
+    """Both options together: rotated Q, K on non-causal attention, stage and chain checks."""
+    T, Hq, Hkv, d = 1100, 4, 2, 128
+    cu = [0, 200, 201, 700, 1100]
+    q, k, v, do = workloads.tensors(T, Hq, Hkv, d, seed=980, outlier_channels=2)
+    stage_and_chain(orc, q, k, v, do, cu, full_window(T, Hq), causal=False, hadamard=True)
+
+
+def test_non_causal_static_scratch_matches_workspace():
+    """flamia_bwd_static on non-causal attention gives the bits of flamia_bwd."""
+    T, Hq, Hkv, d = 3000, 4, 2, 64
+    cu = np.array([0, 1000, 1001, 2500, 3000], np.int32)
+    q, k, v, do = workloads.tensors(T, Hq, Hkv, d, seed=990)
+    a = gpu_call(q, k, v, do, cu, causal=False)
+    b = gpu_call(q, k, v, do, cu, causal=False, static_scratch=True)
+    for nm in ("dq", "dk", "dv", "pi"):
+        assert np.array_equal(a[nm], b[nm]), nm
