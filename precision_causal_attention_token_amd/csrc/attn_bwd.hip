@@ -717,6 +717,7 @@ __global__ __launch_bounds__(DQ_THREADS, 2) void dq_kernel(BwdParams p) {  // tw
 
   if (p.status[0] || p.chunk >= p.status[1]) return;  // not laid out, or a chunk past the last
   const int chunk = p.chunk;
+  const int n_chunks = p.status[1];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int n = lane & 31, hh = lane >> 5;
@@ -753,8 +754,10 @@ __global__ __launch_bounds__(DQ_THREADS, 2) void dq_kernel(BwdParams p) {  // tw
     // the last key tile the unit's rows see: that of its last query tile, or non-causally the
     // document's last one
     const int K = p.causal_mask ? last_qt / 2 : (L - 1) / KV_TILE;
+    int k_lo = 0, kappa_hi = K;  // one chunk: every key tile is in it
+    if (n_chunks > 1) {
     if (p.kv_chunk[tb + K] < chunk) continue;  // (uniform over the workgroup)
-    int k_lo = 0, kappa_hi = -1;
+    kappa_hi = -1;
     for (int k0 = 0; k0 <= K; k0 += 64 * 8) {  // each lane reads up to 8 entries, all in flight
       int ch[8];
 #pragma unroll
@@ -769,6 +772,7 @@ __global__ __launch_bounds__(DQ_THREADS, 2) void dq_kernel(BwdParams p) {  // tw
       }
     }
     if (k_lo > kappa_hi) continue;  // no key tile of this unit's rows in this chunk (uniform)
+    }
     const int qt = qt0 + t4;
     const bool active = qt < n_qt;
     const int q_rel = QT * qt + qrow;
