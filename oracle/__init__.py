@@ -103,15 +103,19 @@ def e8m0_floor(a):
 
 # ---------------------------------------------------------------------------------------
 # the method
-def quantize(x_bits, cu, floor_rule=False, hadamard=False):
+def quantize(x_bits, cu, floor_rule=False, hadamard=False, per_token=False):
     """Token-block quantiser: returns (codes [T,H,d] u8, scales [H,T] u8).  hadamard=True rotates
-    each (token, head) row first (see hadamard())."""
+    each (token, head) row first (see hadamard()); per_token=True gives every token its own
+    exponent (blocks of one token)."""
     x = _c(x_bits, np.uint16)
     T, H, d = x.shape
     cu = _c(cu, np.int32)
     codes = np.empty((T, H, d), np.uint8)
     scales = np.empty((H, T), np.uint8)
-    if hadamard:
+    if per_token:
+        assert not floor_rule and not hadamard
+        lib().orc_quantize_per_token(_p(x), T, H, d, _p(cu), len(cu) - 1, _p(codes), _p(scales))
+    elif hadamard:
         assert not floor_rule
         lib().orc_quantize_hadamard(_p(x), T, H, d, _p(cu), len(cu) - 1, _p(codes), _p(scales))
     else:
@@ -189,9 +193,10 @@ def _sel(mask, n):
 
 
 def fwd(q, sq, k, sk, v, sv, cu, softmax_scale=None, p_shift=8, exact_p=False, want_o64=False,
-        docs=None, kv_heads=None, tail_rows=0, window=None, causal=True):
+        docs=None, kv_heads=None, tail_rows=0, window=None, causal=True, precise=False):
     """causal=False: every key of the row's document is visible (key tiles from the document's
-    last down to tile 0).  Returns (O bits u16 [T,Hq,d], LSE f32 [Hq,T] in log2 units, O64 or None), plus (with
+    last down to tile 0).  precise=True (with per-token operand scales): V's exponent is folded into
+    the probability operand against the row's running maximum of visited V exponents.  Returns (O bits u16 [T,Hq,d], LSE f32 [Hq,T] in log2 units, O64 or None), plus (with
     ``window``, a dict of row/key/head bounds)
     a dict of the per-pair dumps fwd_s (score accumulator), fwd_m (running maximum), fwd_p
     (E4M3 codes), [heads][rows][keys], NaN / 0xFF where not visited.  ``docs`` / ``kv_heads``
@@ -214,28 +219,32 @@ def fwd(q, sq, k, sk, v, sv, cu, softmax_scale=None, p_shift=8, exact_p=False, w
                   _p(cu), len(cu) - 1, int(p_shift), int(bool(exact_p)), _p(o), _p(lse),
                   _p(o64) if o64 is not None else None, _p(sd) if sd is not None else None,
                   _p(sk_) if sk_ is not None else None, int(tail_rows), ctypes.byref(w) if w is not None else None,
-                  int(bool(causal)))
+                  int(bool(causal)), int(bool(precise)))
     return (o, lse, o64) + ((dumps,) if window is not None else ())
 
 
-def quantize_do(do_bits, o_bits, cu):
-    """dO quantiser + D: returns (codes, scales, D f32 [H,T])."""
+def quantize_do(do_bits, o_bits, cu, per_token=False):
+    """dO quantiser + D: returns (codes, scales, D f32 [H,T]); per_token: one exponent per token."""
     do_bits, o_bits = _c(do_bits, np.uint16), _c(o_bits, np.uint16)
     T, H, d = do_bits.shape
     cu = _c(cu, np.int32)
     codes = np.empty((T, H, d), np.uint8)
     scales = np.empty((H, T), np.uint8)
     D = np.empty((H, T), np.float32)
-    lib().orc_quantize_do(_p(do_bits), _p(o_bits), T, H, d, _p(cu), len(cu) - 1, _p(codes), _p(scales), _p(D))
+    lib().orc_quantize_do_ex(_p(do_bits), _p(o_bits), T, H, d, _p(cu), len(cu) - 1, _p(codes), _p(scales), _p(D),
+                             int(bool(per_token)))
     return codes, scales, D
 
 
-def dq_exponents(sk, sv, sdo, cu, Hkv, d, causal_dq):
+def dq_exponents(sk, sv, sdo, cu, Hkv, d, causal_dq, per_token=False):
+    """pi [Hq, T]: sequence-wide (causal_dq False), causal to the row's block end (True), or with
+    per_token=True (the precision options) causal to the row itself."""
     sk, sv, sdo = _c(sk, np.uint8), _c(sv, np.uint8), _c(sdo, np.uint8)
     Hq, T = sdo.shape
     cu = _c(cu, np.int32)
     pi = np.empty((Hq, T), np.int16)
-    lib().orc_dq_exponents(_p(sk), _p(sv), _p(sdo), T, Hq, Hkv, d, _p(cu), len(cu) - 1, int(bool(causal_dq)), _p(pi))
+    mode = 2 if per_token else int(bool(causal_dq))
+    lib().orc_dq_exponents(_p(sk), _p(sv), _p(sdo), T, Hq, Hkv, d, _p(cu), len(cu) - 1, mode, _p(pi))
     return pi
 
 
@@ -245,7 +254,7 @@ class _Dbg(ctypes.Structure):
 
 
 def bwd(q, sq, k, sk, v, sv, do, sdo, lse, D, cu, softmax_scale=None, causal_dq=False, exact=0,
-        want64=False, debug=False, docs=None, kv_heads=None, tail_blocks=0, window=None, causal=True):
+        want64=False, debug=False, docs=None, kv_heads=None, tail_blocks=0, window=None, causal=True, precise=False):
     """Returns dict with dq, dk, dv (u16 BF16 bits), pi (i16 [Hq,T]) and optionally the
     double-precision values (dq64, dk64, dv64) and, for single-document calls, the block
     exponents/codes of the P and dS operands (p_scale, ds_scale [Hq,nb,nb]; p_code,
@@ -256,6 +265,8 @@ def bwd(q, sq, k, sk, v, sv, do, sdo, lse, D, cu, softmax_scale=None, causal_dq=
     causal=False: every key of the row's document is visible (default dQ prescale only)."""
     if not causal and causal_dq:
         raise ValueError("the causal dQ prescale applies to causal attention")
+    if precise and not causal:
+        raise ValueError("the precision options apply to causal attention")
     q, k, v, do = (_c(a, np.uint8) for a in (q, k, v, do))
     sq, sk, sv, sdo = (_c(a, np.uint8) for a in (sq, sk, sv, sdo))
     lse, D = _c(lse, np.float32), _c(D, np.float32)
@@ -288,11 +299,12 @@ def bwd(q, sq, k, sk, v, sv, do, sdo, lse, D, cu, softmax_scale=None, causal_dq=
                   _p(out["dq64"]) if want64 else None, _p(out["dk64"]) if want64 else None,
                   _p(out["dv64"]) if want64 else None, ctypes.byref(dbg) if dbg is not None else None,
                   _p(sd) if sd is not None else None, _p(sk_) if sk_ is not None else None,
-                  int(tail_blocks), ctypes.byref(w) if w is not None else None, int(bool(causal)))
+                  int(tail_blocks), ctypes.byref(w) if w is not None else None, int(bool(causal)),
+                  int(bool(precise)))
     return out
 
 
-def fwd_replay(v, sv, cu, window, S, M, P, Hq, c_scale, p_shift=8, causal=True):
+def fwd_replay(v, sv, cu, window, S, M, P, Hq, c_scale, p_shift=8, causal=True, precise=False):
     """Forward products from given per-pair decisions (score accumulator S, running maximum M,
     codes P, [heads][rows][keys] over ``window``).  Returns (O64 [heads][rows][d], LSE64
     [heads][rows]), NaN for rows not replayed.  c_scale = softmax_scale * log2(e) as used."""
@@ -306,7 +318,8 @@ def fwd_replay(v, sv, cu, window, S, M, P, Hq, c_scale, p_shift=8, causal=True):
     lse64 = np.empty((nh, nr))
     w = _window(window, {})
     lib().orc_fwd_replay(_p(v), _p(sv), T, int(Hq), Hkv, d, ctypes.c_double(c_scale), _p(cu), len(cu) - 1,
-                         int(p_shift), ctypes.byref(w), _p(S), _p(M), _p(P), _p(o64), _p(lse64), int(bool(causal)))
+                         int(p_shift), ctypes.byref(w), _p(S), _p(M), _p(P), _p(o64), _p(lse64), int(bool(causal)),
+                         int(bool(precise)))
     return o64, lse64
 
 

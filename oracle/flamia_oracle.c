@@ -163,17 +163,17 @@ double orc_f16_decode(uint16_t h) {
  * Tokens outside every document get code 0 and scale byte 0.
  * floor_rule = 1 selects the leaking floor exponent (with clipping) as a test foil.
  * ---------------------------------------------------------------------------------- */
-/* The block rule on decoded values v [T][H][d] (double). */
+/* The block rule on decoded values v [T][H][d] (double), with blocks of `blk` tokens. */
 static void quantize_values(const double* v, int T, int H, int d, const int32_t* cu, int n_docs,
-                            uint8_t* codes, uint8_t* scales, int floor_rule) {
+                            uint8_t* codes, uint8_t* scales, int floor_rule, int blk) {
   int k, h, t, c;
   memset(codes, 0, (size_t)T * H * d);
   memset(scales, 0, (size_t)H * T);
   for (k = 0; k < n_docs; ++k) {
     int t_begin = cu[k], t_end = cu[k + 1];
     int t0;
-    for (t0 = t_begin; t0 < t_end; t0 += BLK) {
-      int t1 = t0 + BLK < t_end ? t0 + BLK : t_end;
+    for (t0 = t_begin; t0 < t_end; t0 += blk) {
+      int t1 = t0 + blk < t_end ? t0 + blk : t_end;
       for (h = 0; h < H; ++h) {
         double amax = 0.0;
         int s;
@@ -204,7 +204,19 @@ void orc_quantize(const uint16_t* x, int T, int H, int d, const int32_t* cu, int
   size_t n = (size_t)T * H * d, i;
   double* v = (double*)malloc((n ? n : 1) * sizeof(double));
   for (i = 0; i < n; ++i) v[i] = orc_bf16_decode(x[i]);
-  quantize_values(v, T, H, d, cu, n_docs, codes, scales, floor_rule);
+  quantize_values(v, T, H, d, cu, n_docs, codes, scales, floor_rule, BLK);
+  free(v);
+}
+
+/* Per-token operand scales (jaehun.me §3.2: the precision option that closes the leakage inside
+ * a block): the same rule with blocks of one token, so a token's codes and exponent depend on
+ * that token alone. */
+void orc_quantize_per_token(const uint16_t* x, int T, int H, int d, const int32_t* cu, int n_docs,
+                            uint8_t* codes, uint8_t* scales) {
+  size_t n = (size_t)T * H * d, i;
+  double* v = (double*)malloc((n ? n : 1) * sizeof(double));
+  for (i = 0; i < n; ++i) v[i] = orc_bf16_decode(x[i]);
+  quantize_values(v, T, H, d, cu, n_docs, codes, scales, 0, 1);
   free(v);
 }
 
@@ -251,7 +263,7 @@ void orc_quantize_hadamard(const uint16_t* x, int T, int H, int d, const int32_t
   for (i = 0; i < n; ++i) f[i] = (float)orc_bf16_decode(x[i]);
   orc_hadamard(f, (long)T * H, d);
   for (i = 0; i < n; ++i) v[i] = (double)f[i];
-  quantize_values(v, T, H, d, cu, n_docs, codes, scales, 0);
+  quantize_values(v, T, H, d, cu, n_docs, codes, scales, 0, BLK);
   free(f);
   free(v);
 }
@@ -397,11 +409,26 @@ static long long win_index(const orc_window* w, int h, int row, int key) {
  * computed): only the last tail_rows rows of each document are computed; the outputs of the
  * other rows are left as they were.  win (optional): intermediate dumps, see orc_window.
  * ---------------------------------------------------------------------------------- */
+/* Precision option (jaehun.me §3.2: per-token operand scales; the V scale folded into the
+ * probability operand of P V, since a per-token scale cannot be applied to one 32-key block of
+ * the product).  Reading taken: the probability operand of row i in a key tile is
+ * E4M3(2^(P_SHIFT + e(V_j) - v_i) p_ij) with operand scale 2^(v_i - P_SHIFT), v_i the largest
+ * V exponent among the keys row i has visited so far (this tile included; the first tile is the
+ * diagonal one, so only keys j <= i count), at least -119 so the scale stays an E8M0 byte.
+ * Every factor depends on row i and its visible keys alone. */
+static int fold_ref(const uint8_t* sv_doc, int j0, int j1, int ref) {
+  int j;
+  if (ref < -119) ref = -119;
+  for (j = j0; j < j1; ++j)
+    if ((int)sv_doc[j] - 127 > ref) ref = (int)sv_doc[j] - 127;
+  return ref;
+}
+
 void orc_fwd(const uint8_t* q, const uint8_t* sq, const uint8_t* k, const uint8_t* sk,
              const uint8_t* v, const uint8_t* sv, int T, int Hq, int Hkv, int d,
              double softmax_scale, const int32_t* cu, int n_docs, int p_shift, int exact_p,
              uint16_t* o, float* lse, double* o64, const uint8_t* sel_docs, const uint8_t* sel_kv,
-             int tail_rows, const orc_window* win, int causal) {
+             int tail_rows, const orc_window* win, int causal, int precise) {
   const int group = Hq / Hkv;
   const double c_scale = softmax_scale * 1.4426950408889634074; /* log2(e) */
   double* Qd = deq_all(q, sq, T, Hq, d);
@@ -416,6 +443,7 @@ void orc_fwd(const uint8_t* q, const uint8_t* sq, const uint8_t* k, const uint8_
     double m = -INFINITY, l = 0.0;
     double acc[256];
     double t_tile[KV_TILE], dot_tile[KV_TILE];
+    int vref = -1000; /* precise: running maximum of the visible keys' V exponents */
     const double* qi = Qd + ((size_t)row * Hq + hh) * d;
     if (doc < 0) {
       lse[(size_t)hh * T + row] = INFINITY;
@@ -446,15 +474,19 @@ void orc_fwd(const uint8_t* q, const uint8_t* sq, const uint8_t* k, const uint8_
         m_new = m > mt ? m : mt;
         alpha = (m == -INFINITY) ? 0.0 : exp2(m - m_new);
         for (cc = 0; cc < d; ++cc) acc[cc] *= alpha;
+        if (precise) vref = fold_ref(sv + (size_t)g * T + start, j0, j1, vref);
         for (j = j0; j < j1; ++j) {
           const double* vj = Vd + ((size_t)(start + j) * Hkv + g) * d;
           double p = exp2(t_tile[j - j0] - m_new);
-          double ph = exact_p ? p : ldexp(orc_e4m3_decode(orc_e4m3_rne(ldexp(p, p_shift))), -p_shift);
+          /* precise: V's exponent folded into the probability operand (relative to vref) */
+          const int fold = precise ? (int)sv[(size_t)g * T + start + j] - 127 - vref : 0;
+          const uint8_t code = orc_e4m3_rne(ldexp(p, p_shift + fold));
+          double ph = exact_p ? p : ldexp(orc_e4m3_decode(code), -p_shift - fold);
           long long wi = win_index(win, hh, row, start + j);
           if (wi >= 0) {
             if (win->fwd_s) win->fwd_s[wi] = dot_tile[j - j0];
             if (win->fwd_m) win->fwd_m[wi] = m_new;
-            if (win->fwd_p) win->fwd_p[wi] = orc_e4m3_rne(ldexp(p, p_shift));
+            if (win->fwd_p) win->fwd_p[wi] = code;
           }
           sum += p;
           for (cc = 0; cc < d; ++cc) acc[cc] += ph * vj[cc];
@@ -478,12 +510,13 @@ void orc_fwd(const uint8_t* q, const uint8_t* sq, const uint8_t* k, const uint8_
  * backward's dP product reads) and the stored BF16 output O.  D is stored in FP32;
  * rows outside every document get D = 0.
  * ---------------------------------------------------------------------------------- */
-void orc_quantize_do(const uint16_t* dO, const uint16_t* O, int T, int H, int d,
-                     const int32_t* cu, int n_docs, uint8_t* codes, uint8_t* scales, float* D) {
+void orc_quantize_do_ex(const uint16_t* dO, const uint16_t* O, int T, int H, int d, const int32_t* cu,
+                        int n_docs, uint8_t* codes, uint8_t* scales, float* D, int per_token) {
   int i, h, c;
   int* dm;
   double* dOd;
-  orc_quantize(dO, T, H, d, cu, n_docs, codes, scales, 0);
+  if (per_token) orc_quantize_per_token(dO, T, H, d, cu, n_docs, codes, scales);
+  else orc_quantize(dO, T, H, d, cu, n_docs, codes, scales, 0);
   dm = doc_map(cu, n_docs, T);
   dOd = deq_all(codes, scales, T, H, d);
   for (i = 0; i < T; ++i)
@@ -496,6 +529,11 @@ void orc_quantize_do(const uint16_t* dO, const uint16_t* O, int T, int H, int d,
     }
   free(dm);
   free(dOd);
+}
+
+void orc_quantize_do(const uint16_t* dO, const uint16_t* O, int T, int H, int d,
+                     const int32_t* cu, int n_docs, uint8_t* codes, uint8_t* scales, float* D) {
+  orc_quantize_do_ex(dO, O, T, H, d, cu, n_docs, codes, scales, D, 0);
 }
 
 /* ------------------------------------------------------------------------------------
@@ -543,8 +581,9 @@ void orc_dq_exponents(const uint8_t* sk, const uint8_t* sv, const uint8_t* sdo, 
         if (!causal_dq) {
           E = max_do + max_v + max_k;
         } else {
+          /* causal_dq = 1: maxima up to the row's block end; 2 (per-token scales): up to the row */
           int r = t - cu[kk];
-          int block_end = cu[kk] + (r / BLK + 1) * BLK;
+          int block_end = causal_dq == 2 ? t + 1 : cu[kk] + (r / BLK + 1) * BLK;
           int pv = -1000, pk = -1000, u;
           if (block_end > cu[kk + 1]) block_end = cu[kk + 1];
           for (u = cu[kk]; u < block_end; ++u) {
@@ -602,7 +641,7 @@ void orc_bwd(const uint8_t* q, const uint8_t* sq, const uint8_t* k, const uint8_
              uint16_t* dq, uint16_t* dk, uint16_t* dv, int16_t* pi_out,
              double* dq64, double* dk64, double* dv64, const orc_bwd_debug* dbg,
              const uint8_t* sel_docs, const uint8_t* sel_kv, int tail_blocks, const orc_window* win,
-             int causal) {
+             int causal, int precise) {
   const int group = Hq / Hkv;
   const double c_scale = softmax_scale * 1.4426950408889634074;
   int16_t* pi = (int16_t*)malloc(sizeof(int16_t) * (size_t)Hq * T + 2);
@@ -612,7 +651,7 @@ void orc_bwd(const uint8_t* q, const uint8_t* sq, const uint8_t* k, const uint8_
   double* Kd = deq_all(k, sk, T, Hkv, d);
   double* Vd = deq_all(v, sv, T, Hkv, d);
   double* dOd = deq_all(dO, sdo, T, Hq, d);
-  orc_dq_exponents(sk, sv, sdo, T, Hq, Hkv, d, cu, n_docs, causal_dq, pi);
+  orc_dq_exponents(sk, sv, sdo, T, Hq, Hkv, d, cu, n_docs, precise ? 2 : causal_dq, pi);
   if (pi_out) memcpy(pi_out, pi, sizeof(int16_t) * (size_t)Hq * T);
   for (z = 0; z < n_q; ++z) { dq[z] = 0; if (dq64) dq64[z] = 0.0; }
   for (z = 0; z < n_kv; ++z) {
@@ -628,7 +667,7 @@ void orc_bwd(const uint8_t* q, const uint8_t* sq, const uint8_t* k, const uint8_
     int nb = (L + BLK - 1) / BLK, hq, bq, bk, ii, jj, cc;
     double* dk_acc;
     double* dv_acc;
-    double P[BLK][BLK], dS[BLK][BLK], dPv[BLK][BLK];
+    double P[BLK][BLK], dS[BLK][BLK], dPv[BLK][BLK], dSq[BLK][BLK];
     uint8_t Pc[BLK][BLK], dSc[BLK][BLK];
     double part[BLK * 256];
     double acc16[BLK * 256];
@@ -662,15 +701,41 @@ void orc_bwd(const uint8_t* q, const uint8_t* sq, const uint8_t* k, const uint8_
                   dp += doi[cc] * vj[cc];
                 }
                 p = exp2(dot * c_scale - (double)lse[(size_t)hq * T + start + ii]);
-                P[ii - i0][jj - j0] = p;
                 dPv[ii - i0][jj - j0] = dp;
                 dS[ii - i0][jj - j0] = p * (dp - (double)D[(size_t)hq * T + start + ii]);
+                if (precise) {
+                  /* per-token scales: each gradient product's other operand loses its exponent,
+                   * which moves into P or dS here: dO's into P (for dV), Q's into dS (for dK),
+                   * K's into the dS of dQ (the K fold) */
+                  const int edo = (int)sdo[(size_t)hq * T + start + ii] - 127;
+                  const int eq = (int)sq[(size_t)hq * T + start + ii] - 127;
+                  const int ek = (int)sk[(size_t)g * T + start + jj] - 127;
+                  dSq[ii - i0][jj - j0] = ldexp(dS[ii - i0][jj - j0], ek);
+                  p = ldexp(p, edo);
+                  dS[ii - i0][jj - j0] = ldexp(dS[ii - i0][jj - j0], eq);
+                }
+                P[ii - i0][jj - j0] = p;
                 if (fabs(p) > pmax) pmax = fabs(p);
                 if (fabs(dS[ii - i0][jj - j0]) > dsmax) dsmax = fabs(dS[ii - i0][jj - j0]);
               }
             /* block quantisation of the two product operands */
             sp = orc_e8m0_roundup(pmax);
             sds = orc_e8m0_roundup(dsmax);
+            if (precise) {
+              /* the dS operand of dQ: one exponent per (query row, 32-key block), so no other row's
+               * values enter a row's rounding (query-row-wise dS exponents) */
+              for (ii = i0; ii < i1; ++ii) {
+                double rmax = 0.0;
+                int sr;
+                for (jj = j0; jj < j1 && (!causal || jj <= ii); ++jj)
+                  if (fabs(dSq[ii - i0][jj - j0]) > rmax) rmax = fabs(dSq[ii - i0][jj - j0]);
+                sr = orc_e8m0_roundup(rmax);
+                for (jj = j0; jj < j1; ++jj) {
+                  if (causal && jj > ii) { dSq[ii - i0][jj - j0] = 0.0; continue; }
+                  if (!(exact & 2)) dSq[ii - i0][jj - j0] = ldexp(orc_e4m3_decode(orc_e4m3_rne(ldexp(dSq[ii - i0][jj - j0], -sr))), sr);
+                }
+              }
+            }
             for (ii = i0; ii < i1; ++ii)
               for (jj = j0; jj < j1; ++jj) {
                 if (causal && jj > ii) { Pc[ii - i0][jj - j0] = 0; dSc[ii - i0][jj - j0] = 0; continue; }
@@ -699,17 +764,23 @@ void orc_bwd(const uint8_t* q, const uint8_t* sq, const uint8_t* k, const uint8_
                   if (dbg->ds_code) dbg->ds_code[ci] = dSc[ii - i0][jj - j0];
                 }
             }
-            /* the three gradient products of this block */
+            /* the three gradient products of this block (precise: the folded exponents are taken
+             * back out of the operand that carries them, so deq() of the other operand applies) */
             for (ii = i0; ii < i1; ++ii)
               for (jj = j0; jj < j1 && (!causal || jj <= ii); ++jj) {
-                double ph = P[ii - i0][jj - j0], dsh = dS[ii - i0][jj - j0];
+                double ph = P[ii - i0][jj - j0], dsh = dS[ii - i0][jj - j0], dsq = dsh;
                 const double* qi = Qd + ((size_t)(start + ii) * Hq + hq) * d;
                 const double* doi = dOd + ((size_t)(start + ii) * Hq + hq) * d;
                 const double* kj = Kd + ((size_t)(start + jj) * Hkv + g) * d;
+                if (precise) {
+                  ph = ldexp(ph, 127 - (int)sdo[(size_t)hq * T + start + ii]);
+                  dsh = ldexp(dsh, 127 - (int)sq[(size_t)hq * T + start + ii]);
+                  dsq = ldexp(dSq[ii - i0][jj - j0], 127 - (int)sk[(size_t)g * T + start + jj]);
+                }
                 for (cc = 0; cc < d; ++cc) {
                   dv_acc[(size_t)jj * d + cc] += ph * doi[cc];
                   dk_acc[(size_t)jj * d + cc] += dsh * qi[cc];
-                  part[(size_t)(ii - i0) * d + cc] += dsh * kj[cc];
+                  part[(size_t)(ii - i0) * d + cc] += dsq * kj[cc];
                 }
               }
           }
@@ -766,7 +837,7 @@ void orc_bwd(const uint8_t* q, const uint8_t* sq, const uint8_t* k, const uint8_
  * ---------------------------------------------------------------------------------- */
 void orc_fwd_replay(const uint8_t* v, const uint8_t* sv, int T, int Hq, int Hkv, int d, double c_scale,
                     const int32_t* cu, int n_docs, int p_shift, const orc_window* win, const double* S,
-                    const double* M, const uint8_t* P, double* o64, double* lse64, int causal) {
+                    const double* M, const uint8_t* P, double* o64, double* lse64, int causal, int precise) {
   const int group = Hq / Hkv;
   const int nh = win->head_hi - win->head_lo, nr = win->row_hi - win->row_lo;
   double* Vd = deq_all(v, sv, T, Hkv, d);
@@ -777,6 +848,7 @@ void orc_fwd_replay(const uint8_t* v, const uint8_t* sv, int T, int Hq, int Hkv,
     int hh = win->head_lo + (int)(task / nr), row = win->row_lo + (int)(task % nr), g = hh / group;
     int doc = (row >= 0 && row < T) ? dm[row] : -1, kappa, j, cc;
     double acc[256], m = -INFINITY, l = 0.0;
+    int vref = -1000;
     double* o = o64 + (size_t)task * d;
     lse64[task] = NAN;
     for (cc = 0; cc < d; ++cc) o[cc] = NAN;
@@ -792,10 +864,12 @@ void orc_fwd_replay(const uint8_t* v, const uint8_t* sv, int T, int Hq, int Hkv,
         m_new = M[win_index(win, hh, row, start + j0)];
         alpha = (m == -INFINITY) ? 0.0 : exp2(m - m_new);
         for (cc = 0; cc < d; ++cc) acc[cc] *= alpha;
+        if (precise) vref = fold_ref(sv + (size_t)g * T + start, j0, j1, vref);
         for (j = j0; j < j1; ++j) {
           long long wi = win_index(win, hh, row, start + j);
           const double* vj = Vd + ((size_t)(start + j) * Hkv + g) * d;
-          double ph = ldexp(orc_e4m3_decode(P[wi]), -p_shift);
+          const int fold = precise ? (int)sv[(size_t)g * T + start + j] - 127 - vref : 0;
+          double ph = ldexp(orc_e4m3_decode(P[wi]), -p_shift - fold);
           sum += exp2(S[wi] * c_scale - m_new);
           for (cc = 0; cc < d; ++cc) acc[cc] += ph * vj[cc];
         }
