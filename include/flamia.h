@@ -120,6 +120,10 @@ flamia_status flamia_build_worklist(const int32_t* cu_seqlens, int32_t n_docs, i
  * RN32(1 / sqrt(d)); the block rule above then runs on those FP32 values.  Meant for Q and K
  * together (scores are unchanged in exact arithmetic); the backward then rotates dQ and dK back
  * (flamia_bwd_args.hadamard).  Not with the dO pass.
+ *
+ * Per-token scales ([J] §3.2, the precision options): with per_token = 1 every token of a
+ * document is its own block, so its exponent and codes depend on that token alone (also for the
+ * dO pass).
  * ------------------------------------------------------------------------------------------ */
 typedef struct {
   const void* x;              /* bf16 [T, H, d], element strides below, d contiguous */
@@ -128,6 +132,8 @@ typedef struct {
   uint8_t* codes;             /* out: u8 [T, H, d] contiguous */
   uint8_t* scales;            /* out: u8 [H, T] */
   int32_t hadamard;           /* 1: rotate each row by H / sqrt(d) first (Q and K); 0: plain */
+  int32_t per_token;          /* 1: one exponent per token (blocks of one token; the precision
+                                 options, with flamia_fwd_args.precise / flamia_bwd_args.precise) */
 } flamia_qtensor;
 
 /* Errors: NULL pointers, n_tensors not in [1, 3] (1 with `o`), H < 1, T < 0 or > FLAMIA_MAX_T,
@@ -165,6 +171,13 @@ typedef struct {
   int64_t o_stride_t, o_stride_h;
   float* lse;                     /* out: float32 [Hq, T], log2 units */
   int32_t non_causal;             /* 0: causal (j <= i); 1: every key of the document */
+  int32_t precise;                /* 1: the precision options ([J] §3.2): Q, K, V quantised with
+                                     per_token = 1; V's exponent is folded into the probability
+                                     operand, E4M3(2^(8 + e(V_j) - v_i) p_ij) with operand scale
+                                     2^(v_i - 8), v_i the largest V exponent among the keys row i
+                                     has visited so far (at least -119), and V enters P V with its
+                                     bare codes, so no later token changes row i.  Causal only
+                                     (non_causal = 1 is FLAMIA_ERR_UNSUPPORTED). */
 } flamia_fwd_args;
 
 /* Errors: NULL pointers, sizes, d, head ratio. */
@@ -233,6 +246,7 @@ typedef struct {
                                          quantiser, BF16 round to nearest even), so dq and dk are
                                          the gradients of the unrotated inputs.  Needs dq, dk
                                          16-byte aligned and their strides multiples of 8. */
+  int32_t precise;                    /* the precision options (as in the forward) */
 } flamia_bwd_args;
 
 /* Host.  Backward workspace for n_docs documents of total length T: a header, pi [Hq, T], the

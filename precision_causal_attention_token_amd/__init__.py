@@ -36,7 +36,7 @@ DEFAULT_STORE_BYTES = 4 << 30
 class _QTensor(ctypes.Structure):
     _fields_ = [("x", ctypes.c_void_p), ("stride_t", ctypes.c_int64), ("stride_h", ctypes.c_int64),
                 ("H", ctypes.c_int32), ("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
-                ("hadamard", ctypes.c_int32)]
+                ("hadamard", ctypes.c_int32), ("per_token", ctypes.c_int32)]
 
 
 class _FwdArgs(ctypes.Structure):
@@ -45,7 +45,8 @@ class _FwdArgs(ctypes.Structure):
                 ("T", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32), ("d", ctypes.c_int32),
                 ("softmax_scale", ctypes.c_float), ("cu_seqlens", ctypes.c_void_p), ("n_docs", ctypes.c_int32),
                 ("fwd_list", ctypes.c_void_p), ("o", ctypes.c_void_p), ("o_stride_t", ctypes.c_int64),
-                ("o_stride_h", ctypes.c_int64), ("lse", ctypes.c_void_p), ("non_causal", ctypes.c_int32)]
+                ("o_stride_h", ctypes.c_int64), ("lse", ctypes.c_void_p), ("non_causal", ctypes.c_int32),
+                ("precise", ctypes.c_int32)]
 
 
 class _BwdArgs(ctypes.Structure):
@@ -61,7 +62,7 @@ class _BwdArgs(ctypes.Structure):
                 ("dv_stride_t", ctypes.c_int64), ("dv_stride_h", ctypes.c_int64),
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
                 ("causal_dq_scale", ctypes.c_int32), ("dq_exp_out", ctypes.c_void_p),
-                ("non_causal", ctypes.c_int32), ("hadamard", ctypes.c_int32)]
+                ("non_causal", ctypes.c_int32), ("hadamard", ctypes.c_int32), ("precise", ctypes.c_int32)]
 
 
 _lib = None
@@ -157,10 +158,11 @@ def worklist_items(buf):
     return n, buf[4:4 + 4 * n].view(n, 4)
 
 
-def quantize(xs, cu_seqlens, hadamard=False):
+def quantize(xs, cu_seqlens, hadamard=False, per_token=False):
     """Token-block MXFP8 quantisation of up to three BF16 tensors [T, H, d] in one launch.
     hadamard: a bool for every tensor or one per tensor (rows rotated by H / sqrt(d) first; Q
-    and K of a training call).  Returns a list of (codes u8 [T, H, d], scales u8 [H, T])."""
+    and K of a training call); per_token: one exponent per token (the precision options).
+    Returns a list of (codes u8 [T, H, d], scales u8 [H, T])."""
     lib = load_library()
     n_docs = _check_cu(cu_seqlens)
     T, _, d = xs[0].shape
@@ -176,14 +178,16 @@ def quantize(xs, cu_seqlens, hadamard=False):
         H = x.shape[1]
         codes = torch.empty((T, H, d), dtype=torch.uint8, device=x.device)
         scales = torch.empty((H, T), dtype=torch.uint8, device=x.device)
-        arr[i] = _QTensor(x.data_ptr(), x.stride(0), x.stride(1), H, codes.data_ptr(), scales.data_ptr(), int(rot[i]))
+        arr[i] = _QTensor(x.data_ptr(), x.stride(0), x.stride(1), H, codes.data_ptr(), scales.data_ptr(), int(rot[i]),
+                          int(bool(per_token)))
         outs.append((codes, scales))
     _check(lib.flamia_quantize(arr, len(xs), T, d, _ptr(cu_seqlens), n_docs, None, 0, 0, None, _stream()))
     return outs
 
 
-def quantize_do(do, o, cu_seqlens):
-    """dO quantisation plus D = deq(dO) . O.  Returns (codes, scales, D f32 [H, T])."""
+def quantize_do(do, o, cu_seqlens, per_token=False):
+    """dO quantisation plus D = deq(dO) . O (per_token: one exponent per token).  Returns (codes,
+    scales, D f32 [H, T])."""
     lib = load_library()
     n_docs = _check_cu(cu_seqlens)
     _check_bf16(do, "do")
@@ -193,13 +197,14 @@ def quantize_do(do, o, cu_seqlens):
     scales = torch.empty((H, T), dtype=torch.uint8, device=do.device)
     D = torch.empty((H, T), dtype=torch.float32, device=do.device)
     arr = (_QTensor * 1)()
-    arr[0] = _QTensor(do.data_ptr(), do.stride(0), do.stride(1), H, codes.data_ptr(), scales.data_ptr(), 0)
+    arr[0] = _QTensor(do.data_ptr(), do.stride(0), do.stride(1), H, codes.data_ptr(), scales.data_ptr(), 0,
+                      int(bool(per_token)))
     _check(lib.flamia_quantize(arr, 1, T, d, _ptr(cu_seqlens), n_docs, _ptr(o), o.stride(0), o.stride(1),
                                _ptr(D), _stream()))
     return codes, scales, D
 
 
-def fwd(q, k, v, cu_seqlens, fwd_list, softmax_scale=None, out=None, causal=True):
+def fwd(q, k, v, cu_seqlens, fwd_list, softmax_scale=None, out=None, causal=True, precise=False):
     """Forward on quantised operands.  q, k, v are (codes, scales) pairs; causal=False lets every
     row see every key of its document.  Returns (O bf16 [T, Hq, d], LSE f32 [Hq, T] in log2 units)."""
     lib = load_library()
@@ -211,7 +216,7 @@ def fwd(q, k, v, cu_seqlens, fwd_list, softmax_scale=None, out=None, causal=True
     lse = torch.empty((Hq, T), dtype=torch.float32, device=qc.device)
     a = _FwdArgs(qc.data_ptr(), kc.data_ptr(), vc.data_ptr(), qs.data_ptr(), ks.data_ptr(), vs.data_ptr(),
                  T, Hq, Hkv, d, float(softmax_scale or 0.0), cu_seqlens.data_ptr(), n_docs, fwd_list.data_ptr(),
-                 o.data_ptr(), o.stride(0), o.stride(1), lse.data_ptr(), int(not causal))
+                 o.data_ptr(), o.stride(0), o.stride(1), lse.data_ptr(), int(not causal), int(bool(precise)))
     _check(lib.flamia_fwd(ctypes.byref(a), _stream()))
     return o, lse
 
@@ -234,7 +239,7 @@ def bwd_workspace_bytes_for(cu_seqlens_host, T, Hq, d, causal=True):
 
 
 def bwd(q, k, v, do, lse, D, cu_seqlens, lists, softmax_scale=None, causal_dq_scale=False, want_pi=False,
-        workspace=None, static_scratch=False, causal=True, hadamard=False):
+        workspace=None, static_scratch=False, causal=True, hadamard=False, precise=False):
     """Backward on quantised operands.  q, k, v, do are (codes, scales) pairs; lse, D f32 [Hq, T];
     lists: the micro-batch's Lists.  workspace: a uint8 CUDA tensor of at least
     bwd_workspace_bytes(n_docs, T, Hq, d, 0) bytes, or None to allocate one with the default
@@ -262,7 +267,8 @@ def bwd(q, k, v, do, lse, D, cu_seqlens, lists, softmax_scale=None, causal_dq_sc
                  dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), dq.stride(0), dq.stride(1), dk.stride(0), dk.stride(1),
                  dv.stride(0), dv.stride(1), workspace.data_ptr() if workspace is not None else None,
                  workspace.numel() if workspace is not None else 0, int(bool(causal_dq_scale)),
-                 pi.data_ptr() if pi is not None else None, int(not causal), int(bool(hadamard)))
+                 pi.data_ptr() if pi is not None else None, int(not causal), int(bool(hadamard)),
+                 int(bool(precise)))
     _check((lib.flamia_bwd_static if static_scratch else lib.flamia_bwd)(ctypes.byref(a), _stream()))
     return (dq, dk, dv, pi) if want_pi else (dq, dk, dv)
 

@@ -130,7 +130,10 @@ __device__ __forceinline__ void store_scales(FwdSmem<D>& sm, int kb, int vb, uin
 }
 
 // CAUSAL: keys after the query are masked (else every key of the document is visible).
-template <int D, int W, bool CAUSAL>
+// PRECISE (the precision options, with per-token scales): V's exponent is folded into the
+// probability operand against the row's running maximum of visited V exponents, and V enters
+// the product with its bare codes.
+template <int D, int W, bool CAUSAL, bool PRECISE>
 __global__ __launch_bounds__(fwd_threads<W>(), 8 / W) void fwd_kernel(FwdParams p) {
   constexpr int FWD_THREADS = fwd_threads<W>();
   constexpr int NC = D / 64;   // 64-wide d chunks of the score contraction
@@ -195,6 +198,7 @@ __global__ __launch_bounds__(fwd_threads<W>(), 8 / W) void fwd_kernel(FwdParams 
     for (int db = 0; db < NDB; ++db) oacc[db] = v16f{};
     float m = -__builtin_inff();  // running max, score units
     float l = 0.f;                // this lane's share of the row sum of 2^8 p
+    int vref = -119;              // PRECISE: largest V exponent among the keys visited so far
 
     lds_barrier();  // the previous unit's readers are done with every buffer
     {
@@ -288,11 +292,46 @@ __global__ __launch_bounds__(fwd_threads<W>(), 8 / W) void fwd_kernel(FwdParams 
         int vs[2];
 #pragma unroll
         for (int ci = 0; ci < 2; ++ci) vs[ci] = sm.sv[kb][64 * ci + 32 * hh];
+        // PRECISE: the V exponent bytes of element group (kb4, w4), keys 32 kb4 + 8 w4 + 4 hh + e
+        auto ev_word = [&](int kb4, int w4) {
+          return *reinterpret_cast<const uint32_t*>(&sm.sv[kb][32 * kb4 + 8 * w4 + 4 * hh]);
+        };
+        if constexpr (PRECISE) {
+          // the row's reference: the largest exponent among its visible keys (finite scores; the
+          // mask has made the others -inf) and the keys of earlier tiles, at least -119
+          uint32_t tmax = 0;
+#pragma unroll
+          for (int kb4 = 0; kb4 < 4; ++kb4)
+#pragma unroll
+            for (int w4 = 0; w4 < 4; ++w4) {
+              const uint32_t wv = ev_word(kb4, w4);
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                if (s[kb4][4 * w4 + e] > -__builtin_inff()) tmax = max(tmax, (wv >> (8 * e)) & 0xFFu);
+            }
+          const auto sw = __builtin_amdgcn_permlane32_swap((int)tmax, (int)tmax, false, false);
+          tmax = max((uint32_t)sw[0], (uint32_t)sw[1]);  // both lanes of the query
+          vref = max(vref, (int)tmax - 127);
+        }
+        // the probability codes: E4M3 of 2^8 p, PRECISE times 2^(e(V_j) - vref) (exact)
+        auto pcode = [&](float a0, float a1, float a2, float a3, int kb4, int w4) {
+          if constexpr (PRECISE) {
+            const uint32_t wv = ev_word(kb4, w4);
+            return pack4_fp8(__builtin_ldexpf(a0, (int)(wv & 0xFFu) - 127 - vref),
+                             __builtin_ldexpf(a1, (int)((wv >> 8) & 0xFFu) - 127 - vref),
+                             __builtin_ldexpf(a2, (int)((wv >> 16) & 0xFFu) - 127 - vref),
+                             __builtin_ldexpf(a3, (int)(wv >> 24) - 127 - vref));
+          } else {
+            return pack4_fp8(a0, a1, a2, a3);
+          }
+        };
+        const int v_scale = PRECISE ? 127 : 0;          // bare V codes (PRECISE)
+        const int p_scale = 127 - P_SHIFT + (PRECISE ? vref : 0);
         auto read_v = [&](int k) { return lds_read_tr32<D>(vt, 64 * (k / NDB), 32 * (k % NDB), lane); };
         constexpr int NPV = 2 * NDB;  // matrix instructions: (64-key half ci, d-block db)
         v8i ring[2];
         auto pv_step = [&](int k) {
-          oacc[k % NDB] = mfma_scaled(ring[k & 1], pop[k / NDB], oacc[k % NDB], vs[k / NDB], 127 - P_SHIFT);
+          oacc[k % NDB] = mfma_scaled(ring[k & 1], pop[k / NDB], oacc[k % NDB], PRECISE ? v_scale : vs[k / NDB], p_scale);
           if (k + 2 < NPV) ring[k & 1] = read_v(k + 2);
         };
         // blocks 0, 1: probabilities, row sum, codes
@@ -305,7 +344,7 @@ __global__ __launch_bounds__(fwd_threads<W>(), 8 / W) void fwd_kernel(FwdParams 
             const float p2 = __builtin_amdgcn_exp2f(fmaf(s[kb4][4 * w4 + 2], c, bias));
             const float p3 = __builtin_amdgcn_exp2f(fmaf(s[kb4][4 * w4 + 3], c, bias));
             l += (p0 + p1) + (p2 + p3);
-            pop[0][4 * kb4 + w4] = pack4_fp8(p0, p1, p2, p3);
+            pop[0][4 * kb4 + w4] = pcode(p0, p1, p2, p3, kb4, w4);
           }
         ring[0] = read_v(0);
         ring[1] = read_v(1);
@@ -321,7 +360,7 @@ __global__ __launch_bounds__(fwd_threads<W>(), 8 / W) void fwd_kernel(FwdParams 
 #pragma unroll
               for (int e = 0; e < 4; ++e) s[kb4][4 * w4 + e] = __builtin_amdgcn_exp2f(fmaf(s[kb4][4 * w4 + e], c, bias));
               pop[1][4 * (kb4 - 2) + w4] =
-                  pack4_fp8(s[kb4][4 * w4], s[kb4][4 * w4 + 1], s[kb4][4 * w4 + 2], s[kb4][4 * w4 + 3]);
+                  pcode(s[kb4][4 * w4], s[kb4][4 * w4 + 1], s[kb4][4 * w4 + 2], s[kb4][4 * w4 + 3], kb4, w4);
             }
             // first half, instructions 0 .. NDB - 1, spread over the four half blocks
             const int j = 2 * (kb4 - 2) + hb;
@@ -405,18 +444,19 @@ __global__ __launch_bounds__(fwd_threads<W>(), 8 / W) void fwd_kernel(FwdParams 
 hipError_t launch_fwd(const FwdParams& p, int d, int grid, hipStream_t s) {
   // documents of fewer than 4096 tokens on average: 128-query units, two workgroups per CU
   const bool short_docs = (int64_t)p.n_docs * 4096 > (int64_t)p.T;
-  auto go = [&](auto c) {
-    constexpr bool C = decltype(c)::value;
+  auto go = [&](auto c, auto pr) {
+    constexpr bool C = decltype(c)::value, PR = decltype(pr)::value;
     if (short_docs) {
-      if (d == 128) hipLaunchKernelGGL((fwd_kernel<128, 4, C>), dim3(2 * grid), dim3(fwd_threads<4>()), 0, s, p);
-      else hipLaunchKernelGGL((fwd_kernel<64, 4, C>), dim3(2 * grid), dim3(fwd_threads<4>()), 0, s, p);
+      if (d == 128) hipLaunchKernelGGL((fwd_kernel<128, 4, C, PR>), dim3(2 * grid), dim3(fwd_threads<4>()), 0, s, p);
+      else hipLaunchKernelGGL((fwd_kernel<64, 4, C, PR>), dim3(2 * grid), dim3(fwd_threads<4>()), 0, s, p);
     } else {
-      if (d == 128) hipLaunchKernelGGL((fwd_kernel<128, 8, C>), dim3(grid), dim3(fwd_threads<8>()), 0, s, p);
-      else hipLaunchKernelGGL((fwd_kernel<64, 8, C>), dim3(grid), dim3(fwd_threads<8>()), 0, s, p);
+      if (d == 128) hipLaunchKernelGGL((fwd_kernel<128, 8, C, PR>), dim3(grid), dim3(fwd_threads<8>()), 0, s, p);
+      else hipLaunchKernelGGL((fwd_kernel<64, 8, C, PR>), dim3(grid), dim3(fwd_threads<8>()), 0, s, p);
     }
   };
-  if (p.causal) go(std::true_type{});
-  else go(std::false_type{});
+  if (p.precise) go(std::true_type{}, std::true_type{});  // causal only (checked by the caller)
+  else if (p.causal) go(std::true_type{}, std::false_type{});
+  else go(std::false_type{}, std::false_type{});
   return hipGetLastError();
 }
 

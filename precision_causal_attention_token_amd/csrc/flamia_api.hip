@@ -166,7 +166,7 @@ flamia_status flamia_quantize(const flamia_qtensor* tensors, int32_t n_tensors, 
       return FLAMIA_ERR_SHAPE;
     if (!aligned(t.codes, 16)) return FLAMIA_ERR_SHAPE;
     p.t[i] = QTensorDev{static_cast<const uint16_t*>(t.x), t.stride_t, t.stride_h, t.H, t.codes, t.scales,
-                        t.hadamard ? 1 : 0};
+                        t.hadamard ? 1 : 0, t.per_token ? 1 : 0};
     if (t.H > p.maxH) p.maxH = t.H;
   }
   if (o) {
@@ -189,6 +189,7 @@ flamia_status flamia_fwd(const flamia_fwd_args* a, void* stream) {
   if (a->T < 0 || a->Hq < 1 || a->Hkv < 1 || a->n_docs < 0) return FLAMIA_ERR_SHAPE;
   if (a->d != 64 && a->d != 128) return FLAMIA_ERR_UNSUPPORTED;
   if (a->Hq % a->Hkv) return FLAMIA_ERR_UNSUPPORTED;
+  if (a->precise && a->non_causal) return FLAMIA_ERR_UNSUPPORTED;
   if (a->T > FLAMIA_MAX_T) return FLAMIA_ERR_UNSUPPORTED;
   if (!aligned(a->o, 8) || (a->o_stride_t % 4) || (a->o_stride_h % 4) || a->o_stride_t < 0 || a->o_stride_h < 0)
     return FLAMIA_ERR_SHAPE;
@@ -205,6 +206,7 @@ flamia_status flamia_fwd(const flamia_fwd_args* a, void* stream) {
   p.o = static_cast<uint16_t*>(a->o); p.ost = a->o_stride_t; p.osh = a->o_stride_h;
   p.lse = a->lse;
   p.causal = a->non_causal ? 0 : 1;
+  p.precise = a->precise ? 1 : 0;
 #ifdef FLAMIA_DEBUG_DUMP
   p.dbg = g_dbg;
 #endif
@@ -241,6 +243,7 @@ flamia_status flamia_bwd(const flamia_bwd_args* a, void* stream) {
   if (a->Hq % a->Hkv) return FLAMIA_ERR_UNSUPPORTED;
   if (a->T > FLAMIA_MAX_T) return FLAMIA_ERR_UNSUPPORTED;
   if (a->non_causal && a->causal_dq_scale) return FLAMIA_ERR_UNSUPPORTED;
+  if (a->precise) return FLAMIA_ERR_UNSUPPORTED;  // the backward's precision options: not built yet
   if (a->workspace_bytes < flamia_bwd_workspace_bytes(a->n_docs, a->T, a->Hq, a->d, 0)) return FLAMIA_ERR_WORKSPACE;
   const int64_t st[6] = {a->dq_stride_t, a->dq_stride_h, a->dk_stride_t, a->dk_stride_h, a->dv_stride_t, a->dv_stride_h};
   for (int i = 0; i < 6; ++i)

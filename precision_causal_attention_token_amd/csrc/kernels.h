@@ -46,6 +46,7 @@ struct QTensorDev {
   uint8_t* codes;
   uint8_t* scales;
   int32_t hadamard;  // rows rotated by H / sqrt(d) before quantisation
+  int32_t per_token;  // one exponent per token (blocks of one token)
 };
 
 struct QuantParams {
@@ -70,6 +71,7 @@ struct FwdParams {
   int64_t ost, osh;
   float* lse;
   int32_t causal;  // 1: keys j <= i; 0: every key of the document
+  int32_t precise;  // the precision options (per-token scales, V folded into P)
 #ifdef FLAMIA_DEBUG_DUMP
   DebugDump dbg;
 #endif

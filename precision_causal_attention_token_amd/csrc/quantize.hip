@@ -94,7 +94,12 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantParams p) {
     int16_t st = -1, len = 0;
     if (tau < T) {
       const int k = find_doc(p.cu, p.n_docs, tau);
-      if (k >= 0) {
+      if (k >= 0 && X.per_token) {  // every token is its own block: the window's rows own themselves
+        if (r < WIN) {
+          st = (int16_t)r;
+          len = 1;
+        }
+      } else if (k >= 0) {
         const int c0 = p.cu[k], c1 = p.cu[k + 1];
         const int bs = c0 + ((tau - c0) / BLK) * BLK;
         if (bs >= W0 && bs < W0 + WIN) {
