@@ -246,7 +246,24 @@ typedef struct {
                                          quantiser, BF16 round to nearest even), so dq and dk are
                                          the gradients of the unrotated inputs.  Needs dq, dk
                                          16-byte aligned and their strides multiples of 8. */
-  int32_t precise;                    /* the precision options (as in the forward) */
+  int32_t precise;                    /* 1: the precision options ([J] §3.2), causal only
+                                         (non_causal = 1 is FLAMIA_ERR_UNSUPPORTED): Q, K, V and
+                                         dO quantised with per_token = 1, the forward run with
+                                         precise = 1.  Each gradient product takes the operand it
+                                         contracts over with bare codes and that operand's
+                                         exponent moves into the quantised one before rounding:
+                                           dV_j = sum_i Phat''_ij q(dO_i),  P'' = P 2^e(dO_i),
+                                           dK_j = softmax_scale sum_i dShat''_ij q(Q_i),
+                                                  dS'' = dS 2^e(Q_i)  (32 x 32 block exponents),
+                                           dQ_i as above from dShat'_ij q(K_j), dS' = dS 2^e(K_j)
+                                                  with one exponent per (row i, 32-key block);
+                                         pi_i takes the maxima of e(V), e(K) up to row i itself
+                                         (causal_dq_scale is implied).  No later token then
+                                         changes an earlier row's dQ, nor (through shared
+                                         exponents) an earlier key's dK, dV.  dQ comes from a
+                                         query-stationary pass that recomputes S, dP and dS';
+                                         nothing is stored, so the call runs as one chunk in
+                                         any workspace the default accepts. */
 } flamia_bwd_args;
 
 /* Host.  Backward workspace for n_docs documents of total length T: a header, pi [Hq, T], the

@@ -33,14 +33,21 @@ typedef struct {
   float* fwd_m;     /* forward: running maximum m (score units) that the pair's probability used */
   uint8_t* fwd_p;   /* forward: E4M3 code of 2^8 2^(t_ij - m) */
   float* bwd_s;     /* backward: score accumulator, -inf where masked */
-  float* bwd_dp;    /* backward: D_i - dP_ij as accumulated */
-  uint8_t* bwd_p;   /* backward: Phat code (dV operand) */
+  float* bwd_dp;    /* backward: D_i - dP_ij as accumulated (precision options: times
+                       2^(e(Q_i) - e(dO_i)), the key-tile pass's folded form) */
+  uint8_t* bwd_p;   /* backward: Phat code (dV operand; precision options: of P 2^e(dO_i)) */
   uint8_t* bwd_ps;  /* backward: its 32x32 block exponent byte */
-  uint8_t* bwd_ds;  /* backward: dShat code (dK, dQ operand) */
+  uint8_t* bwd_ds;  /* backward: dShat code (dK, dQ operand; precision options: dK only, of
+                       dS 2^e(Q_i)) */
   uint8_t* bwd_dss; /* backward: its 32x32 block exponent byte */
   float* dq_part;   /* backward: [heads][rows][n_tiles][d], the FP32 dQ partial of each 128-key tile
                        (counted from the document start) times 2^pi, the value converted to FP16 */
   int32_t n_tiles;  /* key tiles per row in dq_part */
+  /* the precision options' query-stationary dQ pass: */
+  float* dq_s;      /* its score accumulator, -inf where masked */
+  float* dq_dp;     /* dP_ij - D_i as it formed it */
+  uint8_t* dq_ds;   /* E4M3 code of dS_ij 2^e(K_j) (the dQ operand) */
+  uint8_t* dq_dss;  /* its exponent byte, one per (row, 32-key block) */
 } flamia_debug_dump;
 
 /* Host.  Set the dump buffers used by every later flamia_fwd / flamia_bwd of this process (the

@@ -78,6 +78,10 @@ struct BwdSmem {
   float dd[NBUF][QT];
   int2 sqdo[NBUF][2];           // block scale bytes {Q, dO} of the step's two query blocks
   int xs_p[2][2][4], xs_d[2][2][4];  // block exponent bytes of (query block, key group)
+  // per-token scales (the precision options), per step row: Q's exponent byte and 2^e(dO_i);
+  // dd then holds D_i 2^(e(Q_i) - e(dO_i))
+  uint8_t sqr[NBUF][QT];
+  alignas(16) float pf[NBUF][QT];
 };
 
 // Step tiles go from global memory straight into LDS (16-byte direct loads: lane l of a wave
@@ -86,7 +90,7 @@ struct BwdSmem {
 // under the tile's swizzle.  Rows past the document end repeat its last row, and 1 KiB blocks
 // wholly past it are zero-filled instead of loaded: every use of those rows is masked to zero,
 // and the values are finite.
-template <int D>
+template <int D, bool PRECISE>
 __device__ __forceinline__ void issue_step_loads(const BwdParams& p, BwdSmem<D>& sm, int b, int doc_start, int L,
                                                  int h, int qt, int cw, int lane) {
   constexpr int CPR = D / 16;                    // 16-byte chunks per row
@@ -128,7 +132,7 @@ __device__ __forceinline__ void issue_step_loads(const BwdParams& p, BwdSmem<D>&
     }
   }
   }
-  if (cw < 2) {  // row statistics: one float per lane
+  if (cw == 0 || (cw == 1 && !PRECISE)) {  // row statistics: one float per lane (D: PRECISE, rescaled first)
     const int qr = min(q0 + lane, L - 1);
     const float* src = (cw == 0 ? p.lse : p.Dv) + (int64_t)h * p.T + doc_start + qr;
     dma_load4(src, lds_addr(cw == 0 ? sm.lse[b] : sm.dd[b]));
@@ -147,8 +151,17 @@ __device__ __forceinline__ void issue_step_loads(const BwdParams& p, BwdSmem<D>&
 // Phase k: producers finish step k and form the products of step k + 1, consumers work on step
 // k - 1 and load step k + 2; one barrier per phase.
 // CAUSAL: keys after the query are masked (else every key of the document is visible).
-template <int D, bool CAUSAL>
+// PRECISE (the precision options, causal, per-token scales): the products that contract over
+// queries take Q and dO with their bare codes, their exponents moving into the other operand
+// before it is block-quantised, P'' = P 2^e(dO_i) for dV and dS'' = dS 2^e(Q_i) for dK, so no
+// later query changes a block's shared exponent except through values it adds itself; dQ is
+// left to a query-stationary pass of its own (nothing is stored).  The folds are exact: D - dP
+// comes out as (D - dP) 2^(e(Q_i) - e(dO_i)) from dO's products taken with Q's exponent and an
+// accumulator started at D 2^(e(Q_i) - e(dO_i)), and P is multiplied by 2^e(dO_i) after the
+// exponential, so their product is dS''.
+template <int D, bool CAUSAL, bool PRECISE>
 __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
+  static_assert(CAUSAL || !PRECISE, "the precision options are causal");
   constexpr int NC = D / 64;
   constexpr int NDB = D / 32;
   __shared__ BwdSmem<D> sm;
@@ -182,7 +195,9 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
     const int doc_start = __builtin_amdgcn_readfirstlane(p.cu[doc]);
     const int L = __builtin_amdgcn_readfirstlane(p.cu[doc + 1]) - doc_start;
     const int n_qt = (L + QT - 1) / QT;
-    const bool store_ds = L > KV_TILE;  // two or more key tiles: dQ in the query-stationary kernel
+    // two or more key tiles: dQ in the query-stationary kernel (PRECISE: always, from its own
+    // recomputation)
+    const bool store_ds = !PRECISE && L > KV_TILE;
     int64_t ds_base = 0;  // the item's first block in the chunk's store
     if (store_ds) {
       const int64_t v = p.kv_off[__builtin_amdgcn_readfirstlane(p.tile_base[doc]) + kappa];
@@ -203,17 +218,33 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
     lds_barrier();  // the previous unit no longer reads LDS
     const int cw = wave - 4;  // consumer index (loads)
     // block scales of the two 32-row query blocks of a step: two lanes of consumer 2 load them
-    // into registers and store them to LDS at the end of the phase
-    auto scale_loads = [&](int h, int qt, int& rsq, int& rsdo) {
-      if (cw == 2 && lane < 2) {
+    // into registers and store them to LDS at the end of the phase.  PRECISE: consumer 1 loads
+    // the per-token exponents and D of the step's 64 rows (one per lane; rows past the document
+    // end repeat its last row) and stores the row tables
+    auto scale_loads = [&](int h, int qt, int& rsq, int& rsdo, float& rd) {
+      if constexpr (PRECISE) {
+        if (cw == 1) {
+          const int qr = min(QT * qt + lane, L - 1);
+          const int64_t ti = (int64_t)h * T + doc_start + qr;
+          rsq = p.sq[ti];
+          rsdo = p.sdo[ti];
+          rd = p.Dv[ti];
+        }
+      } else if (cw == 2 && lane < 2) {
         const int qr = min(QT * qt + 32 * lane, L - 1);
         const int64_t ti = (int64_t)h * T + doc_start + qr;
         rsq = p.sq[ti];
         rsdo = p.sdo[ti];
       }
     };
-    auto scale_store = [&](int b, int qt, int rsq, int rsdo) {
-      if (cw == 2 && lane < 2) {
+    auto scale_store = [&](int b, int qt, int rsq, int rsdo, float rd) {
+      if constexpr (PRECISE) {
+        if (cw == 1) {
+          sm.sqr[b][lane] = (uint8_t)rsq;
+          sm.pf[b][lane] = __builtin_ldexpf(1.0f, rsdo - 127);
+          sm.dd[b][lane] = __builtin_ldexpf(rd, rsq - rsdo);
+        }
+      } else if (cw == 2 && lane < 2) {
         int l = lane;
         asm volatile("" : "+v"(l));  // address formed here, not kept in a register all along
         const bool valid = QT * qt + 32 * l < L;
@@ -227,14 +258,15 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
       return qt_first + (st - hi * nq);
     };
     int rsq = 127, rsdo = 127, rsq1 = 127, rsdo1 = 127;
+    float rd = 0.f, rd1 = 0.f;
     if (!producer) {
-      issue_step_loads<D>(p, sm, 0, doc_start, L, g * grp, qt_first, cw, lane);
-      scale_loads(g * grp, qt_first, rsq, rsdo);
+      issue_step_loads<D, PRECISE>(p, sm, 0, doc_start, L, g * grp, qt_first, cw, lane);
+      scale_loads(g * grp, qt_first, rsq, rsdo, rd);
       if (n_steps > 1) {
         int h1;
         const int qt1 = step_qt(1, h1);
-        issue_step_loads<D>(p, sm, 1, doc_start, L, h1, qt1, cw, lane);
-        scale_loads(h1, qt1, rsq1, rsdo1);
+        issue_step_loads<D, PRECISE>(p, sm, 1, doc_start, L, h1, qt1, cw, lane);
+        scale_loads(h1, qt1, rsq1, rsdo1, rd1);
       }
     }
     {
@@ -264,10 +296,10 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
     }
     if (!producer) {
       __builtin_amdgcn_s_waitcnt(0);  // the direct loads have landed
-      scale_store(0, qt_first, rsq, rsdo);
+      scale_store(0, qt_first, rsq, rsdo, rd);
       if (n_steps > 1) {
         int h1;
-        scale_store(1, step_qt(1, h1), rsq1, rsdo1);
+        scale_store(1, step_qt(1, h1), rsq1, rsdo1, rd1);
       }
     }
     lds_barrier();
@@ -301,12 +333,15 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
           const float4 d4 = *reinterpret_cast<const float4*>(&sm.dd[bb][32 * qb + 8 * j + 4 * hh]);
           pa[4 * j] = d4.x; pa[4 * j + 1] = d4.y; pa[4 * j + 2] = d4.z; pa[4 * j + 3] = d4.w;
         }
+        // A scales: the block bytes, or PRECISE the row's Q exponent for both products
+        const int sq_a = PRECISE ? (int)sm.sqr[bb][32 * qb + n] : sm.sqdo[bb][qb].x;
+        const int sdo_a = PRECISE ? sq_a : sm.sqdo[bb][qb].y;
 #pragma unroll
         for (int cc = 0; cc < NC; ++cc) {
           const v8i aq = lds_read_row32<D>(sm.q[bb], 32 * qb + n, 64 * cc + 32 * hh);
-          sa = mfma_scaled(aq, kreg[cc], cc ? sa : v16f{}, sm.sqdo[bb][qb].x, k_scale);
+          sa = mfma_scaled(aq, kreg[cc], cc ? sa : v16f{}, sq_a, k_scale);
           const v8i ad = lds_read_row32<D>(sm.dO[bb], 32 * qb + n, 64 * cc + 32 * hh);
-          pa = mfma_scaled(ad, vreg[cc], pa, sm.sqdo[bb][qb].y, v_scale);
+          pa = mfma_scaled(ad, vreg[cc], pa, sdo_a, v_scale);
         }
       };
       // One block's softmax terms fused with another block's products.  Softmax of query block
@@ -331,8 +366,18 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
           const float4 d4 = *reinterpret_cast<const float4*>(&sm.dd[bp][32 * qp + 8 * j + 4 * hh]);
           np[4 * j] = d4.x; np[4 * j + 1] = d4.y; np[4 * j + 2] = d4.z; np[4 * j + 3] = d4.w;
         }
-        const int2 sqdo = sm.sqdo[bp][qp];  // one 8-byte read
-        const int sq_s = sqdo.x, sdo_s = sqdo.y;
+        int sq_s, sdo_s;
+        if constexpr (PRECISE) {
+          sq_s = sdo_s = sm.sqr[bp][32 * qp + n];
+        } else {
+          const int2 sqdo = sm.sqdo[bp][qp];  // one 8-byte read
+          sq_s = sqdo.x;
+          sdo_s = sqdo.y;
+        }
+        float4 pf4[4];  // PRECISE: 2^e(dO) of the same rows as lse4
+        if constexpr (PRECISE)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) pf4[j] = *reinterpret_cast<const float4*>(&sm.pf[bs][32 * qs + 8 * j + 4 * hh]);
         // operand m: Q rows (m even) or dO rows (m odd) of column chunk m / 2; two in flight
         auto read_op = [&](int m) {
           return lds_read_row32<D>((m & 1) ? sm.dO[bp] : sm.q[bp], 32 * qp + n, 64 * (m >> 1) + 32 * hh);
@@ -371,8 +416,12 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
               }
             }
 #endif
-            const float pv = __builtin_amdgcn_exp2f(arg);
-            const float dsv = -(pv * pa[i]);  // P (dP - D)
+            float pv = __builtin_amdgcn_exp2f(arg);
+            if constexpr (PRECISE) {  // P'' = P 2^e(dO_i), exact
+              const float4 f = pf4[i / 4];
+              pv *= i % 4 == 0 ? f.x : i % 4 == 1 ? f.y : i % 4 == 2 ? f.z : f.w;
+            }
+            const float dsv = -(pv * pa[i]);  // P (dP - D), PRECISE P'' (D - dP)'' = dS 2^e(Q_i)
             sa[i] = pv;
             pa[i] = dsv;
             pmax = fmaxf(pmax, pv);
@@ -417,7 +466,7 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
         auto hand_over = [&](int qb) {
           sm.xp[x2][kw][qb][lane] = make_int4(pp[4 * qb], pp[4 * qb + 1], pp[4 * qb + 2], pp[4 * qb + 3]);
           sm.xd[x2][kw][qb][lane] = make_int4(pd[4 * qb], pd[4 * qb + 1], pd[4 * qb + 2], pd[4 * qb + 3]);
-          if (!store_ds) {
+          if (!PRECISE && !store_ds) {
             int l = lane;
             asm volatile("" : "+v"(l));  // addresses formed here, not kept in registers all along
             const int nl = l & 31, hl = l >> 5;
@@ -486,8 +535,8 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
         const int qtn = ld_qt;
         const int bn = (ph + 2) & (NBUF - 1);
         if (ph + 2 < n_steps) {  // step ph + 2's tiles, straight into LDS
-          issue_step_loads<D>(p, sm, bn, doc_start, L, ld_h, qtn, cw, lane);
-          scale_loads(ld_h, qtn, rsq, rsdo);
+          issue_step_loads<D, PRECISE>(p, sm, bn, doc_start, L, ld_h, qtn, cw, lane);
+          scale_loads(ld_h, qtn, rsq, rsdo, rd);
           if (++ld_qt == n_qt) {
             ld_qt = qt_first;
             ++ld_h;
@@ -522,7 +571,9 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
             }
             const v8i bp = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
             const v8i bd = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
-            const int2 sqdo_h = sm.sqdo[b][hh];
+            // A scales: the query block's bytes, or PRECISE the bare codes (the exponents are in
+            // P'' and dS'')
+            const int2 sqdo_h = PRECISE ? make_int2(127, 127) : sm.sqdo[b][hh];
             const int sdo_h = sqdo_h.y, sq_h = sqdo_h.x;
             const int sp_h = sm.xs_p[xb][hh][kw], sds_h = sm.xs_d[xb][hh][kw];
             // Operand k (dO^T for even k, Q^T for odd k, d-block k / 2) is read AHEAD matrix
@@ -543,7 +594,7 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
               __builtin_amdgcn_sched_barrier(0);
             }
           }
-          if (!store_ds) {
+          if (!PRECISE && !store_ds) {
             // single key tile: dQ^T = K^T dShat^T here, the only contribution of its rows;
             // consumer w computes d-block w (d = 128) or w % 2 (d = 64) of its query blocks
             const int hi = st / nq;
@@ -596,7 +647,7 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
         }
         if (ph + 2 < n_steps) {
           __builtin_amdgcn_s_waitcnt(0);  // the direct loads have landed
-          scale_store(bn, qtn, rsq, rsdo);
+          scale_store(bn, qtn, rsq, rsdo, rd);
         }
         lds_barrier();  // phase done: operands consumed, the next step's tiles stored
       }
@@ -995,9 +1046,10 @@ __device__ void layout_chunks(const BwdParams& p) {
   }
   const int n_items = p.list[0];
   const int4* items = reinterpret_cast<const int4*>(p.list + 4);
+  // the precision options store nothing (their dQ pass recomputes): one chunk
   auto blocks_of = [&](int u) {
     const int4 it = items[u];
-    return item_blocks(p.cu[it.x + 1] - p.cu[it.x], it.y, p.causal_mask);
+    return p.precise ? (int64_t)0 : item_blocks(p.cu[it.x + 1] - p.cu[it.x], it.y, p.causal_mask);
   };
   auto chunk_of = [&](int64_t P, int64_t b) {
     const int64_t last = P + b - 1;
@@ -1212,12 +1264,20 @@ hipError_t launch_bwd(const BwdParams& p, int d, int grid, hipStream_t s) {
       hipLaunchKernelGGL(dk, dim3(2 * grid), dim3(DQ_THREADS), 0, s, q);
     }
   };
+  if (p.precise) {  // causal only (checked by the caller); one chunk, nothing stored
+    BwdParams q = p;
+    q.chunk = 0;
+    if (d == 128) hipLaunchKernelGGL((bwd_kernel<128, true, true>), dim3(grid), dim3(BWD_THREADS), 0, s, q);
+    else hipLaunchKernelGGL((bwd_kernel<64, true, true>), dim3(grid), dim3(BWD_THREADS), 0, s, q);
+    const hipError_t e = hipGetLastError();
+    return e != hipSuccess ? e : launch_dq_precise(q, d, grid, s);
+  }
   if (d == 128) {
-    if (p.causal_mask) chunks(bwd_kernel<128, true>, dq_kernel<128>);
-    else chunks(bwd_kernel<128, false>, dq_kernel<128>);
+    if (p.causal_mask) chunks(bwd_kernel<128, true, false>, dq_kernel<128>);
+    else chunks(bwd_kernel<128, false, false>, dq_kernel<128>);
   } else {
-    if (p.causal_mask) chunks(bwd_kernel<64, true>, dq_kernel<64>);
-    else chunks(bwd_kernel<64, false>, dq_kernel<64>);
+    if (p.causal_mask) chunks(bwd_kernel<64, true, false>, dq_kernel<64>);
+    else chunks(bwd_kernel<64, false, false>, dq_kernel<64>);
   }
   return hipGetLastError();
 }

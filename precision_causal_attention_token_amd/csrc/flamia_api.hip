@@ -26,7 +26,7 @@ extern "C" flamia_status flamia_debug_set_dump(const flamia_debug_dump* d) {
   if (d->row_hi <= d->row_lo || d->key_hi <= d->key_lo || d->head_hi <= d->head_lo) return FLAMIA_ERR_SHAPE;
   g_dbg = DebugDump{d->row_lo, d->row_hi, d->key_lo, d->key_hi, d->head_lo, d->head_hi, d->fwd_s, d->fwd_m,
                     d->fwd_p, d->bwd_s, d->bwd_dp, d->bwd_p, d->bwd_ps, d->bwd_ds, d->bwd_dss, d->dq_part,
-                    d->n_tiles};
+                    d->n_tiles, d->dq_s, d->dq_dp, d->dq_ds, d->dq_dss};
   return FLAMIA_OK;
 }
 #endif
@@ -243,7 +243,7 @@ flamia_status flamia_bwd(const flamia_bwd_args* a, void* stream) {
   if (a->Hq % a->Hkv) return FLAMIA_ERR_UNSUPPORTED;
   if (a->T > FLAMIA_MAX_T) return FLAMIA_ERR_UNSUPPORTED;
   if (a->non_causal && a->causal_dq_scale) return FLAMIA_ERR_UNSUPPORTED;
-  if (a->precise) return FLAMIA_ERR_UNSUPPORTED;  // the backward's precision options: not built yet
+  if (a->non_causal && a->precise) return FLAMIA_ERR_UNSUPPORTED;  // the precision options are causal
   if (a->workspace_bytes < flamia_bwd_workspace_bytes(a->n_docs, a->T, a->Hq, a->d, 0)) return FLAMIA_ERR_WORKSPACE;
   const int64_t st[6] = {a->dq_stride_t, a->dq_stride_h, a->dk_stride_t, a->dk_stride_h, a->dv_stride_t, a->dv_stride_h};
   for (int i = 0; i < 6; ++i)
@@ -296,8 +296,10 @@ flamia_status flamia_bwd(const flamia_bwd_args* a, void* stream) {
   p.max_chunks = (int32_t)max_chunks;
   p.n_tab = (int32_t)n_tiles(a->n_docs, a->T);
   p.pi_out = a->dq_exp_out;
-  p.causal = a->causal_dq_scale ? 1 : 0;
+  // the precision options take the causal prescale per token (maxima up to the row)
+  p.causal = (a->causal_dq_scale || a->precise) ? 1 : 0;
   p.causal_mask = a->non_causal ? 0 : 1;
+  p.precise = a->precise ? 1 : 0;
 #ifdef FLAMIA_DEBUG_DUMP
   p.dbg = g_dbg;
 #endif

@@ -24,6 +24,10 @@ struct DebugDump {
   uint8_t* bwd_dss;
   float* dq_part;     // [heads][rows][n_tiles][d]: each key tile's dQ partial times 2^pi, as converted to FP16
   int32_t n_tiles;
+  float* dq_s;        // precision options' dQ pass: score accumulator after the mask
+  float* dq_dp;       // dP - D as it formed it
+  uint8_t* dq_ds;     // code of dS 2^e(K_j) and its (row, 32-key block) exponent byte
+  uint8_t* dq_dss;
 };
 // Position of (query head, row) in the window's rows, or -1 outside it.
 __device__ __forceinline__ int64_t dbg_row(const DebugDump& g, int h, int row) {
@@ -109,6 +113,8 @@ struct BwdParams {
   int16_t* pi_out;          // optional copy of pi
   int32_t causal;           // causal dQ prescale option
   int32_t causal_mask;      // 1: keys j <= i; 0: every key of the document
+  int32_t precise;          // the precision options: per-token scales folded into P and dS, dQ
+                            // recomputed query-stationary with row-wise dS exponents
 #ifdef FLAMIA_DEBUG_DUMP
   DebugDump dbg;
 #endif
@@ -122,5 +128,7 @@ hipError_t launch_worklist(const int32_t* cu, int n_docs, int T, int kind, int n
                            hipStream_t s);
 hipError_t launch_fwd(const FwdParams& p, int d, int grid, hipStream_t s);
 hipError_t launch_bwd(const BwdParams& p, int d, int grid, hipStream_t s);
+// dQ under the precision options (query-stationary recomputation), after the key-tile pass.
+hipError_t launch_dq_precise(const BwdParams& p, int d, int grid, hipStream_t s);
 
 }  // namespace flamia

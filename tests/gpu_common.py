@@ -87,7 +87,8 @@ def _dump_struct(win, bufs):
     class Dump(ctypes.Structure):
         _fields_ = [(n, ctypes.c_int32) for n in ("row_lo", "row_hi", "key_lo", "key_hi", "head_lo", "head_hi")] + \
                    [(n, ctypes.c_void_p) for n in ("fwd_s", "fwd_m", "fwd_p", "bwd_s", "bwd_dp", "bwd_p", "bwd_ps",
-                                                   "bwd_ds", "bwd_dss", "dq_part")] + [("n_tiles", ctypes.c_int32)]
+                                                   "bwd_ds", "bwd_dss", "dq_part")] + [("n_tiles", ctypes.c_int32)] + \
+                   [(n, ctypes.c_void_p) for n in ("dq_s", "dq_dp", "dq_ds", "dq_dss")]
     d = Dump(win["row_lo"], win["row_hi"], win["key_lo"], win["key_hi"], win["head_lo"], win["head_hi"])
     for n, t in bufs.items():
         setattr(d, n, t.data_ptr())
@@ -99,8 +100,8 @@ def n_key_tiles(win):
     return -(-(win["key_hi"] - win["key_lo"]) // 128)
 
 
-DUMP_F32 = ("fwd_s", "fwd_m", "bwd_s", "bwd_dp")
-DUMP_U8 = ("fwd_p", "bwd_p", "bwd_ps", "bwd_ds", "bwd_dss")
+DUMP_F32 = ("fwd_s", "fwd_m", "bwd_s", "bwd_dp", "dq_s", "dq_dp")
+DUMP_U8 = ("fwd_p", "bwd_p", "bwd_ps", "bwd_ds", "bwd_dss", "dq_ds", "dq_dss")
 
 
 def gpu_call(q, k, v, do, cu, causal_dq=False, softmax_scale=None, window=None, store_budget=None, causal=True,
@@ -482,7 +483,7 @@ def validate_backward(orc, g, cu, causal_dq=False, softmax_scale=None):
     return dict(replay=r, kv=kv, kmask=kmask, beyond=beyond, dq16=dq16)
 
 
-def validate_dq_partials(orc, g, cu, pi, ss):
+def validate_dq_partials(orc, g, cu, pi, ss, ds_name="bwd_ds", k_bare=False):
     """Each key tile's FP32 dQ partial (times 2^pi, as the GPU converts it to FP16) against the
     exact partial of the GPU's dShat codes and K: within the FP8 instruction's accumulation bound
     (2^-10 of the largest products of its two 64-key chunks, here bounded by chunk maxima of
@@ -494,7 +495,9 @@ def validate_dq_partials(orc, g, cu, pi, ss):
     grp = Hq // g["k"].shape[1]
     causal = g.get("causal", True)
     parts = du["dq_part"]                                                    # [h, r, tiles, d]
-    kd = dequant(g["k"], g["sk"])
+    # the dS operand's codes and exponents (ds_name, ds_name + "s"), and K with its scales or, with
+    # k_bare (the precision options, whose dS operand carries K's exponent), its bare codes
+    kd = dequant(g["k"], np.full_like(g["sk"], 127) if k_bare else g["sk"])
     dm = doc_map(cu, T)
     out = np.zeros(parts.shape[:2] + (d,), np.uint16)
     ss32 = np.float32(ss)
@@ -509,8 +512,8 @@ def validate_dq_partials(orc, g, cu, pi, ss):
         vis = visible_mask(cu, T, win, causal)[rs, a - win["key_lo"]:b - win["key_lo"]]
         last = (np.arange(r0, r1) - a) // 128 if causal else np.full(r1 - r0, nkt - 1)  # last key tile of each row
         for x, h in enumerate(range(win["head_lo"], win["head_hi"])):
-            dsh = orc.e4m3_decode(du["bwd_ds"][x, rs, a - win["key_lo"]:b - win["key_lo"]]) * \
-                np.exp2(du["bwd_dss"][x, rs, a - win["key_lo"]:b - win["key_lo"]].astype(np.float64) - 127)
+            dsh = orc.e4m3_decode(du[ds_name][x, rs, a - win["key_lo"]:b - win["key_lo"]]) * \
+                np.exp2(du[ds_name + "s"][x, rs, a - win["key_lo"]:b - win["key_lo"]].astype(np.float64) - 127)
             dsh = np.where(vis, dsh, 0.0)
             scale = np.exp2(pi[h, r0:r1].astype(np.float64))[:, None]
             acc = np.zeros((r1 - r0, d), np.float16)
@@ -537,6 +540,151 @@ def validate_dq_partials(orc, g, cu, pi, ss):
     say("  dQ partials: %d values vs the exact partials of the GPU's dShat codes, max error / bound %.3f"
         % (n_checked, worst))
     return out
+
+
+def check_row_exponents(name, got_e, vals, vis, orc):
+    """Per (row, 32-key block of one document): the exponent byte is the round-up exponent of the
+    row's largest |value| over the block's visible keys, the same for every key of the block, or
+    one off with that maximum within EXP_REL of the boundary between them.  [h, rows, keys] of ONE
+    document, keys from its start."""
+    h, R, K = vals.shape
+    Kp = -(-K // 32) * 32
+    a = np.zeros((h, R, Kp))
+    a[..., :K] = np.where(vis, np.abs(vals), 0.0)
+    rmax = a.reshape(h, R, Kp // 32, 32).max(-1)                         # [h, R, nbk]
+    e_ref = orc.e8m0_roundup(rmax) + 127
+    ge = np.full((h, R, Kp), -1, np.int64)
+    ge[..., :K] = got_e
+    vb = np.zeros((h, R, Kp), bool)
+    vb[..., :K] = vis
+    gb, vb = ge.reshape(h, R, Kp // 32, 32), vb.reshape(h, R, Kp // 32, 32)
+    any_vis = vb.any(-1)
+    gmax = np.where(vb, gb, -1).max(-1)
+    gmin = np.where(vb, gb, 999).min(-1)
+    assert np.array_equal(gmax[any_vis], gmin[any_vis]), name + ": row exponent not constant over the block"
+    bad = any_vis & (gmax != e_ref)
+    n_bad = int(bad.sum())
+    if n_bad:
+        lo = np.minimum(gmax[bad], e_ref[bad]) - 127
+        near = (np.abs(gmax[bad] - e_ref[bad]) == 1) & (np.abs(rmax[bad] - 448.0 * 2.0 ** lo) <= EXP_REL * rmax[bad])
+        say("    %s row exponents: %d of %d differ from the oracle's, all at a boundary: %s"
+            % (name, n_bad, int(any_vis.sum()), bool(near.all())))
+        assert near.all(), name
+    return n_bad
+
+
+def validate_backward_precise(orc, g, cu, softmax_scale=None):
+    """The precision options' backward (causal, per-token scales): checks 2, 4, 5 as in
+    validate_backward, on the folded operands.  Key-tile pass: D - dP as accumulated (times
+    2^(e(Q_i) - e(dO_i))), P'' = P 2^e(dO_i) and dS'' = dS 2^e(Q_i) with their 32x32 block
+    exponents, and dK, dV replayed from them with Q's and dO's bare codes.  dQ pass: its scores
+    bit-identical to the key-tile pass's, its dP - D, dS' = dS 2^e(K_j) with one exponent per
+    (row, 32-key block), its partials, and dQ replayed with K's bare codes."""
+    win, du = g["window"], g["dumps"]
+    T, Hq, d = g["q"].shape
+    Hkv = g["k"].shape[1]
+    grp = Hq // Hkv
+    ss = 1.0 / np.sqrt(d) if not softmax_scale else softmax_scale
+    c32 = score_scale32(d, softmax_scale)
+    vis = visible_mask(cu, T, win, True)
+    hs = list(range(win["head_lo"], win["head_hi"]))
+    rows = slice(win["row_lo"], win["row_hi"])
+    keys = slice(win["key_lo"], win["key_hi"])
+    pi = orc.dq_exponents(g["sk"], g["sv"], g["sdo"], cu, Hkv, d, True, per_token=True)
+    assert np.array_equal(g["pi"], pi), "pi"
+    eq = np.stack([g["sq"][h, rows] for h in hs]).astype(np.float64)[:, :, None] - 127
+    edo = np.stack([g["sdo"][h, rows] for h in hs]).astype(np.float64)[:, :, None] - 127
+    # 2'. the key-tile pass's folded D - dP and the dQ pass's dP - D against the exact dot products
+    dod, vd = dequant(g["do"], g["sdo"]), dequant(g["v"], g["sv"])
+    DP, DQP = du["bwd_dp"], du["dq_dp"]
+    worst = [0.0, 0.0]
+    for x, h in enumerate(hs):
+        Dr = g["D"][h, rows].astype(np.float64)[:, None]
+        ex = Dr - dod[rows, h] @ vd[keys, h // grp].T
+        bound = ACC_REL * (_chunk_max(dod[rows, h]) @ _chunk_max(vd[keys, h // grp]).T + np.abs(Dr)) + \
+            2.0 ** -22 * np.abs(ex)
+        for y, got in enumerate((DP[x].astype(np.float64) * np.exp2(edo[x] - eq[x]), -DQP[x].astype(np.float64))):
+            err = np.where(vis, np.abs(got - ex), 0.0)
+            worst[y] = max(worst[y], float((err / np.where(vis, bound, 1.0)).max()))
+            assert (err <= bound).all(), "D - dP beyond the accumulation bound"
+    say("  D - dP vs exact dot products: key-tile pass (unfolded) max error / bound %.3f, dQ pass %.3f"
+        % tuple(worst))
+    # the dQ pass's scores: bit-identical to the key-tile pass's, masks included
+    S = du["bwd_s"]
+    assert np.array_equal(np.isnan(S), np.isnan(du["dq_s"])), "dQ pass: pairs visited"
+    assert np.array_equal(S.view(np.uint32), du["dq_s"].view(np.uint32)), "dQ pass: scores"
+    say("  dQ pass scores: bit-identical to the key-tile pass's (%d pairs)" % int((~np.isnan(S)).sum()))
+    # 4'. decisions: P'' and dS'' (32 x 32 blocks), dS' (per row and 32-key block)
+    lse = np.stack([g["lse"][h, rows] for h in hs])[:, :, None]
+    ek = np.stack([g["sk"][h // grp, keys] for h in hs]).astype(np.float64)[:, None, :] - 127
+    with np.errstate(invalid="ignore", over="ignore"):
+        Pv = np.exp2(fma32(S, c32, -lse).astype(np.float64)).astype(np.float32)
+        P2 = (Pv.astype(np.float64) * np.exp2(edo)).astype(np.float32)
+        dS2 = -(P2.astype(np.float64) * DP.astype(np.float64)).astype(np.float32)
+        dS0 = (Pv.astype(np.float64) * DQP.astype(np.float64)).astype(np.float32)
+        dS1 = dS0.astype(np.float64) * np.exp2(ek)
+        # values below FP32's normal range at some step of their formation (the exponential, the
+        # fold, the product, the converted value)
+        sub = lambda x: np.abs(x) < 2.0 ** -126
+        tiny = dict(p=sub(Pv) | sub(P2), ds=sub(Pv) | sub(P2) | sub(dS2), dsq=sub(Pv) | sub(dS0) | sub(dS1))
+    vis3 = np.broadcast_to(vis, S.shape)
+    vals = dict(p=np.where(vis3, P2, 0.0).astype(np.float64), ds=np.where(vis3, dS2, 0.0).astype(np.float64),
+                dsq=np.where(vis3, dS1, 0.0))
+    dm = doc_map(cu, T)
+    counts = dict(p=[0, 0, 0], ds=[0, 0, 0], dsq=[0, 0, 0], tiny=0)
+    for doc in sorted(set(dm[win["row_lo"]:win["row_hi"]]) - {-1}):
+        a, b = int(cu[doc]), int(cu[doc + 1])
+        r0, r1 = max(a, win["row_lo"]), min(b, win["row_hi"])
+        assert (r0 - a) % 32 == 0, "window rows must start on a block of the document"
+        rs, ks = slice(r0 - win["row_lo"], r1 - win["row_lo"]), slice(a - win["key_lo"], b - win["key_lo"])
+        v_doc = np.broadcast_to(vis[rs, ks], (len(hs),) + vis[rs, ks].shape)
+        for nm, code, ex in (("p", du["bwd_p"], du["bwd_ps"]), ("ds", du["bwd_ds"], du["bwd_dss"]),
+                             ("dsq", du["dq_ds"], du["dq_dss"])):
+            label = {"p": "P''", "ds": "dS''", "dsq": "dS'"}[nm]
+            if nm == "dsq":
+                counts[nm][2] += check_row_exponents(label, ex[:, rs, ks], vals[nm][:, rs, ks], v_doc, orc)
+            else:
+                counts[nm][2] += check_block_exponents(label, ex[:, rs, ks], vals[nm][:, rs, ks], v_doc, orc)
+            y = np.where(v_doc, vals[nm][:, rs, ks] * np.exp2(127.0 - ex[:, rs, ks].astype(np.float64)), 0.0)
+            # the hardware returns +0 for values below FP32's normal range (the exponential's result,
+            # a denormal input of the conversion), where the method's value is a tiny nonzero
+            # number; with per-token exponents folded in (and one exponent per row for dS') such a
+            # value can still reach E4M3 resolution.  A zero code is accepted there: the term is
+            # below 2^-126 times an operand of the product, far under the FP32 sums' rounding and,
+            # for dQ, under the FP16 sums' smallest value (|x 2^pi| < 2^-62)
+            lo_ok = tiny[nm][:, rs, ks] & (orc.e4m3_decode(code[:, rs, ks]) == 0)
+            counts["tiny"] += int((lo_ok & v_doc & (orc.e4m3_decode(orc.e4m3_rne(y)) != 0)).sum())
+            nb, nt = check_decision(label + " codes", code[:, rs, ks], y, orc, v_doc, lo_ok=lo_ok)
+            counts[nm][0] += nb
+            counts[nm][1] += nt
+    if counts["tiny"]:
+        say("  %d codes zero where a value on the way is below FP32's normal range (accepted)"
+            % counts["tiny"])
+    for nm, label in (("p", "P''"), ("ds", "dS''"), ("dsq", "dS'")):
+        say("  %-4s: %d / %d codes and %d exponents at a rounding boundary, the rest equal the oracle's rounding"
+            % (label, counts[nm][0], counts[nm][1], counts[nm][2]))
+    # 5'. products against the replays on the GPU's decisions (operands with bare codes where their
+    # exponent was folded into the other one)
+    bare = lambda t: np.full_like(t, 127)
+    r = orc.bwd_replay(g["q"], bare(g["sq"]), g["k"], g["sk"], g["do"], bare(g["sdo"]), cu, pi, win, du["bwd_p"],
+                       du["bwd_ps"], du["bwd_ds"], du["bwd_dss"], ss)
+    rq = orc.bwd_replay(g["q"], g["sq"], g["k"], bare(g["sk"]), g["do"], g["sdo"], cu, pi, win, du["bwd_p"],
+                        du["bwd_ps"], du["dq_ds"], du["dq_dss"], ss)
+    r["dq64"] = rq["dq64"]
+    rmask = dm[win["row_lo"]:win["row_hi"]] >= 0
+    got_dq = np.transpose(g["dq"][rows][:, win["head_lo"]:win["head_hi"]], (1, 0, 2))
+    dq16 = validate_dq_partials(orc, g, cu, pi, ss, ds_name="dq_ds", k_bare=True)
+    same = np.array_equal(got_dq[:, rmask], dq16[:, rmask])
+    say("  stage dQ vs the FP16 sum of the GPU's partials (ascending tiles, two roundings each): bit-identical %s"
+        % same)
+    assert same, "dQ"
+    beyond = {"dQ": bar_check("dQ", got_dq[:, rmask], r["dq64"][:, rmask], orc, enforce=False)}
+    kv = [x for x in range(Hkv) if x * grp >= win["head_lo"] and (x + 1) * grp <= win["head_hi"]]
+    kmask = rmask & ~np.isnan(r["dk64"][kv[0], :, 0]) if kv else rmask
+    for nm, ref in (("dK", r["dk64"]), ("dV", r["dv64"])):
+        got = np.transpose(g[nm.lower()][rows][:, kv], (1, 0, 2))
+        beyond[nm] = bar_check(nm, got[:, kmask], ref[kv][:, kmask], orc)
+    return dict(replay=r, kv=kv, kmask=kmask, beyond=beyond, dq16=dq16)
 
 
 def chain_check(orc, g, ref, cu, fwd_val, bwd_val, zero_in_exact=()):

@@ -100,6 +100,8 @@ def test_host_validation_errors(lib):
     b.dq_stride_t, b.dq_stride_h = 4 * 64 + 4, 64               # 8-byte aligned, not a multiple of 8 elements
     b.dk_stride_t, b.dk_stride_h, b.dv_stride_t, b.dv_stride_h = 128, 64, 128, 64
     assert lib.flamia_bwd(ctypes.byref(b), None) == 2          # the un-rotation needs 16-byte rows
+    b.hadamard, b.non_causal, b.precise = 0, 1, 1
+    assert lib.flamia_bwd(ctypes.byref(b), None) == 3          # the precision options are causal
     # the dO pass is never rotated
     t = (fl._QTensor * 1)()
     t[0] = fl._QTensor(fake, 512, 128, 4, fake, fake, 1)
