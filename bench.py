@@ -33,7 +33,7 @@ PEAK_HBM_GBPS = 8000.0       # MI355X HBM3E
 # scaled by 2.000 and WRITE by 1.000, the factors a 1 GiB copy gives).  Valid only for the
 # backward sources it was measured on (sha256 prefix over attn_bwd.hip, device_common.h,
 # kernels.h); any other build reports null.
-BWD_TRAFFIC = {"workload": "long", "src": "ddac0e7b57dff6a8", "read_bytes": 20.011e9, "write_bytes": 13.078e9}
+BWD_TRAFFIC = {"workload": "long", "src": "13bed93f77bec2aa", "read_bytes": 38.695e9, "write_bytes": 13.084e9}
 
 
 def parse():
@@ -47,6 +47,8 @@ def parse():
                     help="time the non-causal variant (every key of a row's document visible)")
     ap.add_argument("--hadamard", action="store_true",
                     help="rotate Q and K by H / sqrt(d) in the quantiser, dQ and dK back in the backward")
+    ap.add_argument("--precise", action="store_true",
+                    help="time the precision options (per-token scales, folded exponents, row-wise dS exponents)")
     ap.add_argument("--store-gb", type=float, default=None,
                     help="cap the backward's dShat store at this many GiB (chunked backward); default: one chunk")
     ap.add_argument("--cpu-pairs", type=float, default=1.5e8,
@@ -132,6 +134,9 @@ def main():
     if args.non_causal and args.causal_dq:
         print("bench.py: the causal dQ prescale applies to causal attention only", file=sys.stderr)
         sys.exit(2)
+    if args.precise and (args.non_causal or args.hadamard):
+        print("bench.py: the precision options are timed alone on causal attention", file=sys.stderr)
+        sys.exit(2)
     if args.gpus != 1:
         print("bench.py measures one GPU: the path has no multi-GPU component (--gpus %d refused)" % args.gpus,
               file=sys.stderr)
@@ -167,7 +172,9 @@ def main():
         wl_ms.append(e0.elapsed_time(e1))
     # backward workspace: one key-tile chunk for this micro-batch's documents (sized from the
     # lengths the data loader holds on the host; --store-gb caps the store instead)
-    if args.store_gb is None:
+    if args.precise:  # nothing is stored: the smallest workspace
+        ws_bytes = fl.bwd_workspace_bytes(len(cu) - 1, T, Hq, d, 0)
+    elif args.store_gb is None:
         ws_bytes = fl.bwd_workspace_bytes_for(cu, T, Hq, d, causal)
     else:
         ws_bytes = fl.bwd_workspace_bytes(len(cu) - 1, T, Hq, d, int(args.store_gb * (1 << 30)))
@@ -177,14 +184,15 @@ def main():
 
     def step(evs=None):
         if evs: evs[0].record()
-        qz, kz, vz = fl.quantize([q, k, v], cu_d, hadamard=(args.hadamard, args.hadamard, False))
+        qz, kz, vz = fl.quantize([q, k, v], cu_d, hadamard=(args.hadamard, args.hadamard, False),
+                                 per_token=args.precise)
         if evs: evs[1].record()
-        o, lse = fl.fwd(qz, kz, vz, cu_d, lists.fwd, causal=causal)
+        o, lse = fl.fwd(qz, kz, vz, cu_d, lists.fwd, causal=causal, precise=args.precise)
         if evs: evs[2].record()
-        dc, dsc, D = fl.quantize_do(do, o, cu_d)
+        dc, dsc, D = fl.quantize_do(do, o, cu_d, per_token=args.precise)
         if evs: evs[3].record()
         out = fl.bwd(qz, kz, vz, (dc, dsc), lse, D, cu_d, lists, None, args.causal_dq, workspace=ws, causal=causal,
-                     hadamard=args.hadamard)
+                     hadamard=args.hadamard, precise=args.precise)
         if evs: evs[4].record()
         return out
 
@@ -222,11 +230,12 @@ def main():
     dom_flop = bwd_flop if dom == "bwd" else fwd_flop
     achieved = dom_flop / (stages[dom] * 1e-3) / 1e12
     traffic = None
-    if (dom == "bwd" and causal and not args.hadamard and args.workload == BWD_TRAFFIC["workload"]
+    if (dom == "bwd" and causal and not args.hadamard and not args.precise and args.workload == BWD_TRAFFIC["workload"]
             and bwd_source_hash() == BWD_TRAFFIC["src"]):
         traffic = BWD_TRAFFIC["read_bytes"] + BWD_TRAFFIC["write_bytes"]
     roofline = {"bound": "mfma",
-                "kernel": "flamia_bwd (bwd_prologue + bwd_kernel + dq_kernel)" if dom == "bwd" else "flamia_fwd",
+                "kernel": ("flamia_bwd (bwd_prologue + bwd_kernel + %s)" % ("dqp_kernel" if args.precise else "dq_kernel")
+                           if dom == "bwd" else "flamia_fwd"),
                 "achieved": achieved, "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_FP8_TFLOPS,
                 "traffic": traffic, "traffic_unit": "bytes per launch"}
     n_qkv = T * (Hq + 2 * Hkv) * d
@@ -243,7 +252,7 @@ def main():
         "vs_baseline": None, "dtype": "mxfp8_e4m3", "data": "synthetic",
         "config": {"workload": args.workload, "T": T, "Hq": Hq, "Hkv": Hkv, "d": d, "docs": len(cu) - 1,
                    "visible_pairs": pairs, "flop_per_step": flop, "causal_dq_scale": bool(args.causal_dq),
-                   "causal": causal, "hadamard": bool(args.hadamard)},
+                   "causal": causal, "hadamard": bool(args.hadamard), "precise": bool(args.precise)},
         "frac_of_peak": value / PEAK_FP8_TFLOPS,
         "roofline": roofline,
         "quantize": quant,
@@ -252,7 +261,7 @@ def main():
         "peak_mem_GB": torch.cuda.max_memory_allocated() / 1e9,
         "bwd_workspace_GB": ws_bytes / 1e9, "bwd_chunks": chunks,
     }
-    if not args.no_cpu_baseline and causal and not args.hadamard:
+    if not args.no_cpu_baseline and causal and not args.hadamard and not args.precise:
         res["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_pairs)
     print(json.dumps(res), flush=True)
 

@@ -290,15 +290,16 @@ class Lists:
 
 
 def training_call(q, k, v, do, cu_seqlens, lists=None, softmax_scale=None, causal_dq_scale=False, causal=True,
-                  hadamard=False):
+                  hadamard=False, precise=False):
     """One attention training call: quantise Q, K, V -> forward -> quantise dO (+ D) -> backward.
-    Returns dict with o, lse, dq, dk, dv."""
+    precise=True: the precision options (per-token scales in every quantiser pass, the precise
+    forward and backward).  Returns dict with o, lse, dq, dk, dv."""
     T = q.shape[0]
     if lists is None:
         lists = Lists(cu_seqlens, T, causal)
-    qz, kz, vz = quantize([q, k, v], cu_seqlens, hadamard=(hadamard, hadamard, False))
-    o, lse = fwd(qz, kz, vz, cu_seqlens, lists.fwd, softmax_scale, causal=causal)
-    dc, dsc, D = quantize_do(do, o, cu_seqlens)
+    qz, kz, vz = quantize([q, k, v], cu_seqlens, hadamard=(hadamard, hadamard, False), per_token=precise)
+    o, lse = fwd(qz, kz, vz, cu_seqlens, lists.fwd, softmax_scale, causal=causal, precise=precise)
+    dc, dsc, D = quantize_do(do, o, cu_seqlens, per_token=precise)
     dq, dk, dv = bwd(qz, kz, vz, (dc, dsc), lse, D, cu_seqlens, lists, softmax_scale, causal_dq_scale,
-                     causal=causal, hadamard=hadamard)
+                     causal=causal, hadamard=hadamard, precise=precise)
     return dict(o=o, lse=lse, dq=dq, dk=dk, dv=dv)
