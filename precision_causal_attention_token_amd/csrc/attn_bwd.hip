@@ -176,19 +176,19 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
   // this chunk's items: a contiguous range of the backward list
   const int u_lo = p.chunk_start[p.chunk], u_hi = p.chunk_start[p.chunk + 1];
   const int4* items = reinterpret_cast<const int4*>(p.list + 4) + u_lo;
-  const int n_units = (u_hi - u_lo) * p.Hkv;
-  const int G = gridDim.x, wg = blockIdx.x;
   const int grp = p.Hq / p.Hkv;
   const float c = p.c;
   const int T = p.T;
 
   // units (item, KV head) are taken dynamically: the list is sorted by descending cost, so the
-  // longest left go first to whichever workgroup is free
+  // longest left go first to whichever workgroup of the partition is free
+  const UnitPartition up = unit_partition(p.Hkv);
+  const int n_units = (u_hi - u_lo) * up.kv_per;
   __shared__ int unit_slot;
-  int32_t* const counter = p.counters + 2 * p.chunk;
-  for (int u = wg; u < n_units; u = next_unit(counter, &unit_slot)) {
-    const int4 it = items[u / p.Hkv];
-    const int g = u % p.Hkv;
+  int32_t* const counter = p.counters + 16 * p.chunk + up.part;
+  for (int u = up.rank; u < n_units; u = next_unit(counter, &unit_slot, up.first)) {
+    const int4 it = items[u / up.kv_per];
+    const int g = partition_kv(up, u % up.kv_per);
     // unit values are the same in every lane: kept in scalar registers (vector loads would
     // leave them in vector registers for the whole unit)
     const int doc = __builtin_amdgcn_readfirstlane(it.x), kappa = __builtin_amdgcn_readfirstlane(it.y);
@@ -775,9 +775,11 @@ __global__ __launch_bounds__(DQ_THREADS, 2) void dq_kernel(BwdParams p) {  // tw
   const int n_items = p.fwd_list[0];
   const int4* items = reinterpret_cast<const int4*>(p.fwd_list + 4);
   constexpr int PARTS = ITEM_Q / (QT * DQ_QT);  // workgroup units per work item and head
-  const int n_units = n_items * PARTS * p.Hq;
-  const int G = gridDim.x, wg = blockIdx.x;
   const int grp = p.Hq / p.Hkv;
+  // units (part of an item, query head) of the partition's KV heads, in list order
+  const UnitPartition up = unit_partition(p.Hkv);
+  const int hq_per = up.kv_per * grp;           // query heads per partition
+  const int n_units = n_items * PARTS * hq_per;
   const int t4 = wave >> 1, s = wave & 1;     // query tile of the unit, byte-position half
   const int qrow = ds_pos_query(32 * s + n);  // query offset in the tile held by this lane
   int lane_zero;                              // 0, opaque: keeps a load's result in vector registers
@@ -785,11 +787,12 @@ __global__ __launch_bounds__(DQ_THREADS, 2) void dq_kernel(BwdParams p) {  // tw
   const int qb_l = n >> 4;                    // its 32-query block
 
   __shared__ int unit_slot;
-  int32_t* const counter = p.counters + 2 * p.chunk + 1;
-  for (int u = wg; u < n_units; u = next_unit(counter, &unit_slot)) {  // dynamic, as in the key-tile pass
-    const int4 it = items[u / (PARTS * p.Hq)];
+  int32_t* const counter = p.counters + 16 * p.chunk + 8 + up.part;
+  for (int u = up.rank; u < n_units; u = next_unit(counter, &unit_slot, up.first)) {  // dynamic, as in the key-tile pass
+    const int4 it = items[u / (PARTS * hq_per)];
     if (it.z < 2) break;  // single key tile from here on (the list is sorted by cost)
-    const int h = u % p.Hq, g = h / grp, part = (u / p.Hq) % PARTS;
+    const int j = u % hq_per;
+    const int g = partition_kv(up, j / grp), h = g * grp + j % grp, part = (u / hq_per) % PARTS;
     const int doc = it.x, item = it.y;
     const int doc_start = p.cu[doc];
     const int L = p.cu[doc + 1] - doc_start;
@@ -1135,7 +1138,7 @@ __global__ __launch_bounds__(PRO_THREADS) void bwd_prologue(BwdParams p) {
   __shared__ Seg carry_sh;
 
   if ((int)blockIdx.x == p.Hq) {
-    for (int x = threadIdx.x; x < 2 * (p.max_chunks + 1); x += PRO_THREADS) p.counters[x] = 0;
+    for (int x = threadIdx.x; x < 16 * (p.max_chunks + 1); x += PRO_THREADS) p.counters[x] = 0;
     layout_chunks(p);
     return;
   }

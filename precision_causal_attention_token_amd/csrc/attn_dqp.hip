@@ -105,16 +105,19 @@ __global__ __launch_bounds__(DQP_THREADS, 2) void dqp_kernel(BwdParams p) {
   const int n_items = p.fwd_list[0];
   const int4* items = reinterpret_cast<const int4*>(p.fwd_list + 4);
   constexpr int PARTS = ITEM_Q / DQP_QU;
-  const int n_units = n_items * PARTS * p.Hq;
   const int grp = p.Hq / p.Hkv;
+  const UnitPartition up = unit_partition(p.Hkv);  // as in the key-tile pass
+  const int hq_per = up.kv_per * grp;
+  const int n_units = n_items * PARTS * hq_per;
   const float c = p.c;
   const int T = p.T;
 
   __shared__ int unit_slot;
-  int32_t* const counter = p.counters + 1;  // the dQ counter of the one chunk
-  for (int u = blockIdx.x; u < n_units; u = next_unit(counter, &unit_slot)) {
-    const int4 it = items[u / (PARTS * p.Hq)];
-    const int h = u % p.Hq, g = h / grp, part = (u / p.Hq) % PARTS;
+  int32_t* const counter = p.counters + 8 + up.part;  // the dQ counters of the one chunk
+  for (int u = up.rank; u < n_units; u = next_unit(counter, &unit_slot, up.first)) {
+    const int4 it = items[u / (PARTS * hq_per)];
+    const int j = u % hq_per;
+    const int g = partition_kv(up, j / grp), h = g * grp + j % grp, part = (u / hq_per) % PARTS;
     const int doc_start = p.cu[it.x];
     const int L = p.cu[it.x + 1] - doc_start;
     const int q0 = ITEM_Q * it.y + DQP_QU * part;

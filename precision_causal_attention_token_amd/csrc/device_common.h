@@ -54,16 +54,44 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-// Dynamic assignment of a persistent grid's units ([J] §3.4 "Work scheduling"): a workgroup
-// runs unit blockIdx.x first, then takes the next unit from an atomic counter (counted from
-// gridDim.x) when it has finished the current one, so no unit is reserved while its taker is
-// still busy.  Every thread of the workgroup calls this; the value is passed through LDS.
-__device__ __forceinline__ int next_unit(int32_t* counter, int* slot) {
-  if (threadIdx.x == 0) *slot = atomicAdd(counter, 1) + (int)gridDim.x;
+// Dynamic assignment of a persistent grid's units ([J] §3.4 "Work scheduling"): each of the
+// `first` workgroups that share a counter runs one of units 0 .. first - 1 first, then takes the
+// next unit from the atomic counter (counted from `first`) when it has finished the current one,
+// so no unit is reserved while its taker is still busy.  Every thread of the workgroup calls
+// this; the value is passed through LDS.
+__device__ __forceinline__ int next_unit(int32_t* counter, int* slot, int first) {
+  if (threadIdx.x == 0) *slot = atomicAdd(counter, 1) + first;
   lds_barrier();
   const int u = *slot;
   lds_barrier();  // every thread has read it before the next write
   return u;
+}
+
+// The unit partition of the backward's persistent grids.  Workgroups are dispatched to the
+// eight XCDs round robin (workgroup w on XCD w mod 8), and each XCD has an L2 of its own.  With
+// KV heads a multiple of 8 (and a grid of whole rounds), XCD x takes the units of the KV heads
+// g with g mod 8 = x, in list order, from a counter of its own: units of one head, which share
+// its K/V and Q/dO tiles, then meet in one L2.  Otherwise one counter serves the whole grid.
+struct UnitPartition {
+  int part;    // this workgroup's counter (its XCD, or 0)
+  int first;   // workgroups sharing the counter: the first unit index taken from it
+  int rank;    // this workgroup's first unit
+  int kv_per;  // KV heads per counter
+  bool by_xcd;
+};
+__device__ __forceinline__ UnitPartition unit_partition(int Hkv) {
+  const int G = gridDim.x, w = blockIdx.x;
+  UnitPartition u;
+  u.by_xcd = (Hkv & 7) == 0 && (G & 7) == 0;
+  u.part = u.by_xcd ? (w & 7) : 0;
+  u.first = u.by_xcd ? (G >> 3) : G;
+  u.rank = u.by_xcd ? (w >> 3) : w;
+  u.kv_per = u.by_xcd ? (Hkv >> 3) : Hkv;
+  return u;
+}
+// KV head of local index j (0 .. kv_per - 1) of partition `part`.
+__device__ __forceinline__ int partition_kv(const UnitPartition& u, int j) {
+  return u.by_xcd ? u.part + 8 * j : j;
 }
 
 // Accumulator row held by register i of lane group h.

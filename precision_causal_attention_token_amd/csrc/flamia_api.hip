@@ -76,7 +76,7 @@ BwdLayout bwd_layout(int32_t n_docs, int32_t T, int32_t Hq) {
   l.kv_off = off;      off += align256((size_t)n_tiles(n_docs, T) * 8);
   l.chunk_start = off; off += align256((size_t)n_chunk_entries(T) * 4);
   l.chunk_first = off; off += align256((size_t)n_chunk_entries(T) * 8);
-  l.counters = off;    off += align256((size_t)n_chunk_entries(T) * 8);
+  l.counters = off;    off += align256((size_t)n_chunk_entries(T) * 64);  // 16 int32 per chunk
   l.store = off;
   return l;
 }

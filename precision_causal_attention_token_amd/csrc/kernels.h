@@ -100,8 +100,9 @@ struct BwdParams {
   int32_t* kv_chunk;        // workspace: chunk of each (document, key tile), [tiles]
   int64_t* kv_off;          // workspace: its first dShat block within the chunk's store, [tiles]
   int32_t* chunk_start;     // workspace: first backward-list item of each chunk, [tiles + 2]
-  int32_t* counters;        // workspace: per chunk, the next unit of the key-tile and of the dQ
-                            // pass (dynamic assignment), [2 (tiles + 2)], zeroed by the prologue
+  int32_t* counters;        // workspace: per chunk 16 counters, the next unit of the key-tile (0..7)
+                            // and of the dQ pass (8..15), one per XCD partition (dynamic
+                            // assignment), [16 (tiles + 2)], zeroed by the prologue
   int64_t* chunk_first;     // workspace: block prefix of each chunk's first item, [tiles + 2]
   uint8_t* ds_store;        // workspace: dShat blocks of the current chunk, per (block, query head)
                             // 8 KiB of codes and 8 exponent bytes, 8320 bytes apart
