@@ -41,7 +41,11 @@ def lib():
         _lib.orc_e4m3_rne.restype = ctypes.c_uint8
         _lib.orc_e8m0_roundup.restype = ctypes.c_int
         _lib.orc_e8m0_floor.restype = ctypes.c_int
-        for f in ("orc_e4m3_rne", "orc_e8m0_roundup", "orc_e8m0_floor"):
+        _lib.orc_e2m1_decode.restype = ctypes.c_double
+        _lib.orc_e2m1_decode.argtypes = [ctypes.c_uint8]
+        _lib.orc_e2m1_rne.restype = ctypes.c_uint8
+        _lib.orc_e8m0_roundup4.restype = ctypes.c_int
+        for f in ("orc_e4m3_rne", "orc_e8m0_roundup", "orc_e8m0_floor", "orc_e2m1_rne", "orc_e8m0_roundup4"):
             getattr(_lib, f).argtypes = [ctypes.c_double]
         _lib.orc_worklist.restype = ctypes.c_int
         _lib.orc_num_threads.restype = ctypes.c_int
@@ -123,6 +127,37 @@ def quantize(x_bits, cu, floor_rule=False, hadamard=False, per_token=False):
     return codes, scales
 
 
+def e2m1_decode(c):
+    """Values of E2M1 codes (low nibble of each byte)."""
+    c = np.asarray(c, np.uint8)
+    return np.vectorize(lambda x: lib().orc_e2m1_decode(int(x) & 15), otypes=[np.float64])(c) if c.size else \
+        np.zeros(c.shape)
+
+
+def e2m1_rne(y):
+    """Nearest E2M1 codes (ties to even, signed zero kept, beyond 6 saturated)."""
+    y = np.asarray(y, np.float64)
+    return np.vectorize(lambda x: lib().orc_e2m1_rne(float(x)), otypes=[np.uint8])(y) if y.size else \
+        np.zeros(y.shape, np.uint8)
+
+
+def e8m0_roundup4(a):
+    """Smallest s with a <= 6 2^s (clamped to [-127, 127]; 0 gives -127)."""
+    return int(lib().orc_e8m0_roundup4(float(a)))
+
+
+def quantize_mx4(x_bits, cu, hadamard=False):
+    """The 4-bit copy (E2M1 codes, one E8M0 exponent per 32 channels of a token): returns
+    (codes [T,H,d/2] u8, even channel in the low nibble; scales [H,T,d/32] u8)."""
+    x = _c(x_bits, np.uint16)
+    T, H, d = x.shape
+    cu = _c(cu, np.int32)
+    codes = np.empty((T, H, d // 2), np.uint8)
+    scales = np.empty((H, T, d // 32), np.uint8)
+    lib().orc_quantize_mx4(_p(x), T, H, d, _p(cu), len(cu) - 1, int(bool(hadamard)), _p(codes), _p(scales))
+    return codes, scales
+
+
 def hadamard(x):
     """Rows of the last axis (FP32) times H / sqrt(d): FP32 butterflies, strides 1, 2, ..., d/2,
     then the FP32 multiply by RN32(1 / sqrt(d)).  Returns a new float32 array."""
@@ -158,7 +193,7 @@ class _Window(ctypes.Structure):
                 ("key_hi", ctypes.c_int), ("head_lo", ctypes.c_int), ("head_hi", ctypes.c_int),
                 ("fwd_s", ctypes.c_void_p), ("fwd_m", ctypes.c_void_p), ("fwd_p", ctypes.c_void_p),
                 ("bwd_dp", ctypes.c_void_p), ("bwd_p", ctypes.c_void_p), ("bwd_ps", ctypes.c_void_p),
-                ("bwd_ds", ctypes.c_void_p), ("bwd_dss", ctypes.c_void_p)]
+                ("bwd_ds", ctypes.c_void_p), ("bwd_dss", ctypes.c_void_p), ("fwd_ps", ctypes.c_void_p)]
 
 
 def window_shape(win):
@@ -193,7 +228,7 @@ def _sel(mask, n):
 
 
 def fwd(q, sq, k, sk, v, sv, cu, softmax_scale=None, p_shift=8, exact_p=False, want_o64=False,
-        docs=None, kv_heads=None, tail_rows=0, window=None, causal=True, precise=False):
+        docs=None, kv_heads=None, tail_rows=0, window=None, causal=True, precise=False, qk4=None):
     """causal=False: every key of the row's document is visible (key tiles from the document's
     last down to tile 0).  precise=True (with per-token operand scales): V's exponent is folded into
     the probability operand against the row's running maximum of visited V exponents.  Returns (O bits u16 [T,Hq,d], LSE f32 [Hq,T] in log2 units, O64 or None), plus (with
@@ -201,7 +236,12 @@ def fwd(q, sq, k, sk, v, sv, cu, softmax_scale=None, p_shift=8, exact_p=False, w
     a dict of the per-pair dumps fwd_s (score accumulator), fwd_m (running maximum), fwd_p
     (E4M3 codes), [heads][rows][keys], NaN / 0xFF where not visited.  ``docs`` / ``kv_heads``
     (index lists) restrict the work to those documents / KV heads, and tail_rows > 0 to the last
-    tail_rows rows of each document; other rows are zero (O) or NaN (LSE)."""
+    tail_rows rows of each document; other rows are zero (O) or NaN (LSE).
+    qk4 = (q4, sq4, k4, sk4), the 4-bit copies (quantize_mx4): 4-bit scores, and the probability
+    operand quantised per 32-key group in the log domain (the window then also dumps fwd_ps, the
+    group exponent byte of each code)."""
+    if qk4 is not None and precise:
+        raise ValueError("the 4-bit scores and the precision options are separate paths")
     q, k, v = _c(q, np.uint8), _c(k, np.uint8), _c(v, np.uint8)
     sq, sk, sv = _c(sq, np.uint8), _c(sk, np.uint8), _c(sv, np.uint8)
     T, Hq, d = q.shape
@@ -213,13 +253,15 @@ def fwd(q, sq, k, sk, v, sv, cu, softmax_scale=None, p_shift=8, exact_p=False, w
     lse = np.full((Hq, T), np.nan, np.float32)
     o64 = np.zeros((T, Hq, d), np.float64) if want_o64 else None
     sd, sk_ = _sel(docs, len(cu) - 1), _sel(kv_heads, Hkv)
-    dumps = _dump_arrays(window, ("fwd_s", "fwd_m", "fwd_p")) if window is not None else None
+    names = ("fwd_s", "fwd_m", "fwd_p") + (("fwd_ps",) if qk4 is not None else ())
+    dumps = _dump_arrays(window, names) if window is not None else None
     w = _window(window, dumps) if window is not None else None
+    q4 = [_c(a, np.uint8) for a in qk4] if qk4 is not None else None
     lib().orc_fwd(_p(q), _p(sq), _p(k), _p(sk), _p(v), _p(sv), T, Hq, Hkv, d, ctypes.c_double(softmax_scale),
                   _p(cu), len(cu) - 1, int(p_shift), int(bool(exact_p)), _p(o), _p(lse),
                   _p(o64) if o64 is not None else None, _p(sd) if sd is not None else None,
                   _p(sk_) if sk_ is not None else None, int(tail_rows), ctypes.byref(w) if w is not None else None,
-                  int(bool(causal)), int(bool(precise)))
+                  int(bool(causal)), int(bool(precise)), *(_p(a) for a in q4) if q4 else (None,) * 4)
     return (o, lse, o64) + ((dumps,) if window is not None else ())
 
 
@@ -254,7 +296,8 @@ class _Dbg(ctypes.Structure):
 
 
 def bwd(q, sq, k, sk, v, sv, do, sdo, lse, D, cu, softmax_scale=None, causal_dq=False, exact=0,
-        want64=False, debug=False, docs=None, kv_heads=None, tail_blocks=0, window=None, causal=True, precise=False):
+        want64=False, debug=False, docs=None, kv_heads=None, tail_blocks=0, window=None, causal=True, precise=False,
+        qk4=None):
     """Returns dict with dq, dk, dv (u16 BF16 bits), pi (i16 [Hq,T]) and optionally the
     double-precision values (dq64, dk64, dv64) and, for single-document calls, the block
     exponents/codes of the P and dS operands (p_scale, ds_scale [Hq,nb,nb]; p_code,
@@ -262,7 +305,10 @@ def bwd(q, sq, k, sk, v, sv, do, sdo, lse, D, cu, softmax_scale=None, causal_dq=
     blocks of each document: only those rows' dQ and those keys' dK, dV are complete.  With
     ``window`` (row/key/head bounds), out["dumps"] holds the per-pair bwd_dp (D - dP), bwd_p,
     bwd_ps (Phat code, block exponent byte), bwd_ds, bwd_dss (dShat), [heads][rows][keys].
-    causal=False: every key of the row's document is visible (default dQ prescale only)."""
+    causal=False: every key of the row's document is visible (default dQ prescale only).
+    qk4 = (q4, sq4, k4, sk4): the recomputed scores take these 4-bit copies (the forward's)."""
+    if qk4 is not None and precise:
+        raise ValueError("the 4-bit scores and the precision options are separate paths")
     if not causal and causal_dq:
         raise ValueError("the causal dQ prescale applies to causal attention")
     if precise and not causal:
@@ -300,14 +346,15 @@ def bwd(q, sq, k, sk, v, sv, do, sdo, lse, D, cu, softmax_scale=None, causal_dq=
                   _p(out["dv64"]) if want64 else None, ctypes.byref(dbg) if dbg is not None else None,
                   _p(sd) if sd is not None else None, _p(sk_) if sk_ is not None else None,
                   int(tail_blocks), ctypes.byref(w) if w is not None else None, int(bool(causal)),
-                  int(bool(precise)))
+                  int(bool(precise)), *((_p(_c(a, np.uint8)) for a in qk4) if qk4 is not None else (None,) * 4))
     return out
 
 
-def fwd_replay(v, sv, cu, window, S, M, P, Hq, c_scale, p_shift=8, causal=True, precise=False):
+def fwd_replay(v, sv, cu, window, S, M, P, Hq, c_scale, p_shift=8, causal=True, precise=False, PS=None):
     """Forward products from given per-pair decisions (score accumulator S, running maximum M,
-    codes P, [heads][rows][keys] over ``window``).  Returns (O64 [heads][rows][d], LSE64
-    [heads][rows]), NaN for rows not replayed.  c_scale = softmax_scale * log2(e) as used."""
+    codes P, [heads][rows][keys] over ``window``; PS, the 4-bit path's per-pair group exponent
+    bytes, else the fixed shift).  Returns (O64 [heads][rows][d], LSE64 [heads][rows]), NaN for
+    rows not replayed.  c_scale = softmax_scale * log2(e) as used."""
     v, sv = _c(v, np.uint8), _c(sv, np.uint8)
     T, Hkv, d = v.shape
     cu = _c(cu, np.int32)
@@ -319,7 +366,7 @@ def fwd_replay(v, sv, cu, window, S, M, P, Hq, c_scale, p_shift=8, causal=True, 
     w = _window(window, {})
     lib().orc_fwd_replay(_p(v), _p(sv), T, int(Hq), Hkv, d, ctypes.c_double(c_scale), _p(cu), len(cu) - 1,
                          int(p_shift), ctypes.byref(w), _p(S), _p(M), _p(P), _p(o64), _p(lse64), int(bool(causal)),
-                         int(bool(precise)))
+                         int(bool(precise)), _p(_c(PS, np.uint8)) if PS is not None else None)
     return o64, lse64
 
 

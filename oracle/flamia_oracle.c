@@ -221,6 +221,105 @@ void orc_quantize_per_token(const uint16_t* x, int T, int H, int d, const int32_
 }
 
 /* ------------------------------------------------------------------------------------
+ * 4-bit scores (jaehun.me §3.1 "Mixed NVFP4/FP8 path": Q and K stored in a 4-bit format for
+ * the score product and its backward recomputation only, one scale per group of head-dimension
+ * elements within each token; every other product stays 8-bit).  The pages' format is NVFP4
+ * (16-element groups, FP8 scales), an NVIDIA format; the reading taken here is its microscaling
+ * analogue, MXFP4: E2M1 codes (OCP: 1 sign, 2 exponent bits with bias 1, 1 mantissa bit;
+ * values 0, 0.5, 1, 1.5, 2, 3, 4, 6; no infinity or NaN) with one E8M0 exponent per 32
+ * consecutive head-dimension elements of one token.  A token's codes and exponents depend on
+ * that token alone, so this copy cannot leak across tokens (jaehun.me §3.2).  The exponent is
+ * rounded up as for E4M3 (smallest s with amax <= 6 2^s), so no element saturates.
+ * ---------------------------------------------------------------------------------- */
+#define E2M1_MAX 6.0
+
+void orc_hadamard(float* x, long n_rows, int d);
+
+double orc_e2m1_decode(uint8_t c) {
+  static const double mag[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+  double v = mag[c & 7];
+  return (c & 8) ? -v : v;
+}
+
+/* Nearest E2M1 value, ties to the even code (mantissa bit 0); the sign is kept for results
+ * that round to zero; magnitudes beyond 6 saturate to 6 (the round-up exponent never lets one
+ * occur). */
+uint8_t orc_e2m1_rne(double y) {
+  uint8_t sign = signbit(y) ? 8 : 0, best = 0;
+  double a = fabs(y), best_err = INFINITY;
+  int c;
+  if (a >= E2M1_MAX) return (uint8_t)(sign | 7);
+  for (c = 0; c < 8; ++c) {
+    double err = fabs(a - orc_e2m1_decode((uint8_t)c));
+    if (err < best_err || (err == best_err && (c & 1) == 0)) {
+      best_err = err;
+      best = (uint8_t)c;
+    }
+  }
+  return (uint8_t)(sign | best);
+}
+
+/* Smallest integer s with amax <= 6 * 2^s, clamped to [-127, 127]; amax = 0 gives -127. */
+int orc_e8m0_roundup4(double amax) {
+  int e, s;
+  if (amax == 0.0) return -127;
+  frexp(amax, &e);
+  s = e - 3;
+  while (amax > ldexp(E2M1_MAX, s)) s++;
+  while (amax <= ldexp(E2M1_MAX, s - 1)) s--;
+  if (s < -127) s = -127;
+  if (s > 127) s = 127;
+  return s;
+}
+
+/* The 4-bit copy of a tensor.  x: BF16 bit patterns [T][H][d]; for every token of a document
+ * and every head, each group of 32 consecutive channels gets exponent s (byte s + 127 at
+ * scales[h][t][group], d / 32 bytes per (head, token)) and codes E2M1_RNE(x 2^-s), two per byte,
+ * the even channel in the low nibble: codes[t][h][c / 2].  hadamard = 1 rotates each row first,
+ * exactly as orc_quantize_hadamard.  Tokens outside every document: codes 0, scale bytes 0. */
+void orc_quantize_mx4(const uint16_t* x, int T, int H, int d, const int32_t* cu, int n_docs, int hadamard,
+                      uint8_t* codes, uint8_t* scales) {
+  size_t n = (size_t)T * H * d, i;
+  const int ng = d / 32;
+  float* f = (float*)malloc((n ? n : 1) * sizeof(float));
+  int k, t, h, gi, c;
+  for (i = 0; i < n; ++i) f[i] = (float)orc_bf16_decode(x[i]);
+  if (hadamard) orc_hadamard(f, (long)T * H, d);
+  memset(codes, 0, n / 2);
+  memset(scales, 0, (size_t)H * T * ng);
+  for (k = 0; k < n_docs; ++k)
+    for (t = cu[k]; t < cu[k + 1]; ++t)
+      for (h = 0; h < H; ++h)
+        for (gi = 0; gi < ng; ++gi) {
+          const float* xs = f + ((size_t)t * H + h) * d + 32 * gi;
+          double amax = 0.0;
+          int s;
+          for (c = 0; c < 32; ++c)
+            if (fabs((double)xs[c]) > amax) amax = fabs((double)xs[c]);
+          s = orc_e8m0_roundup4(amax);
+          scales[((size_t)h * T + t) * ng + gi] = (uint8_t)(s + 127);
+          for (c = 0; c < 32; ++c) {
+            uint8_t code = orc_e2m1_rne(ldexp((double)xs[c], -s));
+            codes[(((size_t)t * H + h) * d + 32 * gi + c) / 2] |= (uint8_t)(code << (4 * (c & 1)));
+          }
+        }
+  free(f);
+}
+
+/* Decoded copy of a 4-bit tensor, [T][H][d] in double. */
+static double* deq4_all(const uint8_t* codes, const uint8_t* scales, int T, int H, int d) {
+  size_t n = (size_t)T * H * d, z;
+  const int ng = d / 32;
+  double* out = (double*)malloc(sizeof(double) * (n ? n : 1));
+  for (z = 0; z < n; ++z) {
+    int t = (int)(z / ((size_t)H * d)), h = (int)((z / d) % H), c = (int)(z % d);
+    uint8_t code = (uint8_t)((codes[z / 2] >> (4 * (z & 1))) & 15);
+    out[z] = ldexp(orc_e2m1_decode(code), (int)scales[((size_t)h * T + t) * ng + c / 32] - 127);
+  }
+  return out;
+}
+
+/* ------------------------------------------------------------------------------------
  * Hadamard rotation of the head dimension (jaehun.me §3.4 "Hadamard rotation", "Quantization
  * fusion"): each row x of d values becomes x H / sqrt(d), H the d x d Sylvester Hadamard
  * matrix (H_1 = [1], H_2n = [[H_n, H_n], [H_n, -H_n]]), which is symmetric and, normalised,
@@ -380,6 +479,7 @@ typedef struct {
   uint8_t* bwd_ps;
   uint8_t* bwd_ds; /* backward: dShat code and block exponent byte */
   uint8_t* bwd_dss;
+  uint8_t* fwd_ps; /* forward, 4-bit scores: exponent byte of the probability code's 32-key group */
 } orc_window;
 
 static long long win_index(const orc_window* w, int h, int row, int key) {
@@ -428,11 +528,14 @@ void orc_fwd(const uint8_t* q, const uint8_t* sq, const uint8_t* k, const uint8_
              const uint8_t* v, const uint8_t* sv, int T, int Hq, int Hkv, int d,
              double softmax_scale, const int32_t* cu, int n_docs, int p_shift, int exact_p,
              uint16_t* o, float* lse, double* o64, const uint8_t* sel_docs, const uint8_t* sel_kv,
-             int tail_rows, const orc_window* win, int causal, int precise) {
+             int tail_rows, const orc_window* win, int causal, int precise,
+             const uint8_t* q4, const uint8_t* sq4, const uint8_t* k4, const uint8_t* sk4) {
   const int group = Hq / Hkv;
   const double c_scale = softmax_scale * 1.4426950408889634074; /* log2(e) */
-  double* Qd = deq_all(q, sq, T, Hq, d);
-  double* Kd = deq_all(k, sk, T, Hkv, d);
+  /* 4-bit scores (q4 given): the score product takes the 4-bit copies of Q and K */
+  const int qk4 = q4 != NULL;
+  double* Qd = qk4 ? deq4_all(q4, sq4, T, Hq, d) : deq_all(q, sq, T, Hq, d);
+  double* Kd = qk4 ? deq4_all(k4, sk4, T, Hkv, d) : deq_all(k, sk, T, Hkv, d);
   double* Vd = deq_all(v, sv, T, Hkv, d);
   int* dm = doc_map(cu, n_docs, T);
   long long task, n_tasks = (long long)T * Hq;
@@ -475,18 +578,36 @@ void orc_fwd(const uint8_t* q, const uint8_t* sq, const uint8_t* k, const uint8_
         alpha = (m == -INFINITY) ? 0.0 : exp2(m - m_new);
         for (cc = 0; cc < d; ++cc) acc[cc] *= alpha;
         if (precise) vref = fold_ref(sv + (size_t)g * T + start, j0, j1, vref);
+        /* 4-bit scores: the probability operand is quantised in the log domain (jaehun.me §3.4
+         * "Softmax throughput"): one exponent per 32-key group of the tile (keys counted from the
+         * document start), the round-up exponent of the group's largest probability, found from
+         * the group's largest score before any exponential (max_j 2^x_j = 2^max_j x_j); its
+         * codes are E4M3(p 2^-e) with operand scale 2^e.  Reading taken: the group holds the
+         * row's visible keys of those 32. */
+        int e_grp[KV_TILE / 32];
+        if (qk4)
+          for (j = 0; j < KV_TILE / 32; ++j) {
+            int jj, g0 = j0 + 32 * j, g1 = g0 + 32 < j1 ? g0 + 32 : j1;
+            double gmax = -INFINITY;
+            for (jj = g0; jj < g1; ++jj)
+              if (t_tile[jj - j0] > gmax) gmax = t_tile[jj - j0];
+            e_grp[j] = g1 > g0 ? orc_e8m0_roundup(exp2(gmax - m_new)) : -127;
+          }
         for (j = j0; j < j1; ++j) {
           const double* vj = Vd + ((size_t)(start + j) * Hkv + g) * d;
           double p = exp2(t_tile[j - j0] - m_new);
           /* precise: V's exponent folded into the probability operand (relative to vref) */
           const int fold = precise ? (int)sv[(size_t)g * T + start + j] - 127 - vref : 0;
-          const uint8_t code = orc_e4m3_rne(ldexp(p, p_shift + fold));
-          double ph = exact_p ? p : ldexp(orc_e4m3_decode(code), -p_shift - fold);
+          /* the operand's exponent: -p_shift - fold, or the 4-bit path's group exponent */
+          const int pe = qk4 ? e_grp[(j - j0) / 32] : -p_shift - fold;
+          const uint8_t code = orc_e4m3_rne(ldexp(p, -pe));
+          double ph = exact_p ? p : ldexp(orc_e4m3_decode(code), pe);
           long long wi = win_index(win, hh, row, start + j);
           if (wi >= 0) {
             if (win->fwd_s) win->fwd_s[wi] = dot_tile[j - j0];
             if (win->fwd_m) win->fwd_m[wi] = m_new;
             if (win->fwd_p) win->fwd_p[wi] = code;
+            if (qk4 && win->fwd_ps) win->fwd_ps[wi] = (uint8_t)(pe + 127);
           }
           sum += p;
           for (cc = 0; cc < d; ++cc) acc[cc] += ph * vj[cc];
@@ -641,7 +762,8 @@ void orc_bwd(const uint8_t* q, const uint8_t* sq, const uint8_t* k, const uint8_
              uint16_t* dq, uint16_t* dk, uint16_t* dv, int16_t* pi_out,
              double* dq64, double* dk64, double* dv64, const orc_bwd_debug* dbg,
              const uint8_t* sel_docs, const uint8_t* sel_kv, int tail_blocks, const orc_window* win,
-             int causal, int precise) {
+             int causal, int precise,
+             const uint8_t* q4, const uint8_t* sq4, const uint8_t* k4, const uint8_t* sk4) {
   const int group = Hq / Hkv;
   const double c_scale = softmax_scale * 1.4426950408889634074;
   int16_t* pi = (int16_t*)malloc(sizeof(int16_t) * (size_t)Hq * T + 2);
@@ -651,6 +773,10 @@ void orc_bwd(const uint8_t* q, const uint8_t* sq, const uint8_t* k, const uint8_
   double* Kd = deq_all(k, sk, T, Hkv, d);
   double* Vd = deq_all(v, sv, T, Hkv, d);
   double* dOd = deq_all(dO, sdo, T, Hq, d);
+  /* 4-bit scores: the recomputed score takes the forward's 4-bit copies; dK and dQ keep the
+   * 8-bit ones */
+  double* Qs = q4 ? deq4_all(q4, sq4, T, Hq, d) : Qd;
+  double* Ks = q4 ? deq4_all(k4, sk4, T, Hkv, d) : Kd;
   orc_dq_exponents(sk, sv, sdo, T, Hq, Hkv, d, cu, n_docs, precise ? 2 : causal_dq, pi);
   if (pi_out) memcpy(pi_out, pi, sizeof(int16_t) * (size_t)Hq * T);
   for (z = 0; z < n_q; ++z) { dq[z] = 0; if (dq64) dq64[z] = 0.0; }
@@ -692,9 +818,9 @@ void orc_bwd(const uint8_t* q, const uint8_t* sq, const uint8_t* k, const uint8_
               for (jj = j0; jj < j1; ++jj) {
                 double dot = 0.0, dp = 0.0, p;
                 if (causal && jj > ii) { P[ii - i0][jj - j0] = 0.0; dS[ii - i0][jj - j0] = 0.0; continue; }
-                const double* qi = Qd + ((size_t)(start + ii) * Hq + hq) * d;
+                const double* qi = Qs + ((size_t)(start + ii) * Hq + hq) * d;
                 const double* doi = dOd + ((size_t)(start + ii) * Hq + hq) * d;
-                const double* kj = Kd + ((size_t)(start + jj) * Hkv + g) * d;
+                const double* kj = Ks + ((size_t)(start + jj) * Hkv + g) * d;
                 const double* vj = Vd + ((size_t)(start + jj) * Hkv + g) * d;
                 for (cc = 0; cc < d; ++cc) {
                   dot += qi[cc] * kj[cc];
@@ -817,6 +943,8 @@ void orc_bwd(const uint8_t* q, const uint8_t* sq, const uint8_t* k, const uint8_
     free(dv_acc);
   }
   free(pi);
+  if (Qs != Qd) free(Qs);
+  if (Ks != Kd) free(Ks);
   free(Qd); free(Kd); free(Vd); free(dOd);
 }
 
@@ -837,7 +965,8 @@ void orc_bwd(const uint8_t* q, const uint8_t* sq, const uint8_t* k, const uint8_
  * ---------------------------------------------------------------------------------- */
 void orc_fwd_replay(const uint8_t* v, const uint8_t* sv, int T, int Hq, int Hkv, int d, double c_scale,
                     const int32_t* cu, int n_docs, int p_shift, const orc_window* win, const double* S,
-                    const double* M, const uint8_t* P, double* o64, double* lse64, int causal, int precise) {
+                    const double* M, const uint8_t* P, double* o64, double* lse64, int causal, int precise,
+                    const uint8_t* PS) {
   const int group = Hq / Hkv;
   const int nh = win->head_hi - win->head_lo, nr = win->row_hi - win->row_lo;
   double* Vd = deq_all(v, sv, T, Hkv, d);
@@ -869,7 +998,8 @@ void orc_fwd_replay(const uint8_t* v, const uint8_t* sv, int T, int Hq, int Hkv,
           long long wi = win_index(win, hh, row, start + j);
           const double* vj = Vd + ((size_t)(start + j) * Hkv + g) * d;
           const int fold = precise ? (int)sv[(size_t)g * T + start + j] - 127 - vref : 0;
-          double ph = ldexp(orc_e4m3_decode(P[wi]), -p_shift - fold);
+          /* PS (4-bit scores): the code's group exponent byte */
+          double ph = ldexp(orc_e4m3_decode(P[wi]), PS ? (int)PS[wi] - 127 : -p_shift - fold);
           sum += exp2(S[wi] * c_scale - m_new);
           for (cc = 0; cc < d; ++cc) acc[cc] += ph * vj[cc];
         }
