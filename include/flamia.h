@@ -124,6 +124,15 @@ flamia_status flamia_build_worklist(const int32_t* cu_seqlens, int32_t n_docs, i
  * Per-token scales ([J] §3.2, the precision options): with per_token = 1 every token of a
  * document is its own block, so its exponent and codes depend on that token alone (also for the
  * dO pass).
+ *
+ * 4-bit copy for the scores ([J] §3.1 "Mixed NVFP4/FP8 path", as MXFP4, the microscaling
+ * analogue of the pages' NVFP4): with mx4_codes / mx4_scales given, the same pass also writes
+ * E2M1 codes (values 0, 0.5, 1, 1.5, 2, 3, 4, 6; round to nearest even, the sign kept on zero)
+ * with one round-up E8M0 exponent per 32 consecutive channels of one token (smallest s with
+ * amax <= 6 2^s, amax over the FP32 values the 8-bit codes are taken from, rotated when
+ * hadamard = 1).  It feeds only the score product (flamia_fwd_args.q4/k4 and the backward's
+ * recomputation); each token's copy depends on that token alone.  Rows outside every document:
+ * codes and exponent bytes 0.
  * ------------------------------------------------------------------------------------------ */
 typedef struct {
   const void* x;              /* bf16 [T, H, d], element strides below, d contiguous */
@@ -134,10 +143,15 @@ typedef struct {
   int32_t hadamard;           /* 1: rotate each row by H / sqrt(d) first (Q and K); 0: plain */
   int32_t per_token;          /* 1: one exponent per token (blocks of one token; the precision
                                  options, with flamia_fwd_args.precise / flamia_bwd_args.precise) */
+  uint8_t* mx4_codes;         /* optional out (both or neither): the 4-bit copy for the score
+                                 product, E2M1 codes u8 [T, H, d/2], two per byte, the even
+                                 channel in the low nibble, 4-byte aligned */
+  uint8_t* mx4_scales;        /* optional out: its exponents u8 [H, T, d/32] */
 } flamia_qtensor;
 
 /* Errors: NULL pointers, n_tensors not in [1, 3] (1 with `o`), H < 1, T < 0 or > FLAMIA_MAX_T,
- * d not in {64, 128}, n_docs < 0, D NULL when o is given, hadamard with o (UNSUPPORTED). */
+ * d not in {64, 128}, n_docs < 0, D NULL when o is given, hadamard or a 4-bit copy with o
+ * (UNSUPPORTED), only one of mx4_codes / mx4_scales (NULL). */
 flamia_status flamia_quantize(const flamia_qtensor* tensors, int32_t n_tensors, int32_t T, int32_t d,
                               const int32_t* cu_seqlens, int32_t n_docs, const void* o, int64_t o_stride_t,
                               int64_t o_stride_h, float* D, void* stream);
@@ -178,6 +192,17 @@ typedef struct {
                                      has visited so far (at least -119), and V enters P V with its
                                      bare codes, so no later token changes row i.  Causal only
                                      (non_causal = 1 is FLAMIA_ERR_UNSUPPORTED). */
+  const uint8_t *q4, *sq4;        /* optional (all four or none): 4-bit scores ([J] §3.1 "Mixed
+                                     NVFP4/FP8 path", §3.4 "Softmax throughput"): the score
+                                     product takes these E2M1 copies from flamia_quantize (codes
+                                     [T, H, d/2], 16-byte aligned; exponents [H, T, d/32],
+                                     4-byte aligned) instead of q, k, and the P operand is
+                                     quantised in the log domain: per row and tile, each 32-key
+                                     group gets the round-up E8M0 exponent e of its largest p
+                                     (taken from its largest score) and codes E4M3_RNE(p 2^-e)
+                                     with operand scale 2^e; l sums the unrounded p.  Not with
+                                     precise (FLAMIA_ERR_UNSUPPORTED). */
+  const uint8_t *k4, *sk4;
 } flamia_fwd_args;
 
 /* Errors: NULL pointers, sizes, d, head ratio. */
@@ -264,6 +289,10 @@ typedef struct {
                                          query-stationary pass that recomputes S, dP and dS';
                                          nothing is stored, so the call runs as one chunk in
                                          any workspace the default accepts. */
+  const uint8_t *q4, *sq4, *k4, *sk4; /* optional (all four or none, as given to the forward):
+                                         the recomputed scores take these 4-bit copies, bit for
+                                         bit the forward's; dK, dQ keep the 8-bit q, k.  Not with
+                                         precise (FLAMIA_ERR_UNSUPPORTED). */
 } flamia_bwd_args;
 
 /* Host.  Backward workspace for n_docs documents of total length T: a header, pi [Hq, T], the

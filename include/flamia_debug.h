@@ -48,6 +48,8 @@ typedef struct {
   float* dq_dp;     /* dP_ij - D_i as it formed it */
   uint8_t* dq_ds;   /* E4M3 code of dS_ij 2^e(K_j) (the dQ operand) */
   uint8_t* dq_dss;  /* its exponent byte, one per (row, 32-key block) */
+  uint8_t* fwd_ps;  /* forward with 4-bit scores: exponent byte of the probability code's 32-key
+                       group (the log-domain operand scale) */
 } flamia_debug_dump;
 
 /* Host.  Set the dump buffers used by every later flamia_fwd / flamia_bwd of this process (the

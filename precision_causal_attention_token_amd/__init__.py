@@ -36,7 +36,8 @@ DEFAULT_STORE_BYTES = 4 << 30
 class _QTensor(ctypes.Structure):
     _fields_ = [("x", ctypes.c_void_p), ("stride_t", ctypes.c_int64), ("stride_h", ctypes.c_int64),
                 ("H", ctypes.c_int32), ("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
-                ("hadamard", ctypes.c_int32), ("per_token", ctypes.c_int32)]
+                ("hadamard", ctypes.c_int32), ("per_token", ctypes.c_int32),
+                ("mx4_codes", ctypes.c_void_p), ("mx4_scales", ctypes.c_void_p)]
 
 
 class _FwdArgs(ctypes.Structure):
@@ -46,7 +47,8 @@ class _FwdArgs(ctypes.Structure):
                 ("softmax_scale", ctypes.c_float), ("cu_seqlens", ctypes.c_void_p), ("n_docs", ctypes.c_int32),
                 ("fwd_list", ctypes.c_void_p), ("o", ctypes.c_void_p), ("o_stride_t", ctypes.c_int64),
                 ("o_stride_h", ctypes.c_int64), ("lse", ctypes.c_void_p), ("non_causal", ctypes.c_int32),
-                ("precise", ctypes.c_int32)]
+                ("precise", ctypes.c_int32), ("q4", ctypes.c_void_p), ("sq4", ctypes.c_void_p),
+                ("k4", ctypes.c_void_p), ("sk4", ctypes.c_void_p)]
 
 
 class _BwdArgs(ctypes.Structure):
@@ -62,7 +64,8 @@ class _BwdArgs(ctypes.Structure):
                 ("dv_stride_t", ctypes.c_int64), ("dv_stride_h", ctypes.c_int64),
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
                 ("causal_dq_scale", ctypes.c_int32), ("dq_exp_out", ctypes.c_void_p),
-                ("non_causal", ctypes.c_int32), ("hadamard", ctypes.c_int32), ("precise", ctypes.c_int32)]
+                ("non_causal", ctypes.c_int32), ("hadamard", ctypes.c_int32), ("precise", ctypes.c_int32),
+                ("q4", ctypes.c_void_p), ("sq4", ctypes.c_void_p), ("k4", ctypes.c_void_p), ("sk4", ctypes.c_void_p)]
 
 
 _lib = None
@@ -158,11 +161,13 @@ def worklist_items(buf):
     return n, buf[4:4 + 4 * n].view(n, 4)
 
 
-def quantize(xs, cu_seqlens, hadamard=False, per_token=False):
+def quantize(xs, cu_seqlens, hadamard=False, per_token=False, mx4=False):
     """Token-block MXFP8 quantisation of up to three BF16 tensors [T, H, d] in one launch.
     hadamard: a bool for every tensor or one per tensor (rows rotated by H / sqrt(d) first; Q
-    and K of a training call); per_token: one exponent per token (the precision options).
-    Returns a list of (codes u8 [T, H, d], scales u8 [H, T])."""
+    and K of a training call); per_token: one exponent per token (the precision options);
+    mx4: a bool for every tensor or one per tensor, also write the 4-bit copy for the scores.
+    Returns a list of (codes u8 [T, H, d], scales u8 [H, T]), with mx4 followed by the 4-bit
+    copy (codes u8 [T, H, d/2], scales u8 [H, T, d/32]) in each tensor's tuple."""
     lib = load_library()
     n_docs = _check_cu(cu_seqlens)
     T, _, d = xs[0].shape
@@ -171,6 +176,9 @@ def quantize(xs, cu_seqlens, hadamard=False, per_token=False):
     rot = [bool(hadamard)] * len(xs) if isinstance(hadamard, bool) else [bool(r) for r in hadamard]
     if len(rot) != len(xs):
         raise ValueError("one hadamard flag per tensor")
+    four = [bool(mx4)] * len(xs) if isinstance(mx4, bool) else [bool(r) for r in mx4]
+    if len(four) != len(xs):
+        raise ValueError("one mx4 flag per tensor")
     for i, x in enumerate(xs):
         _check_bf16(x, "x")
         if x.shape[0] != T or x.shape[2] != d:
@@ -178,9 +186,14 @@ def quantize(xs, cu_seqlens, hadamard=False, per_token=False):
         H = x.shape[1]
         codes = torch.empty((T, H, d), dtype=torch.uint8, device=x.device)
         scales = torch.empty((H, T), dtype=torch.uint8, device=x.device)
+        c4 = s4 = None
+        if four[i]:
+            c4 = torch.empty((T, H, d // 2), dtype=torch.uint8, device=x.device)
+            s4 = torch.empty((H, T, d // 32), dtype=torch.uint8, device=x.device)
         arr[i] = _QTensor(x.data_ptr(), x.stride(0), x.stride(1), H, codes.data_ptr(), scales.data_ptr(), int(rot[i]),
-                          int(bool(per_token)))
-        outs.append((codes, scales))
+                          int(bool(per_token)), c4.data_ptr() if four[i] else None,
+                          s4.data_ptr() if four[i] else None)
+        outs.append((codes, scales, c4, s4) if four[i] else (codes, scales))
     _check(lib.flamia_quantize(arr, len(xs), T, d, _ptr(cu_seqlens), n_docs, None, 0, 0, None, _stream()))
     return outs
 
@@ -204,19 +217,22 @@ def quantize_do(do, o, cu_seqlens, per_token=False):
     return codes, scales, D
 
 
-def fwd(q, k, v, cu_seqlens, fwd_list, softmax_scale=None, out=None, causal=True, precise=False):
+def fwd(q, k, v, cu_seqlens, fwd_list, softmax_scale=None, out=None, causal=True, precise=False, qk4=False):
     """Forward on quantised operands.  q, k, v are (codes, scales) pairs; causal=False lets every
-    row see every key of its document.  Returns (O bf16 [T, Hq, d], LSE f32 [Hq, T] in log2 units)."""
+    row see every key of its document.  qk4=True: q and k are quantize(..., mx4=True) tuples and
+    the scores take their 4-bit copies (log-domain probability operand).  Returns (O bf16
+    [T, Hq, d], LSE f32 [Hq, T] in log2 units)."""
     lib = load_library()
     n_docs = _check_cu(cu_seqlens)
-    (qc, qs), (kc, ks), (vc, vs) = q, k, v
+    four = (q[2].data_ptr(), q[3].data_ptr(), k[2].data_ptr(), k[3].data_ptr()) if qk4 else (None,) * 4
+    (qc, qs), (kc, ks), (vc, vs) = q[:2], k[:2], v
     T, Hq, d = qc.shape
     Hkv = kc.shape[1]
     o = out if out is not None else torch.empty((T, Hq, d), dtype=torch.bfloat16, device=qc.device)
     lse = torch.empty((Hq, T), dtype=torch.float32, device=qc.device)
     a = _FwdArgs(qc.data_ptr(), kc.data_ptr(), vc.data_ptr(), qs.data_ptr(), ks.data_ptr(), vs.data_ptr(),
                  T, Hq, Hkv, d, float(softmax_scale or 0.0), cu_seqlens.data_ptr(), n_docs, fwd_list.data_ptr(),
-                 o.data_ptr(), o.stride(0), o.stride(1), lse.data_ptr(), int(not causal), int(bool(precise)))
+                 o.data_ptr(), o.stride(0), o.stride(1), lse.data_ptr(), int(not causal), int(bool(precise)), *four)
     _check(lib.flamia_fwd(ctypes.byref(a), _stream()))
     return o, lse
 
@@ -239,7 +255,7 @@ def bwd_workspace_bytes_for(cu_seqlens_host, T, Hq, d, causal=True):
 
 
 def bwd(q, k, v, do, lse, D, cu_seqlens, lists, softmax_scale=None, causal_dq_scale=False, want_pi=False,
-        workspace=None, static_scratch=False, causal=True, hadamard=False, precise=False):
+        workspace=None, static_scratch=False, causal=True, hadamard=False, precise=False, qk4=False):
     """Backward on quantised operands.  q, k, v, do are (codes, scales) pairs; lse, D f32 [Hq, T];
     lists: the micro-batch's Lists.  workspace: a uint8 CUDA tensor of at least
     bwd_workspace_bytes(n_docs, T, Hq, d, 0) bytes, or None to allocate one with the default
@@ -247,10 +263,12 @@ def bwd(q, k, v, do, lse, D, cu_seqlens, lists, softmax_scale=None, causal_dq_sc
     static_scratch=True calls flamia_bwd_static instead (the library's static device scratch; no
     workspace is allocated or passed).
     hadamard=True: Q and K were quantised rotated; dq and dk are rotated back.
+    qk4=True: q and k are quantize(..., mx4=True) tuples; the scores take their 4-bit copies.
     Returns (dq, dk, dv) BF16, plus the prescale exponents pi int16 [Hq, T] if want_pi."""
     lib = load_library()
     n_docs = _check_cu(cu_seqlens)
-    (qc, qs), (kc, ks), (vc, vs), (dc, dsc) = q, k, v, do
+    four = (q[2].data_ptr(), q[3].data_ptr(), k[2].data_ptr(), k[3].data_ptr()) if qk4 else (None,) * 4
+    (qc, qs), (kc, ks), (vc, vs), (dc, dsc) = q[:2], k[:2], v, do
     T, Hq, d = qc.shape
     Hkv = kc.shape[1]
     dev = qc.device
@@ -268,7 +286,7 @@ def bwd(q, k, v, do, lse, D, cu_seqlens, lists, softmax_scale=None, causal_dq_sc
                  dv.stride(0), dv.stride(1), workspace.data_ptr() if workspace is not None else None,
                  workspace.numel() if workspace is not None else 0, int(bool(causal_dq_scale)),
                  pi.data_ptr() if pi is not None else None, int(not causal), int(bool(hadamard)),
-                 int(bool(precise)))
+                 int(bool(precise)), *four)
     _check((lib.flamia_bwd_static if static_scratch else lib.flamia_bwd)(ctypes.byref(a), _stream()))
     return (dq, dk, dv, pi) if want_pi else (dq, dk, dv)
 

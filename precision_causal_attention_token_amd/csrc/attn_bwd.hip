@@ -78,10 +78,16 @@ struct BwdSmem {
   float dd[NBUF][QT];
   int2 sqdo[NBUF][2];           // block scale bytes {Q, dO} of the step's two query blocks
   int xs_p[2][2][4], xs_d[2][2][4];  // block exponent bytes of (query block, key group)
-  // per-token scales (the precision options), per step row: Q's exponent byte and 2^e(dO_i);
-  // dd then holds D_i 2^(e(Q_i) - e(dO_i))
-  uint8_t sqr[NBUF][QT];
-  alignas(16) float pf[NBUF][QT];
+  uint8_t q4[3][QT * D / 2];   // 4-bit scores: the step's 4-bit Q rows (step s in buffer s % 3)
+  union {
+    // per-token scales (the precision options), per step row: Q's exponent byte and 2^e(dO_i);
+    // dd then holds D_i 2^(e(Q_i) - e(dO_i))
+    struct {
+      uint8_t sqr[NBUF][QT];
+      alignas(16) float pf[NBUF][QT];
+    } pr;
+    uint8_t sq4[3][QT * D / 32];  // 4-bit scores: each step row's d/32 exponent bytes
+  } rt;
 };
 
 // Step tiles go from global memory straight into LDS (16-byte direct loads: lane l of a wave
@@ -90,9 +96,9 @@ struct BwdSmem {
 // under the tile's swizzle.  Rows past the document end repeat its last row, and 1 KiB blocks
 // wholly past it are zero-filled instead of loaded: every use of those rows is masked to zero,
 // and the values are finite.
-template <int D, bool PRECISE>
+template <int D, bool PRECISE, bool QK4>
 __device__ __forceinline__ void issue_step_loads(const BwdParams& p, BwdSmem<D>& sm, int b, int doc_start, int L,
-                                                 int h, int qt, int cw, int lane) {
+                                                 int h, int qt, int cw, int lane, int b3) {
   constexpr int CPR = D / 16;                    // 16-byte chunks per row
   constexpr int BLOCKS = QT * D / 1024;          // 1 KiB wave blocks per tile (4 or 8)
   constexpr int PER_WAVE = 2 * BLOCKS / 4;       // Q and dO blocks per consumer wave
@@ -132,6 +138,21 @@ __device__ __forceinline__ void issue_step_loads(const BwdParams& p, BwdSmem<D>&
     }
   }
   }
+  if constexpr (QK4) {
+    // the 4-bit Q rows (d/2 bytes each) into buffer b3: one 1 KiB block per consumer wave
+    constexpr int K4B = D / 2, BQ = QT * K4B / 1024, CPR = K4B / 16;
+    if (cw < BQ) {
+      const int pos = cw * 64 + lane, row = pos / CPR;
+      const int lc = (pos % CPR) ^ lds_swizzle<K4B>(row);
+      uint8_t* dst = sm.q4[b3] + cw * 1024;
+      if (QT * qt + cw * (1024 / K4B) < L) {
+        const int qr = min(QT * qt + row, L - 1);
+        dma_load16(p.q4 + ((int64_t)(doc_start + qr) * p.Hq + h) * K4B + 16 * lc, lds_addr(dst));
+      } else {
+        *reinterpret_cast<uint4*>(dst + 16 * lane) = make_uint4(0, 0, 0, 0);
+      }
+    }
+  }
   if (cw == 0 || (cw == 1 && !PRECISE)) {  // row statistics: one float per lane (D: PRECISE, rescaled first)
     const int qr = min(q0 + lane, L - 1);
     const float* src = (cw == 0 ? p.lse : p.Dv) + (int64_t)h * p.T + doc_start + qr;
@@ -159,9 +180,13 @@ __device__ __forceinline__ void issue_step_loads(const BwdParams& p, BwdSmem<D>&
 // comes out as (D - dP) 2^(e(Q_i) - e(dO_i)) from dO's products taken with Q's exponent and an
 // accumulator started at D 2^(e(Q_i) - e(dO_i)), and P is multiplied by 2^e(dO_i) after the
 // exponential, so their product is dS''.
-template <int D, bool CAUSAL, bool PRECISE>
+// QK4 (4-bit scores): S is recomputed from the forward's E2M1 copies of Q (step tiles) and K
+// (operand registers), their exponent bytes per 32 channels as the instruction's scales; every
+// other product keeps the 8-bit operands.
+template <int D, bool CAUSAL, bool PRECISE, bool QK4>
 __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
   static_assert(CAUSAL || !PRECISE, "the precision options are causal");
+  static_assert(!(PRECISE && QK4), "separate paths");
   constexpr int NC = D / 64;
   constexpr int NDB = D / 32;
   __shared__ BwdSmem<D> sm;
@@ -221,7 +246,14 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
     // into registers and store them to LDS at the end of the phase.  PRECISE: consumer 1 loads
     // the per-token exponents and D of the step's 64 rows (one per lane; rows past the document
     // end repeat its last row) and stores the row tables
-    auto scale_loads = [&](int h, int qt, int& rsq, int& rsdo, float& rd) {
+    auto scale_loads = [&](int h, int qt, int& rsq, int& rsdo, float& rd, uint32_t& rq4) {
+      if constexpr (QK4) {
+        if (cw == 3) {  // the 4-bit Q exponent bytes of the step's rows, one row per lane
+          const int qr = min(QT * qt + lane, L - 1);
+          const uint8_t* e4 = p.sq4 + ((int64_t)h * T + doc_start + qr) * (D / 32);
+          rq4 = D == 128 ? *reinterpret_cast<const uint32_t*>(e4) : (uint32_t)*reinterpret_cast<const uint16_t*>(e4);
+        }
+      }
       if constexpr (PRECISE) {
         if (cw == 1) {
           const int qr = min(QT * qt + lane, L - 1);
@@ -237,11 +269,17 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
         rsdo = p.sdo[ti];
       }
     };
-    auto scale_store = [&](int b, int qt, int rsq, int rsdo, float rd) {
+    auto scale_store = [&](int b, int b3, int qt, int rsq, int rsdo, float rd, uint32_t rq4) {
+      if constexpr (QK4) {
+        if (cw == 3) {
+          if constexpr (D == 128) *reinterpret_cast<uint32_t*>(&sm.rt.sq4[b3][4 * lane]) = rq4;
+          else *reinterpret_cast<uint16_t*>(&sm.rt.sq4[b3][2 * lane]) = (uint16_t)rq4;
+        }
+      }
       if constexpr (PRECISE) {
         if (cw == 1) {
-          sm.sqr[b][lane] = (uint8_t)rsq;
-          sm.pf[b][lane] = __builtin_ldexpf(1.0f, rsdo - 127);
+          sm.rt.pr.sqr[b][lane] = (uint8_t)rsq;
+          sm.rt.pr.pf[b][lane] = __builtin_ldexpf(1.0f, rsdo - 127);
           sm.dd[b][lane] = __builtin_ldexpf(rd, rsq - rsdo);
         }
       } else if (cw == 2 && lane < 2) {
@@ -259,14 +297,15 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
     };
     int rsq = 127, rsdo = 127, rsq1 = 127, rsdo1 = 127;
     float rd = 0.f, rd1 = 0.f;
+    uint32_t rq4 = 0x7F7F7F7Fu, rq41 = 0x7F7F7F7Fu;
     if (!producer) {
-      issue_step_loads<D, PRECISE>(p, sm, 0, doc_start, L, g * grp, qt_first, cw, lane);
-      scale_loads(g * grp, qt_first, rsq, rsdo, rd);
+      issue_step_loads<D, PRECISE, QK4>(p, sm, 0, doc_start, L, g * grp, qt_first, cw, lane, 0);
+      scale_loads(g * grp, qt_first, rsq, rsdo, rd, rq4);
       if (n_steps > 1) {
         int h1;
         const int qt1 = step_qt(1, h1);
-        issue_step_loads<D, PRECISE>(p, sm, 1, doc_start, L, h1, qt1, cw, lane);
-        scale_loads(h1, qt1, rsq1, rsdo1, rd1);
+        issue_step_loads<D, PRECISE, QK4>(p, sm, 1, doc_start, L, h1, qt1, cw, lane, 1);
+        scale_loads(h1, qt1, rsq1, rsdo1, rd1, rq41);
       }
     }
     {
@@ -296,10 +335,10 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
     }
     if (!producer) {
       __builtin_amdgcn_s_waitcnt(0);  // the direct loads have landed
-      scale_store(0, qt_first, rsq, rsdo, rd);
+      scale_store(0, 0, qt_first, rsq, rsdo, rd, rq4);
       if (n_steps > 1) {
         int h1;
-        scale_store(1, step_qt(1, h1), rsq1, rsdo1, rd1);
+        scale_store(1, 1, step_qt(1, h1), rsq1, rsdo1, rd1, rq41);
       }
     }
     lds_barrier();
@@ -320,8 +359,23 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
       v8i kreg[NC], vreg[NC];
 #pragma unroll
       for (int cc = 0; cc < NC; ++cc) {
-        kreg[cc] = lds_read_row32<D>(sm.k, 32 * kw + n, 64 * cc + 32 * hh);
+        if constexpr (!QK4) kreg[cc] = lds_read_row32<D>(sm.k, 32 * kw + n, 64 * cc + 32 * hh);
         vreg[cc] = lds_read_row32<D>(sm.v, 32 * kw + n, 64 * cc + 32 * hh);
+      }
+      // QK4: the key's 4-bit row (16 bytes per chunk) and its exponent byte per 32 channels
+      v4i kreg4[NC];
+      int ks4[NC];
+      if constexpr (QK4) {
+#pragma unroll
+        for (int cc = 0; cc < NC; ++cc) {
+          kreg4[cc] = v4i{0, 0, 0, 0};
+          ks4[cc] = 127;
+          if (key_rel < L) {
+            const int64_t kt = (int64_t)doc_start + key_rel;
+            kreg4[cc] = *reinterpret_cast<const v4i*>(p.k4 + (kt * p.Hkv + g) * (D / 2) + 32 * cc + 16 * hh);
+            ks4[cc] = p.sk4[((int64_t)g * T + kt) * (D / 32) + 2 * cc + hh];
+          }
+        }
       }
       // S and D - dP of query block qb of step st (tiles in buffer st % 4).  The dP accumulator
       // starts at D of its rows: accumulator register 4 j + e holds row 32 qb + 8 j + 4 hh + e,
@@ -334,12 +388,18 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
           pa[4 * j] = d4.x; pa[4 * j + 1] = d4.y; pa[4 * j + 2] = d4.z; pa[4 * j + 3] = d4.w;
         }
         // A scales: the block bytes, or PRECISE the row's Q exponent for both products
-        const int sq_a = PRECISE ? (int)sm.sqr[bb][32 * qb + n] : sm.sqdo[bb][qb].x;
+        const int sq_a = PRECISE ? (int)sm.rt.pr.sqr[bb][32 * qb + n] : sm.sqdo[bb][qb].x;
         const int sdo_a = PRECISE ? sq_a : sm.sqdo[bb][qb].y;
 #pragma unroll
         for (int cc = 0; cc < NC; ++cc) {
-          const v8i aq = lds_read_row32<D>(sm.q[bb], 32 * qb + n, 64 * cc + 32 * hh);
-          sa = mfma_scaled(aq, kreg[cc], cc ? sa : v16f{}, sq_a, k_scale);
+          if constexpr (QK4) {
+            const int b3 = st % 3, row = 32 * qb + n;
+            const v4i aq = lds_read_row16<D / 2>(sm.q4[b3], row, 32 * cc + 16 * hh);
+            sa = mfma_scaled_fp4(aq, kreg4[cc], cc ? sa : v16f{}, sm.rt.sq4[b3][row * (D / 32) + 2 * cc + hh], ks4[cc]);
+          } else {
+            const v8i aq = lds_read_row32<D>(sm.q[bb], 32 * qb + n, 64 * cc + 32 * hh);
+            sa = mfma_scaled(aq, kreg[cc], cc ? sa : v16f{}, sq_a, k_scale);
+          }
           const v8i ad = lds_read_row32<D>(sm.dO[bb], 32 * qb + n, 64 * cc + 32 * hh);
           pa = mfma_scaled(ad, vreg[cc], pa, sdo_a, v_scale);
         }
@@ -368,7 +428,7 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
         }
         int sq_s, sdo_s;
         if constexpr (PRECISE) {
-          sq_s = sdo_s = sm.sqr[bp][32 * qp + n];
+          sq_s = sdo_s = sm.rt.pr.sqr[bp][32 * qp + n];
         } else {
           const int2 sqdo = sm.sqdo[bp][qp];  // one 8-byte read
           sq_s = sqdo.x;
@@ -377,9 +437,19 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
         float4 pf4[4];  // PRECISE: 2^e(dO) of the same rows as lse4
         if constexpr (PRECISE)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) pf4[j] = *reinterpret_cast<const float4*>(&sm.pf[bs][32 * qs + 8 * j + 4 * hh]);
-        // operand m: Q rows (m even) or dO rows (m odd) of column chunk m / 2; two in flight
+          for (int j = 0; j < 4; ++j) pf4[j] = *reinterpret_cast<const float4*>(&sm.rt.pr.pf[bs][32 * qs + 8 * j + 4 * hh]);
+        // operand m: Q rows (m even) or dO rows (m odd) of column chunk m / 2; two in flight.
+        // QK4: the Q rows are the 4-bit copy (16 bytes, in the first half of the operand)
+        const int bp3 = sp_st % 3;
+        int sq4s[NC];
+        if constexpr (QK4)
+#pragma unroll
+          for (int cc = 0; cc < NC; ++cc) sq4s[cc] = sm.rt.sq4[bp3][(32 * qp + n) * (D / 32) + 2 * cc + hh];
         auto read_op = [&](int m) {
+          if (QK4 && !(m & 1)) {
+            const v4i t = lds_read_row16<D / 2>(sm.q4[bp3], 32 * qp + n, 32 * (m >> 1) + 16 * hh);
+            return v8i{t[0], t[1], t[2], t[3], 0, 0, 0, 0};
+          }
           return lds_read_row32<D>((m & 1) ? sm.dO[bp] : sm.q[bp], 32 * qp + n, 64 * (m >> 1) + 32 * hh);
         };
         v8i opnd[2];
@@ -394,7 +464,12 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
 #pragma unroll
         for (int m = 0; m < NM; ++m) {
           const int cc = m / 2;
-          if (m % 2 == 0) ns = mfma_scaled(opnd[0], kreg[cc], cc ? ns : v16f{}, sq_s, k_scale);
+          if (m % 2 == 0) {
+            if constexpr (QK4)
+              ns = mfma_scaled_fp4(v4i{opnd[0][0], opnd[0][1], opnd[0][2], opnd[0][3]}, kreg4[cc], cc ? ns : v16f{},
+                                   sq4s[cc], ks4[cc]);
+            else ns = mfma_scaled(opnd[0], kreg[cc], cc ? ns : v16f{}, sq_s, k_scale);
+          }
           else np = mfma_scaled(opnd[1], vreg[cc], np, sdo_s, v_scale);  // D - dP
           if (m + 2 < NM) opnd[m & 1] = read_op(m + 2);
 #pragma unroll
@@ -534,9 +609,10 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
       for (int ph = 0; ph <= n_steps; ++ph) {
         const int qtn = ld_qt;
         const int bn = (ph + 2) & (NBUF - 1);
+        const int bn3 = (ph + 2) % 3;
         if (ph + 2 < n_steps) {  // step ph + 2's tiles, straight into LDS
-          issue_step_loads<D, PRECISE>(p, sm, bn, doc_start, L, ld_h, qtn, cw, lane);
-          scale_loads(ld_h, qtn, rsq, rsdo, rd);
+          issue_step_loads<D, PRECISE, QK4>(p, sm, bn, doc_start, L, ld_h, qtn, cw, lane, bn3);
+          scale_loads(ld_h, qtn, rsq, rsdo, rd, rq4);
           if (++ld_qt == n_qt) {
             ld_qt = qt_first;
             ++ld_h;
@@ -647,7 +723,7 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
         }
         if (ph + 2 < n_steps) {
           __builtin_amdgcn_s_waitcnt(0);  // the direct loads have landed
-          scale_store(bn, qtn, rsq, rsdo, rd);
+          scale_store(bn, bn3, qtn, rsq, rsdo, rd, rq4);
         }
         lds_barrier();  // phase done: operands consumed, the next step's tiles stored
       }
@@ -1270,17 +1346,28 @@ hipError_t launch_bwd(const BwdParams& p, int d, int grid, hipStream_t s) {
   if (p.precise) {  // causal only (checked by the caller); one chunk, nothing stored
     BwdParams q = p;
     q.chunk = 0;
-    if (d == 128) hipLaunchKernelGGL((bwd_kernel<128, true, true>), dim3(grid), dim3(BWD_THREADS), 0, s, q);
-    else hipLaunchKernelGGL((bwd_kernel<64, true, true>), dim3(grid), dim3(BWD_THREADS), 0, s, q);
+    if (d == 128) hipLaunchKernelGGL((bwd_kernel<128, true, true, false>), dim3(grid), dim3(BWD_THREADS), 0, s, q);
+    else hipLaunchKernelGGL((bwd_kernel<64, true, true, false>), dim3(grid), dim3(BWD_THREADS), 0, s, q);
     const hipError_t e = hipGetLastError();
     return e != hipSuccess ? e : launch_dq_precise(q, d, grid, s);
   }
+  const bool f4 = p.q4 != nullptr;  // 4-bit scores
   if (d == 128) {
-    if (p.causal_mask) chunks(bwd_kernel<128, true, false>, dq_kernel<128>);
-    else chunks(bwd_kernel<128, false, false>, dq_kernel<128>);
+    if (p.causal_mask) {
+      if (f4) chunks(bwd_kernel<128, true, false, true>, dq_kernel<128>);
+      else chunks(bwd_kernel<128, true, false, false>, dq_kernel<128>);
+    } else {
+      if (f4) chunks(bwd_kernel<128, false, false, true>, dq_kernel<128>);
+      else chunks(bwd_kernel<128, false, false, false>, dq_kernel<128>);
+    }
   } else {
-    if (p.causal_mask) chunks(bwd_kernel<64, true, false>, dq_kernel<64>);
-    else chunks(bwd_kernel<64, false, false>, dq_kernel<64>);
+    if (p.causal_mask) {
+      if (f4) chunks(bwd_kernel<64, true, false, true>, dq_kernel<64>);
+      else chunks(bwd_kernel<64, true, false, false>, dq_kernel<64>);
+    } else {
+      if (f4) chunks(bwd_kernel<64, false, false, true>, dq_kernel<64>);
+      else chunks(bwd_kernel<64, false, false, false>, dq_kernel<64>);
+    }
   }
   return hipGetLastError();
 }

@@ -32,10 +32,11 @@ constexpr int fwd_threads() { return 64 * W; }
 
 template <int D>
 struct FwdSmem {
-  uint8_t k[2][KV_TILE * D];
+  uint8_t k[2][KV_TILE * D];  // 4-bit scores: the 4-bit K tile in the first half
   uint8_t v[2][KV_TILE * D];
   uint8_t sk[2][KV_TILE];
   uint8_t sv[2][KV_TILE];
+  uint8_t sk4[2][KV_TILE * D / 32];  // 4-bit scores: each key's d/32 exponent bytes
 };
 
 // Tile i of a unit (key tile kappa_hi - i) sits in K and V buffers i % 2: while tile i is current,
@@ -122,6 +123,70 @@ __device__ __forceinline__ uint32_t tile_offset(const FwdParams& p, int lane) {
   return (uint32_t)(row * p.Hkv * D + 16 * (pc ^ lds_swizzle<D>(row)));
 }
 
+// 4-bit scores: tile kappa's 4-bit K rows (d/2 bytes each) and its V rows into buffers kb, vb by
+// direct loads, the 1 KiB wave blocks dealt round robin over the waves; rows past the document end
+// repeat its last row and blocks wholly past it are zero-filled, as in issue_tile.  Returns the
+// scale word: thread t < 128 the d/32 K exponent bytes of key t, 128 <= t < 256 the V byte of key
+// t - 128.
+template <int D, int W>
+__device__ __forceinline__ uint32_t issue_tile4(const FwdParams& p, FwdSmem<D>& sm, int kb, int vb, int g,
+                                                int doc_start, int L, int kappa, int wave, int lane) {
+  constexpr int K4B = D / 2;                // bytes per 4-bit K row
+  constexpr int BK = KV_TILE * K4B / 1024;  // 1 KiB blocks of the K tile
+  constexpr int BV = KV_TILE * D / 1024;    // and of the V tile
+  for (int wb = __builtin_amdgcn_readfirstlane(wave); wb < BK + BV; wb += W) {
+    if (wb < BK) {
+      constexpr int CPR = K4B / 16;
+      const int pos = wb * 64 + lane, row = pos / CPR;
+      const int lc = (pos % CPR) ^ lds_swizzle<K4B>(row);
+      uint8_t* dst = sm.k[kb] + wb * 1024;
+      if (KV_TILE * kappa + wb * (1024 / K4B) < L) {
+        const int key = min(KV_TILE * kappa + row, L - 1);
+        dma_load16(p.k4 + ((int64_t)(doc_start + key) * p.Hkv + g) * K4B + 16 * lc, lds_addr(dst));
+      } else {
+        *reinterpret_cast<uint4*>(dst + 16 * lane) = make_uint4(0, 0, 0, 0);
+      }
+    } else {
+      constexpr int CPR = D / 16;
+      const int blk = wb - BK, pos = blk * 64 + lane, row = pos / CPR;
+      const int lc = (pos % CPR) ^ lds_swizzle<D>(row);
+      uint8_t* dst = sm.v[vb] + blk * 1024;
+      if (KV_TILE * kappa + blk * (1024 / D) < L) {
+        const int key = min(KV_TILE * kappa + row, L - 1);
+        dma_load16(p.v + ((int64_t)(doc_start + key) * p.Hkv + g) * D + 16 * lc, lds_addr(dst));
+      } else {
+        *reinterpret_cast<uint4*>(dst + 16 * lane) = make_uint4(0, 0, 0, 0);
+      }
+    }
+  }
+  const int tid = threadIdx.x;
+  uint32_t sc = 127;
+  if (tid < 2 * KV_TILE) {
+    const int key = KV_TILE * kappa + (tid & (KV_TILE - 1));
+    if (tid < KV_TILE) {
+      sc = 0x7F7F7F7Fu;
+      if (key < L) {
+        const uint8_t* e4 = p.sk4 + ((int64_t)g * p.T + doc_start + key) * (D / 32);
+        sc = D == 128 ? *reinterpret_cast<const uint32_t*>(e4) : (uint32_t)*reinterpret_cast<const uint16_t*>(e4);
+      }
+    } else if (key < L) {
+      sc = p.sv[(int64_t)g * p.T + doc_start + key];
+    }
+  }
+  return sc;
+}
+
+template <int D>
+__device__ __forceinline__ void store_scales4(FwdSmem<D>& sm, int kb, int vb, uint32_t sc) {
+  const int tid = threadIdx.x;
+  if (tid < KV_TILE) {
+    if constexpr (D == 128) *reinterpret_cast<uint32_t*>(&sm.sk4[kb][4 * tid]) = sc;
+    else *reinterpret_cast<uint16_t*>(&sm.sk4[kb][2 * tid]) = (uint16_t)sc;
+  } else if (tid < 2 * KV_TILE) {
+    sm.sv[vb][tid - KV_TILE] = (uint8_t)sc;
+  }
+}
+
 template <int D>
 __device__ __forceinline__ void store_scales(FwdSmem<D>& sm, int kb, int vb, uint32_t sc) {
   const int tid = threadIdx.x;
@@ -133,8 +198,14 @@ __device__ __forceinline__ void store_scales(FwdSmem<D>& sm, int kb, int vb, uin
 // PRECISE (the precision options, with per-token scales): V's exponent is folded into the
 // probability operand against the row's running maximum of visited V exponents, and V enters
 // the product with its bare codes.
-template <int D, int W, bool CAUSAL, bool PRECISE>
+// QK4 (4-bit scores, [J] §3.1 "Mixed NVFP4/FP8 path", §3.4 "Softmax throughput"): S^T takes the
+// E2M1 copies of K and Q (one exponent per 32 channels of a token, per lane as the instruction's
+// scale bytes), and the probability operand is quantised in the log domain: each 32-key group of
+// the tile gets the round-up exponent of its largest probability, found from the group's largest
+// score (one exponential per group), and its codes are E4M3(p 2^-e) with operand scale 2^e.
+template <int D, int W, bool CAUSAL, bool PRECISE, bool QK4>
 __global__ __launch_bounds__(fwd_threads<W>(), 8 / W) void fwd_kernel(FwdParams p) {
+  static_assert(!(PRECISE && QK4), "separate paths");
   constexpr int FWD_THREADS = fwd_threads<W>();
   constexpr int NC = D / 64;   // 64-wide d chunks of the score contraction
   constexpr int NDB = D / 32;  // 32-wide d blocks of the output
@@ -176,7 +247,21 @@ __global__ __launch_bounds__(fwd_threads<W>(), 8 / W) void fwd_kernel(FwdParams 
     // Q operand (B of S^T): lane (n, hh) holds d = 64c + 32hh .. +31 of query n.
     v8i qop[NC];
     int q_scale = 127;
-    {
+    // QK4: the 4-bit Q operand, the same d range as 16 bytes, and its exponent byte per chunk
+    v4i qop4[NC];
+    int q_scale4[NC];
+    if constexpr (QK4) {
+      const int64_t qa = (int64_t)(doc_start + q_rel);
+#pragma unroll
+      for (int cc = 0; cc < NC; ++cc) {
+        qop4[cc] = v4i{0, 0, 0, 0};
+        q_scale4[cc] = 127;
+        if (row_valid) {
+          qop4[cc] = *reinterpret_cast<const v4i*>(p.q4 + (qa * p.Hq + h) * (D / 2) + 32 * cc + 16 * hh);
+          q_scale4[cc] = p.sq4[((int64_t)h * p.T + qa) * (D / 32) + 2 * cc + hh];
+        }
+      }
+    } else {
       const int64_t qa = (int64_t)(doc_start + q_rel);
 #pragma unroll
       for (int cc = 0; cc < NC; ++cc) {
@@ -202,22 +287,46 @@ __global__ __launch_bounds__(fwd_threads<W>(), 8 / W) void fwd_kernel(FwdParams 
 
     lds_barrier();  // the previous unit's readers are done with every buffer
     {
-      const uint32_t sc = issue_tile<D, W>(p, sm, 0, 0, g, doc_start, L, kappa_hi, wave, lane);
+      const uint32_t sc = QK4 ? issue_tile4<D, W>(p, sm, 0, 0, g, doc_start, L, kappa_hi, wave, lane)
+                              : issue_tile<D, W>(p, sm, 0, 0, g, doc_start, L, kappa_hi, wave, lane);
       __builtin_amdgcn_s_waitcnt(0);  // this wave's direct loads have landed
-      store_scales<D>(sm, 0, 0, sc);
+      if constexpr (QK4) store_scales4<D>(sm, 0, 0, sc);
+      else store_scales<D>(sm, 0, 0, sc);
     }
     lds_barrier();
     for (int kappa = kappa_hi, it = 0; kappa >= 0; --kappa, ++it) {
       const int kb = it & 1;
       uint32_t scn = 127;
-      if (kappa > 0) scn = issue_full_tile<D, W>(p, sm, kb ^ 1, kb ^ 1, g, doc_start, kappa - 1, wave, voff0);
+      if (kappa > 0) {
+        if constexpr (QK4) scn = issue_tile4<D, W>(p, sm, kb ^ 1, kb ^ 1, g, doc_start, L, kappa - 1, wave, lane);
+        else scn = issue_full_tile<D, W>(p, sm, kb ^ 1, kb ^ 1, g, doc_start, kappa - 1, wave, voff0);
+      }
       if (wave_active && kappa <= kd) {
         const uint8_t* kt = sm.k[kb];
         // ---- S^T for the 4 key blocks of the tile.  K operand k (key block k / NC, d chunk
         // k % NC) is read SAHEAD matrix instructions early into a ring of registers, so each
         // instruction finds its operand loaded instead of waiting out an LDS round trip.
         v16f s[4];
-        {
+        if constexpr (QK4) {
+          // S^T from the 4-bit copies: A = K rows (16 bytes per lane and chunk), the key's
+          // exponent byte of d-block 2 cc + hh as the A scale
+          constexpr int K4B = D / 2, NS = 4 * NC, SAHEAD = 3;
+          auto read_k = [&](int k) { return lds_read_row16<K4B>(kt, 32 * (k / NC) + n, 32 * (k % NC) + 16 * hh); };
+          v4i kring[SAHEAD];
+#pragma unroll
+          for (int k = 0; k < SAHEAD; ++k) kring[k] = read_k(k);
+#pragma unroll
+          for (int k = 0; k < NS; ++k) {
+            const int kb4 = k / NC, cc = k % NC;
+            const int ks = sm.sk4[kb][(32 * kb4 + n) * (D / 32) + 2 * cc + hh];
+            s[kb4] = mfma_scaled_fp4(kring[k % SAHEAD], qop4[cc], cc ? s[kb4] : v16f{}, ks, q_scale4[cc]);
+            if (k + SAHEAD < NS) kring[k % SAHEAD] = read_k(k + SAHEAD);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          // the group maxima read these right away: a fixed margin after the last product
+#pragma unroll
+          for (int kb4 = 0; kb4 < 4; ++kb4) mfma_drain(s[kb4]);
+        } else {
           constexpr int NS = 4 * NC, SAHEAD = 3;
           auto read_k = [&](int k) { return lds_read_row32<D>(kt, 32 * (k / NC) + n, 64 * (k % NC) + 32 * hh); };
           v8i kring[SAHEAD];
@@ -263,13 +372,26 @@ __global__ __launch_bounds__(fwd_threads<W>(), 8 / W) void fwd_kernel(FwdParams 
             }
         }
 #endif
-        // ---- running max (raw accumulator units, then scaled once)
+        // ---- running max (raw accumulator units, then scaled once); QK4 keeps each 32-key
+        // group's maximum for its exponent
         float mx = -__builtin_inff();
+        float gmx[4];
+        if constexpr (QK4) {
 #pragma unroll
-        for (int kb4 = 0; kb4 < 4; ++kb4)
+          for (int kb4 = 0; kb4 < 4; ++kb4) {
+            gmx[kb4] = -__builtin_inff();
 #pragma unroll
-          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb4][i]);
-        mx = halves_max(mx);
+            for (int i = 0; i < 16; ++i) gmx[kb4] = fmaxf(gmx[kb4], s[kb4][i]);
+            gmx[kb4] = halves_max(gmx[kb4]);
+            mx = fmaxf(mx, gmx[kb4]);
+          }
+        } else {
+#pragma unroll
+          for (int kb4 = 0; kb4 < 4; ++kb4)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb4][i]);
+          mx = halves_max(mx);
+        }
         const float m_new = fmaxf(m, mx * c);
         const float alpha = __builtin_amdgcn_exp2f(m - m_new);
         if (__any(alpha != 1.0f)) {
@@ -286,7 +408,12 @@ __global__ __launch_bounds__(fwd_threads<W>(), 8 / W) void fwd_kernel(FwdParams 
         // issued in a burst: the first half's run between the exponentials of key blocks 2 and
         // 3 (the probabilities overwrite their scores), the second half's between those blocks'
         // additions to the row sum, which come last (the order of the additions is unchanged).
-        const float bias = (float)P_SHIFT - m_new;
+        // QK4: the probabilities unshifted, each group's exponent byte from its largest one
+        const float bias = QK4 ? -m_new : (float)P_SHIFT - m_new;
+        uint32_t pe[4];
+        if constexpr (QK4)
+#pragma unroll
+          for (int kb4 = 0; kb4 < 4; ++kb4) pe[kb4] = e8m0_byte_nonneg(__builtin_amdgcn_exp2f(fmaf(gmx[kb4], c, -m_new)));
         const uint8_t* vt = sm.v[kb];
         v8i pop[2];
         int vs[2];
@@ -321,6 +448,8 @@ __global__ __launch_bounds__(fwd_threads<W>(), 8 / W) void fwd_kernel(FwdParams 
                              __builtin_ldexpf(a1, (int)((wv >> 8) & 0xFFu) - 127 - vref),
                              __builtin_ldexpf(a2, (int)((wv >> 16) & 0xFFu) - 127 - vref),
                              __builtin_ldexpf(a3, (int)(wv >> 24) - 127 - vref));
+          } else if constexpr (QK4) {
+            return pack4_fp8_scaled(a0, a1, a2, a3, pe[kb4]);
           } else {
             return pack4_fp8(a0, a1, a2, a3);
           }
@@ -330,8 +459,15 @@ __global__ __launch_bounds__(fwd_threads<W>(), 8 / W) void fwd_kernel(FwdParams 
         auto read_v = [&](int k) { return lds_read_tr32<D>(vt, 64 * (k / NDB), 32 * (k % NDB), lane); };
         constexpr int NPV = 2 * NDB;  // matrix instructions: (64-key half ci, d-block db)
         v8i ring[2];
+        // QK4: lane (n, hh) scales key half hh of the 64-key chunk: group 2 ci + hh
+        int psc[2] = {p_scale, p_scale};
+        if constexpr (QK4) {
+          psc[0] = (int)(hh ? pe[1] : pe[0]);
+          psc[1] = (int)(hh ? pe[3] : pe[2]);
+        }
         auto pv_step = [&](int k) {
-          oacc[k % NDB] = mfma_scaled(ring[k & 1], pop[k / NDB], oacc[k % NDB], PRECISE ? v_scale : vs[k / NDB], p_scale);
+          oacc[k % NDB] = mfma_scaled(ring[k & 1], pop[k / NDB], oacc[k % NDB], PRECISE ? v_scale : vs[k / NDB],
+                                      QK4 ? psc[k / NDB] : p_scale);
           if (k + 2 < NPV) ring[k & 1] = read_v(k + 2);
         };
         // blocks 0, 1: probabilities, row sum, codes
@@ -392,22 +528,25 @@ __global__ __launch_bounds__(fwd_threads<W>(), 8 / W) void fwd_kernel(FwdParams 
               const int word = pop[kb4 >> 1][4 * (kb4 & 1) + i / 4];
               if (p.dbg.fwd_p) p.dbg.fwd_p[x] = (uint8_t)(word >> (8 * (i % 4)));
               if (p.dbg.fwd_m) p.dbg.fwd_m[x] = m_new;
+              if (QK4 && p.dbg.fwd_ps) p.dbg.fwd_ps[x] = (uint8_t)pe[kb4];
             }
         }
 #endif
       }
       if (kappa > 0) {
         __builtin_amdgcn_s_waitcnt(0);  // this wave's direct loads have landed
-        store_scales<D>(sm, kb ^ 1, kb ^ 1, scn);
+        if constexpr (QK4) store_scales4<D>(sm, kb ^ 1, kb ^ 1, scn);
+        else store_scales<D>(sm, kb ^ 1, kb ^ 1, scn);
         lds_barrier();
       }
     }
 
-    // ---- epilogue: O = acc / l, LSE = m + log2 l (l in units of 2^-8)
+    // ---- epilogue: O = acc / l, LSE = m + log2 l (l in units of 2^-8; QK4: of 1)
+    constexpr int L_SHIFT = QK4 ? 0 : P_SHIFT;
     if (wave_active) {
       const float lt = halves_sum(l);
       if (row_valid) {
-        const float inv = 256.0f / lt;
+        const float inv = (float)(1 << L_SHIFT) / lt;
         uint16_t* orow = p.o + (int64_t)(doc_start + q_rel) * p.ost + (int64_t)h * p.osh;
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
@@ -419,7 +558,7 @@ __global__ __launch_bounds__(fwd_threads<W>(), 8 / W) void fwd_kernel(FwdParams 
             w.y = pack_bf16(oacc[db][4 * j + 2] * inv, oacc[db][4 * j + 3] * inv);
             *reinterpret_cast<uint2*>(orow + d0) = w;
           }
-        if (hh == 0) p.lse[(int64_t)h * p.T + doc_start + q_rel] = m + __builtin_amdgcn_logf(lt) - (float)P_SHIFT;
+        if (hh == 0) p.lse[(int64_t)h * p.T + doc_start + q_rel] = m + __builtin_amdgcn_logf(lt) - (float)L_SHIFT;
       }
     }
   }
@@ -444,19 +583,24 @@ __global__ __launch_bounds__(fwd_threads<W>(), 8 / W) void fwd_kernel(FwdParams 
 hipError_t launch_fwd(const FwdParams& p, int d, int grid, hipStream_t s) {
   // documents of fewer than 4096 tokens on average: 128-query units, two workgroups per CU
   const bool short_docs = (int64_t)p.n_docs * 4096 > (int64_t)p.T;
-  auto go = [&](auto c, auto pr) {
-    constexpr bool C = decltype(c)::value, PR = decltype(pr)::value;
+  auto go = [&](auto c, auto pr, auto f4) {
+    constexpr bool C = decltype(c)::value, PR = decltype(pr)::value, F4 = decltype(f4)::value;
     if (short_docs) {
-      if (d == 128) hipLaunchKernelGGL((fwd_kernel<128, 4, C, PR>), dim3(2 * grid), dim3(fwd_threads<4>()), 0, s, p);
-      else hipLaunchKernelGGL((fwd_kernel<64, 4, C, PR>), dim3(2 * grid), dim3(fwd_threads<4>()), 0, s, p);
+      if (d == 128) hipLaunchKernelGGL((fwd_kernel<128, 4, C, PR, F4>), dim3(2 * grid), dim3(fwd_threads<4>()), 0, s, p);
+      else hipLaunchKernelGGL((fwd_kernel<64, 4, C, PR, F4>), dim3(2 * grid), dim3(fwd_threads<4>()), 0, s, p);
     } else {
-      if (d == 128) hipLaunchKernelGGL((fwd_kernel<128, 8, C, PR>), dim3(grid), dim3(fwd_threads<8>()), 0, s, p);
-      else hipLaunchKernelGGL((fwd_kernel<64, 8, C, PR>), dim3(grid), dim3(fwd_threads<8>()), 0, s, p);
+      if (d == 128) hipLaunchKernelGGL((fwd_kernel<128, 8, C, PR, F4>), dim3(grid), dim3(fwd_threads<8>()), 0, s, p);
+      else hipLaunchKernelGGL((fwd_kernel<64, 8, C, PR, F4>), dim3(grid), dim3(fwd_threads<8>()), 0, s, p);
     }
   };
-  if (p.precise) go(std::true_type{}, std::true_type{});  // causal only (checked by the caller)
-  else if (p.causal) go(std::true_type{}, std::false_type{});
-  else go(std::false_type{}, std::false_type{});
+  const std::true_type y{};
+  const std::false_type n{};
+  if (p.precise) go(y, y, n);  // causal only (checked by the caller)
+  else if (p.q4) {
+    if (p.causal) go(y, n, y);
+    else go(n, n, y);
+  } else if (p.causal) go(y, n, n);
+  else go(n, n, n);
   return hipGetLastError();
 }
 

@@ -33,6 +33,14 @@ constexpr float LOG2E = 1.4426950408889634f;
 __device__ __forceinline__ v16f mfma_scaled(const v8i& a, const v8i& b, const v16f& c, int sa, int sb) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
 }
+// The same instruction on E2M1 operands (format 4): each lane supplies 16 bytes (registers 0..3;
+// the upper four are not read), lane (n, h) holding K indices 32 h .. 32 h + 31 of row n, two per
+// byte with the lower index in the low nibble, and its scale byte applies to exactly those
+// (established by a probe on the hardware).
+__device__ __forceinline__ v16f mfma_scaled_fp4(const v4i& a, const v4i& b, const v16f& c, int sa, int sb) {
+  const v8i a8 = {a[0], a[1], a[2], a[3], 0, 0, 0, 0}, b8 = {b[0], b[1], b[2], b[3], 0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b8, c, 4, 4, 0, sa, 0, sb);
+}
 
 // End of an accumulation chain whose result is read next.  The scaled FP8 instruction writes
 // its last accumulator registers late; the compiler's padding before the first read has been
@@ -108,9 +116,13 @@ __device__ __forceinline__ int acc_row(int i, int h) { return 8 * (i >> 2) + 4 *
 // COLS = 128 (two rows per 256 bytes): chunk ^ g(m), m = (row >> 1) & 7, g a permutation of 0..7
 //   with g(m) >> 1 distinct over m in {0, 1, 4, 5} and over m in {2, 3, 6, 7};
 // COLS = 64 (four rows per 256 bytes): chunk ^ ((row >> 2) & 3).
+// COLS = 32 (eight rows per 256 bytes; the 4-bit K tile at d = 64, row-major reads only):
+//   chunk ^ ((row >> 3) & 1), so rows r and r + 8 of a 16-row group fill the odd and even groups.
 template <int COLS>
 __device__ __forceinline__ int lds_swizzle(int row) {
-  if constexpr (COLS == 128) {
+  if constexpr (COLS == 32) {  // eight rows per 256 bytes: rows 8 apart take the other chunk
+    return (row >> 3) & 1;
+  } else if constexpr (COLS == 128) {
     const int m = (row >> 1) & 7;
     return 2 * ((m & 1) | (((m >> 2) & 1) << 1)) + ((m >> 1) & 1);
   } else {
@@ -131,6 +143,13 @@ __device__ __forceinline__ v8i lds_read_row32(const uint8_t* tile, int row, int 
   r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
   r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
   return r;
+}
+
+// Row-major 4-bit operand: lane reads 16 contiguous bytes (32 E2M1 values) of `row` at `col`
+// (multiple of 16).
+template <int COLS>
+__device__ __forceinline__ v4i lds_read_row16(const uint8_t* tile, int row, int col) {
+  return *reinterpret_cast<const v4i*>(tile + lds_off<COLS>(row, col));
 }
 
 // Transposed operand: the K dimension runs along the tile's rows.  For the 64-row K chunk that

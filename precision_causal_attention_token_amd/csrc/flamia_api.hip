@@ -26,7 +26,7 @@ extern "C" flamia_status flamia_debug_set_dump(const flamia_debug_dump* d) {
   if (d->row_hi <= d->row_lo || d->key_hi <= d->key_lo || d->head_hi <= d->head_lo) return FLAMIA_ERR_SHAPE;
   g_dbg = DebugDump{d->row_lo, d->row_hi, d->key_lo, d->key_hi, d->head_lo, d->head_hi, d->fwd_s, d->fwd_m,
                     d->fwd_p, d->bwd_s, d->bwd_dp, d->bwd_p, d->bwd_ps, d->bwd_ds, d->bwd_dss, d->dq_part,
-                    d->n_tiles, d->dq_s, d->dq_dp, d->dq_ds, d->dq_dss};
+                    d->n_tiles, d->dq_s, d->dq_dp, d->dq_ds, d->dq_dss, d->fwd_ps};
   return FLAMIA_OK;
 }
 #endif
@@ -165,8 +165,11 @@ flamia_status flamia_quantize(const flamia_qtensor* tensors, int32_t n_tensors, 
     if (!aligned(t.x, 16) || (t.stride_t % 8) || (t.stride_h % 8) || t.stride_t < 0 || t.stride_h < 0)
       return FLAMIA_ERR_SHAPE;
     if (!aligned(t.codes, 16)) return FLAMIA_ERR_SHAPE;
+    if ((t.mx4_codes == nullptr) != (t.mx4_scales == nullptr)) return FLAMIA_ERR_NULL;
+    if (t.mx4_codes && o) return FLAMIA_ERR_UNSUPPORTED;  // the 4-bit copy is for Q and K
+    if (t.mx4_codes && !aligned(t.mx4_codes, 4)) return FLAMIA_ERR_SHAPE;
     p.t[i] = QTensorDev{static_cast<const uint16_t*>(t.x), t.stride_t, t.stride_h, t.H, t.codes, t.scales,
-                        t.hadamard ? 1 : 0, t.per_token ? 1 : 0};
+                        t.hadamard ? 1 : 0, t.per_token ? 1 : 0, t.mx4_codes, t.mx4_scales};
     if (t.H > p.maxH) p.maxH = t.H;
   }
   if (o) {
@@ -195,9 +198,15 @@ flamia_status flamia_fwd(const flamia_fwd_args* a, void* stream) {
     return FLAMIA_ERR_SHAPE;
   if (!aligned(a->q, 16) || !aligned(a->k, 16) || !aligned(a->v, 16) || !aligned(a->fwd_list, 16))
     return FLAMIA_ERR_SHAPE;
+  const int n4 = (a->q4 != nullptr) + (a->sq4 != nullptr) + (a->k4 != nullptr) + (a->sk4 != nullptr);
+  if (n4 != 0 && n4 != 4) return FLAMIA_ERR_NULL;
+  if (n4 && a->precise) return FLAMIA_ERR_UNSUPPORTED;
+  if (n4 && (!aligned(a->q4, 16) || !aligned(a->k4, 16) || !aligned(a->sq4, 4) || !aligned(a->sk4, 4)))
+    return FLAMIA_ERR_SHAPE;
   const int grid = num_cus();
   if (grid <= 0) return FLAMIA_ERR_HIP;
   FwdParams p{};
+  p.q4 = a->q4; p.sq4 = a->sq4; p.k4 = a->k4; p.sk4 = a->sk4;
   p.q = a->q; p.k = a->k; p.v = a->v; p.sq = a->sq; p.sk = a->sk; p.sv = a->sv;
   p.T = a->T; p.Hq = a->Hq; p.Hkv = a->Hkv;
   p.c = score_scale(a->softmax_scale, a->d);
@@ -244,6 +253,11 @@ flamia_status flamia_bwd(const flamia_bwd_args* a, void* stream) {
   if (a->T > FLAMIA_MAX_T) return FLAMIA_ERR_UNSUPPORTED;
   if (a->non_causal && a->causal_dq_scale) return FLAMIA_ERR_UNSUPPORTED;
   if (a->non_causal && a->precise) return FLAMIA_ERR_UNSUPPORTED;  // the precision options are causal
+  const int n4 = (a->q4 != nullptr) + (a->sq4 != nullptr) + (a->k4 != nullptr) + (a->sk4 != nullptr);
+  if (n4 != 0 && n4 != 4) return FLAMIA_ERR_NULL;
+  if (n4 && a->precise) return FLAMIA_ERR_UNSUPPORTED;
+  if (n4 && (!aligned(a->q4, 16) || !aligned(a->k4, 16) || !aligned(a->sq4, 4) || !aligned(a->sk4, 4)))
+    return FLAMIA_ERR_SHAPE;
   if (a->workspace_bytes < flamia_bwd_workspace_bytes(a->n_docs, a->T, a->Hq, a->d, 0)) return FLAMIA_ERR_WORKSPACE;
   const int64_t st[6] = {a->dq_stride_t, a->dq_stride_h, a->dk_stride_t, a->dk_stride_h, a->dv_stride_t, a->dv_stride_h};
   for (int i = 0; i < 6; ++i)
@@ -300,6 +314,7 @@ flamia_status flamia_bwd(const flamia_bwd_args* a, void* stream) {
   p.causal = (a->causal_dq_scale || a->precise) ? 1 : 0;
   p.causal_mask = a->non_causal ? 0 : 1;
   p.precise = a->precise ? 1 : 0;
+  p.q4 = a->q4; p.sq4 = a->sq4; p.k4 = a->k4; p.sk4 = a->sk4;
 #ifdef FLAMIA_DEBUG_DUMP
   p.dbg = g_dbg;
 #endif

@@ -28,6 +28,7 @@ struct DebugDump {
   float* dq_dp;       // dP - D as it formed it
   uint8_t* dq_ds;     // code of dS 2^e(K_j) and its (row, 32-key block) exponent byte
   uint8_t* dq_dss;
+  uint8_t* fwd_ps;    // 4-bit scores: the probability code's 32-key group exponent byte
 };
 // Position of (query head, row) in the window's rows, or -1 outside it.
 __device__ __forceinline__ int64_t dbg_row(const DebugDump& g, int h, int row) {
@@ -51,6 +52,8 @@ struct QTensorDev {
   uint8_t* scales;
   int32_t hadamard;  // rows rotated by H / sqrt(d) before quantisation
   int32_t per_token;  // one exponent per token (blocks of one token)
+  uint8_t* codes4;    // optional 4-bit copy: E2M1 codes [T, H, d/2] (even channel in the low
+  uint8_t* scales4;   // nibble) and one E8M0 byte per 32 channels of a token [H, T, d/32]
 };
 
 struct QuantParams {
@@ -76,6 +79,8 @@ struct FwdParams {
   float* lse;
   int32_t causal;  // 1: keys j <= i; 0: every key of the document
   int32_t precise;  // the precision options (per-token scales, V folded into P)
+  // 4-bit scores (q4 != nullptr): E2M1 copies of Q and K [T, H, d/2] with exponents [H, T, d/32]
+  const uint8_t *q4, *sq4, *k4, *sk4;
 #ifdef FLAMIA_DEBUG_DUMP
   DebugDump dbg;
 #endif
@@ -116,6 +121,7 @@ struct BwdParams {
   int32_t causal_mask;      // 1: keys j <= i; 0: every key of the document
   int32_t precise;          // the precision options: per-token scales folded into P and dS, dQ
                             // recomputed query-stationary with row-wise dS exponents
+  const uint8_t *q4, *sq4, *k4, *sk4;  // 4-bit scores: the forward's E2M1 copies (or nullptr)
 #ifdef FLAMIA_DEBUG_DUMP
   DebugDump dbg;
 #endif

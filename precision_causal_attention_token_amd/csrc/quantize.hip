@@ -60,6 +60,22 @@ __device__ __forceinline__ void hadamard_row(float (&v)[8], int lc) {
 #pragma unroll
   for (int e = 0; e < 8; ++e) v[e] = __fmul_rn(v[e], c);
 }
+// E2M1 (values 0, 0.5, 1, 1.5, 2, 3, 4, 6) of a finite float, round to nearest even, the sign
+// kept on zero, saturating at 6 (never reached under the round-up exponent): the magnitude code
+// counts the thresholds passed, each midpoint going to the neighbour whose mantissa bit is 0.
+__device__ __forceinline__ uint32_t e2m1_rne(float y) {
+  const float a = fabsf(y);
+  const uint32_t c = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+                     (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) + (uint32_t)(a > 5.0f);
+  return c | ((__float_as_uint(y) >> 28) & 8u);
+}
+// Smallest s with amax <= 6 2^s for amax = 1.f 2^E (f in [1, 2)): s = E - 2 + (f > 1.5); adding
+// 2^22 - 1 carries into the exponent field exactly when the mantissa exceeds 0.5.  Clamped to
+// >= -127 (zero and subnormal amax).
+__device__ __forceinline__ int e2m1_exponent(float amax) {
+  const int s = (int)((__float_as_uint(amax) + 0x3FFFFFu) >> 23) - 129;
+  return s < -127 ? -127 : s;
+}
 __device__ __forceinline__ void bf16x8_to_f32(const uint4& w, float (&v)[8]) {
   const uint32_t a[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
@@ -225,8 +241,31 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantParams p) {
         }
       }
       *reinterpret_cast<uint2*>(X.codes + (tau * X.H + h) * D + 8 * lc) = out;
+      if (X.codes4) {
+        // the 4-bit copy from the same FP32 values: a 32-channel group is the quad of lanes
+        // 4 (lc / 4) .. + 3 (rows are whole quads of lanes)
+        float v[8];
+        bf16x8_to_f32(vals[ps], v);
+        if (X.hadamard) hadamard_row<D>(v, lc);
+        float m = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(v[e]));
+        m = fmaxf(m, dpp<0xB1>(m));
+        m = fmaxf(m, dpp<0x4E>(m));
+        const int s4 = e2m1_exponent(m);
+        const float f = exp2i_neg(s4);
+        uint32_t w = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) w |= e2m1_rne(v[e] * f) << (4 * e);
+        *reinterpret_cast<uint32_t*>(X.codes4 + (tau * X.H + h) * (D / 2) + 4 * lc) = w;
+        if ((lc & 3) == 0) X.scales4[((int64_t)h * T + tau) * (D / 32) + lc / 4] = (uint8_t)(s4 + 127);
+      }
     } else if (st == -2) {
       *reinterpret_cast<uint2*>(X.codes + (tau * X.H + h) * D + 8 * lc) = make_uint2(0, 0);
+      if (X.codes4) {
+        *reinterpret_cast<uint32_t*>(X.codes4 + (tau * X.H + h) * (D / 2) + 4 * lc) = 0;
+        if ((lc & 3) == 0) X.scales4[((int64_t)h * T + tau) * (D / 32) + lc / 4] = 0;
+      }
     }
     if (with_d) {
       if constexpr (LPR == 16) {

@@ -37,7 +37,7 @@ import torch
 
 import precision_causal_attention_token_amd as fl
 from precision_causal_attention_token_amd import build as fl_build
-from tests.helpers import bf16_bits, bits_to_f64, cosine, dequant, rms
+from tests.helpers import bf16_bits, bits_to_f64, cosine, dequant, dequant4, rms
 
 COS_MIN = 0.9995
 MAXABS_REL = 2e-2
@@ -88,7 +88,7 @@ def _dump_struct(win, bufs):
         _fields_ = [(n, ctypes.c_int32) for n in ("row_lo", "row_hi", "key_lo", "key_hi", "head_lo", "head_hi")] + \
                    [(n, ctypes.c_void_p) for n in ("fwd_s", "fwd_m", "fwd_p", "bwd_s", "bwd_dp", "bwd_p", "bwd_ps",
                                                    "bwd_ds", "bwd_dss", "dq_part")] + [("n_tiles", ctypes.c_int32)] + \
-                   [(n, ctypes.c_void_p) for n in ("dq_s", "dq_dp", "dq_ds", "dq_dss")]
+                   [(n, ctypes.c_void_p) for n in ("dq_s", "dq_dp", "dq_ds", "dq_dss", "fwd_ps")]
     d = Dump(win["row_lo"], win["row_hi"], win["key_lo"], win["key_hi"], win["head_lo"], win["head_hi"])
     for n, t in bufs.items():
         setattr(d, n, t.data_ptr())
@@ -101,11 +101,11 @@ def n_key_tiles(win):
 
 
 DUMP_F32 = ("fwd_s", "fwd_m", "bwd_s", "bwd_dp", "dq_s", "dq_dp")
-DUMP_U8 = ("fwd_p", "bwd_p", "bwd_ps", "bwd_ds", "bwd_dss", "dq_ds", "dq_dss")
+DUMP_U8 = ("fwd_p", "bwd_p", "bwd_ps", "bwd_ds", "bwd_dss", "dq_ds", "dq_dss", "fwd_ps")
 
 
 def gpu_call(q, k, v, do, cu, causal_dq=False, softmax_scale=None, window=None, store_budget=None, causal=True,
-             static_scratch=False, hadamard=False):
+             static_scratch=False, hadamard=False, qk4=False):
     """Full training call on the GPU through the C ABI; returns numpy arrays (BF16 outputs as
     bit patterns).  causal=False: non-causal attention within each document.  hadamard=True: Q
     and K quantised rotated; dQ and dK are returned in the rotated basis (the backward's own
@@ -131,8 +131,8 @@ def gpu_call(q, k, v, do, cu, causal_dq=False, softmax_scale=None, window=None, 
             assert st == 0, st
         try:
             lists = fl.Lists(cu_d, T, causal)
-            qz, kz, vz = fl.quantize([qd, kd, vd], cu_d, hadamard=(hadamard, hadamard, False))
-            o, lse = fl.fwd(qz, kz, vz, cu_d, lists.fwd, softmax_scale, causal=causal)
+            qz, kz, vz = fl.quantize([qd, kd, vd], cu_d, hadamard=(hadamard, hadamard, False), mx4=(qk4, qk4, False))
+            o, lse = fl.fwd(qz, kz, vz, cu_d, lists.fwd, softmax_scale, causal=causal, qk4=qk4)
             dc, dsc, D = fl.quantize_do(dod, o, cu_d)
             Hq, d = q.shape[1], q.shape[2]
             budget = fl.DEFAULT_STORE_BYTES if store_budget is None else store_budget
@@ -140,12 +140,12 @@ def gpu_call(q, k, v, do, cu, causal_dq=False, softmax_scale=None, window=None, 
             ws.fill_(0xA5)  # the workspace may hold anything on entry
             if static_scratch:
                 dq, dk, dv, pi = fl.bwd(qz, kz, vz, (dc, dsc), lse, D, cu_d, lists, softmax_scale, causal_dq,
-                                        want_pi=True, static_scratch=True, causal=causal)
+                                        want_pi=True, static_scratch=True, causal=causal, qk4=qk4)
                 torch.cuda.synchronize()
                 status, chunks = 0, None
             else:
                 dq, dk, dv, pi = fl.bwd(qz, kz, vz, (dc, dsc), lse, D, cu_d, lists, softmax_scale, causal_dq,
-                                        want_pi=True, workspace=ws, causal=causal)
+                                        want_pi=True, workspace=ws, causal=causal, qk4=qk4)
                 torch.cuda.synchronize()
                 status, chunks = fl.bwd_status(ws)
             assert status == 0, 'backward workspace status'
@@ -156,7 +156,9 @@ def gpu_call(q, k, v, do, cu, causal_dq=False, softmax_scale=None, window=None, 
     n = lambda t: t.cpu().numpy()
     out = dict(q=n(qz[0]), sq=n(qz[1]), k=n(kz[0]), sk=n(kz[1]), v=n(vz[0]), sv=n(vz[1]),
                do=n(dc), sdo=n(dsc), D=n(D), o=b(o), lse=n(lse), dq=b(dq), dk=b(dk), dv=b(dv), pi=n(pi),
-               chunks=chunks, causal=bool(causal), hadamard=bool(hadamard))
+               chunks=chunks, causal=bool(causal), hadamard=bool(hadamard), qk4=bool(qk4))
+    if qk4:
+        out.update(q4=n(qz[2]), sq4=n(qz[3]), k4=n(kz[2]), sk4=n(kz[3]))
     if bufs is not None:
         out["dumps"] = {k_: n(t) for k_, t in bufs.items()}
         out["window"] = dict(window)
@@ -165,12 +167,13 @@ def gpu_call(q, k, v, do, cu, causal_dq=False, softmax_scale=None, window=None, 
 
 def same_outputs(a, b):
     """The debug variant computes exactly what the product library computes."""
-    for nm in ("q", "sq", "k", "sk", "v", "sv", "do", "sdo", "D", "o", "lse", "dq", "dk", "dv", "pi"):
+    for nm in ("q", "sq", "k", "sk", "v", "sv", "do", "sdo", "D", "o", "lse", "dq", "dk", "dv", "pi") + \
+            (("q4", "sq4", "k4", "sk4") if a.get("qk4") else ()):
         assert np.array_equal(a[nm].view(np.uint8), b[nm].view(np.uint8)), nm
 
 
 def oracle_call(orc, q, k, v, do, cu, causal_dq=False, softmax_scale=None, docs=None, kv_heads=None,
-                tail_rows=0, tail_blocks=0, causal=True, hadamard=False):
+                tail_rows=0, tail_blocks=0, causal=True, hadamard=False, qk4=False):
     """The oracle's own end-to-end chain on the BF16 inputs (hadamard: Q, K rotated before
     quantisation, dQ, dK rotated back)."""
     cu = np.asarray(cu, np.int32)
@@ -178,11 +181,16 @@ def oracle_call(orc, q, k, v, do, cu, causal_dq=False, softmax_scale=None, docs=
     for name, x in (("q", q), ("k", k), ("v", v)):
         c, s = orc.quantize(bf16_bits(x), cu, hadamard=hadamard and name in ("q", "k"))
         out[name], out["s" + name] = c, s
+    four = None
+    if qk4:
+        q4, k4 = (orc.quantize_mx4(bf16_bits(x), cu, hadamard=hadamard) for x in (q, k))
+        four = (q4[0], q4[1], k4[0], k4[1])
+        out.update(q4=q4[0], sq4=q4[1], k4=k4[0], sk4=k4[1])
     o, lse, _ = orc.fwd(out["q"], out["sq"], out["k"], out["sk"], out["v"], out["sv"], cu, softmax_scale,
-                        docs=docs, kv_heads=kv_heads, tail_rows=tail_rows, causal=causal)
+                        docs=docs, kv_heads=kv_heads, tail_rows=tail_rows, causal=causal, qk4=four)
     dc, dsc, D = orc.quantize_do(bf16_bits(do), o, cu)
     g = orc.bwd(out["q"], out["sq"], out["k"], out["sk"], out["v"], out["sv"], dc, dsc, lse, D, cu, softmax_scale,
-                causal_dq=causal_dq, docs=docs, kv_heads=kv_heads, tail_blocks=tail_blocks, causal=causal)
+                causal_dq=causal_dq, docs=docs, kv_heads=kv_heads, tail_blocks=tail_blocks, causal=causal, qk4=four)
     out.update(do=dc, sdo=dsc, D=D, o=o, lse=lse, dq=g["dq"], dk=g["dk"], dv=g["dv"], pi=g["pi"])
     if hadamard:
         out["dq_rot"], out["dk_rot"] = out["dq"], out["dk"]
@@ -314,6 +322,51 @@ def check_block_exponents(name, got_e, vals, vis, orc):
     return n_bad
 
 
+def check_group_exponents(PS, S, M, c32, vis, cu, win, orc, causal=True):
+    """4-bit scores: per (head, row, 128-key tile, 32-key group of the document) the exponent
+    byte is the same for every visible key and equals the round-up exponent of
+    2^(fma(max S over the group's visible keys, c, -m)) (the log-domain rule: the group's
+    largest probability from its largest score), or one off with that value within EXP_REL of the
+    boundary between them.  Returns the number at a boundary."""
+    dm = doc_map(cu, max(win["row_hi"], win["key_hi"]))
+    n_bad = 0
+    for doc in sorted(set(dm[win["row_lo"]:win["row_hi"]]) - {-1}):
+        a, b = int(cu[doc]), int(cu[doc + 1])
+        r0, r1 = max(a, win["row_lo"]), min(b, win["row_hi"])
+        rs, ks = slice(r0 - win["row_lo"], r1 - win["row_lo"]), slice(a - win["key_lo"], b - win["key_lo"])
+        L = b - a
+        ng = -(-L // 32)
+        v = np.zeros(vis[rs, ks].shape[:1] + (ng * 32,), bool)
+        v[:, :L] = vis[rs, ks]
+        s = np.full(PS[:, rs, ks].shape[:2] + (ng * 32,), -np.inf, np.float32)
+        s[..., :L] = np.where(vis[rs, ks], S[:, rs, ks], -np.inf)
+        e = np.full(s.shape, -1, np.int64)
+        e[..., :L] = PS[:, rs, ks]
+        vg = v.reshape(v.shape[0], ng, 32)
+        sg = s.reshape(s.shape[0], s.shape[1], ng, 32)
+        eg = e.reshape(e.shape[0], e.shape[1], ng, 32)
+        anyv = vg.any(-1)[None]
+        gmax_e = np.where(vg[None], eg, -1).max(-1)
+        gmin_e = np.where(vg[None], eg, 999).min(-1)
+        assert np.array_equal(gmax_e[np.broadcast_to(anyv, gmax_e.shape)], gmin_e[np.broadcast_to(anyv, gmin_e.shape)]), \
+            "group exponent not constant"
+        gs = sg.max(-1)                                            # [h, r, ng] largest visible score
+        m = np.stack([M[:, rs, ks][..., min(32 * j, L - 1)] for j in range(ng)], -1)   # the tile's running max
+        with np.errstate(invalid="ignore", over="ignore"):
+            pmax = np.exp2(fma32(gs, c32, (-m).astype(np.float32)).astype(np.float64))
+        pmax = np.where(np.isfinite(gs), pmax, 0.0)
+        e_ref = orc.e8m0_roundup(pmax) + 127
+        sel = np.broadcast_to(anyv, gmax_e.shape)
+        bad = sel & (gmax_e != e_ref)
+        if bad.any():
+            lo = np.minimum(gmax_e[bad], e_ref[bad]) - 127
+            near = (np.abs(gmax_e[bad] - e_ref[bad]) == 1) & (np.abs(pmax[bad] - 448.0 * 2.0 ** lo) <= EXP_REL * pmax[bad])
+            say("    group exponents: %d differ from the round-up, all at a boundary: %s" % (int(bad.sum()), bool(near.all())))
+            assert near.all(), "group exponents"
+            n_bad += int(bad.sum())
+    return n_bad
+
+
 def validate_forward(orc, g, cu, softmax_scale=None):
     """Checks 1-5 above for the forward: C1 (against the backward's dump), scores, running maxima,
     probability codes, and O / LSE against the oracle's replay on the GPU's decisions."""
@@ -335,8 +388,12 @@ def validate_forward(orc, g, cu, softmax_scale=None):
         % (int(written.sum()), same))
     assert same
     assert (written[:, vis] if written.ndim == 3 else written).all(), "a visible pair was not visited"
-    # 2. scores against the exact dot products of the codes
-    qd, kd = dequant(g["q"], g["sq"]), dequant(g["k"], g["sk"])
+    # 2. scores against the exact dot products of the codes (4-bit scores: of the 4-bit copies)
+    qk4 = g.get("qk4", False)
+    if qk4:
+        qd, kd = dequant4(g["q4"], g["sq4"]), dequant4(g["k4"], g["sk4"])
+    else:
+        qd, kd = dequant(g["q"], g["sq"]), dequant(g["k"], g["sk"])
     worst = 0.0
     for x, h in enumerate(hs):
         ex = qd[rows, h] @ kd[keys, h // grp].T
@@ -372,16 +429,31 @@ def validate_forward(orc, g, cu, softmax_scale=None):
         assert np.array_equal(got[:, v_doc].view(np.uint32), want[:, v_doc].view(np.uint32)), "running maximum"
         n_m += int(v_doc.sum()) * len(hs)
     say("  running maxima: %d pairs, all equal to the FP32 recomputation" % n_m)
-    # 4. probability codes: E4M3 of 2^(fma(S, c, 8 - m)) (FP32 argument, exact exponential)
-    bias = (np.float32(8.0) - M).astype(np.float32)
+    # 4. probability codes: E4M3 of 2^(fma(S, c, 8 - m)) (FP32 argument, exact exponential);
+    # 4-bit scores: of 2^(fma(S, c, -m)) 2^-e with e the code's 32-key group exponent (PS), which
+    # must be the round-up exponent of the group's largest such value, found from its largest S
+    PS = du["fwd_ps"] if qk4 else None
+    bias = (-M if qk4 else np.float32(8.0) - M).astype(np.float32)
     with np.errstate(invalid="ignore", over="ignore"):
         y = np.exp2(fma32(S, c32, bias).astype(np.float64))
     y = np.where(np.broadcast_to(vis, y.shape), y, 0.0)
-    nbad, ntot = check_decision("probability codes", P, y, orc, np.broadcast_to(vis, P.shape))
+    lo_ok = None
+    if qk4:
+        n_ge = check_group_exponents(PS, S, M, c32, vis, cu, win, orc, causal)
+        say("  group exponents: %d at a boundary, the rest equal the oracle's round-up" % n_ge)
+        # the hardware exponential returns +0 below FP32's normal range; the group exponent can
+        # lift such a probability to E4M3 resolution, so a zero code is accepted there (the term
+        # is below 2^-126 |V| against a row sum of at least 1)
+        lo_ok = (y < 2.0 ** -126) & (orc.e4m3_decode(P) == 0)
+        y = y * np.exp2(127.0 - PS.astype(np.float64))
+        n_tiny = int((lo_ok & np.broadcast_to(vis, P.shape) & (orc.e4m3_decode(orc.e4m3_rne(y)) != 0)).sum())
+        if n_tiny:
+            say("  %d probability codes zero where p is below FP32's normal range (accepted)" % n_tiny)
+    nbad, ntot = check_decision("probability codes", P, y, orc, np.broadcast_to(vis, P.shape), lo_ok=lo_ok)
     say("  probability codes: %d / %d at a rounding boundary, the rest equal the oracle's rounding" % (nbad, ntot))
     # 5. products: O and LSE against the replay on the GPU's decisions
     o64, lse64 = orc.fwd_replay(g["v"], g["sv"], cu, win, S.astype(np.float64), M.astype(np.float64), P, Hq,
-                                float(c32), causal=causal)
+                                float(c32), causal=causal, PS=PS)
     rmask = dm[win["row_lo"]:win["row_hi"]] >= 0
     got_o = np.transpose(g["o"][rows][:, win["head_lo"]:win["head_hi"]], (1, 0, 2))
     beyond = bar_check("O", got_o[:, rmask], o64[:, rmask], orc)
@@ -694,7 +766,7 @@ def chain_check(orc, g, ref, cu, fwd_val, bwd_val, zero_in_exact=()):
     decisions account for (replay minus oracle).  zero_in_exact: outputs that vanish in exact
     arithmetic (rounding-level values: cosine undefined, not gated)."""
     win = g["window"]
-    for nm in ("q", "sq", "k", "sk", "v", "sv", "do", "sdo", "pi"):
+    for nm in ("q", "sq", "k", "sk", "v", "sv", "do", "sdo", "pi") + (("q4", "sq4", "k4", "sk4") if g.get("qk4") else ()):
         assert np.array_equal(g[nm], ref[nm]), nm
     T = g["q"].shape[0]
     dm = doc_map(cu, T)
@@ -762,14 +834,14 @@ def doc_window(cu, doc, heads, tail_blocks=0):
 
 
 def stage_and_chain(orc, q, k, v, do, cu, window, causal_dq=False, release=None, tail=False, zero_in_exact=(),
-                    causal=True, hadamard=False):
+                    causal=True, hadamard=False, qk4=False):
     """Debug run in `window` (compared bit for bit with the product library's run `release`, made
     here if not given), decision checks and replays (stage), then the oracle's own chain (its
     work restricted to the window's documents, KV heads and, with tail=True, document tail)."""
     cu = np.asarray(cu, np.int32)
     if release is None:
-        release = gpu_call(q, k, v, do, cu, causal_dq, causal=causal, hadamard=hadamard)
-    g = gpu_call(q, k, v, do, cu, causal_dq, window=window, causal=causal, hadamard=hadamard)
+        release = gpu_call(q, k, v, do, cu, causal_dq, causal=causal, hadamard=hadamard, qk4=qk4)
+    g = gpu_call(q, k, v, do, cu, causal_dq, window=window, causal=causal, hadamard=hadamard, qk4=qk4)
     same_outputs(g, release)
     say("  debug variant: outputs bit-identical to libflamia.so")
     fv = validate_forward(orc, g, cu)
@@ -783,7 +855,7 @@ def stage_and_chain(orc, q, k, v, do, cu, window, causal_dq=False, release=None,
     if tail:
         tr = window["row_hi"] - window["row_lo"]
         kw.update(tail_rows=tr, tail_blocks=-(-tr // 32))
-    ref = oracle_call(orc, q, k, v, do, cu, causal_dq, causal=causal, hadamard=hadamard, **kw)
+    ref = oracle_call(orc, q, k, v, do, cu, causal_dq, causal=causal, hadamard=hadamard, qk4=qk4, **kw)
     if hadamard:  # the GPU run above returns dQ, dK in the rotated basis
         ref["dq"], ref["dk"] = ref["dq_rot"], ref["dk_rot"]
     chain_check(orc, g, ref, cu, fv, bv, zero_in_exact)

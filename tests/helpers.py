@@ -33,6 +33,18 @@ def dequant(codes, scales):
     return v * np.exp2(e.astype(np.float64))
 
 
+_E2M1 = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0, -0.0, -0.5, -1.0, -1.5, -2.0, -3.0, -4.0, -6.0])
+
+
+def dequant4(codes, scales):
+    """4-bit copy -> float64 [T,H,d]: codes [T,H,d/2] u8 (even channel in the low nibble, E2M1
+    per the OCP table), scales [H,T,d/32] u8 (one E8M0 byte per 32 channels)."""
+    T, H, d2 = codes.shape
+    nib = np.stack([codes & 15, codes >> 4], -1).reshape(T, H, 2 * d2)
+    e = np.repeat(scales.transpose(1, 0, 2).astype(np.int64) - 127, 32, axis=2)
+    return _E2M1[nib] * np.exp2(e.astype(np.float64))
+
+
 def exact_attention(q, k, v, cu, softmax_scale, do=None, causal=True):
     """Softmax attention per document (causal, or every key of the document), FP64, GQA by
     contiguous head groups.

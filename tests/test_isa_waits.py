@@ -10,10 +10,11 @@ from precision_causal_attention_token_amd import build
 from tests import isa_waits
 
 # (source, symbol pattern, instantiations: head dims 64 and 128, times causal and non-causal for
-# the forward and key-tile kernels (and the causal precision-option variants of both), times the
-# forward's two workgroup shapes; the precision options' dQ kernel per head dim)
-KERNELS = [("attn_fwd.hip", r"_ZN6flamia12_GLOBAL__N_110fwd_kernelI\w+", 12),
-           ("attn_bwd.hip", r"_ZN6flamia12_GLOBAL__N_110bwd_kernelI\w+", 6),
+# the forward and key-tile kernels, with and without 4-bit scores (and the causal precision-option
+# variants of both), times the forward's two workgroup shapes; the precision options' dQ kernel
+# per head dim)
+KERNELS = [("attn_fwd.hip", r"_ZN6flamia12_GLOBAL__N_110fwd_kernelI\w+", 20),
+           ("attn_bwd.hip", r"_ZN6flamia12_GLOBAL__N_110bwd_kernelI\w+", 10),
            ("attn_bwd.hip", r"_ZN6flamia12_GLOBAL__N_19dq_kernelI\w+", 2),
            ("attn_dqp.hip", r"_ZN6flamia12_GLOBAL__N_110dqp_kernelI\w+", 2)]
 
