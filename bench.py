@@ -47,6 +47,8 @@ def parse():
                     help="time the non-causal variant (every key of a row's document visible)")
     ap.add_argument("--hadamard", action="store_true",
                     help="rotate Q and K by H / sqrt(d) in the quantiser, dQ and dK back in the backward")
+    ap.add_argument("--qk4", action="store_true",
+                    help="time the 4-bit score path (MXFP4 copy of Q and K, log-domain probability operand)")
     ap.add_argument("--precise", action="store_true",
                     help="time the precision options (per-token scales, folded exponents, row-wise dS exponents)")
     ap.add_argument("--store-gb", type=float, default=None,
@@ -134,7 +136,7 @@ def main():
     if args.non_causal and args.causal_dq:
         print("bench.py: the causal dQ prescale applies to causal attention only", file=sys.stderr)
         sys.exit(2)
-    if args.precise and (args.non_causal or args.hadamard):
+    if args.precise and (args.non_causal or args.hadamard or args.qk4):
         print("bench.py: the precision options are timed alone on causal attention", file=sys.stderr)
         sys.exit(2)
     if args.gpus != 1:
@@ -185,14 +187,14 @@ def main():
     def step(evs=None):
         if evs: evs[0].record()
         qz, kz, vz = fl.quantize([q, k, v], cu_d, hadamard=(args.hadamard, args.hadamard, False),
-                                 per_token=args.precise)
+                                 per_token=args.precise, mx4=(args.qk4, args.qk4, False))
         if evs: evs[1].record()
-        o, lse = fl.fwd(qz, kz, vz, cu_d, lists.fwd, causal=causal, precise=args.precise)
+        o, lse = fl.fwd(qz, kz, vz, cu_d, lists.fwd, causal=causal, precise=args.precise, qk4=args.qk4)
         if evs: evs[2].record()
         dc, dsc, D = fl.quantize_do(do, o, cu_d, per_token=args.precise)
         if evs: evs[3].record()
         out = fl.bwd(qz, kz, vz, (dc, dsc), lse, D, cu_d, lists, None, args.causal_dq, workspace=ws, causal=causal,
-                     hadamard=args.hadamard, precise=args.precise)
+                     hadamard=args.hadamard, precise=args.precise, qk4=args.qk4)
         if evs: evs[4].record()
         return out
 
@@ -230,7 +232,8 @@ def main():
     dom_flop = bwd_flop if dom == "bwd" else fwd_flop
     achieved = dom_flop / (stages[dom] * 1e-3) / 1e12
     traffic = None
-    if (dom == "bwd" and causal and not args.hadamard and not args.precise and args.workload == BWD_TRAFFIC["workload"]
+    if (dom == "bwd" and causal and not args.hadamard and not args.precise and not args.qk4
+            and args.workload == BWD_TRAFFIC["workload"]
             and bwd_source_hash() == BWD_TRAFFIC["src"]):
         traffic = BWD_TRAFFIC["read_bytes"] + BWD_TRAFFIC["write_bytes"]
     roofline = {"bound": "mfma",
@@ -240,6 +243,8 @@ def main():
                 "traffic": traffic, "traffic_unit": "bytes per launch"}
     n_qkv = T * (Hq + 2 * Hkv) * d
     qkv_bytes = 3 * n_qkv + T * (Hq + 2 * Hkv)
+    if args.qk4:  # the 4-bit copies of Q and K: d/2 code bytes and d/32 exponent bytes per row
+        qkv_bytes += T * (Hq + Hkv) * (d // 2 + d // 32)
     do_bytes = 5 * T * Hq * d + 5 * T * Hq
     quant = {"qkv_GBps": qkv_bytes / (stages["quantize_qkv"] * 1e-3) / 1e9,
              "do_GBps": do_bytes / (stages["quantize_do"] * 1e-3) / 1e9, "peak_GBps": PEAK_HBM_GBPS}
@@ -252,7 +257,8 @@ def main():
         "vs_baseline": None, "dtype": "mxfp8_e4m3", "data": "synthetic",
         "config": {"workload": args.workload, "T": T, "Hq": Hq, "Hkv": Hkv, "d": d, "docs": len(cu) - 1,
                    "visible_pairs": pairs, "flop_per_step": flop, "causal_dq_scale": bool(args.causal_dq),
-                   "causal": causal, "hadamard": bool(args.hadamard), "precise": bool(args.precise)},
+                   "causal": causal, "hadamard": bool(args.hadamard), "precise": bool(args.precise),
+                   "qk4": bool(args.qk4)},
         "frac_of_peak": value / PEAK_FP8_TFLOPS,
         "roofline": roofline,
         "quantize": quant,
@@ -261,7 +267,7 @@ def main():
         "peak_mem_GB": torch.cuda.max_memory_allocated() / 1e9,
         "bwd_workspace_GB": ws_bytes / 1e9, "bwd_chunks": chunks,
     }
-    if not args.no_cpu_baseline and causal and not args.hadamard and not args.precise:
+    if not args.no_cpu_baseline and causal and not args.hadamard and not args.precise and not args.qk4:
         res["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_pairs)
     print(json.dumps(res), flush=True)
 

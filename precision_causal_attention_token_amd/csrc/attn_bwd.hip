@@ -140,8 +140,15 @@ __device__ __forceinline__ void issue_step_loads(const BwdParams& p, BwdSmem<D>&
   }
   if constexpr (QK4) {
     // the 4-bit Q rows (d/2 bytes each) into buffer b3: one 1 KiB block per consumer wave
-    constexpr int K4B = D / 2, BQ = QT * K4B / 1024, CPR = K4B / 16;
-    if (cw < BQ) {
+    constexpr int K4B = D / 2, BQ = QT * K4B / 1024, CPR = K4B / 16, RQ = 1024 / K4B;
+    if (cw < BQ && QT * qt + QT <= L) {
+      // a tile inside the document: one wave-uniform base, and a lane offset that the block's
+      // row step (16 or 32 rows) leaves unswizzled
+      const int row = lane / CPR;
+      const uint32_t voff = (uint32_t)(row * p.Hq * K4B + 16 * ((lane % CPR) ^ lds_swizzle<K4B>(row)));
+      const uint8_t* base = p.q4 + ((int64_t)(doc_start + QT * qt + cw * RQ) * p.Hq + h) * K4B;
+      dma_load16_sv(base, voff, lds_addr(sm.q4[b3] + cw * 1024));
+    } else if (cw < BQ) {
       const int pos = cw * 64 + lane, row = pos / CPR;
       const int lc = (pos % CPR) ^ lds_swizzle<K4B>(row);
       uint8_t* dst = sm.q4[b3] + cw * 1024;
@@ -390,12 +397,16 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
         // A scales: the block bytes, or PRECISE the row's Q exponent for both products
         const int sq_a = PRECISE ? (int)sm.rt.pr.sqr[bb][32 * qb + n] : sm.sqdo[bb][qb].x;
         const int sdo_a = PRECISE ? sq_a : sm.sqdo[bb][qb].y;
+        int sq4p[NC];
+        if constexpr (QK4)
+#pragma unroll
+          for (int cc = 0; cc < NC; ++cc) sq4p[cc] = sm.rt.sq4[st % 3][(32 * qb + n) * (D / 32) + 2 * cc + hh];
 #pragma unroll
         for (int cc = 0; cc < NC; ++cc) {
           if constexpr (QK4) {
             const int b3 = st % 3, row = 32 * qb + n;
             const v4i aq = lds_read_row16<D / 2>(sm.q4[b3], row, 32 * cc + 16 * hh);
-            sa = mfma_scaled_fp4(aq, kreg4[cc], cc ? sa : v16f{}, sm.rt.sq4[b3][row * (D / 32) + 2 * cc + hh], ks4[cc]);
+            sa = mfma_scaled_fp4(aq, kreg4[cc], cc ? sa : v16f{}, sq4p[cc], ks4[cc]);
           } else {
             const v8i aq = lds_read_row32<D>(sm.q[bb], 32 * qb + n, 64 * cc + 32 * hh);
             sa = mfma_scaled(aq, kreg[cc], cc ? sa : v16f{}, sq_a, k_scale);

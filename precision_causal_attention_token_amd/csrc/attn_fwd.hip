@@ -176,6 +176,49 @@ __device__ __forceinline__ uint32_t issue_tile4(const FwdParams& p, FwdSmem<D>& 
   return sc;
 }
 
+// A tile wholly inside the document (every tile after a unit's first), 4-bit scores: each block
+// is one wave-uniform base address plus a per-lane offset.  Within a K block the row step of
+// the block leaves the swizzle unchanged (rows 16 or 32 apart), so one K offset serves every
+// block; V blocks take issue_full_tile's offset with the swizzle of their row step.
+template <int D, int W>
+__device__ __forceinline__ uint32_t issue_full_tile4(const FwdParams& p, FwdSmem<D>& sm, int kb, int vb, int g,
+                                                     int doc_start, int kappa, int wave, uint32_t voff_k,
+                                                     uint32_t voff_v) {
+  constexpr int K4B = D / 2, BK = KV_TILE * K4B / 1024, BV = KV_TILE * D / 1024;
+  constexpr int RK = 1024 / K4B, RV = 1024 / D;  // rows per block
+  const int64_t row0 = doc_start + KV_TILE * kappa;
+  for (int wb = __builtin_amdgcn_readfirstlane(wave); wb < BK + BV; wb += W) {
+    if (wb < BK) {
+      const uint8_t* base = p.k4 + ((row0 + wb * RK) * p.Hkv + g) * K4B;
+      dma_load16_sv(base, voff_k, lds_addr(sm.k[kb] + wb * 1024));
+    } else {
+      const int blk = wb - BK;
+      const uint8_t* base = p.v + ((row0 + blk * RV) * p.Hkv + g) * D;
+      dma_load16_sv(base, voff_v ^ (16 * lds_swizzle<D>(blk * RV)), lds_addr(sm.v[vb] + blk * 1024));
+    }
+  }
+  const int tid = threadIdx.x;
+  uint32_t sc = 127;
+  if (tid < 2 * KV_TILE) {
+    const int64_t key = row0 + (tid & (KV_TILE - 1));
+    if (tid < KV_TILE) {
+      const uint8_t* e4 = p.sk4 + ((int64_t)g * p.T + key) * (D / 32);
+      sc = D == 128 ? *reinterpret_cast<const uint32_t*>(e4) : (uint32_t)*reinterpret_cast<const uint16_t*>(e4);
+    } else {
+      sc = p.sv[(int64_t)g * p.T + key];
+    }
+  }
+  return sc;
+}
+// Per-lane byte offset, from its block's first row, of the chunk the lane fetches in a 4-bit K
+// block of a full tile.
+template <int D>
+__device__ __forceinline__ uint32_t tile_offset4(const FwdParams& p, int lane) {
+  constexpr int K4B = D / 2, CPR = K4B / 16;
+  const int row = lane / CPR, pc = lane % CPR;
+  return (uint32_t)(row * p.Hkv * K4B + 16 * (pc ^ lds_swizzle<K4B>(row)));
+}
+
 template <int D>
 __device__ __forceinline__ void store_scales4(FwdSmem<D>& sm, int kb, int vb, uint32_t sc) {
   const int tid = threadIdx.x;
@@ -223,6 +266,7 @@ __global__ __launch_bounds__(fwd_threads<W>(), 8 / W) void fwd_kernel(FwdParams 
   const int grp = p.Hq / p.Hkv;
   const float c = p.c;
   const uint32_t voff0 = tile_offset<D>(p, lane);
+  const uint32_t voff4 = QK4 ? tile_offset4<D>(p, lane) : 0u;
 
   for (int round = 0;; ++round) {
     const int u = round * G + ((round & 1) ? (G - 1 - wg) : wg);
@@ -298,7 +342,7 @@ __global__ __launch_bounds__(fwd_threads<W>(), 8 / W) void fwd_kernel(FwdParams 
       const int kb = it & 1;
       uint32_t scn = 127;
       if (kappa > 0) {
-        if constexpr (QK4) scn = issue_tile4<D, W>(p, sm, kb ^ 1, kb ^ 1, g, doc_start, L, kappa - 1, wave, lane);
+        if constexpr (QK4) scn = issue_full_tile4<D, W>(p, sm, kb ^ 1, kb ^ 1, g, doc_start, kappa - 1, wave, voff4, voff0);
         else scn = issue_full_tile<D, W>(p, sm, kb ^ 1, kb ^ 1, g, doc_start, kappa - 1, wave, voff0);
       }
       if (wave_active && kappa <= kd) {
@@ -315,11 +359,13 @@ __global__ __launch_bounds__(fwd_threads<W>(), 8 / W) void fwd_kernel(FwdParams 
           v4i kring[SAHEAD];
 #pragma unroll
           for (int k = 0; k < SAHEAD; ++k) kring[k] = read_k(k);
+          int ks[NS];  // all read ahead: an instruction never waits for its scale byte
+#pragma unroll
+          for (int k = 0; k < NS; ++k) ks[k] = sm.sk4[kb][(32 * (k / NC) + n) * (D / 32) + 2 * (k % NC) + hh];
 #pragma unroll
           for (int k = 0; k < NS; ++k) {
             const int kb4 = k / NC, cc = k % NC;
-            const int ks = sm.sk4[kb][(32 * kb4 + n) * (D / 32) + 2 * cc + hh];
-            s[kb4] = mfma_scaled_fp4(kring[k % SAHEAD], qop4[cc], cc ? s[kb4] : v16f{}, ks, q_scale4[cc]);
+            s[kb4] = mfma_scaled_fp4(kring[k % SAHEAD], qop4[cc], cc ? s[kb4] : v16f{}, ks[k], q_scale4[cc]);
             if (k + SAHEAD < NS) kring[k % SAHEAD] = read_k(k + SAHEAD);
             __builtin_amdgcn_sched_barrier(0);
           }

@@ -60,15 +60,11 @@ __device__ __forceinline__ void hadamard_row(float (&v)[8], int lc) {
 #pragma unroll
   for (int e = 0; e < 8; ++e) v[e] = __fmul_rn(v[e], c);
 }
-// E2M1 (values 0, 0.5, 1, 1.5, 2, 3, 4, 6) of a finite float, round to nearest even, the sign
-// kept on zero, saturating at 6 (never reached under the round-up exponent): the magnitude code
-// counts the thresholds passed, each midpoint going to the neighbour whose mantissa bit is 0.
-__device__ __forceinline__ uint32_t e2m1_rne(float y) {
-  const float a = fabsf(y);
-  const uint32_t c = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
-                     (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) + (uint32_t)(a > 5.0f);
-  return c | ((__float_as_uint(y) >> 28) & 8u);
-}
+// E2M1 codes (values 0, 0.5, 1, 1.5, 2, 3, 4, 6) come from the hardware conversion
+// v_cvt_scalef32_pk_fp4_f32 with scale 1 on values already scaled exactly by 2^-s: it rounds to
+// nearest even and keeps the sign on zero (checked on the hardware against the definition,
+// every midpoint and its float neighbours included); values never exceed 6 under the round-up
+// exponent.
 // Smallest s with amax <= 6 2^s for amax = 1.f 2^E (f in [1, 2)): s = E - 2 + (f > 1.5); adding
 // 2^22 - 1 carries into the exponent field exactly when the mantissa exceeds 0.5.  Clamped to
 // >= -127 (zero and subnormal amax).
@@ -253,10 +249,12 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantParams p) {
         m = fmaxf(m, dpp<0xB1>(m));
         m = fmaxf(m, dpp<0x4E>(m));
         const int s4 = e2m1_exponent(m);
-        const float f = exp2i_neg(s4);
+        const float f = exp2i_neg(s4);  // exact scaling here; the conversion then takes scale 1
         uint32_t w = 0;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) w |= e2m1_rne(v[e] * f) << (4 * e);
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[0] * f, v[1] * f, 1.0f, 0);
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[2] * f, v[3] * f, 1.0f, 1);
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[4] * f, v[5] * f, 1.0f, 2);
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[6] * f, v[7] * f, 1.0f, 3);
         *reinterpret_cast<uint32_t*>(X.codes4 + (tau * X.H + h) * (D / 2) + 4 * lc) = w;
         if ((lc & 3) == 0) X.scales4[((int64_t)h * T + tau) * (D / 32) + lc / 4] = (uint8_t)(s4 + 127);
       }
