@@ -33,7 +33,7 @@ PEAK_HBM_GBPS = 8000.0       # MI355X HBM3E
 # scaled by 2.000 and WRITE by 1.000, the factors a 1 GiB copy gives).  Valid only for the
 # backward sources it was measured on (sha256 prefix over attn_bwd.hip, device_common.h,
 # kernels.h); any other build reports null.
-BWD_TRAFFIC = {"workload": "long", "src": "6ff6eb138850b3aa", "read_bytes": 18.104e9, "write_bytes": 13.067e9}
+BWD_TRAFFIC = {"workload": "long", "src": "530b12c004f7c5d2", "read_bytes": 18.116e9, "write_bytes": 13.065e9}
 
 
 def parse():
