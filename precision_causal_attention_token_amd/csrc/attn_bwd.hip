@@ -422,12 +422,13 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
       // one matrix instruction, the operand read of the next one and a slice of the softmax
       // elements, so the matrix unit works while the vector unit does, and only one operand is
       // in flight at a time.
+      // bp, bs: the step buffers of the products' and the softmax's steps (constants of the
+      // unrolled phase loop, so the buffer offsets fold into the LDS instructions)
       auto fused = [&](int sp_st, int qp, v16f& ns, v16f& np, int ss, int qs, int q0, int sh, v16f& sa, v16f& pa,
-                       int* pp4, int* pd4, uint32_t& sp, uint32_t& sds, auto masked) {
+                       int* pp4, int* pd4, uint32_t& sp, uint32_t& sds, auto masked, int bp, int bs) {
         constexpr bool MASK = decltype(masked)::value;
         constexpr int NM = 2 * NC;     // matrix instructions of the products
         constexpr int EPM = 16 / NM;   // softmax elements per chunk
-        const int bp = sp_st & (NBUF - 1), bs = ss & (NBUF - 1);
         float4 lse4[4];  // rows acc_row(4 j + e, hh) = 32 qs + 8 j + 4 hh + e
 #pragma unroll
         for (int j = 0; j < 4; ++j)
@@ -515,12 +516,15 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
           }
           __builtin_amdgcn_sched_barrier(0);
         }
-        sp = e8m0_byte_nonneg(wave_max_nonneg(pmax));  // E8M0 bytes of the block exponents
-        sds = e8m0_byte_nonneg(wave_max_nonneg(dmax));
+        float fp, fd;  // the scales 2^(byte - 127)
+        float pm, dm;
+        wave_max2_nonneg(pmax, dmax, pm, dm);
+        sp = e8m0_byte_uniform(pm, fp);  // E8M0 bytes of the block exponents
+        sds = e8m0_byte_uniform(dm, fd);
 #pragma unroll
         for (int w4 = 0; w4 < 4; ++w4) {
-          pp4[w4] = pack4_fp8_scaled(sa[4 * w4], sa[4 * w4 + 1], sa[4 * w4 + 2], sa[4 * w4 + 3], sp);
-          pd4[w4] = pack4_fp8_scaled(pa[4 * w4], pa[4 * w4 + 1], pa[4 * w4 + 2], pa[4 * w4 + 3], sds);
+          pp4[w4] = pack4_fp8_scalef(sa[4 * w4], sa[4 * w4 + 1], sa[4 * w4 + 2], sa[4 * w4 + 3], fp);
+          pd4[w4] = pack4_fp8_scalef(pa[4 * w4], pa[4 * w4 + 1], pa[4 * w4 + 2], pa[4 * w4 + 3], fd);
         }
 #ifdef FLAMIA_DEBUG_DUMP
         if (p.dbg.bwd_p || p.dbg.bwd_ds) {  // test builds: codes and block exponent bytes
@@ -536,14 +540,16 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
         }
 #endif
       };
-      // Phase ph works on step ph.  Block 0's products were made in the phase before (cs, cp);
-      // block 1's are issued while block 0's softmax terms are formed, and block 0 of the next
-      // step while block 1's are.  The last step has no successor: it recomputes its own
-      // block 0, which is not used.
+      // Phase ph works on step ph (step buffer BB = ph mod 4, a constant of the unrolled loop).
+      // Block 0's products were made in the phase before (cs, cp); block 1's are issued while
+      // block 0's softmax terms are formed, and block 0 of the next step while block 1's are.
+      // The last step has no successor: its block-0 products read the next buffer's stale tiles
+      // (finite, or whatever LDS held) into registers that are never used.
       v16f cs, cp, xs, xq;
-      auto phase_body = [&](int ph, int h, int qt, auto masked) {
+      auto phase_body = [&](int ph, int h, int qt, auto masked, auto BB) {
+        constexpr int bb = decltype(BB)::value, bn = (bb + 1) & (NBUF - 1);
         const int q0 = QT * qt;
-        const int x2 = ph & 1;
+        constexpr int x2 = bb & 1;
         int pp[8], pd[8];
         uint32_t sp[2], sds[2];  // E8M0 bytes
         // hand over query block qb's operands as soon as they exist, so the writes retire under
@@ -563,12 +569,12 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
             }
           }
         };
-        fused(ph, 1, xs, xq, ph, 0, q0, h, cs, cp, pp, pd, sp[0], sds[0], masked);
+        fused(ph, 1, xs, xq, ph, 0, q0, h, cs, cp, pp, pd, sp[0], sds[0], masked, bb, bb);
         // empty uses of freshly issued products keep their matrix instructions among the vector
         // work they overlap, instead of sunk past the hand-over towards their next use
         asm volatile("" ::"v"(xs), "v"(xq));
         hand_over(0);
-        fused(min(ph + 1, n_steps - 1), 0, cs, cp, ph, 1, q0, h, xs, xq, pp + 4, pd + 4, sp[1], sds[1], masked);
+        fused(min(ph + 1, n_steps - 1), 0, cs, cp, ph, 1, q0, h, xs, xq, pp + 4, pd + 4, sp[1], sds[1], masked, bn, bb);
         asm volatile("" ::"v"(cs), "v"(cp));
         hand_over(1);
         if (lane == 0) {
@@ -589,19 +595,29 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_kernel(BwdParams p) {
       // document and, causally, below the key tile (then every key of the tile is inside the
       // document too) or, non-causally, when the key tile is wholly inside it as well
       const bool keys_full = !CAUSAL && KV_TILE * kappa + KV_TILE <= L;
-      for (int ph = 0; ph <= n_steps; ++ph) {
+      // phase ph, or false past the last one (n_steps + 1 phases, one barrier each)
+      auto phase = [&](int ph, auto BB) {
+        if (ph > n_steps) return false;
         if (ph < n_steps) {
           // all 64 x 128 pairs visible: the query tile lies wholly below the key tile and
           // inside the document (then every key of the tile is inside it too)
           if ((CAUSAL ? cur_qt >= 2 * kappa + 2 : keys_full) && QT * cur_qt + QT <= L)
-            phase_body(ph, cur_h, cur_qt, std::false_type{});
-          else phase_body(ph, cur_h, cur_qt, std::true_type{});
+            phase_body(ph, cur_h, cur_qt, std::false_type{}, BB);
+          else phase_body(ph, cur_h, cur_qt, std::true_type{}, BB);
           if (++cur_qt == n_qt) {
             cur_qt = qt_first;
             ++cur_h;
           }
         }
         lds_barrier();  // phase done: operands handed over, the next tiles in place
+        return true;
+      };
+      static_assert(NBUF == 4, "the phase loop is unrolled over the four step buffers");
+      for (int ph = 0;; ph += NBUF) {
+        if (!phase(ph, std::integral_constant<int, 0>{})) break;
+        if (!phase(ph + 1, std::integral_constant<int, 1>{})) break;
+        if (!phase(ph + 2, std::integral_constant<int, 2>{})) break;
+        if (!phase(ph + 3, std::integral_constant<int, 3>{})) break;
       }
     } else {
       // lane-dependent values re-derived from an opaque copy of the lane index: addresses

@@ -225,6 +225,17 @@ __device__ __forceinline__ uint32_t e8m0_byte_nonneg(float amax) {
   if (b >= 0x7F800000u) return 255;  // infinity or NaN
   return max((b + 0x1FFFFFu) >> 23, 8u) - 8u;
 }
+// The same for a wave-uniform maximum, in scalar instructions, with the scale 2^(byte - 127) as a
+// float beside the byte (the scaled conversions take it from a scalar register).
+__device__ __forceinline__ uint32_t e8m0_byte_uniform(float amax, float& scale) {
+  const uint32_t b = (uint32_t)__builtin_amdgcn_readfirstlane((int)__float_as_uint(amax));
+  const uint32_t e = (b + 0x1FFFFFu) >> 23;
+  uint32_t r = e > 8u ? e - 8u : 0u;
+  r = b >= 0x7F800000u ? 255u : r;  // infinity or NaN
+  r = (uint32_t)__builtin_amdgcn_readfirstlane((int)r);
+  scale = __uint_as_float((uint32_t)__builtin_amdgcn_readfirstlane((int)(r << 23)));
+  return r;
+}
 // 2^-s as a float, for s in [-127, 127].
 __device__ __forceinline__ float exp2i_neg(int s) { return __uint_as_float((uint32_t)(127 - s) << 23); }
 __device__ __forceinline__ float exp2i(int s) { return __uint_as_float((uint32_t)(127 + s) << 23); }
@@ -247,6 +258,11 @@ __device__ __forceinline__ int pack4_fp8(float a0, float a1, float a2, float a3)
 // (checked on the hardware for every exponent).
 // The scale is given as its E8M0 byte s + 127.
 typedef short v2s __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ int pack4_fp8_scalef(float a0, float a1, float a2, float a3, float scale) {
+  const v2s lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(__builtin_bit_cast(v2s, a0), a0, a1, scale, false);
+  const v2s r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lo, a2, a3, scale, true);
+  return __builtin_bit_cast(int, r);
+}
 __device__ __forceinline__ int pack4_fp8_scaled(float a0, float a1, float a2, float a3, uint32_t sbyte) {
   const float scale = __uint_as_float(sbyte << 23);
   // the first conversion's upper half is overwritten by the second: any value will do there
@@ -271,20 +287,23 @@ __device__ __forceinline__ float wave_max(float x) {
   auto b = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
   return fmaxf(__int_as_float((int)b[0]), __int_as_float((int)b[1]));
 }
-// Maximum over the wave of a non-negative float, as an unsigned maximum of the bit patterns
-// (the same order for non-negative floats).  Four DPP steps give every lane its row's maximum;
-// row_bcast:15 then row_bcast:31 carry the row maxima up to the last row, and lane 63 holds the
-// wave's maximum, returned as a wave-uniform value (so what follows can run on the scalar unit).
-// Each step is one vector instruction: the DPP move folds into the maximum.
-__device__ __forceinline__ float wave_max_nonneg(float x) {
-  uint32_t u = __float_as_uint(x);
+// Maxima over the wave of two non-negative floats a and b at once (unsigned maxima of the bit
+// patterns, the same order for non-negative floats).  One permlane32 swap pairs each value's upper
+// half of the wave with its lower half, so after one maximum lanes 0-31 carry a's partial maxima
+// and lanes 32-63 b's; four DPP steps finish each row of 16 and one permlane16 swap joins the two
+// rows of each half.  Lane 0 then holds a's maximum and lane 32 b's (returned wave-uniform): one
+// chain of cross-lane steps instead of one per value.
+__device__ __forceinline__ void wave_max2_nonneg(float a, float b, float& ma, float& mb) {
+  const auto s = __builtin_amdgcn_permlane32_swap(__float_as_int(a), __float_as_int(b), false, false);
+  uint32_t u = max((uint32_t)s[0], (uint32_t)s[1]);
   u = max(u, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
   u = max(u, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
   u = max(u, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, 0x124, 0xF, 0xF, false));  // row_ror:4
   u = max(u, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, 0x128, 0xF, 0xF, false));  // row_ror:8
-  u = max(u, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, 0x142, 0xA, 0xF, false));  // row_bcast:15, rows 1, 3
-  u = max(u, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, 0x143, 0xC, 0xF, false));  // row_bcast:31, rows 2, 3
-  return __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)u, 63));
+  const auto t = __builtin_amdgcn_permlane16_swap((int)u, (int)u, false, false);
+  u = max((uint32_t)t[0], (uint32_t)t[1]);
+  ma = __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)u, 0));
+  mb = __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)u, 32));
 }
 // Combine the two lane groups (l and l ^ 32).
 __device__ __forceinline__ float halves_max(float x) {
