@@ -33,7 +33,7 @@ PEAK_HBM_GBPS = 8000.0       # MI355X HBM3E
 # scaled by 2.000 and WRITE by 1.000, the factors a 1 GiB copy gives).  Valid only for the
 # backward sources it was measured on (sha256 prefix over attn_bwd.hip, device_common.h,
 # kernels.h); any other build reports null.
-BWD_TRAFFIC = {"workload": "long", "src": "530b12c004f7c5d2", "read_bytes": 18.116e9, "write_bytes": 13.065e9}
+BWD_TRAFFIC = {"workload": "long", "src": "9d1e4ca1d626a003", "read_bytes": 18.087e9, "write_bytes": 13.035e9}
 
 
 def parse():
@@ -181,6 +181,9 @@ def main():
     else:
         ws_bytes = fl.bwd_workspace_bytes(len(cu) - 1, T, Hq, d, int(args.store_gb * (1 << 30)))
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    # the longest document, from the same host lengths: the backward launches its key-tile chunks
+    # for documents no longer than this
+    max_doc_len = int(np.max(np.diff(cu))) if len(cu) > 1 else 0
 
     stage_names = ("quantize_qkv", "fwd", "quantize_do", "bwd")
 
@@ -194,7 +197,7 @@ def main():
         dc, dsc, D = fl.quantize_do(do, o, cu_d, per_token=args.precise)
         if evs: evs[3].record()
         out = fl.bwd(qz, kz, vz, (dc, dsc), lse, D, cu_d, lists, None, args.causal_dq, workspace=ws, causal=causal,
-                     hadamard=args.hadamard, precise=args.precise, qk4=args.qk4)
+                     hadamard=args.hadamard, precise=args.precise, qk4=args.qk4, max_doc_len=max_doc_len)
         if evs: evs[4].record()
         return out
 

@@ -293,6 +293,18 @@ typedef struct {
                                          the recomputed scores take these 4-bit copies, bit for
                                          bit the forward's; dK, dQ keep the 8-bit q, k.  Not with
                                          precise (FLAMIA_ERR_UNSUPPORTED). */
+  int32_t max_doc_len;                /* optional (<= 0: not given): the length of the longest
+                                         document, or any larger number.  The key-tile and dQ
+                                         passes are launched once per chunk that the documents
+                                         could need, counted without the lengths (no copy of
+                                         cu_seqlens reaches the host): for any documents of total
+                                         length T, or with this bound for documents no longer
+                                         than max_doc_len (sum of L^2 <= max_doc_len * T), which
+                                         is most often one chunk and saves the launches that
+                                         would find nothing to do.  A call whose documents need
+                                         more chunks than were launched (a bound below the longest
+                                         document can cause it) sets status word 3 in the
+                                         workspace, and its gradient passes do not run. */
 } flamia_bwd_args;
 
 /* Host.  Backward workspace for n_docs documents of total length T: a header, pi [Hq, T], the
@@ -315,7 +327,9 @@ size_t flamia_bwd_workspace_bytes_for(const int32_t* cu_seqlens_host, int32_t n_
 
 /* Errors: NULL pointers, sizes, d, head ratio, a workspace smaller than
  * flamia_bwd_workspace_bytes(n_docs, T, Hq, d, 0) (FLAMIA_ERR_WORKSPACE).  The status word (first
- * int32 of the workspace) is 0 once the backward has run. */
+ * int32 of the workspace) is 0 once the backward has run, 3 when the documents could not be laid
+ * out in the launched chunks (inconsistent cu_seqlens, or max_doc_len below the longest
+ * document); then the gradient passes do not run. */
 flamia_status flamia_bwd(const flamia_bwd_args* args, void* stream);
 
 /* ------------------------------------------------------------------------------------------

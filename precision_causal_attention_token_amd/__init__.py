@@ -65,7 +65,8 @@ class _BwdArgs(ctypes.Structure):
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
                 ("causal_dq_scale", ctypes.c_int32), ("dq_exp_out", ctypes.c_void_p),
                 ("non_causal", ctypes.c_int32), ("hadamard", ctypes.c_int32), ("precise", ctypes.c_int32),
-                ("q4", ctypes.c_void_p), ("sq4", ctypes.c_void_p), ("k4", ctypes.c_void_p), ("sk4", ctypes.c_void_p)]
+                ("q4", ctypes.c_void_p), ("sq4", ctypes.c_void_p), ("k4", ctypes.c_void_p), ("sk4", ctypes.c_void_p),
+                ("max_doc_len", ctypes.c_int32)]
 
 
 _lib = None
@@ -255,7 +256,8 @@ def bwd_workspace_bytes_for(cu_seqlens_host, T, Hq, d, causal=True):
 
 
 def bwd(q, k, v, do, lse, D, cu_seqlens, lists, softmax_scale=None, causal_dq_scale=False, want_pi=False,
-        workspace=None, static_scratch=False, causal=True, hadamard=False, precise=False, qk4=False):
+        workspace=None, static_scratch=False, causal=True, hadamard=False, precise=False, qk4=False,
+        max_doc_len=0):
     """Backward on quantised operands.  q, k, v, do are (codes, scales) pairs; lse, D f32 [Hq, T];
     lists: the micro-batch's Lists.  workspace: a uint8 CUDA tensor of at least
     bwd_workspace_bytes(n_docs, T, Hq, d, 0) bytes, or None to allocate one with the default
@@ -264,6 +266,9 @@ def bwd(q, k, v, do, lse, D, cu_seqlens, lists, softmax_scale=None, causal_dq_sc
     workspace is allocated or passed).
     hadamard=True: Q and K were quantised rotated; dq and dk are rotated back.
     qk4=True: q and k are quantize(..., mx4=True) tuples; the scores take their 4-bit copies.
+    max_doc_len: a host bound of the longest document (0: none); the key-tile chunks are then
+    launched for documents no longer than it (fewer empty launches).  A bound below the longest
+    document can leave the call unrun: bwd_status(workspace) then reads status 3.
     Returns (dq, dk, dv) BF16, plus the prescale exponents pi int16 [Hq, T] if want_pi."""
     lib = load_library()
     n_docs = _check_cu(cu_seqlens)
@@ -286,7 +291,7 @@ def bwd(q, k, v, do, lse, D, cu_seqlens, lists, softmax_scale=None, causal_dq_sc
                  dv.stride(0), dv.stride(1), workspace.data_ptr() if workspace is not None else None,
                  workspace.numel() if workspace is not None else 0, int(bool(causal_dq_scale)),
                  pi.data_ptr() if pi is not None else None, int(not causal), int(bool(hadamard)),
-                 int(bool(precise)), *four)
+                 int(bool(precise)), *four, int(max_doc_len))
     _check((lib.flamia_bwd_static if static_scratch else lib.flamia_bwd)(ctypes.byref(a), _stream()))
     return (dq, dk, dv, pi) if want_pi else (dq, dk, dv)
 
@@ -308,10 +313,10 @@ class Lists:
 
 
 def training_call(q, k, v, do, cu_seqlens, lists=None, softmax_scale=None, causal_dq_scale=False, causal=True,
-                  hadamard=False, precise=False):
+                  hadamard=False, precise=False, max_doc_len=0):
     """One attention training call: quantise Q, K, V -> forward -> quantise dO (+ D) -> backward.
     precise=True: the precision options (per-token scales in every quantiser pass, the precise
-    forward and backward).  Returns dict with o, lse, dq, dk, dv."""
+    forward and backward).  max_doc_len: as in bwd.  Returns dict with o, lse, dq, dk, dv."""
     T = q.shape[0]
     if lists is None:
         lists = Lists(cu_seqlens, T, causal)
@@ -319,5 +324,5 @@ def training_call(q, k, v, do, cu_seqlens, lists=None, softmax_scale=None, causa
     o, lse = fwd(qz, kz, vz, cu_seqlens, lists.fwd, softmax_scale, causal=causal, precise=precise)
     dc, dsc, D = quantize_do(do, o, cu_seqlens, per_token=precise)
     dq, dk, dv = bwd(qz, kz, vz, (dc, dsc), lse, D, cu_seqlens, lists, softmax_scale, causal_dq_scale,
-                     causal=causal, hadamard=hadamard, precise=precise)
+                     causal=causal, hadamard=hadamard, precise=precise, max_doc_len=max_doc_len)
     return dict(o=o, lse=lse, dq=dq, dk=dk, dv=dv)

@@ -103,6 +103,11 @@ int64_t worst_blocks_nc(int32_t T) {
   const int64_t t = T;
   return (t * t) / 8192 + 5 * t / 64 + 3;
 }
+// The same bounds for documents no longer than M tokens: sum L^2 <= M T.
+int64_t worst_blocks_max(int32_t T, int32_t M, bool non_causal) {
+  const int64_t t = T, m = std::min<int64_t>(M, T);
+  return non_causal ? (m * t) / 8192 + 5 * t / 64 + 3 : (m * t) / 16384 + 5 * t / 128 + 3;
+}
 }  // namespace
 
 extern "C" {
@@ -300,12 +305,15 @@ flamia_status flamia_bwd(const flamia_bwd_args* a, void* stream) {
   p.ds_store = ws + lay.store;
   // Chunks: the store holds cap blocks per query head; a chunk spans chunk_cap = cap - (largest
   // item) blocks of last-block positions, so it never overflows the store; the launches cover
-  // the most chunks any documents of total length T could need (those past the laid-out count
-  // exit at once).
+  // the most chunks any documents of total length T (no longer than max_doc_len, when given)
+  // could need (those past the laid-out count exit at once; a layout that needs more fails with
+  // status 3 in the prologue).
   const int64_t cap = (int64_t)((a->workspace_bytes - lay.store) / DS_BLOCK_BYTES) / a->Hq;
   p.chunk_cap = cap - max_item_blocks(a->T);
   if (p.chunk_cap < max_item_blocks(a->T)) return FLAMIA_ERR_WORKSPACE;
-  const int64_t max_chunks = ((a->non_causal ? worst_blocks_nc(a->T) : worst_blocks(a->T)) - 1) / p.chunk_cap + 1;
+  const int64_t worst = a->max_doc_len > 0 ? worst_blocks_max(a->T, a->max_doc_len, a->non_causal != 0)
+                                           : (a->non_causal ? worst_blocks_nc(a->T) : worst_blocks(a->T));
+  const int64_t max_chunks = (worst - 1) / p.chunk_cap + 1;
   if (max_chunks + 2 > n_chunk_entries(a->T)) return FLAMIA_ERR_WORKSPACE;
   p.max_chunks = (int32_t)max_chunks;
   p.n_tab = (int32_t)n_tiles(a->n_docs, a->T);

@@ -105,14 +105,15 @@ DUMP_U8 = ("fwd_p", "bwd_p", "bwd_ps", "bwd_ds", "bwd_dss", "dq_ds", "dq_dss", "
 
 
 def gpu_call(q, k, v, do, cu, causal_dq=False, softmax_scale=None, window=None, store_budget=None, causal=True,
-             static_scratch=False, hadamard=False, qk4=False):
+             static_scratch=False, hadamard=False, qk4=False, max_doc_len=0):
     """Full training call on the GPU through the C ABI; returns numpy arrays (BF16 outputs as
     bit patterns).  causal=False: non-causal attention within each document.  hadamard=True: Q
     and K quantised rotated; dQ and dK are returned in the rotated basis (the backward's own
     un-rotation is checked on its own).  With `window` (row/key/head bounds) the call runs the debug variant and the
     result also holds its per-pair dumps under "dumps" ([heads][rows][keys]).  store_budget: the
     backward's dShat store (default: the binding's default; 0: the smallest accepted, many
-    chunks); the key-tile chunks run are returned under "chunks"."""
+    chunks); the key-tile chunks run are returned under "chunks".  max_doc_len: the backward's
+    bound of the longest document (0: none)."""
     dev = torch.device("cuda:0")
     cu_d = torch.as_tensor(np.asarray(cu, np.int32)).to(dev)
     T = q.shape[0]
@@ -145,7 +146,7 @@ def gpu_call(q, k, v, do, cu, causal_dq=False, softmax_scale=None, window=None, 
                 status, chunks = 0, None
             else:
                 dq, dk, dv, pi = fl.bwd(qz, kz, vz, (dc, dsc), lse, D, cu_d, lists, softmax_scale, causal_dq,
-                                        want_pi=True, workspace=ws, causal=causal, qk4=qk4)
+                                        want_pi=True, workspace=ws, causal=causal, qk4=qk4, max_doc_len=max_doc_len)
                 torch.cuda.synchronize()
                 status, chunks = fl.bwd_status(ws)
             assert status == 0, 'backward workspace status'

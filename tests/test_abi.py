@@ -3,6 +3,8 @@ its host-side argument checks return the documented statuses.  No kernel is laun
 import ctypes
 import os
 import re
+import shutil
+import subprocess
 
 import numpy as np
 
@@ -114,3 +116,26 @@ def test_list_kinds(lib):
         assert lib.flamia_build_worklist(fake, 1, 1000, kind, 4, fake, 16, None) == 4
     assert lib.flamia_build_worklist(fake, 1, 1000, 4, 4, fake, 1 << 20, None) == 2   # unknown kind
     assert lib.flamia_status_str(6) == b"call too large for the static scratch"
+
+
+@pytest.mark.skipif(not shutil.which("gcc"), reason="gcc not installed")
+def test_binding_structs_match_the_header(tmp_path):
+    """Every argument struct of the Python binding has the C header's layout: the same size and,
+    field by field, the same offsets (the header compiled by gcc, offsetof printed)."""
+    structs = {"flamia_qtensor": fl._QTensor, "flamia_fwd_args": fl._FwdArgs, "flamia_bwd_args": fl._BwdArgs}
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "flamia.h"', "int main(void) {"]
+    for cname, py in structs.items():
+        lines.append('  printf("%s sizeof %%zu\\n", sizeof(%s));' % (cname, cname))
+        for f, _ in py._fields_:
+            lines.append('  printf("%s %s %%zu\\n", offsetof(%s, %s));' % (cname, f, cname, f))
+    lines += ["  return 0;", "}"]
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c99", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    got = dict(l.rsplit(" ", 1) for l in subprocess.run([str(exe)], capture_output=True, text=True,
+                                                        check=True).stdout.splitlines())
+    for cname, py in structs.items():
+        assert int(got[cname + " sizeof"]) == ctypes.sizeof(py), cname
+        for f, _ in py._fields_:
+            assert int(got["%s %s" % (cname, f)]) == getattr(py, f).offset, (cname, f)

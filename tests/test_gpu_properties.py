@@ -122,6 +122,36 @@ def test_chunked_backward_bit_identical(causal_dq):
         assert np.array_equal(one[nm], many[nm]), nm
 
 
+def test_max_doc_len_bound():
+    """The backward's bound of the longest document (fewer chunk launches): with the true longest
+    length the outputs and the chunk count are those of the unbounded call, in the smallest
+    workspace (several chunks) and in a one-chunk store; a bound so low that the launched chunks
+    cannot hold the documents makes the call report status 3 (the gradient passes do not run)."""
+    T, Hq, Hkv, d = 4096, 4, 2, 128
+    cu = np.array([0, 1500, 1501, 1700, 3000, 4096], np.int32)
+    q, k, v, do = workloads.tensors(T, Hq, Hkv, d, seed=731)
+    for budget in (0, 1 << 40):
+        free = gpu_call(q, k, v, do, cu, True, store_budget=budget)
+        bound = gpu_call(q, k, v, do, cu, True, store_budget=budget, max_doc_len=1500)
+        assert free["chunks"] == bound["chunks"]
+        for nm in ("dq", "dk", "dv", "pi"):
+            assert np.array_equal(free[nm], bound[nm]), nm
+        say("max_doc_len = 1500, store budget %d: %d chunk(s), bit-identical" % (budget, free["chunks"]))
+    # too low: launches for documents of at most 200 tokens, the smallest store
+    dev = torch.device("cuda:0")
+    cu_d = torch.as_tensor(cu).to(dev)
+    lists = fl.Lists(cu_d, T, True)
+    qz, kz, vz = fl.quantize([x.to(dev) for x in (q, k, v)], cu_d)
+    o, lse = fl.fwd(qz, kz, vz, cu_d, lists.fwd)
+    dc, dsc, D = fl.quantize_do(do.to(dev), o, cu_d)
+    ws = torch.empty(fl.bwd_workspace_bytes(len(cu) - 1, T, Hq, d, 0), dtype=torch.uint8, device=dev)
+    dq, dk, dv = fl.bwd(qz, kz, vz, (dc, dsc), lse, D, cu_d, lists, workspace=ws, max_doc_len=200)
+    torch.cuda.synchronize()
+    status, _ = fl.bwd_status(ws)
+    assert status == 3
+    say("max_doc_len = 200 below the 1500-token document: status %d" % status)
+
+
 def test_chunked_backward_long_document():
     """The 65536-token workload's documents with a 1 GiB store (several chunks, one 29368-token
     document spread over them) against one chunk: dQ, dK, dV bit-identical."""
