@@ -65,6 +65,17 @@ def test_mx4_parity(orc, case):
     gc.stage_and_chain(orc, q, k, v, do, cu, gc.full_window(T, Hq), causal=causal, qk4=True)
 
 
+def test_mx4_with_rotation(orc):
+    """4-bit copies of rotated Q and K (the rotation inside the quantiser, before both copies):
+    stage and chain against the oracle's rotated 4-bit chain (dQ, dK compared in the rotated
+    basis, as the other rotation tests do)."""
+    T, Hq, Hkv, d = 1100, 4, 2, 128
+    cu = np.array([0, 300, 301, 700, 1100], np.int32)
+    q, k, v, do = workloads.tensors(T, Hq, Hkv, d, seed=1640, outlier_channels=2)
+    gc.say("4-bit scores on rotated Q and K")
+    gc.stage_and_chain(orc, q, k, v, do, cu, gc.full_window(T, Hq), hadamard=True, qk4=True)
+
+
 def test_mx4_chunked_backward_identical():
     """Smallest workspace (several key-tile chunks) and the static scratch: bit-identical."""
     T, Hq, Hkv, d = 1536, 4, 2, 128
