@@ -55,6 +55,9 @@ def parse():
                     help="cap the backward's dShat store at this many GiB (chunked backward); default: one chunk")
     ap.add_argument("--cpu-pairs", type=float, default=1.5e8,
                     help="query-key pairs (summed over heads) in the CPU-oracle sample")
+    ap.add_argument("--graph", action="store_true",
+                    help="time replays of one step captured in a HIP graph (stage times from eager steps after "
+                         "the timed region)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibration-copy-mb", type=int, default=0,
                     help="before warmup, run one plain device-to-device copy of this many MiB (reference "
@@ -216,16 +219,35 @@ def main():
     torch.cuda.synchronize()
     status, chunks = fl.bwd_status(ws)
     assert status == 0
+    graph = None
+    if args.graph:  # one step captured on a side stream's graph, after one call there
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        torch.cuda.synchronize()
 
     # timed region: exactly K steps, bracketed by device synchronisation
     all_evs = [[ev() for _ in range(5)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(all_evs[i])
+        if graph is not None:
+            graph.replay()
+        else:
+            step(all_evs[i])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
+    if graph is not None:  # stage times: the same number of eager steps, after the timed region
+        for i in range(args.steps):
+            step(all_evs[i])
+        torch.cuda.synchronize()
     stages = {nm: float(np.median([e[j].elapsed_time(e[j + 1]) for e in all_evs])) for j, nm in enumerate(stage_names)}
     assert fl.bwd_status(ws)[0] == 0
 
@@ -261,7 +283,7 @@ def main():
         "config": {"workload": args.workload, "T": T, "Hq": Hq, "Hkv": Hkv, "d": d, "docs": len(cu) - 1,
                    "visible_pairs": pairs, "flop_per_step": flop, "causal_dq_scale": bool(args.causal_dq),
                    "causal": causal, "hadamard": bool(args.hadamard), "precise": bool(args.precise),
-                   "qk4": bool(args.qk4)},
+                   "qk4": bool(args.qk4), "graph": bool(args.graph)},
         "frac_of_peak": value / PEAK_FP8_TFLOPS,
         "roofline": roofline,
         "quantize": quant,
