@@ -48,6 +48,7 @@ def lib():
         for f in ("orc_e4m3_rne", "orc_e8m0_roundup", "orc_e8m0_floor", "orc_e2m1_rne", "orc_e8m0_roundup4"):
             getattr(_lib, f).argtypes = [ctypes.c_double]
         _lib.orc_worklist.restype = ctypes.c_int
+        _lib.orc_schedule_dynamic.restype = ctypes.c_int
         _lib.orc_num_threads.restype = ctypes.c_int
     return _lib
 
@@ -186,6 +187,13 @@ def worklist(cu, kind, n_workers):
     n = lib().orc_worklist(_p(cu), n_docs, int(kind), int(n_workers), _p(out), cap)
     assert n >= 0
     return out[:n].copy()
+
+
+def schedule_dynamic(cu, kind):
+    """1 if a list of this kind over cu is taken dynamically (non-causal, longest document >= 4x
+    the average), else 0."""
+    cu = _c(cu, np.int32)
+    return int(lib().orc_schedule_dynamic(_p(cu), len(cu) - 1, int(kind)))
 
 
 class _Window(ctypes.Structure):

@@ -413,6 +413,23 @@ static int* doc_map(const int32_t* cu, int n_docs, int T) {
  * (serpentine) directions across n_workers.  Output: 4 ints per item
  * {doc, blk, cost, worker}.  Returns the item count, or -1 if cap is too small.
  * ---------------------------------------------------------------------------------- */
+/* Schedule of a list (jaehun.me §3.4 "Work scheduling"): non-causal calls take their units
+ * dynamically when the longest document is at least 4 times the average document length, the
+ * average taken over the call's n_docs documents (empty ones included); longest * n_docs >=
+ * 4 * (total length) in integers.  Causal lists: 0 here (the forward walks them statically; the
+ * backward takes its units dynamically whatever the flag).  Returns 1 for dynamic, else 0. */
+int orc_schedule_dynamic(const int32_t* cu, int n_docs, int kind) {
+  long long longest = 0, total = 0;
+  int k;
+  if (kind < 2 || n_docs <= 0) return 0;
+  for (k = 0; k < n_docs; ++k) {
+    const long long L = (long long)cu[k + 1] - cu[k];
+    if (L > longest) longest = L;
+    total += L;
+  }
+  return total > 0 && longest * n_docs >= 4 * total;
+}
+
 static int cmp_items(const void* a, const void* b) {
   const int32_t* x = (const int32_t*)a;
   const int32_t* y = (const int32_t*)b;

@@ -69,3 +69,19 @@ def test_extreme_packing_lists(orc):
         t = orc.worklist(toks, kind, 256)
         assert len(t) == 131072 and np.all(t[:, 2] == 1)
         assert np.array_equal(t[:, 0], np.arange(131072)) and not t[:, 1].any()
+
+
+def test_schedule_rule(orc):
+    """[J] §3.4 "Work scheduling": non-causal calls switch to dynamic assignment when the longest
+    document is at least 4x the average.  Hand-worked cases: the pages' skewed mix (one 8192-token
+    document and 224 of 256: longest 8192 against an average of 291), equal lengths, the boundary
+    on both sides (longest exactly 4x the average, and one token short), empty documents counted
+    in the average, no documents; causal kinds never."""
+    cases = [([8192] + [256] * 224, 1), ([512] * 4, 0), ([8, 0, 0, 0], 1), ([7, 1, 0, 0], 0),
+             ([12, 1, 1, 1, 0, 0, 0, 0, 0, 0, 0, 0], 1), ([3, 3, 3, 3], 0), ([], 0), ([0, 0], 0)]
+    for lens, want in cases:
+        cu = workloads.cu_seqlens(lens)
+        for kind in (0, 1):
+            assert orc.schedule_dynamic(cu, kind) == 0, (lens, kind)
+        for kind in (2, 3):
+            assert orc.schedule_dynamic(cu, kind) == want, (lens, kind)
