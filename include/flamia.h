@@ -76,7 +76,17 @@ const char* flamia_status_str(flamia_status s);
  * The list is built on the GPU with no host synchronisation; build it once per micro-batch
  * and reuse it for every layer.
  *
- * Buffer layout: int32 header[4] = {n_items, kind, n_docs, 0}, then n_items flamia_work_item.
+ * Schedule ([J] §3.4 "Work scheduling"): a non-causal list whose longest document is at least
+ * 4 times the average document length (over all n_docs documents, empty ones included:
+ * longest * n_docs >= 4 * total length) is marked for dynamic assignment; the forward then hands
+ * out its units from a counter instead of walking them in serpentine order.  Causal lists are not
+ * marked: the forward walks them statically, and the backward takes its units dynamically for
+ * every list.
+ *
+ * Buffer layout: int32 header[4] = {n_items, kind, n_docs, dynamic (0 or 1)}, then n_items
+ * flamia_work_item; after the room for the items (16 + 16 * (ceil(T / 128) + n_docs) bytes from
+ * the start), 16 int32 unit counters of the forward, cleared by the build and left cleared by
+ * every forward that uses them.  Forwards sharing a marked list must not overlap in time.
  * ------------------------------------------------------------------------------------------ */
 typedef struct {
   int32_t doc;    /* document index */
@@ -87,8 +97,8 @@ typedef struct {
 
 typedef enum { FLAMIA_LIST_FWD = 0, FLAMIA_LIST_BWD = 1, FLAMIA_LIST_FWD_NC = 2, FLAMIA_LIST_BWD_NC = 3 } flamia_list_kind;
 
-/* Host.  Bytes needed for a list over n_docs documents of total length T (an upper bound:
- * 16 + 16 * (ceil(T / 128) + n_docs)). */
+/* Host.  Bytes needed for a list over n_docs documents of total length T:
+ * 16 + 16 * (ceil(T / 128) + n_docs) (header and an upper bound of the items) + 64 (counters). */
 size_t flamia_worklist_bytes(int32_t n_docs, int32_t T, int32_t kind);
 
 /* Enqueue the work-list build.  cu_seqlens: device int32 [n_docs + 1].  list: device buffer of
@@ -165,8 +175,9 @@ flamia_status flamia_quantize(const flamia_qtensor* tensors, int32_t n_tensors, 
  * tile 0, the running max m updated once per tile; per tile p_j = 2^(t_ij - m),
  * l = 2^(m_old - m) l + sum p_j, and the P operand is E4M3_RNE(2^8 p_j) with scale 2^-8.
  * O_i = BF16(acc / l) is written into the packed output; LSE_i = m + log2 l.
- * Work comes from a FLAMIA_LIST_FWD list built for the same cu_seqlens; (item, head) units are
- * spread over a persistent grid in list order.  Invalid rows get O = 0 and LSE = +inf.
+ * Work comes from a FLAMIA_LIST_FWD list built for the same cu_seqlens, n_docs and T; (item,
+ * head) units are spread over a persistent grid in list order, statically (serpentine), or, for a
+ * list marked dynamic, from the list's counter.  Invalid rows get O = 0 and LSE = +inf.
  * Non-causal attention (non_causal = 1; [J] §3.4 "Backward pass", §4.8): every key of the
  * row's document is visible; the key tiles are visited from the document's last one down to
  * tile 0.  Batched attention is the special case of documents of equal length.  Either list kind

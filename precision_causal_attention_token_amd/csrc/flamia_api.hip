@@ -130,7 +130,7 @@ int32_t flamia_num_workers(void) { return num_cus(); }
 size_t flamia_worklist_bytes(int32_t n_docs, int32_t T, int32_t kind) {
   (void)kind;
   if (n_docs < 0 || T < 0) return 0;
-  return 16 + 16 * ((size_t)((T + 127) / 128) + (size_t)n_docs);
+  return worklist_ctr_offset(n_docs, T) + 4 * FWD_CTR_WORDS;
 }
 
 flamia_status flamia_build_worklist(const int32_t* cu_seqlens, int32_t n_docs, int32_t T, int32_t kind,
@@ -141,8 +141,9 @@ flamia_status flamia_build_worklist(const int32_t* cu_seqlens, int32_t n_docs, i
   if (T > FLAMIA_MAX_T_WORKLIST) return FLAMIA_ERR_UNSUPPORTED;
   if (list_bytes < flamia_worklist_bytes(n_docs, T, kind)) return FLAMIA_ERR_WORKSPACE;
   if (!aligned(list, 16)) return FLAMIA_ERR_SHAPE;
-  hipError_t e = launch_worklist(cu_seqlens, n_docs, T, kind, n_workers, static_cast<int32_t*>(list),
-                                 static_cast<hipStream_t>(stream));
+  int32_t* l = static_cast<int32_t*>(list);
+  hipError_t e = launch_worklist(cu_seqlens, n_docs, T, kind, n_workers, l,
+                                 l + worklist_ctr_offset(n_docs, T) / 4, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FLAMIA_OK : FLAMIA_ERR_HIP;
 }
 
@@ -217,6 +218,8 @@ flamia_status flamia_fwd(const flamia_fwd_args* a, void* stream) {
   p.c = score_scale(a->softmax_scale, a->d);
   p.cu = a->cu_seqlens; p.n_docs = a->n_docs;
   p.list = static_cast<const int32_t*>(a->fwd_list);
+  // the list's unit counters, after the items of a list built for these n_docs and T
+  p.ctr = const_cast<int32_t*>(p.list) + worklist_ctr_offset(a->n_docs, a->T) / 4;
   p.o = static_cast<uint16_t*>(a->o); p.ost = a->o_stride_t; p.osh = a->o_stride_h;
   p.lse = a->lse;
   p.causal = a->non_causal ? 0 : 1;

@@ -44,6 +44,11 @@ __device__ __forceinline__ int64_t dbg_index(const DebugDump& g, int h, int row,
 }
 #endif
 
+// int32 words of the forward's unit counters after a work list's items
+constexpr int FWD_CTR_WORDS = 16;
+// byte offset of those counters in a list buffer over n_docs documents of total length T
+inline size_t worklist_ctr_offset(int n_docs, int T) { return 16 + 16 * ((size_t)((T + 127) / 128) + (size_t)n_docs); }
+
 struct QTensorDev {
   const uint16_t* x;
   int64_t st, sh;   // element strides
@@ -81,6 +86,9 @@ struct FwdParams {
   int32_t precise;  // the precision options (per-token scales, V folded into P)
   // 4-bit scores (q4 != nullptr): E2M1 copies of Q and K [T, H, d/2] with exponents [H, T, d/32]
   const uint8_t *q4, *sq4, *k4, *sk4;
+  // the list's unit counters (a list with header word 3 = 1 is taken dynamically): [0] the next
+  // unit, [1] workgroups done; the last workgroup to finish clears both for the next call
+  int32_t* ctr;
 #ifdef FLAMIA_DEBUG_DUMP
   DebugDump dbg;
 #endif
@@ -132,7 +140,7 @@ hipError_t launch_quantize(const QuantParams& p, int d, hipStream_t s);
 // rotated operands back to the inputs' basis.
 hipError_t launch_unrotate(uint16_t* x, int64_t st, int64_t sh, int T, int H, int d, hipStream_t s);
 hipError_t launch_worklist(const int32_t* cu, int n_docs, int T, int kind, int n_workers, int32_t* list,
-                           hipStream_t s);
+                           int32_t* ctr, hipStream_t s);
 hipError_t launch_fwd(const FwdParams& p, int d, int grid, hipStream_t s);
 hipError_t launch_bwd(const BwdParams& p, int d, int grid, hipStream_t s);
 // dQ under the precision options (query-stationary recomputation), after the key-tile pass.

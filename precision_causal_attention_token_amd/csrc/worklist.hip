@@ -73,9 +73,15 @@ __device__ __forceinline__ int n_items_of(int L, int m) {
   return (KIND % 2 == 0) ? ceil_div(L, 256) : m;
 }
 
+// The list's schedule ([J] §3.4 "Work scheduling"): a non-causal list is taken dynamically when
+// its longest document is at least 4 times the average document length (over all n_docs
+// documents): longest * n_docs >= 4 * total, in integers.  Causal lists keep 0 (the forward walks
+// them statically; the backward takes its units dynamically whatever the flag).  `ctr`: the
+// forward's unit counters after the items, cleared here.
 template <int KIND>
 __global__ __launch_bounds__(NT) void worklist_kernel(const int32_t* __restrict__ cu, int n_docs, int max_cost,
-                                                      int max_long, int G, int32_t* __restrict__ list) {
+                                                      int max_long, int G, int32_t* __restrict__ list,
+                                                      int32_t* __restrict__ ctr) {
   extern __shared__ int smem[];
   int* hist = smem;                        // [max_cost + 2]: items per cost
   int* before = hist + (max_cost + 2);     // [max_cost + 2]: items of larger cost
@@ -84,15 +90,20 @@ __global__ __launch_bounds__(NT) void worklist_kernel(const int32_t* __restrict_
   int* scratch = long_m + max_long;        // [NT/64 + 1]
 
   const int tid = threadIdx.x;
+  __shared__ int longest;
   for (int c = tid; c < max_cost + 2; c += NT) hist[c] = 0;
+  if (tid == 0) longest = 0;
+  if (tid < FWD_CTR_WORDS) ctr[tid] = 0;
   __syncthreads();
 
   // ---- phase A: per-thread contiguous range of documents
   const int per = ceil_div(n_docs, NT);
   const int k0 = min(tid * per, n_docs), k1 = min(k0 + per, n_docs);
   int n1 = 0, nl = 0;
+  int lmax = 0;
   for (int k = k0; k < k1; ++k) {
     const int L = cu[k + 1] - cu[k];
+    lmax = max(lmax, L);
     const int m = ceil_div(L, 128);
     if (KIND == 1 ? (m >= 1) : (m == 1)) n1++;
     if (m >= 2) {
@@ -109,6 +120,7 @@ __global__ __launch_bounds__(NT) void worklist_kernel(const int32_t* __restrict_
     }
   }
   if (n1) atomicAdd(&hist[1], n1);
+  if (KIND >= 2 && lmax) atomicMax(&longest, lmax);
   int tot1, totl;
   const int base1 = wg_exclusive_scan(n1, scratch, &tot1);
   const int basel = wg_exclusive_scan(nl, scratch, &totl);
@@ -142,7 +154,8 @@ __global__ __launch_bounds__(NT) void worklist_kernel(const int32_t* __restrict_
       list[0] = total;
       list[1] = KIND;
       list[2] = n_docs;
-      list[3] = 0;
+      const int64_t tokens = n_docs > 0 ? (int64_t)cu[n_docs] - cu[0] : 0;
+      list[3] = (KIND >= 2 && tokens > 0 && (int64_t)longest * n_docs >= 4 * tokens) ? 1 : 0;
     }
   }
   __syncthreads();
@@ -191,14 +204,14 @@ size_t worklist_lds_bytes(int T) {
 }
 
 hipError_t launch_worklist(const int32_t* cu, int n_docs, int T, int kind, int n_workers, int32_t* list,
-                           hipStream_t s) {
+                           int32_t* ctr, hipStream_t s) {
   const int max_cost = (T + 127) / 128 + 1;
   const int max_long = T / 129 + 2;
   const size_t lds = worklist_lds_bytes(T);
   auto go = [&](auto kern) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3(1), dim3(NT), lds, s, cu, n_docs, max_cost, max_long, n_workers, list);
+    hipLaunchKernelGGL(kern, dim3(1), dim3(NT), lds, s, cu, n_docs, max_cost, max_long, n_workers, list, ctr);
     return hipGetLastError();
   };
   switch (kind) {

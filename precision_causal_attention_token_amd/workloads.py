@@ -17,9 +17,11 @@ those pages use are not available, so synthetic draws stand in for them):
   [4096, 32768] with probability 1/2 each; Q, V, dO ~ N(0,1), K ~ Student-t(3).
 * ``tokens``   T=131072, H=8, d=128; 131072 one-token documents.
 * ``onedoc``   T=131072, H=8, d=128; one 131072-token document.
+* ``skewed``   T=65536, H=16, d=128; one 8192-token document followed by 224 of 256 tokens
+  (the pages' skewed mix "8192 + 224 x 256"); N(0,1).
 
 Lengths use ``numpy.random.default_rng(n)`` and data ``torch.Generator().manual_seed(1000+n)``
-with n the workload's number (1..5, 5 for both extreme-packing variants); the last
+with n the workload's number (1..5, 5 for both extreme-packing variants, 6 for the skewed mix); the last
 document of a row is truncated so lengths sum to the row size.
 """
 from dataclasses import dataclass
@@ -27,8 +29,8 @@ from dataclasses import dataclass
 import numpy as np
 import torch
 
-WORKLOADS = ("single", "lognormal", "gqa", "long", "tokens", "onedoc")
-_NUMBER = {"single": 1, "lognormal": 2, "gqa": 3, "long": 4, "tokens": 5, "onedoc": 5}
+WORKLOADS = ("single", "lognormal", "gqa", "long", "tokens", "onedoc", "skewed")
+_NUMBER = {"single": 1, "lognormal": 2, "gqa": 3, "long": 4, "tokens": 5, "onedoc": 5, "skewed": 6}
 
 
 @dataclass
@@ -46,6 +48,7 @@ SHAPES = {
     "long": Shape(65536, 16, 16, 128),
     "tokens": Shape(131072, 8, 8, 128),
     "onedoc": Shape(131072, 8, 8, 128),
+    "skewed": Shape(65536, 16, 16, 128),
 }
 
 
@@ -78,6 +81,8 @@ def doc_lengths(name, seed=None):
         return [1] * T
     if name == "onedoc":
         return [T]
+    if name == "skewed":
+        return [8192] + [256] * 224
     raise KeyError(name)
 
 

@@ -42,7 +42,7 @@ def test_status_strings(lib):
 
 
 def test_size_queries(lib):
-    assert lib.flamia_worklist_bytes(3, 1000, 0) == 16 + 16 * (8 + 3)
+    assert lib.flamia_worklist_bytes(3, 1000, 0) == 16 + 16 * (8 + 3) + 64   # header, items, forward counters
     assert lib.flamia_worklist_bytes(-1, 10, 0) == 0
     T, Hq, d = 1000, 4, 64
     blk = 8192 + 128

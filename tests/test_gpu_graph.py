@@ -13,24 +13,30 @@ from tests.gpu_common import say
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("variant", ["default", "causal_dq_chunked"])
+@pytest.mark.parametrize("variant", ["default", "causal_dq_chunked", "noncausal_dynamic"])
 def test_graph_replays_match_eager(variant):
+    """noncausal_dynamic: a skewed non-causal call, whose forward takes its units from the list's
+    counters (cleared by each run for the next)."""
     T, Hq, Hkv, d = 1536, 4, 2, 128
-    cu = np.array([0, 700, 705, 1300, 1301, 1536], np.int32)
+    causal = variant != "noncausal_dynamic"
+    cu = np.array([0, 700, 705, 1300, 1301, 1536] if causal else [0, 1280] + [1280 + 32 * i for i in range(1, 9)],
+                  np.int32)
     dev = torch.device("cuda:0")
     q, k, v, do = (x.to(dev) for x in workloads.tensors(T, Hq, Hkv, d, seed=1700))
     cu_d = torch.as_tensor(cu).to(dev)
-    lists = fl.Lists(cu_d, T, True)  # built once per micro-batch, outside the graph
-    causal_dq = variant != "default"
+    lists = fl.Lists(cu_d, T, causal)  # built once per micro-batch, outside the graph
+    if not causal:
+        assert int(lists.fwd[3].item()) == 1
+    causal_dq = variant == "causal_dq_chunked"
     budget = 0 if variant == "causal_dq_chunked" else fl.DEFAULT_STORE_BYTES
     ws = torch.empty(fl.bwd_workspace_bytes(len(cu) - 1, T, Hq, d, budget), dtype=torch.uint8, device=dev)
     names = ("o", "lse", "dq", "dk", "dv")
 
     def call():
         qz, kz, vz = fl.quantize([q, k, v], cu_d)
-        o, lse = fl.fwd(qz, kz, vz, cu_d, lists.fwd)
+        o, lse = fl.fwd(qz, kz, vz, cu_d, lists.fwd, causal=causal)
         dc, dsc, D = fl.quantize_do(do, o, cu_d)
-        dq, dk, dv = fl.bwd(qz, kz, vz, (dc, dsc), lse, D, cu_d, lists, None, causal_dq, workspace=ws)
+        dq, dk, dv = fl.bwd(qz, kz, vz, (dc, dsc), lse, D, cu_d, lists, None, causal_dq, workspace=ws, causal=causal)
         return dict(o=o, lse=lse, dq=dq, dk=dk, dv=dv)
 
     eager = {n: x.clone() for n, x in call().items()}

@@ -7,6 +7,7 @@ import numpy as np
 import pytest
 import torch
 
+import precision_causal_attention_token_amd as fl
 from precision_causal_attention_token_amd import workloads
 from tests.gpu_common import doc_window, full_window, gpu_call, say, stage_and_chain, token_mask
 from tests.helpers import bits_to_f64, cosine, exact_attention
@@ -21,6 +22,8 @@ NC_SMALL = [
     ("nc-offsets-gqa4-d64-empty", 1200, 4, 1, 64, [9, 40, 41, 555, 555, 1100], {}),
     ("nc-ragged-d64-studentt", 1000, 2, 1, 64, [0, 129, 383, 385, 1000], dict(k_dist="student_t3")),
     ("nc-one-4096-d128-8wave", 4096, 2, 2, 128, [0, 4096], {}),
+    # longest document >= 4x the average: the forward takes its units dynamically
+    ("nc-skewed-dynamic-d128", 2560, 4, 2, 128, [0, 2048] + [2048 + 64 * i for i in range(1, 9)], {}),
 ]
 
 
@@ -74,6 +77,27 @@ def test_non_causal_long_document_tail(orc):
     cu = np.array([0, T], np.int32)
     q, k, v, do = workloads.tensors(T, Hq, Hkv, d, seed=970)
     stage_and_chain(orc, q, k, v, do, cu, doc_window(cu, 0, (1, 2), tail_blocks=4), tail=True, causal=False)
+
+
+def test_non_causal_dynamic_schedule_8wave(orc):
+    """A 16384-token document and three empty ones (longest = 4x the average: a dynamic list, on
+    the 8-wave forward): the last 128 rows of one head against the oracle; the forward run twice on
+    the same list (its counters cleared by the first) gives the same bits and leaves them cleared."""
+    T, Hq, Hkv, d = 16384, 2, 1, 128
+    cu = np.array([0, T, T, T, T], np.int32)
+    q, k, v, do = workloads.tensors(T, Hq, Hkv, d, seed=975)
+    stage_and_chain(orc, q, k, v, do, cu, doc_window(cu, 0, (1, 2), tail_blocks=4), tail=True, causal=False)
+    dev = torch.device("cuda:0")
+    cu_d = torch.as_tensor(cu).to(dev)
+    lists = fl.Lists(cu_d, T, causal=False)
+    assert int(lists.fwd[3].item()) == 1
+    qz, kz, vz = fl.quantize([x.to(dev) for x in (q, k, v)], cu_d)
+    runs = [fl.fwd(qz, kz, vz, cu_d, lists.fwd, causal=False) for _ in range(2)]
+    torch.cuda.synchronize()
+    assert torch.equal(runs[0][0], runs[1][0]) and torch.equal(runs[0][1], runs[1][1])
+    ctr = lists.fwd[(16 + 16 * ((T + 127) // 128 + len(cu) - 1)) // 4:][:16]
+    assert not ctr.any()
+    say("  dynamic forward: two runs on one list bit-identical, counters cleared")
 
 
 def test_non_causal_with_hadamard_rotation(orc):

@@ -108,6 +108,9 @@ def _list_case(orc, cu, G=None):
         assert n == len(ref), (kind, n, len(ref))
         assert np.array_equal(items.cpu().numpy(), ref), kind
         assert int(buf[1].item()) == kind and int(buf[2].item()) == len(cu) - 1
+        assert int(buf[3].item()) == orc.schedule_dynamic(cu, kind), ("schedule", kind)
+        ctr = buf[(16 + 16 * ((T + 127) // 128 + len(cu) - 1)) // 4:]
+        assert ctr.numel() >= 16 and not ctr[:16].any()  # the forward's counters, cleared
     say("  work lists ok: docs=%d T=%d" % (len(cu) - 1, T))
 
 
@@ -123,7 +126,7 @@ def test_worklist_random(orc):
     _list_case(orc, [0, 0, 0], G=3)     # empty documents only
 
 
-@pytest.mark.parametrize("name", ["single", "lognormal", "gqa", "long", "tokens", "onedoc"])
+@pytest.mark.parametrize("name", ["single", "lognormal", "gqa", "long", "tokens", "onedoc", "skewed"])
 def test_worklist_workloads(orc, name):
     say("work lists: %s" % name)
     _list_case(orc, workloads.cu_seqlens(workloads.doc_lengths(name)))
