@@ -186,7 +186,13 @@ flamia_status flamia_quantize(const flamia_qtensor* tensors, int32_t n_tensors, 
     p.osh = o_stride_h;
     p.D = D;
   }
-  if ((int64_t)p.maxH * ((T + 127) / 128) > 0x7FFFFFFF) return FLAMIA_ERR_UNSUPPORTED;  // grid size
+  int64_t wgs = 0;
+  for (int i = 0; i < n_tensors; ++i) {
+    p.wg_base[i] = (int32_t)wgs;
+    wgs += (int64_t)tensors[i].H * ((T + 127) / 128);
+    if (wgs > 0x7FFFFFFF) return FLAMIA_ERR_UNSUPPORTED;  // grid size
+  }
+  p.wg_base[n_tensors] = (int32_t)wgs;
   hipError_t e = launch_quantize(p, d, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FLAMIA_OK : FLAMIA_ERR_HIP;
 }

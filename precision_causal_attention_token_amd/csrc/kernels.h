@@ -65,6 +65,7 @@ struct QuantParams {
   QTensorDev t[3];
   int32_t n_tensors;
   int32_t T, maxH;
+  int32_t wg_base[4];  // first workgroup of each tensor's (window, head) units; [n_tensors]: total
   const int32_t* cu;
   int32_t n_docs;
   const uint16_t* o;  // dO pass only

@@ -92,12 +92,16 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantParams p) {
   __shared__ int16_t bexp[ROWS];        // exponent for every owned row
 
   const int tid = threadIdx.x;
-  // heads vary fastest over the grid, so the workgroups running at one time read whole token
-  // rows ([T, H, d] packs a token's heads together) rather than one head's slice of many rows
-  const int h = blockIdx.x % p.maxH;
-  const int W0 = (blockIdx.x / p.maxH) * WIN;
-  const QTensorDev& X = p.t[blockIdx.y];
-  if (h >= X.H) return;
+  // One grid over every tensor's (window, head) units, tensor after tensor (no idle workgroups
+  // for tensors with fewer heads).  Heads vary fastest, so the workgroups running at one time
+  // read whole token rows ([T, H, d] packs a token's heads together) rather than one head's
+  // slice of many rows.
+  int ti = 0;
+  while (ti + 1 < p.n_tensors && (int)blockIdx.x >= p.wg_base[ti + 1]) ++ti;
+  const QTensorDev& X = p.t[ti];
+  const int local = (int)blockIdx.x - p.wg_base[ti];
+  const int h = local % X.H;
+  const int W0 = (local / X.H) * WIN;
   const int T = p.T;
 
   // ---- ownership of each row of the window
@@ -313,7 +317,7 @@ hipError_t launch_unrotate(uint16_t* x, int64_t st, int64_t sh, int T, int H, in
 
 hipError_t launch_quantize(const QuantParams& p, int d, hipStream_t s) {
   if (p.T == 0) return hipSuccess;
-  dim3 grid(p.maxH * ((p.T + WIN - 1) / WIN), p.n_tensors);  // (window, head) with the head fastest
+  const dim3 grid(p.wg_base[p.n_tensors]);  // every tensor's (window, head) units
   if (d == 128) hipLaunchKernelGGL(quantize_kernel<128>, grid, dim3(256), 0, s, p);
   else hipLaunchKernelGGL(quantize_kernel<64>, grid, dim3(256), 0, s, p);
   return hipGetLastError();
