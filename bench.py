@@ -33,7 +33,7 @@ PEAK_HBM_GBPS = 8000.0       # MI355X HBM3E
 # scaled by 2.000 and WRITE by 1.000, the factors a 1 GiB copy gives).  Valid only for the
 # backward sources it was measured on (sha256 prefix over attn_bwd.hip, device_common.h,
 # kernels.h); any other build reports null.
-BWD_TRAFFIC = {"workload": "long", "src": "9d1e4ca1d626a003", "read_bytes": 18.087e9, "write_bytes": 13.035e9}
+BWD_TRAFFIC = {"workload": "long", "src": "0e12f4568918393e", "read_bytes": 18.074e9, "write_bytes": 13.033e9}
 
 
 def parse():
