@@ -83,10 +83,12 @@ const char* flamia_status_str(flamia_status s);
  * marked: the forward walks them statically, and the backward takes its units dynamically for
  * every list.
  *
- * Buffer layout: int32 header[4] = {n_items, kind, n_docs, dynamic (0 or 1)}, then n_items
+ * Buffer layout: int32 header[4] = {n_items, kind, n_docs, counters}, then n_items
  * flamia_work_item; after the room for the items (16 + 16 * (ceil(T / 128) + n_docs) bytes from
- * the start), 16 int32 unit counters of the forward, cleared by the build and left cleared by
- * every forward that uses them.  Forwards sharing a marked list must not overlap in time.
+ * the start), 16 int32 unit counters of the forward, cleared by the build.  `counters` is 0 for a
+ * list walked statically, else the counters' position in int32 words from the buffer's start
+ * (the list is marked dynamic); every forward on a marked list leaves its counters cleared, and
+ * forwards sharing a marked list must not overlap in time.
  * ------------------------------------------------------------------------------------------ */
 typedef struct {
   int32_t doc;    /* document index */
@@ -191,7 +193,8 @@ typedef struct {
   float softmax_scale;            /* <= 0 selects 1 / sqrt(d) */
   const int32_t* cu_seqlens;      /* [n_docs + 1] */
   int32_t n_docs;
-  const void* fwd_list;           /* FLAMIA_LIST_FWD list for cu_seqlens */
+  void* fwd_list;                 /* FLAMIA_LIST_FWD list for cu_seqlens (a list marked dynamic
+                                     is written: its unit counters, cleared again by the call) */
   void* o;                        /* out: bf16 [T, Hq, d], element strides below */
   int64_t o_stride_t, o_stride_h;
   float* lse;                     /* out: float32 [Hq, T], log2 units */

@@ -144,8 +144,9 @@ def num_workers():
 
 # ----------------------------------------------------------------------------------------
 def build_worklist(cu_seqlens, T, kind, n_workers=None):
-    """Sorted work list (int32 buffer: header {n_items, kind, n_docs, dynamic} + 4 ints per item,
-    then the forward's unit counters)."""
+    """Sorted work list (int32 buffer: header {n_items, kind, n_docs, counters} + 4 ints per item,
+    then the forward's unit counters; `counters` is their word position for a list marked
+    dynamic, else 0)."""
     lib = load_library()
     n_docs = _check_cu(cu_seqlens)
     nbytes = lib.flamia_worklist_bytes(n_docs, int(T), int(kind))

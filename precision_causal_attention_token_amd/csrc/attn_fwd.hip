@@ -269,14 +269,17 @@ __global__ __launch_bounds__(fwd_threads<W>(), 8 / W) void fwd_kernel(FwdParams 
   const uint32_t voff4 = QK4 ? tile_offset4<D>(p, lane) : 0u;
 
   // Units: the static serpentine walk (round r of workgroup w takes r G + w, or r G + G - 1 - w on
-  // odd rounds), or, for a list whose header asks for it, dynamically: each workgroup takes its
-  // first unit by index and each next one from the list's counter when it has finished the last
-  const bool dyn = p.list[3] != 0;
+  // odd rounds), or, for a list whose header word 3 gives the position of its unit counters,
+  // dynamically: each workgroup takes its first unit by index and each next one from the counter
+  // ([0]) when it has finished the last; [1] counts the workgroups done
+  const int ctr_pos = p.list[3];
+  const bool dyn = ctr_pos != 0;
+  int32_t* const ctr = p.list + ctr_pos;
   __shared__ int unit_slot;
   int u = wg;
   for (int round = 0;; ++round) {
     if (!dyn) u = round * G + ((round & 1) ? (G - 1 - wg) : wg);
-    else if (round > 0) u = next_unit(p.ctr, &unit_slot, G);
+    else if (round > 0) u = next_unit(ctr, &unit_slot, G);
     if (u >= n_units) break;
     const int4 it = items[u / (PARTS * p.Hq)];
     const int h = u % p.Hq, g = h / grp, part = (u / p.Hq) % PARTS;
@@ -617,9 +620,9 @@ __global__ __launch_bounds__(fwd_threads<W>(), 8 / W) void fwd_kernel(FwdParams 
   }
   // dynamic lists: every workgroup has taken its last unit (its counter value came back before
   // this add), so the last one to get here clears the counters for the next call on the list
-  if (dyn && tid == 0 && atomicAdd(&p.ctr[1], 1) == G - 1) {
-    atomicExch(&p.ctr[0], 0);
-    atomicExch(&p.ctr[1], 0);
+  if (dyn && tid == 0 && atomicAdd(&ctr[1], 1) == G - 1) {
+    atomicExch(&ctr[0], 0);
+    atomicExch(&ctr[1], 0);
   }
 
   // ---- rows outside every document: O = 0, LSE = +inf

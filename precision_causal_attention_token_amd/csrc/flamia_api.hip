@@ -223,9 +223,7 @@ flamia_status flamia_fwd(const flamia_fwd_args* a, void* stream) {
   p.T = a->T; p.Hq = a->Hq; p.Hkv = a->Hkv;
   p.c = score_scale(a->softmax_scale, a->d);
   p.cu = a->cu_seqlens; p.n_docs = a->n_docs;
-  p.list = static_cast<const int32_t*>(a->fwd_list);
-  // the list's unit counters, after the items of a list built for these n_docs and T
-  p.ctr = const_cast<int32_t*>(p.list) + worklist_ctr_offset(a->n_docs, a->T) / 4;
+  p.list = static_cast<int32_t*>(a->fwd_list);
   p.o = static_cast<uint16_t*>(a->o); p.ost = a->o_stride_t; p.osh = a->o_stride_h;
   p.lse = a->lse;
   p.causal = a->non_causal ? 0 : 1;

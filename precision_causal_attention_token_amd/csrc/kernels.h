@@ -79,7 +79,7 @@ struct FwdParams {
   float c;  // softmax_scale * log2(e), rounded once to float
   const int32_t* cu;
   int32_t n_docs;
-  const int32_t* list;
+  int32_t* list;  // written only at a dynamic list's unit counters
   uint16_t* o;
   int64_t ost, osh;
   float* lse;
@@ -87,9 +87,6 @@ struct FwdParams {
   int32_t precise;  // the precision options (per-token scales, V folded into P)
   // 4-bit scores (q4 != nullptr): E2M1 copies of Q and K [T, H, d/2] with exponents [H, T, d/32]
   const uint8_t *q4, *sq4, *k4, *sk4;
-  // the list's unit counters (a list with header word 3 = 1 is taken dynamically): [0] the next
-  // unit, [1] workgroups done; the last workgroup to finish clears both for the next call
-  int32_t* ctr;
 #ifdef FLAMIA_DEBUG_DUMP
   DebugDump dbg;
 #endif

@@ -75,9 +75,10 @@ __device__ __forceinline__ int n_items_of(int L, int m) {
 
 // The list's schedule ([J] §3.4 "Work scheduling"): a non-causal list is taken dynamically when
 // its longest document is at least 4 times the average document length (over all n_docs
-// documents): longest * n_docs >= 4 * total, in integers.  Causal lists keep 0 (the forward walks
-// them statically; the backward takes its units dynamically whatever the flag).  `ctr`: the
-// forward's unit counters after the items, cleared here.
+// documents): longest * n_docs >= 4 * total, in integers.  Header word 3 then holds the position
+// (in int32 words from the list's start) of the forward's unit counters `ctr`, after the room
+// for the items, cleared here; causal lists keep 0 (the forward walks them statically; the
+// backward takes its units dynamically whatever the word).
 template <int KIND>
 __global__ __launch_bounds__(NT) void worklist_kernel(const int32_t* __restrict__ cu, int n_docs, int max_cost,
                                                       int max_long, int G, int32_t* __restrict__ list,
@@ -155,7 +156,7 @@ __global__ __launch_bounds__(NT) void worklist_kernel(const int32_t* __restrict_
       list[1] = KIND;
       list[2] = n_docs;
       const int64_t tokens = n_docs > 0 ? (int64_t)cu[n_docs] - cu[0] : 0;
-      list[3] = (KIND >= 2 && tokens > 0 && (int64_t)longest * n_docs >= 4 * tokens) ? 1 : 0;
+      list[3] = (KIND >= 2 && tokens > 0 && (int64_t)longest * n_docs >= 4 * tokens) ? (int)(ctr - list) : 0;
     }
   }
   __syncthreads();

@@ -26,7 +26,7 @@ def test_graph_replays_match_eager(variant):
     cu_d = torch.as_tensor(cu).to(dev)
     lists = fl.Lists(cu_d, T, causal)  # built once per micro-batch, outside the graph
     if not causal:
-        assert int(lists.fwd[3].item()) == 1
+        assert int(lists.fwd[3].item()) != 0  # marked dynamic
     causal_dq = variant == "causal_dq_chunked"
     budget = 0 if variant == "causal_dq_chunked" else fl.DEFAULT_STORE_BYTES
     ws = torch.empty(fl.bwd_workspace_bytes(len(cu) - 1, T, Hq, d, budget), dtype=torch.uint8, device=dev)

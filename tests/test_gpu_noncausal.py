@@ -90,7 +90,7 @@ def test_non_causal_dynamic_schedule_8wave(orc):
     dev = torch.device("cuda:0")
     cu_d = torch.as_tensor(cu).to(dev)
     lists = fl.Lists(cu_d, T, causal=False)
-    assert int(lists.fwd[3].item()) == 1
+    assert int(lists.fwd[3].item()) != 0  # marked dynamic
     qz, kz, vz = fl.quantize([x.to(dev) for x in (q, k, v)], cu_d)
     runs = [fl.fwd(qz, kz, vz, cu_d, lists.fwd, causal=False) for _ in range(2)]
     torch.cuda.synchronize()

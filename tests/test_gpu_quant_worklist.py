@@ -108,9 +108,9 @@ def _list_case(orc, cu, G=None):
         assert n == len(ref), (kind, n, len(ref))
         assert np.array_equal(items.cpu().numpy(), ref), kind
         assert int(buf[1].item()) == kind and int(buf[2].item()) == len(cu) - 1
-        assert int(buf[3].item()) == orc.schedule_dynamic(cu, kind), ("schedule", kind)
-        ctr = buf[(16 + 16 * ((T + 127) // 128 + len(cu) - 1)) // 4:]
-        assert ctr.numel() >= 16 and not ctr[:16].any()  # the forward's counters, cleared
+        pos = (16 + 16 * ((T + 127) // 128 + len(cu) - 1)) // 4  # the forward's counters
+        assert int(buf[3].item()) == (pos if orc.schedule_dynamic(cu, kind) else 0), ("schedule", kind)
+        assert buf.numel() >= pos + 16 and not buf[pos:pos + 16].any()  # cleared by the build
     say("  work lists ok: docs=%d T=%d" % (len(cu) - 1, T))
 
 
