@@ -49,6 +49,7 @@ def lib():
             getattr(_lib, f).argtypes = [ctypes.c_double]
         _lib.orc_worklist.restype = ctypes.c_int
         _lib.orc_schedule_dynamic.restype = ctypes.c_int
+        _lib.orc_small_docs.restype = ctypes.c_int
         _lib.orc_num_threads.restype = ctypes.c_int
     return _lib
 
@@ -187,6 +188,12 @@ def worklist(cu, kind, n_workers):
     n = lib().orc_worklist(_p(cu), n_docs, int(kind), int(n_workers), _p(out), cap)
     assert n >= 0
     return out[:n].copy()
+
+
+def small_docs(cu):
+    """Number of documents of 1 .. 32 tokens (their items close every list)."""
+    cu = _c(cu, np.int32)
+    return int(lib().orc_small_docs(_p(cu), len(cu) - 1))
 
 
 def schedule_dynamic(cu, kind):

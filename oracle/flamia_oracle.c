@@ -409,8 +409,11 @@ static int* doc_map(const int32_t* cu, int n_docs, int T) {
  * kind 1 (backward): one item per 128-key tile kappa of a document; cost = number of
  *   128-query tiles at or after the key tile, ceil((L - 128 kappa) / 128).
  * Items are enumerated document by document, block by block, then sorted by descending
- * cost with ties kept in enumeration order; `worker` tags the items in alternating
- * (serpentine) directions across n_workers.  Output: 4 ints per item
+ * cost; among items of equal cost, those of documents longer than ORC_SMALL_DOC tokens come
+ * first and those of shorter documents (always a single item of cost 1) last, each kept in
+ * enumeration order (the pages fix no order among equal costs; this one puts the short
+ * documents, which a pass of their own can take, at the end of the list).  `worker` tags the
+ * items in alternating (serpentine) directions across n_workers.  Output: 4 ints per item
  * {doc, blk, cost, worker}.  Returns the item count, or -1 if cap is too small.
  * ---------------------------------------------------------------------------------- */
 /* Schedule of a list (jaehun.me §3.4 "Work scheduling"): non-causal calls take their units
@@ -430,10 +433,24 @@ int orc_schedule_dynamic(const int32_t* cu, int n_docs, int kind) {
   return total > 0 && longest * n_docs >= 4 * total;
 }
 
+#define ORC_SMALL_DOC 32
+
+/* Number of documents of 1 .. ORC_SMALL_DOC tokens: the items at the end of every list. */
+int orc_small_docs(const int32_t* cu, int n_docs) {
+  int k, n = 0;
+  for (k = 0; k < n_docs; ++k) {
+    const int L = cu[k + 1] - cu[k];
+    if (L >= 1 && L <= ORC_SMALL_DOC) n++;
+  }
+  return n;
+}
+
+/* items while sorting: {doc, blk, cost, enumeration index, small document (0 or 1)} */
 static int cmp_items(const void* a, const void* b) {
   const int32_t* x = (const int32_t*)a;
   const int32_t* y = (const int32_t*)b;
   if (x[2] != y[2]) return x[2] > y[2] ? -1 : 1; /* cost descending */
+  if (x[4] != y[4]) return x[4] < y[4] ? -1 : 1; /* longer documents first */
   return x[3] < y[3] ? -1 : (x[3] > y[3]); /* then enumeration order */
 }
 
@@ -445,7 +462,7 @@ int orc_worklist(const int32_t* cu, int n_docs, int kind, int n_workers, int32_t
     n += (kind % 2 == 0) ? (L + 255) / 256 : (L + 127) / 128;
   }
   if (n > cap) return -1;
-  tmp = (int32_t*)malloc(sizeof(int32_t) * 4 * (n > 0 ? n : 1));
+  tmp = (int32_t*)malloc(sizeof(int32_t) * 5 * (n > 0 ? n : 1));
   n = 0;
   for (k = 0; k < n_docs; ++k) {
     int L = cu[k + 1] - cu[k], b;
@@ -460,19 +477,20 @@ int orc_worklist(const int32_t* cu, int n_docs, int kind, int n_workers, int32_t
       } else {
         cost = (L - 128 * b + 127) / 128;
       }
-      tmp[4 * n + 0] = k;
-      tmp[4 * n + 1] = b;
-      tmp[4 * n + 2] = cost;
-      tmp[4 * n + 3] = n; /* enumeration index, for the stable tie-break */
+      tmp[5 * n + 0] = k;
+      tmp[5 * n + 1] = b;
+      tmp[5 * n + 2] = cost;
+      tmp[5 * n + 3] = n; /* enumeration index, for the stable tie-break */
+      tmp[5 * n + 4] = L <= ORC_SMALL_DOC;
       n++;
     }
   }
-  qsort(tmp, (size_t)n, sizeof(int32_t) * 4, cmp_items);
+  qsort(tmp, (size_t)n, sizeof(int32_t) * 5, cmp_items);
   for (i = 0; i < n; ++i) {
     int r = i / n_workers, w = i % n_workers;
-    out[4 * i + 0] = tmp[4 * i + 0];
-    out[4 * i + 1] = tmp[4 * i + 1];
-    out[4 * i + 2] = tmp[4 * i + 2];
+    out[4 * i + 0] = tmp[5 * i + 0];
+    out[4 * i + 1] = tmp[5 * i + 1];
+    out[4 * i + 2] = tmp[5 * i + 2];
     out[4 * i + 3] = (r % 2 == 0) ? w : n_workers - 1 - w;
   }
   free(tmp);

@@ -20,14 +20,21 @@ def _check(orc, cu, G=7):
         n = (L + 255) // 256
         total = (n * (n - 1) + m)[L > 0].sum() if kind == 0 else (m * (m + 1) // 2).sum()
         assert items[:, 2].sum() == total
-        # W3: a permutation of the enumeration, non-increasing cost, ties in enumeration order
+        # W3: a permutation of the enumeration, non-increasing cost; among equal costs the
+        # documents longer than 32 tokens first, then the shorter ones (one item each, at the
+        # end of the list), each in enumeration order
         enum = [(k, b) for k in range(len(L)) for b in range(int((L[k] + size - 1) // size))]
         assert sorted(map(tuple, items[:, :2].tolist())) == enum
         assert np.all(np.diff(items[:, 2]) <= 0)
+        small = L[items[:, 0]] <= 32
+        n_small = int(((L >= 1) & (L <= 32)).sum())
+        assert orc.small_docs(cu) == n_small
+        assert not small[:len(items) - n_small].any() and small[len(items) - n_small:].all()
         for c in np.unique(items[:, 2]):
-            sel = items[items[:, 2] == c, :2]
-            keys = sel[:, 0].astype(np.int64) * 1_000_000 + sel[:, 1]
-            assert np.all(np.diff(keys) > 0)
+            for sm in (False, True):
+                sel = items[(items[:, 2] == c) & (small == sm), :2]
+                keys = sel[:, 0].astype(np.int64) * 1_000_000 + sel[:, 1]
+                assert np.all(np.diff(keys) > 0)
         # each item's cost against its own definition (brute force over its keys)
         for doc, blk, cost, _ in items[:50]:
             Ld = int(L[doc])
@@ -85,3 +92,21 @@ def test_schedule_rule(orc):
             assert orc.schedule_dynamic(cu, kind) == 0, (lens, kind)
         for kind in (2, 3):
             assert orc.schedule_dynamic(cu, kind) == want, (lens, kind)
+
+
+def test_small_documents_last(orc):
+    """W5: a hand-worked list.  Lengths 40, 5, 200, 1, 33, 0, 32, 129: documents 1, 3 and 6
+    have at most 32 tokens, so their single cost-1 items close each list, after the cost-1
+    items of documents 0 and 4 (and, backward, of the last key tiles of documents 2 and 7)."""
+    cu = workloads.cu_seqlens([40, 5, 200, 1, 33, 0, 32, 129])
+    want = {
+        0: [(2, 0, 2), (7, 0, 2), (0, 0, 1), (4, 0, 1), (1, 0, 1), (3, 0, 1), (6, 0, 1)],
+        1: [(2, 0, 2), (7, 0, 2), (0, 0, 1), (2, 1, 1), (4, 0, 1), (7, 1, 1), (1, 0, 1), (3, 0, 1), (6, 0, 1)],
+        2: [(2, 0, 2), (7, 0, 2), (0, 0, 1), (4, 0, 1), (1, 0, 1), (3, 0, 1), (6, 0, 1)],
+        3: [(2, 0, 2), (2, 1, 2), (7, 0, 2), (7, 1, 2), (0, 0, 1), (4, 0, 1), (1, 0, 1), (3, 0, 1), (6, 0, 1)],
+    }
+    for kind, ref in want.items():
+        items = orc.worklist(cu, kind, 3)
+        assert [tuple(x) for x in items[:, :3].tolist()] == ref, kind
+        assert items[:, 3].tolist() == [0, 1, 2, 2, 1, 0, 0, 1, 2][:len(ref)]
+    assert orc.small_docs(cu) == 3
