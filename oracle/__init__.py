@@ -191,7 +191,7 @@ def worklist(cu, kind, n_workers):
 
 
 def small_docs(cu):
-    """Number of documents of 1 .. 32 tokens (their items close every list)."""
+    """Number of documents of 1 .. 8 tokens (their items close every list)."""
     cu = _c(cu, np.int32)
     return int(lib().orc_small_docs(_p(cu), len(cu) - 1))
 

@@ -433,7 +433,7 @@ int orc_schedule_dynamic(const int32_t* cu, int n_docs, int kind) {
   return total > 0 && longest * n_docs >= 4 * total;
 }
 
-#define ORC_SMALL_DOC 32
+#define ORC_SMALL_DOC 8
 
 /* Number of documents of 1 .. ORC_SMALL_DOC tokens: the items at the end of every list. */
 int orc_small_docs(const int32_t* cu, int n_docs) {

@@ -135,8 +135,8 @@ def test_noncausal_worklists_brute_force(orc, kind):
         ref = []
         for k, L in enumerate(lens):
             nb = (L + 255) // 256 if kind == 2 else (L + 127) // 128
-            # equal costs: documents of more than 32 tokens first (short ones close the list)
-            ref += [(-((L + 127) // 128), int(L <= 32), k, b) for b in range(nb)]
+            # equal costs: documents of more than 8 tokens first (short ones close the list)
+            ref += [(-((L + 127) // 128), int(L <= 8), k, b) for b in range(nb)]
         ref.sort()
         assert len(got) == len(ref)
         for i, ((negc, _, k, b), row) in enumerate(zip(ref, got)):

@@ -21,13 +21,13 @@ def _check(orc, cu, G=7):
         total = (n * (n - 1) + m)[L > 0].sum() if kind == 0 else (m * (m + 1) // 2).sum()
         assert items[:, 2].sum() == total
         # W3: a permutation of the enumeration, non-increasing cost; among equal costs the
-        # documents longer than 32 tokens first, then the shorter ones (one item each, at the
+        # documents longer than 8 tokens first, then the shorter ones (one item each, at the
         # end of the list), each in enumeration order
         enum = [(k, b) for k in range(len(L)) for b in range(int((L[k] + size - 1) // size))]
         assert sorted(map(tuple, items[:, :2].tolist())) == enum
         assert np.all(np.diff(items[:, 2]) <= 0)
-        small = L[items[:, 0]] <= 32
-        n_small = int(((L >= 1) & (L <= 32)).sum())
+        small = L[items[:, 0]] <= 8
+        n_small = int(((L >= 1) & (L <= 8)).sum())
         assert orc.small_docs(cu) == n_small
         assert not small[:len(items) - n_small].any() and small[len(items) - n_small:].all()
         for c in np.unique(items[:, 2]):
@@ -95,10 +95,10 @@ def test_schedule_rule(orc):
 
 
 def test_small_documents_last(orc):
-    """W5: a hand-worked list.  Lengths 40, 5, 200, 1, 33, 0, 32, 129: documents 1, 3 and 6
-    have at most 32 tokens, so their single cost-1 items close each list, after the cost-1
+    """W5: a hand-worked list.  Lengths 40, 5, 200, 1, 9, 0, 8, 129: documents 1, 3 and 6
+    have at most 8 tokens, so their single cost-1 items close each list, after the cost-1
     items of documents 0 and 4 (and, backward, of the last key tiles of documents 2 and 7)."""
-    cu = workloads.cu_seqlens([40, 5, 200, 1, 33, 0, 32, 129])
+    cu = workloads.cu_seqlens([40, 5, 200, 1, 9, 0, 8, 129])
     want = {
         0: [(2, 0, 2), (7, 0, 2), (0, 0, 1), (4, 0, 1), (1, 0, 1), (3, 0, 1), (6, 0, 1)],
         1: [(2, 0, 2), (7, 0, 2), (0, 0, 1), (2, 1, 1), (4, 0, 1), (7, 1, 1), (1, 0, 1), (3, 0, 1), (6, 0, 1)],
