@@ -12,7 +12,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libflamia.so")
 DEBUG_LIB = os.path.join(os.path.dirname(HERE), "tests", "_build", "libflamia_debug.so")
-SOURCES = ["flamia_api.hip", "quantize.hip", "worklist.hip", "attn_fwd.hip", "attn_bwd.hip", "attn_dqp.hip"]
+SOURCES = ["flamia_api.hip", "quantize.hip", "worklist.hip", "attn_fwd.hip", "attn_bwd.hip", "attn_dqp.hip", "attn_small.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -875,7 +875,7 @@ __global__ __launch_bounds__(DQ_THREADS, 2) void dq_kernel(BwdParams p) {  // tw
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int n = lane & 31, hh = lane >> 5;
-  const int n_items = p.fwd_list[0];
+  const int n_items = list_walk_items(p.fwd_list, p.T, p.small);
   const int4* items = reinterpret_cast<const int4*>(p.fwd_list + 4);
   constexpr int PARTS = ITEM_Q / (QT * DQ_QT);  // workgroup units per work item and head
   const int grp = p.Hq / p.Hkv;
@@ -1150,7 +1150,7 @@ __device__ void layout_chunks(const BwdParams& p) {
     if (tid == PRO_THREADS - 1) p.tile_base[nd] = (int32_t)part[tid];
     __syncthreads();
   }
-  const int n_items = p.list[0];
+  const int n_items = list_walk_items(p.list, p.T, p.small);  // short documents: the small-document pass
   const int4* items = reinterpret_cast<const int4*>(p.list + 4);
   // the precision options store nothing (their dQ pass recomputes): one chunk
   auto blocks_of = [&](int u) {
@@ -1362,6 +1362,10 @@ hipError_t launch_bwd(const BwdParams& p, int d, int grid, hipStream_t s) {
   // dQ pass consumes it (stream order keeps the two apart and the chunks in sequence)
   if (d == 128) hipLaunchKernelGGL(bwd_prologue<128>, dim3(p.Hq + 1), dim3(PRO_THREADS), 0, s, p);
   else hipLaunchKernelGGL(bwd_prologue<64>, dim3(p.Hq + 1), dim3(PRO_THREADS), 0, s, p);
+  if (p.small) {  // the short documents' rows (after the prologue: pi, and the layout's status)
+    const hipError_t e = launch_small_bwd(p, d, s);
+    if (e != hipSuccess) return e;
+  }
   auto chunks = [&](auto bk, auto dk) {
     for (int c = 0; c < p.max_chunks; ++c) {
       BwdParams q = p;

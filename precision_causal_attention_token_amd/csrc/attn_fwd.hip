@@ -257,7 +257,7 @@ __global__ __launch_bounds__(fwd_threads<W>(), 8 / W) void fwd_kernel(FwdParams 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int n = lane & 31, hh = lane >> 5;
-  const int n_items = p.list[0];
+  const int n_items = list_walk_items(p.list, p.T, p.small);  // short documents: the small-document pass
   const int4* items = reinterpret_cast<const int4*>(p.list + 4);
   constexpr int QU = 32 * W;                 // queries per workgroup unit
   constexpr int PARTS = ITEM_Q / QU;         // units per work item and head
@@ -663,7 +663,8 @@ hipError_t launch_fwd(const FwdParams& p, int d, int grid, hipStream_t s) {
     else go(n, n, y);
   } else if (p.causal) go(y, n, n);
   else go(n, n, n);
-  return hipGetLastError();
+  const hipError_t e = hipGetLastError();
+  return (e == hipSuccess && p.small) ? launch_small_fwd(p, d, s) : e;
 }
 
 }  // namespace flamia

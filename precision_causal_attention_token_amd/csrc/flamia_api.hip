@@ -228,6 +228,7 @@ flamia_status flamia_fwd(const flamia_fwd_args* a, void* stream) {
   p.lse = a->lse;
   p.causal = a->non_causal ? 0 : 1;
   p.precise = a->precise ? 1 : 0;
+  p.small = small_docs_pass(a->precise != 0, n4 != 0, a->Hq, a->Hkv);
 #ifdef FLAMIA_DEBUG_DUMP
   p.dbg = g_dbg;
 #endif
@@ -330,6 +331,7 @@ flamia_status flamia_bwd(const flamia_bwd_args* a, void* stream) {
   p.causal_mask = a->non_causal ? 0 : 1;
   p.precise = a->precise ? 1 : 0;
   p.q4 = a->q4; p.sq4 = a->sq4; p.k4 = a->k4; p.sk4 = a->sk4;
+  p.small = small_docs_pass(a->precise != 0, n4 != 0, a->Hq, a->Hkv);
 #ifdef FLAMIA_DEBUG_DUMP
   p.dbg = g_dbg;
 #endif

@@ -47,7 +47,27 @@ __device__ __forceinline__ int64_t dbg_index(const DebugDump& g, int h, int row,
 // int32 words of the forward's unit counters after a work list's items
 constexpr int FWD_CTR_WORDS = 16;
 // byte offset of those counters in a list buffer over n_docs documents of total length T
-inline size_t worklist_ctr_offset(int n_docs, int T) { return 16 + 16 * ((size_t)((T + 127) / 128) + (size_t)n_docs); }
+__host__ __device__ inline size_t worklist_ctr_offset(int n_docs, int T) {
+  return 16 + 16 * ((size_t)((T + 127) / 128) + (size_t)n_docs);
+}
+// Documents of at most SMALL_DOC tokens: one token block each, so every product over one of them
+// takes a single exponent per operand.  The work lists put their items last and count them in
+// counter word 2; on the default 8-bit path the small-document pass takes them instead (its
+// lanes form each row's products one after another, so longer documents stay on the tiles).
+constexpr int SMALL_DOC = 8;
+constexpr int SMALL_MAX_GROUP = 8;  // query heads per KV head the small-document pass takes
+// Whether a call leaves the short documents to the small-document pass (forward and backward
+// decide alike, so both passes form each score the same way): the default 8-bit path.
+inline int small_docs_pass(bool precise, bool qk4, int Hq, int Hkv) {
+  return (!precise && !qk4 && Hq / Hkv <= SMALL_MAX_GROUP) ? 1 : 0;
+}
+// Items an attention kernel walks: the whole list, or (skip_small) all but the closing items of
+// the short documents.
+__device__ __forceinline__ int list_walk_items(const int32_t* list, int T, int skip_small) {
+  const int n = list[0];
+  if (!skip_small) return n;
+  return n - list[worklist_ctr_offset(list[2], T) / 4 + 2];
+}
 
 struct QTensorDev {
   const uint16_t* x;
@@ -87,6 +107,7 @@ struct FwdParams {
   int32_t precise;  // the precision options (per-token scales, V folded into P)
   // 4-bit scores (q4 != nullptr): E2M1 copies of Q and K [T, H, d/2] with exponents [H, T, d/32]
   const uint8_t *q4, *sq4, *k4, *sk4;
+  int32_t small;  // 1: documents of at most SMALL_DOC tokens are left to the small-document pass
 #ifdef FLAMIA_DEBUG_DUMP
   DebugDump dbg;
 #endif
@@ -128,6 +149,7 @@ struct BwdParams {
   int32_t precise;          // the precision options: per-token scales folded into P and dS, dQ
                             // recomputed query-stationary with row-wise dS exponents
   const uint8_t *q4, *sq4, *k4, *sk4;  // 4-bit scores: the forward's E2M1 copies (or nullptr)
+  int32_t small;  // 1: documents of at most SMALL_DOC tokens are left to the small-document pass
 #ifdef FLAMIA_DEBUG_DUMP
   DebugDump dbg;
 #endif
@@ -141,6 +163,11 @@ hipError_t launch_worklist(const int32_t* cu, int n_docs, int T, int kind, int n
                            int32_t* ctr, hipStream_t s);
 hipError_t launch_fwd(const FwdParams& p, int d, int grid, hipStream_t s);
 hipError_t launch_bwd(const BwdParams& p, int d, int grid, hipStream_t s);
+// The small-document pass (documents of 1 .. SMALL_DOC tokens, default 8-bit path): forward
+// O / LSE and backward dQ / dK / dV of those documents' rows.  The backward's runs after the
+// prologue (it reads pi).
+hipError_t launch_small_fwd(const FwdParams& p, int d, hipStream_t s);
+hipError_t launch_small_bwd(const BwdParams& p, int d, hipStream_t s);
 // dQ under the precision options (query-stationary recomputation), after the key-tile pass.
 hipError_t launch_dq_precise(const BwdParams& p, int d, int grid, hipStream_t s);
 

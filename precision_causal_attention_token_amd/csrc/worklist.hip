@@ -14,7 +14,10 @@
 // items (n = ceil(L/256), or m) sit together, in block order, at
 //   #items of cost > m  +  #items of documents k' < k of cost m.
 // Cost-1 items come from documents with m == 1 (FWD) or m >= 1 (BWD) and are placed by a
-// prefix count over documents.  Items of cost >= 2 exist only in "long" documents (m >= 2,
+// prefix count over documents: those of documents longer than SMALL_DOC tokens first, then
+// those of the shorter ones (every kind gives such a document one item of cost 1), which
+// therefore close the list; their number goes to word 2 of the counters after the items, so
+// the attention kernels can leave them to the small-document pass.  Items of cost >= 2 exist only in "long" documents (m >= 2,
 // at most T/129 of them), which are listed in LDS; for every cost c one thread walks that
 // list in document order and emits the items of cost c.
 #include "device_common.h"
@@ -100,13 +103,14 @@ __global__ __launch_bounds__(NT) void worklist_kernel(const int32_t* __restrict_
   // ---- phase A: per-thread contiguous range of documents
   const int per = ceil_div(n_docs, NT);
   const int k0 = min(tid * per, n_docs), k1 = min(k0 + per, n_docs);
-  int n1 = 0, nl = 0;
+  int n1 = 0, ns = 0, nl = 0;
   int lmax = 0;
   for (int k = k0; k < k1; ++k) {
     const int L = cu[k + 1] - cu[k];
     lmax = max(lmax, L);
     const int m = ceil_div(L, 128);
-    if (KIND == 1 ? (m >= 1) : (m == 1)) n1++;
+    if (L >= 1 && L <= SMALL_DOC) ns++;
+    else if (KIND == 1 ? (m >= 1) : (m == 1)) n1++;
     if (m >= 2) {
       nl++;
       if (KIND == 0) {
@@ -120,11 +124,13 @@ __global__ __launch_bounds__(NT) void worklist_kernel(const int32_t* __restrict_
       }
     }
   }
-  if (n1) atomicAdd(&hist[1], n1);
+  if (n1 + ns) atomicAdd(&hist[1], n1 + ns);
   if (KIND >= 2 && lmax) atomicMax(&longest, lmax);
-  int tot1, totl;
+  int tot1, tots, totl;
   const int base1 = wg_exclusive_scan(n1, scratch, &tot1);
+  const int bases = wg_exclusive_scan(ns, scratch, &tots);
   const int basel = wg_exclusive_scan(nl, scratch, &totl);
+  if (tid == 0) ctr[2] = tots;  // after the clearing above (the scans synchronise)
   {
     int j = basel;
     for (int k = k0; k < k1; ++k) {
@@ -162,16 +168,17 @@ __global__ __launch_bounds__(NT) void worklist_kernel(const int32_t* __restrict_
   __syncthreads();
 
   int4* items = reinterpret_cast<int4*>(list + 4);
-  // ---- phase C1: cost-1 items, placed by document order
+  // ---- phase C1: cost-1 items, placed by document order (short documents after the others)
   {
-    int r = base1;
+    int r = base1, rs = tot1 + bases;
     const int b1 = before[1];
     for (int k = k0; k < k1; ++k) {
-      const int m = ceil_div(cu[k + 1] - cu[k], 128);
-      if (KIND == 1 ? (m >= 1) : (m == 1)) {
-        const int pos = b1 + r;
+      const int L = cu[k + 1] - cu[k];
+      const int m = ceil_div(L, 128);
+      const bool small = L >= 1 && L <= SMALL_DOC;
+      if (small || (KIND == 1 ? (m >= 1) : (m == 1))) {
+        const int pos = b1 + (small ? rs++ : r++);
         items[pos] = make_int4(k, KIND == 1 ? m - 1 : 0, 1, serpentine(pos, G));
-        r++;
       }
     }
   }

@@ -110,7 +110,9 @@ def _list_case(orc, cu, G=None):
         assert int(buf[1].item()) == kind and int(buf[2].item()) == len(cu) - 1
         pos = (16 + 16 * ((T + 127) // 128 + len(cu) - 1)) // 4  # the forward's counters
         assert int(buf[3].item()) == (pos if orc.schedule_dynamic(cu, kind) else 0), ("schedule", kind)
-        assert buf.numel() >= pos + 16 and not buf[pos:pos + 16].any()  # cleared by the build
+        ctr = buf[pos:pos + 16].cpu().numpy()
+        assert buf.numel() >= pos + 16 and not ctr[:2].any() and not ctr[3:].any()  # cleared by the build
+        assert int(ctr[2]) == orc.small_docs(cu), ("short documents closing the list", kind)
     say("  work lists ok: docs=%d T=%d" % (len(cu) - 1, T))
 
 
