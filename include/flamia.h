@@ -70,8 +70,10 @@ const char* flamia_status_str(flamia_status s);
  * FLAMIA_LIST_FWD_NC, FLAMIA_LIST_BWD_NC: the same items for non-causal attention, where every
  *   item of a document visits (serves) all of its ceil(L / 128) key (query) tiles: that is the
  *   cost of each of them, so a document's items stay together in block order.
- * Items are enumerated by (document, block) and stably sorted by descending cost; `worker`
- * tags them in alternating (serpentine) order over n_workers: for list index i, with
+ * Items are enumerated by (document, block) and stably sorted by descending cost, except that
+ * among equal costs the items of documents of 1 .. 8 tokens (one item of cost 1 each) come after
+ * the others: they close the list.  `worker` tags them in alternating (serpentine) order over
+ * n_workers: for list index i, with
  * r = i / n_workers, worker = i % n_workers if r is even, else n_workers - 1 - i % n_workers.
  * The list is built on the GPU with no host synchronisation; build it once per micro-batch
  * and reuse it for every layer.
@@ -85,10 +87,13 @@ const char* flamia_status_str(flamia_status s);
  *
  * Buffer layout: int32 header[4] = {n_items, kind, n_docs, counters}, then n_items
  * flamia_work_item; after the room for the items (16 + 16 * (ceil(T / 128) + n_docs) bytes from
- * the start), 16 int32 unit counters of the forward, cleared by the build.  `counters` is 0 for a
- * list walked statically, else the counters' position in int32 words from the buffer's start
- * (the list is marked dynamic); every forward on a marked list leaves its counters cleared, and
- * forwards sharing a marked list must not overlap in time.
+ * the start), 16 int32 unit counters of the forward, cleared by the build, except word 2, which
+ * holds the number of documents of 1 .. 8 tokens (the items that close the list; on the default
+ * 8-bit path with at most 8 query heads per KV head, flamia_fwd and flamia_bwd leave them to a
+ * small-document pass and the tile kernels walk the others).  `counters` is 0 for a list walked
+ * statically, else the counters' position in int32 words from the buffer's start (the list is
+ * marked dynamic); every forward on a marked list leaves words 0 and 1 cleared, and forwards
+ * sharing a marked list must not overlap in time.
  * ------------------------------------------------------------------------------------------ */
 typedef struct {
   int32_t doc;    /* document index */
