@@ -1138,15 +1138,15 @@ __device__ void layout_chunks(const BwdParams& p) {
     const int per = (nd + PRO_THREADS - 1) / PRO_THREADS;
     const int lo = min(nd, tid * per), hi = min(nd, lo + per);
     int64_t sum = 0;
-    for (int k = lo; k < hi; ++k) sum += (p.cu[k + 1] - p.cu[k] + KV_TILE - 1) / KV_TILE;
+    for_docs(p.cu, lo, hi, [&](int, int L) { sum += (L + KV_TILE - 1) / KV_TILE; });
     part[tid] = sum;
     __syncthreads();
     block_scan(part);
     int64_t run = part[tid] - sum;
-    for (int k = lo; k < hi; ++k) {
+    for_docs(p.cu, lo, hi, [&](int k, int L) {
       p.tile_base[k] = (int32_t)run;
-      run += (p.cu[k + 1] - p.cu[k] + KV_TILE - 1) / KV_TILE;
-    }
+      run += (L + KV_TILE - 1) / KV_TILE;
+    });
     if (tid == PRO_THREADS - 1) p.tile_base[nd] = (int32_t)part[tid];
     __syncthreads();
   }
@@ -1298,19 +1298,24 @@ __global__ __launch_bounds__(PRO_THREADS) void bwd_prologue(BwdParams p) {
   }
 
   // causal: running maxima of the V and K block exponents from each document's start
-  if (tid == 0) carry_sh = Seg{0, -1, -1};
+  __shared__ int n_marked;
+  if (tid == 0) {
+    carry_sh = Seg{0, -1, -1};
+    kstart = 0;  // first document starting at or after C0: 0 for C0 = 0 (cu[0] >= 0)
+    n_marked = 0;
+  }
   for (int C0 = 0; C0 < T; C0 += PRO_CHUNK) {
     for (int x = tid; x < PRO_CHUNK; x += PRO_THREADS) flags[x] = 0;
-    if (tid == 0) {  // first document starting at or after C0
-      int lo = 0, hi = p.n_docs;  // lower bound over cu[0 .. n_docs-1]
-      while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (p.cu[mid] < C0) lo = mid + 1; else hi = mid;
-      }
-      kstart = lo;
-    }
     __syncthreads();
-    for (int k = kstart + tid; k < p.n_docs && p.cu[k] < C0 + PRO_CHUNK; k += PRO_THREADS) flags[p.cu[k] - C0] = 1;
+    // every document starting in the chunk is marked once (a thread stops at its first document
+    // past the chunk; the ones after it start later still), so the next chunk's first document
+    // is kstart plus their number
+    int marked = 0;
+    for (int k = kstart + tid; k < p.n_docs && p.cu[k] < C0 + PRO_CHUNK; k += PRO_THREADS) {
+      flags[p.cu[k] - C0] = 1;
+      ++marked;
+    }
+    if (marked) atomicAdd(&n_marked, marked);
     __syncthreads();
     // thread-local inclusive scan of 4 tokens
     Seg loc[4];
@@ -1351,6 +1356,10 @@ __global__ __launch_bounds__(PRO_THREADS) void bwd_prologue(BwdParams p) {
     }
     __syncthreads();
     if (tid == PRO_THREADS - 1) carry_sh = seg_op(pre, run);
+    if (tid == 0) {
+      kstart += n_marked;
+      n_marked = 0;
+    }
     __syncthreads();
   }
 }

@@ -352,6 +352,22 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{a, b}, b2));
 }
 
+// f(k, L) for the documents k of [k0, k1) in order, with L = cu[k + 1] - cu[k]: the bounds are
+// loaded 32 documents at a time, every load of a batch issued before the first is used (one
+// round trip per batch instead of one per document).
+template <typename F>
+__device__ __forceinline__ void for_docs(const int32_t* __restrict__ cu, int k0, int k1, F&& f) {
+  constexpr int B = 32;
+  for (int kb = k0; kb < k1; kb += B) {
+    int c[B + 1];
+#pragma unroll
+    for (int x = 0; x <= B; ++x) c[x] = kb + x <= k1 ? cu[kb + x] : 0;
+#pragma unroll
+    for (int x = 0; x < B; ++x)
+      if (kb + x < k1) f(kb + x, c[x + 1] - c[x]);
+  }
+}
+
 // Document containing token t: the k with cu[k] <= t < cu[k+1], or -1.
 __device__ __forceinline__ int find_doc(const int32_t* __restrict__ cu, int n_docs, int t) {
   if (n_docs <= 0 || t < cu[0] || t >= cu[n_docs]) return -1;

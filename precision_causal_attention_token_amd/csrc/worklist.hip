@@ -105,12 +105,12 @@ __global__ __launch_bounds__(NT) void worklist_kernel(const int32_t* __restrict_
   const int k0 = min(tid * per, n_docs), k1 = min(k0 + per, n_docs);
   int n1 = 0, ns = 0, nl = 0;
   int lmax = 0;
-  for (int k = k0; k < k1; ++k) {
-    const int L = cu[k + 1] - cu[k];
+  for_docs(cu, k0, k1, [&](int, int L) {
     lmax = max(lmax, L);
     const int m = ceil_div(L, 128);
-    if (L >= 1 && L <= SMALL_DOC) ns++;
-    else if (KIND == 1 ? (m >= 1) : (m == 1)) n1++;
+    const bool small = L >= 1 && L <= SMALL_DOC;
+    ns += small ? 1 : 0;
+    n1 += (!small && (KIND == 1 ? (m >= 1) : (m == 1))) ? 1 : 0;
     if (m >= 2) {
       nl++;
       if (KIND == 0) {
@@ -123,7 +123,7 @@ __global__ __launch_bounds__(NT) void worklist_kernel(const int32_t* __restrict_
         atomicAdd(&hist[m], n_items_of<KIND>(L, m));
       }
     }
-  }
+  });
   if (n1 + ns) atomicAdd(&hist[1], n1 + ns);
   if (KIND >= 2 && lmax) atomicMax(&longest, lmax);
   int tot1, tots, totl;
@@ -133,14 +133,14 @@ __global__ __launch_bounds__(NT) void worklist_kernel(const int32_t* __restrict_
   if (tid == 0) ctr[2] = tots;  // after the clearing above (the scans synchronise)
   {
     int j = basel;
-    for (int k = k0; k < k1; ++k) {
-      const int m = ceil_div(cu[k + 1] - cu[k], 128);
+    for_docs(cu, k0, k1, [&](int k, int L) {
+      const int m = ceil_div(L, 128);
       if (m >= 2) {
         long_doc[j] = k;
         long_m[j] = m;
         j++;
       }
-    }
+    });
   }
   __syncthreads();
 
@@ -170,17 +170,27 @@ __global__ __launch_bounds__(NT) void worklist_kernel(const int32_t* __restrict_
   int4* items = reinterpret_cast<int4*>(list + 4);
   // ---- phase C1: cost-1 items, placed by document order (short documents after the others)
   {
-    int r = base1, rs = tot1 + bases;
     const int b1 = before[1];
-    for (int k = k0; k < k1; ++k) {
-      const int L = cu[k + 1] - cu[k];
+    // the two runs of positions this thread fills, each with its serpentine round and worker
+    // stepped along instead of divided out per item
+    int pr = b1 + base1, ps = b1 + tot1 + bases;
+    int rr = pr / G, wr = pr - rr * G, rq = ps / G, wq = ps - rq * G;
+    for_docs(cu, k0, k1, [&](int k, int L) {
       const int m = ceil_div(L, 128);
       const bool small = L >= 1 && L <= SMALL_DOC;
       if (small || (KIND == 1 ? (m >= 1) : (m == 1))) {
-        const int pos = b1 + (small ? rs++ : r++);
-        items[pos] = make_int4(k, KIND == 1 ? m - 1 : 0, 1, serpentine(pos, G));
+        // (selects, no pointer to either counter: both stay in registers)
+        const int pos = small ? ps : pr, round = small ? rq : rr, w = small ? wq : wr;
+        items[pos] = make_int4(k, KIND == 1 ? m - 1 : 0, 1, (round & 1) ? (G - 1 - w) : w);
+        const int w1 = w + 1 == G ? 0 : w + 1, r1 = w + 1 == G ? round + 1 : round;
+        ps = small ? ps + 1 : ps;
+        rq = small ? r1 : rq;
+        wq = small ? w1 : wq;
+        pr = small ? pr : pr + 1;
+        rr = small ? rr : r1;
+        wr = small ? wr : w1;
       }
-    }
+    });
   }
   // ---- phase C2: items of cost >= 2, one thread per cost walking the long documents in order
   for (int c = 2 + tid; c <= max_cost; c += NT) {
