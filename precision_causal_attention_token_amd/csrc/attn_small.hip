@@ -30,7 +30,12 @@ namespace {
 
 constexpr int NL = 64;              // lanes: tokens w0 .. w0 + 63
 constexpr int SW = NL - SMALL_DOC;  // window of document starts per unit: such a document ends by w0 + 63
-constexpr int HEADS_PER_WAVE = 4;  // forward: query heads of one window per wave
+constexpr int HEADS_PER_WAVE = 4;  // heads of one window per wave: query heads forward, KV heads backward
+
+// Documents of 1 .. SMALL_DOC tokens in a work list (counter word 2, written by the list build).
+__device__ __forceinline__ int small_docs_of(const int32_t* list, int T) {
+  return list[worklist_ctr_offset(list[2], T) / 4 + 2];
+}
 
 // First k in [0, n) with cu[k] > x (n if none), searched by the 64 lanes together: each round
 // probes the last entry of 64 equal pieces and keeps the piece where the comparison turns.
@@ -197,6 +202,7 @@ __global__ __launch_bounds__(NL) void small_fwd_kernel(FwdParams p) {
   __shared__ int cw[NL];
   __shared__ float s_row[NL][SMALL_DOC + 1];   // the lane's scores (row i, key a + jo)
   __shared__ uint8_t p_row[NL][SMALL_DOC + 4];  // its probability codes
+  if (small_docs_of(p.list, p.T) == 0) return;  // uniform: the list has no short documents
   const int lane = threadIdx.x, w0 = SW * (int)blockIdx.x;
   int a, b;
   const bool own = window_docs(p.cu, p.n_docs, w0, lane, cw, a, b);
@@ -270,10 +276,10 @@ __global__ __launch_bounds__(NL) void small_fwd_kernel(FwdParams p) {
   }
 }
 
-// ---- backward: one wave per (window, KV head, 64 columns of the gradients), over the group's
-// query heads; the waves of one (window, KV head) form the same P, dS and codes (the scores need
-// every column) and write their own columns of dQ, dK and dV (all 128 columns in one wave's
-// registers would spill)
+// ---- backward: one wave per (window, four KV heads); for each KV head and each 64 columns of
+// the gradients, over the group's query heads (every column pass forms the same P, dS and codes,
+// since the scores need all of d, and writes its own columns of dQ, dK and dV: all 128 columns in
+// registers at once would spill)
 template <int D>
 __global__ __launch_bounds__(NL) void small_bwd_kernel(BwdParams p) {
   constexpr int RS = D + 16;  // LDS row stride of K, V
@@ -290,20 +296,28 @@ __global__ __launch_bounds__(NL) void small_bwd_kernel(BwdParams p) {
     struct { float pv[NL][SMALL_DOC + 1], ds[NL][SMALL_DOC + 1]; } f;
     struct { uint8_t q[NL * RC], dO[NL * RC]; } r;
   } u;
-  if (p.status[0]) return;  // the prologue found cu_seqlens that do not fit (uniform)
-  const int lane = threadIdx.x, w0 = SW * (int)blockIdx.x, g = blockIdx.y, d0 = DC * (int)blockIdx.z;
-  const bool dump = blockIdx.z == 0;  // test builds: one wave of each (window, KV head) dumps
+  // uniform exits: the prologue found cu_seqlens that do not fit, or the list has no short
+  // documents (the call's waves then end after one load)
+  if (p.status[0] || small_docs_of(p.list, p.T) == 0) return;
+  const int lane = threadIdx.x, w0 = SW * (int)blockIdx.x;
   int a, b;
   const bool own = window_docs(p.cu, p.n_docs, w0, lane, cw, a, b);
   if (!__any(own)) return;  // uniform: no barrier is left waiting
   const int t = w0 + lane, L = b - a;
   const float c = p.c, ss = p.softmax_scale;
   const int grp = p.Hq / p.Hkv;
+  const int g_end = min(p.Hkv, HEADS_PER_WAVE * ((int)blockIdx.y + 1));
+#pragma unroll 1
+  for (int g = HEADS_PER_WAVE * (int)blockIdx.y; g < g_end; ++g) {
+  __syncthreads();  // the previous KV head's readers are done with the rows
   stage_rows<D>(p.k, p.sk, p.Hkv, g, p.T, w0, lane, kr, ks);
   stage_rows<D>(p.v, p.sv, p.Hkv, g, p.T, w0, lane, vr, vs);
   __syncthreads();
+#pragma unroll 1
+  for (int d0 = 0; d0 < D; d0 += DC) {
+  const bool dump = d0 == 0;  // test builds: one column pass dumps the decisions
 
-  float ak[DC], av[DC];  // dK, dV of key t, this wave's columns, summed over the group's heads
+  float ak[DC], av[DC];  // dK, dV of key t, these columns, summed over the group's heads
 #pragma unroll
   for (int d = 0; d < DC; ++d) { ak[d] = 0.f; av[d] = 0.f; }
   uint32_t sp = 0, sd = 0;  // the document's block exponent bytes, current head
@@ -446,6 +460,8 @@ __global__ __launch_bounds__(NL) void small_bwd_kernel(BwdParams p) {
       store_bf16x32(vrow + c0, av + c0, 1.f);
     }
   }
+  }  // column passes
+  }  // KV heads
 }
 
 }  // namespace
@@ -461,7 +477,7 @@ hipError_t launch_small_fwd(const FwdParams& p, int d, hipStream_t s) {
 hipError_t launch_small_bwd(const BwdParams& p, int d, hipStream_t s) {
   if (p.T <= 0 || p.n_docs <= 0) return hipSuccess;
   if (p.Hq / p.Hkv > SMALL_MAX_GROUP) return hipErrorInvalidValue;  // the caller keeps such calls on the tile kernels
-  const dim3 grid((p.T + SW - 1) / SW, p.Hkv, d / 64);  // 64 gradient columns per wave
+  const dim3 grid((p.T + SW - 1) / SW, (p.Hkv + HEADS_PER_WAVE - 1) / HEADS_PER_WAVE);
   if (d == 128) hipLaunchKernelGGL(small_bwd_kernel<128>, grid, dim3(NL), 0, s, p);
   else hipLaunchKernelGGL(small_bwd_kernel<64>, grid, dim3(NL), 0, s, p);
   return hipGetLastError();
