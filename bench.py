@@ -28,12 +28,12 @@ METRIC_NC = "non-causal MXFP8 attn fwd+bwd TFLOPS incl. quantize; % of MI355X MX
 PEAK_FP8_TFLOPS = 5000.0     # MI355X dense FP8 / MXFP8 matrix peak
 PEAK_HBM_GBPS = 8000.0       # MI355X HBM3E
 
-# HBM bytes per flamia_bwd call (prologue + key-tile + dQ kernels) on the `long` workload, from
-# the FETCH_SIZE / WRITE_SIZE passes summarised in profiles/flamia_long_hbm_traffic.md (FETCH
-# scaled by 2.000 and WRITE by 1.000, the factors a 1 GiB copy gives).  Valid only for the
-# backward sources it was measured on (sha256 prefix over attn_bwd.hip, device_common.h,
-# kernels.h); any other build reports null.
-BWD_TRAFFIC = {"workload": "long", "src": "0e12f4568918393e", "read_bytes": 18.074e9, "write_bytes": 13.033e9}
+# HBM bytes per flamia_bwd call (prologue, small-document pass, key-tile + dQ kernels) on the
+# `long` workload, from the FETCH_SIZE / WRITE_SIZE passes summarised in
+# profiles/flamia_long_hbm_traffic.md (FETCH scaled by 2.000 and WRITE by 1.000, the factors a
+# 1 GiB copy gives).  Valid only for the backward sources it was measured on (sha256 prefix over
+# attn_bwd.hip, attn_small.hip, device_common.h, kernels.h); any other build reports null.
+BWD_TRAFFIC = {"workload": "long", "src": "7e86b7f822b4d927", "read_bytes": 18.112e9, "write_bytes": 13.033e9}
 
 
 def parse():
@@ -68,7 +68,7 @@ def parse():
 def bwd_source_hash():
     import hashlib
     h = hashlib.sha256()
-    for f in ("attn_bwd.hip", "device_common.h", "kernels.h"):
+    for f in ("attn_bwd.hip", "attn_small.hip", "device_common.h", "kernels.h"):
         with open(os.path.join(ROOT, "precision_causal_attention_token_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
