@@ -33,7 +33,7 @@ PEAK_HBM_GBPS = 8000.0       # MI355X HBM3E
 # profiles/flamia_long_hbm_traffic.md (FETCH scaled by 2.000 and WRITE by 1.000, the factors a
 # 1 GiB copy gives).  Valid only for the backward sources it was measured on (sha256 prefix over
 # attn_bwd.hip, attn_small.hip, device_common.h, kernels.h); any other build reports null.
-BWD_TRAFFIC = {"workload": "long", "src": "7e86b7f822b4d927", "read_bytes": 18.112e9, "write_bytes": 13.033e9}
+BWD_TRAFFIC = {"workload": "long", "src": "9cafb9f6f4e63e8a", "read_bytes": 18.116e9, "write_bytes": 13.033e9}
 
 
 def parse():

@@ -1134,20 +1134,45 @@ __device__ void layout_chunks(const BwdParams& p) {
   __shared__ int64_t part[PRO_THREADS];
   const int tid = threadIdx.x;
   {
+    // each wave takes a contiguous span of documents in groups of 64 (lane l: document
+    // base + l), so the bounds' loads and the table's stores are coalesced; the waves' totals
+    // give each span its start
+    constexpr int NWV = PRO_THREADS / 64;
+    const int lane = tid & 63, wave = tid >> 6;
     const int nd = p.n_docs;
-    const int per = (nd + PRO_THREADS - 1) / PRO_THREADS;
-    const int lo = min(nd, tid * per), hi = min(nd, lo + per);
-    int64_t sum = 0;
-    for_docs(p.cu, lo, hi, [&](int, int L) { sum += (L + KV_TILE - 1) / KV_TILE; });
-    part[tid] = sum;
+    const int per_w = ((nd + NWV - 1) / NWV + 63) / 64 * 64;
+    const int w_lo = min(nd, wave * per_w), w_hi = min(nd, w_lo + per_w);
+    auto tiles = [&](int k) { return (int64_t)((p.cu[k + 1] - p.cu[k] + KV_TILE - 1) / KV_TILE); };
+    int64_t tot = 0;
+    for (int k = w_lo + lane; k < w_hi; k += 64) tot += tiles(k);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) tot += __shfl_xor(tot, off, 64);
+    if (lane == 0) part[wave] = tot;
     __syncthreads();
-    block_scan(part);
-    int64_t run = part[tid] - sum;
-    for_docs(p.cu, lo, hi, [&](int k, int L) {
-      p.tile_base[k] = (int32_t)run;
-      run += (L + KV_TILE - 1) / KV_TILE;
-    });
-    if (tid == PRO_THREADS - 1) p.tile_base[nd] = (int32_t)part[tid];
+    if (tid == 0) {
+      int64_t run = 0;
+      for (int w = 0; w < NWV; ++w) {
+        const int64_t t = part[w];
+        part[w] = run;
+        run += t;
+      }
+      part[NWV] = run;
+    }
+    __syncthreads();
+    int64_t run = part[wave];
+    for (int k0 = w_lo; k0 < w_hi; k0 += 64) {
+      const int k = k0 + lane;
+      const int64_t v = k < w_hi ? tiles(k) : 0;
+      int64_t incl = v;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int64_t y = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += y;
+      }
+      if (k < w_hi) p.tile_base[k] = (int32_t)(run + incl - v);
+      run += __shfl(incl, 63, 64);
+    }
+    if (tid == 0) p.tile_base[nd] = (int32_t)part[NWV];
     __syncthreads();
   }
   const int n_items = list_walk_items(p.list, p.T, p.small);  // short documents: the small-document pass
