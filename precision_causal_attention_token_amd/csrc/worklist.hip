@@ -100,22 +100,31 @@ __global__ __launch_bounds__(NT) void worklist_kernel(const int32_t* __restrict_
   if (tid < FWD_CTR_WORDS) ctr[tid] = 0;
   __syncthreads();
 
-  // ---- phase A: per-thread contiguous range of documents
-  const int per = ceil_div(n_docs, NT);
-  const int k0 = min(tid * per, n_docs), k1 = min(k0 + per, n_docs);
-  int n1 = 0, ns = 0, nl = 0;
+  // ---- phase A: each wave takes a contiguous span of documents, 64 at a time (lane l: document
+  // g0 + l), so the bounds' loads here and the items' stores of phase C1 are coalesced; positions
+  // inside a group come from ballots (lanes below with the same kind of item)
+  constexpr int NWV = NT / 64;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int per_w = (ceil_div(n_docs, NWV) + 63) / 64 * 64;
+  const int w_lo = min(n_docs, wave * per_w), w_hi = min(n_docs, w_lo + per_w);
+  __shared__ int wsum[3][NWV], wbase[3][NWV], wtot[3];
+  int n1 = 0, ns = 0, nl = 0;  // wave-uniform: cost-1 items of longer documents, short documents, long documents
   int lmax = 0;
-  for_docs(cu, k0, k1, [&](int, int L) {
+  for (int g0 = w_lo; g0 < w_hi; g0 += 64) {
+    const int k = g0 + lane;
+    const bool in = k < w_hi;
+    const int L = in ? cu[k + 1] - cu[k] : 0;
     lmax = max(lmax, L);
     const int m = ceil_div(L, 128);
     const bool small = L >= 1 && L <= SMALL_DOC;
-    ns += small ? 1 : 0;
-    n1 += (!small && (KIND == 1 ? (m >= 1) : (m == 1))) ? 1 : 0;
+    const bool one = in && !small && (KIND == 1 ? (m >= 1) : (m == 1));
+    n1 += __popcll(__ballot(one));
+    ns += __popcll(__ballot(small));
+    nl += __popcll(__ballot(m >= 2));
     if (m >= 2) {
-      nl++;
       if (KIND == 0) {
         const int n = ceil_div(L, 256);
-        for (int b = 0; b + 1 < n; ++b) atomicAdd(&hist[2 * b + 2], 1);
+        for (int bb = 0; bb + 1 < n; ++bb) atomicAdd(&hist[2 * bb + 2], 1);
         atomicAdd(&hist[m], 1);
       } else if (KIND == 1) {
         for (int c = 2; c <= m; ++c) atomicAdd(&hist[c], 1);
@@ -123,24 +132,42 @@ __global__ __launch_bounds__(NT) void worklist_kernel(const int32_t* __restrict_
         atomicAdd(&hist[m], n_items_of<KIND>(L, m));
       }
     }
-  });
-  if (n1 + ns) atomicAdd(&hist[1], n1 + ns);
-  if (KIND >= 2 && lmax) atomicMax(&longest, lmax);
-  int tot1, tots, totl;
-  const int base1 = wg_exclusive_scan(n1, scratch, &tot1);
-  const int bases = wg_exclusive_scan(ns, scratch, &tots);
-  const int basel = wg_exclusive_scan(nl, scratch, &totl);
-  if (tid == 0) ctr[2] = tots;  // after the clearing above (the scans synchronise)
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) lmax = max(lmax, __shfl_xor(lmax, off, 64));
+  if (lane == 0) {
+    if (n1 + ns) atomicAdd(&hist[1], n1 + ns);
+    if (KIND >= 2 && lmax) atomicMax(&longest, lmax);
+    wsum[0][wave] = n1;
+    wsum[1][wave] = ns;
+    wsum[2][wave] = nl;
+  }
+  __syncthreads();
+  if (tid < 3) {  // exclusive prefix over the waves, in document order
+    int run = 0;
+    for (int w = 0; w < NWV; ++w) {
+      wbase[tid][w] = run;
+      run += wsum[tid][w];
+    }
+    wtot[tid] = run;
+  }
+  __syncthreads();
+  const int base1 = wbase[0][wave], bases = wbase[1][wave], basel = wbase[2][wave];
+  const int tot1 = wtot[0], tots = wtot[1], totl = wtot[2];
+  if (tid == 0) ctr[2] = tots;  // after the clearing above (the barriers order them)
   {
     int j = basel;
-    for_docs(cu, k0, k1, [&](int k, int L) {
-      const int m = ceil_div(L, 128);
+    for (int g0 = w_lo; g0 < w_hi; g0 += 64) {
+      const int k = g0 + lane;
+      const int m = k < w_hi ? ceil_div(cu[k + 1] - cu[k], 128) : 0;
+      const uint64_t bl = __ballot(m >= 2);
       if (m >= 2) {
-        long_doc[j] = k;
-        long_m[j] = m;
-        j++;
+        const int pos = j + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bl >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bl, 0u));
+        long_doc[pos] = k;
+        long_m[pos] = m;
       }
-    });
+      j += __popcll(bl);
+    }
   }
   __syncthreads();
 
@@ -171,26 +198,30 @@ __global__ __launch_bounds__(NT) void worklist_kernel(const int32_t* __restrict_
   // ---- phase C1: cost-1 items, placed by document order (short documents after the others)
   {
     const int b1 = before[1];
-    // the two runs of positions this thread fills, each with its serpentine round and worker
-    // stepped along instead of divided out per item
-    int pr = b1 + base1, ps = b1 + tot1 + bases;
-    int rr = pr / G, wr = pr - rr * G, rq = ps / G, wq = ps - rq * G;
-    for_docs(cu, k0, k1, [&](int k, int L) {
+    const float rG = 1.0f / (float)G;
+    int r = b1 + base1, rs = b1 + tot1 + bases;  // wave-uniform: next position of each run
+    for (int g0 = w_lo; g0 < w_hi; g0 += 64) {
+      const int k = g0 + lane;
+      const bool in = k < w_hi;
+      const int L = in ? cu[k + 1] - cu[k] : 0;
       const int m = ceil_div(L, 128);
       const bool small = L >= 1 && L <= SMALL_DOC;
-      if (small || (KIND == 1 ? (m >= 1) : (m == 1))) {
-        // (selects, no pointer to either counter: both stay in registers)
-        const int pos = small ? ps : pr, round = small ? rq : rr, w = small ? wq : wr;
+      const bool one = in && !small && (KIND == 1 ? (m >= 1) : (m == 1));
+      const uint64_t bs = __ballot(small), bo = __ballot(one);
+      if (small || one) {
+        const uint64_t bb = small ? bs : bo;
+        const int below = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bb >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bb, 0u));
+        const int pos = (small ? rs : r) + below;
+        // serpentine tag: round = pos / G from a float estimate, corrected exactly
+        int round = (int)((float)pos * rG);
+        while (round > 0 && round * G > pos) --round;
+        while ((round + 1) * G <= pos) ++round;
+        const int w = pos - round * G;
         items[pos] = make_int4(k, KIND == 1 ? m - 1 : 0, 1, (round & 1) ? (G - 1 - w) : w);
-        const int w1 = w + 1 == G ? 0 : w + 1, r1 = w + 1 == G ? round + 1 : round;
-        ps = small ? ps + 1 : ps;
-        rq = small ? r1 : rq;
-        wq = small ? w1 : wq;
-        pr = small ? pr : pr + 1;
-        rr = small ? rr : r1;
-        wr = small ? wr : w1;
       }
-    });
+      r += __popcll(bo);
+      rs += __popcll(bs);
+    }
   }
   // ---- phase C2: items of cost >= 2, one thread per cost walking the long documents in order
   for (int c = 2 + tid; c <= max_cost; c += NT) {
