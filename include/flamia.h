@@ -224,7 +224,10 @@ typedef struct {
   const uint8_t *k4, *sk4;
 } flamia_fwd_args;
 
-/* Errors: NULL pointers, sizes, d, head ratio. */
+/* Errors: NULL pointers, sizes, d, head ratio.  On the default 8-bit path (neither precise nor the
+ * 4-bit scores) with at most 8 query heads per KV head, documents of 1 .. 8 tokens (the items that
+ * close the work list) go through a small-document pass launched by this call; flamia_bwd decides
+ * alike, so both passes form each score the same way. */
 flamia_status flamia_fwd(const flamia_fwd_args* args, void* stream);
 
 /* ------------------------------------------------------------------------------------------
@@ -348,7 +351,8 @@ size_t flamia_bwd_workspace_bytes_for(const int32_t* cu_seqlens_host, int32_t n_
  * flamia_bwd_workspace_bytes(n_docs, T, Hq, d, 0) (FLAMIA_ERR_WORKSPACE).  The status word (first
  * int32 of the workspace) is 0 once the backward has run, 3 when the documents could not be laid
  * out in the launched chunks (inconsistent cu_seqlens, or max_doc_len below the longest
- * document); then the gradient passes do not run. */
+ * document); then the gradient passes do not run.  Documents of 1 .. 8 tokens take the
+ * small-document pass under the same condition as in flamia_fwd. */
 flamia_status flamia_bwd(const flamia_bwd_args* args, void* stream);
 
 /* ------------------------------------------------------------------------------------------
